@@ -1,0 +1,287 @@
+"""TurboQuant oracle: a plain, slow, float64 statement of what the method computes.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module. It shares no code with the HIP path
+(the library under kv_cache_vector_06_amd/ and include/), and the HIP path
+never imports it.
+
+Pages cited below, by key:
+  [DG]  "The Distortion Guarantee — How Good Is This?"
+        (igniting.github.io/turboquant/slides/section-09)
+  [B31] "I Spent 31 Hours On The Math Behind Turboquant So You Dont Have To"
+        (onlylabs.fyi, Baseten research)
+  [OM]  "TurboQuant của Google: nén KV cache 6 lần, hay một paper cũ 9 tháng
+        được PR lại?" (omelet.tech)
+  [WY]  "内存厂商的噩梦来了：谷歌一篇论文如何让 KV Cache 内存占用缩小六倍"
+        (wuyi.wiki)
+
+Every function is float64. Library primitives used as single steps:
+`scipy.special.betainc` (the regularized incomplete beta function, i.e. the
+CDF of a Beta law), `numpy` matrix products, `argmin`, `packbits`.
+
+Readings of points the pages leave open (each is listed in the design doc too):
+  * codebook density: the exact law of one coordinate of a uniform unit
+    vector in R^d, f_d(x) = C_d (1-x^2)^((d-3)/2) on [-1,1] ([OM] section
+    "Trick đầu tiên…", eq. f(x)); C_d is the normaliser Γ(d/2)/(√π Γ((d-1)/2)).
+  * ties in nearest-centroid search go to the lower index.
+  * a zero vector has norm 0 and unit direction u = 0; every later step then
+    follows its plain definition.
+  * prod keeps the 1-bit QJL sketch of the residual in the original space,
+    r = u - Πᵀ c[idx], with projection S (d x d), bit_j = [ (S r)_j >= 0 ].
+  * the prod reconstruction scale is √(π/2)/d · ‖r‖ (derived in
+    `dequant_prod`; the pages print the estimator without it).
+  * bits per coordinate: mse uses b bits; prod uses b-1 bits of Lloyd-Max
+    plus the 1-bit sketch ([OM] section on QJL; [WY] section 4.3).
+  * packing: code j of a vector occupies bits [j·b, j·b+b) of that vector's
+    byte string, least significant bit first; sketch bit j is bit j.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+from scipy.special import betainc
+
+__all__ = [
+    "coord_norm_const", "coord_density", "coord_mass", "coord_first_moment",
+    "coord_second_moment", "lloyd_max", "codebook_mse", "nearest_centroid",
+    "pack_codes", "unpack_codes", "pack_signs", "unpack_signs",
+    "encode_mse", "encode_prod", "dequant_mse", "dequant_prod",
+    "attention", "decode_attention",
+]
+
+
+# ---------------------------------------------------------------------------
+# The coordinate law after a random rotation  ([OM] "Trick đầu tiên…", eq. f(x))
+# ---------------------------------------------------------------------------
+
+def coord_norm_const(d: int) -> float:
+    """C_d such that C_d (1-x^2)^((d-3)/2) integrates to 1 on [-1, 1]."""
+    return math.exp(math.lgamma(d / 2) - math.lgamma((d - 1) / 2)) / math.sqrt(math.pi)
+
+
+def coord_density(x, d: int):
+    """f_d(x) = C_d (1-x^2)^((d-3)/2): one coordinate of a uniform unit vector."""
+    x = np.asarray(x, dtype=np.float64)
+    return coord_norm_const(d) * np.clip(1.0 - x * x, 0.0, None) ** ((d - 3) / 2)
+
+
+def _cdf(x, d: int):
+    # (1+X)/2 ~ Beta((d-1)/2, (d-1)/2) when X has density f_d.
+    a = (d - 1) / 2
+    return betainc(a, a, (1.0 + np.clip(np.asarray(x, np.float64), -1.0, 1.0)) / 2)
+
+
+def coord_mass(a, b, d: int):
+    """∫_a^b f_d(x) dx."""
+    return _cdf(b, d) - _cdf(a, d)
+
+
+def coord_first_moment(a, b, d: int):
+    """∫_a^b x f_d(x) dx = C_d/(d-1) [(1-a²)^((d-1)/2) - (1-b²)^((d-1)/2)]."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    e = (d - 1) / 2
+    g = lambda x: np.clip(1.0 - x * x, 0.0, None) ** e
+    return coord_norm_const(d) / (d - 1) * (g(a) - g(b))
+
+
+def coord_second_moment(a, b, d: int):
+    """∫_a^b x² f_d(x) dx.
+
+    Uses (1-x²) f_d = ((d-1)/d) f_{d+2}, so ∫x² f_d = ∫f_d - ((d-1)/d) ∫f_{d+2}."""
+    return coord_mass(a, b, d) - (d - 1) / d * coord_mass(a, b, d + 2)
+
+
+# ---------------------------------------------------------------------------
+# Lloyd-Max codebook  ([OM] "Lloyd-Max quantizer: chia bucket đúng chỗ", eq. C(f,b))
+# ---------------------------------------------------------------------------
+
+def lloyd_max(d: int, bits: int, tol: float = 1e-13, max_iter: int = 200000, init=None):
+    """Lloyd-Max quantizer of f_d with 2^bits levels.
+
+    Minimises Σ_i ∫_{cell i} (x - c_i)² f_d(x) dx by the two Lloyd conditions:
+    cell edges at midpoints of neighbouring centroids, centroids at the
+    conditional mean of their cell. Starts from the Gaussian N(0,1/d)
+    quantiles at (i+1/2)/K unless `init` is given.
+
+    Returns (centroids[K] ascending, boundaries[K-1], D) where D = d × the
+    per-coordinate MSE, i.e. the expected ‖u - ũ‖² of a unit vector.
+    bits = 0 gives the single centroid 0 and D = 1. Iteration stops when no
+    centroid moves by more than `tol` × (1/√d), the coordinate's scale.
+    """
+    if bits == 0:
+        return np.zeros(1), np.zeros(0), 1.0
+    K = 1 << bits
+    if init is None:
+        from scipy.stats import norm
+        c = norm.ppf((np.arange(K) + 0.5) / K) / math.sqrt(d)
+    else:
+        c = np.array(init, dtype=np.float64)
+    for _ in range(max_iter):
+        t = 0.5 * (c[:-1] + c[1:])
+        lo = np.concatenate(([-1.0], t))
+        hi = np.concatenate((t, [1.0]))
+        c_new = coord_first_moment(lo, hi, d) / coord_mass(lo, hi, d)
+        delta = np.max(np.abs(c_new - c))
+        c = c_new
+        if delta < tol / math.sqrt(d):
+            break
+    else:
+        raise RuntimeError("Lloyd-Max did not converge")
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t, codebook_mse(c, t, d)
+
+
+def codebook_mse(c, t, d: int) -> float:
+    """d × Σ_i ∫_{t_{i-1}}^{t_i} (x - c_i)² f_d(x) dx  (MSE of a unit vector)."""
+    c = np.asarray(c, np.float64)
+    lo = np.concatenate(([-1.0], t))
+    hi = np.concatenate((t, [1.0]))
+    per = (coord_second_moment(lo, hi, d) - 2 * c * coord_first_moment(lo, hi, d)
+           + c * c * coord_mass(lo, hi, d))
+    return float(d * np.sum(per))
+
+
+def nearest_centroid(y, c):
+    """idx = argmin_i |y - c_i|, ties to the lower index ([OM] Lloyd-Max section)."""
+    y = np.asarray(y, np.float64)
+    return np.argmin(np.abs(y[..., None] - np.asarray(c, np.float64)), axis=-1).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Bit packing: LSB-first stream per vector
+# ---------------------------------------------------------------------------
+
+def pack_codes(idx, bits: int) -> np.ndarray:
+    """[N, d] codes → [N, d·bits/8] bytes; code j at bits [j·bits, j·bits+bits)."""
+    idx = np.asarray(idx, np.int64)
+    N, d = idx.shape
+    if bits == 0:
+        return np.zeros((N, 0), np.uint8)
+    planes = (idx[:, :, None] >> np.arange(bits)) & 1          # [N, d, bits]
+    return np.packbits(planes.reshape(N, d * bits).astype(np.uint8), axis=1, bitorder="little")
+
+
+def unpack_codes(packed, d: int, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, np.uint8)
+    N = packed.shape[0]
+    if bits == 0:
+        return np.zeros((N, d), np.int64)
+    stream = np.unpackbits(packed, axis=1, bitorder="little")[:, : d * bits]
+    planes = stream.reshape(N, d, bits).astype(np.int64)
+    return np.sum(planes << np.arange(bits), axis=-1)
+
+
+def pack_signs(z) -> np.ndarray:
+    """[N, m] real → [N, m/8] bytes, bit j = 1 iff z_j >= 0 (sign(0) = +1)."""
+    return np.packbits((np.asarray(z) >= 0).astype(np.uint8), axis=1, bitorder="little")
+
+
+def unpack_signs(packed, m: int) -> np.ndarray:
+    """→ [N, m] of ±1.0."""
+    bits = np.unpackbits(np.asarray(packed, np.uint8), axis=1, bitorder="little")[:, :m]
+    return np.where(bits == 1, 1.0, -1.0)
+
+
+# ---------------------------------------------------------------------------
+# Encode / dequantize
+# ---------------------------------------------------------------------------
+
+def _unit(X):
+    X = np.asarray(X, np.float64)
+    n = np.sqrt(np.sum(X * X, axis=1))
+    u = np.zeros_like(X)
+    nz = n > 0
+    u[nz] = X[nz] / n[nz, None]
+    return n, u
+
+
+def encode_mse(X, rot, c, bits: int):
+    """TurboQuant-mse encode ([DG] "rotate, quantize"; [OM] rotation and Lloyd-Max sections).
+
+    n = ‖x‖ is kept unquantized (the HN thread on qwik-news notes the norm is
+    one scalar per vector); u = x/n; y = Π u; idx_j = nearest centroid of y_j.
+    Returns dict(codes=[N, d·bits/8] uint8, norms=[N] float64, idx=[N,d], y=[N,d]).
+    """
+    n, u = _unit(X)
+    y = u @ np.asarray(rot, np.float64).T
+    idx = nearest_centroid(y, c)
+    return dict(codes=pack_codes(idx, bits), norms=n, idx=idx, y=y)
+
+
+def encode_prod(X, rot, proj, c_m, bits: int):
+    """TurboQuant-prod encode ([OM] QJL section; [WY] sections 4.2-4.3).
+
+    (bits-1)-bit mse quantizer on u, residual r = u - Πᵀ c[idx] in the
+    original space, γ = ‖r‖, and the 1-bit sketch sign(S r).
+    `c_m` is the (bits-1)-bit codebook (the single centroid 0 when bits == 1).
+    """
+    bm = bits - 1
+    n, u = _unit(X)
+    R = np.asarray(rot, np.float64)
+    S = np.asarray(proj, np.float64)
+    y = u @ R.T
+    idx = nearest_centroid(y, c_m)
+    u_mse = np.asarray(c_m, np.float64)[idx] @ R           # Πᵀ c[idx], row form
+    r = u - u_mse
+    gamma = np.sqrt(np.sum(r * r, axis=1))
+    z = r @ S.T
+    return dict(codes=pack_codes(idx, bm), norms=n, qjl=pack_signs(z), gammas=gamma,
+                idx=idx, y=y, z=z)
+
+
+def dequant_mse(codes, norms, rot, c, bits: int):
+    """x̃ = n Πᵀ c[idx]."""
+    d = np.asarray(rot).shape[0]
+    idx = unpack_codes(codes, d, bits)
+    return np.asarray(norms, np.float64)[:, None] * (np.asarray(c, np.float64)[idx] @ np.asarray(rot, np.float64))
+
+
+def dequant_prod(codes, norms, qjl, gammas, rot, proj, c_m, bits: int):
+    """x̃ = n (Πᵀ c[idx] + √(π/2)/d · γ · Sᵀ s), s_j = ±1.
+
+    Scale derivation (the pages print the correction term without it): for
+    one Gaussian row σ of S, (⟨σ,y⟩, ⟨σ,r⟩) is jointly Gaussian with
+    covariance from the Baseten page's fact S·x ~ N(0, ‖x‖² I), so
+    E[⟨σ,y⟩ sign⟨σ,r⟩] = √(2/π) ⟨y,r⟩/‖r‖. Summing d rows and multiplying by
+    √(π/2) ‖r‖ / d makes E⟨y, x̃⟩ = ⟨y, x⟩, the unbiasedness [OM] states in
+    its QJL section.
+    """
+    d = np.asarray(rot).shape[0]
+    m = np.asarray(proj).shape[0]
+    bm = bits - 1
+    idx = unpack_codes(codes, d, bm)
+    s = unpack_signs(qjl, m)
+    base = np.asarray(c_m, np.float64)[idx] @ np.asarray(rot, np.float64)
+    corr = (math.sqrt(math.pi / 2) / m) * np.asarray(gammas, np.float64)[:, None] * (s @ np.asarray(proj, np.float64))
+    return np.asarray(norms, np.float64)[:, None] * (base + corr)
+
+
+# ---------------------------------------------------------------------------
+# Attention  ([B31] "KV Cache: The problem": softmax(Q·Kᵀ/√d)·V)
+# ---------------------------------------------------------------------------
+
+def attention(q, K, V, scale: float):
+    """One query over T keys/values: softmax(K q · scale) V, float64."""
+    q = np.asarray(q, np.float64)
+    s = np.asarray(K, np.float64) @ q * scale
+    p = np.exp(s - np.max(s))
+    p /= np.sum(p)
+    return p @ np.asarray(V, np.float64)
+
+
+def decode_attention(q, K, V, scale: float, ctx_lens=None, heads=None):
+    """q [B,Hq,d]; K,V [B,Hkv,T,d] (already dequantized); query head h reads
+    KV head h // (Hq/Hkv). `ctx_lens[b]` limits the tokens of batch b.
+    `heads` optionally restricts the evaluation to a list of (b, h) pairs.
+    Returns out [B,Hq,d] (rows not evaluated are NaN)."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.full((B, Hq, d), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    for b, h in pairs:
+        L = K.shape[2] if ctx_lens is None else int(ctx_lens[b])
+        out[b, h] = attention(q[b, h], K[b, h // G, :L], V[b, h // G, :L], scale)
+    return out

@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs shared by the HIP path and the oracle.
+
+This module only draws random numbers and lays them out; it holds none of the
+quantizer's arithmetic (no norms, no codebook, no quantization, no attention).
+Every generator is `numpy.random.default_rng(seed)` (PCG64) in float64, then
+rounded to the stated storage dtype, so the GPU and the oracle consume the
+same bytes.
+
+The random draws the method makes are inputs here, as the pages treat them:
+  * the rotation is the orthogonal factor of a QR factorisation of an iid
+    N(0,1) square matrix ("TurboQuant của Google…", omelet.tech, section
+    "Trick đầu tiên: xoay ngẫu nhiên trước khi nén"); the sign of each column
+    is fixed by the sign of R's diagonal so the draw is Haar-distributed;
+  * the QJL projection is an iid N(0,1) square matrix ("内存厂商的噩梦来了…",
+    wuyi.wiki, section 4.2; and the Gaussian-projection fact on "I Spent 31
+    Hours On The Math Behind Turboquant…", onlylabs.fyi).
+
+Workload shapes follow the Llama-3.1-8B cache shape the Baseten page uses
+(8 KV heads, head dim 128; section "KV Cache: The problem").
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+# Seeds for the per-layer constant matrices (one rotation for keys, one for
+# values, one projection), and the per-config data seed base.
+SEED_ROT_K = 1001
+SEED_ROT_V = 1002
+SEED_PROJ = 1003
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64/float32 values to bfloat16 (round to nearest even).
+
+    Returns the rounded values as float32 (exactly representable)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-exact."""
+    return (np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rotation(d: int, seed: int) -> np.ndarray:
+    """Haar-random orthogonal d x d matrix as float32 (y = R @ u)."""
+    g = rng(seed).standard_normal((d, d))
+    q, r = np.linalg.qr(g)
+    q = q * np.sign(np.diag(r))[None, :]
+    return np.ascontiguousarray(q, dtype=np.float32)
+
+
+def projection(d: int, seed: int) -> np.ndarray:
+    """iid N(0,1) d x d matrix as float32."""
+    return np.ascontiguousarray(rng(seed).standard_normal((d, d)), dtype=np.float32)
+
+
+def gaussian(shape, seed: int, dtype: str = "fp32") -> np.ndarray:
+    """iid N(0,1) values rounded to `dtype` ("fp32" or "bf16"), returned as float32."""
+    x = rng(seed).standard_normal(shape)
+    return round_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+
+
+def outlier_kv(B: int, H: int, T: int, d: int, seed: int, n_outliers: int = 4,
+               scale: float = 10.0, dtype: str = "bf16") -> np.ndarray:
+    """[B,H,T,d] N(0,1) cache with `n_outliers` seeded channels per head scaled.
+
+    The same channels are scaled for every token of a head (a per-channel
+    outlier pattern); channels are drawn without replacement per head."""
+    g = rng(seed)
+    x = g.standard_normal((B, H, T, d))
+    for h in range(H):
+        ch = g.choice(d, size=n_outliers, replace=False)
+        x[:, h, :, ch] *= scale
+    return round_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+
+
+def lognormal_kv(B: int, H: int, T: int, d: int, seed: int, sigma: float = 0.5,
+                 dtype: str = "bf16") -> np.ndarray:
+    """[B,H,T,d] N(0,I) directions times per-(b,h,t) LogNormal(0, sigma) scales."""
+    g = rng(seed)
+    x = g.standard_normal((B, H, T, d))
+    s = g.lognormal(0.0, sigma, size=(B, H, T, 1))
+    x = x * s
+    return round_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    """One decode workload: the cache shape, the quantizers and the data recipe."""
+    name: str
+    B: int
+    Hkv: int
+    Hq: int
+    T: int
+    d: int
+    k_variant: str      # "mse" or "prod"
+    k_bits: int         # total bits per coordinate for keys
+    v_bits: int         # bits per coordinate for values (MSE)
+    recipe: str         # "gaussian", "outlier", "lognormal"
+    dtype: str          # storage dtype of the raw K/V ("fp32" or "bf16")
+    seed_base: int
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+# The five workloads. "K" is 1024 tokens.
+CONFIGS = {
+    1: DecodeConfig("mse3_d128_4096_fp32", 1, 1, 1, 4096, 128, "mse", 3, 3, "gaussian", "fp32", 10),
+    2: DecodeConfig("llama8b_b4_32k", 1, 8, 32, 32768, 128, "mse", 4, 4, "outlier", "bf16", 20),
+    3: DecodeConfig("llama8b_prod3_128k", 1, 8, 32, 131072, 128, "prod", 3, 3, "outlier", "bf16", 30),
+    4: DecodeConfig("batch64_b2_16k", 64, 8, 32, 16384, 128, "mse", 2, 2, "lognormal", "bf16", 40),
+    5: DecodeConfig("gqa8_prod4_128k_b4", 4, 8, 64, 131072, 128, "prod", 4, 4, "gaussian", "bf16", 50),
+}
+
+
+def make_kv(cfg: DecodeConfig, T: int | None = None, B: int | None = None):
+    """Raw K and V caches [B,Hkv,T,d] (float32 values, bf16-exact when dtype is bf16).
+
+    `T`/`B` override the config's context length / batch for smaller cases
+    that keep the same value distribution."""
+    T = cfg.T if T is None else T
+    B = cfg.B if B is None else B
+    sk, sv = cfg.seed_base + 0, cfg.seed_base + 1
+    if cfg.recipe == "gaussian":
+        k = gaussian((B, cfg.Hkv, T, cfg.d), sk, cfg.dtype)
+        v = gaussian((B, cfg.Hkv, T, cfg.d), sv, cfg.dtype)
+    elif cfg.recipe == "outlier":
+        k = outlier_kv(B, cfg.Hkv, T, cfg.d, sk, dtype=cfg.dtype)
+        v = outlier_kv(B, cfg.Hkv, T, cfg.d, sv, dtype=cfg.dtype)
+    elif cfg.recipe == "lognormal":
+        k = lognormal_kv(B, cfg.Hkv, T, cfg.d, sk, dtype=cfg.dtype)
+        v = lognormal_kv(B, cfg.Hkv, T, cfg.d, sv, dtype=cfg.dtype)
+    else:
+        raise ValueError(cfg.recipe)
+    return k, v
+
+
+def make_query(cfg: DecodeConfig, B: int | None = None) -> np.ndarray:
+    """fp32 N(0,1) queries [B,Hq,d]."""
+    B = cfg.B if B is None else B
+    return gaussian((B, cfg.Hq, cfg.d), cfg.seed_base + 2, "fp32")
+
+
+def constants(d: int = 128):
+    """(rotation for keys, rotation for values, QJL projection), float32."""
+    return rotation(d, SEED_ROT_K), rotation(d, SEED_ROT_V), projection(d, SEED_PROJ)
