@@ -128,6 +128,10 @@ def lloyd_max(d: int, bits: int, tol: float = 1e-13, max_iter: int = 200000, ini
             break
     else:
         raise RuntimeError("Lloyd-Max did not converge")
+    # f_d is even, so the optimum is antisymmetric; make it exactly so, which
+    # puts the middle boundary at 0 and lets a tie at y = 0 resolve to the
+    # lower index as nearest_centroid states.
+    c = 0.5 * (c - c[::-1])
     t = 0.5 * (c[:-1] + c[1:])
     return c, t, codebook_mse(c, t, d)
 

@@ -62,7 +62,7 @@ def test_one_bit_closed_form(books):
     cd = math.gamma(D / 2) / (math.sqrt(math.pi) * math.gamma((D - 1) / 2))
     e_abs = 2 * cd / (D - 1)
     c, t, Dm = books[1]
-    assert abs(t[0]) < 1e-15
+    assert t[0] == 0.0
     np.testing.assert_allclose(c, [-e_abs, e_abs], rtol=1e-12)
     assert abs(Dm - (1 - D * e_abs ** 2)) < 1e-12
     # d → ∞: E|X|·√d → √(2/π), D → 1 - 2/π (the pages' 0.36).
@@ -115,9 +115,9 @@ def test_gaussian_limit_textbook():
 def test_symmetry_and_sorted(books):
     for b, (c, t, _) in books.items():
         K = 1 << b
-        np.testing.assert_allclose(c[::-1], -c, atol=1e-15)
+        np.testing.assert_array_equal(c[::-1], -c)
         assert np.all(np.diff(c) > 0)
-        assert abs(t[K // 2 - 1]) < 1e-15
+        assert t[K // 2 - 1] == 0.0
         np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), atol=0)
 
 

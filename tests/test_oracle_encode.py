@@ -215,6 +215,14 @@ def test_mse_biased_prod_not_at_one_bit(books):
     assert abs(p.mean()) < 4 * p.std() / math.sqrt(p.size)
 
 
+def test_tie_at_zero_goes_to_lower_index(books):
+    # y = 0 sits exactly on the middle boundary: both middle centroids are at
+    # the same distance and the lower index wins.
+    for b in (1, 2, 3, 4):
+        c = books[b][0]
+        assert nearest_centroid(np.zeros(3), c).tolist() == [(1 << b) // 2 - 1] * 3
+
+
 def test_zero_vector(books):
     c, _, _ = books[3]
     rot = synth.rotation(D, 1)
