@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""TurboQuant hot-path benchmark on one MI355X.
+
+Workload: batch 4 x 8 KV heads x 131072 tokens, 64 query heads (GQA 8),
+d = 128; keys TurboQuant-prod at 4 bits (3-bit Lloyd-Max + 1-bit QJL sketch),
+values TurboQuant-mse at 4 bits; bf16 N(0,1) synthetic K/V (seeded). Plus the
+prefill-scale encode sweep over 2^20 tokens x 8 heads.
+
+One step = one pass of the whole hot path on resident inputs: encode the new
+token's key and value of every (batch, KV head) and append them to the packed
+cache (tq_encode with output slots), then decode attention of every query head
+over the 131072-token packed cache (tq_attn_decode phases 1-3).
+
+Prints one JSON line. `value` is packed-cache bytes read by decode per step /
+step time (GB/s). `roofline` is for the dominant kernel (the split-attention
+launch), timed with HIP events around that launch on its stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = 5
+
+
+def _src_hash(name: str) -> str:
+    with open(os.path.join(ROOT, "kv_cache_vector_06_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_file: str, src: str, launches_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when absent or taken on another version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != _src_hash(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, seconds_hint=20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import synth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    Rk, Rv, S = synth.constants(cfg.d)
+    T = cfg.T
+    K, V = synth.make_kv(cfg, T=T, B=1)
+    Kx, Vx = K[0, 0].astype(np.float64), V[0, 0].astype(np.float64)
+    q = synth.make_query(cfg, B=1)[0, : cfg.G].astype(np.float64)
+    ck = oracle.lloyd_max(cfg.d, cfg.k_bits - 1)[0]
+    cv = oracle.lloyd_max(cfg.d, cfg.v_bits)[0]
+    chunk = 8192
+    t0 = time.perf_counter()
+    ek = [oracle.encode_prod(Kx[i:i + chunk], Rk, S, ck, cfg.k_bits) for i in range(0, T, chunk)]
+    ev = [oracle.encode_mse(Vx[i:i + chunk], Rv, cv, cfg.v_bits) for i in range(0, T, chunk)]
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Kt = np.concatenate([oracle.dequant_prod(e["codes"], e["norms"], e["qjl"], e["gammas"], Rk, S, ck, cfg.k_bits)
+                         for e in ek])
+    Vt = np.concatenate([oracle.dequant_mse(e["codes"], e["norms"], Rv, cv, cfg.v_bits) for e in ev])
+    for h in range(cfg.G):
+        oracle.attention(q[h], Kt, Vt, 1 / math.sqrt(cfg.d))
+    t_dec = time.perf_counter() - t0
+    bytes_unit = T * bytes_per_token(cfg)
+    return {
+        "value": round(bytes_unit / t_dec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"1 of {cfg.B * cfg.Hkv} (batch, KV head) units: {T} tokens, {cfg.G} query heads; "
+                  f"decode = dequantize + softmax attention, float64",
+        "decode_s": round(t_dec, 3),
+        "encode_mvec_s": round(2 * T / t_enc / 1e6, 5), "encode_s": round(t_enc, 3),
+        "encode_sample": f"{2 * T} vectors (keys prod-{cfg.k_bits}, values mse-{cfg.v_bits})",
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def bytes_per_token(cfg) -> int:
+    """Algorithmic packed bytes per token per KV head: codes + fp32 norm for
+    keys and values, plus the 16-byte sketch and fp32 γ for prod keys."""
+    d = cfg.d
+    kb = cfg.k_bits - 1 if cfg.k_variant == "prod" else cfg.k_bits
+    k = d * kb // 8 + 4 + ((d // 8 + 4) if cfg.k_variant == "prod" else 0)
+    v = d * cfg.v_bits // 8 + 4
+    return k + v
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-encode-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this hot path runs on one GPU only (no multi-GPU path is built); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from kv_cache_vector_06_amd import torch_api as TA
+
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    cfg = synth.CONFIGS[WORKLOAD]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    B, Hkv, Hq, T, d = cfg.B, cfg.Hkv, cfg.Hq, cfg.T, cfg.d
+    Rk, Rv, S = synth.constants(d)
+    kq = TA.Quantizer(Rk, cfg.k_bits, cfg.k_variant, S, dev)
+    vq = TA.Quantizer(Rv, cfg.v_bits, "mse", None, dev)
+
+    log(f"[bench] generating {cfg.name}: B={B} Hkv={Hkv} T={T}")
+    K, V = synth.make_kv(cfg)
+    kg = torch.from_numpy(K.reshape(-1, d)).to(torch.bfloat16).to(dev)
+    vg = torch.from_numpy(V.reshape(-1, d)).to(torch.bfloat16).to(dev)
+    del K, V
+    n_vec = B * Hkv * T
+    kc = TA.Packed(kq, n_vec, dev)
+    vc = TA.Packed(vq, n_vec, dev)
+    TA.encode(kq, kg, kc)
+    TA.encode(vq, vg, vc)
+    torch.cuda.synchronize()
+    log("[bench] packed cache ready")
+
+    q = torch.from_numpy(synth.make_query(cfg)).to(dev)
+    g = np.random.default_rng(cfg.seed_base + 5)
+    knew = torch.from_numpy(synth.round_bf16(g.standard_normal((B * Hkv, d)).astype(np.float32))).to(torch.bfloat16).to(dev)
+    vnew = torch.from_numpy(synth.round_bf16(g.standard_normal((B * Hkv, d)).astype(np.float32))).to(torch.bfloat16).to(dev)
+    slots = (torch.arange(B * Hkv, dtype=torch.int64, device=dev) * T + (T - 1))
+    dec = TA.Decoder(B, Hq, Hkv, T, dev)
+    out = torch.empty_like(q)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        TA.encode(kq, knew, kc, slots)
+        TA.encode(vq, vnew, vc, slots)
+        dec(kq, vq, q, kc, vc, out=out, phase=1)
+        if i is not None:
+            ev0[i].record()
+        dec(kq, vq, q, kc, vc, out=out, phase=2)
+        if i is not None:
+            ev1[i].record()
+        dec(kq, vq, q, kc, vc, out=out, phase=3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    k_ms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(args.steps))
+    k_avg = sum(k_ms) / len(k_ms)
+    bpt = bytes_per_token(cfg)
+    dec_bytes = n_vec * bpt
+    value = dec_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (k_avg * 1e-3) / 1e9
+    log(f"[bench] step {ms_step:.4f} ms; split-attention kernel avg {k_avg * 1e3:.1f} us "
+        f"(min {k_ms[0] * 1e3:.1f}, max {k_ms[-1] * 1e3:.1f}); {achieved:.0f} GB/s")
+
+    # Same kernel after writing 1 GiB elsewhere (the 256 MB last-level cache
+    # then holds nothing of the packed cache): shows cache residency effects.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    fl = []
+    for i in range(5):
+        flush.fill_(float(i))
+        dec(kq, vq, q, kc, vc, out=out, phase=1)
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        dec(kq, vq, q, kc, vc, out=out, phase=2)
+        b_.record()
+        torch.cuda.synchronize()
+        fl.append(a_.elapsed_time(b_))
+    del flush
+    flushed_us = sorted(fl)[len(fl) // 2] * 1e3
+    log(f"[bench] split-attention after a cache flush: median {flushed_us:.1f} us")
+
+    enc = {}
+    enc_roof = None
+    if not args.no_encode_sweep:
+        del kc, vc
+        torch.cuda.empty_cache()
+        n_sweep = (1 << 20) * 8
+        xs = torch.cat([kg, vg])[:n_sweep]
+        for label, bits, var in (("mse1", 1, "mse"), ("mse2", 2, "mse"), ("mse3", 3, "mse"), ("mse4", 4, "mse"),
+                                 ("prod4", 4, "prod")):
+            qq = TA.Quantizer(Rk, bits, var, S if var == "prod" else None, dev)
+            pk = TA.Packed(qq, n_sweep, dev)
+            TA.encode(qq, xs, pk)
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 3
+            a_.record()
+            for _ in range(reps):
+                TA.encode(qq, xs, pk)
+            b_.record()
+            torch.cuda.synchronize()
+            ms = a_.elapsed_time(b_) / reps
+            enc[label] = round(n_sweep / (ms * 1e-3) / 1e6, 1)
+            if label == "mse4":
+                eb = n_sweep * (2 * d + d * 4 // 8 + 4)
+                enc_roof = {"kernel": "encode_kernel<4,mse,bf16>", "bound": "hbm",
+                            "achieved": round(eb / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                            "traffic": _traffic("encode_mse4_sweep.counters.json", "tq_encode.hip", eb)}
+            del pk, qq
+            log(f"[bench] encode {label}: {enc[label]} Mvec/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(cfg)
+
+    rec = {
+        "metric": "packed-KV decode-attn HBM GB/s (% of peak) @128K ctx; encode Mvec/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32",
+        "data": "synthetic (seeded bf16 N(0,1) K/V, fp32 N(0,1) queries)",
+        "config": {"workload": cfg.name, "B": B, "Hkv": Hkv, "Hq": Hq, "ctx": T, "d": d,
+                   "keys": f"prod-{cfg.k_bits}", "values": f"mse-{cfg.v_bits}",
+                   "step": "append 1 token per (batch, KV head) + decode all query heads",
+                   "packed_bytes_per_token_head": bpt, "packed_cache_bytes": dec_bytes},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "roofline": {"kernel": "attn_split_kernel<3,prod,4>", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic("attn_split_gqa8_prod4_128k.counters.json", "tq_decode.hip", dec_bytes),
+                     "avg_launch_us": round(k_avg * 1e3, 2), "after_cache_flush_us": round(flushed_us, 2)},
+        "encode_mvec_s": enc,
+        "encode_roofline": enc_roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

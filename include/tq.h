@@ -1,0 +1,227 @@
+/*
+ * tq.h — C ABI of the TurboQuant hot path on AMD Instinct MI355X (gfx950).
+ *
+ * TurboQuant compresses each key/value vector of an LLM KV cache online:
+ * keep its norm, rotate it by a fixed random orthogonal matrix, quantize every
+ * rotated coordinate to the nearest of 2^b Lloyd-Max centroids and store the
+ * index; the inner-product ("prod") variant spends one of the b bits on a
+ * 1-bit QJL sketch of the residual. Decode attention scores a full-precision
+ * query against the packed keys, applies softmax and averages the packed
+ * values.
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [DG]  "The Distortion Guarantee — How Good Is This?" (igniting.github.io
+ *         turboquant slides, section 9)
+ *   [B31] "I Spent 31 Hours On The Math Behind Turboquant So You Dont Have To"
+ *         (onlylabs.fyi, Baseten)
+ *   [OM]  "TurboQuant của Google: nén KV cache 6 lần, hay một paper cũ 9 tháng
+ *         được PR lại?" (omelet.tech)
+ *   [WY]  "内存厂商的噩梦来了：谷歌一篇论文如何让 KV Cache 内存占用缩小六倍"
+ *         (wuyi.wiki)
+ *
+ * Conventions for every entry point:
+ *   - All functions are extern "C" and return an int status: 0 (TQ_OK) or a
+ *     negative tq_status. No C++ exception crosses the ABI.
+ *   - Argument checks are synchronous: on any error nothing is launched and
+ *     no output is written.
+ *   - Pointers named "device" must point to HIP device memory (or memory the
+ *     GPU can address); "host" pointers to host memory. The caller owns every
+ *     buffer; the library never allocates or frees memory and keeps no global
+ *     mutable state, so calls on different streams may run concurrently as
+ *     long as they do not write the same buffers.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Launches are
+ *     asynchronous on it; a launch failure returns TQ_ERR_HIP, and faults
+ *     during execution surface at the caller's next synchronization.
+ *   - Head dimension d must be 128 for the GPU entry points.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1,  /* null pointer, bad size, inconsistent shapes        */
+  TQ_ERR_UNSUPPORTED = -2,  /* d != 128, bits outside 1..4, unknown variant/dtype  */
+  TQ_ERR_HIP = -3,          /* a HIP launch or runtime call failed                */
+  TQ_ERR_WORKSPACE = -4,    /* workspace / prepared buffer too small or misaligned */
+  TQ_ERR_NO_CONVERGE = -5   /* Lloyd-Max iteration did not converge               */
+};
+
+enum tq_variant { TQ_MSE = 0, TQ_PROD = 1 };
+enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 };
+
+/* Head dimension supported by the GPU kernels. */
+#define TQ_HEAD_DIM 128
+
+/*
+ * tq_codebook — Lloyd-Max scalar quantizer for one rotated coordinate (host).
+ *
+ * Defined by [OM] section "Lloyd-Max quantizer: chia bucket đúng chỗ",
+ * eq. C(f,b): 2^bits centroids minimising Σ_i ∫_{cell i} (x - c_i)² f(x) dx,
+ * for the density of one coordinate of a uniformly random unit vector in R^d,
+ * f(x) = C (1-x²)^((d-3)/2) on [-1,1] ([OM] section "Trick đầu tiên: xoay
+ * ngẫu nhiên trước khi nén", eq. f(x)).
+ *
+ *   d          dimension, 2 <= d <= 65536 (any d; the GPU kernels need 128)
+ *   bits       0..8 (0 gives the single centroid 0, used by prod at b = 1)
+ *   centroids  host out, double[2^bits], ascending, exactly antisymmetric
+ *              (c[K-1-i] == -c[i])
+ *   boundaries host out, double[2^bits - 1] (may be NULL when bits == 0),
+ *              boundaries[i] = (c[i] + c[i+1]) / 2; the middle one is 0.0
+ *   mse_unit   host out or NULL: d × the per-coordinate distortion, i.e. the
+ *              expected ‖u - ũ‖² of a unit vector ([DG] "The Upper Bound")
+ * Errors: TQ_ERR_INVALID_ARG (null outputs, d < 2), TQ_ERR_UNSUPPORTED
+ * (bits > 8 or d > 65536), TQ_ERR_NO_CONVERGE.
+ */
+int tq_codebook(int d, int bits, double* centroids, double* boundaries, double* mse_unit);
+
+/*
+ * One quantizer instance (one per role: keys or values of a layer).
+ * Every pointer is device memory owned by the caller; the library reads them.
+ *   d          128
+ *   bits       total bits per coordinate, 1..4
+ *   variant    TQ_MSE: bits-bit Lloyd-Max codes
+ *              TQ_PROD: (bits-1)-bit Lloyd-Max codes + 1-bit QJL sketch of
+ *              the residual ([OM] QJL section; [WY] section 4.3)
+ *   rot        float[d][d] row-major, the orthogonal Π; the rotated vector is
+ *              y = Π·u ([OM] "Trick đầu tiên…")
+ *   proj       float[d][d] row-major Gaussian S of the QJL sketch (PROD), else NULL
+ *   centroids  float[2^bm] from tq_codebook(d, bm) rounded to float, bm = bits
+ *              (MSE) or bits-1 (PROD); must be antisymmetric like the output
+ *              of tq_codebook
+ *   boundaries float[2^bm - 1], the midpoints (NULL allowed when bm == 0)
+ *   prep       device buffer of tq_prep_bytes() bytes, 256-byte aligned,
+ *              filled by tq_prepare() from the fields above before the
+ *              quantizer is used by tq_encode / tq_attn_decode
+ */
+typedef struct tq_quantizer {
+  int d;
+  int bits;
+  int variant;
+  const float* rot;
+  const float* proj;
+  const float* centroids;
+  const float* boundaries;
+  void* prep;
+} tq_quantizer;
+
+/*
+ * Packed vectors, vector-major; caller-owned device memory.
+ *   codes   uint8[n][d*bm/8]: code j of a vector occupies bits [j·bm, j·bm+bm)
+ *           of that vector's byte string, least significant bit first (byte k
+ *           holds stream bits 8k..8k+7); every 32 codes fill bm whole 32-bit
+ *           words. NULL allowed when bm == 0.
+ *   norms   float[n], ‖x‖ kept unquantized (the qwik-news HN thread: one
+ *           scalar per vector, stored as is)
+ *   qjl     uint8[n][d/8] (PROD, else NULL): bit j = 1 iff (S·r)_j >= 0, same
+ *           LSB-first order
+ *   gammas  float[n] (PROD, else NULL): ‖r‖, the residual norm the QJL
+ *           estimator scales by
+ * Buffers must be 16-byte aligned.
+ */
+typedef struct tq_packed {
+  uint8_t* codes;
+  float* norms;
+  uint8_t* qjl;
+  float* gammas;
+} tq_packed;
+
+/* Size in bytes of the prepared-operand buffer of one quantizer. */
+size_t tq_prep_bytes(void);
+
+/*
+ * tq_prepare — derive the GPU operands of a quantizer into q->prep.
+ * Splits Π (and S·Πᵀ for PROD) into the matrix-core operand layout the
+ * encoder uses. Run once per quantizer (after its rot/proj/centroids are
+ * written), on `stream`; later calls on the same stream see the result.
+ * Errors: TQ_ERR_INVALID_ARG (null q/fields, prep misaligned),
+ * TQ_ERR_UNSUPPORTED (d, bits, variant), TQ_ERR_HIP.
+ */
+int tq_prepare(const tq_quantizer* q, void* stream);
+
+/*
+ * tq_encode — TurboQuant encode of n vectors ([DG] "rotate, quantize, done";
+ * [OM] sections "Trick đầu tiên…" and "Lloyd-Max quantizer…" for MSE; [OM]
+ * QJL section and [WY] section 4.3 for PROD).
+ *   norm n = ‖x‖; u = x/n (u = 0 when n = 0); y = Π·u;
+ *   idx_j = #{i : boundaries[i] < y_j} (the nearest centroid, ties to the
+ *   lower index); PROD adds r = u - Πᵀc[idx], γ = ‖r‖, bits sign(S·r).
+ *   q         prepared quantizer
+ *   x         device, n rows of d values, dtype x_dtype (TQ_F32 or TQ_BF16),
+ *             row i at x + i*x_row_stride elements; rows 16-byte aligned
+ *   n         number of vectors, >= 0 (0 is a no-op)
+ *   x_row_stride  elements between rows, >= d, multiple of 8
+ *   out       device outputs (see tq_packed)
+ *   out_slot  device int64[n] or NULL: row i is stored at slot out_slot[i] of
+ *             `out` (NULL: at slot i). This appends new tokens into a cache
+ *             laid out as in tq_attn_decode. Slots must be >= 0, inside the
+ *             caller's buffers and distinct; they are not checked.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP.
+ */
+int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int64_t n,
+              int64_t x_row_stride, const tq_packed* out, const int64_t* out_slot,
+              void* stream);
+
+/*
+ * tq_attn_decode_workspace — bytes of device workspace tq_attn_decode needs
+ * for this shape (a pure function of its arguments). Returns 0 for invalid
+ * shapes.
+ */
+size_t tq_attn_decode_workspace(int B, int Hq, int Hkv, int64_t max_ctx);
+
+/*
+ * tq_attn_decode — one decode step of attention over a packed KV cache.
+ * For every batch b and query head h, with KV head kv = h / (Hq/Hkv):
+ *   out[b][h] = Σ_t softmax_t(scale·⟨q[b][h], k̃_t⟩) · ṽ_t
+ * over t < ctx_lens[b] ([B31] section "KV Cache: The problem":
+ * softmax(Q·Kᵀ/√d)·V; the query stays full precision, the "asymmetric
+ * estimator" of [WY] section 4.2), where k̃, ṽ are the dequantized vectors:
+ *   MSE:  x̃ = n Πᵀ c[idx]
+ *   PROD: x̃ = n (Πᵀ c[idx] + √(π/2)/d · γ · Sᵀ s),  s_j = ±1 from the sketch.
+ *   kq, vq     prepared quantizers of keys and values (vq must be TQ_MSE)
+ *   query      device float[B][Hq][d]
+ *   ctx_lens   device int32[B] or NULL (all max_ctx); values are clamped to
+ *              [0, max_ctx]; a batch with length 0 gets an all-zero output
+ *   max_ctx    tokens allocated per (b, kv head), >= 1
+ *   k_cache, v_cache  packed caches: vector index ((b*Hkv + kv)*max_ctx + t)
+ *   scale      softmax scale, usually 1/√d
+ *   out        device float[B][Hq][d]
+ *   workspace  device, >= tq_attn_decode_workspace(B, Hq, Hkv, max_ctx)
+ *              bytes, 256-byte aligned; contents need not be initialised
+ * Errors: TQ_ERR_INVALID_ARG (null pointers, B/Hq/Hkv < 1, Hq % Hkv != 0,
+ * max_ctx < 1), TQ_ERR_UNSUPPORTED (d, bits, value quantizer not MSE),
+ * TQ_ERR_WORKSPACE, TQ_ERR_HIP.
+ */
+int tq_attn_decode(const tq_quantizer* kq, const tq_quantizer* vq, const float* query,
+                   int B, int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx,
+                   const tq_packed* k_cache, const tq_packed* v_cache, float scale,
+                   float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * tq_attn_decode_phase — one of the three launches tq_attn_decode makes, for
+ * callers that schedule or time them separately (same arguments, same checks):
+ *   phase 1: query operands (Π_K·q and S·q per query head) into the workspace
+ *   phase 2: split attention over the packed cache → per-split partials
+ *   phase 3: combine the splits and rotate back into `out`
+ * Running phases 1, 2, 3 in order on one stream equals tq_attn_decode. Phase
+ * 2 reads what phase 1 wrote and phase 3 what phase 2 wrote, in `workspace`.
+ * Errors: as tq_attn_decode, plus TQ_ERR_INVALID_ARG for another phase value.
+ */
+int tq_attn_decode_phase(int phase, const tq_quantizer* kq, const tq_quantizer* vq,
+                         const float* query, int B, int Hq, int Hkv, const int32_t* ctx_lens,
+                         int64_t max_ctx, const tq_packed* k_cache, const tq_packed* v_cache,
+                         float scale, float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H_ */

@@ -1,0 +1,69 @@
+// Device-side building blocks shared by the encode and decode kernels:
+// matrix-core operand types, the 16x16x32 fp16 MFMA, lane helpers and the
+// fixed operand-layout constants. gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;           // head dimension
+constexpr int kWave = 64;
+constexpr float kCentScale = 64.0f;   // centroids enter fp16 tables as c·64·σ
+
+// Header of a quantizer's prepared buffer (written by tq_prepare).
+constexpr size_t kPrepHeaderBytes = 256;
+struct PrepHeader {
+  float sigma;       // centroid scale σ in [1, 2), see prepare_kernel
+  float sigma_err;   // max relative fp16 error of c·64·σ over the centroids
+};
+
+// D(16x16, fp32) += A(16x32, fp16) · B(32x16, fp16).
+// Lane l holds row l%16 of A and column l%16 of B, both over the K-slice of
+// lane group l/16; the result row 4*(l/16)+i, column l%16 sits in element i.
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t f2h_bits(float x) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  return static_cast<uint32_t>(f2h_bits(lo)) | (static_cast<uint32_t>(f2h_bits(hi)) << 16);
+}
+
+// fp16 split of a float: x ≈ hi + lo with both halves fp16 (≈22-bit mantissa).
+__device__ __forceinline__ void split_h(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f2h_bits(x);
+  lo = f2h_bits(x - h2f(hi));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Reduce over the four lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum4g(float v) {
+  v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+__device__ __forceinline__ float max4g(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+
+}  // namespace tq

@@ -1,0 +1,520 @@
+// TurboQuant encoder on gfx950: norm → rotation on the matrix cores →
+// Lloyd-Max nearest-centroid codes → LSB-first bit packing; the prod variant
+// adds the residual, its norm γ and the 1-bit QJL sketch sign(S·r).
+//
+// Method: "The Distortion Guarantee — How Good Is This?" ("rotate, quantize,
+// done"); "TurboQuant của Google…" (omelet.tech) sections "Trick đầu tiên:
+// xoay ngẫu nhiên trước khi nén" (Π from QR of a Gaussian, y = Π·u) and
+// "Lloyd-Max quantizer: chia bucket đúng chỗ" (store the nearest-centroid
+// index), and its QJL section ((b-1)-bit quantizer, residual, 1-bit sketch);
+// "内存厂商的噩梦来了…" (wuyi.wiki) sections 4.2-4.3.
+//
+// Precision. A code may differ from an exact-arithmetic encoder only where the
+// rotated coordinate lies within ~1e-7 of a boundary, so Π·x needs fp32-level
+// accuracy. The rotation runs on the fp16 matrix cores with Π split into two
+// fp16 parts (hi + lo ≈ 22-bit mantissa) and x converted exactly: bf16 inputs
+// fit fp16 after scaling the vector by a power of two (2^-e, max|x| = m·2^e)
+// so that every component is below 1 in magnitude; fp32 inputs are split into
+// two fp16 parts as well. Products of fp16 values are exact in the fp32
+// accumulator. The prod sketch uses S' = S·Πᵀ on the rotated residual
+// r̂ = y - c[idx] (S'·r̂ = S·r exactly), with three fp16-split passes.
+#include <hip/hip_runtime.h>
+
+#include "tq.h"
+#include "tq_device.h"
+
+namespace tq {
+
+// Prepared buffer: a 256-byte header (PrepHeader), then two fragment sets of
+// 2 parts × 8 row tiles × 4 K-steps × 64 lanes × 16 bytes.
+constexpr int kFragsPerSet = 2 * 8 * 4;               // (part, t, s)
+constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB
+constexpr size_t kPrepBytes = kPrepHeaderBytes + 2 * kSetBytes;
+constexpr float kRotScale = 16.0f;                    // |Π| <= 1 → |16Π| <= 16
+constexpr float kResScale = 64.0f;                    // residual scale for the sketch
+
+__host__ __device__ constexpr int frag_index(int part, int t, int s) { return (part * 8 + t) * 4 + s; }
+
+// Output row held by A-row i of row tile t: lane group i/4 ends up holding
+// rows 32*(i/4) + 4t + (i%4), so each lane group owns 32 consecutive outputs.
+__device__ __forceinline__ int out_row(int t, int i) { return 32 * (i >> 2) + 4 * t + (i & 3); }
+
+// ---------------------------------------------------------------------------
+// tq_prepare: fragment the rotation (and S' = S·Πᵀ) into matrix-core A operands
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__ rot,
+                                                       const float* __restrict__ proj,
+                                                       const float* __restrict__ centroids, int bm,
+                                                       uint8_t* __restrict__ prep_base) {
+  __shared__ float red[1024];
+  __shared__ int redi[1024];
+  const int tid = threadIdx.x;
+  // Centroid scale σ in [1, 2): the centroid magnitudes times 64σ are as close
+  // to fp16 values as any σ on a 2^-18 grid makes them (max relative error
+  // over the magnitudes, smallest σ on ties).
+  {
+    const int half = bm > 0 ? (1 << bm) / 2 : 0;
+    float best = INFINITY;
+    int bi = 0;
+    for (int k = tid; k < (1 << 18); k += 1024) {
+      const float sg = 1.0f + float(k) * (1.0f / (1 << 18));
+      float err = 0.f;
+      for (int m = 0; m < half; ++m) {
+        const float v = centroids[half + m] * kCentScale * sg;
+        if (v > 0.f) err = fmaxf(err, fabsf(h2f(f2h_bits(v)) - v) / v);
+      }
+      if (err < best) {
+        best = err;
+        bi = k;
+      }
+    }
+    red[tid] = best;
+    redi[tid] = bi;
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+      if (tid < w && (red[tid + w] < red[tid] || (red[tid + w] == red[tid] && redi[tid + w] < redi[tid]))) {
+        red[tid] = red[tid + w];
+        redi[tid] = redi[tid + w];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      PrepHeader* h = reinterpret_cast<PrepHeader*>(prep_base);
+      h->sigma = 1.0f + float(redi[0]) * (1.0f / (1 << 18));
+      h->sigma_err = red[0];
+    }
+    __syncthreads();
+  }
+  uint16_t* prep = reinterpret_cast<uint16_t*>(prep_base + kPrepHeaderBytes);
+  // Rotation fragments: A(t, s)[lane (i, g)][j] = 16·Π[out_row(t,i)][32s + 8g + j].
+  for (int e = tid; e < 8 * 4 * 64 * 8; e += 1024) {
+    const int j = e & 7, lane = (e >> 3) & 63, s = (e >> 9) & 3, t = e >> 11;
+    const int i = lane & 15, g = lane >> 4;
+    const float v = kRotScale * rot[out_row(t, i) * kD + 32 * s + 8 * g + j];
+    uint16_t hi, lo;
+    split_h(v, hi, lo);
+    prep[(frag_index(0, t, s) * 64 + lane) * 8 + j] = hi;
+    prep[(frag_index(1, t, s) * 64 + lane) * 8 + j] = lo;
+  }
+  if (proj == nullptr) return;
+  // S'[a][c] = Σ_k S[a][k] Π[c][k] in double; scaled by a power of two so that
+  // max|S'| lands in [8, 16).
+  auto sprime = [&](int a, int c) {
+    double acc = 0.0;
+    for (int k = 0; k < kD; ++k) acc += double(proj[a * kD + k]) * double(rot[c * kD + k]);
+    return acc;
+  };
+  float mx = 0.f;
+  for (int e = tid; e < kD * kD; e += 1024) mx = fmaxf(mx, fabsf(float(sprime(e / kD, e % kD))));
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  int ex = 0;
+  if (mx > 0.f) frexpf(mx, &ex);   // mx = m·2^ex, m in [0.5, 1)
+  const double sc = ldexp(1.0, 4 - ex);
+  uint16_t* pp = prep + kSetBytes / 2;
+  // A(t, s)[lane (i, g)][j] = S'[out_row(t,i)][32g + 8s + j] (the rotated residual
+  // columns a lane group holds itself).
+  for (int e = tid; e < 8 * 4 * 64 * 8; e += 1024) {
+    const int j = e & 7, lane = (e >> 3) & 63, s = (e >> 9) & 3, t = e >> 11;
+    const int i = lane & 15, g = lane >> 4;
+    const float v = float(sc * sprime(out_row(t, i), 32 * g + 8 * s + j));
+    uint16_t hi, lo;
+    split_h(v, hi, lo);
+    pp[(frag_index(0, t, s) * 64 + lane) * 8 + j] = hi;
+    pp[(frag_index(1, t, s) * 64 + lane) * 8 + j] = lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Encode kernel
+// ---------------------------------------------------------------------------
+struct EncodeArgs {
+  const void* x;
+  int64_t n;
+  int64_t stride;       // elements between rows
+  uint8_t* codes;
+  float* norms;
+  uint8_t* qjl;
+  float* gammas;
+  const u32x4* prep;
+  const float* centroids;
+  const float* boundaries;
+  const int64_t* slot;  // output slot of each row, or null for slot = row
+};
+
+constexpr int kEncWaves = 8;
+
+// Thresholds of an antisymmetric codebook with K = 2^BM levels, held in
+// scalars: tp[j] = boundaries[K/2-1+j] (tp[0] = 0) and the centroid
+// magnitudes cm[m] = centroids[K/2+m].
+struct Book {
+  float t1, t2, t3, t4, t5, t6, t7;
+  float c0, c1, c2, c3, c4, c5, c6, c7;
+};
+
+// Nearest-centroid code of y: idx = #{i : t_i < y}. With a = |y|:
+//   y > 0:  idx = K/2 + #{j >= 1 : tp[j] <  a}
+//   y <= 0: idx = K/2 - 1 - #{j >= 1 : tp[j] <= a}
+// and "tp <= a" is "tp < nextup(a)" on floats. Also returns the magnitude
+// index m (the centroid is +cm[m] when y > 0, -cm[m] otherwise).
+template <int BM>
+__device__ __forceinline__ uint32_t quantize(float y, const Book& bk, int& m, bool& pos) {
+  constexpr int K = 1 << BM;
+  pos = y > 0.f;
+  float a = fabsf(y);
+  a = pos ? a : __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) + 1u);
+  m = 0;
+  if constexpr (BM == 2) {
+    m = a > bk.t1;
+  } else if constexpr (BM == 3) {
+    const int b1 = a > bk.t2;
+    const float th = b1 ? bk.t3 : bk.t1;
+    m = 2 * b1 + (a > th);
+  } else if constexpr (BM == 4) {
+    const int b2 = a > bk.t4;
+    const float t1 = b2 ? bk.t6 : bk.t2;
+    const int b1 = a > t1;
+    const float thi = b1 ? bk.t7 : bk.t5;
+    const float tlo = b1 ? bk.t3 : bk.t1;
+    const float t0 = b2 ? thi : tlo;
+    m = 4 * b2 + 2 * b1 + (a > t0);
+  }
+  if constexpr (BM == 0) return 0u;
+  return pos ? uint32_t(K / 2 + m) : uint32_t(K / 2 - 1 - m);
+}
+
+template <int BM>
+__device__ __forceinline__ float centroid_mag(const Book& bk, int m) {
+  if constexpr (BM <= 1) return bk.c0;
+  float c = (m & 1) ? bk.c1 : bk.c0;
+  if constexpr (BM >= 3) {
+    const float c23 = (m & 1) ? bk.c3 : bk.c2;
+    c = (m & 2) ? c23 : c;
+  }
+  if constexpr (BM >= 4) {
+    const float c45 = (m & 1) ? bk.c5 : bk.c4;
+    const float c67 = (m & 1) ? bk.c7 : bk.c6;
+    const float chi = (m & 2) ? c67 : c45;
+    c = (m & 4) ? chi : c;
+  }
+  return c;
+}
+
+template <int BM, bool PROD, bool F32IN>
+__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
+  __shared__ u32x4 lds_rot[kFragsPerSet * 64];
+  __shared__ u32x4 lds_proj[PROD ? kFragsPerSet * 64 : 1];
+  constexpr int K = 1 << BM;
+
+  for (int i = threadIdx.x; i < kFragsPerSet * 64; i += blockDim.x) {
+    lds_rot[i] = a.prep[i];
+    if constexpr (PROD) lds_proj[i] = a.prep[kFragsPerSet * 64 + i];
+  }
+  Book bk{};
+  if constexpr (BM >= 1) {
+    const float* tb = a.boundaries + (K / 2 - 1);
+    const float* cb = a.centroids + K / 2;
+    bk.c0 = cb[0];
+    if constexpr (K / 2 > 1) { bk.t1 = tb[1]; bk.c1 = cb[1]; }
+    if constexpr (K / 2 > 2) { bk.t2 = tb[2]; bk.t3 = tb[3]; bk.c2 = cb[2]; bk.c3 = cb[3]; }
+    if constexpr (K / 2 > 4) {
+      bk.t4 = tb[4]; bk.t5 = tb[5]; bk.t6 = tb[6]; bk.t7 = tb[7];
+      bk.c4 = cb[4]; bk.c5 = cb[5]; bk.c6 = cb[6]; bk.c7 = cb[7];
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t ntiles = (a.n + 15) / 16;
+  for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles;
+       tile += int64_t(gridDim.x) * kEncWaves) {
+    const int64_t rowi = tile * 16 + n;
+    const bool valid = rowi < a.n;
+    const int64_t row = valid ? rowi : a.n - 1;
+    const int64_t vec = a.slot ? a.slot[row] : row;   // output slot
+    // The operand fragments in LDS are the same every tile; an opaque lane
+    // offset keeps the compiler from hoisting all 64 KiB of them into
+    // registers ahead of the loop.
+    int lofs = lane;
+    asm volatile("" : "+v"(lofs));
+
+    // Columns held by this lane: slot 8s + j <-> column 32s + 8g + j.
+    // The vector is scaled by 2^-e with max|x| = m·2^e (m in [0.5, 1)): the
+    // squares can then neither overflow nor vanish, and every scaled component
+    // is below 1, so bf16 values convert to fp16 exactly.
+    float xv[32];
+    if constexpr (!F32IN) {
+      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xr + 32 * s);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          xv[8 * s + 2 * k] = bf16_to_f32(w[k] & 0xffffu);
+          xv[8 * s + 2 * k + 1] = bf16_to_f32(w[k] >> 16);
+        }
+      }
+    } else {
+      const float* xr = static_cast<const float*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(xr + 32 * s);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(xr + 32 * s + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          xv[8 * s + k] = w0[k];
+          xv[8 * s + 4 + k] = w1[k];
+        }
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(xv[q]));
+    amax = max4g(amax);
+    int ex = 0;
+    if (amax > 0.f) frexpf(amax, &ex);
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      xv[q] = (amax > 0.f) ? ldexpf(xv[q], -ex) : 0.f;
+      ss = fmaf(xv[q], xv[q], ss);
+    }
+    ss = sum4g(ss);
+    const float rs = sqrtf(ss);                 // ‖x‖·2^-e
+    const float nrm = ldexpf(rs, ex);
+    u32x4 bx[4], bxl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (!F32IN) {
+          bx[s][k] = pack_h2(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+        } else {
+          uint16_t h0, l0, h1, l1;
+          split_h(xv[8 * s + 2 * k], h0, l0);
+          split_h(xv[8 * s + 2 * k + 1], h1, l1);
+          bx[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
+          bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
+        }
+      }
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const u32x4 ah = lds_rot[frag_index(0, t, s) * 64 + lofs];
+        const u32x4 al = lds_rot[frag_index(1, t, s) * 64 + lofs];
+        acc[t] = mfma(ah, bx[s], acc[t]);
+        acc[t] = mfma(al, bx[s], acc[t]);
+        if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
+      }
+    }
+
+    // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j.
+    const float up = (rs > 0.f) ? 1.0f / (kRotScale * rs) : 0.f;
+    uint32_t w[BM > 0 ? BM : 1];
+#pragma unroll
+    for (int k = 0; k < (BM > 0 ? BM : 1); ++k) w[k] = 0u;
+    u32x4 brh[4], brl[4];
+    float r2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float res[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = acc[t][j] * up;
+        int m;
+        bool pos;
+        const uint32_t code = quantize<BM>(y, bk, m, pos);
+        if constexpr (BM > 0) {
+          const int q = 4 * t + j;
+          const int bit = q * BM, wi = bit >> 5, off = bit & 31;
+          w[wi] |= code << off;
+          if (off + BM > 32) w[wi + 1] |= code >> (32 - off);
+        }
+        if constexpr (PROD) {
+          float c = 0.f;
+          if constexpr (BM >= 1) {
+            c = centroid_mag<BM>(bk, m);
+            c = pos ? c : -c;
+          }
+          res[j] = y - c;
+          r2 = fmaf(res[j], res[j], r2);
+        }
+      }
+      if constexpr (PROD) {
+        // q = 4t + j  ->  K-step s = t/2, dword 2(t%2) + j/2, half j%2.
+        uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
+        split_h(res[0] * kResScale, h0, l0);
+        split_h(res[1] * kResScale, h1, l1);
+        split_h(res[2] * kResScale, h2, l2);
+        split_h(res[3] * kResScale, h3, l3);
+        const int s = t >> 1, k0 = 2 * (t & 1);
+        brh[s][k0] = uint32_t(h0) | (uint32_t(h1) << 16);
+        brh[s][k0 + 1] = uint32_t(h2) | (uint32_t(h3) << 16);
+        brl[s][k0] = uint32_t(l0) | (uint32_t(l1) << 16);
+        brl[s][k0 + 1] = uint32_t(l2) | (uint32_t(l3) << 16);
+      }
+    }
+
+    if constexpr (BM > 0) {
+      if (valid) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + vec * (16 * BM) + 4 * BM * g);
+        if constexpr (BM == 4) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        } else if constexpr (BM == 2) {
+          *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+        } else {
+#pragma unroll
+          for (int k = 0; k < BM; ++k) dst[k] = w[k];
+        }
+      }
+    }
+    if (valid && g == 0) a.norms[vec] = nrm;
+
+    if constexpr (PROD) {
+      r2 = sum4g(r2);
+      f32x4 z[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) z[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const u32x4 sh = lds_proj[frag_index(0, t, s) * 64 + lofs];
+          const u32x4 sl = lds_proj[frag_index(1, t, s) * 64 + lofs];
+          z[t] = mfma(sh, brh[s], z[t]);
+          z[t] = mfma(sl, brh[s], z[t]);
+          z[t] = mfma(sh, brl[s], z[t]);
+        }
+      }
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bits |= uint32_t(z[t][j] >= 0.f) << (4 * t + j);
+      }
+      if (valid) {
+        *reinterpret_cast<uint32_t*>(a.qjl + vec * 16 + 4 * g) = bits;
+        if (g == 0) a.gammas[vec] = sqrtf(r2);
+      }
+    }
+  }
+}
+
+template <int BM, bool PROD>
+hipError_t launch_encode_t(const EncodeArgs& a, bool f32in, int grid, hipStream_t st) {
+  if (f32in)
+    hipLaunchKernelGGL((encode_kernel<BM, PROD, true>), dim3(grid), dim3(kEncWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((encode_kernel<BM, PROD, false>), dim3(grid), dim3(kEncWaves * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+namespace {
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_quantizer(const tq_quantizer* q) {
+  if (q == nullptr) return TQ_ERR_INVALID_ARG;
+  if (q->d != TQ_HEAD_DIM) return TQ_ERR_UNSUPPORTED;
+  if (q->variant != TQ_MSE && q->variant != TQ_PROD) return TQ_ERR_UNSUPPORTED;
+  if (q->bits < 1 || q->bits > 4) return TQ_ERR_UNSUPPORTED;
+  const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
+  if (q->rot == nullptr || q->centroids == nullptr || q->prep == nullptr) return TQ_ERR_INVALID_ARG;
+  if (bm > 0 && q->boundaries == nullptr) return TQ_ERR_INVALID_ARG;
+  if (q->variant == TQ_PROD && q->proj == nullptr) return TQ_ERR_INVALID_ARG;
+  if (!aligned(q->prep, 256)) return TQ_ERR_WORKSPACE;
+  return TQ_OK;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+}  // namespace
+
+extern "C" size_t tq_prep_bytes(void) { return kPrepBytes; }
+
+extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
+  const int st = check_quantizer(q);
+  if (st != TQ_OK) return st;
+  const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
+  hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), q->rot,
+                     q->variant == TQ_PROD ? q->proj : nullptr, q->centroids, bm,
+                     static_cast<uint8_t*>(q->prep));
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+// Exported for the decoder, which checks quantizers the same way.
+int tq_check_quantizer(const tq_quantizer* q) { return check_quantizer(q); }
+int tq_device_cus() { return device_cus(); }
+
+extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int64_t n,
+                         int64_t x_row_stride, const tq_packed* out, const int64_t* out_slot,
+                         void* stream) {
+  int st = check_quantizer(q);
+  if (st != TQ_OK) return st;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_UNSUPPORTED;
+  if (n < 0 || out == nullptr) return TQ_ERR_INVALID_ARG;
+  if (n == 0) return TQ_OK;
+  if (x == nullptr || x_row_stride < TQ_HEAD_DIM || (x_row_stride % 8) != 0) return TQ_ERR_INVALID_ARG;
+  const bool prod = q->variant == TQ_PROD;
+  const int bm = prod ? q->bits - 1 : q->bits;
+  if (out->norms == nullptr || (bm > 0 && out->codes == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (prod && (out->qjl == nullptr || out->gammas == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || (bm > 0 && !aligned(out->codes, 16)) || !aligned(out->norms, 4) ||
+      (prod && (!aligned(out->qjl, 16) || !aligned(out->gammas, 4))))
+    return TQ_ERR_INVALID_ARG;
+
+  EncodeArgs a;
+  a.x = x;
+  a.n = n;
+  a.stride = x_row_stride;
+  a.codes = out->codes;
+  a.norms = out->norms;
+  a.qjl = out->qjl;
+  a.gammas = out->gammas;
+  a.prep = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(q->prep) + kPrepHeaderBytes);
+  a.centroids = q->centroids;
+  a.boundaries = q->boundaries;
+  a.slot = out_slot;
+  const int64_t tiles = (n + 15) / 16;
+  const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
+  const int cap = device_cus() * (prod ? 1 : 2);
+  const int grid = static_cast<int>(want < cap ? want : cap);
+  const bool f32 = x_dtype == TQ_F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!prod) {
+    switch (bm) {
+      case 1: e = launch_encode_t<1, false>(a, f32, grid, s); break;
+      case 2: e = launch_encode_t<2, false>(a, f32, grid, s); break;
+      case 3: e = launch_encode_t<3, false>(a, f32, grid, s); break;
+      default: e = launch_encode_t<4, false>(a, f32, grid, s); break;
+    }
+  } else {
+    switch (bm) {
+      case 0: e = launch_encode_t<0, true>(a, f32, grid, s); break;
+      case 1: e = launch_encode_t<1, true>(a, f32, grid, s); break;
+      case 2: e = launch_encode_t<2, true>(a, f32, grid, s); break;
+      default: e = launch_encode_t<3, true>(a, f32, grid, s); break;
+    }
+  }
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}

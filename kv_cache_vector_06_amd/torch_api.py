@@ -1,0 +1,110 @@
+"""Torch-facing helpers over the C ABI: device buffers from PyTorch, the
+current HIP stream, and argument marshalling. No arithmetic of the method
+happens here; it all runs in libtq.so."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+class Quantizer:
+    """One TurboQuant quantizer (rotation, optional QJL projection, codebook,
+    prepared operands), all resident on `device`."""
+
+    def __init__(self, rot: np.ndarray, bits: int, variant: str = "mse",
+                 proj: np.ndarray | None = None, device: str = "cuda"):
+        d = rot.shape[0]
+        self.d, self.bits = d, bits
+        self.variant = L.TQ_PROD if variant == "prod" else L.TQ_MSE
+        self.bm = bits - 1 if self.variant == L.TQ_PROD else bits
+        c, t, self.mse_unit = L.tq_codebook(d, self.bm)
+        self.centroids64, self.boundaries64 = c, t
+        dev = torch.device(device)
+        self.rot = torch.as_tensor(np.ascontiguousarray(rot, np.float32)).to(dev)
+        self.proj = None
+        if self.variant == L.TQ_PROD:
+            if proj is None:
+                raise ValueError("prod quantizer needs a projection")
+            self.proj = torch.as_tensor(np.ascontiguousarray(proj, np.float32)).to(dev)
+        self.centroids = torch.as_tensor(c.astype(np.float32)).to(dev)
+        self.boundaries = torch.as_tensor(np.concatenate([t, [0.0]]).astype(np.float32)).to(dev)
+        self.prep = torch.empty(L.tq_prep_bytes(), dtype=torch.uint8, device=dev)
+        self.c = L.tq_quantizer(d, bits, self.variant, _ptr(self.rot), _ptr(self.proj),
+                                _ptr(self.centroids), _ptr(self.boundaries), _ptr(self.prep))
+        L.tq_prepare(self.c, _stream())
+
+    @property
+    def code_bytes(self) -> int:
+        return self.d * self.bm // 8
+
+
+class Packed:
+    """Packed vectors for n slots (see tq_packed in include/tq.h)."""
+
+    def __init__(self, q: Quantizer, n: int, device: str = "cuda"):
+        dev = torch.device(device)
+        self.n = n
+        self.codes = torch.zeros((n, q.code_bytes), dtype=torch.uint8, device=dev)
+        self.norms = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.qjl = self.gammas = None
+        if q.variant == L.TQ_PROD:
+            self.qjl = torch.zeros((n, q.d // 8), dtype=torch.uint8, device=dev)
+            self.gammas = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.c = L.tq_packed(_ptr(self.codes) if q.code_bytes else None, _ptr(self.norms),
+                             _ptr(self.qjl), _ptr(self.gammas))
+
+
+def encode(q: Quantizer, x: torch.Tensor, out: Packed | None = None,
+           slots: torch.Tensor | None = None) -> Packed:
+    """Encode rows of x ([n, d], float32 or bfloat16, on the GPU); with `slots`
+    (int64[n] on the GPU) row i goes to slot slots[i] of `out`."""
+    if x.dim() != 2 or x.shape[1] != q.d or x.stride(1) != 1:
+        raise ValueError("x must be [n, d] with unit column stride")
+    dt = {torch.float32: L.TQ_F32, torch.bfloat16: L.TQ_BF16}[x.dtype]
+    n = x.shape[0]
+    if slots is not None and (slots.dtype != torch.int64 or slots.numel() != n or out is None):
+        raise ValueError("slots must be int64[n] and come with an output buffer")
+    out = out if out is not None else Packed(q, n, x.device)
+    L.tq_encode(q.c, x.data_ptr(), dt, n, x.stride(0), out.c, _ptr(slots), _stream())
+    return out
+
+
+class Decoder:
+    """Reusable decode-attention call for one cache shape (owns the workspace)."""
+
+    def __init__(self, B: int, Hq: int, Hkv: int, max_ctx: int, device: str = "cuda"):
+        self.B, self.Hq, self.Hkv, self.max_ctx = B, Hq, Hkv, max_ctx
+        self.ws_bytes = L.tq_attn_decode_workspace(B, Hq, Hkv, max_ctx)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid decode shape")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=torch.device(device))
+
+    def __call__(self, kq: Quantizer, vq: Quantizer, query: torch.Tensor, kc: Packed, vc: Packed,
+                 ctx_lens: torch.Tensor | None = None, scale: float | None = None,
+                 out: torch.Tensor | None = None, phase: int = 0) -> torch.Tensor:
+        B, Hq, d = query.shape
+        if (B, Hq) != (self.B, self.Hq) or query.dtype != torch.float32 or not query.is_contiguous():
+            raise ValueError("query must be contiguous float32 [B, Hq, d] of the decoder's shape")
+        if ctx_lens is not None and (ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B):
+            raise ValueError("ctx_lens must be int32[B]")
+        out = out if out is not None else torch.empty_like(query)
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        args = (kq.c, vq.c, query.data_ptr(), B, Hq, self.Hkv, _ptr(ctx_lens), self.max_ctx,
+                kc.c, vc.c, scale, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+        if phase == 0:
+            L.tq_attn_decode(*args)
+        else:
+            L.tq_attn_decode_phase(phase, *args)
+        return out

@@ -2,9 +2,9 @@
 
 This module only draws random numbers and lays them out; it holds none of the
 quantizer's arithmetic (no norms, no codebook, no quantization, no attention).
-Every generator is `numpy.random.default_rng(seed)` (PCG64) in float64, then
-rounded to the stated storage dtype, so the GPU and the oracle consume the
-same bytes.
+Every generator is `numpy.random.default_rng(seed)` (PCG64); data are drawn
+as float32 standard normals (the constant matrices in float64) and rounded to
+the stated storage dtype, so the GPU and the oracle consume the same bytes.
 
 The random draws the method makes are inputs here, as the pages treat them:
   * the rotation is the orthogonal factor of a QR factorisation of an iid
@@ -35,12 +35,16 @@ def rng(seed: int) -> np.random.Generator:
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float64/float32 values to bfloat16 (round to nearest even).
+    """Round finite float64/float32 values to bfloat16 (round to nearest even).
 
     Returns the rounded values as float32 (exactly representable)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (u.astype(np.uint32) << 16).view(np.float32)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    u += r          # finite inputs cannot overflow 32 bits
+    u &= 0xFFFF0000
+    return u.view(np.float32)
 
 
 def bf16_bits(x32: np.ndarray) -> np.ndarray:
@@ -63,8 +67,8 @@ def projection(d: int, seed: int) -> np.ndarray:
 
 def gaussian(shape, seed: int, dtype: str = "fp32") -> np.ndarray:
     """iid N(0,1) values rounded to `dtype` ("fp32" or "bf16"), returned as float32."""
-    x = rng(seed).standard_normal(shape)
-    return round_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+    x = rng(seed).standard_normal(shape, dtype=np.float32)
+    return round_bf16(x) if dtype == "bf16" else x
 
 
 def outlier_kv(B: int, H: int, T: int, d: int, seed: int, n_outliers: int = 4,
@@ -74,21 +78,21 @@ def outlier_kv(B: int, H: int, T: int, d: int, seed: int, n_outliers: int = 4,
     The same channels are scaled for every token of a head (a per-channel
     outlier pattern); channels are drawn without replacement per head."""
     g = rng(seed)
-    x = g.standard_normal((B, H, T, d))
+    x = g.standard_normal((B, H, T, d), dtype=np.float32)
     for h in range(H):
         ch = g.choice(d, size=n_outliers, replace=False)
-        x[:, h, :, ch] *= scale
-    return round_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+        x[:, h, :, ch] *= np.float32(scale)
+    return round_bf16(x) if dtype == "bf16" else x
 
 
 def lognormal_kv(B: int, H: int, T: int, d: int, seed: int, sigma: float = 0.5,
                  dtype: str = "bf16") -> np.ndarray:
     """[B,H,T,d] N(0,I) directions times per-(b,h,t) LogNormal(0, sigma) scales."""
     g = rng(seed)
-    x = g.standard_normal((B, H, T, d))
-    s = g.lognormal(0.0, sigma, size=(B, H, T, 1))
-    x = x * s
-    return round_bf16(x) if dtype == "bf16" else x.astype(np.float32)
+    x = g.standard_normal((B, H, T, d), dtype=np.float32)
+    s = g.lognormal(0.0, sigma, size=(B, H, T, 1)).astype(np.float32)
+    x *= s
+    return round_bf16(x) if dtype == "bf16" else x
 
 
 @dataclasses.dataclass(frozen=True)

@@ -1,0 +1,137 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and compare it with the oracle under the parity rules:
+  * packing is bit-exact for identical codes;
+  * at most 1e-5 of coordinates may get a different code, and only where the
+    oracle's float64 rotated value lies within 1e-6 of a boundary;
+  * sketch bits (on vectors whose codes all match) may differ only where
+    |(S r)_j| < 1e-6, at most 1e-5 of bits; γ within 1e-5 relative there;
+  * norms within 1e-6 relative;
+  * attention outputs within 1e-3 relative L2 per (batch, head)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import synth
+from kv_cache_vector_06_amd import _lib as L
+from kv_cache_vector_06_amd import torch_api as T
+from oracle import (decode_attention, dequant_mse, dequant_prod, encode_mse, encode_prod,
+                    lloyd_max, pack_codes, unpack_codes, unpack_signs)
+
+D = 128
+DEV = "cuda:0"
+_BOOKS = {}
+
+
+def book(bits):
+    if bits not in _BOOKS:
+        _BOOKS[bits] = lloyd_max(D, bits)
+    return _BOOKS[bits]
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_gpu_x(x32: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)          # exact: the values are bf16-representable
+    return t.to(DEV)
+
+
+def oracle_encode(X: np.ndarray, rot, proj, bits: int, variant: str, chunk: int = 8192):
+    """Oracle encode in chunks (bounded memory); returns dict of arrays."""
+    outs = []
+    for i in range(0, X.shape[0], chunk):
+        Xi = X[i:i + chunk].astype(np.float64)
+        if variant == "prod":
+            outs.append(encode_prod(Xi, rot, proj, book(bits - 1)[0], bits))
+        else:
+            outs.append(encode_mse(Xi, rot, book(bits)[0], bits))
+    return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
+
+
+def oracle_dequant(enc, rot, proj, bits, variant):
+    if variant == "prod":
+        return dequant_prod(enc["codes"], enc["norms"], enc["qjl"], enc["gammas"], rot, proj,
+                            book(bits - 1)[0], bits)
+    return dequant_mse(enc["codes"], enc["norms"], rot, book(bits)[0], bits)
+
+
+def gpu_packed_arrays(p: T.Packed, q: T.Quantizer):
+    torch.cuda.synchronize()
+    out = dict(norms=p.norms.cpu().numpy())
+    out["codes"] = p.codes.cpu().numpy() if q.code_bytes else np.zeros((p.n, 0), np.uint8)
+    if p.qjl is not None:
+        out["qjl"] = p.qjl.cpu().numpy()
+        out["gammas"] = p.gammas.cpu().numpy()
+    return out
+
+
+def check_encode(gpu: dict, ref: dict, bits: int, variant: str, rows=None):
+    """Assert the encode parity rules; returns a dict of measured rates."""
+    bm = bits - 1 if variant == "prod" else bits
+    sel = slice(None) if rows is None else rows
+    gn, rn = gpu["norms"][sel].astype(np.float64), ref["norms"]
+    nz = rn > 0
+    assert np.all(gn[~nz] == 0)
+    rel = np.abs(gn[nz] - rn[nz]) / rn[nz]
+    assert rel.max(initial=0) <= 1e-6, rel.max()
+    stats = dict(norm_rel=float(rel.max(initial=0)))
+    n = rn.shape[0]
+    vec_ok = np.ones(n, bool)
+    if bm > 0:
+        gc = gpu["codes"][sel]
+        gidx = unpack_codes(gc, D, bm)
+        assert np.array_equal(pack_codes(gidx, bm), gc), "packing is not the LSB-first stream of the codes"
+        mism = gidx != ref["idx"]
+        t = book(bm)[1]
+        dist = np.min(np.abs(ref["y"][..., None] - t), axis=-1)
+        assert np.all(dist[mism] < 1e-6), "code mismatch away from a boundary"
+        assert mism.sum() <= 1e-5 * mism.size, (mism.sum(), mism.size)
+        vec_ok = ~mism.any(axis=1)
+        stats["code_mismatch"] = int(mism.sum())
+    if variant == "prod":
+        gs = unpack_signs(gpu["qjl"][sel], D)
+        rs = unpack_signs(ref["qjl"], D)
+        bad = (gs != rs) & vec_ok[:, None]
+        assert np.all(np.abs(ref["z"][bad]) < 1e-6), "sketch bit flipped away from zero"
+        assert bad.sum() <= 1e-5 * bad.size, (bad.sum(), bad.size)
+        gg = gpu["gammas"][sel].astype(np.float64)[vec_ok]
+        rg = ref["gammas"][vec_ok]
+        ok = rg > 0
+        grel = np.abs(gg[ok] - rg[ok]) / rg[ok]
+        assert grel.max(initial=0) <= 1e-5, grel.max()
+        assert np.all(gg[~ok] <= 1e-6)
+        stats["sketch_mismatch"] = int(bad.sum())
+        stats["gamma_rel"] = float(grel.max(initial=0))
+    return stats
+
+
+def packed_from_oracle(enc: dict, q: T.Quantizer) -> T.Packed:
+    """Upload an oracle-produced packed cache (norms/γ rounded to float32)."""
+    n = enc["norms"].shape[0]
+    p = T.Packed(q, n, DEV)
+    if q.code_bytes:
+        p.codes.copy_(torch.from_numpy(np.ascontiguousarray(enc["codes"])))
+    p.norms.copy_(torch.from_numpy(enc["norms"].astype(np.float32)))
+    if p.qjl is not None:
+        p.qjl.copy_(torch.from_numpy(np.ascontiguousarray(enc["qjl"])))
+        p.gammas.copy_(torch.from_numpy(enc["gammas"].astype(np.float32)))
+    return p
+
+
+def rel_l2_per_head(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    num = np.linalg.norm(out - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return num / np.maximum(den, 1e-300)
+
+
+def quantizers(cfg):
+    Rk, Rv, S = synth.constants(cfg.d)
+    kq = T.Quantizer(Rk, cfg.k_bits, cfg.k_variant, S if cfg.k_variant == "prod" else None, DEV)
+    vq = T.Quantizer(Rv, cfg.v_bits, "mse", None, DEV)
+    return kq, vq, Rk, Rv, S

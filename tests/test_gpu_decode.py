@@ -1,0 +1,145 @@
+"""GPU parity of tq_attn_decode against the oracle (through the C ABI):
+(i) both sides decode the oracle-produced cache; (ii) GPU encode + GPU decode
+against oracle encode + oracle attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from kv_cache_vector_06_amd import torch_api as T
+from gpu_util import (DEV, book, check_encode, gpu_packed_arrays, oracle_dequant, oracle_encode,
+                      packed_from_oracle, quantizers, rel_l2_per_head, say, to_gpu_x)
+from oracle import decode_attention
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _flat(x):
+    return x.reshape(-1, x.shape[-1])
+
+
+def _near_ties(enc, bits, variant):
+    """Rows whose oracle encode has a rotated coordinate within 1e-6 of a
+    boundary or a sketch value within 1e-6 of zero: there a different but
+    equally valid code or bit is allowed, and with few tokens one such flip
+    moves the attention output by up to ~1e-2."""
+    bm = bits - 1 if variant == "prod" else bits
+    bad = np.zeros(enc["norms"].shape[0], bool)
+    if bm > 0:
+        t = book(bm)[1]
+        bad |= (np.min(np.abs(enc["y"][..., None] - t), axis=-1) < 1e-6).any(axis=1)
+    if variant == "prod":
+        bad |= (np.abs(enc["z"]) < 1e-6).any(axis=1)
+    return np.nonzero(bad)[0]
+
+
+def encode_away_from_ties(X, rot, proj, bits, variant, seed, dtype):
+    """Oracle encode of X; rows near a tie are redrawn (in place) until none
+    is. Uses the oracle only; the HIP path then encodes the same rows."""
+    enc = oracle_encode(X, rot, proj, bits, variant)
+    g = np.random.default_rng(seed)
+    for _ in range(20):
+        rows = _near_ties(enc, bits, variant)
+        if rows.size == 0:
+            return enc
+        new = X[rows] * (1 + 0.01 * g.standard_normal(X[rows].shape)).astype(np.float32)
+        X[rows] = synth.round_bf16(new) if dtype == "bf16" else new
+        sub = oracle_encode(X[rows], rot, proj, bits, variant)
+        for k in enc:
+            enc[k][rows] = sub[k]
+    raise AssertionError("could not move rows away from ties")
+
+
+def run_case(cfg, T_ctx, B, lens=None, end_to_end=True):
+    say("case", cfg.name, "T", T_ctx, "B", B, "lens", lens)
+    kq, vq, Rk, Rv, S = quantizers(cfg)
+    K, V = synth.make_kv(cfg, T=T_ctx, B=B)
+    q = synth.make_query(cfg, B=B)
+    K, V = np.ascontiguousarray(K), np.ascontiguousarray(V)
+    ek = encode_away_from_ties(_flat(K), Rk, S, cfg.k_bits, cfg.k_variant, cfg.seed_base + 7, cfg.dtype)
+    ev = encode_away_from_ties(_flat(V), Rv, None, cfg.v_bits, "mse", cfg.seed_base + 8, cfg.dtype)
+    shape = (B, cfg.Hkv, T_ctx, 128)
+    Kt = oracle_dequant(ek, Rk, S, cfg.k_bits, cfg.k_variant).reshape(shape)
+    Vt = oracle_dequant(ev, Rv, None, cfg.v_bits, "mse").reshape(shape)
+    live = [(b, h) for b in range(B) for h in range(cfg.Hq) if lens is None or lens[b] > 0]
+    ref = decode_attention(q, Kt, Vt, 1 / math.sqrt(128), ctx_lens=lens, heads=live)
+    dec = T.Decoder(B, cfg.Hq, cfg.Hkv, T_ctx, DEV)
+    qg = torch.from_numpy(q).to(DEV)
+    lg = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    # (i) oracle cache
+    out = dec(kq, vq, qg, packed_from_oracle(ek, kq), packed_from_oracle(ev, vq), lg).cpu().numpy()
+    empty = np.zeros((B,), bool) if lens is None else (np.array(lens) == 0)
+    assert np.all(out[empty] == 0)
+    r = rel_l2_per_head(out[~empty], ref[~empty])
+    say("  oracle-cache rel L2 max", r.max())
+    assert r.max() <= TOL
+    if end_to_end:
+        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
+        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
+        # Away from ties the encodes agree exactly (codes, sketch bits).
+        ks = check_encode(gpu_packed_arrays(kp, kq), ek, cfg.k_bits, cfg.k_variant)
+        vs = check_encode(gpu_packed_arrays(vp, vq), ev, cfg.v_bits, "mse")
+        assert ks.get("code_mismatch", 0) == 0 and ks.get("sketch_mismatch", 0) == 0
+        assert vs.get("code_mismatch", 0) == 0
+        out2 = dec(kq, vq, qg, kp, vp, lg).cpu().numpy()
+        r2 = rel_l2_per_head(out2[~empty], ref[~empty])
+        say("  end-to-end rel L2 max", r2.max())
+        assert r2.max() <= TOL
+    return r.max()
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_decode_configs_small(cfg_id):
+    cfg = synth.CONFIGS[cfg_id]
+    B = min(cfg.B, 2)
+    run_case(cfg, 1000 + 7, B)                       # several 32-token blocks, ragged tail
+
+
+@pytest.mark.parametrize("cfg_id", [3, 5])
+def test_decode_ragged_lengths(cfg_id):
+    cfg = synth.CONFIGS[cfg_id]
+    run_case(cfg, 2500, 4, lens=[2500, 1, 0, 777])
+
+
+def test_decode_more_heads_than_a_group():
+    # 16 query heads per KV head: two head groups share the KV head.
+    base = synth.CONFIGS[5]
+    cfg = synth.DecodeConfig("gqa16", 1, 2, 32, 600, 128, "prod", 3, 2, "gaussian", "bf16", 70)
+    run_case(cfg, 600, 1)
+
+
+def test_decode_odd_group_and_mse1():
+    cfg = synth.DecodeConfig("g3_b1", 2, 2, 6, 300, 128, "mse", 1, 1, "lognormal", "bf16", 80)
+    run_case(cfg, 300, 2)
+    cfg = synth.DecodeConfig("prod1", 1, 2, 4, 300, 128, "prod", 1, 3, "gaussian", "fp32", 81)
+    run_case(cfg, 300, 1)
+
+
+def test_decode_full_size_sampled():
+    # 128K context at the benchmark's shape (prod-3 keys, mse-3 values, GQA 4),
+    # GPU encode + decode; the oracle evaluates two KV heads' query heads.
+    cfg = synth.CONFIGS[3]
+    kq, vq, Rk, Rv, S = quantizers(cfg)
+    say("generating", cfg.name)
+    K, V = synth.make_kv(cfg)
+    q = synth.make_query(cfg)
+    encs = {}
+    for kvh in (0, 5):
+        encs[kvh] = (encode_away_from_ties(K[0, kvh], Rk, S, cfg.k_bits, cfg.k_variant, 300 + kvh, cfg.dtype),
+                     encode_away_from_ties(V[0, kvh], Rv, None, cfg.v_bits, "mse", 310 + kvh, cfg.dtype))
+    kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
+    vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
+    dec = T.Decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T, DEV)
+    out = dec(kq, vq, torch.from_numpy(q).to(DEV), kp, vp).cpu().numpy()
+    for kvh in (0, 5):
+        ek, ev = encs[kvh]
+        Kt = oracle_dequant(ek, Rk, S, cfg.k_bits, cfg.k_variant)[None, None]
+        Vt = oracle_dequant(ev, Rv, None, cfg.v_bits, "mse")[None, None]
+        hs = list(range(kvh * cfg.G, (kvh + 1) * cfg.G))
+        ref = decode_attention(q[:, hs], Kt, Vt, 1 / math.sqrt(128))
+        r = rel_l2_per_head(out[0, hs], ref[0])
+        say("  full-size kv head", kvh, "rel L2", r.max())
+        assert r.max() <= TOL

@@ -1,0 +1,115 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every entry point include/tq.h declares, its host codebook agrees with the
+oracle, and invalid arguments are rejected before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_06_amd._lib as L
+from oracle import lloyd_max
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "tq.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = _declared()
+    assert set(names) == set(L.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("d", [16, 64, 128, 256])
+def test_codebook_matches_oracle(d):
+    for b in range(0, 5):
+        c, t, mse = L.tq_codebook(d, b)
+        co, to, mo = lloyd_max(d, b)
+        np.testing.assert_allclose(c, co, atol=1e-11 / np.sqrt(d))
+        np.testing.assert_allclose(t, to, atol=1e-11 / np.sqrt(d))
+        assert abs(mse - mo) < 1e-11
+        np.testing.assert_array_equal(c[::-1], -c)       # exact antisymmetry
+        if b:
+            assert t[(1 << b) // 2 - 1] == 0.0
+
+
+def test_codebook_errors():
+    lib = L.load()
+    c = np.zeros(256)
+    t = np.zeros(256)
+    assert lib.tq_codebook(128, 3, None, t.ctypes.data, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_codebook(1, 3, c.ctypes.data, t.ctypes.data, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_codebook(128, 9, c.ctypes.data, t.ctypes.data, None) == L.TQ_ERR_UNSUPPORTED
+    assert lib.tq_codebook(128, 3, c.ctypes.data, None, None) == L.TQ_ERR_INVALID_ARG
+    assert L.tq_status_string(L.TQ_ERR_WORKSPACE).startswith("workspace")
+
+
+def test_workspace_sizes():
+    assert L.tq_attn_decode_workspace(1, 32, 8, 131072) > 0
+    assert L.tq_attn_decode_workspace(0, 32, 8, 100) == 0
+    assert L.tq_attn_decode_workspace(1, 30, 8, 100) == 0
+    assert L.tq_attn_decode_workspace(1, 32, 8, 0) == 0
+    # Monotone in context length and batch.
+    assert L.tq_attn_decode_workspace(4, 64, 8, 131072) >= L.tq_attn_decode_workspace(1, 64, 8, 131072)
+
+
+def _fake_quantizer(d=128, bits=3, variant=L.TQ_MSE):
+    # Non-null, aligned fake device pointers: argument checks never dereference them.
+    p = 1 << 20
+    return L.tq_quantizer(d, bits, variant, p, p if variant == L.TQ_PROD else None, p, p, p)
+
+
+def test_argument_errors_are_synchronous():
+    lib = L.load()
+    q = _fake_quantizer()
+    pk = L.tq_packed(1 << 20, 1 << 20, None, None)
+    byref = ctypes.byref
+    # encode
+    assert lib.tq_encode(None, 1 << 20, L.TQ_BF16, 10, 128, byref(pk), None, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_encode(byref(_fake_quantizer(d=64)), 1 << 20, L.TQ_BF16, 10, 128, byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
+    assert lib.tq_encode(byref(_fake_quantizer(bits=5)), 1 << 20, L.TQ_BF16, 10, 128, byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
+    assert lib.tq_encode(byref(q), 1 << 20, 7, 10, 128, byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
+    assert lib.tq_encode(byref(q), 1 << 20, L.TQ_BF16, -1, 128, byref(pk), None, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_encode(byref(q), 1 << 20, L.TQ_BF16, 10, 100, byref(pk), None, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_encode(byref(q), None, L.TQ_BF16, 10, 128, byref(pk), None, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_encode(byref(q), (1 << 20) + 4, L.TQ_BF16, 10, 128, byref(pk), None, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_encode(byref(q), 1 << 20, L.TQ_BF16, 0, 128, byref(pk), None, None) == L.TQ_OK   # no-op
+    prod = _fake_quantizer(bits=3, variant=L.TQ_PROD)
+    assert lib.tq_encode(byref(prod), 1 << 20, L.TQ_BF16, 10, 128, byref(pk), None, None) == L.TQ_ERR_INVALID_ARG
+    unaligned_prep = _fake_quantizer()
+    unaligned_prep.prep = (1 << 20) + 16
+    assert lib.tq_prepare(byref(unaligned_prep), None) == L.TQ_ERR_WORKSPACE
+    # decode
+    ws = L.tq_attn_decode_workspace(1, 32, 8, 1000)
+    args = lambda **kw: dict(dict(kq=byref(q), vq=byref(q), query=1 << 20, B=1, Hq=32, Hkv=8, lens=None,
+                                  T=1000, kc=byref(pk), vc=byref(pk), scale=0.1, out=1 << 20,
+                                  ws=1 << 20, wsb=ws), **kw)
+    call = lambda a: lib.tq_attn_decode(a["kq"], a["vq"], a["query"], a["B"], a["Hq"], a["Hkv"], a["lens"],
+                                        a["T"], a["kc"], a["vc"], a["scale"], a["out"], a["ws"], a["wsb"], None)
+    assert call(args(Hq=30)) == L.TQ_ERR_INVALID_ARG
+    assert call(args(B=0)) == L.TQ_ERR_INVALID_ARG
+    assert call(args(T=0)) == L.TQ_ERR_INVALID_ARG
+    assert call(args(query=None)) == L.TQ_ERR_INVALID_ARG
+    assert call(args(wsb=ws - 1)) == L.TQ_ERR_WORKSPACE
+    assert call(args(ws=(1 << 20) + 128)) == L.TQ_ERR_WORKSPACE
+    assert call(args(vq=byref(prod))) == L.TQ_ERR_UNSUPPORTED
+    assert call(args(kq=byref(prod))) == L.TQ_ERR_INVALID_ARG       # packed keys lack the sketch arrays
+    a = args(Hq=30)
+    for ph in (1, 2, 3):
+        assert lib.tq_attn_decode_phase(ph, a["kq"], a["vq"], a["query"], a["B"], a["Hq"], a["Hkv"], a["lens"],
+                                        a["T"], a["kc"], a["vc"], a["scale"], a["out"], a["ws"], a["wsb"],
+                                        None) == L.TQ_ERR_INVALID_ARG
+    a = args()
+    for ph in (0, 4):
+        assert lib.tq_attn_decode_phase(ph, a["kq"], a["vq"], a["query"], a["B"], a["Hq"], a["Hkv"], a["lens"],
+                                        a["T"], a["kc"], a["vc"], a["scale"], a["out"], a["ws"], a["wsb"],
+                                        None) == L.TQ_ERR_INVALID_ARG
