@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-encode-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 512 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this hot path runs on one GPU only (no multi-GPU path is built); "
@@ -165,6 +167,13 @@ def main():
             ev1[i].record()
         dec(kq, vq, q, kc, vc, out=out, phase=3)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                # reads 512 MiB, writes 512 MiB
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

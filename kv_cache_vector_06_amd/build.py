@@ -13,7 +13,10 @@ LIB = os.path.join(HERE, "libtq.so")
 SOURCES = ["tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled on purpose for every device pass.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-core accumulators are kept in ordinary VGPRs (no AGPR copies around
+# the occasional rescale of the attention accumulator).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

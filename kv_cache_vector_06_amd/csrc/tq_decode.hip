@@ -46,8 +46,10 @@ constexpr int kDecWaves = 4;
 constexpr int kBlockTok = 32;            // tokens per wavefront step
 constexpr int kMaxHeads = 8;             // query heads per unit
 constexpr int kPartStride = 132;         // floats per (unit, split, head) partial: M, L, pad, pad, acc[128]
-constexpr int kQFrags = 16;             // q' hi, q' lo, q_S hi, q_S lo × 4 K-steps
+constexpr int kQFrags = 8;              // q' (hi | lo columns), q_S (hi | lo) × 4 K-steps
 constexpr size_t kUnitBytes = kQFrags * 1024 + 256;  // operand fragments + scales
+constexpr int64_t kMaxSplitsPlan = 4096;        // splits per unit (merge keeps one weight each)
+constexpr int64_t kMaxCtx = int64_t(1) << 26;   // tokens per (batch, KV head): 32-bit offsets
 
 struct Plan {
   int ngroups, units, nsplit, split_len;
@@ -64,6 +66,7 @@ inline Plan make_plan(int B, int Hq, int Hkv, int64_t max_ctx) {
   const int64_t max_by_len = (max_ctx + 511) / 512;
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
+  if (want > kMaxSplitsPlan) want = kMaxSplitsPlan;
   const int64_t per = (max_ctx + want - 1) / want;
   const int64_t gran = kDecWaves * kBlockTok;
   p.split_len = static_cast<int>((per + gran - 1) / gran * gran);
@@ -86,78 +89,74 @@ struct PrepArgs {
   uint8_t* ws;
 };
 
+// grid (unit, 8): block c computes head column c (zero when c >= heads in the
+// unit) and zeroes column c + 8. Threads 0..127 compute (Π_K q)_r, threads
+// 128..255 (S q)_r.
 __global__ __launch_bounds__(256) void query_prep_kernel(PrepArgs a) {
-  __shared__ float qin[kMaxHeads][kD];
-  __shared__ float qp[kMaxHeads][kD];
-  __shared__ float qs[kMaxHeads][kD];
-  __shared__ float red[2][kMaxHeads][32];
-  const int unit = blockIdx.x;
+  __shared__ float qin[kD];
+  __shared__ float val[2][kD];
+  __shared__ float red[2][4];
+  __shared__ float scl[2];
+  const int unit = blockIdx.x, c = blockIdx.y;
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
   const int b = unit / (a.ngroups * a.Hkv);
-  const int h0 = kvh * a.G + grp * kMaxHeads;
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
-  const int tid = threadIdx.x;
-  for (int e = tid; e < gc * kD; e += 256) qin[e / kD][e % kD] = a.query[(size_t(b) * a.Hq + h0 + e / kD) * kD + e % kD];
+  const bool live = c < gc;
+  const int tid = threadIdx.x, which = tid >> 7, r = tid & 127;
+  const size_t h = size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + c;
+  if (live && tid < kD) qin[tid] = a.query[h * kD + tid];
   __syncthreads();
   // score = log2(e)·scale·n·(⟨Πq, c⟩ + √(π/2)/d·γ·⟨Sq, s⟩); centroids enter ×64σ.
-  const float sq = a.scale * kLog2e / (kCentScale * a.kh->sigma);
-  const float ss = a.scale * kLog2e * 1.2533141373155003f / kD;   // √(π/2)/d
-  for (int e = tid; e < gc * kD; e += 256) {
-    const int c = e / kD, r = e % kD;
-    float acc = 0.f, acc2 = 0.f;
-    for (int k = 0; k < kD; ++k) acc = fmaf(a.rot_k[r * kD + k], qin[c][k], acc);
-    qp[c][r] = acc * sq;
-    if (a.proj) {
-      for (int k = 0; k < kD; ++k) acc2 = fmaf(a.proj[r * kD + k], qin[c][k], acc2);
-      qs[c][r] = acc2 * ss;
+  float v = 0.f;
+  const float* M = which ? a.proj : a.rot_k;
+  if (live && M != nullptr) {
+    const f32x4* row = reinterpret_cast<const f32x4*>(M + r * kD);
+#pragma unroll 8
+    for (int k = 0; k < kD / 4; ++k) {
+      const f32x4 m = row[k];
+      v = fmaf(m[0], qin[4 * k], v);
+      v = fmaf(m[1], qin[4 * k + 1], v);
+      v = fmaf(m[2], qin[4 * k + 2], v);
+      v = fmaf(m[3], qin[4 * k + 3], v);
     }
+    v *= which ? a.scale * kLog2e * 1.2533141373155003f / kD            // √(π/2)/d
+               : a.scale * kLog2e / (kCentScale * a.kh->sigma);
   }
+  val[which][r] = v;
+  // Per-column power-of-two scale putting max|·| in [2^9, 2^10) for fp16.
+  float m = fabsf(v);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((tid & 63) == 0) red[which][(tid >> 6) & 1] = m;
   __syncthreads();
-  // Per-head power-of-two scale putting max|·| in [2^9, 2^10) for fp16.
-  if (tid < 2 * kMaxHeads * 32) {
-    const int which = tid / (kMaxHeads * 32), c = (tid / 32) % kMaxHeads, l = tid % 32;
-    float m = 0.f;
-    if (c < gc && (which == 0 || a.proj))
-      for (int r = l; r < kD; r += 32) m = fmaxf(m, fabsf(which ? qs[c][r] : qp[c][r]));
-    red[which][c][l] = m;
-  }
-  __syncthreads();
-  __shared__ float scl[2][kMaxHeads];
-  if (tid < 2 * kMaxHeads) {
-    const int which = tid / kMaxHeads, c = tid % kMaxHeads;
-    float m = 0.f;
-    for (int l = 0; l < 32; ++l) m = fmaxf(m, red[which][c][l]);
+  if (tid < 2) {
+    const float mx = fmaxf(red[tid][0], red[tid][1]);
     int ex = 0;
-    if (m > 0.f) frexpf(m, &ex);
-    scl[which][c] = (m > 0.f) ? ldexpf(1.0f, 10 - ex) : 1.0f;
+    if (mx > 0.f) frexpf(mx, &ex);
+    scl[tid] = (mx > 0.f) ? ldexpf(1.0f, 10 - ex) : 1.0f;
   }
   __syncthreads();
   uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   uint16_t* fr = reinterpret_cast<uint16_t*>(blk);
-  // Fragment f, lane l = (n, g), slot j: column n (head), rotated dim 32g + 8(f%4) + j;
-  // f/4 = 0: q' hi, 1: q' lo, 2: q_S hi, 3: q_S lo.
-  for (int e = tid; e < kQFrags * 64 * 8; e += 256) {
-    const int j = e & 7, lane = (e >> 3) & 63, f = e >> 9;
-    const int n = lane & 15, g = lane >> 4, s = f & 3;
-    const int dim = 32 * g + 8 * s + j;
-    uint16_t v = 0;
-    if (n < gc) {
+  // Fragment f, lane (n, g), slot j: rotated dim 32g + 8(f%4) + j; f/4 = 0: q',
+  // 1: q_S. Column n < 8 holds the fp16 hi part of head n, column n + 8 the lo
+  // part: one matrix-core pass gives both, and a row rotation by 8 lanes adds
+  // them. This block writes columns c and c + 8.
+  for (int e = tid; e < 2 * kQFrags * 4 * 8; e += 256) {
+    const int j = e & 7, g = (e >> 3) & 3, f = (e >> 5) & 7, half = e >> 8;
+    const int dim = 32 * g + 8 * (f & 3) + j;
+    uint16_t out = 0;
+    if (live) {
       uint16_t hi, lo;
-      if (f < 8) {
-        split_h(qp[n][dim] * scl[0][n], hi, lo);
-        v = (f < 4) ? hi : lo;
-      } else if (a.proj) {
-        split_h(qs[n][dim] * scl[1][n], hi, lo);
-        v = (f < 12) ? hi : lo;
-      }
+      const int w = f >> 2;
+      split_h(val[w][dim] * scl[w], hi, lo);
+      out = half ? lo : hi;
     }
-    fr[e] = v;
+    fr[(f * 64 + g * 16 + c + 8 * half) * 8 + j] = out;
   }
-  float* sc = reinterpret_cast<float*>(blk + kQFrags * 1024);
-  if (tid < 32) {
-    const int which = tid / 16, c = tid % 16;
-    sc[tid] = (c < gc) ? 1.0f / scl[which][c] : 0.f;
+  if (tid < 2) {
+    float* sc = reinterpret_cast<float*>(blk + kQFrags * 1024);
+    sc[tid * 16 + c] = live ? 1.0f / scl[tid] : 0.f;
   }
 }
 
@@ -204,70 +203,394 @@ template <int BK> struct KLut {
   static constexpr int u32_per_entry = (per / 2) * (lo ? 2 : 1);
 };
 
-// A operands of K-step s from the lane's 32 key codes (hi; lo for 4 bits).
-template <int BK>
-__device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 1], int s,
-                                             const uint32_t* lut, u32x4& hi, u32x4& lo) {
+// A operands of K-step S from the lane's 32 key codes (hi; lo for 4 bits).
+template <int BK, int S>
+__device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 1], const uint32_t* lut,
+                                             u32x4& hi, u32x4& lo) {
   if constexpr (BK == 4) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t e = (kw[s] >> (8 * p)) & 0xffu;
+      const uint32_t e = (kw[S] >> (8 * p)) & 0xffu;
       const u32x2 v = *reinterpret_cast<const u32x2*>(lut + 2 * e);
       hi[p] = v[0];
       lo[p] = v[1];
     }
   } else if constexpr (BK == 3) {
-    uint32_t e[4];
-    // s is a compile-time constant after unrolling in the caller.
-#define TQ_K3(S)                                  \
-  if (s == S) {                                   \
-    e[0] = bits_at<24 * S + 0, 6>(kw);            \
-    e[1] = bits_at<24 * S + 6, 6>(kw);            \
-    e[2] = bits_at<24 * S + 12, 6>(kw);           \
-    e[3] = bits_at<24 * S + 18, 6>(kw);           \
-  }
-    TQ_K3(0) TQ_K3(1) TQ_K3(2) TQ_K3(3)
-#undef TQ_K3
-#pragma unroll
-    for (int p = 0; p < 4; ++p) hi[p] = lut[e[p]];
+    hi[0] = lut[bits_at<24 * S + 0, 6>(kw)];
+    hi[1] = lut[bits_at<24 * S + 6, 6>(kw)];
+    hi[2] = lut[bits_at<24 * S + 12, 6>(kw)];
+    hi[3] = lut[bits_at<24 * S + 18, 6>(kw)];
   } else if constexpr (BK == 2) {
-    const uint32_t h = (kw[s >> 1] >> (16 * (s & 1))) & 0xffffu;
+    const uint32_t h = kw[S >> 1] >> (16 * (S & 1));
     const u32x2 q0 = *reinterpret_cast<const u32x2*>(lut + 2 * (h & 0xffu));
-    const u32x2 q1 = *reinterpret_cast<const u32x2*>(lut + 2 * (h >> 8));
+    const u32x2 q1 = *reinterpret_cast<const u32x2*>(lut + 2 * ((h >> 8) & 0xffu));
     hi = u32x4{q0[0], q0[1], q1[0], q1[1]};
   } else if constexpr (BK == 1) {
-    const uint32_t e = (kw[0] >> (8 * s)) & 0xffu;
-    hi = *reinterpret_cast<const u32x4*>(lut + 4 * e);
+    hi = *reinterpret_cast<const u32x4*>(lut + 4 * ((kw[0] >> (8 * S)) & 0xffu));
   }
 }
 
-// Codes of dims 8n..8n+7 of one value vector, right-aligned (8·BV bits).
+// Value codes of dims 8n..8n+7 → "nibble form": code of dim 8n+r in bits
+// [4r, 4r+BV). Spreads 8 fields of BV bits to 4-bit spacing.
 template <int BV>
-__device__ __forceinline__ uint32_t load_vgroup(const uint8_t* vec, int n) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(vec);
+__device__ __forceinline__ uint32_t to_nibbles(uint32_t w) {
   if constexpr (BV == 4) {
-    return w[n];
+    return w;
+  } else if constexpr (BV == 3) {
+    const uint32_t t = __builtin_amdgcn_ubfe(w, 0, 12) | ((w << 4) & 0x0fff0000u);
+    const uint32_t u = (t & 0x003f003fu) | ((t << 2) & 0x3f003f00u);
+    return (u & 0x07070707u) | ((u << 1) & 0x70707070u);
   } else if constexpr (BV == 2) {
-    return (w[n >> 1] >> (16 * (n & 1))) & 0xffffu;
-  } else if constexpr (BV == 1) {
-    return (w[n >> 2] >> (8 * (n & 3))) & 0xffu;
-  } else {  // BV == 3: bits 24n .. 24n+23
-    const int w0 = (3 * n) >> 2, off = (24 * n) & 31;
-    const uint32_t lo = w[w0];
-    const uint32_t hi = (off > 8) ? w[w0 + 1] : 0u;
-    return __builtin_amdgcn_alignbit(hi, lo, off) & 0xffffffu;
+    const uint32_t t = (w & 0xffu) | ((w << 8) & 0x00ff0000u);
+    const uint32_t u = (t & 0x000f000fu) | ((t << 4) & 0x0f000f00u);
+    return (u & 0x03030303u) | ((u << 2) & 0x30303030u);
+  } else {
+    const uint32_t t = (w & 0x0fu) | ((w << 12) & 0x000f0000u);
+    const uint32_t u = (t & 0x00030003u) | ((t << 6) & 0x03000300u);
+    return (u & 0x01010101u) | ((u << 3) & 0x10101010u);
   }
+}
+
+// ---- LDS staging of 32-token blocks ----------------------------------------
+// Each wavefront owns a ring of kStages stage buffers. A block's packed data
+// is copied HBM → LDS by the direct-to-LDS loads (global_load_lds: each lane
+// names a global address, the wavefront fills consecutive LDS), so loads for
+// blocks i+1 and i+2 are in flight while block i is computed without holding
+// registers. Stage layout (bytes): key codes [32][16·BK] | sketch [32][16] |
+// value codes [32][16·BV], padded to a multiple of 1024; then key norms [32],
+// value norms [32], γ [32] and 128 bytes of slack, each 4 bytes per token.
+constexpr int kStages = 3;
+
+template <int BK, bool PROD, int BV>
+struct Stage {
+  static constexpr int kc = 0;
+  static constexpr int qj = kc + 512 * BK;
+  static constexpr int vc = qj + (PROD ? 512 : 0);
+  static constexpr int codes = vc + 512 * BV;
+  static constexpr int ncode_dma = (codes + 1023) / 1024;       // 16-byte-per-lane loads
+  static constexpr int kn = ncode_dma * 1024;
+  static constexpr int vn = kn + 128;
+  static constexpr int kg = vn + 128;
+  static constexpr int bytes = kn + 512;
+  static constexpr int nnorm_dma = PROD ? 2 : 1;                 // 4-byte-per-lane loads
+  static constexpr int dma = ncode_dma + nnorm_dma;              // loads per block
+};
+
+#define TQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Issue the direct-to-LDS loads of the block starting at token t0 into `st`
+// (a wave-uniform LDS address). Without AL, token indices past `last` are
+// clamped to it (those tokens are masked later).
+template <int BK, bool PROD, int BV, bool AL>
+__device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t last, int lane,
+                                            const uint8_t* kc, const uint8_t* kq, const uint8_t* vc,
+                                            const float* kn, const float* vn, const float* kg) {
+  using L = Stage<BK, PROD, BV>;
+  auto cl = [&](uint32_t t) { return AL ? t : (t < last ? t : last); };
+#pragma unroll
+  for (int c = 0; c < L::ncode_dma; ++c) {
+    const int o = 1024 * c + 16 * lane;
+    const void* src;
+    if (BK > 0 && o < L::qj) {
+      const int rb = 16 * BK;
+      src = kc + size_t(cl(t0 + o / rb)) * rb + (o % rb);
+    } else if (PROD && o < L::vc) {
+      const int oo = o - L::qj;
+      src = kq + size_t(cl(t0 + oo / 16)) * 16 + (oo % 16);
+    } else if (o < L::codes) {
+      // Row slot s of a 16-token tile holds token 4(s%4) + s/4: the four lane
+      // groups then read four different bank ranges.
+      const int oo = o - L::vc, rb = 16 * BV;
+      const int row = oo / rb, tile = row >> 4, sl = row & 15;
+      const int tok = 16 * tile + 4 * (sl & 3) + (sl >> 2);
+      src = vc + size_t(cl(t0 + tok)) * rb + (oo % rb);
+    } else {
+      src = vc + size_t(cl(t0)) * (16 * BV);          // padding lanes: a valid dummy source
+    }
+    __builtin_amdgcn_global_load_lds(src, TQ_LDS(st + 1024 * c), 16, 0, 0);
+  }
+  {
+    const uint32_t t = cl(t0 + (lane & 31));
+    const float* src = (lane < 32) ? kn + t : vn + t;
+    __builtin_amdgcn_global_load_lds(src, TQ_LDS(st + L::kn), 4, 0, 0);
+  }
+  if constexpr (PROD) {
+    const uint32_t t = cl(t0 + (lane & 31));
+    __builtin_amdgcn_global_load_lds(kg + t, TQ_LDS(st + L::kg), 4, 0, 0);
+  }
+}
+
+// One lane's registers of a staged block. Score slot j = 4τ + i is token
+// 16τ + 4g + i of the block; key tile τ row n is token 16τ + n.
+template <int BK, bool PROD, int BV>
+struct Block {
+  uint32_t kw[2][BK > 0 ? BK : 1];
+  uint32_t qw[2];
+  float nk[8], gk[8], nv[8];
+  uint32_t vw[8];        // value code word holding dims 8n..8n+7 of slot j
+  uint32_t vw2[8];       // the following word (3-bit codes that straddle)
+};
+
+// Per-lane LDS byte offsets of the staged reads (add the stage base).
+struct StageOffsets {
+  uint32_t n, k, q, v0, v1;
+};
+
+template <int BK, bool PROD, int BV>
+__device__ __forceinline__ StageOffsets stage_offsets(int n, int g) {
+  using L = Stage<BK, PROD, BV>;
+  StageOffsets o;
+  o.n = L::kn + 16 * g;
+  o.k = L::kc + n * 16 * BK + 4 * BK * g;
+  o.q = L::qj + 16 * n + 4 * g;
+  const int vword = BV == 4 ? n : BV == 2 ? (n >> 1) : BV == 1 ? (n >> 2) : ((3 * n) >> 2);
+  o.v0 = L::vc + g * 16 * BV + 4 * vword;        // slot (g, i) sits in row 4i + g
+  o.v1 = o.v0 + 16 * 16 * BV;
+  return o;
+}
+
+// Read a staged block into registers. The wait for the block's loads (all
+// but the newest `pending` loads of this wavefront done) and the wait for the
+// LDS reads are inside each asm statement, so no output is used early.
+#define TQ_VMW "s_waitcnt vmcnt(%[pend])\n\t"
+#define TQ_NORMS "ds_read_b128 %[n0], %[an]\n\tds_read_b128 %[n1], %[an] offset:64\n\t"       \
+                 "ds_read_b128 %[n2], %[an] offset:128\n\tds_read_b128 %[n3], %[an] offset:192\n\t"
+#define TQ_GAMMA "ds_read_b128 %[n4], %[an] offset:256\n\tds_read_b128 %[n5], %[an] offset:320\n\t"
+#define TQ_QJ "ds_read2_b32 %[q0], %[aq] offset1:64\n\t"
+#define TQ_LGK "s_waitcnt lgkmcnt(0)"
+
+template <int BK, bool PROD, int BV, int PEND>
+__device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, const StageOffsets& o) {
+  const uint32_t an = sb + o.n, ak = sb + o.k, aq = sb + o.q, av0 = sb + o.v0, av1 = sb + o.v1;
+  f32x4 n0, n1, n2, n3, n4, n5;
+  u32x2 q0, v0, v1, v2, v3, v4, v5, v6, v7;
+  // Norms (+ γ, sketch) and value codes.
+#define TQ_VPAIRS(A, B, C)                                                                          \
+  "ds_read2_b32 %[v0], %[av0] offset1:" #A "\n\tds_read2_b32 %[v1], %[av0] offset0:" #B " offset1:" #C "\n\t" \
+  "ds_read2_b32 %[v2], %[av1] offset1:" #A "\n\tds_read2_b32 %[v3], %[av1] offset0:" #B " offset1:" #C "\n\t"
+#define TQ_VPAIRS3                                                                                   \
+  "ds_read2_b32 %[v0], %[av0] offset1:1\n\tds_read2_b32 %[v1], %[av0] offset0:48 offset1:49\n\t"     \
+  "ds_read2_b32 %[v2], %[av0] offset0:96 offset1:97\n\tds_read2_b32 %[v3], %[av0] offset0:144 offset1:145\n\t" \
+  "ds_read2_b32 %[v4], %[av1] offset1:1\n\tds_read2_b32 %[v5], %[av1] offset0:48 offset1:49\n\t"     \
+  "ds_read2_b32 %[v6], %[av1] offset0:96 offset1:97\n\tds_read2_b32 %[v7], %[av1] offset0:144 offset1:145\n\t"
+#define TQ_OUT4 [n0] "=v"(n0), [n1] "=v"(n1), [n2] "=v"(n2), [n3] "=v"(n3), [v0] "=v"(v0), [v1] "=v"(v1), \
+                [v2] "=v"(v2), [v3] "=v"(v3)
+#define TQ_IN [pend] "n"(PEND), [an] "v"(an), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1)
+  if constexpr (BV == 3) {
+    if constexpr (PROD)
+      asm volatile(TQ_VMW TQ_NORMS TQ_GAMMA TQ_QJ TQ_VPAIRS3 TQ_LGK
+                   : TQ_OUT4, [v4] "=v"(v4), [v5] "=v"(v5), [v6] "=v"(v6), [v7] "=v"(v7), [n4] "=v"(n4),
+                     [n5] "=v"(n5), [q0] "=v"(q0)
+                   : TQ_IN : "memory");
+    else
+      asm volatile(TQ_VMW TQ_NORMS TQ_VPAIRS3 TQ_LGK
+                   : TQ_OUT4, [v4] "=v"(v4), [v5] "=v"(v5), [v6] "=v"(v6), [v7] "=v"(v7)
+                   : TQ_IN : "memory");
+  } else {
+#define TQ_CASE(BVV, A, B, C)                                                                       \
+  if constexpr (BV == BVV) {                                                                        \
+    if constexpr (PROD)                                                                             \
+      asm volatile(TQ_VMW TQ_NORMS TQ_GAMMA TQ_QJ TQ_VPAIRS(A, B, C) TQ_LGK                         \
+                   : TQ_OUT4, [n4] "=v"(n4), [n5] "=v"(n5), [q0] "=v"(q0) : TQ_IN : "memory");      \
+    else                                                                                            \
+      asm volatile(TQ_VMW TQ_NORMS TQ_VPAIRS(A, B, C) TQ_LGK : TQ_OUT4 : TQ_IN : "memory");         \
+  }
+    // slot i is 4 rows (16·BV dwords) after slot i-1; pairs (0, 1) and (2, 3) of each tile
+    TQ_CASE(4, 64, 128, 192) TQ_CASE(2, 32, 64, 96) TQ_CASE(1, 16, 32, 48)
+#undef TQ_CASE
+  }
+#undef TQ_VPAIRS
+#undef TQ_VPAIRS3
+#undef TQ_OUT4
+#undef TQ_IN
+  // Key codes (own asm statement; the stage is already complete).
+  if constexpr (BK == 4) {
+    u32x4 k0, k1;
+    asm volatile("ds_read_b128 %[k0], %[ak]\n\tds_read_b128 %[k1], %[ak] offset:1024\n\t" TQ_LGK
+                 : [k0] "=v"(k0), [k1] "=v"(k1) : [ak] "v"(ak) : "memory");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { R.kw[0][k] = k0[k]; R.kw[1][k] = k1[k]; }
+  } else if constexpr (BK == 3) {
+    u32x2 k0, k1, k2;
+    asm volatile("ds_read2_b32 %[k0], %[ak] offset1:192\n\tds_read2_b32 %[k1], %[ak] offset0:1 offset1:193\n\t"
+                 "ds_read2_b32 %[k2], %[ak] offset0:2 offset1:194\n\t" TQ_LGK
+                 : [k0] "=v"(k0), [k1] "=v"(k1), [k2] "=v"(k2) : [ak] "v"(ak) : "memory");
+    R.kw[0][0] = k0[0]; R.kw[1][0] = k0[1];
+    R.kw[0][1] = k1[0]; R.kw[1][1] = k1[1];
+    R.kw[0][2] = k2[0]; R.kw[1][2] = k2[1];
+  } else if constexpr (BK == 2) {
+    u32x4 k0;
+    asm volatile("ds_read2_b64 %[k0], %[ak] offset1:64\n\t" TQ_LGK : [k0] "=v"(k0) : [ak] "v"(ak) : "memory");
+    R.kw[0][0] = k0[0]; R.kw[0][1] = k0[1]; R.kw[1][0] = k0[2]; R.kw[1][1] = k0[3];
+  } else if constexpr (BK == 1) {
+    u32x2 k0;
+    asm volatile("ds_read2_b32 %[k0], %[ak] offset1:64\n\t" TQ_LGK : [k0] "=v"(k0) : [ak] "v"(ak) : "memory");
+    R.kw[0][0] = k0[0]; R.kw[1][0] = k0[1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    R.nk[i] = n0[i]; R.nk[4 + i] = n1[i];
+    R.nv[i] = n2[i]; R.nv[4 + i] = n3[i];
+    if constexpr (PROD) { R.gk[i] = n4[i]; R.gk[4 + i] = n5[i]; }
+  }
+  if constexpr (PROD) { R.qw[0] = q0[0]; R.qw[1] = q0[1]; }
+  if constexpr (BV == 3) {
+    const u32x2 vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { R.vw[j] = vv[j][0]; R.vw2[j] = vv[j][1]; }
+  } else {
+    const u32x2 vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { R.vw[2 * k] = vv[k][0]; R.vw[2 * k + 1] = vv[k][1]; }
+  }
+}
+#undef TQ_VMW
+#undef TQ_NORMS
+#undef TQ_GAMMA
+#undef TQ_QJ
+#undef TQ_LGK
+
+struct SoftmaxState {
+  float m;        // reference max (log2 domain) of this lane's head
+  float l;        // Σ 2^(s - m) over this lane's tokens
+  float nvs;      // value-norm scale (wave-uniform)
+};
+
+constexpr float kLazy = 8.0f;   // rescale only when a score exceeds m by more than 2^8
+
+// Add the value of the lane 8 columns over (row rotation by 8 within each
+// 16-lane row): column h gets hi + lo of head h.
+__device__ __forceinline__ float add_ror8(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
 }
 
 template <int BK, bool PROD, int BV>
+__device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint32_t t0, uint32_t t_end,
+                                             int n, int g, const uint32_t* lut_k, const u32x4* lut_q,
+                                             const uint32_t* lut_v, const u32x4 (&bq)[4], const u32x4 (&bs)[4],
+                                             float iqs, float iqss, SoftmaxState& st, f32x4 (&acc)[8]) {
+  // ---- scores: column n = head n % 8 (hi part for n < 8, lo part above) ----
+  float sc[8];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    f32x4 dm = f32x4{0.f, 0.f, 0.f, 0.f}, dq = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BK > 0) {
+      u32x4 ah, al;
+#define TQ_KSTEP(S)                                              \
+  key_operands<BK, S>(R.kw[tau], lut_k, ah, al);                 \
+  dm = mfma(ah, bq[S], dm);                                      \
+  if constexpr (KLut<BK>::lo) dm = mfma(al, bq[S], dm);
+      TQ_KSTEP(0) TQ_KSTEP(1) TQ_KSTEP(2) TQ_KSTEP(3)
+#undef TQ_KSTEP
+    }
+    if constexpr (PROD) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dq = mfma(lut_q[(R.qw[tau] >> (8 * s)) & 0xffu], bs[s], dq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * tau + i;
+      float v = add_ror8(dm[i]) * iqs;
+      if constexpr (PROD) v = fmaf(R.gk[j] * add_ror8(dq[i]), iqss, v);
+      sc[j] = v * R.nk[j];
+    }
+  }
+  float nv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) nv[j] = R.nv[j];
+  if (t0 + kBlockTok > t_end) {            // last block of the range: mask
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = t0 + 16 * (j >> 2) + 4 * g + (j & 3) < t_end;
+      sc[j] = ok ? sc[j] : -INFINITY;
+      nv[j] = ok ? nv[j] : 0.f;
+    }
+  }
+
+  // ---- online softmax (log2 domain), lazily rescaled ----------------------
+  float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mloc = max4g(mloc);
+  float nvloc = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
+                      fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
+  nvloc = max4g(nvloc);                     // same on every lane
+  const bool grow_m = mloc > st.m + kLazy;
+  if (__builtin_expect(__any(grow_m) || nvloc > st.nvs, 0)) {
+    const float m_new = grow_m ? mloc : st.m;
+    const float alpha = exp2f(st.m - m_new);   // 0 when st.m = -inf, 1 when unchanged
+    const float nvs_new = nvloc > st.nvs ? 2.f * nvloc : st.nvs;
+    const float beta = st.nvs / nvs_new;       // 0 at the first block (acc is 0 then)
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float fi = __shfl(alpha, (4 * g + i) & 7, 64) * beta;   // row 4g+i holds head (4g+i)%8
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
+    }
+    st.m = m_new;
+    st.nvs = nvs_new;
+  }
+  const float inv_nvs = __builtin_amdgcn_rcpf(st.nvs);
+  // A operand of P·V: row n < 8 carries the fp16 hi part of head n's weights,
+  // row n + 8 the lo part; rows h and h + 8 of the result are summed at the end.
+  const bool lo_row = n >= 8;
+  u32x4 pa;
+  float psum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float p0 = __builtin_amdgcn_exp2f(sc[2 * k] - st.m), p1 = __builtin_amdgcn_exp2f(sc[2 * k + 1] - st.m);
+    psum += p0 + p1;
+    uint16_t h0, l0, h1, l1;
+    split_h(p0 * (nv[2 * k] * inv_nvs), h0, l0);
+    split_h(p1 * (nv[2 * k + 1] * inv_nvs), h1, l1);
+    pa[k] = lo_row ? (uint32_t(l0) | (uint32_t(l1) << 16)) : (uint32_t(h0) | (uint32_t(h1) << 16));
+  }
+  st.l += psum;
+
+  // ---- P·V: B operand column n = dim 8n + r, rows = token slots -----------
+  uint32_t X[4], Y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t a0, a1;
+    if constexpr (BV == 3) {
+      const int off = (24 * n) & 31;
+      a0 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k], R.vw[2 * k], off));
+      a1 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k + 1], R.vw[2 * k + 1], off));
+    } else if constexpr (BV == 2) {
+      a0 = to_nibbles<2>(R.vw[2 * k] >> (16 * (n & 1)));
+      a1 = to_nibbles<2>(R.vw[2 * k + 1] >> (16 * (n & 1)));
+    } else if constexpr (BV == 1) {
+      a0 = to_nibbles<1>(R.vw[2 * k] >> (8 * (n & 3)));
+      a1 = to_nibbles<1>(R.vw[2 * k + 1] >> (8 * (n & 3)));
+    } else {
+      a0 = R.vw[2 * k];
+      a1 = R.vw[2 * k + 1];
+    }
+    // byte q of X: (slot 2k, slot 2k+1) codes of dim 8n + 2q; of Y: dim 8n + 2q + 1
+    X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
+    Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    u32x4 bv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bv[k] = lut_v[(((r & 1) ? Y[k] : X[k]) >> (8 * (r >> 1))) & 0xffu];
+    acc[r] = mfma(pa, bv, acc[r]);
+  }
+}
+
+template <int BK, bool PROD, int BV, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) {
-  constexpr int KB = BK > 0 ? BK : 1;
   constexpr int kLutK = KLut<BK>::entries * KLut<BK>::u32_per_entry;
   __shared__ uint32_t lut_k[kLutK > 0 ? kLutK : 1] __attribute__((aligned(16)));
   __shared__ u32x4 lut_q[PROD ? 256 : 1];
-  __shared__ uint32_t lut_v[1 << (2 * BV)];
+  __shared__ uint32_t lut_v[256];
   __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads], wnv[kDecWaves];
-  __shared__ float wacc[kDecWaves][kMaxHeads][kD];
+  using SL = Stage<BK, PROD, BV>;
+  // Per wavefront: the stage ring, large enough to hold the 16 x 128 fp32
+  // accumulator rows in the epilogue.
+  constexpr int kRing = kStages * SL::bytes > 2 * kMaxHeads * kD * 4 ? kStages * SL::bytes : 2 * kMaxHeads * kD * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[kDecWaves][kRing];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -311,28 +634,28 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     }
   }
   {
+    // entry (a | b << 4): the fp16 centroids of codes a (low half) and b.
     constexpr int KV = 1 << BV;
     const float vs = kCentScale * a.vh->sigma;
-    for (int e = tid; e < KV * KV; e += blockDim.x)
-      lut_v[e] = uint32_t(f2h_bits(a.vcent[e & (KV - 1)] * vs)) |
-                 (uint32_t(f2h_bits(a.vcent[e >> BV] * vs)) << 16);
+    for (int e = tid; e < 256; e += blockDim.x) {
+      const int ca = e & 15, cb = e >> 4;
+      lut_v[e] = (ca < KV && cb < KV)
+                     ? uint32_t(f2h_bits(a.vcent[ca] * vs)) | (uint32_t(f2h_bits(a.vcent[cb] * vs)) << 16)
+                     : 0u;
+    }
   }
 
   // ---- query operands --------------------------------------------------------
   const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bqh[4], bql[4], bqs[4], bqsl[4];
+  u32x4 bq[4], bs[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    bqh[s] = fr[s * 64 + lane];
-    bql[s] = fr[(4 + s) * 64 + lane];
-    if constexpr (PROD) {
-      bqs[s] = fr[(8 + s) * 64 + lane];
-      bqsl[s] = fr[(12 + s) * 64 + lane];
-    }
+    bq[s] = fr[s * 64 + lane];
+    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
   }
   const float* scl = reinterpret_cast<const float*>(blk + kQFrags * 1024);
-  const float inv_qs = scl[n], inv_qss = scl[16 + n];
+  const float iqs = scl[n & 7], iqss = scl[16 + (n & 7)];
   __syncthreads();
 
   // ---- token range of this wavefront ---------------------------------------
@@ -342,155 +665,68 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     L = l < 0 ? 0 : (l > a.max_ctx ? a.max_ctx : l);
   }
   const int64_t per_wave = a.split_len / kDecWaves;
-  const int64_t t_begin = int64_t(split) * a.split_len + wave * per_wave;
-  const int64_t t_end = min(t_begin + per_wave, L);
+  const int64_t tb = int64_t(split) * a.split_len + wave * per_wave;
+  const int64_t te = min(tb + per_wave, L);
+  const uint32_t t_begin = static_cast<uint32_t>(tb);
+  const uint32_t t_end = te > tb ? static_cast<uint32_t>(te) : t_begin;
+  const uint32_t last = L > 0 ? static_cast<uint32_t>(L - 1) : 0u;
   const int64_t base = (int64_t(b) * a.Hkv + kvh) * a.max_ctx;
+  const uint8_t* kc = BK > 0 ? a.kc + base * (16 * BK) : a.vc;
+  const float* kn = a.kn + base;
+  const uint8_t* kq = PROD ? a.kq + base * 16 : a.vc;
+  const float* kg = PROD ? a.kg + base : a.kn;
+  const uint8_t* vc = a.vc + base * (16 * BV);
+  const float* vn = a.vn + base;
 
-  float m_run = -INFINITY, l_run = 0.f, nvs = 0.f;
+  SoftmaxState st{-INFINITY, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kBlockTok) {
-    const int64_t last = L - 1;
-    // Key codes of token t0 + 16τ + n, the lane's 32 codes (dims 32g..32g+31).
-    uint32_t kw[2][KB];
-    uint32_t qw[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      int64_t tk = t0 + 16 * tau + n;
-      tk = tk < last ? tk : last;
-      if constexpr (BK > 0) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.kc + (base + tk) * (16 * BK) + 4 * BK * g);
-        if constexpr (BK == 4) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-          kw[tau][0] = v[0]; kw[tau][1] = v[1]; kw[tau][2] = v[2]; kw[tau][3] = v[3];
-        } else if constexpr (BK == 2) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-          kw[tau][0] = v[0]; kw[tau][1] = v[1];
-        } else {
-#pragma unroll
-          for (int k = 0; k < BK; ++k) kw[tau][k] = src[k];
-        }
-      }
-      if constexpr (PROD) qw[tau] = *reinterpret_cast<const uint32_t*>(a.kq + (base + tk) * 16 + 4 * g);
+  // Ring of kStages LDS stages: block i is read from stage i % kStages after
+  // blocks i+1 (and the loads for i+2 are issued right after the read).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint8_t* ring = &stage[wv][0];
+  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const StageOffsets so = stage_offsets<BK, PROD, BV>(n, g);
+  const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
+  if (nblk > 0)
+    stage_block<BK, PROD, BV, AL>(ring, t_begin, last, lane, kc, kq, vc, kn, vn, kg);
+  if (nblk > 1)
+    stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, kq, vc, kn, vn, kg);
+  int cur = 0;
+  for (uint32_t i = 0; i < nblk; ++i) {
+    const uint32_t t0 = t_begin + i * kBlockTok;
+    Block<BK, PROD, BV> R;
+    const uint32_t sb = ring_addr + cur * SL::bytes;
+    if (i + 1 < nblk)
+      read_block<BK, PROD, BV, SL::dma>(R, sb, so);
+    else
+      read_block<BK, PROD, BV, 0>(R, sb, so);
+    if (i + 2 < nblk) {
+      const int nx = cur == 0 ? 2 : cur - 1;            // (cur + 2) % 3
+      stage_block<BK, PROD, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, kq, vc, kn, vn,
+                                    kg);
     }
-    // Per-token scalars for the lane's 8 score slots j = 4τ + i <-> token t0 + 16τ + 4g + i.
-    float nk[8], gk[8], nv[8];
-    uint32_t cw[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int64_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
-      t = t < last ? t : last;
-      nk[j] = a.kn[base + t];
-      if constexpr (PROD) gk[j] = a.kg[base + t];
-      nv[j] = a.vn[base + t];
-      cw[j] = load_vgroup<BV>(a.vc + (base + t) * (16 * BV), n);
-    }
-
-    // ---- scores: column n = head, rows = 16 tokens of tile τ --------------
-    float sc[8];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 dm = f32x4{0.f, 0.f, 0.f, 0.f}, dq = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (BK > 0) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          u32x4 ah, al;
-          key_operands<BK>(kw[tau], s, lut_k, ah, al);
-          dm = mfma(ah, bqh[s], dm);
-          dm = mfma(ah, bql[s], dm);
-          if constexpr (KLut<BK>::lo) dm = mfma(al, bqh[s], dm);
-        }
-      }
-      if constexpr (PROD) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 sg = lut_q[(qw[tau] >> (8 * s)) & 0xffu];
-          dq = mfma(sg, bqs[s], dq);
-          dq = mfma(sg, bqsl[s], dq);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * tau + i;
-        float v = dm[i] * inv_qs;
-        if constexpr (PROD) v = fmaf(gk[j] * dq[i], inv_qss, v);
-        v *= nk[j];
-        const int64_t t = t0 + 16 * tau + 4 * g + i;
-        sc[j] = (t < t_end) ? v : -INFINITY;
-      }
-    }
-
-    // ---- online softmax (log2 domain), reduced per wavefront ---------------
-    float mloc = sc[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[j]);
-    mloc = max4g(mloc);
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
-    float p[8], psum = 0.f, nvloc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(sc[j] - m_new);
-      psum += p[j];
-      nvloc = fmaxf(nvloc, (sc[j] > -INFINITY) ? nv[j] : 0.f);
-    }
-    l_run = fmaf(l_run, alpha, psum);
-    nvloc = max4g(nvloc);
-    const float nvs_new = fmaxf(nvs, nvloc);
-    const float beta = nvs_new > 0.f ? nvs / nvs_new : 1.f;
-    const float inv_nvs = nvs_new > 0.f ? 1.f / nvs_new : 0.f;
-    u32x4 pa, pal;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint16_t h0, l0, h1, l1;
-      split_h(p[2 * k] * nv[2 * k] * inv_nvs, h0, l0);
-      split_h(p[2 * k + 1] * nv[2 * k + 1] * inv_nvs, h1, l1);
-      pa[k] = uint32_t(h0) | (uint32_t(h1) << 16);
-      pal[k] = uint32_t(l0) | (uint32_t(l1) << 16);
-    }
-    const float f = alpha * beta;
-    if (__any(f != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float fi = __shfl(f, 4 * g + i, 64);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
-      }
-    }
-    m_run = m_new;
-    nvs = nvs_new;
-
-    // ---- P·V: B operand column n = dim 8n + r, rows = token slots ----------
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      u32x4 bv;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t ca = (cw[2 * k] >> (BV * r)) & ((1u << BV) - 1u);
-        const uint32_t cb = (cw[2 * k + 1] >> (BV * r)) & ((1u << BV) - 1u);
-        bv[k] = lut_v[ca | (cb << BV)];
-      }
-      acc[r] = mfma(pa, bv, acc[r]);
-      acc[r] = mfma(pal, bv, acc[r]);
-    }
+    attend_block<BK, PROD, BV>(R, t0, t_end, n, g, lut_k, lut_q, lut_v, bq, bs, iqs, iqss, st, acc);
+    cur = cur == 2 ? 0 : cur + 1;
   }
-  l_run = sum4g(l_run);
+  const float l_run = sum4g(st.l);
 
   // ---- merge the workgroup's wavefronts ------------------------------------
   if (g == 0 && n < kMaxHeads) {
-    wm[wave][n] = m_run;
+    wm[wave][n] = st.m;
     wl[wave][n] = l_run;
   }
-  if (lane == 0) wnv[wave] = nvs;
+  if (lane == 0) wnv[wave] = st.nvs;
+  // The wavefront's stage ring is free now: reuse it for its accumulator
+  // (rows 0..7: hi-weight parts of heads 0..7, rows 8..15: lo-weight parts).
+  float* wacc_own = reinterpret_cast<float*>(&stage[wave][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int head = 4 * g + i;
-    if (head < kMaxHeads) {
+    const int row = 4 * g + i;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) wacc[wave][head][8 * n + r] = acc[r][i];
-    }
+    for (int r = 0; r < 8; ++r) wacc_own[row * kD + 8 * n + r] = acc[r][i];
   }
   __syncthreads();
   float* out = a.part + ((size_t(unit) * a.nsplit + split) * kMaxHeads) * kPartStride;
@@ -505,7 +741,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
       for (int w = 0; w < kDecWaves; ++w) {
         const float fw = exp2f(wm[w][head] - M);
         Ls = fmaf(fw, wl[w][head], Ls);
-        A = fmaf(fw * wnv[w], wacc[w][head][dim], A);
+        const float* wa = reinterpret_cast<const float*>(&stage[w][0]);
+        A = fmaf(fw * wnv[w], wa[head * kD + dim] + wa[(head + 8) * kD + dim], A);
       }
     }
     float* o = out + head * kPartStride;
@@ -528,47 +765,71 @@ struct MergeArgs {
   int Hq, Hkv, G, ngroups, nsplit;
 };
 
+constexpr int kMaxSplits = 4096;
+
 __global__ __launch_bounds__(kD) void merge_kernel(MergeArgs a) {
+  __shared__ float wsp[kMaxSplits];
   __shared__ float orot[kD];
+  __shared__ float red[2][2];
   const int bh = blockIdx.x;
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int kvh = h / a.G, hin = h % a.G;
   const int unit = (b * a.Hkv + kvh) * a.ngroups + hin / kMaxHeads;
   const int slot = hin % kMaxHeads;
-  const int dim = threadIdx.x;
+  const int tid = threadIdx.x;
   const float* p = a.part + (size_t(unit) * a.nsplit * kMaxHeads + slot) * kPartStride;
   const size_t stride = size_t(kMaxHeads) * kPartStride;
+  // Max over splits, then weights 2^(M_s - M) and the total sum.
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, p[s * stride]);
-  float Ls = 0.f, A = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float* ps = p + s * stride;
-      const float f = exp2f(ps[0] - M);
-      Ls = fmaf(f, ps[1], Ls);
-      A = fmaf(f, ps[4 + dim], A);
-    }
+  for (int s = tid; s < a.nsplit; s += kD) M = fmaxf(M, p[s * stride]);
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if ((tid & 63) == 0) red[0][tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  float Ls = 0.f;
+  for (int s = tid; s < a.nsplit; s += kD) {
+    const float w = (M > -INFINITY) ? exp2f(p[s * stride] - M) : 0.f;
+    wsp[s] = w;
+    Ls = fmaf(w, p[s * stride + 1], Ls);
   }
-  orot[dim] = (Ls > 0.f) ? A / (Ls * kCentScale * a.vh->sigma) : 0.f;
+  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
+  if ((tid & 63) == 0) red[1][tid >> 6] = Ls;
+  __syncthreads();
+  Ls = red[1][0] + red[1][1];
+  float A = 0.f;
+  int s = 0;
+  for (; s + 8 <= a.nsplit; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[(s + k) * stride + 4 + tid];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) A = fmaf(wsp[s + k], v[k], A);
+  }
+  for (; s < a.nsplit; ++s) A = fmaf(wsp[s], p[s * stride + 4 + tid], A);
+  orot[tid] = (Ls > 0.f) ? A / (Ls * kCentScale * a.vh->sigma) : 0.f;
   __syncthreads();
   float o = 0.f;
-  for (int j = 0; j < kD; ++j) o = fmaf(a.rot_v[j * kD + dim], orot[j], o);
-  a.out[size_t(bh) * kD + dim] = o;
+#pragma unroll 16
+  for (int j = 0; j < kD; ++j) o = fmaf(a.rot_v[j * kD + tid], orot[j], o);
+  a.out[size_t(bh) * kD + tid] = o;
 }
 
 template <int BK, bool PROD, int BV>
-hipError_t launch_attn_t(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_split_kernel<BK, PROD, BV>), grid, dim3(kDecWaves * 64), 0, st, a);
+hipError_t launch_attn_t(const AttnArgs& a, bool al, dim3 grid, hipStream_t st) {
+  if (al)
+    hipLaunchKernelGGL((attn_split_kernel<BK, PROD, BV, true>), grid, dim3(kDecWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<BK, PROD, BV, false>), grid, dim3(kDecWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int BK, bool PROD>
-hipError_t launch_attn_bv(const AttnArgs& a, int bv, dim3 grid, hipStream_t st) {
+hipError_t launch_attn_bv(const AttnArgs& a, int bv, bool al, dim3 grid, hipStream_t st) {
   switch (bv) {
-    case 1: return launch_attn_t<BK, PROD, 1>(a, grid, st);
-    case 2: return launch_attn_t<BK, PROD, 2>(a, grid, st);
-    case 3: return launch_attn_t<BK, PROD, 3>(a, grid, st);
-    default: return launch_attn_t<BK, PROD, 4>(a, grid, st);
+    case 1: return launch_attn_t<BK, PROD, 1>(a, al, grid, st);
+    case 2: return launch_attn_t<BK, PROD, 2>(a, al, grid, st);
+    case 3: return launch_attn_t<BK, PROD, 3>(a, al, grid, st);
+    default: return launch_attn_t<BK, PROD, 4>(a, al, grid, st);
   }
 }
 
@@ -577,7 +838,7 @@ hipError_t launch_attn_bv(const AttnArgs& a, int bv, dim3 grid, hipStream_t st) 
 using namespace tq;
 
 extern "C" size_t tq_attn_decode_workspace(int B, int Hq, int Hkv, int64_t max_ctx) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 1) return 0;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 1 || max_ctx > kMaxCtx) return 0;
   return make_plan(B, Hq, Hkv, max_ctx).bytes;
 }
 
@@ -596,6 +857,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   if (query == nullptr || out == nullptr || k_cache == nullptr || v_cache == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 1) return TQ_ERR_INVALID_ARG;
+  if (max_ctx > kMaxCtx) return TQ_ERR_UNSUPPORTED;
   const bool prod = kq->variant == TQ_PROD;
   const int bk = prod ? kq->bits - 1 : kq->bits;
   if (k_cache->norms == nullptr || (bk > 0 && k_cache->codes == nullptr)) return TQ_ERR_INVALID_ARG;
@@ -614,7 +876,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   if (phase == 0 || phase == 1) {
     PrepArgs pa{query, kq->rot, prod ? kq->proj : nullptr, static_cast<const PrepHeader*>(kq->prep), scale,
                 Hq, Hkv, G, p.ngroups, ws};
-    hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(256), 0, s, pa);
+    hipLaunchKernelGGL(query_prep_kernel, dim3(p.units, kMaxHeads), dim3(256), 0, s, pa);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   if (phase == 0 || phase == 2) {
@@ -640,20 +902,21 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
     aa.split_len = p.split_len;
     const dim3 grid(p.nsplit, p.units);
     const int bv = vq->bits;
+    const bool al = (max_ctx % kBlockTok) == 0;
     hipError_t e;
     if (!prod) {
       switch (bk) {
-        case 1: e = launch_attn_bv<1, false>(aa, bv, grid, s); break;
-        case 2: e = launch_attn_bv<2, false>(aa, bv, grid, s); break;
-        case 3: e = launch_attn_bv<3, false>(aa, bv, grid, s); break;
-        default: e = launch_attn_bv<4, false>(aa, bv, grid, s); break;
+        case 1: e = launch_attn_bv<1, false>(aa, bv, al, grid, s); break;
+        case 2: e = launch_attn_bv<2, false>(aa, bv, al, grid, s); break;
+        case 3: e = launch_attn_bv<3, false>(aa, bv, al, grid, s); break;
+        default: e = launch_attn_bv<4, false>(aa, bv, al, grid, s); break;
       }
     } else {
       switch (bk) {
-        case 0: e = launch_attn_bv<0, true>(aa, bv, grid, s); break;
-        case 1: e = launch_attn_bv<1, true>(aa, bv, grid, s); break;
-        case 2: e = launch_attn_bv<2, true>(aa, bv, grid, s); break;
-        default: e = launch_attn_bv<3, true>(aa, bv, grid, s); break;
+        case 0: e = launch_attn_bv<0, true>(aa, bv, al, grid, s); break;
+        case 1: e = launch_attn_bv<1, true>(aa, bv, al, grid, s); break;
+        case 2: e = launch_attn_bv<2, true>(aa, bv, al, grid, s); break;
+        default: e = launch_attn_bv<3, true>(aa, bv, al, grid, s); break;
       }
     }
     if (e != hipSuccess) return TQ_ERR_HIP;
