@@ -15,21 +15,22 @@
 //   1. query_prep: q' = Π_K q, q_S = S q per query head, scaled into the log2
 //      domain, split into fp16 hi/lo matrix-core B operands.
 //   2. attn_split: grid (token split, unit). A unit is one (batch, KV head,
-//      group of <= 8 query heads). Each wavefront streams 32-token blocks:
-//      codes → fp16 operands through LDS lookup tables, scores on the matrix
-//      cores (heads padded to 16 columns), online softmax reduced per
+//      group of <= 8 query heads). A workgroup of 8 wavefronts fills one
+//      compute unit; each wavefront streams 32-token blocks through its LDS
+//      ring: codes → fp16 operands through LDS lookup tables, scores on the
+//      matrix cores (heads padded to 16 columns), online softmax reduced per
 //      wavefront, P·V on the matrix cores into a rotated-space accumulator.
-//      The four wavefronts of a workgroup merge in LDS and write one partial
-//      (max, sum, acc[128]) per head.
+//      The wavefronts merge in LDS and write one partial (max, sum, acc[128])
+//      per head.
 //   3. merge: log-sum-exp combine of the splits, then o = Π_Vᵀ acc / sum.
 //
 // Precision (rel. L2 vs an fp64 evaluation ~1e-5..1e-4 on Llama-shaped data):
 // centroids enter the fp16 tables as c·64·σ with a per-codebook σ in [1, 2)
 // chosen by tq_prepare so that they are nearly fp16-exact (≤ 2e-5 relative
 // error for ≤ 3-bit codebooks, ≤ 1e-4 for 4-bit ones, whose key table also
-// carries the fp16 remainder); q' and q_S are split into fp16 hi + lo, so each
-// score takes two (three for 4-bit keys) matrix-core passes; the softmax
-// weights are split hi + lo for the two P·V passes; all sums are fp32.
+// carries the fp16 remainder); q' and q_S are split into fp16 hi + lo (held in
+// separate matrix columns of one pass); the softmax weights are split hi + lo
+// (separate matrix rows of one pass); all sums are fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -37,17 +38,17 @@
 #include "tq_device.h"
 
 int tq_check_quantizer(const tq_quantizer* q);
-int tq_device_cus();
 
 namespace tq {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;             // wavefronts per split workgroup (2 per SIMD)
 constexpr int kBlockTok = 32;            // tokens per wavefront step
 constexpr int kMaxHeads = 8;             // query heads per unit
 constexpr int kPartStride = 132;         // floats per (unit, split, head) partial: M, L, pad, pad, acc[128]
 constexpr int kQFrags = 8;              // q' (hi | lo columns), q_S (hi | lo) × 4 K-steps
 constexpr size_t kUnitBytes = kQFrags * 1024 + 256;  // operand fragments + scales
+constexpr int kTargetGroups = 256;       // split workgroups per launch: one per compute unit
 constexpr int64_t kMaxSplitsPlan = 4096;        // splits per unit (merge keeps one weight each)
 constexpr int64_t kMaxCtx = int64_t(1) << 26;   // tokens per (batch, KV head): 32-bit offsets
 
@@ -61,14 +62,15 @@ inline Plan make_plan(int B, int Hq, int Hkv, int64_t max_ctx) {
   const int G = Hq / Hkv;
   p.ngroups = (G + kMaxHeads - 1) / kMaxHeads;
   p.units = B * Hkv * p.ngroups;
-  // Aim for ~2048 workgroups over the chip, at least 512 tokens per split.
-  int64_t want = (2048 + p.units - 1) / p.units;
-  const int64_t max_by_len = (max_ctx + 511) / 512;
+  // With fewer units than compute units, split the tokens so that one round
+  // of workgroups covers the chip, keeping at least 8 blocks per wavefront.
+  const int64_t gran = int64_t(kDecWaves) * kBlockTok;
+  int64_t want = p.units >= kTargetGroups ? 1 : kTargetGroups / p.units;
+  const int64_t max_by_len = (max_ctx + 8 * gran - 1) / (8 * gran);
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
   if (want > kMaxSplitsPlan) want = kMaxSplitsPlan;
   const int64_t per = (max_ctx + want - 1) / want;
-  const int64_t gran = kDecWaves * kBlockTok;
   p.split_len = static_cast<int>((per + gran - 1) / gran * gran);
   p.nsplit = static_cast<int>((max_ctx + p.split_len - 1) / p.split_len);
   p.part_off = (size_t(p.units) * kUnitBytes + 255) / 256 * 256;
@@ -95,8 +97,8 @@ struct PrepArgs {
 __global__ __launch_bounds__(256) void query_prep_kernel(PrepArgs a) {
   __shared__ float qin[kD];
   __shared__ float val[2][kD];
-  __shared__ float red[2][4];
-  __shared__ float scl[2];
+  __shared__ float red[4];
+  __shared__ float scl;
   const int unit = blockIdx.x, c = blockIdx.y;
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
@@ -124,16 +126,17 @@ __global__ __launch_bounds__(256) void query_prep_kernel(PrepArgs a) {
                : a.scale * kLog2e / (kCentScale * a.kh->sigma);
   }
   val[which][r] = v;
-  // Per-column power-of-two scale putting max|·| in [2^9, 2^10) for fp16.
+  // One power-of-two scale per head for both operands (the kernel adds the
+  // sketch term before scaling back), putting max|·| in [2^9, 2^10) for fp16.
   float m = fabsf(v);
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((tid & 63) == 0) red[which][(tid >> 6) & 1] = m;
+  if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
-  if (tid < 2) {
-    const float mx = fmaxf(red[tid][0], red[tid][1]);
+  if (tid == 0) {
+    const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     int ex = 0;
     if (mx > 0.f) frexpf(mx, &ex);
-    scl[tid] = (mx > 0.f) ? ldexpf(1.0f, 10 - ex) : 1.0f;
+    scl = (mx > 0.f) ? ldexpf(1.0f, 10 - ex) : 1.0f;
   }
   __syncthreads();
   uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
@@ -148,15 +151,14 @@ __global__ __launch_bounds__(256) void query_prep_kernel(PrepArgs a) {
     uint16_t out = 0;
     if (live) {
       uint16_t hi, lo;
-      const int w = f >> 2;
-      split_h(val[w][dim] * scl[w], hi, lo);
+      split_h(val[f >> 2][dim] * scl, hi, lo);
       out = half ? lo : hi;
     }
     fr[(f * 64 + g * 16 + c + 8 * half) * 8 + j] = out;
   }
-  if (tid < 2) {
+  if (tid == 0) {
     float* sc = reinterpret_cast<float*>(blk + kQFrags * 1024);
-    sc[tid * 16 + c] = live ? 1.0f / scl[tid] : 0.f;
+    sc[c] = live ? 1.0f / scl : 0.f;
   }
 }
 
@@ -181,53 +183,83 @@ struct AttnArgs {
   int Hkv, G, ngroups, nsplit, split_len;
 };
 
-// W bits at compile-time bit offset OFF of a little-endian word array.
-template <int OFF, int W, int N>
-__device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[N]) {
-  constexpr int wi = OFF >> 5, off = OFF & 31;
-  constexpr uint32_t mask = (W >= 32) ? 0xffffffffu : ((1u << W) - 1u);
-  if constexpr (off + W <= 32) {
-    return (w[wi] >> off) & mask;
-  } else {
-    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], off) & mask;
-  }
+// W bits at compile-time bit offset OFF of a little-endian word array,
+// returned shifted left by SH. The extract is one v_bfe_u32 (an alignbit
+// first when the field straddles two words), written as asm so that it is not
+// split into a shift and a mask; the shift then folds into the address add
+// (v_lshl_add_u32): two operations per table address.
+template <int OFF, int W>
+__device__ __forceinline__ uint32_t bfe_u32(uint32_t x) {
+  uint32_t r;
+  asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "n"(OFF), "n"(W));
+  return r;
 }
 
-// Key-code lookup tables. Each entry covers a group of codes (pairs for 3/4
-// bits, quads for 2, octets for 1) and holds their fp16 centroids c·64σ
-// packed in pairs; 4-bit tables append the fp16 remainders (lo parts).
+template <int OFF, int W, int SH, int N>
+__device__ __forceinline__ uint32_t field_shl(const uint32_t (&w)[N]) {
+  constexpr int wi = OFF >> 5, off = OFF & 31;
+  if constexpr (off + W <= 32)
+    return bfe_u32<off, W>(w[wi]) << SH;
+  else
+    return bfe_u32<0, W>(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], off)) << SH;
+}
+
+// ---- lookup tables in LDS -------------------------------------------------
+// Codes index small tables with per-lane addresses. Random lanes hitting one
+// LDS bank serialise, so the tables read most often are kept as kCopies
+// private copies: copy c = lane % 32 of entry e sits at e·(kCopies·width) +
+// c·width, and the 32 lanes of a half-wavefront always read 32 different banks.
+constexpr int kCopies = 32;
+
+// Key tables. Each entry covers a group of codes (pairs for 3 and 4 bits,
+// quads for 2, octets for 1) and holds their fp16 centroids c·64σ packed in
+// pairs; the 4-bit table appends the fp16 remainders (lo parts). The 3-bit
+// pair table (64 entries) is private per lane; the others are shared.
 template <int BK> struct KLut {
-  static constexpr bool lo = BK == 4;
-  static constexpr int per = BK >= 3 ? 2 : BK == 2 ? 4 : 8;       // codes per entry
-  static constexpr int entries = BK == 3 ? 64 : BK >= 1 ? 256 : 0;
-  static constexpr int u32_per_entry = (per / 2) * (lo ? 2 : 1);
+  static constexpr bool priv = BK == 3;
+  static constexpr int per = (BK == 3 || BK == 4) ? 2 : BK == 2 ? 4 : 8;     // codes per entry
+  static constexpr int entries = BK == 3 ? 64 : 256;
+  static constexpr int dwords = BK == 1 ? 4 : (BK == 2 || BK == 4) ? 2 : 1;  // per entry
+  static constexpr int bytes = BK == 0 ? 16 : priv ? entries * kCopies * 4 : entries * dwords * 4;
 };
 
 // A operands of K-step S from the lane's 32 key codes (hi; lo for 4 bits).
+// `lut` is the table; `lane4` the byte offset of the lane's private copy.
 template <int BK, int S>
-__device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 1], const uint32_t* lut,
-                                             u32x4& hi, u32x4& lo) {
+__device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 1], const uint8_t* lut,
+                                             uint32_t lane4, u32x4& hi, u32x4& lo) {
   if constexpr (BK == 4) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t e = (kw[S] >> (8 * p)) & 0xffu;
-      const u32x2 v = *reinterpret_cast<const u32x2*>(lut + 2 * e);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(lut + (e << 3));
       hi[p] = v[0];
       lo[p] = v[1];
     }
   } else if constexpr (BK == 3) {
-    hi[0] = lut[bits_at<24 * S + 0, 6>(kw)];
-    hi[1] = lut[bits_at<24 * S + 6, 6>(kw)];
-    hi[2] = lut[bits_at<24 * S + 12, 6>(kw)];
-    hi[3] = lut[bits_at<24 * S + 18, 6>(kw)];
+    // entry e of copy c at byte 128e + 4c
+    hi[0] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 0, 6, 7>(kw) + lane4));
+    hi[1] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 6, 6, 7>(kw) + lane4));
+    hi[2] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 12, 6, 7>(kw) + lane4));
+    hi[3] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 18, 6, 7>(kw) + lane4));
   } else if constexpr (BK == 2) {
     const uint32_t h = kw[S >> 1] >> (16 * (S & 1));
-    const u32x2 q0 = *reinterpret_cast<const u32x2*>(lut + 2 * (h & 0xffu));
-    const u32x2 q1 = *reinterpret_cast<const u32x2*>(lut + 2 * ((h >> 8) & 0xffu));
+    const u32x2 q0 = *reinterpret_cast<const u32x2*>(lut + ((h & 0xffu) << 3));
+    const u32x2 q1 = *reinterpret_cast<const u32x2*>(lut + (((h >> 8) & 0xffu) << 3));
     hi = u32x4{q0[0], q0[1], q1[0], q1[1]};
   } else if constexpr (BK == 1) {
-    hi = *reinterpret_cast<const u32x4*>(lut + 4 * ((kw[0] >> (8 * S)) & 0xffu));
+    hi = *reinterpret_cast<const u32x4*>(lut + (((kw[0] >> (8 * S)) & 0xffu) << 4));
   }
+}
+
+// Sketch operand of K-step S: the 8 sign bits of the step, as fp16 ±1 (bit
+// set → +1), from a private table of the 16 nibbles (2 dwords per entry).
+template <int S>
+__device__ __forceinline__ u32x4 sign_operand(uint32_t qw, const uint8_t* lut, uint32_t lane8) {
+  const uint32_t w[1] = {qw};
+  const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S, 4, 8>(w) + lane8));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S + 4, 4, 8>(w) + lane8));
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // Value codes of dims 8n..8n+7 → "nibble form": code of dim 8n+r in bits
@@ -254,69 +286,116 @@ __device__ __forceinline__ uint32_t to_nibbles(uint32_t w) {
 // ---- LDS staging of 32-token blocks ----------------------------------------
 // Each wavefront owns a ring of kStages stage buffers. A block's packed data
 // is copied HBM → LDS by the direct-to-LDS loads (global_load_lds: each lane
-// names a global address, the wavefront fills consecutive LDS), so loads for
-// blocks i+1 and i+2 are in flight while block i is computed without holding
-// registers. Stage layout (bytes): key codes [32][16·BK] | sketch [32][16] |
-// value codes [32][16·BV], padded to a multiple of 1024; then key norms [32],
-// value norms [32], γ [32] and 128 bytes of slack, each 4 bytes per token.
+// names a global address and the wavefront fills consecutive LDS, 16 bytes per
+// lane), so the loads for blocks i+1 and i+2 are in flight while block i is
+// computed, without holding registers. Each load instruction reads one array:
+// a block's 32 rows of 16·bits bytes take bits/2 wavefront loads plus a
+// half-wavefront (32-lane) one when bits is odd. Stage layout (bytes): key
+// codes [32][16·BK] | sketch [32][16] | value codes [32][16·BV] (rows
+// transposed within each 16-token tile) | key norms [32] | value norms [32] |
+// γ [32].
 constexpr int kStages = 3;
+
+template <int BITS>
+struct RowLoads {
+  static constexpr int full = BITS / 2;     // 64-lane loads of 16 bytes per lane
+  static constexpr int half = BITS & 1;     // one 32-lane load
+};
 
 template <int BK, bool PROD, int BV>
 struct Stage {
   static constexpr int kc = 0;
   static constexpr int qj = kc + 512 * BK;
   static constexpr int vc = qj + (PROD ? 512 : 0);
-  static constexpr int codes = vc + 512 * BV;
-  static constexpr int ncode_dma = (codes + 1023) / 1024;       // 16-byte-per-lane loads
-  static constexpr int kn = ncode_dma * 1024;
+  static constexpr int kn = vc + 512 * BV;
   static constexpr int vn = kn + 128;
   static constexpr int kg = vn + 128;
-  static constexpr int bytes = kn + 512;
-  static constexpr int nnorm_dma = PROD ? 2 : 1;                 // 4-byte-per-lane loads
-  static constexpr int dma = ncode_dma + nnorm_dma;              // loads per block
+  static constexpr int bytes = kg + (PROD ? 128 : 0);
+  // load instructions per block: codes, sketch (32 lanes), norms and γ (32 lanes, 4 bytes each)
+  static constexpr int dma = RowLoads<BK>::full + RowLoads<BK>::half + (PROD ? 1 : 0) +
+                             RowLoads<BV>::full + RowLoads<BV>::half + (PROD ? 3 : 2);
 };
+
+// Row r (0..31) of a staged value block holds token 16(r/16) + 4(r%4) + (r%16)/4,
+// so that the four lane groups reading token slots (g, i) hit four bank ranges.
+__device__ __forceinline__ uint32_t vrow_token(uint32_t r) {
+  const uint32_t sl = r & 15;
+  return 16 * (r >> 4) + 4 * (sl & 3) + (sl >> 2);
+}
+
+// Per-lane source coordinates of the code loads. Load j of an array covers
+// the 16-byte pieces L = 64j + lane of the block: row L / bits, byte 16(L % bits).
+struct DmaLane {
+  uint32_t ktok[2], kcol[2], koff[2];   // key codes: token, byte in row, byte offset from the block
+  uint32_t vtok[2], vcol[2], voff[2];   // value codes (rows transposed within tiles)
+  uint32_t ntok;                        // sketch rows, norms and γ: lane % 32
+};
+
+template <int BK, int BV>
+__device__ __forceinline__ DmaLane dma_lane(int lane) {
+  DmaLane d{};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t L = 64 * j + lane;
+    if constexpr (BK > 0) {
+      d.ktok[j] = L / BK;
+      d.kcol[j] = 16 * (L % BK);
+      d.koff[j] = 16 * L;
+    }
+    d.vtok[j] = vrow_token(L / BV);
+    d.vcol[j] = 16 * (L % BV);
+    d.voff[j] = d.vtok[j] * (16 * BV) + d.vcol[j];
+  }
+  d.ntok = lane & 31;
+  return d;
+}
 
 #define TQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Issue the direct-to-LDS loads of the block starting at token t0 into `st`
 // (a wave-uniform LDS address). Without AL, token indices past `last` are
-// clamped to it (those tokens are masked later).
+// clamped to it (those tokens are masked later); with AL every token of the
+// block exists.
 template <int BK, bool PROD, int BV, bool AL>
-__device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t last, int lane,
+__device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t last, int lane, const DmaLane& d,
                                             const uint8_t* kc, const uint8_t* kq, const uint8_t* vc,
                                             const float* kn, const float* vn, const float* kg) {
   using L = Stage<BK, PROD, BV>;
-  auto cl = [&](uint32_t t) { return AL ? t : (t < last ? t : last); };
+  using KD = RowLoads<BK>;
+  using VD = RowLoads<BV>;
+  constexpr int KR = 16 * BK, VR = 16 * BV;
+  // Source of a 16-byte piece (token tok, byte col) of an array with rows of
+  // RB bytes: with AL the block's first row is a wave-uniform base and the
+  // lane part a fixed offset; otherwise the token is clamped to `last`.
+  auto src = [&](const uint8_t* arr, int rb, uint32_t tok, uint32_t col, uint32_t off) -> const uint8_t* {
+    if constexpr (AL) return arr + size_t(t0) * rb + off;
+    else return arr + size_t(min(t0 + tok, last)) * rb + col;
+  };
+  auto nsrc = [&](const float* arr) -> const float* {
+    if constexpr (AL) return arr + t0 + d.ntok;
+    else return arr + min(t0 + d.ntok, last);
+  };
 #pragma unroll
-  for (int c = 0; c < L::ncode_dma; ++c) {
-    const int o = 1024 * c + 16 * lane;
-    const void* src;
-    if (BK > 0 && o < L::qj) {
-      const int rb = 16 * BK;
-      src = kc + size_t(cl(t0 + o / rb)) * rb + (o % rb);
-    } else if (PROD && o < L::vc) {
-      const int oo = o - L::qj;
-      src = kq + size_t(cl(t0 + oo / 16)) * 16 + (oo % 16);
-    } else if (o < L::codes) {
-      // Row slot s of a 16-token tile holds token 4(s%4) + s/4: the four lane
-      // groups then read four different bank ranges.
-      const int oo = o - L::vc, rb = 16 * BV;
-      const int row = oo / rb, tile = row >> 4, sl = row & 15;
-      const int tok = 16 * tile + 4 * (sl & 3) + (sl >> 2);
-      src = vc + size_t(cl(t0 + tok)) * rb + (oo % rb);
-    } else {
-      src = vc + size_t(cl(t0)) * (16 * BV);          // padding lanes: a valid dummy source
-    }
-    __builtin_amdgcn_global_load_lds(src, TQ_LDS(st + 1024 * c), 16, 0, 0);
-  }
-  {
-    const uint32_t t = cl(t0 + (lane & 31));
-    const float* src = (lane < 32) ? kn + t : vn + t;
-    __builtin_amdgcn_global_load_lds(src, TQ_LDS(st + L::kn), 4, 0, 0);
-  }
-  if constexpr (PROD) {
-    const uint32_t t = cl(t0 + (lane & 31));
-    __builtin_amdgcn_global_load_lds(kg + t, TQ_LDS(st + L::kg), 4, 0, 0);
+  for (int j = 0; j < KD::full; ++j)
+    __builtin_amdgcn_global_load_lds(src(kc, KR, d.ktok[j], d.kcol[j], d.koff[j]), TQ_LDS(st + L::kc + 1024 * j),
+                                     16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < VD::full; ++j)
+    __builtin_amdgcn_global_load_lds(src(vc, VR, d.vtok[j], d.vcol[j], d.voff[j]), TQ_LDS(st + L::vc + 1024 * j),
+                                     16, 0, 0);
+  if (lane < 32) {
+    constexpr int kj = KD::full, vj = VD::full;
+    if constexpr (KD::half)
+      __builtin_amdgcn_global_load_lds(src(kc, KR, d.ktok[kj], d.kcol[kj], d.koff[kj]),
+                                       TQ_LDS(st + L::kc + 1024 * kj), 16, 0, 0);
+    if constexpr (PROD)
+      __builtin_amdgcn_global_load_lds(src(kq, 16, d.ntok, 0, 16 * d.ntok), TQ_LDS(st + L::qj), 16, 0, 0);
+    if constexpr (VD::half)
+      __builtin_amdgcn_global_load_lds(src(vc, VR, d.vtok[vj], d.vcol[vj], d.voff[vj]),
+                                       TQ_LDS(st + L::vc + 1024 * vj), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(nsrc(kn), TQ_LDS(st + L::kn), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(nsrc(vn), TQ_LDS(st + L::vn), 4, 0, 0);
+    if constexpr (PROD) __builtin_amdgcn_global_load_lds(nsrc(kg), TQ_LDS(st + L::kg), 4, 0, 0);
   }
 }
 
@@ -450,10 +529,17 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 #undef TQ_QJ
 #undef TQ_LGK
 
+// Online softmax state of one lane (its head is column n % 8). The stored
+// weights are 2^(s - mk)·n_v with mk = m + log2(nvs): the value-norm scale nvs
+// (a power of two, at least twice every value norm seen) keeps them below 2^8
+// for fp16, and a partial (mk, l, acc) combines with others through 2^(mk - M)
+// alone.
 struct SoftmaxState {
-  float m;        // reference max (log2 domain) of this lane's head
-  float l;        // Σ 2^(s - m) over this lane's tokens
-  float nvs;      // value-norm scale (wave-uniform)
+  float m;        // reference max of the scores (log2 domain)
+  float mk;       // m + knv
+  float l;        // Σ 2^(s - mk) over this lane's tokens
+  float nvs;      // value-norm scale 2^knv (wave-uniform); 0 until a nonzero norm is seen
+  float knv;
 };
 
 constexpr float kLazy = 8.0f;   // rescale only when a score exceeds m by more than 2^8
@@ -464,12 +550,48 @@ __device__ __forceinline__ float add_ror8(float v) {
   return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
 }
 
+// max of 8 values with three v_max3_f32 and one v_max_f32 (no NaN
+// canonicalisation: the scores and norms are never signalling NaNs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max8f(const float (&v)[8]) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(max3f(v[0], v[1], v[2])), "v"(max3f(v[3], v[4], v[5])));
+  return max3f(r, v[6], v[7]);
+}
+
+struct Luts {
+  const uint8_t* k;
+  const uint8_t* q;
+  const uint8_t* v;
+  uint32_t klane, qlane, vlane;   // byte offsets of the lane's private copies
+};
+
+// P·V for dims 8n + r: the B operand's four dwords are the fp16 pairs of the
+// value codes in byte r/2 of X (r even) or Y (r odd), from the private table.
+template <int R>
+__device__ __forceinline__ void pv_step(const uint32_t (&X)[4], const uint32_t (&Y)[4], const Luts& T,
+                                        const u32x4& pa, f32x4& acc) {
+  u32x4 bv;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t xy[1] = {(R & 1) ? Y[k] : X[k]};
+    bv[k] = *reinterpret_cast<const uint32_t*>(T.v + (field_shl<8 * (R >> 1), 8, 7>(xy) + T.vlane));
+  }
+  acc = mfma(pa, bv, acc);
+}
+
 template <int BK, bool PROD, int BV>
 __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint32_t t0, uint32_t t_end,
-                                             int n, int g, const uint32_t* lut_k, const u32x4* lut_q,
-                                             const uint32_t* lut_v, const u32x4 (&bq)[4], const u32x4 (&bs)[4],
-                                             float iqs, float iqss, SoftmaxState& st, f32x4 (&acc)[8]) {
+                                             int n, int g, const Luts& T, const u32x4 (&bq)[4],
+                                             const u32x4 (&bs)[4], float iqs, uint32_t lomask,
+                                             SoftmaxState& st, f32x4 (&acc)[8]) {
   // ---- scores: column n = head n % 8 (hi part for n < 8, lo part above) ----
+  // u = ⟨q', c⟩ + γ⟨q_S, s⟩ for this lane's part; the row rotation adds the
+  // other part, and the key norm and the query scale finish the score.
   float sc[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
@@ -477,28 +599,29 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
     if constexpr (BK > 0) {
       u32x4 ah, al;
 #define TQ_KSTEP(S)                                              \
-  key_operands<BK, S>(R.kw[tau], lut_k, ah, al);                 \
+  key_operands<BK, S>(R.kw[tau], T.k, T.klane, ah, al);          \
   dm = mfma(ah, bq[S], dm);                                      \
-  if constexpr (KLut<BK>::lo) dm = mfma(al, bq[S], dm);
+  if constexpr (BK == 4) dm = mfma(al, bq[S], dm);
       TQ_KSTEP(0) TQ_KSTEP(1) TQ_KSTEP(2) TQ_KSTEP(3)
 #undef TQ_KSTEP
     }
     if constexpr (PROD) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dq = mfma(lut_q[(R.qw[tau] >> (8 * s)) & 0xffu], bs[s], dq);
+      dq = mfma(sign_operand<0>(R.qw[tau], T.q, T.qlane), bs[0], dq);
+      dq = mfma(sign_operand<1>(R.qw[tau], T.q, T.qlane), bs[1], dq);
+      dq = mfma(sign_operand<2>(R.qw[tau], T.q, T.qlane), bs[2], dq);
+      dq = mfma(sign_operand<3>(R.qw[tau], T.q, T.qlane), bs[3], dq);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * tau + i;
-      float v = add_ror8(dm[i]) * iqs;
-      if constexpr (PROD) v = fmaf(R.gk[j] * add_ror8(dq[i]), iqss, v);
-      sc[j] = v * R.nk[j];
+      const float u = PROD ? fmaf(R.gk[j], dq[i], dm[i]) : dm[i];
+      sc[j] = add_ror8(u) * R.nk[j];       // the score is sc·iqs
     }
   }
   float nv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) nv[j] = R.nv[j];
-  if (t0 + kBlockTok > t_end) {            // last block of the range: mask
+  if (__builtin_expect(t0 + kBlockTok > t_end, 0)) {   // last block of the range: mask
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool ok = t0 + 16 * (j >> 2) + 4 * g + (j & 3) < t_end;
@@ -508,44 +631,50 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
   }
 
   // ---- online softmax (log2 domain), lazily rescaled ----------------------
-  float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  mloc = max4g(mloc);
-  float nvloc = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
-                      fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
-  nvloc = max4g(nvloc);                     // same on every lane
-  const bool grow_m = mloc > st.m + kLazy;
-  if (__builtin_expect(__any(grow_m) || nvloc > st.nvs, 0)) {
-    const float m_new = grow_m ? mloc : st.m;
-    const float alpha = exp2f(st.m - m_new);   // 0 when st.m = -inf, 1 when unchanged
-    const float nvs_new = nvloc > st.nvs ? 2.f * nvloc : st.nvs;
-    const float beta = st.nvs / nvs_new;       // 0 at the first block (acc is 0 then)
-    st.l *= alpha;
+  const float mloc = max8f(sc) * iqs;
+  const float nvl = max8f(nv);
+  if (__builtin_expect(__any(mloc > st.m + kLazy || nvl > st.nvs), 0)) {
+    const float mg = max4g(mloc);           // this block's max for the head
+    const float nvw = max4g(nvl);           // this block's max value norm (every lane)
+    const float m_new = mg > st.m + kLazy ? mg : st.m;
+    float nvs_new = st.nvs, knv_new = st.knv;
+    if (nvw > st.nvs) {
+      int e;
+      frexpf(nvw, &e);                      // nvw < 2^e
+      nvs_new = ldexpf(1.0f, e + 1);
+      knv_new = static_cast<float>(e + 1);
+    }
+    const float mk_new = m_new + knv_new;
+    const float f = st.mk == -INFINITY ? 0.f : exp2f(st.mk - mk_new);
+    st.l *= f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float fi = __shfl(alpha, (4 * g + i) & 7, 64) * beta;   // row 4g+i holds head (4g+i)%8
+      const float fi = __shfl(f, (4 * g + i) & 7, 64);   // row 4g+i holds head (4g+i)%8
 #pragma unroll
       for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
     }
     st.m = m_new;
+    st.mk = mk_new;
     st.nvs = nvs_new;
+    st.knv = knv_new;
   }
-  const float inv_nvs = __builtin_amdgcn_rcpf(st.nvs);
   // A operand of P·V: row n < 8 carries the fp16 hi part of head n's weights,
-  // row n + 8 the lo part; rows h and h + 8 of the result are summed at the end.
-  const bool lo_row = n >= 8;
+  // row n + 8 the lo part (the weight minus its value truncated to fp16
+  // precision); rows h and h + 8 of the result are summed at the end.
   u32x4 pa;
-  float psum = 0.f;
+  const float nmk = -st.mk;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float p0 = __builtin_amdgcn_exp2f(sc[2 * k] - st.m), p1 = __builtin_amdgcn_exp2f(sc[2 * k + 1] - st.m);
-    psum += p0 + p1;
-    uint16_t h0, l0, h1, l1;
-    split_h(p0 * (nv[2 * k] * inv_nvs), h0, l0);
-    split_h(p1 * (nv[2 * k + 1] * inv_nvs), h1, l1);
-    pa[k] = lo_row ? (uint32_t(l0) | (uint32_t(l1) << 16)) : (uint32_t(h0) | (uint32_t(h1) << 16));
+    float x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * k + e], iqs, nmk));
+      st.l += p;
+      const float w = p * nv[2 * k + e];
+      x[e] = w - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, w) & lomask);
+    }
+    pa[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
   }
-  st.l += psum;
 
   // ---- P·V: B operand column n = dim 8n + r, rows = token slots -----------
   uint32_t X[4], Y[4];
@@ -570,80 +699,96 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
     X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
     Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
   }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    u32x4 bv;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bv[k] = lut_v[(((r & 1) ? Y[k] : X[k]) >> (8 * (r >> 1))) & 0xffu];
-    acc[r] = mfma(pa, bv, acc[r]);
-  }
+  pv_step<0>(X, Y, T, pa, acc[0]);
+  pv_step<1>(X, Y, T, pa, acc[1]);
+  pv_step<2>(X, Y, T, pa, acc[2]);
+  pv_step<3>(X, Y, T, pa, acc[3]);
+  pv_step<4>(X, Y, T, pa, acc[4]);
+  pv_step<5>(X, Y, T, pa, acc[5]);
+  pv_step<6>(X, Y, T, pa, acc[6]);
+  pv_step<7>(X, Y, T, pa, acc[7]);
 }
 
 template <int BK, bool PROD, int BV, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) {
-  constexpr int kLutK = KLut<BK>::entries * KLut<BK>::u32_per_entry;
-  __shared__ uint32_t lut_k[kLutK > 0 ? kLutK : 1] __attribute__((aligned(16)));
-  __shared__ u32x4 lut_q[PROD ? 256 : 1];
-  __shared__ uint32_t lut_v[256];
-  __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads], wnv[kDecWaves];
   using SL = Stage<BK, PROD, BV>;
+  using KL = KLut<BK>;
+  __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t lut_v[256 * kCopies * 4];
+  __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
   // Per wavefront: the stage ring, large enough to hold the 16 x 128 fp32
   // accumulator rows in the epilogue.
   constexpr int kRing = kStages * SL::bytes > 2 * kMaxHeads * kD * 4 ? kStages * SL::bytes : 2 * kMaxHeads * kD * 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[kDecWaves][kRing];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][kRing];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar token ranges
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, unit = blockIdx.y;
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
   const int b = unit / (a.ngroups * a.Hkv);
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
+  constexpr int nthr = kDecWaves * 64;
 
   // ---- lookup tables -------------------------------------------------------
   if constexpr (BK > 0) {
     constexpr int KK = 1 << BK;
     const float ks = kCentScale * a.kh->sigma;
-    for (int e = tid; e < KLut<BK>::entries; e += blockDim.x) {
-      uint32_t* dst = lut_k + e * KLut<BK>::u32_per_entry;
-      constexpr int per = KLut<BK>::per;
-      uint16_t hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < per; ++i) {
-        const int code = (e >> (BK * i)) & (KK - 1);
-        split_h(a.kcent[code] * ks, hi[i], lo[i]);
+    uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
+    if constexpr (KL::priv) {
+      for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
+        const int e = idx / kCopies;
+        lk[idx] = pack_h2(a.kcent[e & (KK - 1)] * ks, a.kcent[e >> BK] * ks);
       }
+    } else {
+      for (int e = tid; e < KL::entries; e += nthr) {
+        constexpr int per = KL::per;
+        uint16_t hi[8], lo[8];
 #pragma unroll
-      for (int i = 0; i < per / 2; ++i) {
-        dst[i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
-        if constexpr (KLut<BK>::lo) dst[per / 2 + i] = uint32_t(lo[2 * i]) | (uint32_t(lo[2 * i + 1]) << 16);
+        for (int i = 0; i < per; ++i) {
+          const int code = (e >> (BK * i)) & (KK - 1);
+          split_h(a.kcent[code] * ks, hi[i], lo[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < per / 2; ++i) {
+          lk[e * KL::dwords + i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
+          if constexpr (BK == 4) lk[e * KL::dwords + 1] = uint32_t(lo[0]) | (uint32_t(lo[1]) << 16);
+        }
       }
     }
   }
   if constexpr (PROD) {
-    for (int e = tid; e < 256; e += blockDim.x) {
-      u32x4 v;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t s0 = ((e >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u;
-        const uint32_t s1 = ((e >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u;
-        v[k] = s0 | (s1 << 16);
-      }
-      lut_q[e] = v;
+    // entry e (4 sign bits), dword w: signs of bits 2w and 2w + 1
+    uint32_t* lq = reinterpret_cast<uint32_t*>(lut_q);
+    for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
+      const int e = idx / (2 * kCopies), w = idx & 1;
+      const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
+      const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
+      lq[idx] = s0 | (s1 << 16);
     }
   }
   {
-    // entry (a | b << 4): the fp16 centroids of codes a (low half) and b.
+    // entry (c0 | c1 << 4): the fp16 centroids of value codes c0 (low half) and c1.
     constexpr int KV = 1 << BV;
     const float vs = kCentScale * a.vh->sigma;
-    for (int e = tid; e < 256; e += blockDim.x) {
-      const int ca = e & 15, cb = e >> 4;
-      lut_v[e] = (ca < KV && cb < KV)
-                     ? uint32_t(f2h_bits(a.vcent[ca] * vs)) | (uint32_t(f2h_bits(a.vcent[cb] * vs)) << 16)
-                     : 0u;
+    uint32_t* lv = reinterpret_cast<uint32_t*>(lut_v);
+    for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
+      const int e = idx / kCopies;
+      const int c0 = e & 15, c1 = e >> 4;
+      lv[idx] = (c0 < KV && c1 < KV) ? pack_h2(a.vcent[c0] * vs, a.vcent[c1] * vs) : 0u;
     }
   }
+  Luts T;
+  T.k = lut_k;
+  T.q = lut_q;
+  T.v = lut_v;
+  T.klane = KL::priv ? 4u * (lane & 31) : 0u;
+  T.qlane = 8u * (lane & 31);
+  T.vlane = 4u * (lane & 31);
+  const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
 
   // ---- query operands --------------------------------------------------------
   const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
@@ -654,8 +799,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     bq[s] = fr[s * 64 + lane];
     if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
   }
-  const float* scl = reinterpret_cast<const float*>(blk + kQFrags * 1024);
-  const float iqs = scl[n & 7], iqss = scl[16 + (n & 7)];
+  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   __syncthreads();
 
   // ---- token range of this wavefront ---------------------------------------
@@ -678,22 +822,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const uint8_t* vc = a.vc + base * (16 * BV);
   const float* vn = a.vn + base;
 
-  SoftmaxState st{-INFINITY, 0.f, 0.f};
+  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Ring of kStages LDS stages: block i is read from stage i % kStages after
   // blocks i+1 (and the loads for i+2 are issued right after the read).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint8_t* ring = &stage[wv][0];
+  uint8_t* ring = &stage[wave][0];
   const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
   const StageOffsets so = stage_offsets<BK, PROD, BV>(n, g);
+  const DmaLane dl = dma_lane<BK, BV>(lane);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
   if (nblk > 0)
-    stage_block<BK, PROD, BV, AL>(ring, t_begin, last, lane, kc, kq, vc, kn, vn, kg);
+    stage_block<BK, PROD, BV, AL>(ring, t_begin, last, lane, dl, kc, kq, vc, kn, vn, kg);
   if (nblk > 1)
-    stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, kq, vc, kn, vn, kg);
+    stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, vc, kn, vn, kg);
   int cur = 0;
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint32_t t0 = t_begin + i * kBlockTok;
@@ -705,22 +849,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
       read_block<BK, PROD, BV, 0>(R, sb, so);
     if (i + 2 < nblk) {
       const int nx = cur == 0 ? 2 : cur - 1;            // (cur + 2) % 3
-      stage_block<BK, PROD, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, kq, vc, kn, vn,
-                                    kg);
+      stage_block<BK, PROD, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, dl, kc, kq, vc, kn,
+                                    vn, kg);
     }
-    attend_block<BK, PROD, BV>(R, t0, t_end, n, g, lut_k, lut_q, lut_v, bq, bs, iqs, iqss, st, acc);
+    attend_block<BK, PROD, BV>(R, t0, t_end, n, g, T, bq, bs, iqs, lomask, st, acc);
     cur = cur == 2 ? 0 : cur + 1;
   }
   const float l_run = sum4g(st.l);
 
   // ---- merge the workgroup's wavefronts ------------------------------------
   if (g == 0 && n < kMaxHeads) {
-    wm[wave][n] = st.m;
+    wm[wave][n] = st.mk;
     wl[wave][n] = l_run;
   }
-  if (lane == 0) wnv[wave] = st.nvs;
-  // The wavefront's stage ring is free now: reuse it for its accumulator
-  // (rows 0..7: hi-weight parts of heads 0..7, rows 8..15: lo-weight parts).
+  // The wavefront's stage ring is free now (its last read waited for every
+  // load): reuse it for its accumulator (rows 0..7: hi-weight parts of heads
+  // 0..7, rows 8..15: lo-weight parts).
   float* wacc_own = reinterpret_cast<float*>(&stage[wave][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -730,7 +874,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   }
   __syncthreads();
   float* out = a.part + ((size_t(unit) * a.nsplit + split) * kMaxHeads) * kPartStride;
-  for (int e = tid; e < gc * kD; e += blockDim.x) {
+  for (int e = tid; e < gc * kD; e += nthr) {
     const int head = e / kD, dim = e % kD;
     float M = -INFINITY;
 #pragma unroll
@@ -742,7 +886,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
         const float fw = exp2f(wm[w][head] - M);
         Ls = fmaf(fw, wl[w][head], Ls);
         const float* wa = reinterpret_cast<const float*>(&stage[w][0]);
-        A = fmaf(fw * wnv[w], wa[head * kD + dim] + wa[(head + 8) * kD + dim], A);
+        A = fmaf(fw, wa[head * kD + dim] + wa[(head + 8) * kD + dim], A);
       }
     }
     float* o = out + head * kPartStride;
