@@ -39,6 +39,8 @@
 
 int tq_check_quantizer(const tq_quantizer* q);
 
+#define TQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 namespace tq {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -87,79 +89,164 @@ struct PrepArgs {
   const float* proj;   // null unless the keys carry the sketch
   const PrepHeader* kh;
   float scale;
-  int Hq, Hkv, G, ngroups;
+  int Hq, Hkv, G, ngroups, units;
   uint8_t* ws;
 };
 
-// grid (unit, 8): block c computes head column c (zero when c >= heads in the
-// unit) and zeroes column c + 8. Threads 0..127 compute (Π_K q)_r, threads
-// 128..255 (S q)_r.
-__global__ __launch_bounds__(256) void query_prep_kernel(PrepArgs a) {
-  __shared__ float qin[kD];
-  __shared__ float val[2][kD];
-  __shared__ float red[4];
-  __shared__ float scl;
-  const int unit = blockIdx.x, c = blockIdx.y;
+// One wavefront per unit. q' = Π_K q and q_S = S q = S'·q' (S' = S·Πᵀ) run on
+// the matrix cores with the key quantizer's prepared operands, in the
+// encoder's three-pass form (fp16 hi/lo of the matrix times fp16 hi/lo of the
+// power-of-two-scaled vector, fp32 sums), so both are fp32-accurate. Columns n
+// and n + 8 carry head n % 8; lane (n, g) ends up holding rotated dims
+// 32g..32g+31 of its column, which is exactly its share of the split kernel's
+// B operands.
+__device__ __forceinline__ void split_pairs(const float (&v)[32], u32x4 (&hi)[4], u32x4 (&lo)[4]) {
+  // v[q], q = 8s + 2k + h  ->  K-step s, dword k, half h
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint16_t h0, l0, h1, l1;
+      split_h(v[8 * s + 2 * k], h0, l0);
+      split_h(v[8 * s + 2 * k + 1], h1, l1);
+      hi[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
+      lo[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
+    }
+}
+
+// Σ_s A(t, s)·B(s) over the three hi/lo passes for the 8 row tiles; element j
+// of tile t is output row 32g + 4t + j of this lane's column.
+__device__ __forceinline__ void frag_matvec(const u32x4* frag, int lane, const u32x4 (&bh)[4],
+                                            const u32x4 (&bl)[4], float (&y)[32]) {
+  // the 8 row tiles' accumulation chains are interleaved
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 ah = frag[frag_index(0, t, s) * 64 + lane];
+      const u32x4 al = frag[frag_index(1, t, s) * 64 + lane];
+      acc[t] = mfma(ah, bh[s], acc[t]);
+      acc[t] = mfma(al, bh[s], acc[t]);
+      acc[t] = mfma(ah, bl[s], acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[4 * t + j] = acc[t][j];
+}
+
+__device__ __forceinline__ int max_exponent(float (&v)[32]) {
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 32; ++q) m = fmaxf(m, fabsf(v[q]));
+  m = max4g(m);
+  int ex = 0;
+  if (m > 0.f) frexpf(m, &ex);
+  return ex;
+}
+
+constexpr int kPrepWaves = 4;     // units per workgroup; they share the staged operands
+
+__global__ __launch_bounds__(kPrepWaves * 64) void query_prep_kernel(PrepArgs a) {
+  __shared__ u32x4 lds_f[2 * kFragsPerSet * 64];       // 16Π, then S' (128 KiB)
+  {
+    // direct-to-LDS copy of the operand fragments, all loads before one wait
+    const int ln = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.kh) + kPrepHeaderBytes);
+    const int chunks = (a.proj != nullptr ? 2 : 1) * kFragsPerSet;
+    for (int c = wv; c < chunks; c += kPrepWaves)
+      __builtin_amdgcn_global_load_lds(src + c * 64 + ln, TQ_LDS(lds_f + c * 64), 16, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  const int unit = blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+  if (unit >= a.units) return;
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
   const int b = unit / (a.ngroups * a.Hkv);
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, c = n & 7;
   const bool live = c < gc;
-  const int tid = threadIdx.x, which = tid >> 7, r = tid & 127;
-  const size_t h = size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + c;
-  if (live && tid < kD) qin[tid] = a.query[h * kD + tid];
-  __syncthreads();
+  const u32x4* frag = lds_f;
+  // B operand of the rotation: slot 8s + j of this lane is dim 32s + 8g + j.
+  float xv[32];
+  {
+    const float* qr = a.query + (size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + (live ? c : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(qr + 32 * s);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(qr + 32 * s + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        xv[8 * s + k] = live ? w0[k] : 0.f;
+        xv[8 * s + 4 + k] = live ? w1[k] : 0.f;
+      }
+    }
+  }
+  const int ex = max_exponent(xv);
+#pragma unroll
+  for (int q = 0; q < 32; ++q) xv[q] = ldexpf(xv[q], -ex);
+  u32x4 bh[4], bl[4];
+  split_pairs(xv, bh, bl);
+  float qp[32];                                   // q' = Π q, dims 32g + q
+  frag_matvec(frag, lane, bh, bl, qp);
+#pragma unroll
+  for (int q = 0; q < 32; ++q) qp[q] = ldexpf(qp[q], ex) * (1.0f / kRotScale);
+  float qs[32];                                   // q_S = S q, dims 32g + q
+#pragma unroll
+  for (int q = 0; q < 32; ++q) qs[q] = 0.f;
+  if (a.proj != nullptr) {
+    // B operand of the sketch: K-step s, lane group g holds dims 32g + 8s + j,
+    // which this lane computed itself.
+    float y[32];
+    const int e2 = max_exponent(qp);
+#pragma unroll
+    for (int q = 0; q < 32; ++q) y[q] = ldexpf(qp[q], -e2);
+    split_pairs(y, bh, bl);
+    frag_matvec(frag + kFragsPerSet * 64, lane, bh, bl, qs);
+    const float inv = 1.0f / a.kh->sp_scale;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) qs[q] = ldexpf(qs[q], e2) * inv;
+  }
   // score = log2(e)·scale·n·(⟨Πq, c⟩ + √(π/2)/d·γ·⟨Sq, s⟩); centroids enter ×64σ.
-  float v = 0.f;
-  const float* M = which ? a.proj : a.rot_k;
-  if (live && M != nullptr) {
-    const f32x4* row = reinterpret_cast<const f32x4*>(M + r * kD);
-#pragma unroll 8
-    for (int k = 0; k < kD / 4; ++k) {
-      const f32x4 m = row[k];
-      v = fmaf(m[0], qin[4 * k], v);
-      v = fmaf(m[1], qin[4 * k + 1], v);
-      v = fmaf(m[2], qin[4 * k + 2], v);
-      v = fmaf(m[3], qin[4 * k + 3], v);
-    }
-    v *= which ? a.scale * kLog2e * 1.2533141373155003f / kD            // √(π/2)/d
-               : a.scale * kLog2e / (kCentScale * a.kh->sigma);
+  const float fk = a.scale * kLog2e / (kCentScale * a.kh->sigma);
+  const float fs = a.scale * kLog2e * 1.2533141373155003f / kD;       // √(π/2)/d
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    qp[q] *= fk;
+    qs[q] *= fs;
+    m = fmaxf(m, fmaxf(fabsf(qp[q]), fabsf(qs[q])));
   }
-  val[which][r] = v;
-  // One power-of-two scale per head for both operands (the kernel adds the
-  // sketch term before scaling back), putting max|·| in [2^9, 2^10) for fp16.
-  float m = fabsf(v);
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int ex = 0;
-    if (mx > 0.f) frexpf(mx, &ex);
-    scl = (mx > 0.f) ? ldexpf(1.0f, 10 - ex) : 1.0f;
-  }
-  __syncthreads();
+  // One power-of-two scale per head for both operands (the split kernel adds
+  // the sketch term before scaling back), putting max|·| in [2^9, 2^10).
+  m = max4g(m);
+  int e3 = 0;
+  if (m > 0.f) frexpf(m, &e3);
+  const float scl = m > 0.f ? ldexpf(1.0f, 10 - e3) : 1.0f;
+  // Fragment f (f < 4: q', K-step f; f >= 4: q_S, K-step f - 4), lane (n, g),
+  // slot j: dim 32g + 8(f%4) + j; column n < 8 takes the fp16 hi part, column
+  // n + 8 the lo part, so one matrix-core pass gives both.
   uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
-  uint16_t* fr = reinterpret_cast<uint16_t*>(blk);
-  // Fragment f, lane (n, g), slot j: rotated dim 32g + 8(f%4) + j; f/4 = 0: q',
-  // 1: q_S. Column n < 8 holds the fp16 hi part of head n, column n + 8 the lo
-  // part: one matrix-core pass gives both, and a row rotation by 8 lanes adds
-  // them. This block writes columns c and c + 8.
-  for (int e = tid; e < 2 * kQFrags * 4 * 8; e += 256) {
-    const int j = e & 7, g = (e >> 3) & 3, f = (e >> 5) & 7, half = e >> 8;
-    const int dim = 32 * g + 8 * (f & 3) + j;
-    uint16_t out = 0;
-    if (live) {
-      uint16_t hi, lo;
-      split_h(val[f >> 2][dim] * scl, hi, lo);
-      out = half ? lo : hi;
+  u32x4* fr = reinterpret_cast<u32x4*>(blk);
+#pragma unroll
+  for (int f = 0; f < kQFrags; ++f) {
+    const float* v = f < 4 ? qp : qs;
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint16_t h0, l0, h1, l1;
+      split_h(v[8 * (f & 3) + 2 * k] * scl, h0, l0);
+      split_h(v[8 * (f & 3) + 2 * k + 1] * scl, h1, l1);
+      o[k] = n < 8 ? (uint32_t(h0) | (uint32_t(h1) << 16)) : (uint32_t(l0) | (uint32_t(l1) << 16));
     }
-    fr[(f * 64 + g * 16 + c + 8 * half) * 8 + j] = out;
+    fr[f * 64 + lane] = o;
   }
-  if (tid == 0) {
-    float* sc = reinterpret_cast<float*>(blk + kQFrags * 1024);
-    sc[c] = live ? 1.0f / scl : 0.f;
-  }
+  if (g == 0 && n < kMaxHeads) reinterpret_cast<float*>(blk + kQFrags * 1024)[n] = live ? 1.0f / scl : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -349,8 +436,6 @@ __device__ __forceinline__ DmaLane dma_lane(int lane) {
   d.ntok = lane & 31;
   return d;
 }
-
-#define TQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Issue the direct-to-LDS loads of the block starting at token t0 into `st`
 // (a wave-uniform LDS address). Without AL, token indices past `last` are
@@ -873,7 +958,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     for (int r = 0; r < 8; ++r) wacc_own[row * kD + 8 * n + r] = acc[r][i];
   }
   __syncthreads();
-  float* out = a.part + ((size_t(unit) * a.nsplit + split) * kMaxHeads) * kPartStride;
+  float* part = a.part + ((size_t(unit) * a.nsplit + split) * kMaxHeads) * kPartStride;
   for (int e = tid; e < gc * kD; e += nthr) {
     const int head = e / kD, dim = e % kD;
     float M = -INFINITY;
@@ -889,7 +974,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
         A = fmaf(fw, wa[head * kD + dim] + wa[(head + 8) * kD + dim], A);
       }
     }
-    float* o = out + head * kPartStride;
+    float* o = part + head * kPartStride;
     o[4 + dim] = A;
     if (dim == 0) {
       o[0] = M;
@@ -909,53 +994,81 @@ struct MergeArgs {
   int Hq, Hkv, G, ngroups, nsplit;
 };
 
-constexpr int kMaxSplits = 4096;
+// One workgroup per unit. Log-sum-exp combination of the splits per (head,
+// dim), then o = Π_Vᵀ·acc for the unit's heads: thread t takes output dim
+// t % 128 over a quarter of the contraction, so each row of Π_V is read once
+// for all heads. All loads of a thread are issued before their first use
+// (the Π_V column piece, then up to 16 splits' partials at a time).
+constexpr int kMergeChunk = 16;
 
-__global__ __launch_bounds__(kD) void merge_kernel(MergeArgs a) {
-  __shared__ float wsp[kMaxSplits];
-  __shared__ float orot[kD];
-  __shared__ float red[2][2];
-  const int bh = blockIdx.x;
-  const int h = bh % a.Hq, b = bh / a.Hq;
-  const int kvh = h / a.G, hin = h % a.G;
-  const int unit = (b * a.Hkv + kvh) * a.ngroups + hin / kMaxHeads;
-  const int slot = hin % kMaxHeads;
+__global__ __launch_bounds__(512) void merge_kernel(MergeArgs a) {
+  __shared__ float acc[kMaxHeads][kD];
+  __shared__ float red[4][kMaxHeads][kD];
+  const int unit = blockIdx.x;
+  const int grp = unit % a.ngroups;
+  const int kvh = (unit / a.ngroups) % a.Hkv;
+  const int b = unit / (a.ngroups * a.Hkv);
+  const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
   const int tid = threadIdx.x;
-  const float* p = a.part + (size_t(unit) * a.nsplit * kMaxHeads + slot) * kPartStride;
-  const size_t stride = size_t(kMaxHeads) * kPartStride;
-  // Max over splits, then weights 2^(M_s - M) and the total sum.
-  float M = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += kD) M = fmaxf(M, p[s * stride]);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if ((tid & 63) == 0) red[0][tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
-  float Ls = 0.f;
-  for (int s = tid; s < a.nsplit; s += kD) {
-    const float w = (M > -INFINITY) ? exp2f(p[s * stride] - M) : 0.f;
-    wsp[s] = w;
-    Ls = fmaf(w, p[s * stride + 1], Ls);
-  }
-  for (int o = 32; o > 0; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
-  if ((tid & 63) == 0) red[1][tid >> 6] = Ls;
-  __syncthreads();
-  Ls = red[1][0] + red[1][1];
-  float A = 0.f;
-  int s = 0;
-  for (; s + 8 <= a.nsplit; s += 8) {
-    float v[8];
+  const int r = tid & (kD - 1), jq = tid >> 7;
+  float pv[kD / 4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = p[(s + k) * stride + 4 + tid];
+  for (int j = 0; j < kD / 4; ++j) pv[j] = a.rot_v[(jq * (kD / 4) + j) * kD + r];
+  const float* up = a.part + size_t(unit) * a.nsplit * kMaxHeads * kPartStride;
+  const size_t sstride = size_t(kMaxHeads) * kPartStride;
+  const float inv_cs = 1.0f / (kCentScale * a.vh->sigma);
+  for (int e = tid; e < kMaxHeads * kD; e += 512) {
+    const int head = e / kD, dim = e % kD;
+    float v = 0.f;
+    if (head < gc) {
+      const float* ph = up + head * kPartStride;
+      float M = -INFINITY, Ls = 0.f, A = 0.f;
+      for (int s0 = 0; s0 < a.nsplit; s0 += kMergeChunk) {
+        float ms[kMergeChunk], ls[kMergeChunk], as[kMergeChunk];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) A = fmaf(wsp[s + k], v[k], A);
+        for (int i = 0; i < kMergeChunk; ++i) {
+          const bool ok = s0 + i < a.nsplit;
+          const float* q = ph + (ok ? s0 + i : 0) * sstride;
+          ms[i] = ok ? q[0] : -INFINITY;
+          ls[i] = ok ? q[1] : 0.f;
+          as[i] = ok ? q[4 + dim] : 0.f;
+        }
+        float mc = M;
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) mc = fmaxf(mc, ms[i]);
+        if (mc > -INFINITY) {
+          const float fo = M > -INFINITY ? exp2f(M - mc) : 0.f;
+          Ls *= fo;
+          A *= fo;
+#pragma unroll
+          for (int i = 0; i < kMergeChunk; ++i) {
+            const float fw = exp2f(ms[i] - mc);
+            Ls = fmaf(fw, ls[i], Ls);
+            A = fmaf(fw, as[i], A);
+          }
+          M = mc;
+        }
+      }
+      v = Ls > 0.f ? A * inv_cs / Ls : 0.f;
+    }
+    acc[head][dim] = v;
   }
-  for (; s < a.nsplit; ++s) A = fmaf(wsp[s], p[s * stride + 4 + tid], A);
-  orot[tid] = (Ls > 0.f) ? A / (Ls * kCentScale * a.vh->sigma) : 0.f;
   __syncthreads();
-  float o = 0.f;
-#pragma unroll 16
-  for (int j = 0; j < kD; ++j) o = fmaf(a.rot_v[j * kD + tid], orot[j], o);
-  a.out[size_t(bh) * kD + tid] = o;
+  float o[kMaxHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) o[h] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kD / 4; ++j)
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) o[h] = fmaf(pv[j], acc[h][jq * (kD / 4) + j], o[h]);
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) red[jq][h][r] = o[h];
+  __syncthreads();
+  for (int e = tid; e < gc * kD; e += 512) {
+    const int head = e / kD, dim = e % kD;
+    const size_t hq = size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + head;
+    a.out[hq * kD + dim] = red[0][head][dim] + red[1][head][dim] + red[2][head][dim] + red[3][head][dim];
+  }
 }
 
 template <int BK, bool PROD, int BV>
@@ -1019,8 +1132,9 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
 
   if (phase == 0 || phase == 1) {
     PrepArgs pa{query, kq->rot, prod ? kq->proj : nullptr, static_cast<const PrepHeader*>(kq->prep), scale,
-                Hq, Hkv, G, p.ngroups, ws};
-    hipLaunchKernelGGL(query_prep_kernel, dim3(p.units, kMaxHeads), dim3(256), 0, s, pa);
+                Hq, Hkv, G, p.ngroups, p.units, ws};
+    hipLaunchKernelGGL(query_prep_kernel, dim3((p.units + kPrepWaves - 1) / kPrepWaves), dim3(kPrepWaves * 64), 0,
+                       s, pa);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   if (phase == 0 || phase == 2) {
@@ -1067,7 +1181,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   }
   if (phase == 0 || phase == 3) {
     MergeArgs ma{part, vq->rot, static_cast<const PrepHeader*>(vq->prep), out, Hq, Hkv, G, p.ngroups, p.nsplit};
-    hipLaunchKernelGGL(merge_kernel, dim3(B * Hq), dim3(kD), 0, s, ma);
+    hipLaunchKernelGGL(merge_kernel, dim3(p.units), dim3(512), 0, s, ma);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   return TQ_OK;

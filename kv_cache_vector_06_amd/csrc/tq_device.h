@@ -17,12 +17,27 @@ constexpr int kD = 128;           // head dimension
 constexpr int kWave = 64;
 constexpr float kCentScale = 64.0f;   // centroids enter fp16 tables as c·64·σ
 
-// Header of a quantizer's prepared buffer (written by tq_prepare).
+// A quantizer's prepared buffer (written by tq_prepare): a 256-byte header,
+// then two sets of matrix-core A operands, each 2 parts (fp16 hi, lo) × 8 row
+// tiles × 4 K-steps × 64 lanes × 16 bytes: 16Π, and (prod) S' = S·Πᵀ scaled
+// by the power of two sp_scale. Fragment (part, t, s), lane (i, g), slot j
+// holds row out_row(t, i) and column 32s + 8g + j (16Π) or 32g + 8s + j (S').
 constexpr size_t kPrepHeaderBytes = 256;
 struct PrepHeader {
   float sigma;       // centroid scale σ in [1, 2), see prepare_kernel
   float sigma_err;   // max relative fp16 error of c·64·σ over the centroids
+  float sp_scale;    // the power of two S' is scaled by in its fragments
 };
+constexpr int kFragsPerSet = 2 * 8 * 4;               // (part, t, s)
+constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB
+constexpr size_t kPrepBytes = kPrepHeaderBytes + 2 * kSetBytes;
+constexpr float kRotScale = 16.0f;                    // |Π| <= 1 → |16Π| <= 16
+
+__host__ __device__ constexpr int frag_index(int part, int t, int s) { return (part * 8 + t) * 4 + s; }
+
+// Output row held by A-row i of row tile t: lane group i/4 ends up holding
+// rows 32*(i/4) + 4t + (i%4), so each lane group owns 32 consecutive outputs.
+__device__ __forceinline__ int out_row(int t, int i) { return 32 * (i >> 2) + 4 * t + (i & 3); }
 
 // D(16x16, fp32) += A(16x32, fp16) · B(32x16, fp16).
 // Lane l holds row l%16 of A and column l%16 of B, both over the K-slice of

@@ -25,19 +25,7 @@
 
 namespace tq {
 
-// Prepared buffer: a 256-byte header (PrepHeader), then two fragment sets of
-// 2 parts × 8 row tiles × 4 K-steps × 64 lanes × 16 bytes.
-constexpr int kFragsPerSet = 2 * 8 * 4;               // (part, t, s)
-constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB
-constexpr size_t kPrepBytes = kPrepHeaderBytes + 2 * kSetBytes;
-constexpr float kRotScale = 16.0f;                    // |Π| <= 1 → |16Π| <= 16
 constexpr float kResScale = 64.0f;                    // residual scale for the sketch
-
-__host__ __device__ constexpr int frag_index(int part, int t, int s) { return (part * 8 + t) * 4 + s; }
-
-// Output row held by A-row i of row tile t: lane group i/4 ends up holding
-// rows 32*(i/4) + 4t + (i%4), so each lane group owns 32 consecutive outputs.
-__device__ __forceinline__ int out_row(int t, int i) { return 32 * (i >> 2) + 4 * t + (i & 3); }
 
 // ---------------------------------------------------------------------------
 // tq_prepare: fragment the rotation (and S' = S·Πᵀ) into matrix-core A operands
@@ -82,6 +70,7 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__
       PrepHeader* h = reinterpret_cast<PrepHeader*>(prep_base);
       h->sigma = 1.0f + float(redi[0]) * (1.0f / (1 << 18));
       h->sigma_err = red[0];
+      h->sp_scale = 0.f;
     }
     __syncthreads();
   }
@@ -128,11 +117,30 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__
     pp[(frag_index(0, t, s) * 64 + lane) * 8 + j] = hi;
     pp[(frag_index(1, t, s) * 64 + lane) * 8 + j] = lo;
   }
+  if (tid == 0) reinterpret_cast<PrepHeader*>(prep_base)->sp_scale = float(sc);
 }
 
 // ---------------------------------------------------------------------------
 // Encode kernel
 // ---------------------------------------------------------------------------
+#define TQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Copy the 64 KiB fragment set at `src` (and the next one, when `dst2` is not
+// null) to LDS: wavefront w of the workgroup issues chunks w, w + W, ... of
+// 64 × 16 bytes, then every load is waited for and the workgroup synchronises.
+__device__ __forceinline__ void stage_frags(const u32x4* src, u32x4* dst, u32x4* dst2, int tid) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = __builtin_amdgcn_readfirstlane(static_cast<int>(blockDim.x) >> 6);
+  constexpr int chunks = kFragsPerSet;   // 64 × 64 × 16 B = 64 KiB
+  for (int c = wave; c < chunks; c += nw) {
+    __builtin_amdgcn_global_load_lds(src + c * 64 + lane, TQ_LDS(dst + c * 64), 16, 0, 0);
+    if (dst2 != nullptr)
+      __builtin_amdgcn_global_load_lds(src + (chunks + c) * 64 + lane, TQ_LDS(dst2 + c * 64), 16, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 struct EncodeArgs {
   const void* x;
   int64_t n;
@@ -210,11 +218,12 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   __shared__ u32x4 lds_rot[kFragsPerSet * 64];
   __shared__ u32x4 lds_proj[PROD ? kFragsPerSet * 64 : 1];
   constexpr int K = 1 << BM;
+  const u32x4* frot = lds_rot;
+  const u32x4* fproj = lds_proj;
 
-  for (int i = threadIdx.x; i < kFragsPerSet * 64; i += blockDim.x) {
-    lds_rot[i] = a.prep[i];
-    if constexpr (PROD) lds_proj[i] = a.prep[kFragsPerSet * 64 + i];
-  }
+  // Stage the operand fragments with direct-to-LDS loads (1 KiB per wavefront
+  // instruction), all issued before a single wait.
+  stage_frags(a.prep, lds_rot, PROD ? lds_proj : nullptr, threadIdx.x);
   Book bk{};
   if constexpr (BM >= 1) {
     const float* tb = a.boundaries + (K / 2 - 1);
@@ -311,8 +320,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x4 ah = lds_rot[frag_index(0, t, s) * 64 + lofs];
-        const u32x4 al = lds_rot[frag_index(1, t, s) * 64 + lofs];
+        const u32x4 ah = frot[frag_index(0, t, s) * 64 + lofs];
+        const u32x4 al = frot[frag_index(1, t, s) * 64 + lofs];
         acc[t] = mfma(ah, bx[s], acc[t]);
         acc[t] = mfma(al, bx[s], acc[t]);
         if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
@@ -390,8 +399,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const u32x4 sh = lds_proj[frag_index(0, t, s) * 64 + lofs];
-          const u32x4 sl = lds_proj[frag_index(1, t, s) * 64 + lofs];
+          const u32x4 sh = fproj[frag_index(0, t, s) * 64 + lofs];
+          const u32x4 sl = fproj[frag_index(1, t, s) * 64 + lofs];
           z[t] = mfma(sh, brh[s], z[t]);
           z[t] = mfma(sl, brh[s], z[t]);
           z[t] = mfma(sh, brl[s], z[t]);
