@@ -298,16 +298,28 @@ __device__ __forceinline__ uint32_t field_shl(const uint32_t (&w)[N]) {
 // c·width, and the 32 lanes of a half-wavefront always read 32 different banks.
 constexpr int kCopies = 32;
 
+// The private tables share one 64 KiB region of 256 rows × 256 bytes (copy
+// c = lane % 32):
+//   value pairs: entry e in row e at byte 4c (the lower half of the row), so
+//     that one byte permute forms the address (entry in bits 8..15, 4c in
+//     bits 0..7);
+//   3-bit key pairs: entry e in row e at byte 128 + 4c;
+//   sketch nibbles: entry e in rows 64 + 2e + c/16 at byte 128 + 8(c % 16).
+constexpr int kTabBytes = 256 * 256;
+constexpr uint32_t kTabK = 128;
+constexpr uint32_t kTabQ = 64 * 256 + 128;
+
 // Key tables. Each entry covers a group of codes (pairs for 3 and 4 bits,
 // quads for 2, octets for 1) and holds their fp16 centroids c·64σ packed in
 // pairs; the 4-bit table appends the fp16 remainders (lo parts). The 3-bit
-// pair table (64 entries) is private per lane; the others are shared.
+// pair table (64 entries) is private per lane (in the shared region); the
+// others are shared by all lanes.
 template <int BK> struct KLut {
   static constexpr bool priv = BK == 3;
   static constexpr int per = (BK == 3 || BK == 4) ? 2 : BK == 2 ? 4 : 8;     // codes per entry
   static constexpr int entries = BK == 3 ? 64 : 256;
   static constexpr int dwords = BK == 1 ? 4 : (BK == 2 || BK == 4) ? 2 : 1;  // per entry
-  static constexpr int bytes = BK == 0 ? 16 : priv ? entries * kCopies * 4 : entries * dwords * 4;
+  static constexpr int bytes = (BK == 0 || priv) ? 16 : entries * dwords * 4;   // the separate shared table
 };
 
 // A operands of K-step S from the lane's 32 key codes (hi; lo for 4 bits).
@@ -324,11 +336,11 @@ __device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 
       lo[p] = v[1];
     }
   } else if constexpr (BK == 3) {
-    // entry e of copy c at byte 128e + 4c
-    hi[0] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 0, 6, 7>(kw) + lane4));
-    hi[1] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 6, 6, 7>(kw) + lane4));
-    hi[2] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 12, 6, 7>(kw) + lane4));
-    hi[3] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 18, 6, 7>(kw) + lane4));
+    // entry e of copy c at byte 256e + 128 + 4c (lane4 = 128 + 4c)
+    hi[0] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 0, 6, 8>(kw) + lane4));
+    hi[1] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 6, 6, 8>(kw) + lane4));
+    hi[2] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 12, 6, 8>(kw) + lane4));
+    hi[3] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 18, 6, 8>(kw) + lane4));
   } else if constexpr (BK == 2) {
     const uint32_t h = kw[S >> 1] >> (16 * (S & 1));
     const u32x2 q0 = *reinterpret_cast<const u32x2*>(lut + ((h & 0xffu) << 3));
@@ -340,12 +352,13 @@ __device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 
 }
 
 // Sketch operand of K-step S: the 8 sign bits of the step, as fp16 ±1 (bit
-// set → +1), from a private table of the 16 nibbles (2 dwords per entry).
+// set → +1), from a private table of the 16 nibbles (2 dwords per entry;
+// entry e of copy c at byte 512e + lane8, lane8 = kTabQ + 256(c/16) + 8(c%16)).
 template <int S>
 __device__ __forceinline__ u32x4 sign_operand(uint32_t qw, const uint8_t* lut, uint32_t lane8) {
   const uint32_t w[1] = {qw};
-  const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S, 4, 8>(w) + lane8));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S + 4, 4, 8>(w) + lane8));
+  const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S, 4, 9>(w) + lane8));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S + 4, 4, 9>(w) + lane8));
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
@@ -381,7 +394,7 @@ __device__ __forceinline__ uint32_t to_nibbles(uint32_t w) {
 // codes [32][16·BK] | sketch [32][16] | value codes [32][16·BV] (rows
 // transposed within each 16-token tile) | key norms [32] | value norms [32] |
 // γ [32].
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 
 template <int BITS>
 struct RowLoads {
@@ -452,13 +465,24 @@ __device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t l
   // Source of a 16-byte piece (token tok, byte col) of an array with rows of
   // RB bytes: with AL the block's first row is a wave-uniform base and the
   // lane part a fixed offset; otherwise the token is clamped to `last`.
+  // The lane offsets pass through an empty asm so that the compiler keeps
+  // only the 32-bit offsets live across blocks (not one 64-bit pointer per load).
   auto src = [&](const uint8_t* arr, int rb, uint32_t tok, uint32_t col, uint32_t off) -> const uint8_t* {
-    if constexpr (AL) return arr + size_t(t0) * rb + off;
-    else return arr + size_t(min(t0 + tok, last)) * rb + col;
+    if constexpr (AL) {
+      asm volatile("" : "+v"(off));
+      return arr + size_t(t0) * rb + off;
+    } else {
+      return arr + size_t(min(t0 + tok, last)) * rb + col;
+    }
   };
   auto nsrc = [&](const float* arr) -> const float* {
-    if constexpr (AL) return arr + t0 + d.ntok;
-    else return arr + min(t0 + d.ntok, last);
+    if constexpr (AL) {
+      uint32_t off = d.ntok;
+      asm volatile("" : "+v"(off));
+      return arr + t0 + off;
+    } else {
+      return arr + min(t0 + d.ntok, last);
+    }
   };
 #pragma unroll
   for (int j = 0; j < KD::full; ++j)
@@ -655,18 +679,21 @@ struct Luts {
   uint32_t klane, qlane, vlane;   // byte offsets of the lane's private copies
 };
 
-// P·V for dims 8n + r: the B operand's four dwords are the fp16 pairs of the
-// value codes in byte r/2 of X (r even) or Y (r odd), from the private table.
+// B operand of P·V for dims 8n + r: four dwords, the fp16 pairs of the value
+// codes in byte r/2 of X (r even) or Y (r odd), from the private table.
 template <int R>
-__device__ __forceinline__ void pv_step(const uint32_t (&X)[4], const uint32_t (&Y)[4], const Luts& T,
-                                        const u32x4& pa, f32x4& acc) {
+__device__ __forceinline__ u32x4 pv_operand(const uint32_t (&X)[4], const uint32_t (&Y)[4], const Luts& T) {
+  // address = (byte R/2 of X or Y) · 256 + 4c: one byte permute; selector
+  // bytes: 0 → byte 0 of vlane (4c), 4 + R/2 → that code byte, 2 and 3 →
+  // the zero upper bytes of vlane
+  constexpr uint32_t sel = 0x03020000u | ((4u + (R >> 1)) << 8);
   u32x4 bv;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t xy[1] = {(R & 1) ? Y[k] : X[k]};
-    bv[k] = *reinterpret_cast<const uint32_t*>(T.v + (field_shl<8 * (R >> 1), 8, 7>(xy) + T.vlane));
+    const uint32_t xy = (R & 1) ? Y[k] : X[k];
+    bv[k] = *reinterpret_cast<const uint32_t*>(T.v + __builtin_amdgcn_perm(xy, T.vlane, sel));
   }
-  acc = mfma(pa, bv, acc);
+  return bv;
 }
 
 template <int BK, bool PROD, int BV>
@@ -674,6 +701,41 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
                                              int n, int g, const Luts& T, const u32x4 (&bq)[4],
                                              const u32x4 (&bs)[4], float iqs, uint32_t lomask,
                                              SoftmaxState& st, f32x4 (&acc)[8]) {
+  // ---- P·V operands first (they do not depend on the scores, so their
+  // table reads overlap the score work): column n = dim 8n + r, rows = token
+  // slots.
+  uint32_t X[4], Y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t a0, a1;
+    if constexpr (BV == 3) {
+      const int off = (24 * n) & 31;
+      a0 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k], R.vw[2 * k], off));
+      a1 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k + 1], R.vw[2 * k + 1], off));
+    } else if constexpr (BV == 2) {
+      a0 = to_nibbles<2>(R.vw[2 * k] >> (16 * (n & 1)));
+      a1 = to_nibbles<2>(R.vw[2 * k + 1] >> (16 * (n & 1)));
+    } else if constexpr (BV == 1) {
+      a0 = to_nibbles<1>(R.vw[2 * k] >> (8 * (n & 3)));
+      a1 = to_nibbles<1>(R.vw[2 * k + 1] >> (8 * (n & 3)));
+    } else {
+      a0 = R.vw[2 * k];
+      a1 = R.vw[2 * k + 1];
+    }
+    // byte q of X: (slot 2k, slot 2k+1) codes of dim 8n + 2q; of Y: dim 8n + 2q + 1
+    X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
+    Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
+  }
+  u32x4 bv[8];
+  bv[0] = pv_operand<0>(X, Y, T);
+  bv[1] = pv_operand<1>(X, Y, T);
+  bv[2] = pv_operand<2>(X, Y, T);
+  bv[3] = pv_operand<3>(X, Y, T);
+  bv[4] = pv_operand<4>(X, Y, T);
+  bv[5] = pv_operand<5>(X, Y, T);
+  bv[6] = pv_operand<6>(X, Y, T);
+  bv[7] = pv_operand<7>(X, Y, T);
+
   // ---- scores: column n = head n % 8 (hi part for n < 8, lo part above) ----
   // u = ⟨q', c⟩ + γ⟨q_S, s⟩ for this lane's part; the row rotation adds the
   // other part, and the key norm and the query scale finish the score.
@@ -761,46 +823,17 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
     pa[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
   }
 
-  // ---- P·V: B operand column n = dim 8n + r, rows = token slots -----------
-  uint32_t X[4], Y[4];
+  // ---- P·V -------------------------------------------------------------------
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t a0, a1;
-    if constexpr (BV == 3) {
-      const int off = (24 * n) & 31;
-      a0 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k], R.vw[2 * k], off));
-      a1 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k + 1], R.vw[2 * k + 1], off));
-    } else if constexpr (BV == 2) {
-      a0 = to_nibbles<2>(R.vw[2 * k] >> (16 * (n & 1)));
-      a1 = to_nibbles<2>(R.vw[2 * k + 1] >> (16 * (n & 1)));
-    } else if constexpr (BV == 1) {
-      a0 = to_nibbles<1>(R.vw[2 * k] >> (8 * (n & 3)));
-      a1 = to_nibbles<1>(R.vw[2 * k + 1] >> (8 * (n & 3)));
-    } else {
-      a0 = R.vw[2 * k];
-      a1 = R.vw[2 * k + 1];
-    }
-    // byte q of X: (slot 2k, slot 2k+1) codes of dim 8n + 2q; of Y: dim 8n + 2q + 1
-    X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
-    Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
-  }
-  pv_step<0>(X, Y, T, pa, acc[0]);
-  pv_step<1>(X, Y, T, pa, acc[1]);
-  pv_step<2>(X, Y, T, pa, acc[2]);
-  pv_step<3>(X, Y, T, pa, acc[3]);
-  pv_step<4>(X, Y, T, pa, acc[4]);
-  pv_step<5>(X, Y, T, pa, acc[5]);
-  pv_step<6>(X, Y, T, pa, acc[6]);
-  pv_step<7>(X, Y, T, pa, acc[7]);
+  for (int r = 0; r < 8; ++r) acc[r] = mfma(pa, bv[r], acc[r]);
 }
 
 template <int BK, bool PROD, int BV, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) {
   using SL = Stage<BK, PROD, BV>;
   using KL = KLut<BK>;
+  __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t lut_v[256 * kCopies * 4];
   __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
   // Per wavefront: the stage ring, large enough to hold the 16 x 128 fp32
   // accumulator rows in the epilogue.
@@ -825,8 +858,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
     if constexpr (KL::priv) {
       for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
-        const int e = idx / kCopies;
-        lk[idx] = pack_h2(a.kcent[e & (KK - 1)] * ks, a.kcent[e >> BK] * ks);
+        const int e = idx / kCopies, c = idx % kCopies;
+        *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) =
+            pack_h2(a.kcent[e & (KK - 1)] * ks, a.kcent[e >> BK] * ks);
       }
     } else {
       for (int e = tid; e < KL::entries; e += nthr) {
@@ -847,32 +881,32 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   }
   if constexpr (PROD) {
     // entry e (4 sign bits), dword w: signs of bits 2w and 2w + 1
-    uint32_t* lq = reinterpret_cast<uint32_t*>(lut_q);
     for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
-      const int e = idx / (2 * kCopies), w = idx & 1;
+      const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
       const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
       const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
-      lq[idx] = s0 | (s1 << 16);
+      *reinterpret_cast<uint32_t*>(tab + kTabQ + 512 * e + 256 * (c >> 4) + 8 * (c & 15) + 4 * w) = s0 | (s1 << 16);
     }
   }
   {
     // entry (c0 | c1 << 4): the fp16 centroids of value codes c0 (low half) and c1.
     constexpr int KV = 1 << BV;
     const float vs = kCentScale * a.vh->sigma;
-    uint32_t* lv = reinterpret_cast<uint32_t*>(lut_v);
     for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
-      const int e = idx / kCopies;
+      const int e = idx / kCopies, c = idx % kCopies;
       const int c0 = e & 15, c1 = e >> 4;
-      lv[idx] = (c0 < KV && c1 < KV) ? pack_h2(a.vcent[c0] * vs, a.vcent[c1] * vs) : 0u;
+      *reinterpret_cast<uint32_t*>(tab + 256 * e + 4 * c) =
+          (c0 < KV && c1 < KV) ? pack_h2(a.vcent[c0] * vs, a.vcent[c1] * vs) : 0u;
     }
   }
   Luts T;
-  T.k = lut_k;
-  T.q = lut_q;
-  T.v = lut_v;
-  T.klane = KL::priv ? 4u * (lane & 31) : 0u;
-  T.qlane = 8u * (lane & 31);
-  T.vlane = 4u * (lane & 31);
+  const uint32_t cp = lane & 31;            // private copy of this lane
+  T.k = KL::priv ? tab : lut_k;
+  T.q = tab;
+  T.v = tab;
+  T.klane = KL::priv ? kTabK + 4u * cp : 0u;
+  T.qlane = kTabQ + 256u * (cp >> 4) + 8u * (cp & 15);
+  T.vlane = 4u * cp;
   const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
 
   // ---- query operands --------------------------------------------------------
@@ -933,12 +967,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     else
       read_block<BK, PROD, BV, 0>(R, sb, so);
     if (i + 2 < nblk) {
-      const int nx = cur == 0 ? 2 : cur - 1;            // (cur + 2) % 3
+      // block i + 2 goes to stage (cur + 2) % kStages: with two stages, the one
+      // just read (read_block waited for all of its reads)
+      const int nx = (cur + 2) % kStages;
       stage_block<BK, PROD, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, dl, kc, kq, vc, kn,
                                     vn, kg);
     }
     attend_block<BK, PROD, BV>(R, t0, t_end, n, g, T, bq, bs, iqs, lomask, st, acc);
-    cur = cur == 2 ? 0 : cur + 1;
+    cur = cur + 1 == kStages ? 0 : cur + 1;
   }
   const float l_run = sum4g(st.l);
 
