@@ -552,7 +552,11 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
   const uint32_t an = sb + o.n, ak = sb + o.k, aq = sb + o.q, av0 = sb + o.v0, av1 = sb + o.v1;
   f32x4 n0, n1, n2, n3, n4, n5;
   u32x2 q0, v0, v1, v2, v3, v4, v5, v6, v7;
-  // Norms (+ γ, sketch) and value codes.
+  u32x4 ka, kb;         // key words: BK = 4 (two tiles), BK = 2 (both tiles)
+  u32x2 k0, k1, k2;     // key words: BK = 3 (word pairs), BK = 1
+  // One asm statement per layout: the wait for the block's loads, every read
+  // of the stage (norms, γ, sketch, value and key codes), then the wait for
+  // the reads, so no output is used early.
 #define TQ_VPAIRS(A, B, C)                                                                          \
   "ds_read2_b32 %[v0], %[av0] offset1:" #A "\n\tds_read2_b32 %[v1], %[av0] offset0:" #B " offset1:" #C "\n\t" \
   "ds_read2_b32 %[v2], %[av1] offset1:" #A "\n\tds_read2_b32 %[v3], %[av1] offset0:" #B " offset1:" #C "\n\t"
@@ -561,58 +565,66 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
   "ds_read2_b32 %[v2], %[av0] offset0:96 offset1:97\n\tds_read2_b32 %[v3], %[av0] offset0:144 offset1:145\n\t" \
   "ds_read2_b32 %[v4], %[av1] offset1:1\n\tds_read2_b32 %[v5], %[av1] offset0:48 offset1:49\n\t"     \
   "ds_read2_b32 %[v6], %[av1] offset0:96 offset1:97\n\tds_read2_b32 %[v7], %[av1] offset0:144 offset1:145\n\t"
+#define TQ_KR4 "ds_read_b128 %[ka], %[ak]\n\tds_read_b128 %[kb], %[ak] offset:1024\n\t"
+#define TQ_KR3 "ds_read2_b32 %[k0], %[ak] offset1:192\n\tds_read2_b32 %[k1], %[ak] offset0:1 offset1:193\n\t" \
+               "ds_read2_b32 %[k2], %[ak] offset0:2 offset1:194\n\t"
+#define TQ_KR2 "ds_read2_b64 %[ka], %[ak] offset1:64\n\t"
+#define TQ_KR1 "ds_read2_b32 %[k0], %[ak] offset1:64\n\t"
+#define TQ_KR0 ""
+#define TQ_KO4 , [ka] "=v"(ka), [kb] "=v"(kb)
+#define TQ_KO3 , [k0] "=v"(k0), [k1] "=v"(k1), [k2] "=v"(k2)
+#define TQ_KO2 , [ka] "=v"(ka)
+#define TQ_KO1 , [k0] "=v"(k0)
+#define TQ_KO0
 #define TQ_OUT4 [n0] "=v"(n0), [n1] "=v"(n1), [n2] "=v"(n2), [n3] "=v"(n3), [v0] "=v"(v0), [v1] "=v"(v1), \
                 [v2] "=v"(v2), [v3] "=v"(v3)
-#define TQ_IN [pend] "n"(PEND), [an] "v"(an), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1)
-  if constexpr (BV == 3) {
-    if constexpr (PROD)
-      asm volatile(TQ_VMW TQ_NORMS TQ_GAMMA TQ_QJ TQ_VPAIRS3 TQ_LGK
-                   : TQ_OUT4, [v4] "=v"(v4), [v5] "=v"(v5), [v6] "=v"(v6), [v7] "=v"(v7), [n4] "=v"(n4),
-                     [n5] "=v"(n5), [q0] "=v"(q0)
-                   : TQ_IN : "memory");
-    else
-      asm volatile(TQ_VMW TQ_NORMS TQ_VPAIRS3 TQ_LGK
-                   : TQ_OUT4, [v4] "=v"(v4), [v5] "=v"(v5), [v6] "=v"(v6), [v7] "=v"(v7)
-                   : TQ_IN : "memory");
-  } else {
-#define TQ_CASE(BVV, A, B, C)                                                                       \
-  if constexpr (BV == BVV) {                                                                        \
-    if constexpr (PROD)                                                                             \
-      asm volatile(TQ_VMW TQ_NORMS TQ_GAMMA TQ_QJ TQ_VPAIRS(A, B, C) TQ_LGK                         \
-                   : TQ_OUT4, [n4] "=v"(n4), [n5] "=v"(n5), [q0] "=v"(q0) : TQ_IN : "memory");      \
-    else                                                                                            \
-      asm volatile(TQ_VMW TQ_NORMS TQ_VPAIRS(A, B, C) TQ_LGK : TQ_OUT4 : TQ_IN : "memory");         \
+#define TQ_VO3 , [v4] "=v"(v4), [v5] "=v"(v5), [v6] "=v"(v6), [v7] "=v"(v7)
+#define TQ_VON
+#define TQ_OUTP , [n4] "=v"(n4), [n5] "=v"(n5), [q0] "=v"(q0)
+#define TQ_IN [pend] "n"(PEND), [an] "v"(an), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1), [ak] "v"(ak)
+#define TQ_K(VP, VS, KB)                                                                           \
+  if constexpr (BK == KB) {                                                                        \
+    if constexpr (PROD)                                                                            \
+      asm volatile(TQ_VMW TQ_NORMS TQ_GAMMA TQ_QJ VP TQ_KR##KB TQ_LGK                              \
+                   : TQ_OUT4 TQ_VO##VS TQ_OUTP TQ_KO##KB : TQ_IN : "memory");                      \
+    else                                                                                           \
+      asm volatile(TQ_VMW TQ_NORMS VP TQ_KR##KB TQ_LGK : TQ_OUT4 TQ_VO##VS TQ_KO##KB : TQ_IN : "memory"); \
   }
-    // slot i is 4 rows (16·BV dwords) after slot i-1; pairs (0, 1) and (2, 3) of each tile
-    TQ_CASE(4, 64, 128, 192) TQ_CASE(2, 32, 64, 96) TQ_CASE(1, 16, 32, 48)
-#undef TQ_CASE
-  }
+#define TQ_V(VP, VS) TQ_K(VP, VS, 0) TQ_K(VP, VS, 1) TQ_K(VP, VS, 2) TQ_K(VP, VS, 3) TQ_K(VP, VS, 4)
+  // slot i is 4 rows (16·BV dwords) after slot i-1; pairs (0, 1) and (2, 3) of each tile
+  if constexpr (BV == 3) { TQ_V(TQ_VPAIRS3, 3) }
+  if constexpr (BV == 4) { TQ_V(TQ_VPAIRS(64, 128, 192), N) }
+  if constexpr (BV == 2) { TQ_V(TQ_VPAIRS(32, 64, 96), N) }
+  if constexpr (BV == 1) { TQ_V(TQ_VPAIRS(16, 32, 48), N) }
+#undef TQ_V
+#undef TQ_K
 #undef TQ_VPAIRS
 #undef TQ_VPAIRS3
+#undef TQ_KR4
+#undef TQ_KR3
+#undef TQ_KR2
+#undef TQ_KR1
+#undef TQ_KR0
+#undef TQ_KO4
+#undef TQ_KO3
+#undef TQ_KO2
+#undef TQ_KO1
+#undef TQ_KO0
 #undef TQ_OUT4
+#undef TQ_VO3
+#undef TQ_VON
+#undef TQ_OUTP
 #undef TQ_IN
-  // Key codes (own asm statement; the stage is already complete).
   if constexpr (BK == 4) {
-    u32x4 k0, k1;
-    asm volatile("ds_read_b128 %[k0], %[ak]\n\tds_read_b128 %[k1], %[ak] offset:1024\n\t" TQ_LGK
-                 : [k0] "=v"(k0), [k1] "=v"(k1) : [ak] "v"(ak) : "memory");
 #pragma unroll
-    for (int k = 0; k < 4; ++k) { R.kw[0][k] = k0[k]; R.kw[1][k] = k1[k]; }
+    for (int k = 0; k < 4; ++k) { R.kw[0][k] = ka[k]; R.kw[1][k] = kb[k]; }
   } else if constexpr (BK == 3) {
-    u32x2 k0, k1, k2;
-    asm volatile("ds_read2_b32 %[k0], %[ak] offset1:192\n\tds_read2_b32 %[k1], %[ak] offset0:1 offset1:193\n\t"
-                 "ds_read2_b32 %[k2], %[ak] offset0:2 offset1:194\n\t" TQ_LGK
-                 : [k0] "=v"(k0), [k1] "=v"(k1), [k2] "=v"(k2) : [ak] "v"(ak) : "memory");
     R.kw[0][0] = k0[0]; R.kw[1][0] = k0[1];
     R.kw[0][1] = k1[0]; R.kw[1][1] = k1[1];
     R.kw[0][2] = k2[0]; R.kw[1][2] = k2[1];
   } else if constexpr (BK == 2) {
-    u32x4 k0;
-    asm volatile("ds_read2_b64 %[k0], %[ak] offset1:64\n\t" TQ_LGK : [k0] "=v"(k0) : [ak] "v"(ak) : "memory");
-    R.kw[0][0] = k0[0]; R.kw[0][1] = k0[1]; R.kw[1][0] = k0[2]; R.kw[1][1] = k0[3];
+    R.kw[0][0] = ka[0]; R.kw[0][1] = ka[1]; R.kw[1][0] = ka[2]; R.kw[1][1] = ka[3];
   } else if constexpr (BK == 1) {
-    u32x2 k0;
-    asm volatile("ds_read2_b32 %[k0], %[ak] offset1:64\n\t" TQ_LGK : [k0] "=v"(k0) : [ak] "v"(ak) : "memory");
     R.kw[0][0] = k0[0]; R.kw[1][0] = k0[1];
   }
 #pragma unroll
