@@ -196,6 +196,60 @@ __device__ __forceinline__ uint32_t quantize(float y, const Book& bk, int& m, bo
   return pos ? uint32_t(K / 2 + m) : uint32_t(K / 2 - 1 - m);
 }
 
+// The same search on the matrix-core output acc = S·y (S > 0, one per
+// vector), against thresholds scaled by S and compared as bit patterns
+// (non-negative floats order like their bit patterns): with a = |acc| and
+// m = #{j >= 1 : T_j < a} (acc > 0) or #{j >= 1 : T_j <= a} (acc <= 0, ties
+// to the lower index; "T <= a" is "T < a + 1 ulp"), the code is K/2 + m or
+// K/2 - 1 - m, i.e. m ^ K/2 or m ^ (K/2 - 1).
+struct ScaledBook {
+  uint32_t t[8];   // bits of S·t_j, j = 1 .. K/2 - 1
+  float c[8];      // S·(centroid magnitudes)
+};
+
+template <int BM>
+__device__ __forceinline__ uint32_t quantize_scaled(float acc, const ScaledBook& sb, uint32_t& m, bool& pos) {
+  constexpr uint32_t K2 = (1u << BM) / 2;
+  const uint32_t vb = __builtin_bit_cast(uint32_t, acc);
+  pos = static_cast<int32_t>(vb) > 0;
+  const uint32_t ab = (vb & 0x7fffffffu) + (pos ? 0u : 1u);
+  m = 0u;
+  if constexpr (BM == 2) {
+    m = ab > sb.t[1];
+  } else if constexpr (BM == 3) {
+    const uint32_t c1 = ab > sb.t[2];
+    const uint32_t th = c1 ? sb.t[3] : sb.t[1];
+    m = c1 + c1 + (ab > th);
+  } else if constexpr (BM == 4) {
+    const uint32_t c2 = ab > sb.t[4];
+    const uint32_t ta = c2 ? sb.t[6] : sb.t[2];
+    const uint32_t c1 = ab > ta;
+    const uint32_t th = c1 ? sb.t[7] : sb.t[5];
+    const uint32_t tl = c1 ? sb.t[3] : sb.t[1];
+    const uint32_t m2 = c2 + c2 + c1;
+    m = m2 + m2 + (ab > (c2 ? th : tl));
+  }
+  if constexpr (BM == 0) return 0u;
+  return m ^ (pos ? K2 : K2 - 1u);
+}
+
+template <int BM>
+__device__ __forceinline__ float scaled_mag(const ScaledBook& sb, uint32_t m) {
+  if constexpr (BM <= 1) return sb.c[0];
+  float c = (m & 1) ? sb.c[1] : sb.c[0];
+  if constexpr (BM >= 3) {
+    const float c23 = (m & 1) ? sb.c[3] : sb.c[2];
+    c = (m & 2) ? c23 : c;
+  }
+  if constexpr (BM >= 4) {
+    const float c45 = (m & 1) ? sb.c[5] : sb.c[4];
+    const float c67 = (m & 1) ? sb.c[7] : sb.c[6];
+    const float chi = (m & 2) ? c67 : c45;
+    c = (m & 4) ? chi : c;
+  }
+  return c;
+}
+
 template <int BM>
 __device__ __forceinline__ float centroid_mag(const Book& bk, int m) {
   if constexpr (BM <= 1) return bk.c0;
@@ -241,8 +295,39 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t ntiles = (a.n + 15) / 16;
-  for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles;
-       tile += int64_t(gridDim.x) * kEncWaves) {
+  const int64_t tstride = int64_t(gridDim.x) * kEncWaves;
+  // Raw input words of this lane's row for one tile: columns 32s + 8g + j.
+  // The next tile's words are loaded while the current one is computed.
+  constexpr int kRaw = F32IN ? 8 : 4;
+  auto load_raw = [&](int64_t tile, u32x4 (&raw)[kRaw]) {
+    const int64_t rowi = tile * 16 + n;
+    const int64_t row = rowi < a.n ? rowi : a.n - 1;
+    if constexpr (!F32IN) {
+      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(xr + 32 * s);
+    } else {
+      const float* xr = static_cast<const float*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        raw[2 * s] = *reinterpret_cast<const u32x4*>(xr + 32 * s);
+        raw[2 * s + 1] = *reinterpret_cast<const u32x4*>(xr + 32 * s + 4);
+      }
+    }
+  };
+  // (bf16 input only; fp32 input, twice the registers, loads its tile in place.)
+  u32x4 raw_next[kRaw];
+  int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave;
+  if (!F32IN && tile < ntiles) load_raw(tile, raw_next);
+  for (; tile < ntiles; tile += tstride) {
+    u32x4 raw[kRaw];
+    if constexpr (F32IN) {
+      load_raw(tile, raw);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kRaw; ++k) raw[k] = raw_next[k];
+      if (tile + tstride < ntiles) load_raw(tile + tstride, raw_next);
+    }
     const int64_t rowi = tile * 16 + n;
     const bool valid = rowi < a.n;
     const int64_t row = valid ? rowi : a.n - 1;
@@ -259,22 +344,19 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     // is below 1, so bf16 values convert to fp16 exactly.
     float xv[32];
     if constexpr (!F32IN) {
-      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.stride + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(xr + 32 * s);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          xv[8 * s + 2 * k] = bf16_to_f32(w[k] & 0xffffu);
-          xv[8 * s + 2 * k + 1] = bf16_to_f32(w[k] >> 16);
+          xv[8 * s + 2 * k] = bf16_to_f32(raw[s][k] & 0xffffu);
+          xv[8 * s + 2 * k + 1] = bf16_to_f32(raw[s][k] >> 16);
         }
       }
     } else {
-      const float* xr = static_cast<const float*>(a.x) + row * a.stride + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(xr + 32 * s);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(xr + 32 * s + 4);
+        const f32x4 w0 = __builtin_bit_cast(f32x4, raw[2 * s]);
+        const f32x4 w1 = __builtin_bit_cast(f32x4, raw[2 * s + 1]);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           xv[8 * s + k] = w0[k];
@@ -328,22 +410,35 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       }
     }
 
-    // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j.
-    const float up = (rs > 0.f) ? 1.0f / (kRotScale * rs) : 0.f;
+    // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j, and
+    // acc = S·y with S = 16‖x‖·2^-e (any S > 0 for a zero vector, whose acc is 0).
+    const float S = (rs > 0.f) ? kRotScale * rs : 1.0f;
+    const float up = 1.0f / S;
+    ScaledBook sb;
+    {
+      const float tb[8] = {0.f, bk.t1, bk.t2, bk.t3, bk.t4, bk.t5, bk.t6, bk.t7};
+      const float cb[8] = {bk.c0, bk.c1, bk.c2, bk.c3, bk.c4, bk.c5, bk.c6, bk.c7};
+#pragma unroll
+      for (int j = 1; j < K / 2; ++j) sb.t[j] = __builtin_bit_cast(uint32_t, tb[j] * S);
+      if constexpr (PROD) {
+#pragma unroll
+        for (int j = 0; j < (K / 2 > 0 ? K / 2 : 1); ++j) sb.c[j] = cb[j] * S;
+      }
+    }
     uint32_t w[BM > 0 ? BM : 1];
 #pragma unroll
     for (int k = 0; k < (BM > 0 ? BM : 1); ++k) w[k] = 0u;
     u32x4 brh[4], brl[4];
     float r2 = 0.f;
+    const float rsc = up * kResScale;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       float res[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float y = acc[t][j] * up;
-        int m;
+        uint32_t m;
         bool pos;
-        const uint32_t code = quantize<BM>(y, bk, m, pos);
+        const uint32_t code = quantize_scaled<BM>(acc[t][j], sb, m, pos);
         if constexpr (BM > 0) {
           const int q = 4 * t + j;
           const int bit = q * BM, wi = bit >> 5, off = bit & 31;
@@ -353,20 +448,21 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
         if constexpr (PROD) {
           float c = 0.f;
           if constexpr (BM >= 1) {
-            c = centroid_mag<BM>(bk, m);
+            c = scaled_mag<BM>(sb, m);
             c = pos ? c : -c;
           }
-          res[j] = y - c;
-          r2 = fmaf(res[j], res[j], r2);
+          const float racc = acc[t][j] - c;      // S·(y - c)
+          r2 = fmaf(racc, racc, r2);
+          res[j] = racc * rsc;                   // 64·(y - c)
         }
       }
       if constexpr (PROD) {
         // q = 4t + j  ->  K-step s = t/2, dword 2(t%2) + j/2, half j%2.
         uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
-        split_h(res[0] * kResScale, h0, l0);
-        split_h(res[1] * kResScale, h1, l1);
-        split_h(res[2] * kResScale, h2, l2);
-        split_h(res[3] * kResScale, h3, l3);
+        split_h(res[0], h0, l0);
+        split_h(res[1], h1, l1);
+        split_h(res[2], h2, l2);
+        split_h(res[3], h3, l3);
         const int s = t >> 1, k0 = 2 * (t & 1);
         brh[s][k0] = uint32_t(h0) | (uint32_t(h1) << 16);
         brh[s][k0 + 1] = uint32_t(h2) | (uint32_t(h3) << 16);
@@ -414,7 +510,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       }
       if (valid) {
         *reinterpret_cast<uint32_t*>(a.qjl + vec * 16 + 4 * g) = bits;
-        if (g == 0) a.gammas[vec] = sqrtf(r2);
+        if (g == 0) a.gammas[vec] = sqrtf(r2) * up;
       }
     }
   }
