@@ -303,11 +303,12 @@ constexpr int kCopies = 32;
 //   value pairs: entry e in row e at byte 4c (the lower half of the row), so
 //     that one byte permute forms the address (entry in bits 8..15, 4c in
 //     bits 0..7);
-//   3-bit key pairs: entry e in row e at byte 128 + 4c;
-//   sketch nibbles: entry e in rows 64 + 2e + c/16 at byte 128 + 8(c % 16).
+//   3-bit key pairs: entry e in row e at byte 128 + 4c.
+// The sketch-nibble table (8 bytes per copy) lives in its own 4 KiB array,
+// entry e of copy c at byte 256e + 8c: the upper halves of the rows above
+// only reach half of the banks.
 constexpr int kTabBytes = 256 * 256;
 constexpr uint32_t kTabK = 128;
-constexpr uint32_t kTabQ = 64 * 256 + 128;
 
 // Key tables. Each entry covers a group of codes (pairs for 3 and 4 bits,
 // quads for 2, octets for 1) and holds their fp16 centroids c·64σ packed in
@@ -353,12 +354,12 @@ __device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 
 
 // Sketch operand of K-step S: the 8 sign bits of the step, as fp16 ±1 (bit
 // set → +1), from a private table of the 16 nibbles (2 dwords per entry;
-// entry e of copy c at byte 512e + lane8, lane8 = kTabQ + 256(c/16) + 8(c%16)).
+// entry e of copy c at byte 256e + 8c).
 template <int S>
 __device__ __forceinline__ u32x4 sign_operand(uint32_t qw, const uint8_t* lut, uint32_t lane8) {
   const uint32_t w[1] = {qw};
-  const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S, 4, 9>(w) + lane8));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S + 4, 4, 9>(w) + lane8));
+  const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S, 4, 8>(w) + lane8));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S + 4, 4, 8>(w) + lane8));
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
@@ -846,6 +847,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   using KL = KLut<BK>;
   __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
+  __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
   __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
   // Per wavefront: the stage ring, large enough to hold the 16 x 128 fp32
   // accumulator rows in the epilogue.
@@ -897,7 +899,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
       const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
       const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
       const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
-      *reinterpret_cast<uint32_t*>(tab + kTabQ + 512 * e + 256 * (c >> 4) + 8 * (c & 15) + 4 * w) = s0 | (s1 << 16);
+      *reinterpret_cast<uint32_t*>(lut_q + 256 * e + 8 * c + 4 * w) = s0 | (s1 << 16);
     }
   }
   {
@@ -914,10 +916,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   Luts T;
   const uint32_t cp = lane & 31;            // private copy of this lane
   T.k = KL::priv ? tab : lut_k;
-  T.q = tab;
+  T.q = lut_q;
   T.v = tab;
   T.klane = KL::priv ? kTabK + 4u * cp : 0u;
-  T.qlane = kTabQ + 256u * (cp >> 4) + 8u * (cp & 15);
+  T.qlane = 8u * cp;
   T.vlane = 4u * cp;
   const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
 
