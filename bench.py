@@ -7,9 +7,10 @@ values TurboQuant-mse at 4 bits; bf16 N(0,1) synthetic K/V (seeded). Plus the
 prefill-scale encode sweep over 2^20 tokens x 8 heads.
 
 One step = one pass of the whole hot path on resident inputs: encode the new
-token's key and value of every (batch, KV head) and append them to the packed
-cache (tq_encode with output slots), then decode attention of every query head
-over the 131072-token packed cache (tq_attn_decode). Steps rotate over three
+token's key and value of every (batch, KV head), append them to the packed
+cache, then decode attention of every query head over the 131072-token packed
+cache (tq_decode_step: the appends and the query operands in one launch, then
+the split attention and the merge). Steps rotate over three
 copies of the packed cache, so no step finds its cache in the 256 MB
 last-level cache.
 
@@ -166,24 +167,23 @@ def main():
     g = np.random.default_rng(cfg.seed_base + 5)
     knew = torch.from_numpy(synth.round_bf16(g.standard_normal((B * Hkv, d)).astype(np.float32))).to(torch.bfloat16).to(dev)
     vnew = torch.from_numpy(synth.round_bf16(g.standard_normal((B * Hkv, d)).astype(np.float32))).to(torch.bfloat16).to(dev)
-    slots = (torch.arange(B * Hkv, dtype=torch.int64, device=dev) * T + (T - 1))
     dec = TA.Decoder(B, Hq, Hkv, T, dev)
     out = torch.empty_like(q)
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
     def step(i, ev=None):
+        # tq_decode_step: the new token of every (batch, KV head) goes to slot
+        # T - 1 (ctx_lens = NULL: every row is T long), then attention.
         kc, vc = kcs[i % ncopy], vcs[i % ncopy]
-        TA.encode(kq, knew, kc, slots)
-        TA.encode(vq, vnew, vc, slots)
         if ev is None:
-            dec(kq, vq, q, kc, vc, out=out)
+            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out)
         else:
-            dec(kq, vq, q, kc, vc, out=out, phase=1)
+            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out, phase=1)
             ev[0].record()
-            dec(kq, vq, q, kc, vc, out=out, phase=2)
+            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out, phase=2)
             ev[1].record()
-            dec(kq, vq, q, kc, vc, out=out, phase=3)
+            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out, phase=3)
 
     if args.copy_calibration:
         src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)

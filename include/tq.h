@@ -218,6 +218,46 @@ int tq_attn_decode_phase(int phase, const tq_quantizer* kq, const tq_quantizer* 
                          int64_t max_ctx, const tq_packed* k_cache, const tq_packed* v_cache,
                          float scale, float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * tq_decode_step — one online decode step: append the new key and value of
+ * every (batch, KV head) to the packed caches, then decode attention over
+ * the caches including them. Each token is compressed as it arrives and
+ * attention reads the compressed cache ([WY] section 5, KV-cache
+ * compression online; [B31] section "KV Cache: The problem").
+ *   k_new, v_new  device rows of d values, dtype x_dtype (TQ_F32 or
+ *                 TQ_BF16): row b*Hkv + kv (kv < Hkv) at x_row_stride*row
+ *                 elements, 16-byte aligned; x_row_stride >= d, multiple of 8
+ *   ctx_lens      device int32[B] or NULL (all max_ctx): the lengths AFTER
+ *                 the append. The new rows of batch b are encoded exactly as
+ *                 tq_encode encodes them and written to token slot
+ *                 ctx_lens[b] - 1; a batch whose length is outside
+ *                 [1, max_ctx] gets no write.
+ *   other arguments as tq_attn_decode (same workspace size).
+ * The result equals tq_encode of the new rows into those slots followed by
+ * tq_attn_decode, bit for bit; the appends and the query operands share one
+ * launch, so the step takes three launches instead of five.
+ * Errors: as tq_attn_decode and tq_encode (TQ_ERR_INVALID_ARG for null or
+ * misaligned rows or a bad stride, TQ_ERR_UNSUPPORTED for another dtype).
+ */
+int tq_decode_step(const tq_quantizer* kq, const tq_quantizer* vq, const void* k_new,
+                   const void* v_new, int x_dtype, int64_t x_row_stride, const float* query,
+                   int B, int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx,
+                   const tq_packed* k_cache, const tq_packed* v_cache, float scale, float* out,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * tq_decode_step_phase — one of tq_decode_step's three launches (same
+ * arguments and checks): phase 1 appends the new rows and forms the query
+ * operands, phases 2 and 3 are those of tq_attn_decode_phase. Running 1, 2, 3
+ * in order on one stream equals tq_decode_step.
+ * Errors: as tq_decode_step, plus TQ_ERR_INVALID_ARG for another phase value.
+ */
+int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_quantizer* vq,
+                         const void* k_new, const void* v_new, int x_dtype, int64_t x_row_stride,
+                         const float* query, int B, int Hq, int Hkv, const int32_t* ctx_lens,
+                         int64_t max_ctx, const tq_packed* k_cache, const tq_packed* v_cache,
+                         float scale, float* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* tq_status_string(int status);
 

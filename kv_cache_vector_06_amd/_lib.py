@@ -26,7 +26,7 @@ TQ_HEAD_DIM = 128
 # Every function include/tq.h declares.
 EXPORTED = ("tq_codebook", "tq_prep_bytes", "tq_prepare", "tq_encode",
             "tq_attn_decode_workspace", "tq_attn_decode", "tq_attn_decode_phase",
-            "tq_status_string")
+            "tq_decode_step", "tq_decode_step_phase", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -75,6 +75,12 @@ def load() -> ctypes.CDLL:
     lib.tq_attn_decode.restype = I
     lib.tq_attn_decode_phase.argtypes = [I] + lib.tq_attn_decode.argtypes
     lib.tq_attn_decode_phase.restype = I
+    lib.tq_decode_step.argtypes = [ctypes.POINTER(tq_quantizer), ctypes.POINTER(tq_quantizer), P, P, I, I64,
+                                   P, I, I, I, P, I64, ctypes.POINTER(tq_packed),
+                                   ctypes.POINTER(tq_packed), ctypes.c_float, P, P, SZ, P]
+    lib.tq_decode_step.restype = I
+    lib.tq_decode_step_phase.argtypes = [I] + lib.tq_decode_step.argtypes
+    lib.tq_decode_step_phase.restype = I
     lib.tq_status_string.argtypes = [I]
     lib.tq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -137,3 +143,25 @@ def tq_attn_decode_phase(phase: int, kq: tq_quantizer, vq: tq_quantizer, query: 
                                        int(Hq), int(Hkv), ctx_lens, int(max_ctx), ctypes.byref(k_cache),
                                        ctypes.byref(v_cache), float(scale), out, workspace,
                                        int(ws_bytes), stream), "tq_attn_decode_phase")
+
+
+def tq_decode_step(kq: tq_quantizer, vq: tq_quantizer, k_new: int, v_new: int, x_dtype: int,
+                   x_row_stride: int, query: int, B: int, Hq: int, Hkv: int, ctx_lens: int | None,
+                   max_ctx: int, k_cache: tq_packed, v_cache: tq_packed, scale: float, out: int,
+                   workspace: int, ws_bytes: int, stream: int | None) -> None:
+    _check(load().tq_decode_step(ctypes.byref(kq), ctypes.byref(vq), k_new, v_new, int(x_dtype),
+                                 int(x_row_stride), query, int(B), int(Hq), int(Hkv), ctx_lens,
+                                 int(max_ctx), ctypes.byref(k_cache), ctypes.byref(v_cache), float(scale),
+                                 out, workspace, int(ws_bytes), stream), "tq_decode_step")
+
+
+def tq_decode_step_phase(phase: int, kq: tq_quantizer, vq: tq_quantizer, k_new: int, v_new: int,
+                         x_dtype: int, x_row_stride: int, query: int, B: int, Hq: int, Hkv: int,
+                         ctx_lens: int | None, max_ctx: int, k_cache: tq_packed, v_cache: tq_packed,
+                         scale: float, out: int, workspace: int, ws_bytes: int,
+                         stream: int | None) -> None:
+    _check(load().tq_decode_step_phase(int(phase), ctypes.byref(kq), ctypes.byref(vq), k_new, v_new,
+                                       int(x_dtype), int(x_row_stride), query, int(B), int(Hq), int(Hkv),
+                                       ctx_lens, int(max_ctx), ctypes.byref(k_cache), ctypes.byref(v_cache),
+                                       float(scale), out, workspace, int(ws_bytes), stream),
+           "tq_decode_step_phase")

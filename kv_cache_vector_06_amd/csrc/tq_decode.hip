@@ -36,6 +36,7 @@
 
 #include "tq.h"
 #include "tq_device.h"
+#include "tq_rowtile.h"
 
 int tq_check_quantizer(const tq_quantizer* q);
 
@@ -93,13 +94,16 @@ struct PrepArgs {
   uint8_t* ws;
 };
 
-// One wavefront per unit. q' = Π_K q and q_S = S q = S'·q' (S' = S·Πᵀ) run on
-// the matrix cores with the key quantizer's prepared operands, in the
-// encoder's three-pass form (fp16 hi/lo of the matrix times fp16 hi/lo of the
-// power-of-two-scaled vector, fp32 sums), so both are fp32-accurate. Columns n
-// and n + 8 carry head n % 8; lane (n, g) ends up holding rotated dims
-// 32g..32g+31 of its column, which is exactly its share of the split kernel's
-// B operands.
+__device__ __forceinline__ int max_exponent(float (&v)[32]) {
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 32; ++q) m = fmaxf(m, fabsf(v[q]));
+  m = max4g(m);
+  int ex = 0;
+  if (m > 0.f) frexpf(m, &ex);
+  return ex;
+}
+
 __device__ __forceinline__ void split_pairs(const float (&v)[32], u32x4 (&hi)[4], u32x4 (&lo)[4]) {
   // v[q], q = 8s + 2k + h  ->  K-step s, dword k, half h
 #pragma unroll
@@ -114,64 +118,49 @@ __device__ __forceinline__ void split_pairs(const float (&v)[32], u32x4 (&hi)[4]
     }
 }
 
-// Σ_s A(t, s)·B(s) over the three hi/lo passes for the 8 row tiles; element j
-// of tile t is output row 32g + 4t + j of this lane's column.
-__device__ __forceinline__ void frag_matvec(const u32x4* frag, int lane, const u32x4 (&bh)[4],
-                                            const u32x4 (&bl)[4], float (&y)[32]) {
-  // the 8 row tiles' accumulation chains are interleaved
-  f32x4 acc[8];
+// Four values of one column into the two dwords of fp16 pairs (v0, v1),
+// (v2, v3) after scaling by scl: the hi parts, or the lo parts.
+__device__ __forceinline__ u32x2 hilo_pairs(const float (&v)[4], float scl, bool hi) {
+  uint16_t h[4], l[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 ah = frag[frag_index(0, t, s) * 64 + lane];
-      const u32x4 al = frag[frag_index(1, t, s) * 64 + lane];
-      acc[t] = mfma(ah, bh[s], acc[t]);
-      acc[t] = mfma(al, bh[s], acc[t]);
-      acc[t] = mfma(ah, bl[s], acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) y[4 * t + j] = acc[t][j];
+  for (int j = 0; j < 4; ++j) split_h(v[j] * scl, h[j], l[j]);
+  return hi ? u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)}
+            : u32x2{uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16)};
 }
 
-__device__ __forceinline__ int max_exponent(float (&v)[32]) {
-  float m = 0.f;
-#pragma unroll
-  for (int q = 0; q < 32; ++q) m = fmaxf(m, fabsf(v[q]));
-  m = max4g(m);
-  int ex = 0;
-  if (m > 0.f) frexpf(m, &ex);
-  return ex;
-}
-
-constexpr int kPrepWaves = 4;     // units per workgroup; they share the staged operands
-
-__global__ __launch_bounds__(kPrepWaves * 64) void query_prep_kernel(PrepArgs a) {
-  __shared__ u32x4 lds_f[2 * kFragsPerSet * 64];       // 16Π, then S' (128 KiB)
-  {
-    // direct-to-LDS copy of the operand fragments, all loads before one wait
-    const int ln = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.kh) + kPrepHeaderBytes);
-    const int chunks = (a.proj != nullptr ? 2 : 1) * kFragsPerSet;
-    for (int c = wv; c < chunks; c += kPrepWaves)
-      __builtin_amdgcn_global_load_lds(src + c * 64 + ln, TQ_LDS(lds_f + c * 64), 16, 0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  const int unit = blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
-  if (unit >= a.units) return;
+// Query operands of one unit, row-tile parallel: a workgroup of 8 wavefronts
+// per unit, wavefront t forming rotated dims 32g + 4t + j (j < 4) of every
+// column. q' = Π_K q and q_S = S q = S'·q' (S' = S·Πᵀ) run on the matrix cores
+// with the key quantizer's prepared fragments, each in three hi/lo passes
+// (fp16 hi/lo of the matrix times fp16 hi/lo of the power-of-two-scaled
+// vector, fp32 sums), so both are fp32-accurate. The column maxima and the
+// sketch's B operand meet in LDS. Columns n and n + 8 carry head n % 8: hi
+// parts in n < 8, lo parts in n >= 8, so one pass of the split kernel's
+// matrix cores gives both.
+__device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X) {
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
   const int b = unit / (a.ngroups * a.Hkv);
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, c = n & 7;
+  const int n = lane & 15, g = lane >> 4, c = n & 7;
   const bool live = c < gc;
-  const u32x4* frag = lds_f;
+  const bool prod = a.proj != nullptr;
+  const u32x4* frag = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.kh) + kPrepHeaderBytes);
+  u32x4 rh[4], rl[4], ph[4], pl[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    rh[s] = frag[frag_index(0, t, s) * 64 + lane];
+    rl[s] = frag[frag_index(1, t, s) * 64 + lane];
+  }
+  if (prod) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ph[s] = frag[(kFragsPerSet + frag_index(0, t, s)) * 64 + lane];
+      pl[s] = frag[(kFragsPerSet + frag_index(1, t, s)) * 64 + lane];
+    }
+  }
   // B operand of the rotation: slot 8s + j of this lane is dim 32s + 8g + j.
   float xv[32];
   {
@@ -192,61 +181,109 @@ __global__ __launch_bounds__(kPrepWaves * 64) void query_prep_kernel(PrepArgs a)
   for (int q = 0; q < 32; ++q) xv[q] = ldexpf(xv[q], -ex);
   u32x4 bh[4], bl[4];
   split_pairs(xv, bh, bl);
-  float qp[32];                                   // q' = Π q, dims 32g + q
-  frag_matvec(frag, lane, bh, bl, qp);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < 32; ++q) qp[q] = ldexpf(qp[q], ex) * (1.0f / kRotScale);
-  float qs[32];                                   // q_S = S q, dims 32g + q
+  for (int s = 0; s < 4; ++s) {
+    acc = mfma(rh[s], bh[s], acc);
+    acc = mfma(rl[s], bh[s], acc);
+    acc = mfma(rh[s], bl[s], acc);
+  }
+  float qp[4], qs[4];                            // dims 32g + 4t + j
 #pragma unroll
-  for (int q = 0; q < 32; ++q) qs[q] = 0.f;
-  if (a.proj != nullptr) {
-    // B operand of the sketch: K-step s, lane group g holds dims 32g + 8s + j,
-    // which this lane computed itself.
-    float y[32];
-    const int e2 = max_exponent(qp);
+  for (int j = 0; j < 4; ++j) {
+    qp[j] = ldexpf(acc[j], ex) * (1.0f / kRotScale);
+    qs[j] = 0.f;
+  }
+  if (prod) {
+    // B operand of the sketch: q' scaled by 2^-e2 (max|q'| = m·2^e2), split
+    // hi/lo; K-step s, dword k of lane group g is dims 32g + 8s + 2k, +1.
+    float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) y[q] = ldexpf(qp[q], -e2);
-    split_pairs(y, bh, bl);
-    frag_matvec(frag + kFragsPerSet * 64, lane, bh, bl, qs);
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(qp[j]));
+    m = max4g(m);
+    if (g == 0) X.red[0][t][n] = m;
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) m = fmaxf(m, X.red[0][tt][n]);
+    int e2 = 0;
+    if (m > 0.f) frexpf(m, &e2);
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = ldexpf(qp[j], -e2);
+    X.b[0][t][lane] = hilo_pairs(y, 1.0f, true);
+    X.b[1][t][lane] = hilo_pairs(y, 1.0f, false);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x2 e0 = X.b[0][2 * s][lane], e1 = X.b[0][2 * s + 1][lane];
+      const u32x2 f0 = X.b[1][2 * s][lane], f1 = X.b[1][2 * s + 1][lane];
+      bh[s] = u32x4{e0[0], e0[1], e1[0], e1[1]};
+      bl[s] = u32x4{f0[0], f0[1], f1[0], f1[1]};
+    }
+    f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      z = mfma(ph[s], bh[s], z);
+      z = mfma(pl[s], bh[s], z);
+      z = mfma(ph[s], bl[s], z);
+    }
     const float inv = 1.0f / a.kh->sp_scale;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) qs[q] = ldexpf(qs[q], e2) * inv;
+    for (int j = 0; j < 4; ++j) qs[j] = ldexpf(z[j], e2) * inv;
   }
   // score = log2(e)·scale·n·(⟨Πq, c⟩ + √(π/2)/d·γ·⟨Sq, s⟩); centroids enter ×64σ.
   const float fk = a.scale * kLog2e / (kCentScale * a.kh->sigma);
   const float fs = a.scale * kLog2e * 1.2533141373155003f / kD;       // √(π/2)/d
   float m = 0.f;
 #pragma unroll
-  for (int q = 0; q < 32; ++q) {
-    qp[q] *= fk;
-    qs[q] *= fs;
-    m = fmaxf(m, fmaxf(fabsf(qp[q]), fabsf(qs[q])));
+  for (int j = 0; j < 4; ++j) {
+    qp[j] *= fk;
+    qs[j] *= fs;
+    m = fmaxf(m, fmaxf(fabsf(qp[j]), fabsf(qs[j])));
   }
   // One power-of-two scale per head for both operands (the split kernel adds
   // the sketch term before scaling back), putting max|·| in [2^9, 2^10).
   m = max4g(m);
+  if (g == 0) X.red[1][t][n] = m;
+  __syncthreads();
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) m = fmaxf(m, X.red[1][tt][n]);
   int e3 = 0;
   if (m > 0.f) frexpf(m, &e3);
   const float scl = m > 0.f ? ldexpf(1.0f, 10 - e3) : 1.0f;
   // Fragment f (f < 4: q', K-step f; f >= 4: q_S, K-step f - 4), lane (n, g),
-  // slot j: dim 32g + 8(f%4) + j; column n < 8 takes the fp16 hi part, column
-  // n + 8 the lo part, so one matrix-core pass gives both.
+  // slot j holds dim 32g + 8(f%4) + j: this wavefront's dims are dwords
+  // 2(t%2), 2(t%2) + 1 of fragments t/2 and 4 + t/2.
   uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   u32x4* fr = reinterpret_cast<u32x4*>(blk);
-#pragma unroll
-  for (int f = 0; f < kQFrags; ++f) {
-    const float* v = f < 4 ? qp : qs;
-    u32x4 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint16_t h0, l0, h1, l1;
-      split_h(v[8 * (f & 3) + 2 * k] * scl, h0, l0);
-      split_h(v[8 * (f & 3) + 2 * k + 1] * scl, h1, l1);
-      o[k] = n < 8 ? (uint32_t(h0) | (uint32_t(h1) << 16)) : (uint32_t(l0) | (uint32_t(l1) << 16));
-    }
-    fr[f * 64 + lane] = o;
-  }
-  if (g == 0 && n < kMaxHeads) reinterpret_cast<float*>(blk + kQFrags * 1024)[n] = live ? 1.0f / scl : 0.f;
+  reinterpret_cast<u32x2*>(fr + (t >> 1) * 64 + lane)[t & 1] = hilo_pairs(qp, scl, n < 8);
+  reinterpret_cast<u32x2*>(fr + (4 + (t >> 1)) * 64 + lane)[t & 1] = hilo_pairs(qs, scl, n < 8);
+  if (t == 0 && g == 0 && n < kMaxHeads) reinterpret_cast<float*>(blk + kQFrags * 1024)[n] = live ? 1.0f / scl : 0.f;
+}
+
+__global__ __launch_bounds__(kRowWaves * 64) void query_prep_kernel(PrepArgs a) {
+  __shared__ RowXchg X;
+  row_prep(a, blockIdx.x, X);
+}
+
+// A decode step's small work in one launch: workgroups [0, ktiles) append the
+// new keys, the next vtiles the new values (row-tile encoders, one 16-row tile
+// each), the last `units` form the query operands.
+struct StepArgs {
+  PrepArgs prep;
+  RowEncArgs kenc, venc;
+  int ktiles, vtiles;
+};
+
+__global__ __launch_bounds__(kRowWaves * 64) void step_prologue_kernel(StepArgs a) {
+  __shared__ RowXchg X;
+  const int bid = blockIdx.x;
+  if (bid < a.ktiles)
+    row_encode(a.kenc, bid, X);
+  else if (bid < a.ktiles + a.vtiles)
+    row_encode(a.venc, bid - a.ktiles, X);
+  else
+    row_prep(a.prep, bid - a.ktiles - a.vtiles, X);
 }
 
 // ---------------------------------------------------------------------------
@@ -1151,10 +1188,45 @@ extern "C" size_t tq_attn_decode_workspace(int B, int Hq, int Hkv, int64_t max_c
 
 namespace {
 
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The new key and value rows of a decode step (null for plain decode).
+struct StepRows {
+  const void* k_new;
+  const void* v_new;
+  int x_dtype;
+  int64_t x_row_stride;
+};
+
+RowEncArgs append_args(const tq_quantizer* q, const StepRows& r, const void* x, int rows, const int32_t* ctx_lens,
+                       int64_t max_ctx, int Hkv, const tq_packed* cache) {
+  RowEncArgs e{};
+  const bool prod = q->variant == TQ_PROD;
+  e.x = x;
+  e.n = rows;
+  e.stride = r.x_row_stride;
+  e.f32in = r.x_dtype == TQ_F32;
+  e.bm = prod ? q->bits - 1 : q->bits;
+  e.prod = prod;
+  e.codes = cache->codes;
+  e.norms = cache->norms;
+  e.qjl = cache->qjl;
+  e.gammas = cache->gammas;
+  e.frags = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(q->prep) + kPrepHeaderBytes);
+  e.centroids = q->centroids;
+  e.boundaries = q->boundaries;
+  e.slot = nullptr;
+  e.lens = ctx_lens;
+  e.max_ctx = max_ctx;
+  e.hkv = Hkv;
+  e.append = 1;
+  return e;
+}
+
 int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const float* query, int B,
                 int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx, const tq_packed* k_cache,
                 const tq_packed* v_cache, float scale, float* out, void* workspace, size_t ws_bytes,
-                void* stream) {
+                void* stream, const StepRows* step = nullptr) {
   if (phase < 0 || phase > 3) return TQ_ERR_INVALID_ARG;
   int st = tq_check_quantizer(kq);
   if (st != TQ_OK) return st;
@@ -1173,6 +1245,16 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   if ((reinterpret_cast<uintptr_t>(k_cache->codes) | reinterpret_cast<uintptr_t>(v_cache->codes) |
        reinterpret_cast<uintptr_t>(prod ? k_cache->qjl : nullptr)) % 16 != 0)
     return TQ_ERR_INVALID_ARG;
+  if (step != nullptr) {
+    // The appended rows are written through the same pointers.
+    if (step->x_dtype != TQ_F32 && step->x_dtype != TQ_BF16) return TQ_ERR_UNSUPPORTED;
+    if (step->k_new == nullptr || step->v_new == nullptr || !aligned(step->k_new, 16) ||
+        !aligned(step->v_new, 16) || step->x_row_stride < TQ_HEAD_DIM || step->x_row_stride % 8 != 0)
+      return TQ_ERR_INVALID_ARG;
+    if (!aligned(k_cache->norms, 4) || !aligned(v_cache->norms, 4) || (prod && !aligned(k_cache->gammas, 4)))
+      return TQ_ERR_INVALID_ARG;
+    if (int64_t(B) * Hkv > (int64_t(1) << 30)) return TQ_ERR_UNSUPPORTED;
+  }
   const Plan p = make_plan(B, Hq, Hkv, max_ctx);
   if (ws_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1183,8 +1265,17 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   if (phase == 0 || phase == 1) {
     PrepArgs pa{query, kq->rot, prod ? kq->proj : nullptr, static_cast<const PrepHeader*>(kq->prep), scale,
                 Hq, Hkv, G, p.ngroups, p.units, ws};
-    hipLaunchKernelGGL(query_prep_kernel, dim3((p.units + kPrepWaves - 1) / kPrepWaves), dim3(kPrepWaves * 64), 0,
-                       s, pa);
+    if (step == nullptr) {
+      hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
+    } else {
+      StepArgs sa;
+      sa.prep = pa;
+      const int rows = B * Hkv;
+      sa.kenc = append_args(kq, *step, step->k_new, rows, ctx_lens, max_ctx, Hkv, k_cache);
+      sa.venc = append_args(vq, *step, step->v_new, rows, ctx_lens, max_ctx, Hkv, v_cache);
+      sa.ktiles = sa.vtiles = (rows + 15) / 16;
+      hipLaunchKernelGGL(step_prologue_kernel, dim3(sa.ktiles + sa.vtiles + p.units), dim3(kRowWaves * 64), 0, s, sa);
+    }
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   if (phase == 0 || phase == 2) {
@@ -1255,4 +1346,25 @@ extern "C" int tq_attn_decode_phase(int phase, const tq_quantizer* kq, const tq_
   if (phase < 1 || phase > 3) return TQ_ERR_INVALID_ARG;
   return decode_call(phase, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out,
                      workspace, ws_bytes, stream);
+}
+
+extern "C" int tq_decode_step(const tq_quantizer* kq, const tq_quantizer* vq, const void* k_new,
+                              const void* v_new, int x_dtype, int64_t x_row_stride, const float* query,
+                              int B, int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx,
+                              const tq_packed* k_cache, const tq_packed* v_cache, float scale, float* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  const StepRows r{k_new, v_new, x_dtype, x_row_stride};
+  return decode_call(0, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out,
+                     workspace, ws_bytes, stream, &r);
+}
+
+extern "C" int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_quantizer* vq,
+                                    const void* k_new, const void* v_new, int x_dtype, int64_t x_row_stride,
+                                    const float* query, int B, int Hq, int Hkv, const int32_t* ctx_lens,
+                                    int64_t max_ctx, const tq_packed* k_cache, const tq_packed* v_cache,
+                                    float scale, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (phase < 1 || phase > 3) return TQ_ERR_INVALID_ARG;
+  const StepRows r{k_new, v_new, x_dtype, x_row_stride};
+  return decode_call(phase, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out,
+                     workspace, ws_bytes, stream, &r);
 }

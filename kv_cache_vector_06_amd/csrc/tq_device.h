@@ -32,6 +32,7 @@ constexpr int kFragsPerSet = 2 * 8 * 4;               // (part, t, s)
 constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB
 constexpr size_t kPrepBytes = kPrepHeaderBytes + 2 * kSetBytes;
 constexpr float kRotScale = 16.0f;                    // |Π| <= 1 → |16Π| <= 16
+constexpr float kResScale = 64.0f;                    // residual scale of the sketch operand
 
 __host__ __device__ constexpr int frag_index(int part, int t, int s) { return (part * 8 + t) * 4 + s; }
 

@@ -22,10 +22,10 @@
 
 #include "tq.h"
 #include "tq_device.h"
+#include "tq_rowtile.h"
 
 namespace tq {
 
-constexpr float kResScale = 64.0f;                    // residual scale for the sketch
 
 // ---------------------------------------------------------------------------
 // tq_prepare: fragment the rotation (and S' = S·Πᵀ) into matrix-core A operands
@@ -516,6 +516,15 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   }
 }
 
+// Encodes of at most this many 16-row tiles take the row-tile-parallel form:
+// one workgroup per tile, no staging of the fragments in LDS.
+constexpr int64_t kRowTileMax = 64;
+
+__global__ __launch_bounds__(kRowWaves * 64) void row_encode_kernel(RowEncArgs a) {
+  __shared__ RowXchg X;
+  row_encode(a, blockIdx.x, X);
+}
+
 template <int BM, bool PROD>
 hipError_t launch_encode_t(const EncodeArgs& a, bool f32in, int grid, hipStream_t st) {
   if (f32in)
@@ -600,11 +609,30 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
   a.boundaries = q->boundaries;
   a.slot = out_slot;
   const int64_t tiles = (n + 15) / 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (tiles <= kRowTileMax) {
+    RowEncArgs r{};
+    r.x = x;
+    r.n = n;
+    r.stride = x_row_stride;
+    r.f32in = x_dtype == TQ_F32;
+    r.bm = bm;
+    r.prod = prod;
+    r.codes = out->codes;
+    r.norms = out->norms;
+    r.qjl = out->qjl;
+    r.gammas = out->gammas;
+    r.frags = a.prep;
+    r.centroids = q->centroids;
+    r.boundaries = q->boundaries;
+    r.slot = out_slot;
+    hipLaunchKernelGGL(row_encode_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kRowWaves * 64), 0, s, r);
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+  }
   const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
   const int cap = device_cus() * (prod ? 1 : 2);
   const int grid = static_cast<int>(want < cap ? want : cap);
   const bool f32 = x_dtype == TQ_F32;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (!prod) {
     switch (bm) {

@@ -108,3 +108,34 @@ class Decoder:
         else:
             L.tq_attn_decode_phase(phase, *args)
         return out
+
+    def step(self, kq: Quantizer, vq: Quantizer, k_new: torch.Tensor, v_new: torch.Tensor,
+             query: torch.Tensor, kc: Packed, vc: Packed, ctx_lens: torch.Tensor | None = None,
+             scale: float | None = None, out: torch.Tensor | None = None, phase: int = 0) -> torch.Tensor:
+        """One decode step: append k_new/v_new ([B, Hkv, d] or [B*Hkv, d], float32
+        or bfloat16, unit column stride) at token ctx_lens[b] - 1 of each cache,
+        then attend (tq_decode_step)."""
+        B, Hq, d = query.shape
+        if (B, Hq) != (self.B, self.Hq) or query.dtype != torch.float32 or not query.is_contiguous():
+            raise ValueError("query must be contiguous float32 [B, Hq, d] of the decoder's shape")
+        if ctx_lens is not None and (ctx_lens.dtype != torch.int32 or ctx_lens.numel() != B):
+            raise ValueError("ctx_lens must be int32[B]")
+        rows = []
+        for x in (k_new, v_new):
+            x2 = x.reshape(-1, x.shape[-1])
+            if x2.shape != (B * self.Hkv, d) or x2.stride(1) != 1 or x.dtype != k_new.dtype:
+                raise ValueError("new rows must be [B*Hkv, d] with unit column stride and one dtype")
+            rows.append(x2)
+        if rows[0].stride(0) != rows[1].stride(0):
+            raise ValueError("k_new and v_new must share a row stride")
+        dt = {torch.float32: L.TQ_F32, torch.bfloat16: L.TQ_BF16}[k_new.dtype]
+        out = out if out is not None else torch.empty_like(query)
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        args = (kq.c, vq.c, rows[0].data_ptr(), rows[1].data_ptr(), dt, rows[0].stride(0), query.data_ptr(),
+                B, Hq, self.Hkv, _ptr(ctx_lens), self.max_ctx, kc.c, vc.c, scale, out.data_ptr(),
+                self.ws.data_ptr(), self.ws_bytes, _stream())
+        if phase == 0:
+            L.tq_decode_step(*args)
+        else:
+            L.tq_decode_step_phase(phase, *args)
+        return out

@@ -135,3 +135,35 @@ def quantizers(cfg):
     kq = T.Quantizer(Rk, cfg.k_bits, cfg.k_variant, S if cfg.k_variant == "prod" else None, DEV)
     vq = T.Quantizer(Rv, cfg.v_bits, "mse", None, DEV)
     return kq, vq, Rk, Rv, S
+
+
+def _near_ties(enc, bits, variant):
+    """Rows whose oracle encode has a rotated coordinate within 1e-6 of a
+    boundary or a sketch value within 1e-6 of zero: there a different but
+    equally valid code or bit is allowed, and with few tokens one such flip
+    moves the attention output by up to ~1e-2."""
+    bm = bits - 1 if variant == "prod" else bits
+    bad = np.zeros(enc["norms"].shape[0], bool)
+    if bm > 0:
+        t = book(bm)[1]
+        bad |= (np.min(np.abs(enc["y"][..., None] - t), axis=-1) < 1e-6).any(axis=1)
+    if variant == "prod":
+        bad |= (np.abs(enc["z"]) < 1e-6).any(axis=1)
+    return np.nonzero(bad)[0]
+
+
+def encode_away_from_ties(X, rot, proj, bits, variant, seed, dtype):
+    """Oracle encode of X; rows near a tie are redrawn (in place) until none
+    is. Uses the oracle only; the HIP path then encodes the same rows."""
+    enc = oracle_encode(X, rot, proj, bits, variant)
+    g = np.random.default_rng(seed)
+    for _ in range(20):
+        rows = _near_ties(enc, bits, variant)
+        if rows.size == 0:
+            return enc
+        new = X[rows] * (1 + 0.01 * g.standard_normal(X[rows].shape)).astype(np.float32)
+        X[rows] = synth.round_bf16(new) if dtype == "bf16" else new
+        sub = oracle_encode(X[rows], rot, proj, bits, variant)
+        for k in enc:
+            enc[k][rows] = sub[k]
+    raise AssertionError("could not move rows away from ties")

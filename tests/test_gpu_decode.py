@@ -9,7 +9,7 @@ import torch
 
 import synth
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import (DEV, book, check_encode, gpu_packed_arrays, oracle_dequant, oracle_encode,
+from gpu_util import (DEV, check_encode, encode_away_from_ties, gpu_packed_arrays, oracle_dequant,
                       packed_from_oracle, quantizers, rel_l2_per_head, say, to_gpu_x)
 from oracle import decode_attention
 
@@ -19,38 +19,6 @@ TOL = 1e-3
 
 def _flat(x):
     return x.reshape(-1, x.shape[-1])
-
-
-def _near_ties(enc, bits, variant):
-    """Rows whose oracle encode has a rotated coordinate within 1e-6 of a
-    boundary or a sketch value within 1e-6 of zero: there a different but
-    equally valid code or bit is allowed, and with few tokens one such flip
-    moves the attention output by up to ~1e-2."""
-    bm = bits - 1 if variant == "prod" else bits
-    bad = np.zeros(enc["norms"].shape[0], bool)
-    if bm > 0:
-        t = book(bm)[1]
-        bad |= (np.min(np.abs(enc["y"][..., None] - t), axis=-1) < 1e-6).any(axis=1)
-    if variant == "prod":
-        bad |= (np.abs(enc["z"]) < 1e-6).any(axis=1)
-    return np.nonzero(bad)[0]
-
-
-def encode_away_from_ties(X, rot, proj, bits, variant, seed, dtype):
-    """Oracle encode of X; rows near a tie are redrawn (in place) until none
-    is. Uses the oracle only; the HIP path then encodes the same rows."""
-    enc = oracle_encode(X, rot, proj, bits, variant)
-    g = np.random.default_rng(seed)
-    for _ in range(20):
-        rows = _near_ties(enc, bits, variant)
-        if rows.size == 0:
-            return enc
-        new = X[rows] * (1 + 0.01 * g.standard_normal(X[rows].shape)).astype(np.float32)
-        X[rows] = synth.round_bf16(new) if dtype == "bf16" else new
-        sub = oracle_encode(X[rows], rot, proj, bits, variant)
-        for k in enc:
-            enc[k][rows] = sub[k]
-    raise AssertionError("could not move rows away from ties")
 
 
 def run_case(cfg, T_ctx, B, lens=None, end_to_end=True):

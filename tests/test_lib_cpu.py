@@ -113,3 +113,37 @@ def test_argument_errors_are_synchronous():
         assert lib.tq_attn_decode_phase(ph, a["kq"], a["vq"], a["query"], a["B"], a["Hq"], a["Hkv"], a["lens"],
                                         a["T"], a["kc"], a["vc"], a["scale"], a["out"], a["ws"], a["wsb"],
                                         None) == L.TQ_ERR_INVALID_ARG
+
+
+def test_decode_step_argument_errors_are_synchronous():
+    lib = L.load()
+    q = _fake_quantizer()
+    pk = L.tq_packed(1 << 20, 1 << 20, None, None)
+    byref = ctypes.byref
+    ws = L.tq_attn_decode_workspace(2, 32, 8, 1000)
+    base = dict(kq=byref(q), vq=byref(q), kn=1 << 20, vn=1 << 21, dt=L.TQ_BF16, stride=128, query=1 << 20,
+                B=2, Hq=32, Hkv=8, lens=None, T=1000, kc=byref(pk), vc=byref(pk), scale=0.1, out=1 << 20,
+                ws=1 << 20, wsb=ws)
+
+    def call(phase=None, **kw):
+        a = dict(base, **kw)
+        rest = (a["kq"], a["vq"], a["kn"], a["vn"], a["dt"], a["stride"], a["query"], a["B"], a["Hq"], a["Hkv"],
+                a["lens"], a["T"], a["kc"], a["vc"], a["scale"], a["out"], a["ws"], a["wsb"], None)
+        return lib.tq_decode_step(*rest) if phase is None else lib.tq_decode_step_phase(phase, *rest)
+
+    assert call(kn=None) == L.TQ_ERR_INVALID_ARG
+    assert call(vn=None) == L.TQ_ERR_INVALID_ARG
+    assert call(kn=(1 << 20) + 8) == L.TQ_ERR_INVALID_ARG          # rows must be 16-byte aligned
+    assert call(stride=100) == L.TQ_ERR_INVALID_ARG
+    assert call(stride=132) == L.TQ_ERR_INVALID_ARG
+    assert call(dt=5) == L.TQ_ERR_UNSUPPORTED
+    assert call(Hq=30) == L.TQ_ERR_INVALID_ARG
+    assert call(query=None) == L.TQ_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == L.TQ_ERR_WORKSPACE
+    prod = _fake_quantizer(bits=3, variant=L.TQ_PROD)
+    assert call(vq=byref(prod)) == L.TQ_ERR_UNSUPPORTED
+    assert call(kq=byref(prod)) == L.TQ_ERR_INVALID_ARG            # packed keys lack the sketch arrays
+    for ph in (0, 4, -1):
+        assert call(phase=ph) == L.TQ_ERR_INVALID_ARG
+    for ph in (1, 2, 3):
+        assert call(phase=ph, kn=None) == L.TQ_ERR_INVALID_ARG
