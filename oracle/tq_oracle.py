@@ -46,7 +46,7 @@ __all__ = [
     "coord_second_moment", "lloyd_max", "codebook_mse", "nearest_centroid",
     "pack_codes", "unpack_codes", "pack_signs", "unpack_signs",
     "encode_mse", "encode_prod", "dequant_mse", "dequant_prod",
-    "attention", "decode_attention",
+    "attention", "decode_attention", "fwht", "hadamard_rotate",
 ]
 
 
@@ -185,6 +185,42 @@ def unpack_signs(packed, m: int) -> np.ndarray:
     """→ [N, m] of ±1.0."""
     bits = np.unpackbits(np.asarray(packed, np.uint8), axis=1, bitorder="little")[:, :m]
     return np.where(bits == 1, 1.0, -1.0)
+
+
+# ---------------------------------------------------------------------------
+# Randomized Walsh-Hadamard rotation  ([WY] section 4.3: the WHT as the
+# efficient replacement of the dense rotation matrix)
+# ---------------------------------------------------------------------------
+
+def fwht(v):
+    """Unnormalised Walsh-Hadamard transform along the last axis: v ↦ H v with
+    H the Sylvester Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]],
+    so H[i][j] = (-1)^popcount(i & j)); the length must be a power of two.
+    Butterflies of span 1, 2, 4, ...: pairs (a, b) at distance h become
+    (a + b, a - b)."""
+    v = np.array(v, dtype=np.float64, copy=True)
+    n = v.shape[-1]
+    if n & (n - 1):
+        raise ValueError("length must be a power of two")
+    lead = v.shape[:-1]
+    h = 1
+    while h < n:
+        w = v.reshape(lead + (n // (2 * h), 2, h))
+        a = w[..., 0, :].copy()
+        b = w[..., 1, :].copy()
+        w[..., 0, :] = a + b
+        w[..., 1, :] = a - b
+        v = w.reshape(lead + (n,))
+        h *= 2
+    return v
+
+
+def hadamard_rotate(u, signs):
+    """y = H diag(s) u / √d, the randomized Hadamard rotation of the rows of u
+    (s the ±1 sign vector). It is orthogonal since H Hᵀ = d I."""
+    u = np.asarray(u, np.float64)
+    s = np.asarray(signs, np.float64)
+    return fwht(u * s) / math.sqrt(u.shape[-1])
 
 
 # ---------------------------------------------------------------------------

@@ -28,6 +28,8 @@ import numpy as np
 SEED_ROT_K = 1001
 SEED_ROT_V = 1002
 SEED_PROJ = 1003
+SEED_HAD_K = 1004
+SEED_HAD_V = 1005
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -58,6 +60,23 @@ def rotation(d: int, seed: int) -> np.ndarray:
     q, r = np.linalg.qr(g)
     q = q * np.sign(np.diag(r))[None, :]
     return np.ascontiguousarray(q, dtype=np.float32)
+
+
+def hadamard_rotation(d: int, seed: int) -> np.ndarray:
+    """Randomized Walsh-Hadamard rotation H_d·diag(s)/√d as float32 (y = R @ u):
+    H_d the Sylvester Hadamard matrix (d a power of two), s iid uniform ±1."""
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    if h.shape[0] != d:
+        raise ValueError("d must be a power of two")
+    s = rng(seed).choice(np.array([-1.0, 1.0]), size=d)
+    return np.ascontiguousarray(h * s[None, :] / np.sqrt(d), dtype=np.float32)
+
+
+def hadamard_constants(d: int = 128):
+    """(Hadamard rotation for keys, for values, QJL projection), float32."""
+    return hadamard_rotation(d, SEED_HAD_K), hadamard_rotation(d, SEED_HAD_V), projection(d, SEED_PROJ)
 
 
 def projection(d: int, seed: int) -> np.ndarray:
