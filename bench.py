@@ -18,6 +18,9 @@ Prints one JSON line. `value` is packed-cache bytes read by decode per step /
 step time (GB/s), timed without any event between the steps. `roofline` is
 for the dominant kernel (the split-attention launch), timed with HIP events
 around that launch on its stream in a second run of the same steps.
+`hadamard_step_ms` / `hadamard_value` time the same step with randomized
+Walsh-Hadamard rotations for keys and values; the encode sweep adds mse-4 and
+prod-4 with that rotation.
 """
 from __future__ import annotations
 
@@ -172,18 +175,18 @@ def main():
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    def step(i, ev=None):
+    def step(i, ev=None, qs=(kq, vq)):
         # tq_decode_step: the new token of every (batch, KV head) goes to slot
         # T - 1 (ctx_lens = NULL: every row is T long), then attention.
         kc, vc = kcs[i % ncopy], vcs[i % ncopy]
         if ev is None:
-            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out)
+            dec.step(*qs, knew, vnew, q, kc, vc, out=out)
         else:
-            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out, phase=1)
+            dec.step(*qs, knew, vnew, q, kc, vc, out=out, phase=1)
             ev[0].record()
-            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out, phase=2)
+            dec.step(*qs, knew, vnew, q, kc, vc, out=out, phase=2)
             ev[1].record()
-            dec.step(kq, vq, knew, vnew, q, kc, vc, out=out, phase=3)
+            dec.step(*qs, knew, vnew, q, kc, vc, out=out, phase=3)
 
     if args.copy_calibration:
         src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)
@@ -234,6 +237,24 @@ def main():
     flushed_us = sorted(fl)[len(fl) // 2] * 1e3
     log(f"[bench] split-attention after a read-only cache flush: median {flushed_us:.1f} us")
 
+    # The same step with randomized Walsh-Hadamard rotations for keys and
+    # values (the caches re-encoded with them).
+    Rkh, Rvh, _ = synth.hadamard_constants(d)
+    kqh = TA.Quantizer(Rkh, cfg.k_bits, cfg.k_variant, S, dev, "hadamard")
+    vqh = TA.Quantizer(Rvh, cfg.v_bits, "mse", None, dev, "hadamard")
+    for c in range(ncopy):
+        TA.encode(kqh, kg, kcs[c])
+        TA.encode(vqh, vg, vcs[c])
+    for i in range(args.warmup):
+        step(i, qs=(kqh, vqh))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, qs=(kqh, vqh))
+    torch.cuda.synchronize()
+    had_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    log(f"[bench] step with Hadamard rotations {had_ms:.4f} ms")
+
     enc = {}
     enc_roof = None
     if not args.no_encode_sweep:
@@ -241,9 +262,11 @@ def main():
         torch.cuda.empty_cache()
         n_sweep = (1 << 20) * 8
         xs = torch.cat([kg, vg])[:n_sweep]
-        for label, bits, var in (("mse1", 1, "mse"), ("mse2", 2, "mse"), ("mse3", 3, "mse"), ("mse4", 4, "mse"),
-                                 ("prod4", 4, "prod")):
-            qq = TA.Quantizer(Rk, bits, var, S if var == "prod" else None, dev)
+        for label, bits, var, rot in (("mse1", 1, "mse", "dense"), ("mse2", 2, "mse", "dense"),
+                                      ("mse3", 3, "mse", "dense"), ("mse4", 4, "mse", "dense"),
+                                      ("prod4", 4, "prod", "dense"), ("mse4_hadamard", 4, "mse", "hadamard"),
+                                      ("prod4_hadamard", 4, "prod", "hadamard")):
+            qq = TA.Quantizer(Rk if rot == "dense" else Rkh, bits, var, S if var == "prod" else None, dev, rot)
             pk = TA.Packed(qq, n_sweep, dev)
             TA.encode(qq, xs, pk)
             a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -292,6 +315,8 @@ def main():
                      "traffic": _traffic("attn_split_gqa8_prod4_128k.counters.json", "tq_decode.hip", dec_bytes),
                      "avg_launch_us": round(k_avg * 1e3, 2), "after_read_flush_us": round(flushed_us, 2),
                      "cache_copies": ncopy},
+        "hadamard_step_ms": round(had_ms, 5),
+        "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
         "encode_mvec_s": enc,
         "encode_roofline": enc_roof,
         "cpu_baseline": cpu,

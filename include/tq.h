@@ -54,6 +54,7 @@ enum tq_status {
 };
 
 enum tq_variant { TQ_MSE = 0, TQ_PROD = 1 };
+enum tq_rotation { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 };
 enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 };
 
 /* Head dimension supported by the GPU kernels. */
@@ -99,6 +100,16 @@ int tq_codebook(int d, int bits, double* centroids, double* boundaries, double* 
  *   prep       device buffer of tq_prep_bytes() bytes, 256-byte aligned,
  *              filled by tq_prepare() from the fields above before the
  *              quantizer is used by tq_encode / tq_attn_decode
+ *   rotation   TQ_ROT_DENSE (0): rot is any orthogonal matrix (the Haar-random
+ *              Π of [OM] "Trick đầu tiên…"); its fp16 hi/lo split enters the
+ *              matrix cores.
+ *              TQ_ROT_HADAMARD (1): rot is the randomized Walsh–Hadamard
+ *              rotation Π = H·diag(s)/√d (H the Sylvester Hadamard matrix,
+ *              s ∈ {±1}^d), the faster matrix alternative (WHT) that [WY]
+ *              section 4.3 names after its code listing. Only the signs of rot's
+ *              entries enter the matrix cores (H·diag(s), exact in fp16) and
+ *              1/√d is applied in fp32; rot itself must hold that matrix
+ *              (the decode merge reads it as given).
  */
 typedef struct tq_quantizer {
   int d;
@@ -109,6 +120,7 @@ typedef struct tq_quantizer {
   const float* centroids;
   const float* boundaries;
   void* prep;
+  int rotation;
 } tq_quantizer;
 
 /*
@@ -141,7 +153,7 @@ size_t tq_prep_bytes(void);
  * encoder uses. Run once per quantizer (after its rot/proj/centroids are
  * written), on `stream`; later calls on the same stream see the result.
  * Errors: TQ_ERR_INVALID_ARG (null q/fields, prep misaligned),
- * TQ_ERR_UNSUPPORTED (d, bits, variant), TQ_ERR_HIP.
+ * TQ_ERR_UNSUPPORTED (d, bits, variant, rotation), TQ_ERR_HIP.
  */
 int tq_prepare(const tq_quantizer* q, void* stream);
 

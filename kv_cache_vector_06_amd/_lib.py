@@ -21,6 +21,8 @@ TQ_MSE = 0
 TQ_PROD = 1
 TQ_F32 = 0
 TQ_BF16 = 1
+TQ_ROT_DENSE = 0
+TQ_ROT_HADAMARD = 1
 TQ_HEAD_DIM = 128
 
 # Every function include/tq.h declares.
@@ -39,7 +41,7 @@ class tq_quantizer(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("bits", ctypes.c_int), ("variant", ctypes.c_int),
                 ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
                 ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p),
-                ("prep", ctypes.c_void_p)]
+                ("prep", ctypes.c_void_p), ("rotation", ctypes.c_int)]
 
 
 class tq_packed(ctypes.Structure):

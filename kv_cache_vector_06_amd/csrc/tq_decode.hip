@@ -191,7 +191,7 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
   float qp[4], qs[4];                            // dims 32g + 4t + j
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    qp[j] = ldexpf(acc[j], ex) * (1.0f / kRotScale);
+    qp[j] = ldexpf(acc[j], ex) / a.kh->rot_scale;
     qs[j] = 0.f;
   }
   if (prod) {

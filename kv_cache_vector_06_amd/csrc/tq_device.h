@@ -19,19 +19,22 @@ constexpr float kCentScale = 64.0f;   // centroids enter fp16 tables as cÂ·64Â·Ï
 
 // A quantizer's prepared buffer (written by tq_prepare): a 256-byte header,
 // then two sets of matrix-core A operands, each 2 parts (fp16 hi, lo) Ã— 8 row
-// tiles Ã— 4 K-steps Ã— 64 lanes Ã— 16 bytes: 16Î , and (prod) S' = SÂ·Î áµ€ scaled
-// by the power of two sp_scale. Fragment (part, t, s), lane (i, g), slot j
+// tiles Ã— 4 K-steps Ã— 64 lanes Ã— 16 bytes: rot_scaleÂ·Î , and (prod) S' = SÂ·Î áµ€
+// scaled by the power of two sp_scale. Fragment (part, t, s), lane (i, g), slot j
 // holds row out_row(t, i) and column 32s + 8g + j (16Î ) or 32g + 8s + j (S').
 constexpr size_t kPrepHeaderBytes = 256;
 struct PrepHeader {
   float sigma;       // centroid scale Ïƒ in [1, 2), see prepare_kernel
   float sigma_err;   // max relative fp16 error of cÂ·64Â·Ïƒ over the centroids
   float sp_scale;    // the power of two S' is scaled by in its fragments
+  float rot_scale;   // the rotation fragments hold rot_scaleÂ·Î : 16 (dense Î , fp16
+                     // hi + lo), or âˆšd for a randomized Hadamard Î  = HÂ·diag(s)/âˆšd,
+                     // whose fragments HÂ·diag(s) are exact Â±1 (lo parts zero)
 };
 constexpr int kFragsPerSet = 2 * 8 * 4;               // (part, t, s)
 constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB
 constexpr size_t kPrepBytes = kPrepHeaderBytes + 2 * kSetBytes;
-constexpr float kRotScale = 16.0f;                    // |Î | <= 1 â†’ |16Î | <= 16
+constexpr float kRotScale = 16.0f;                    // dense Î : |Î | <= 1 â†’ |16Î | <= 16
 constexpr float kResScale = 64.0f;                    // residual scale of the sketch operand
 
 __host__ __device__ constexpr int frag_index(int part, int t, int s) { return (part * 8 + t) * 4 + s; }

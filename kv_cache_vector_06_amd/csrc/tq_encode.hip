@@ -33,7 +33,7 @@ namespace tq {
 __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__ rot,
                                                        const float* __restrict__ proj,
                                                        const float* __restrict__ centroids, int bm,
-                                                       uint8_t* __restrict__ prep_base) {
+                                                       int hadamard, uint8_t* __restrict__ prep_base) {
   __shared__ float red[1024];
   __shared__ int redi[1024];
   const int tid = threadIdx.x;
@@ -71,17 +71,25 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__
       h->sigma = 1.0f + float(redi[0]) * (1.0f / (1 << 18));
       h->sigma_err = red[0];
       h->sp_scale = 0.f;
+      h->rot_scale = hadamard ? sqrtf(float(kD)) : kRotScale;
     }
     __syncthreads();
   }
   uint16_t* prep = reinterpret_cast<uint16_t*>(prep_base + kPrepHeaderBytes);
-  // Rotation fragments: A(t, s)[lane (i, g)][j] = 16·Π[out_row(t,i)][32s + 8g + j].
+  // Rotation fragments: A(t, s)[lane (i, g)][j] = rot_scale·Π[out_row(t,i)][32s + 8g + j]:
+  // the fp16 hi/lo split of 16Π, or for a randomized Hadamard Π = H·diag(s)/√d
+  // the exact ±1 entries of H·diag(s) (the signs of Π's entries) with zero lo parts.
   for (int e = tid; e < 8 * 4 * 64 * 8; e += 1024) {
     const int j = e & 7, lane = (e >> 3) & 63, s = (e >> 9) & 3, t = e >> 11;
     const int i = lane & 15, g = lane >> 4;
-    const float v = kRotScale * rot[out_row(t, i) * kD + 32 * s + 8 * g + j];
+    const float r = rot[out_row(t, i) * kD + 32 * s + 8 * g + j];
     uint16_t hi, lo;
-    split_h(v, hi, lo);
+    if (hadamard) {
+      hi = r > 0.f ? 0x3c00u : r < 0.f ? 0xbc00u : 0u;
+      lo = 0u;
+    } else {
+      split_h(kRotScale * r, hi, lo);
+    }
     prep[(frag_index(0, t, s) * 64 + lane) * 8 + j] = hi;
     prep[(frag_index(1, t, s) * 64 + lane) * 8 + j] = lo;
   }
@@ -278,6 +286,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   // Stage the operand fragments with direct-to-LDS loads (1 KiB per wavefront
   // instruction), all issued before a single wait.
   stage_frags(a.prep, lds_rot, PROD ? lds_proj : nullptr, threadIdx.x);
+  const float rot_scale =
+      reinterpret_cast<const PrepHeader*>(reinterpret_cast<const uint8_t*>(a.prep) - kPrepHeaderBytes)->rot_scale;
   Book bk{};
   if constexpr (BM >= 1) {
     const float* tb = a.boundaries + (K / 2 - 1);
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
 
     // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j, and
     // acc = S·y with S = 16‖x‖·2^-e (any S > 0 for a zero vector, whose acc is 0).
-    const float S = (rs > 0.f) ? kRotScale * rs : 1.0f;
+    const float S = (rs > 0.f) ? rot_scale * rs : 1.0f;
     const float up = 1.0f / S;
     ScaledBook sb;
     {
@@ -551,6 +561,7 @@ int check_quantizer(const tq_quantizer* q) {
   if (bm > 0 && q->boundaries == nullptr) return TQ_ERR_INVALID_ARG;
   if (q->variant == TQ_PROD && q->proj == nullptr) return TQ_ERR_INVALID_ARG;
   if (!aligned(q->prep, 256)) return TQ_ERR_WORKSPACE;
+  if (q->rotation != TQ_ROT_DENSE && q->rotation != TQ_ROT_HADAMARD) return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
 }
 
@@ -571,7 +582,7 @@ extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
   const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
   hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), q->rot,
                      q->variant == TQ_PROD ? q->proj : nullptr, q->centroids, bm,
-                     static_cast<uint8_t*>(q->prep));
+                     q->rotation == TQ_ROT_HADAMARD ? 1 : 0, static_cast<uint8_t*>(q->prep));
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

@@ -147,7 +147,7 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
         bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
       }
     }
-  // acc = S·y for rotated coordinates 32g + 4t + j, S = 16‖x‖·2^-e.
+  // acc = S·y for rotated coordinates 32g + 4t + j, S = rot_scale·‖x‖·2^-e.
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -159,7 +159,9 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
   // Scaled codebook: T[j] = bits(S·t_j) for 1 <= j < K/2 (all ones above,
   // never below a magnitude), cs[m] = S·(centroid magnitude m).
   const uint32_t K2 = a.bm > 0 ? (1u << a.bm) / 2 : 0u;
-  const float S = (rs > 0.f) ? kRotScale * rs : 1.0f;
+  const float rot_scale =
+      reinterpret_cast<const PrepHeader*>(reinterpret_cast<const uint8_t*>(a.frags) - kPrepHeaderBytes)->rot_scale;
+  const float S = (rs > 0.f) ? rot_scale * rs : 1.0f;
   const float up = 1.0f / S;
   uint32_t T[8];
   float cs[8];

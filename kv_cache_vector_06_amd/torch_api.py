@@ -24,7 +24,9 @@ class Quantizer:
     prepared operands), all resident on `device`."""
 
     def __init__(self, rot: np.ndarray, bits: int, variant: str = "mse",
-                 proj: np.ndarray | None = None, device: str = "cuda"):
+                 proj: np.ndarray | None = None, device: str = "cuda", rotation: str = "dense"):
+        """`rotation` is "dense" (any orthogonal rot) or "hadamard" (rot is the
+        randomized Walsh-Hadamard rotation H·diag(s)/√d)."""
         d = rot.shape[0]
         self.d, self.bits = d, bits
         self.variant = L.TQ_PROD if variant == "prod" else L.TQ_MSE
@@ -41,8 +43,9 @@ class Quantizer:
         self.centroids = torch.as_tensor(c.astype(np.float32)).to(dev)
         self.boundaries = torch.as_tensor(np.concatenate([t, [0.0]]).astype(np.float32)).to(dev)
         self.prep = torch.empty(L.tq_prep_bytes(), dtype=torch.uint8, device=dev)
+        self.rotation = {"dense": L.TQ_ROT_DENSE, "hadamard": L.TQ_ROT_HADAMARD}[rotation]
         self.c = L.tq_quantizer(d, bits, self.variant, _ptr(self.rot), _ptr(self.proj),
-                                _ptr(self.centroids), _ptr(self.boundaries), _ptr(self.prep))
+                                _ptr(self.centroids), _ptr(self.boundaries), _ptr(self.prep), self.rotation)
         L.tq_prepare(self.c, _stream())
 
     @property

@@ -130,10 +130,12 @@ def rel_l2_per_head(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return num / np.maximum(den, 1e-300)
 
 
-def quantizers(cfg):
-    Rk, Rv, S = synth.constants(cfg.d)
-    kq = T.Quantizer(Rk, cfg.k_bits, cfg.k_variant, S if cfg.k_variant == "prod" else None, DEV)
-    vq = T.Quantizer(Rv, cfg.v_bits, "mse", None, DEV)
+def quantizers(cfg, rotation="dense"):
+    """Key and value quantizers of a workload with dense (Haar) or randomized
+    Hadamard rotations, and the float32 matrices both sides read."""
+    Rk, Rv, S = synth.constants(cfg.d) if rotation == "dense" else synth.hadamard_constants(cfg.d)
+    kq = T.Quantizer(Rk, cfg.k_bits, cfg.k_variant, S if cfg.k_variant == "prod" else None, DEV, rotation)
+    vq = T.Quantizer(Rv, cfg.v_bits, "mse", None, DEV, rotation)
     return kq, vq, Rk, Rv, S
 
 

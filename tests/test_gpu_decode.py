@@ -21,9 +21,9 @@ def _flat(x):
     return x.reshape(-1, x.shape[-1])
 
 
-def run_case(cfg, T_ctx, B, lens=None, end_to_end=True):
-    say("case", cfg.name, "T", T_ctx, "B", B, "lens", lens)
-    kq, vq, Rk, Rv, S = quantizers(cfg)
+def run_case(cfg, T_ctx, B, lens=None, end_to_end=True, rotation="dense"):
+    say("case", cfg.name, "T", T_ctx, "B", B, "lens", lens, rotation)
+    kq, vq, Rk, Rv, S = quantizers(cfg, rotation)
     K, V = synth.make_kv(cfg, T=T_ctx, B=B)
     q = synth.make_query(cfg, B=B)
     K, V = np.ascontiguousarray(K), np.ascontiguousarray(V)
@@ -84,6 +84,14 @@ def test_decode_odd_group_and_mse1():
     run_case(cfg, 300, 2)
     cfg = synth.DecodeConfig("prod1", 1, 2, 4, 300, 128, "prod", 1, 3, "gaussian", "fp32", 81)
     run_case(cfg, 300, 1)
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3, 5])
+def test_decode_hadamard_rotation(cfg_id):
+    # Randomized Walsh-Hadamard rotations for keys and values (exact ±1
+    # matrix-core operands, 1/√d in fp32), same parity rules.
+    cfg = synth.CONFIGS[cfg_id]
+    run_case(cfg, 1000 + 7, min(cfg.B, 2), rotation="hadamard")
 
 
 def test_decode_full_size_sampled():

@@ -29,6 +29,31 @@ def test_encode_parity(consts, bits, variant, dtype):
     say(st)
 
 
+@pytest.mark.parametrize("bits,variant,dtype", CASES)
+def test_encode_parity_hadamard(bits, variant, dtype):
+    # Randomized Walsh-Hadamard rotation: exact ±1 operands, 1/√d in fp32.
+    # Outlier-channel data, plus a zero row and one-hot rows (which this
+    # rotation maps to flat vectors of ±1/√d).
+    Rk, _, S = synth.hadamard_constants(128)
+    n = 2048 + 37
+    X = synth.outlier_kv(1, 1, n, 128, seed=400 + bits, dtype=dtype)[0, 0].copy()
+    X[0] = 0.0
+    X[1] = 0.0
+    X[1, 5] = 3.0
+    X[2] = 0.0
+    X[2, 127] = -0.5
+    say("encode hadamard", bits, variant, dtype, n)
+    q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV, "hadamard")
+    xg = to_gpu_x(X, dtype)
+    p = T.encode(q, xg)
+    g = gpu_packed_arrays(p, q)
+    st = check_encode(g, oracle_encode(X, Rk, S, bits, variant), bits, variant)
+    say(st)
+    small = gpu_packed_arrays(T.encode(q, xg[:37]), q)       # the row-tile encoder
+    for k in g:
+        np.testing.assert_array_equal(small[k], g[k][:37])
+
+
 @pytest.mark.parametrize("variant", ["mse", "prod"])
 def test_encode_edge_cases(consts, variant):
     Rk, _, S = consts

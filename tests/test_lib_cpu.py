@@ -147,3 +147,14 @@ def test_decode_step_argument_errors_are_synchronous():
         assert call(phase=ph) == L.TQ_ERR_INVALID_ARG
     for ph in (1, 2, 3):
         assert call(phase=ph, kn=None) == L.TQ_ERR_INVALID_ARG
+
+
+def test_unknown_rotation_is_rejected():
+    lib = L.load()
+    q = _fake_quantizer()
+    q.rotation = 7
+    pk = L.tq_packed(1 << 20, 1 << 20, None, None)
+    assert lib.tq_prepare(ctypes.byref(q), None) == L.TQ_ERR_UNSUPPORTED
+    assert lib.tq_encode(ctypes.byref(q), 1 << 20, L.TQ_BF16, 10, 128, ctypes.byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
+    q.rotation = L.TQ_ROT_HADAMARD
+    assert lib.tq_encode(ctypes.byref(q), 1 << 20, 7, 10, 128, ctypes.byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
