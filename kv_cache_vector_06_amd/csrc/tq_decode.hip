@@ -751,9 +751,7 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
                                              int n, int g, const Luts& T, const u32x4 (&bq)[4],
                                              const u32x4 (&bs)[4], float iqs, uint32_t lomask,
                                              SoftmaxState& st, f32x4 (&acc)[8]) {
-  // ---- P·V operands first (they do not depend on the scores, so their
-  // table reads overlap the score work): column n = dim 8n + r, rows = token
-  // slots.
+  // Value codes regrouped for the pair-table addresses.
   uint32_t X[4], Y[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -776,6 +774,55 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
     X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
     Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
   }
+  // ---- scores: column n = head n % 8 (hi part for n < 8, lo part above) ----
+  // Every table read of both tiles' score operands is issued before the
+  // first product, so the block waits for one LDS round trip instead of one
+  // per product (the scheduler would otherwise put each read just before its
+  // product); the value-table reads follow the products and complete while
+  // the softmax runs.
+  u32x4 kh[2][4], kl[2][4], sg[2][4];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    if constexpr (BK > 0) {
+      key_operands<BK, 0>(R.kw[tau], T.k, T.klane, kh[tau][0], kl[tau][0]);
+      key_operands<BK, 1>(R.kw[tau], T.k, T.klane, kh[tau][1], kl[tau][1]);
+      key_operands<BK, 2>(R.kw[tau], T.k, T.klane, kh[tau][2], kl[tau][2]);
+      key_operands<BK, 3>(R.kw[tau], T.k, T.klane, kh[tau][3], kl[tau][3]);
+    }
+    if constexpr (PROD) {
+      sg[tau][0] = sign_operand<0>(R.qw[tau], T.q, T.qlane);
+      sg[tau][1] = sign_operand<1>(R.qw[tau], T.q, T.qlane);
+      sg[tau][2] = sign_operand<2>(R.qw[tau], T.q, T.qlane);
+      sg[tau][3] = sign_operand<3>(R.qw[tau], T.q, T.qlane);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  // u = ⟨q', c⟩ + γ⟨q_S, s⟩ for this lane's part; the row rotation adds the
+  // other part, and the key norm and the query scale finish the score.
+  float sc[8];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    f32x4 dm = f32x4{0.f, 0.f, 0.f, 0.f}, dq = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BK > 0) {
+#pragma unroll
+      for (int S = 0; S < 4; ++S) {
+        dm = mfma(kh[tau][S], bq[S], dm);
+        if constexpr (BK == 4) dm = mfma(kl[tau][S], bq[S], dm);
+      }
+    }
+    if constexpr (PROD) {
+#pragma unroll
+      for (int S = 0; S < 4; ++S) dq = mfma(sg[tau][S], bs[S], dq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * tau + i;
+      const float u = PROD ? fmaf(R.gk[j], dq[i], dm[i]) : dm[i];
+      sc[j] = add_ror8(u) * R.nk[j];       // the score is sc·iqs
+    }
+  }
+  // ---- P·V operands: column n = dim 8n + r, rows = token slots ----
   u32x4 bv[8];
   bv[0] = pv_operand<0>(X, Y, T);
   bv[1] = pv_operand<1>(X, Y, T);
@@ -785,36 +832,6 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
   bv[5] = pv_operand<5>(X, Y, T);
   bv[6] = pv_operand<6>(X, Y, T);
   bv[7] = pv_operand<7>(X, Y, T);
-
-  // ---- scores: column n = head n % 8 (hi part for n < 8, lo part above) ----
-  // u = ⟨q', c⟩ + γ⟨q_S, s⟩ for this lane's part; the row rotation adds the
-  // other part, and the key norm and the query scale finish the score.
-  float sc[8];
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    f32x4 dm = f32x4{0.f, 0.f, 0.f, 0.f}, dq = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BK > 0) {
-      u32x4 ah, al;
-#define TQ_KSTEP(S)                                              \
-  key_operands<BK, S>(R.kw[tau], T.k, T.klane, ah, al);          \
-  dm = mfma(ah, bq[S], dm);                                      \
-  if constexpr (BK == 4) dm = mfma(al, bq[S], dm);
-      TQ_KSTEP(0) TQ_KSTEP(1) TQ_KSTEP(2) TQ_KSTEP(3)
-#undef TQ_KSTEP
-    }
-    if constexpr (PROD) {
-      dq = mfma(sign_operand<0>(R.qw[tau], T.q, T.qlane), bs[0], dq);
-      dq = mfma(sign_operand<1>(R.qw[tau], T.q, T.qlane), bs[1], dq);
-      dq = mfma(sign_operand<2>(R.qw[tau], T.q, T.qlane), bs[2], dq);
-      dq = mfma(sign_operand<3>(R.qw[tau], T.q, T.qlane), bs[3], dq);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * tau + i;
-      const float u = PROD ? fmaf(R.gk[j], dq[i], dm[i]) : dm[i];
-      sc[j] = add_ror8(u) * R.nk[j];       // the score is sc·iqs
-    }
-  }
   float nv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) nv[j] = R.nv[j];
