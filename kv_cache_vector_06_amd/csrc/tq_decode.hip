@@ -335,12 +335,14 @@ __device__ __forceinline__ uint32_t field_shl(const uint32_t (&w)[N]) {
 // c·width, and the 32 lanes of a half-wavefront always read 32 different banks.
 constexpr int kCopies = 32;
 
-// The private tables share one 64 KiB region of 256 rows × 256 bytes (copy
-// c = lane % 32):
-//   value pairs: entry e in row e at byte 4c (the lower half of the row), so
-//     that one byte permute forms the address (entry in bits 8..15, 4c in
-//     bits 0..7);
-//   3-bit key pairs: entry e in row e at byte 128 + 4c.
+// The private tables share one 64 KiB region of 256 rows × 256 bytes:
+//   value pairs: entry e in row e at byte 4c, c = lane % 32 (the lower half
+//     of the row), so that one byte permute forms the address (entry in bits
+//     8..15, 4c in bits 0..7);
+//   3-bit key pairs: entry e in row e at byte 128 + 4c, c = lane % 32;
+//   4-bit key pairs and 2-bit key quads (8-byte entries, indexed by a whole
+//     code byte): entry e in row e at byte 128 + 8c', c' = lane % 16 (two
+//     lanes of a half-wavefront share a copy), addressed by one byte permute.
 // The sketch-nibble table (8 bytes per copy) lives in its own 4 KiB array,
 // entry e of copy c at byte 256e + 8c: the upper halves of the rows above
 // only reach half of the banks.
@@ -349,16 +351,24 @@ constexpr uint32_t kTabK = 128;
 
 // Key tables. Each entry covers a group of codes (pairs for 3 and 4 bits,
 // quads for 2, octets for 1) and holds their fp16 centroids c·64σ packed in
-// pairs; the 4-bit table appends the fp16 remainders (lo parts). The 3-bit
-// pair table (64 entries) is private per lane (in the shared region); the
-// others are shared by all lanes.
+// pairs; the 4-bit table appends the fp16 remainders (lo parts). The 2-, 3-
+// and 4-bit tables are private copies in the shared region; the 1-bit octet
+// table is shared by all lanes.
 template <int BK> struct KLut {
-  static constexpr bool priv = BK == 3;
+  static constexpr bool priv = BK >= 2;
+  static constexpr bool byte_indexed = BK == 2 || BK == 4;   // 8-byte entries, 16 copies
   static constexpr int per = (BK == 3 || BK == 4) ? 2 : BK == 2 ? 4 : 8;     // codes per entry
   static constexpr int entries = BK == 3 ? 64 : 256;
   static constexpr int dwords = BK == 1 ? 4 : (BK == 2 || BK == 4) ? 2 : 1;  // per entry
   static constexpr int bytes = (BK == 0 || priv) ? 16 : entries * dwords * 4;   // the separate shared table
 };
+
+// Byte offset of entry (byte B of w) in a row-per-entry table: the entry in
+// bits 8..15, the lane's copy offset (< 256) in bits 0..7; one byte permute.
+template <int B>
+__device__ __forceinline__ uint32_t row_addr(uint32_t w, uint32_t lane_off) {
+  return __builtin_amdgcn_perm(w, lane_off, 0x03020000u | ((4u + B) << 8));
+}
 
 // A operands of K-step S from the lane's 32 key codes (hi; lo for 4 bits).
 // `lut` is the table; `lane4` the byte offset of the lane's private copy.
@@ -366,13 +376,13 @@ template <int BK, int S>
 __device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 1], const uint8_t* lut,
                                              uint32_t lane4, u32x4& hi, u32x4& lo) {
   if constexpr (BK == 4) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t e = (kw[S] >> (8 * p)) & 0xffu;
-      const u32x2 v = *reinterpret_cast<const u32x2*>(lut + (e << 3));
-      hi[p] = v[0];
-      lo[p] = v[1];
-    }
+    // entry (pair code byte p of word S) of copy c' at byte 256e + 128 + 8c' (lane4 = 128 + 8c')
+    const u32x2 v0 = *reinterpret_cast<const u32x2*>(lut + row_addr<0>(kw[S], lane4));
+    const u32x2 v1 = *reinterpret_cast<const u32x2*>(lut + row_addr<1>(kw[S], lane4));
+    const u32x2 v2 = *reinterpret_cast<const u32x2*>(lut + row_addr<2>(kw[S], lane4));
+    const u32x2 v3 = *reinterpret_cast<const u32x2*>(lut + row_addr<3>(kw[S], lane4));
+    hi = u32x4{v0[0], v1[0], v2[0], v3[0]};
+    lo = u32x4{v0[1], v1[1], v2[1], v3[1]};
   } else if constexpr (BK == 3) {
     // entry e of copy c at byte 256e + 128 + 4c (lane4 = 128 + 4c)
     hi[0] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 0, 6, 8>(kw) + lane4));
@@ -380,9 +390,9 @@ __device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 
     hi[2] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 12, 6, 8>(kw) + lane4));
     hi[3] = *reinterpret_cast<const uint32_t*>(lut + (field_shl<24 * S + 18, 6, 8>(kw) + lane4));
   } else if constexpr (BK == 2) {
-    const uint32_t h = kw[S >> 1] >> (16 * (S & 1));
-    const u32x2 q0 = *reinterpret_cast<const u32x2*>(lut + ((h & 0xffu) << 3));
-    const u32x2 q1 = *reinterpret_cast<const u32x2*>(lut + (((h >> 8) & 0xffu) << 3));
+    // quads: bytes 2(S%2), 2(S%2) + 1 of word S/2
+    const u32x2 q0 = *reinterpret_cast<const u32x2*>(lut + row_addr<2 * (S & 1)>(kw[S >> 1], lane4));
+    const u32x2 q1 = *reinterpret_cast<const u32x2*>(lut + row_addr<2 * (S & 1) + 1>(kw[S >> 1], lane4));
     hi = u32x4{q0[0], q0[1], q1[0], q1[1]};
   } else if constexpr (BK == 1) {
     hi = *reinterpret_cast<const u32x4*>(lut + (((kw[0] >> (8 * S)) & 0xffu) << 4));
@@ -919,65 +929,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
   constexpr int nthr = kDecWaves * 64;
 
-  // ---- lookup tables -------------------------------------------------------
-  if constexpr (BK > 0) {
-    constexpr int KK = 1 << BK;
-    const float ks = kCentScale * a.kh->sigma;
-    uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
-    if constexpr (KL::priv) {
-      for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
-        const int e = idx / kCopies, c = idx % kCopies;
-        *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) =
-            pack_h2(a.kcent[e & (KK - 1)] * ks, a.kcent[e >> BK] * ks);
-      }
-    } else {
-      for (int e = tid; e < KL::entries; e += nthr) {
-        constexpr int per = KL::per;
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int i = 0; i < per; ++i) {
-          const int code = (e >> (BK * i)) & (KK - 1);
-          split_h(a.kcent[code] * ks, hi[i], lo[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < per / 2; ++i) {
-          lk[e * KL::dwords + i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
-          if constexpr (BK == 4) lk[e * KL::dwords + 1] = uint32_t(lo[0]) | (uint32_t(lo[1]) << 16);
-        }
-      }
-    }
-  }
-  if constexpr (PROD) {
-    // entry e (4 sign bits), dword w: signs of bits 2w and 2w + 1
-    for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
-      const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
-      const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
-      const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
-      *reinterpret_cast<uint32_t*>(lut_q + 256 * e + 8 * c + 4 * w) = s0 | (s1 << 16);
-    }
-  }
-  {
-    // entry (c0 | c1 << 4): the fp16 centroids of value codes c0 (low half) and c1.
-    constexpr int KV = 1 << BV;
-    const float vs = kCentScale * a.vh->sigma;
-    for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
-      const int e = idx / kCopies, c = idx % kCopies;
-      const int c0 = e & 15, c1 = e >> 4;
-      *reinterpret_cast<uint32_t*>(tab + 256 * e + 4 * c) =
-          (c0 < KV && c1 < KV) ? pack_h2(a.vcent[c0] * vs, a.vcent[c1] * vs) : 0u;
-    }
-  }
-  Luts T;
-  const uint32_t cp = lane & 31;            // private copy of this lane
-  T.k = KL::priv ? tab : lut_k;
-  T.q = lut_q;
-  T.v = tab;
-  T.klane = KL::priv ? kTabK + 4u * cp : 0u;
-  T.qlane = 8u * cp;
-  T.vlane = 4u * cp;
-  const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
-
-  // ---- query operands --------------------------------------------------------
+  // ---- query operands (loads issued first; used in the loop) ---------------
   const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
   u32x4 bq[4], bs[4];
@@ -987,7 +939,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
   }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
-  __syncthreads();
+  // the scaled centroids for the table build: values in 0..15, keys in 16..31
+  __shared__ float cent[32];
+  if (tid < 32) {
+    constexpr int KK = BK > 0 ? (1 << BK) : 1, KV = 1 << BV;
+    float v = 0.f;
+    if (tid < 16) {
+      if (tid < KV) v = a.vcent[tid] * (kCentScale * a.vh->sigma);
+    } else if (BK > 0 && tid - 16 < KK) {
+      v = a.kcent[tid - 16] * (kCentScale * a.kh->sigma);
+    }
+    cent[tid] = v;
+  }
 
   // ---- token range of this wavefront ---------------------------------------
   int64_t L = a.max_ctx;
@@ -1009,13 +972,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const uint8_t* vc = a.vc + base * (16 * BV);
   const float* vn = a.vn + base;
 
-  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
-  f32x4 acc[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();   // the centroids
 
-  // Ring of kStages LDS stages: block i is read from stage i % kStages after
-  // blocks i+1 (and the loads for i+2 are issued right after the read).
+  // ---- lookup tables (the value pair table first: the compiler orders its
+  // LDS writes after any pending direct-to-LDS loads) -------------------------
+  const float* vcs = cent;
+  const float* kcs = cent + 16;
+  {
+    // entry (c0 | c1 << 4): the fp16 centroids of value codes c0 (low half) and c1.
+    constexpr int KV = 1 << BV;
+    for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
+      const int e = idx / kCopies, c = idx % kCopies;
+      const int c0 = e & 15, c1 = e >> 4;
+      *reinterpret_cast<uint32_t*>(tab + 256 * e + 4 * c) = (c0 < KV && c1 < KV) ? pack_h2(vcs[c0], vcs[c1]) : 0u;
+    }
+  }
+  // The first two blocks' loads go out before the tables are built.
   uint8_t* ring = &stage[wave][0];
   const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
   const StageOffsets so = stage_offsets<BK, PROD, BV>(n, g);
@@ -1025,6 +997,71 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     stage_block<BK, PROD, BV, AL>(ring, t_begin, last, lane, dl, kc, kq, vc, kn, vn, kg);
   if (nblk > 1)
     stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, vc, kn, vn, kg);
+
+  if constexpr (BK > 0) {
+    constexpr int KK = 1 << BK;
+    if constexpr (KL::byte_indexed) {
+      // entry e: BK = 4: codes (e & 15, e >> 4), hi pair then lo pair;
+      // BK = 2: codes (e >> 2i) & 3, i < 4, as two pairs
+      for (int idx = tid; idx < 256 * 16; idx += nthr) {
+        const int e = idx >> 4, c = idx & 15;
+        uint32_t w0, w1;
+        if constexpr (BK == 4) {
+          uint16_t h0, l0, h1, l1;
+          split_h(kcs[e & 15], h0, l0);
+          split_h(kcs[e >> 4], h1, l1);
+          w0 = uint32_t(h0) | (uint32_t(h1) << 16);
+          w1 = uint32_t(l0) | (uint32_t(l1) << 16);
+        } else {
+          w0 = pack_h2(kcs[e & 3], kcs[(e >> 2) & 3]);
+          w1 = pack_h2(kcs[(e >> 4) & 3], kcs[e >> 6]);
+        }
+        *reinterpret_cast<u32x2*>(tab + 256 * e + kTabK + 8 * c) = u32x2{w0, w1};
+      }
+    } else if constexpr (KL::priv) {
+      for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
+        const int e = idx / kCopies, c = idx % kCopies;
+        *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) = pack_h2(kcs[e & (KK - 1)], kcs[e >> BK]);
+      }
+    } else {
+      uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
+      for (int e = tid; e < KL::entries; e += nthr) {
+        constexpr int per = KL::per;
+        uint16_t hi[8];
+#pragma unroll
+        for (int i = 0; i < per; ++i) hi[i] = f2h_bits(kcs[(e >> (BK * i)) & (KK - 1)]);
+#pragma unroll
+        for (int i = 0; i < per / 2; ++i) lk[e * KL::dwords + i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
+      }
+    }
+  }
+  if constexpr (PROD) {
+    // entry e (4 sign bits), dword w: signs of bits 2w and 2w + 1
+    for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
+      const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
+      const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
+      const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
+      *reinterpret_cast<uint32_t*>(lut_q + 256 * e + 8 * c + 4 * w) = s0 | (s1 << 16);
+    }
+  }
+  Luts T;
+  const uint32_t cp = lane & 31;            // private copy of this lane
+  T.k = KL::priv ? tab : lut_k;
+  T.q = lut_q;
+  T.v = tab;
+  T.klane = KL::byte_indexed ? kTabK + 8u * (lane & 15) : KL::priv ? kTabK + 4u * cp : 0u;
+  T.qlane = 8u * cp;
+  T.vlane = 4u * cp;
+  const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
+  __syncthreads();
+
+  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
+  f32x4 acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Block i is read from stage i % kStages; the loads for block i + 2 go
+  // into the stage just read.
   int cur = 0;
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint32_t t0 = t_begin + i * kBlockTok;

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-      xv[q] = (amax > 0.f) ? ldexpf(xv[q], -ex) : 0.f;
+      xv[q] = ldexpf(xv[q], -ex);    // a zero row stays ±0 (ex = 0)
       ss = fmaf(xv[q], xv[q], ss);
     }
     ss = sum4g(ss);

@@ -125,7 +125,7 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
   float ss = 0.f;
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
-    xv[q] = (amax > 0.f) ? ldexpf(xv[q], -ex) : 0.f;
+    xv[q] = ldexpf(xv[q], -ex);    // a zero row stays ±0 (ex = 0)
     ss = fmaf(xv[q], xv[q], ss);
   }
   ss = sum4g(ss);
