@@ -119,3 +119,60 @@ def test_decode_full_size_sampled():
         r = rel_l2_per_head(out[0, hs], ref[0])
         say("  full-size kv head", kvh, "rel L2", r.max())
         assert r.max() <= TOL
+
+
+def _full_size_units(cfg, units, seed, use_step):
+    """Full-size decode of `cfg` on the GPU (encode + decode, or the fused
+    decode step whose new token is the last one), with the oracle evaluating
+    the query heads of the sampled (batch, KV head) units."""
+    kq, vq, Rk, Rv, S = quantizers(cfg)
+    say("generating", cfg.name)
+    K, V = synth.make_kv(cfg)
+    q = synth.make_query(cfg)
+    encs = {}
+    for (b, kvh) in units:
+        encs[(b, kvh)] = (encode_away_from_ties(K[b, kvh], Rk, S, cfg.k_bits, cfg.k_variant, seed + 2 * kvh + 17 * b,
+                                                cfg.dtype),
+                          encode_away_from_ties(V[b, kvh], Rv, None, cfg.v_bits, "mse", seed + 2 * kvh + 17 * b + 1,
+                                                cfg.dtype))
+    dec = T.Decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T, DEV)
+    qg = torch.from_numpy(q).to(DEV)
+    if use_step:
+        # the cache holds tokens 0..T-2; the step appends token T-1 of every row
+        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
+        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
+        last = torch.arange(cfg.B * cfg.Hkv, device=DEV) * cfg.T + cfg.T - 1
+        for p in (kp, vp):
+            p.norms[last] = 0.0
+            p.codes[last] = 0
+            if p.qjl is not None:
+                p.qjl[last] = 0
+                p.gammas[last] = 0.0
+        kn = to_gpu_x(np.ascontiguousarray(K[:, :, -1].reshape(-1, 128)), cfg.dtype)
+        vn = to_gpu_x(np.ascontiguousarray(V[:, :, -1].reshape(-1, 128)), cfg.dtype)
+        out = dec.step(kq, vq, kn, vn, qg, kp, vp).cpu().numpy()
+    else:
+        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
+        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
+        out = dec(kq, vq, qg, kp, vp).cpu().numpy()
+    for (b, kvh), (ek, ev) in encs.items():
+        Kt = oracle_dequant(ek, Rk, S, cfg.k_bits, cfg.k_variant)[None, None]
+        Vt = oracle_dequant(ev, Rv, None, cfg.v_bits, "mse")[None, None]
+        hs = list(range(kvh * cfg.G, (kvh + 1) * cfg.G))
+        ref = decode_attention(q[b:b + 1, hs], Kt, Vt, 1 / math.sqrt(128))
+        r = rel_l2_per_head(out[b, hs], ref[0])
+        say("  full-size", cfg.name, "unit", (b, kvh), "rel L2", r.max())
+        assert r.max() <= TOL
+
+
+def test_decode_step_full_size_benchmark_shape_sampled():
+    # The benchmark's launch configuration: tq_decode_step at batch 4 x 8 KV
+    # heads x 131072 tokens, 64 query heads (prod-4 keys, mse-4 values); the
+    # oracle evaluates two (batch, KV head) units.
+    _full_size_units(synth.CONFIGS[5], [(0, 0), (3, 6)], 500, use_step=True)
+
+
+def test_decode_full_size_batched_sampled():
+    # 64 sequences x 16384 tokens, 8 KV heads, 32 query heads, mse-2 keys and
+    # values, log-normal per-token norms; two units sampled.
+    _full_size_units(synth.CONFIGS[4], [(0, 3), (63, 7)], 600, use_step=False)
