@@ -47,6 +47,7 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_signs", "unpack_signs",
     "encode_mse", "encode_prod", "dequant_mse", "dequant_prod",
     "attention", "decode_attention", "fwht", "hadamard_rotate",
+    "search_topk", "recall_1_at_k",
 ]
 
 
@@ -325,3 +326,34 @@ def decode_attention(q, K, V, scale: float, ctx_lens=None, heads=None):
         L = K.shape[2] if ctx_lens is None else int(ctx_lens[b])
         out[b, h] = attention(q[b, h], K[b, h // G, :L], V[b, h // G, :L], scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Inner-product vector search over a packed database  ([WY] section 6.4:
+# TurboQuant used for nearest-neighbour search by inner product, scored by
+# recall 1@k)
+# ---------------------------------------------------------------------------
+
+def search_topk(Q, X, k: int):
+    """For each query row q of Q, the k rows x of X with the largest ⟨q, x⟩,
+    best first; equal scores are ordered by the lower row index. X is the
+    database as the searcher sees it (for a packed database, its dequantized
+    vectors). Returns (scores [nq, k] float64, index [nq, k] int64)."""
+    Q = np.asarray(Q, np.float64)
+    X = np.asarray(X, np.float64)
+    S = Q @ X.T
+    n = X.shape[0]
+    idx = np.empty((Q.shape[0], k), np.int64)
+    for i in range(Q.shape[0]):
+        # sort by (-score, index): lexsort takes the last key as the primary one
+        order = np.lexsort((np.arange(n), -S[i]))
+        idx[i] = order[:k]
+    return np.take_along_axis(S, idx, axis=1), idx
+
+
+def recall_1_at_k(true_top1, found):
+    """Fraction of queries whose true nearest neighbour (true_top1[i]) is among
+    the k indices found[i] (recall 1@k)."""
+    true_top1 = np.asarray(true_top1).reshape(-1)
+    found = np.asarray(found)
+    return float(np.mean([true_top1[i] in found[i] for i in range(found.shape[0])]))
