@@ -270,6 +270,38 @@ int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_quantizer* 
                          int64_t max_ctx, const tq_packed* k_cache, const tq_packed* v_cache,
                          float scale, float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * tq_search_workspace — bytes of device workspace tq_search needs for these
+ * sizes (a pure function of its arguments); 0 for invalid sizes.
+ */
+size_t tq_search_workspace(int nq, int64_t n, int k);
+
+/*
+ * tq_search — inner-product top-k over a packed database ([WY] section 6.4:
+ * nearest-neighbour search by inner product over TurboQuant-encoded vectors,
+ * scored by recall 1@k). For each query q_i, the k database vectors x_j
+ * (j < n) with the largest estimated inner product ⟨q_i, x̃_j⟩, x̃ the
+ * dequantized vector of tq_attn_decode's formulas (PROD: the unbiased
+ * estimator), best first; equal scores are ordered by the lower index.
+ *   q          prepared quantizer of the database (either variant, 1..4 bits)
+ *   query      device float[nq][d], 16-byte aligned
+ *   nq         number of queries, >= 1
+ *   db         packed database, vector j in slot j (see tq_packed)
+ *   n          database size, 1 <= n <= 2^26
+ *   k          1 <= k <= min(32, n)
+ *   scores     device float[nq][k]: the estimated inner products
+ *   index      device int64[nq][k]: the vectors' slots
+ *   workspace  device, >= tq_search_workspace(nq, n, k) bytes, 256-byte
+ *              aligned; contents need not be initialised
+ * Three launches on `stream`: the query operands, the scan (each workgroup
+ * keeps its best k per query), and the merge over workgroups.
+ * Errors: TQ_ERR_INVALID_ARG (null or misaligned pointers, nq < 1, k < 1,
+ * k > n), TQ_ERR_UNSUPPORTED (k > 32, n > 2^26, d, bits, variant),
+ * TQ_ERR_WORKSPACE, TQ_ERR_HIP.
+ */
+int tq_search(const tq_quantizer* q, const float* query, int nq, const tq_packed* db, int64_t n, int k,
+              float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* tq_status_string(int status);
 

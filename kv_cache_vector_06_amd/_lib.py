@@ -28,7 +28,8 @@ TQ_HEAD_DIM = 128
 # Every function include/tq.h declares.
 EXPORTED = ("tq_codebook", "tq_prep_bytes", "tq_prepare", "tq_encode",
             "tq_attn_decode_workspace", "tq_attn_decode", "tq_attn_decode_phase",
-            "tq_decode_step", "tq_decode_step_phase", "tq_status_string")
+            "tq_decode_step", "tq_decode_step_phase", "tq_search_workspace", "tq_search",
+            "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -83,6 +84,10 @@ def load() -> ctypes.CDLL:
     lib.tq_decode_step.restype = I
     lib.tq_decode_step_phase.argtypes = [I] + lib.tq_decode_step.argtypes
     lib.tq_decode_step_phase.restype = I
+    lib.tq_search_workspace.argtypes = [I, I64, I]
+    lib.tq_search_workspace.restype = SZ
+    lib.tq_search.argtypes = [ctypes.POINTER(tq_quantizer), P, I, ctypes.POINTER(tq_packed), I64, I, P, P, P, SZ, P]
+    lib.tq_search.restype = I
     lib.tq_status_string.argtypes = [I]
     lib.tq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -167,3 +172,13 @@ def tq_decode_step_phase(phase: int, kq: tq_quantizer, vq: tq_quantizer, k_new: 
                                        ctx_lens, int(max_ctx), ctypes.byref(k_cache), ctypes.byref(v_cache),
                                        float(scale), out, workspace, int(ws_bytes), stream),
            "tq_decode_step_phase")
+
+
+def tq_search_workspace(nq: int, n: int, k: int) -> int:
+    return int(load().tq_search_workspace(int(nq), int(n), int(k)))
+
+
+def tq_search(q: tq_quantizer, query: int, nq: int, db: tq_packed, n: int, k: int, scores: int, index: int,
+              workspace: int, ws_bytes: int, stream: int | None) -> None:
+    _check(load().tq_search(ctypes.byref(q), query, int(nq), ctypes.byref(db), int(n), int(k), scores, index,
+                            workspace, int(ws_bytes), stream), "tq_search")

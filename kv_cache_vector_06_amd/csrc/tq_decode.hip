@@ -459,9 +459,11 @@ struct Stage {
   static constexpr int vn = kn + 128;
   static constexpr int kg = vn + 128;
   static constexpr int bytes = kg + (PROD ? 128 : 0);
-  // load instructions per block: codes, sketch (32 lanes), norms and γ (32 lanes, 4 bytes each)
+  // load instructions per block: codes, sketch (32 lanes), norms and γ (32
+  // lanes, 4 bytes each); BV = 0 stages keys only (the value norms' slot stays
+  // reserved so that the norm offsets do not move)
   static constexpr int dma = RowLoads<BK>::full + RowLoads<BK>::half + (PROD ? 1 : 0) +
-                             RowLoads<BV>::full + RowLoads<BV>::half + (PROD ? 3 : 2);
+                             RowLoads<BV>::full + RowLoads<BV>::half + 1 + (BV > 0 ? 1 : 0) + (PROD ? 1 : 0);
 };
 
 // Row r (0..31) of a staged value block holds token 16(r/16) + 4(r%4) + (r%16)/4,
@@ -490,9 +492,11 @@ __device__ __forceinline__ DmaLane dma_lane(int lane) {
       d.kcol[j] = 16 * (L % BK);
       d.koff[j] = 16 * L;
     }
-    d.vtok[j] = vrow_token(L / BV);
-    d.vcol[j] = 16 * (L % BV);
-    d.voff[j] = d.vtok[j] * (16 * BV) + d.vcol[j];
+    if constexpr (BV > 0) {
+      d.vtok[j] = vrow_token(L / BV);
+      d.vcol[j] = 16 * (L % BV);
+      d.voff[j] = d.vtok[j] * (16 * BV) + d.vcol[j];
+    }
   }
   d.ntok = lane & 31;
   return d;
@@ -551,7 +555,7 @@ __device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t l
       __builtin_amdgcn_global_load_lds(src(vc, VR, d.vtok[vj], d.vcol[vj], d.voff[vj]),
                                        TQ_LDS(st + L::vc + 1024 * vj), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(nsrc(kn), TQ_LDS(st + L::kn), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(nsrc(vn), TQ_LDS(st + L::vn), 4, 0, 0);
+    if constexpr (BV > 0) __builtin_amdgcn_global_load_lds(nsrc(vn), TQ_LDS(st + L::vn), 4, 0, 0);
     if constexpr (PROD) __builtin_amdgcn_global_load_lds(nsrc(kg), TQ_LDS(st + L::kg), 4, 0, 0);
   }
 }
@@ -587,10 +591,13 @@ __device__ __forceinline__ StageOffsets stage_offsets(int n, int g) {
 
 // Read a staged block into registers. The wait for the block's loads (all
 // but the newest `pending` loads of this wavefront done) and the wait for the
-// LDS reads are inside each asm statement, so no output is used early.
+// LDS reads are inside each asm statement, so no output is used early. The
+// reads land asynchronously while later reads of the same statement still use
+// their address registers, so every output is early-clobber (never shares a
+// register with an input), and no statement has an output that goes unused.
 #define TQ_VMW "s_waitcnt vmcnt(%[pend])\n\t"
-#define TQ_NORMS "ds_read_b128 %[n0], %[an]\n\tds_read_b128 %[n1], %[an] offset:64\n\t"       \
-                 "ds_read_b128 %[n2], %[an] offset:128\n\tds_read_b128 %[n3], %[an] offset:192\n\t"
+#define TQ_NORMS "ds_read_b128 %[n0], %[an]\n\tds_read_b128 %[n1], %[an] offset:64\n\t"
+#define TQ_VNORMS "ds_read_b128 %[n2], %[an] offset:128\n\tds_read_b128 %[n3], %[an] offset:192\n\t"
 #define TQ_GAMMA "ds_read_b128 %[n4], %[an] offset:256\n\tds_read_b128 %[n5], %[an] offset:320\n\t"
 #define TQ_QJ "ds_read2_b32 %[q0], %[aq] offset1:64\n\t"
 #define TQ_LGK "s_waitcnt lgkmcnt(0)"
@@ -619,24 +626,32 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 #define TQ_KR2 "ds_read2_b64 %[ka], %[ak] offset1:64\n\t"
 #define TQ_KR1 "ds_read2_b32 %[k0], %[ak] offset1:64\n\t"
 #define TQ_KR0 ""
-#define TQ_KO4 , [ka] "=v"(ka), [kb] "=v"(kb)
-#define TQ_KO3 , [k0] "=v"(k0), [k1] "=v"(k1), [k2] "=v"(k2)
-#define TQ_KO2 , [ka] "=v"(ka)
-#define TQ_KO1 , [k0] "=v"(k0)
+#define TQ_KO4 , [ka] "=&v"(ka), [kb] "=&v"(kb)
+#define TQ_KO3 , [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2)
+#define TQ_KO2 , [ka] "=&v"(ka)
+#define TQ_KO1 , [k0] "=&v"(k0)
 #define TQ_KO0
-#define TQ_OUT4 [n0] "=v"(n0), [n1] "=v"(n1), [n2] "=v"(n2), [n3] "=v"(n3), [v0] "=v"(v0), [v1] "=v"(v1), \
-                [v2] "=v"(v2), [v3] "=v"(v3)
-#define TQ_VO3 , [v4] "=v"(v4), [v5] "=v"(v5), [v6] "=v"(v6), [v7] "=v"(v7)
-#define TQ_VON
-#define TQ_OUTP , [n4] "=v"(n4), [n5] "=v"(n5), [q0] "=v"(q0)
+#define TQ_OUT2 [n0] "=&v"(n0), [n1] "=&v"(n1)
+#define TQ_NO3 , [n2] "=&v"(n2), [n3] "=&v"(n3)
+#define TQ_NON TQ_NO3
+#define TQ_NO0
+#define TQ_NR3 TQ_VNORMS
+#define TQ_NRN TQ_VNORMS
+#define TQ_NR0 ""
+#define TQ_VO3 , [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3), \
+               [v4] "=&v"(v4), [v5] "=&v"(v5), [v6] "=&v"(v6), [v7] "=&v"(v7)
+#define TQ_VON , [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3)
+#define TQ_VO0
+#define TQ_OUTP , [n4] "=&v"(n4), [n5] "=&v"(n5), [q0] "=&v"(q0)
 #define TQ_IN [pend] "n"(PEND), [an] "v"(an), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1), [ak] "v"(ak)
 #define TQ_K(VP, VS, KB)                                                                           \
   if constexpr (BK == KB) {                                                                        \
     if constexpr (PROD)                                                                            \
-      asm volatile(TQ_VMW TQ_NORMS TQ_GAMMA TQ_QJ VP TQ_KR##KB TQ_LGK                              \
-                   : TQ_OUT4 TQ_VO##VS TQ_OUTP TQ_KO##KB : TQ_IN : "memory");                      \
+      asm volatile(TQ_VMW TQ_NORMS TQ_NR##VS TQ_GAMMA TQ_QJ VP TQ_KR##KB TQ_LGK                    \
+                   : TQ_OUT2 TQ_NO##VS TQ_VO##VS TQ_OUTP TQ_KO##KB : TQ_IN : "memory");            \
     else                                                                                           \
-      asm volatile(TQ_VMW TQ_NORMS VP TQ_KR##KB TQ_LGK : TQ_OUT4 TQ_VO##VS TQ_KO##KB : TQ_IN : "memory"); \
+      asm volatile(TQ_VMW TQ_NORMS TQ_NR##VS VP TQ_KR##KB TQ_LGK                                   \
+                   : TQ_OUT2 TQ_NO##VS TQ_VO##VS TQ_KO##KB : TQ_IN : "memory");                    \
   }
 #define TQ_V(VP, VS) TQ_K(VP, VS, 0) TQ_K(VP, VS, 1) TQ_K(VP, VS, 2) TQ_K(VP, VS, 3) TQ_K(VP, VS, 4)
   // slot i is 4 rows (16·BV dwords) after slot i-1; pairs (0, 1) and (2, 3) of each tile
@@ -644,6 +659,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
   if constexpr (BV == 4) { TQ_V(TQ_VPAIRS(64, 128, 192), N) }
   if constexpr (BV == 2) { TQ_V(TQ_VPAIRS(32, 64, 96), N) }
   if constexpr (BV == 1) { TQ_V(TQ_VPAIRS(16, 32, 48), N) }
+  if constexpr (BV == 0) { TQ_V("", 0) }
 #undef TQ_V
 #undef TQ_K
 #undef TQ_VPAIRS
@@ -658,9 +674,16 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 #undef TQ_KO2
 #undef TQ_KO1
 #undef TQ_KO0
-#undef TQ_OUT4
+#undef TQ_OUT2
+#undef TQ_NO3
+#undef TQ_NON
+#undef TQ_NO0
+#undef TQ_NR3
+#undef TQ_NRN
+#undef TQ_NR0
 #undef TQ_VO3
 #undef TQ_VON
+#undef TQ_VO0
 #undef TQ_OUTP
 #undef TQ_IN
   if constexpr (BK == 4) {
@@ -678,7 +701,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     R.nk[i] = n0[i]; R.nk[4 + i] = n1[i];
-    R.nv[i] = n2[i]; R.nv[4 + i] = n3[i];
+    if constexpr (BV > 0) { R.nv[i] = n2[i]; R.nv[4 + i] = n3[i]; }
     if constexpr (PROD) { R.gk[i] = n4[i]; R.gk[4 + i] = n5[i]; }
   }
   if constexpr (PROD) { R.qw[0] = q0[0]; R.qw[1] = q0[1]; }
@@ -686,7 +709,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
     const u32x2 vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
 #pragma unroll
     for (int j = 0; j < 8; ++j) { R.vw[j] = vv[j][0]; R.vw2[j] = vv[j][1]; }
-  } else {
+  } else if constexpr (BV > 0) {
     const u32x2 vv[4] = {v0, v1, v2, v3};
 #pragma unroll
     for (int k = 0; k < 4; ++k) { R.vw[2 * k] = vv[k][0]; R.vw[2 * k + 1] = vv[k][1]; }
@@ -694,6 +717,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 }
 #undef TQ_VMW
 #undef TQ_NORMS
+#undef TQ_VNORMS
 #undef TQ_GAMMA
 #undef TQ_QJ
 #undef TQ_LGK
@@ -756,6 +780,59 @@ __device__ __forceinline__ u32x4 pv_operand(const uint32_t (&X)[4], const uint32
   return bv;
 }
 
+// Scores of a staged block: column n = head n % 8 (hi part for n < 8, lo part
+// above); slot j = 4τ + i is token 16τ + 4g + i. The score is sc·iqs.
+template <int BK, bool PROD, int BV>
+__device__ __forceinline__ void block_scores(const Block<BK, PROD, BV>& R, const Luts& T, const u32x4 (&bq)[4],
+                                             const u32x4 (&bs)[4], float (&sc)[8]) {
+  // Every table read of both tiles' score operands is issued before the
+  // first product, so the block waits for one LDS round trip instead of one
+  // per product (the scheduler would otherwise put each read just before its
+  // product); the value-table reads follow the products and complete while
+  // the softmax runs.
+  u32x4 kh[2][4], kl[2][4], sg[2][4];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    if constexpr (BK > 0) {
+      key_operands<BK, 0>(R.kw[tau], T.k, T.klane, kh[tau][0], kl[tau][0]);
+      key_operands<BK, 1>(R.kw[tau], T.k, T.klane, kh[tau][1], kl[tau][1]);
+      key_operands<BK, 2>(R.kw[tau], T.k, T.klane, kh[tau][2], kl[tau][2]);
+      key_operands<BK, 3>(R.kw[tau], T.k, T.klane, kh[tau][3], kl[tau][3]);
+    }
+    if constexpr (PROD) {
+      sg[tau][0] = sign_operand<0>(R.qw[tau], T.q, T.qlane);
+      sg[tau][1] = sign_operand<1>(R.qw[tau], T.q, T.qlane);
+      sg[tau][2] = sign_operand<2>(R.qw[tau], T.q, T.qlane);
+      sg[tau][3] = sign_operand<3>(R.qw[tau], T.q, T.qlane);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  // u = ⟨q', c⟩ + γ⟨q_S, s⟩ for this lane's part; the row rotation adds the
+  // other part, and the key norm and the query scale finish the score.
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    f32x4 dm = f32x4{0.f, 0.f, 0.f, 0.f}, dq = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BK > 0) {
+#pragma unroll
+      for (int S = 0; S < 4; ++S) {
+        dm = mfma(kh[tau][S], bq[S], dm);
+        if constexpr (BK == 4) dm = mfma(kl[tau][S], bq[S], dm);
+      }
+    }
+    if constexpr (PROD) {
+#pragma unroll
+      for (int S = 0; S < 4; ++S) dq = mfma(sg[tau][S], bs[S], dq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * tau + i;
+      const float u = PROD ? fmaf(R.gk[j], dq[i], dm[i]) : dm[i];
+      sc[j] = add_ror8(u) * R.nk[j];       // the score is sc·iqs
+    }
+  }
+}
+
 template <int BK, bool PROD, int BV>
 __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint32_t t0, uint32_t t_end,
                                              int n, int g, const Luts& T, const u32x4 (&bq)[4],
@@ -784,54 +861,8 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
     X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
     Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
   }
-  // ---- scores: column n = head n % 8 (hi part for n < 8, lo part above) ----
-  // Every table read of both tiles' score operands is issued before the
-  // first product, so the block waits for one LDS round trip instead of one
-  // per product (the scheduler would otherwise put each read just before its
-  // product); the value-table reads follow the products and complete while
-  // the softmax runs.
-  u32x4 kh[2][4], kl[2][4], sg[2][4];
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    if constexpr (BK > 0) {
-      key_operands<BK, 0>(R.kw[tau], T.k, T.klane, kh[tau][0], kl[tau][0]);
-      key_operands<BK, 1>(R.kw[tau], T.k, T.klane, kh[tau][1], kl[tau][1]);
-      key_operands<BK, 2>(R.kw[tau], T.k, T.klane, kh[tau][2], kl[tau][2]);
-      key_operands<BK, 3>(R.kw[tau], T.k, T.klane, kh[tau][3], kl[tau][3]);
-    }
-    if constexpr (PROD) {
-      sg[tau][0] = sign_operand<0>(R.qw[tau], T.q, T.qlane);
-      sg[tau][1] = sign_operand<1>(R.qw[tau], T.q, T.qlane);
-      sg[tau][2] = sign_operand<2>(R.qw[tau], T.q, T.qlane);
-      sg[tau][3] = sign_operand<3>(R.qw[tau], T.q, T.qlane);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  // u = ⟨q', c⟩ + γ⟨q_S, s⟩ for this lane's part; the row rotation adds the
-  // other part, and the key norm and the query scale finish the score.
   float sc[8];
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    f32x4 dm = f32x4{0.f, 0.f, 0.f, 0.f}, dq = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BK > 0) {
-#pragma unroll
-      for (int S = 0; S < 4; ++S) {
-        dm = mfma(kh[tau][S], bq[S], dm);
-        if constexpr (BK == 4) dm = mfma(kl[tau][S], bq[S], dm);
-      }
-    }
-    if constexpr (PROD) {
-#pragma unroll
-      for (int S = 0; S < 4; ++S) dq = mfma(sg[tau][S], bs[S], dq);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * tau + i;
-      const float u = PROD ? fmaf(R.gk[j], dq[i], dm[i]) : dm[i];
-      sc[j] = add_ror8(u) * R.nk[j];       // the score is sc·iqs
-    }
-  }
+  block_scores<BK, PROD, BV>(R, T, bq, bs, sc);
   // ---- P·V operands: column n = dim 8n + r, rows = token slots ----
   u32x4 bv[8];
   bv[0] = pv_operand<0>(X, Y, T);
@@ -1212,6 +1243,311 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 4. Inner-product search over a packed database
+// ---------------------------------------------------------------------------
+// The k database vectors with the largest ⟨q, x̃⟩ for each query ("内存厂商的
+// 噩梦来了…" (wuyi.wiki) section 6.4: nearest-neighbour search by inner product
+// over TurboQuant-encoded vectors). The scores are the decode kernel's key
+// scores with the softmax scale chosen so that they are plain inner
+// products: query operands from query_prep_kernel for groups of up to 8
+// queries, then one workgroup per (split, query group) streams its share of
+// the database through the decode kernel's LDS staging and tables, keys only.
+//
+// A candidate (score, index) is better than another when its score is larger,
+// or equal with a smaller index. As one 64-bit key: the score's
+// order-preserving bits above the complement of the index; 0 is below every
+// candidate.
+constexpr int kSearchMaxK = 32;
+constexpr int kCand = 64;          // candidate slots per (wavefront, query)
+
+__device__ __forceinline__ uint64_t cand_key(float s, uint32_t idx) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, s + 0.0f);   // -0 ranks as +0
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (uint64_t(o) << 32) | uint64_t(~idx);
+}
+__device__ __forceinline__ float key_score(uint64_t k) {
+  const uint32_t o = uint32_t(k >> 32);
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~uint32_t(k); }
+
+// Bitonic sort of one key per lane over the 64 lanes, best (largest) first.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t k, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t plo = __shfl_xor(uint32_t(k), stride, 64);
+      const uint32_t phi = __shfl_xor(uint32_t(k >> 32), stride, 64);
+      const uint64_t p = (uint64_t(phi) << 32) | plo;
+      // blocks of `size` lanes alternate direction (the last block is one
+      // descending run); in a pair the lower lane of a descending block keeps
+      // the larger key
+      const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      k = keep_max ? (k > p ? k : p) : (k < p ? k : p);
+    }
+  }
+  return k;
+}
+
+// Candidate buffers of a search workgroup: per (wavefront, query) up to kCand
+// keys, their count and the score a new candidate must beat.
+struct SearchLds {
+  uint64_t cand[kDecWaves][kMaxHeads][kCand];
+  uint32_t cnt[kDecWaves][kMaxHeads];
+  float thr[kDecWaves][kMaxHeads];
+};
+
+// Keep the best k of query c's candidates (sorted, best first); once k are
+// held, the k-th score is the bar for new ones. Whole wavefront.
+__device__ __forceinline__ void compact_cands(SearchLds& S, int wave, int c, int k, int lane) {
+  const uint32_t m = S.cnt[wave][c];
+  uint64_t key = uint32_t(lane) < m ? S.cand[wave][c][lane] : 0ull;
+  key = wave_sort_desc(key, lane);
+  if (lane < k) S.cand[wave][c][lane] = key;
+  const uint32_t klo = __shfl(uint32_t(key), k - 1, 64), khi = __shfl(uint32_t(key >> 32), k - 1, 64);
+  if (lane == 0) {
+    S.cnt[wave][c] = m < uint32_t(k) ? m : uint32_t(k);
+    S.thr[wave][c] = m >= uint32_t(k) ? key_score((uint64_t(khi) << 32) | klo) : -INFINITY;
+  }
+}
+
+struct SearchArgs {
+  const uint8_t* kc;
+  const float* kn;
+  const uint8_t* kq;
+  const float* kg;
+  int64_t n;
+  const float* kcent;
+  const PrepHeader* kh;
+  const uint8_t* ws;
+  uint64_t* part;     // [units][nsplit][8][k] best-first keys of each split
+  int ngroups, nq, nsplit, split_len, k;
+};
+
+template <int BK, bool PROD, bool AL>
+__global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs a) {
+  using SL = Stage<BK, PROD, 0>;
+  using KL = KLut<BK>;
+  __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
+  __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][kStages * SL::bytes];
+  __shared__ SearchLds S;
+  __shared__ float cent[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, unit = blockIdx.y;
+  const int gc = min(kMaxHeads, a.nq - unit * kMaxHeads);
+  const int k = a.k;
+  constexpr int nthr = kDecWaves * 64;
+
+  // ---- query operands and centroids ----
+  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
+  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
+  u32x4 bq[4], bs[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bq[s] = fr[s * 64 + lane];
+    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
+  }
+  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
+  if (tid < 16) cent[tid] = (BK > 0 && tid < (1 << BK)) ? a.kcent[tid] * (kCentScale * a.kh->sigma) : 0.f;
+  if (lane < kMaxHeads) {
+    S.cnt[wave][lane] = 0u;
+    S.thr[wave][lane] = -INFINITY;
+  }
+
+  // ---- token range of this wavefront ----
+  const int64_t per_wave = a.split_len / kDecWaves;
+  const int64_t tb = int64_t(split) * a.split_len + wave * per_wave;
+  const int64_t te = min(tb + per_wave, a.n);
+  const uint32_t t_begin = static_cast<uint32_t>(tb);
+  const uint32_t t_end = te > tb ? static_cast<uint32_t>(te) : t_begin;
+  const uint32_t last = static_cast<uint32_t>(a.n - 1);
+  const uint8_t* kc = BK > 0 ? a.kc : reinterpret_cast<const uint8_t*>(a.kn);
+  const uint8_t* kq = PROD ? a.kq : reinterpret_cast<const uint8_t*>(a.kn);
+  const float* kg = PROD ? a.kg : a.kn;
+  __syncthreads();   // the centroids
+
+  uint8_t* ring = &stage[wave][0];
+  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const StageOffsets so = stage_offsets<BK, PROD, 0>(n, g);
+  const DmaLane dl = dma_lane<BK, 0>(lane);
+  const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
+  if (nblk > 0) stage_block<BK, PROD, 0, AL>(ring, t_begin, last, lane, dl, kc, kq, kc, a.kn, a.kn, kg);
+  if (nblk > 1)
+    stage_block<BK, PROD, 0, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, kc, a.kn, a.kn, kg);
+
+  // ---- key and sketch tables (as in the decode kernel) ----
+  if constexpr (BK > 0) {
+    constexpr int KK = 1 << BK;
+    if constexpr (KL::byte_indexed) {
+      for (int idx = tid; idx < 256 * 16; idx += nthr) {
+        const int e = idx >> 4, c = idx & 15;
+        uint32_t w0, w1;
+        if constexpr (BK == 4) {
+          uint16_t h0, l0, h1, l1;
+          split_h(cent[e & 15], h0, l0);
+          split_h(cent[e >> 4], h1, l1);
+          w0 = uint32_t(h0) | (uint32_t(h1) << 16);
+          w1 = uint32_t(l0) | (uint32_t(l1) << 16);
+        } else {
+          w0 = pack_h2(cent[e & 3], cent[(e >> 2) & 3]);
+          w1 = pack_h2(cent[(e >> 4) & 3], cent[e >> 6]);
+        }
+        *reinterpret_cast<u32x2*>(tab + 256 * e + kTabK + 8 * c) = u32x2{w0, w1};
+      }
+    } else if constexpr (KL::priv) {
+      for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
+        const int e = idx / kCopies, c = idx % kCopies;
+        *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) = pack_h2(cent[e & (KK - 1)], cent[e >> BK]);
+      }
+    } else {
+      uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
+      for (int e = tid; e < KL::entries; e += nthr) {
+        constexpr int per = KL::per;
+        uint16_t hi[8];
+#pragma unroll
+        for (int i = 0; i < per; ++i) hi[i] = f2h_bits(cent[(e >> (BK * i)) & (KK - 1)]);
+#pragma unroll
+        for (int i = 0; i < per / 2; ++i) lk[e * KL::dwords + i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
+      }
+    }
+  }
+  if constexpr (PROD) {
+    for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
+      const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
+      const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
+      const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
+      *reinterpret_cast<uint32_t*>(lut_q + 256 * e + 8 * c + 4 * w) = s0 | (s1 << 16);
+    }
+  }
+  Luts T;
+  const uint32_t cp = lane & 31;
+  T.k = KL::priv ? tab : lut_k;
+  T.q = lut_q;
+  T.v = tab;
+  T.klane = KL::byte_indexed ? kTabK + 8u * (lane & 15) : KL::priv ? kTabK + 4u * cp : 0u;
+  T.qlane = 8u * cp;
+  T.vlane = 4u * cp;
+  __syncthreads();
+
+  // ---- scan: scores of 32 vectors per block; candidates above the bar go to
+  // the buffer of their query (lanes n < 8 hold query n; lanes n + 8 the same
+  // scores) ----
+  const int c = n & 7;
+  float bar = -INFINITY;
+  int cur = 0;
+  for (uint32_t i = 0; i < nblk; ++i) {
+    const uint32_t t0 = t_begin + i * kBlockTok;
+    Block<BK, PROD, 0> R;
+    const uint32_t sb = ring_addr + cur * SL::bytes;
+    if (i + 1 < nblk)
+      read_block<BK, PROD, 0, SL::dma>(R, sb, so);
+    else
+      read_block<BK, PROD, 0, 0>(R, sb, so);
+    if (i + 2 < nblk)
+      stage_block<BK, PROD, 0, AL>(ring + ((cur + 2) % kStages) * SL::bytes, t0 + 2 * kBlockTok, last, lane, dl, kc,
+                                   kq, kc, a.kn, a.kn, kg);
+    float sc[8];
+    block_scores<BK, PROD, 0>(R, T, bq, bs, sc);
+    if (n < 8 && c < gc) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+        const float s = sc[j] * iqs;
+        if (t < t_end && s > bar) {
+          const uint32_t pos = atomicAdd(&S.cnt[wave][c], 1u);
+          if (pos < uint32_t(kCand)) S.cand[wave][c][pos] = cand_key(s, t);
+        }
+      }
+    }
+    // at most 32 new candidates per query per block: compact above 32
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < kMaxHeads; ++q) {
+      if (S.cnt[wave][q] > uint32_t(kCand / 2)) {
+        compact_cands(S, wave, q, k, lane);
+        any = true;
+      }
+    }
+    if (any) bar = S.thr[wave][c];
+    cur = cur + 1 == kStages ? 0 : cur + 1;
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxHeads; ++q) compact_cands(S, wave, q, k, lane);
+  __syncthreads();
+
+  // ---- the workgroup's best k per query: wavefront w merges query w ----
+  if (wave < gc) {
+    const int q = wave;
+    uint64_t best = 0ull;
+    for (int w = 0; w < kDecWaves; ++w) {
+      const uint32_t m = S.cnt[w][q];
+      uint64_t key = 0ull;
+      if (lane < k)
+        key = best;
+      else if (lane >= 32 && uint32_t(lane - 32) < m)
+        key = S.cand[w][q][lane - 32];
+      best = wave_sort_desc(key, lane);
+    }
+    if (lane < k) a.part[((size_t(unit) * a.nsplit + split) * kMaxHeads + q) * a.k + lane] = best;
+  }
+}
+
+// One workgroup per query: the best k over all splits, best first.
+__global__ __launch_bounds__(kDecWaves * 64) void search_merge_kernel(const uint64_t* __restrict__ part, int nsplit,
+                                                                      int k, float* __restrict__ scores,
+                                                                      int64_t* __restrict__ index) {
+  __shared__ uint64_t wbest[kDecWaves][kSearchMaxK];
+  const int qi = blockIdx.x;
+  const int unit = qi / kMaxHeads, q = qi % kMaxHeads;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  // wavefront w merges splits w, w + 8, ...: the running best in lanes
+  // [0, k), the next split's list in lanes [32, 32 + k)
+  uint64_t best = 0ull;
+  for (int s = wave; s < nsplit; s += kDecWaves) {
+    uint64_t key = 0ull;
+    if (lane < k)
+      key = best;
+    else if (lane >= 32 && lane - 32 < k)
+      key = part[((size_t(unit) * nsplit + s) * kMaxHeads + q) * k + (lane - 32)];
+    best = wave_sort_desc(key, lane);
+  }
+  if (lane < k) wbest[wave][lane] = best;
+  __syncthreads();
+  if (wave == 0) {
+    best = 0ull;
+    for (int w = 0; w < kDecWaves; ++w) {
+      uint64_t key = 0ull;
+      if (lane < k)
+        key = best;
+      else if (lane >= 32 && lane - 32 < k)
+        key = wbest[w][lane - 32];
+      best = wave_sort_desc(key, lane);
+    }
+    if (lane < k) {
+      scores[size_t(qi) * k + lane] = key_score(best);
+      index[size_t(qi) * k + lane] = static_cast<int64_t>(key_index(best));
+    }
+  }
+}
+
+template <int BK, bool PROD>
+hipError_t launch_search_t(const SearchArgs& a, bool al, dim3 grid, hipStream_t st) {
+  if (al)
+    hipLaunchKernelGGL((search_scan_kernel<BK, PROD, true>), grid, dim3(kDecWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((search_scan_kernel<BK, PROD, false>), grid, dim3(kDecWaves * 64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int BK, bool PROD, int BV>
 hipError_t launch_attn_t(const AttnArgs& a, bool al, dim3 grid, hipStream_t st) {
   if (al)
@@ -1421,4 +1757,73 @@ extern "C" int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_
   const StepRows r{k_new, v_new, x_dtype, x_row_stride};
   return decode_call(phase, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out,
                      workspace, ws_bytes, stream, &r);
+}
+
+extern "C" size_t tq_search_workspace(int nq, int64_t n, int k) {
+  if (nq < 1 || n < 1 || n > kMaxCtx || k < 1 || k > kSearchMaxK || k > n) return 0;
+  const Plan p = make_plan(1, nq, 1, n);
+  return p.part_off + size_t(p.units) * p.nsplit * kMaxHeads * k * sizeof(uint64_t);
+}
+
+extern "C" int tq_search(const tq_quantizer* q, const float* query, int nq, const tq_packed* db, int64_t n, int k,
+                         float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream) {
+  const int st = tq_check_quantizer(q);
+  if (st != TQ_OK) return st;
+  if (query == nullptr || db == nullptr || scores == nullptr || index == nullptr || workspace == nullptr)
+    return TQ_ERR_INVALID_ARG;
+  if (nq < 1 || n < 1 || k < 1 || k > n) return TQ_ERR_INVALID_ARG;
+  if (k > kSearchMaxK || n > kMaxCtx) return TQ_ERR_UNSUPPORTED;
+  const bool prod = q->variant == TQ_PROD;
+  const int bk = prod ? q->bits - 1 : q->bits;
+  if (db->norms == nullptr || (bk > 0 && db->codes == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (prod && (db->qjl == nullptr || db->gammas == nullptr)) return TQ_ERR_INVALID_ARG;
+  if (!aligned(query, 16) || (bk > 0 && !aligned(db->codes, 16)) || !aligned(db->norms, 4) ||
+      (prod && (!aligned(db->qjl, 16) || !aligned(db->gammas, 4))))
+    return TQ_ERR_INVALID_ARG;
+  const Plan p = make_plan(1, nq, 1, n);
+  const size_t need = p.part_off + size_t(p.units) * p.nsplit * kMaxHeads * k * sizeof(uint64_t);
+  if (ws_bytes < need || !aligned(workspace, 256)) return TQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const PrepHeader* kh = static_cast<const PrepHeader*>(q->prep);
+  // query operands with log2(e)·scale = 1: the scores are plain inner products
+  PrepArgs pa{query, q->rot, prod ? q->proj : nullptr, kh, 0.69314718055994531f, nq, 1, nq, p.ngroups, p.units, ws};
+  hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
+  if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+  SearchArgs sa;
+  sa.kc = db->codes;
+  sa.kn = db->norms;
+  sa.kq = db->qjl;
+  sa.kg = db->gammas;
+  sa.n = n;
+  sa.kcent = q->centroids;
+  sa.kh = kh;
+  sa.ws = ws;
+  sa.part = reinterpret_cast<uint64_t*>(ws + p.part_off);
+  sa.ngroups = p.ngroups;
+  sa.nq = nq;
+  sa.nsplit = p.nsplit;
+  sa.split_len = p.split_len;
+  sa.k = k;
+  const dim3 grid(p.nsplit, p.units);
+  const bool al = (n % kBlockTok) == 0;
+  hipError_t e;
+  if (!prod) {
+    switch (bk) {
+      case 1: e = launch_search_t<1, false>(sa, al, grid, s); break;
+      case 2: e = launch_search_t<2, false>(sa, al, grid, s); break;
+      case 3: e = launch_search_t<3, false>(sa, al, grid, s); break;
+      default: e = launch_search_t<4, false>(sa, al, grid, s); break;
+    }
+  } else {
+    switch (bk) {
+      case 0: e = launch_search_t<0, true>(sa, al, grid, s); break;
+      case 1: e = launch_search_t<1, true>(sa, al, grid, s); break;
+      case 2: e = launch_search_t<2, true>(sa, al, grid, s); break;
+      default: e = launch_search_t<3, true>(sa, al, grid, s); break;
+    }
+  }
+  if (e != hipSuccess) return TQ_ERR_HIP;
+  hipLaunchKernelGGL(search_merge_kernel, dim3(nq), dim3(kDecWaves * 64), 0, s, sa.part, p.nsplit, k, scores, index);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

@@ -142,3 +142,24 @@ class Decoder:
         else:
             L.tq_decode_step_phase(phase, *args)
         return out
+
+
+def search(q: Quantizer, queries: torch.Tensor, db: Packed, k: int, n: int | None = None,
+           workspace: torch.Tensor | None = None):
+    """Inner-product top-k of each query row over the first n vectors of the
+    packed database `db` (tq_search). Returns (scores [nq, k] float32,
+    index [nq, k] int64), best first."""
+    if queries.dim() != 2 or queries.dtype != torch.float32 or not queries.is_contiguous():
+        raise ValueError("queries must be contiguous float32 [nq, d]")
+    nq = queries.shape[0]
+    n = db.n if n is None else n
+    ws_bytes = L.tq_search_workspace(nq, n, k)
+    if ws_bytes == 0:
+        raise ValueError("invalid search sizes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=queries.device)
+    scores = torch.empty((nq, k), dtype=torch.float32, device=queries.device)
+    index = torch.empty((nq, k), dtype=torch.int64, device=queries.device)
+    L.tq_search(q.c, queries.data_ptr(), nq, db.c, n, k, scores.data_ptr(), index.data_ptr(),
+                workspace.data_ptr(), ws_bytes, _stream())
+    return scores, index

@@ -158,3 +158,35 @@ def test_unknown_rotation_is_rejected():
     assert lib.tq_encode(ctypes.byref(q), 1 << 20, L.TQ_BF16, 10, 128, ctypes.byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
     q.rotation = L.TQ_ROT_HADAMARD
     assert lib.tq_encode(ctypes.byref(q), 1 << 20, 7, 10, 128, ctypes.byref(pk), None, None) == L.TQ_ERR_UNSUPPORTED
+
+
+def test_search_argument_errors_are_synchronous():
+    lib = L.load()
+    q = _fake_quantizer()
+    pk = L.tq_packed(1 << 20, 1 << 20, None, None)
+    byref = ctypes.byref
+    ws = L.tq_search_workspace(10, 1000, 8)
+    assert ws > 0
+    assert L.tq_search_workspace(0, 1000, 8) == 0
+    assert L.tq_search_workspace(10, 1000, 0) == 0
+    assert L.tq_search_workspace(10, 1000, 33) == 0
+    assert L.tq_search_workspace(10, 5, 8) == 0
+    assert L.tq_search_workspace(10, 10 ** 6, 8) >= ws
+
+    def call(**kw):
+        a = dict(dict(q=byref(q), query=1 << 20, nq=10, db=byref(pk), n=1000, k=8, s=1 << 20, i=1 << 21,
+                      ws=1 << 22, wsb=ws), **kw)
+        return lib.tq_search(a["q"], a["query"], a["nq"], a["db"], a["n"], a["k"], a["s"], a["i"], a["ws"], a["wsb"],
+                             None)
+
+    assert call(query=None) == L.TQ_ERR_INVALID_ARG
+    assert call(query=(1 << 20) + 4) == L.TQ_ERR_INVALID_ARG
+    assert call(s=None) == L.TQ_ERR_INVALID_ARG
+    assert call(i=None) == L.TQ_ERR_INVALID_ARG
+    assert call(nq=0) == L.TQ_ERR_INVALID_ARG
+    assert call(k=0) == L.TQ_ERR_INVALID_ARG
+    assert call(n=5) == L.TQ_ERR_INVALID_ARG            # k > n
+    assert call(k=33, n=1000) == L.TQ_ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == L.TQ_ERR_WORKSPACE
+    assert call(ws=(1 << 22) + 64) == L.TQ_ERR_WORKSPACE
+    assert call(q=byref(_fake_quantizer(bits=3, variant=L.TQ_PROD))) == L.TQ_ERR_INVALID_ARG   # no sketch arrays
