@@ -105,14 +105,18 @@ def cpu_baseline(cfg, units=6):
     }
 
 
-def bytes_per_token(cfg) -> int:
-    """Algorithmic packed bytes per token per KV head: codes + fp32 norm for
-    keys and values, plus the 16-byte sketch and fp32 γ for prod keys."""
+def key_bytes(cfg) -> int:
+    """Packed bytes of one key vector: codes + fp32 norm, plus the 16-byte
+    sketch and fp32 γ for prod keys."""
     d = cfg.d
     kb = cfg.k_bits - 1 if cfg.k_variant == "prod" else cfg.k_bits
-    k = d * kb // 8 + 4 + ((d // 8 + 4) if cfg.k_variant == "prod" else 0)
-    v = d * cfg.v_bits // 8 + 4
-    return k + v
+    return d * kb // 8 + 4 + ((d // 8 + 4) if cfg.k_variant == "prod" else 0)
+
+
+def bytes_per_token(cfg) -> int:
+    """Algorithmic packed bytes per token per KV head: the key's, and the
+    value's codes + fp32 norm."""
+    return key_bytes(cfg) + cfg.d * cfg.v_bits // 8 + 4
 
 
 def main():
@@ -291,6 +295,40 @@ def main():
     log(f"[bench] {cfg3.name}: split attention after a cache flush {cfg3_us:.1f} us, "
         f"{cfg3_bytes / cfg3_us / 1e3:.0f} GB/s")
 
+    # Inner-product search: the first 2^20 key rows as a prod-4 database
+    # (index build = their encode), 64 N(0,1) queries, top 10 each; recall 1@10
+    # against the exact top-1 of the unquantized rows.
+    n_db, nq_s, k_s = 1 << 20, 64, 10
+    db = TA.Packed(kq, n_db, dev)
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    TA.encode(kq, kg[:n_db], db)
+    a_.record()
+    TA.encode(kq, kg[:n_db], db)
+    b_.record()
+    torch.cuda.synchronize()
+    build_ms = a_.elapsed_time(b_)
+    qs_ = torch.from_numpy(np.random.default_rng(cfg.seed_base + 7).standard_normal((nq_s, d)).astype(np.float32)).to(dev)
+    ws_s = torch.empty(TA.L.tq_search_workspace(nq_s, n_db, k_s), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        TA.search(kq, qs_, db, k_s, workspace=ws_s)
+    reps = 20
+    a_.record()
+    for _ in range(reps):
+        _, s_idx = TA.search(kq, qs_, db, k_s, workspace=ws_s)
+    b_.record()
+    torch.cuda.synchronize()
+    s_us = a_.elapsed_time(b_) / reps * 1e3
+    top1 = (qs_ @ kg[:n_db].float().T).argmax(dim=1)
+    recall = float((s_idx == top1[:, None]).any(dim=1).float().mean())
+    db_bytes = n_db * key_bytes(cfg)
+    search = {"workload": f"db {n_db} x d{d} prod-{cfg.k_bits}, {nq_s} queries, top {k_s}",
+              "us": round(s_us, 1), "gpairs_s": round(nq_s * n_db / (s_us * 1e-6) / 1e9, 1),
+              "db_gbs": round(db_bytes / (s_us * 1e-6) / 1e9, 1),
+              "db_streamed_gbs": round((nq_s + 7) // 8 * db_bytes / (s_us * 1e-6) / 1e9, 1),
+              "recall_1_at_10": round(recall, 4), "index_build_ms": round(build_ms, 4)}
+    del db, ws_s
+    log(f"[bench] search: {search}")
+
     enc = {}
     enc_roof = None
     if not args.no_encode_sweep:
@@ -355,6 +393,7 @@ def main():
                                    "frac": round(cfg3_bytes / cfg3_us / 1e3 / PEAK_HBM_GBS, 4)},
         "hadamard_step_ms": round(had_ms, 5),
         "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
+        "search": search,
         "encode_mvec_s": enc,
         "encode_roofline": enc_roof,
         "cpu_baseline": cpu,

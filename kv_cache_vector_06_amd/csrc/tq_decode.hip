@@ -1272,45 +1272,97 @@ __device__ __forceinline__ float key_score(uint64_t k) {
 }
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~uint32_t(k); }
 
-// Bitonic sort of one key per lane over the 64 lanes, best (largest) first.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t k, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t plo = __shfl_xor(uint32_t(k), stride, 64);
-      const uint32_t phi = __shfl_xor(uint32_t(k >> 32), stride, 64);
-      const uint64_t p = (uint64_t(phi) << 32) | plo;
-      // blocks of `size` lanes alternate direction (the last block is one
-      // descending run); in a pair the lower lane of a descending block keeps
-      // the larger key
-      const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
-      k = keep_max ? (k > p ? k : p) : (k < p ? k : p);
-    }
+// Value of lane (lane ^ M) of v for M = 1, 2, 4, 8, 16, 32: DPP moves within
+// rows (quad permutes; a half-row mirror, i ^ 7, then the quad reversal,
+// i ^ 3; a rotation by 8) and the gfx950 row swaps across rows, none of which
+// goes through the LDS pipe as a general lane shuffle does.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);          // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);          // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const uint32_t m = __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    return __builtin_amdgcn_update_dpp(0u, m, 0x1B, 0xF, 0xF, false);          // quad_perm 3,2,1,0
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false);         // row_ror 8
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(M == 32, "xor_lane");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? p[0] : p[1];
   }
-  return k;
+}
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+  return (uint64_t(xor_lane<M>(uint32_t(v >> 32), lane)) << 32) | xor_lane<M>(uint32_t(v), lane);
+}
+// Value of lane 63 - lane: the row mirror (i ^ 15), then across rows.
+__device__ __forceinline__ uint64_t reverse_lanes64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, uint32_t(v), 0x140, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, uint32_t(v >> 32), 0x140, 0xF, 0xF, false);
+  return xor_lane64<32>(xor_lane64<16>((uint64_t(hi) << 32) | lo, lane), lane);
 }
 
+// Compare-exchange steps STRIDE, STRIDE/2, ..., 1 of a bitonic network whose
+// blocks of SIZE lanes alternate direction (SIZE = 64: one descending run); in
+// a pair, the lower lane of a descending block keeps the larger key.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint64_t bitonic_steps(uint64_t k, int lane) {
+  const uint64_t p = xor_lane64<STRIDE>(k, lane);
+  const bool keep_max = ((lane & SIZE) == 0) == ((lane & STRIDE) == 0);
+  k = keep_max ? (k > p ? k : p) : (k < p ? k : p);
+  if constexpr (STRIDE > 1)
+    return bitonic_steps<SIZE, STRIDE / 2>(k, lane);
+  else
+    return k;
+}
+template <int SIZE>
+__device__ __forceinline__ uint64_t bitonic_sort_from(uint64_t k, int lane) {
+  k = bitonic_steps<SIZE, SIZE / 2>(k, lane);
+  if constexpr (SIZE < 64)
+    return bitonic_sort_from<SIZE * 2>(k, lane);
+  else
+    return k;
+}
+
+// Bitonic sort of one key per lane over the 64 lanes, best (largest) first.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t k, int lane) { return bitonic_sort_from<2>(k, lane); }
+
+// Merge of a bitonic sequence over the 64 lanes (lanes 0..31 descending,
+// lanes 32..63 ascending) into one descending run: two sorted lists of up to
+// 32 keys, the second loaded in reverse order, in six compare-exchange steps.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t k, int lane) { return bitonic_steps<64, 32>(k, lane); }
+
 // Candidate buffers of a search workgroup: per (wavefront, query) up to kCand
-// keys, their count and the score a new candidate must beat.
+// keys, and the count each wavefront holds at the end of its scan.
 struct SearchLds {
   uint64_t cand[kDecWaves][kMaxHeads][kCand];
   uint32_t cnt[kDecWaves][kMaxHeads];
-  float thr[kDecWaves][kMaxHeads];
 };
 
-// Keep the best k of query c's candidates (sorted, best first); once k are
-// held, the k-th score is the bar for new ones. Whole wavefront.
-__device__ __forceinline__ void compact_cands(SearchLds& S, int wave, int c, int k, int lane) {
-  const uint32_t m = S.cnt[wave][c];
+// A candidate store the compiler does not see as an LDS access: as a plain
+// store it would first wait for every direct-to-LDS load in flight (it cannot
+// tell the candidate buffer from the staging ring), which stalls the scan on
+// the prefetch of the block after next. A wavefront's LDS accesses execute in
+// order, so the compaction's reads still see these stores.
+__device__ __forceinline__ void lds_store_key(uint32_t addr, uint64_t v) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Sort the m (<= kCand) candidates of query c, keep the best k (best first)
+// and return the k-th score, the bar for new candidates (-inf while fewer
+// than k are held). Whole wavefront.
+__device__ __forceinline__ float compact_cands(SearchLds& S, int wave, int c, int k, int lane, uint32_t m) {
   uint64_t key = uint32_t(lane) < m ? S.cand[wave][c][lane] : 0ull;
   key = wave_sort_desc(key, lane);
   if (lane < k) S.cand[wave][c][lane] = key;
-  const uint32_t klo = __shfl(uint32_t(key), k - 1, 64), khi = __shfl(uint32_t(key >> 32), k - 1, 64);
-  if (lane == 0) {
-    S.cnt[wave][c] = m < uint32_t(k) ? m : uint32_t(k);
-    S.thr[wave][c] = m >= uint32_t(k) ? key_score((uint64_t(khi) << 32) | klo) : -INFINITY;
-  }
+  const uint32_t klo = __builtin_amdgcn_readlane(uint32_t(key), k - 1);
+  const uint32_t khi = __builtin_amdgcn_readlane(uint32_t(key >> 32), k - 1);
+  return m >= uint32_t(k) ? key_score((uint64_t(khi) << 32) | klo) : -INFINITY;
 }
 
 struct SearchArgs {
@@ -1326,14 +1378,29 @@ struct SearchArgs {
   int ngroups, nq, nsplit, split_len, k;
 };
 
+// LDS of the search scan: the key table holds only the rows its entries use
+// (no value half), and the rest of the 160 KiB goes to a deeper staging ring
+// than the decode kernel's, since a keys-only block carries half the bytes.
+template <int BK, bool PROD>
+struct SearchPlan {
+  using KL = KLut<BK>;
+  static constexpr int tab_bytes = KL::priv ? KL::entries * 256 : 256;
+  static constexpr int fixed = tab_bytes + KL::bytes + (PROD ? 16 * kCopies * 8 : 16) +
+                               int(sizeof(SearchLds)) + 64 + 1024;
+  static constexpr int ring = (160 * 1024 - fixed) / (kDecWaves * Stage<BK, PROD, 0>::bytes);
+  static constexpr int stages = ring > 4 ? 4 : ring;
+  static_assert(stages >= 2, "search staging ring");
+};
+
 template <int BK, bool PROD, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs a) {
   using SL = Stage<BK, PROD, 0>;
   using KL = KLut<BK>;
-  __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
+  constexpr int NST = SearchPlan<BK, PROD>::stages;
+  __shared__ __attribute__((aligned(256))) uint8_t tab[SearchPlan<BK, PROD>::tab_bytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
   __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][kStages * SL::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][NST * SL::bytes];
   __shared__ SearchLds S;
   __shared__ float cent[16];
 
@@ -1357,10 +1424,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   if (tid < 16) cent[tid] = (BK > 0 && tid < (1 << BK)) ? a.kcent[tid] * (kCentScale * a.kh->sigma) : 0.f;
-  if (lane < kMaxHeads) {
-    S.cnt[wave][lane] = 0u;
-    S.thr[wave][lane] = -INFINITY;
-  }
 
   // ---- token range of this wavefront ----
   const int64_t per_wave = a.split_len / kDecWaves;
@@ -1379,9 +1442,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   const StageOffsets so = stage_offsets<BK, PROD, 0>(n, g);
   const DmaLane dl = dma_lane<BK, 0>(lane);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
-  if (nblk > 0) stage_block<BK, PROD, 0, AL>(ring, t_begin, last, lane, dl, kc, kq, kc, a.kn, a.kn, kg);
-  if (nblk > 1)
-    stage_block<BK, PROD, 0, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, kc, a.kn, a.kn, kg);
+#pragma unroll
+  for (int b = 0; b < NST; ++b)
+    if (uint32_t(b) < nblk)
+      stage_block<BK, PROD, 0, AL>(ring + b * SL::bytes, t_begin + b * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
+                                   a.kn, kg);
 
   // ---- key and sketch tables (as in the decode kernel) ----
   if constexpr (BK > 0) {
@@ -1438,104 +1503,169 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   __syncthreads();
 
   // ---- scan: scores of 32 vectors per block; candidates above the bar go to
-  // the buffer of their query (lanes n < 8 hold query n; lanes n + 8 the same
-  // scores) ----
+  // the buffer of their query. Lanes n and n + 8 hold query n % 8 with equal
+  // scores and keep equal counts; lanes n < 8 store. ----
   const int c = n & 7;
+  const bool live = c < gc;
+  const uint32_t cand_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&S.cand[wave][c][0]));
   float bar = -INFINITY;
+  uint32_t cnt = 0;
   int cur = 0;
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint32_t t0 = t_begin + i * kBlockTok;
     Block<BK, PROD, 0> R;
     const uint32_t sb = ring_addr + cur * SL::bytes;
-    if (i + 1 < nblk)
-      read_block<BK, PROD, 0, SL::dma>(R, sb, so);
+    // the blocks after this one already issued: their loads may stay in flight
+    const uint32_t ahead = min(nblk - 1 - i, uint32_t(NST - 1));
+    if (ahead == uint32_t(NST - 1))
+      read_block<BK, PROD, 0, (NST - 1) * SL::dma>(R, sb, so);
+    else if (NST > 3 && ahead == 2)
+      read_block<BK, PROD, 0, (NST > 3 ? 2 : 0) * SL::dma>(R, sb, so);
+    else if (NST > 2 && ahead == 1)
+      read_block<BK, PROD, 0, (NST > 2 ? 1 : 0) * SL::dma>(R, sb, so);
     else
       read_block<BK, PROD, 0, 0>(R, sb, so);
-    if (i + 2 < nblk)
-      stage_block<BK, PROD, 0, AL>(ring + ((cur + 2) % kStages) * SL::bytes, t0 + 2 * kBlockTok, last, lane, dl, kc,
-                                   kq, kc, a.kn, a.kn, kg);
+    if (i + NST < nblk)
+      stage_block<BK, PROD, 0, AL>(ring + cur * SL::bytes, t0 + NST * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
+                                   a.kn, kg);
     float sc[8];
     block_scores<BK, PROD, 0>(R, T, bq, bs, sc);
-    if (n < 8 && c < gc) {
+    uint32_t msk = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j) {
+      sc[j] *= iqs;
+      const uint32_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+      if (t < t_end && sc[j] > bar) msk |= 1u << j;
+    }
+    if (!live) msk = 0;
+    // slots of this lane's candidates: after those of the lower lane groups
+    // (lanes n + 16g, g = 0..3, hold the same query)
+    const uint32_t nl = __builtin_popcount(msk);
+    const uint32_t n16 = xor_lane<16>(nl, lane);
+    const uint32_t pair = nl + n16;
+    const uint32_t p32 = xor_lane<32>(pair, lane);
+    const uint32_t total = pair + p32;
+    // one candidate per lane per round, lowest slot first (usually one round)
+    uint32_t rem = n < 8 ? msk : 0u;
+    uint32_t pos = cnt + ((g & 1) ? n16 : 0u) + ((g & 2) ? p32 : 0u);
+    while (__ballot(rem != 0u)) {
+      if (rem != 0u) {
+        const uint32_t j = __builtin_ctz(rem);
+        rem &= rem - 1u;
+        const bool b0 = j & 1u, b1 = j & 2u, b2 = j & 4u;
+        const float a0 = b0 ? sc[1] : sc[0], a1 = b0 ? sc[3] : sc[2];
+        const float a2 = b0 ? sc[5] : sc[4], a3 = b0 ? sc[7] : sc[6];
+        const float s = b2 ? (b1 ? a3 : a2) : (b1 ? a1 : a0);
         const uint32_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
-        const float s = sc[j] * iqs;
-        if (t < t_end && s > bar) {
-          const uint32_t pos = atomicAdd(&S.cnt[wave][c], 1u);
-          if (pos < uint32_t(kCand)) S.cand[wave][c][pos] = cand_key(s, t);
-        }
+        if (pos < uint32_t(kCand)) lds_store_key(cand_base + 8 * pos, cand_key(s, t));
+        ++pos;
       }
     }
-    // at most 32 new candidates per query per block: compact above 32
-    bool any = false;
-#pragma unroll
-    for (int q = 0; q < kMaxHeads; ++q) {
-      if (S.cnt[wave][q] > uint32_t(kCand / 2)) {
-        compact_cands(S, wave, q, k, lane);
-        any = true;
+    cnt += total;
+    // at most 32 new candidates per query per block: keep the best k of a
+    // query once it holds more than 32
+    uint64_t over = __ballot(lane < kMaxHeads && cnt > uint32_t(kCand / 2));
+    while (over) {
+      const int q = __builtin_ctzll(over);
+      over &= over - 1;
+      const uint32_t mq = __builtin_amdgcn_readlane(cnt, q);
+      const float thr = compact_cands(S, wave, q, k, lane, mq);
+      if (c == q) {
+        cnt = mq < uint32_t(k) ? mq : uint32_t(k);
+        bar = thr;
       }
     }
-    if (any) bar = S.thr[wave][c];
-    cur = cur + 1 == kStages ? 0 : cur + 1;
+    cur = cur + 1 == NST ? 0 : cur + 1;
   }
-#pragma unroll
-  for (int q = 0; q < kMaxHeads; ++q) compact_cands(S, wave, q, k, lane);
+  for (int q = 0; q < gc; ++q) {
+    const uint32_t mq = __builtin_amdgcn_readlane(cnt, q);
+    compact_cands(S, wave, q, k, lane, mq);
+    if (lane == 0) S.cnt[wave][q] = mq < uint32_t(k) ? mq : uint32_t(k);
+  }
   __syncthreads();
 
-  // ---- the workgroup's best k per query: wavefront w merges query w ----
+  // ---- the workgroup's best k per query: wavefront q merges query q's lists
+  // (each sorted, best first) ----
   if (wave < gc) {
     const int q = wave;
     uint64_t best = 0ull;
     for (int w = 0; w < kDecWaves; ++w) {
       const uint32_t m = S.cnt[w][q];
-      uint64_t key = 0ull;
-      if (lane < k)
-        key = best;
-      else if (lane >= 32 && uint32_t(lane - 32) < m)
-        key = S.cand[w][q][lane - 32];
-      best = wave_sort_desc(key, lane);
+      uint64_t key = best;
+      if (lane >= 32) key = uint32_t(63 - lane) < m ? S.cand[w][q][63 - lane] : 0ull;
+      best = wave_merge_desc(key, lane);
     }
     if (lane < k) a.part[((size_t(unit) * a.nsplit + split) * kMaxHeads + q) * a.k + lane] = best;
   }
 }
 
+// The 32 best of two descending runs of a wavefront's lanes 0..31: a in this
+// call's lanes 0..31, b's lanes 0..31 reversed into lanes 32..63.
+__device__ __forceinline__ uint64_t merge_runs(uint64_t a, uint64_t b, int lane) {
+  const uint64_t r = reverse_lanes64(b, lane);
+  return wave_merge_desc(lane < 32 ? a : r, lane);
+}
+
 // One workgroup per query: the best k over all splits, best first.
+// Wavefront w runs kMergeChains independent merge chains over splits
+// w + 8c + 8·kMergeChains·r (round r), with round r + 1's lists loaded before
+// round r merges; the chains then merge within the wavefront and the
+// wavefronts' runs in a three-level tree.
+constexpr int kMergeChains = 4;
 __global__ __launch_bounds__(kDecWaves * 64) void search_merge_kernel(const uint64_t* __restrict__ part, int nsplit,
                                                                       int k, float* __restrict__ scores,
                                                                       int64_t* __restrict__ index) {
-  __shared__ uint64_t wbest[kDecWaves][kSearchMaxK];
+  __shared__ uint64_t wbest[kDecWaves][32];
   const int qi = blockIdx.x;
   const int unit = qi / kMaxHeads, q = qi % kMaxHeads;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  // wavefront w merges splits w, w + 8, ...: the running best in lanes
-  // [0, k), the next split's list in lanes [32, 32 + k)
-  uint64_t best = 0ull;
-  for (int s = wave; s < nsplit; s += kDecWaves) {
-    uint64_t key = 0ull;
-    if (lane < k)
-      key = best;
-    else if (lane >= 32 && lane - 32 < k)
-      key = part[((size_t(unit) * nsplit + s) * kMaxHeads + q) * k + (lane - 32)];
-    best = wave_sort_desc(key, lane);
+  const uint64_t* lists = part + size_t(unit) * nsplit * kMaxHeads * k;
+  // lanes 32..63 hold a list reversed (lane 63 its best), the rest 0. Every
+  // lane loads from an address inside the lists and the keys it does not hold
+  // are cleared only when merged, so no load sits under a branch and the next
+  // round's loads stay in flight while this round merges.
+  const bool upper = lane >= 32 && 63 - lane < k;
+  const int ek = min(63 - lane, k - 1);
+  auto list_key = [&](int s) -> uint64_t {
+    return lists[(size_t(min(s, nsplit - 1)) * kMaxHeads + q) * k + ek];
+  };
+  constexpr int step = kDecWaves * kMergeChains;
+  uint64_t best[kMergeChains], nxt[kMergeChains];
+#pragma unroll
+  for (int c = 0; c < kMergeChains; ++c) {
+    best[c] = 0ull;
+    nxt[c] = list_key(wave + kDecWaves * c);
   }
-  if (lane < k) wbest[wave][lane] = best;
+  for (int s0 = wave; s0 < nsplit; s0 += step) {
+    uint64_t cur[kMergeChains];
+#pragma unroll
+    for (int c = 0; c < kMergeChains; ++c) {
+      cur[c] = nxt[c];
+      nxt[c] = list_key(s0 + step + kDecWaves * c);
+    }
+#pragma unroll
+    for (int c = 0; c < kMergeChains; ++c) {
+      const uint64_t x = (upper && s0 + kDecWaves * c < nsplit) ? cur[c] : 0ull;
+      best[c] = wave_merge_desc(lane < 32 ? best[c] : x, lane);
+    }
+  }
+  uint64_t b = merge_runs(merge_runs(best[0], best[1], lane), merge_runs(best[2], best[3], lane), lane);
+  if (lane < 32) wbest[wave][lane] = b;
   __syncthreads();
-  if (wave == 0) {
-    best = 0ull;
-    for (int w = 0; w < kDecWaves; ++w) {
-      uint64_t key = 0ull;
-      if (lane < k)
-        key = best;
-      else if (lane >= 32 && lane - 32 < k)
-        key = wbest[w][lane - 32];
-      best = wave_sort_desc(key, lane);
+#pragma unroll
+  for (int span = 1; span < kDecWaves; span *= 2) {
+    if ((wave & (2 * span - 1)) == 0) {
+      const uint64_t o = lane >= 32 ? wbest[wave + span][63 - lane] : 0ull;
+      b = wave_merge_desc(lane < 32 ? b : o, lane);
     }
-    if (lane < k) {
-      scores[size_t(qi) * k + lane] = key_score(best);
-      index[size_t(qi) * k + lane] = static_cast<int64_t>(key_index(best));
-    }
+    __syncthreads();
+    if ((wave & (2 * span - 1)) == 0 && lane < 32) wbest[wave][lane] = b;
+    __syncthreads();
+  }
+  if (wave == 0 && lane < k) {
+    scores[size_t(qi) * k + lane] = key_score(b);
+    index[size_t(qi) * k + lane] = static_cast<int64_t>(key_index(b));
   }
 }
 
