@@ -34,6 +34,14 @@ Readings of points the pages leave open (each is listed in the design doc too):
     plus the 1-bit sketch ([OM] section on QJL; [WY] section 4.3).
   * packing: code j of a vector occupies bits [j·b, j·b+b) of that vector's
     byte string, least significant bit first; sketch bit j is bit j.
+  * outlier-channel split ([OM] section on the 3.5-bit experiment): two
+    independent TurboQuant-mse instances, one on the 32 outlier channels at
+    b+1 bits (codebook for d = 32) and one on the other 96 at b bits
+    (codebook for d = 96), each with its own norm and rotation. The channel
+    list is the caller's (the pages give no selection rule). The printed
+    average, (32·3 + 96·2)/128 = 2.5, is 2.25 bits of codes; the other 0.25
+    bit per channel matches two 16-bit group norms. The counts and widths
+    are kept as printed.
 """
 from __future__ import annotations
 
@@ -48,6 +56,8 @@ __all__ = [
     "encode_mse", "encode_prod", "dequant_mse", "dequant_prod",
     "attention", "decode_attention", "fwht", "hadamard_rotate",
     "search_topk", "recall_1_at_k",
+    "SPLIT_OUTLIERS", "split_positions", "split_widths", "pack_split", "unpack_split",
+    "encode_split", "dequant_split",
 ]
 
 
@@ -296,6 +306,97 @@ def dequant_prod(codes, norms, qjl, gammas, rot, proj, c_m, bits: int):
     base = np.asarray(c_m, np.float64)[idx] @ np.asarray(rot, np.float64)
     corr = (math.sqrt(math.pi / 2) / m) * np.asarray(gammas, np.float64)[:, None] * (s @ np.asarray(proj, np.float64))
     return np.asarray(norms, np.float64)[:, None] * (base + corr)
+
+
+# ---------------------------------------------------------------------------
+# Outlier-channel split  ([OM] section "Thực nghiệm: 3.5 bit…": the 128
+# channels of a head form two groups, 32 outlier channels at one bit more than
+# the 96 regular ones; e.g. 32 at 3 bits + 96 at 2 bits)
+# ---------------------------------------------------------------------------
+
+SPLIT_OUTLIERS = 32
+
+
+def split_positions(d: int = 128):
+    """Where each group's coordinates sit in a split vector's code string (a
+    storage layout, ours): position p holds an outlier coordinate iff
+    p mod 8 < 2. Returns (P_o, P_r): outlier coordinate k sits at P_o[k],
+    regular coordinate k at P_r[k], each group in its own order."""
+    p = np.arange(d)
+    return p[p % 8 < 2], p[p % 8 >= 2]
+
+
+def split_widths(bits: int, d: int = 128):
+    """Code width of each position: bits + 1 at outlier positions, bits elsewhere."""
+    w = np.full(d, bits, np.int64)
+    w[split_positions(d)[0]] = bits + 1
+    return w
+
+
+def pack_split(idx, bits: int) -> np.ndarray:
+    """[N, d] codes in position order → [N, (d·bits + 32)/8] bytes: the codes
+    one after another, position 0 first, each least significant bit first,
+    with the width of its position."""
+    idx = np.asarray(idx, np.int64)
+    N, d = idx.shape
+    w = split_widths(bits, d)
+    stream = []
+    for p in range(d):
+        for k in range(w[p]):
+            stream.append((idx[:, p] >> k) & 1)
+    return np.packbits(np.stack(stream, axis=1).astype(np.uint8), axis=1, bitorder="little")
+
+
+def unpack_split(packed, bits: int, d: int = 128) -> np.ndarray:
+    packed = np.asarray(packed, np.uint8)
+    w = split_widths(bits, d)
+    stream = np.unpackbits(packed, axis=1, bitorder="little").astype(np.int64)
+    out = np.zeros((packed.shape[0], d), np.int64)
+    at = 0
+    for p in range(d):
+        for k in range(w[p]):
+            out[:, p] |= stream[:, at] << k
+            at += 1
+    return out
+
+
+def _regular_channels(ch_o, d: int):
+    mask = np.ones(d, bool)
+    mask[np.asarray(ch_o)] = False
+    return np.nonzero(mask)[0]
+
+
+def encode_split(X, ch_o, rot_o, rot_r, c_o, c_r, bits: int):
+    """Outlier-channel split encode: two independent TurboQuant-mse instances.
+    The outlier channels ch_o (32 raw channel indices, in the order that
+    rot_o's columns follow) are encoded with their own norm, rotation rot_o
+    (32×32) and Lloyd-Max codebook c_o (d = 32, bits + 1 bits); the other 96
+    channels, in increasing order, with rot_r (96×96) and c_r (d = 96, bits).
+    Returns dict(codes=[N, (128·bits+32)/8] uint8, norms=[N, 2] (outlier,
+    regular), idx=[N,128] in position order, idx_o, idx_r)."""
+    X = np.asarray(X, np.float64)
+    d = X.shape[1]
+    ch_r = _regular_channels(ch_o, d)
+    eo = encode_mse(X[:, np.asarray(ch_o)], rot_o, c_o, bits + 1)
+    er = encode_mse(X[:, ch_r], rot_r, c_r, bits)
+    P_o, P_r = split_positions(d)
+    idx = np.zeros((X.shape[0], d), np.int64)
+    idx[:, P_o] = eo["idx"]
+    idx[:, P_r] = er["idx"]
+    return dict(codes=pack_split(idx, bits), norms=np.stack([eo["norms"], er["norms"]], axis=1), idx=idx,
+                idx_o=eo["idx"], idx_r=er["idx"])
+
+
+def dequant_split(codes, norms, ch_o, rot_o, rot_r, c_o, c_r, bits: int, d: int = 128):
+    """x̃ with x̃[ch_o] = n_o Π_oᵀ c_o[idx_o] and x̃[ch_r] = n_r Π_rᵀ c_r[idx_r]."""
+    idx = unpack_split(codes, bits, d)
+    P_o, P_r = split_positions(d)
+    norms = np.asarray(norms, np.float64)
+    ch_r = _regular_channels(ch_o, d)
+    out = np.zeros((idx.shape[0], d))
+    out[:, np.asarray(ch_o)] = norms[:, :1] * (np.asarray(c_o, np.float64)[idx[:, P_o]] @ np.asarray(rot_o, np.float64))
+    out[:, ch_r] = norms[:, 1:] * (np.asarray(c_r, np.float64)[idx[:, P_r]] @ np.asarray(rot_r, np.float64))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -30,6 +30,13 @@ SEED_ROT_V = 1002
 SEED_PROJ = 1003
 SEED_HAD_K = 1004
 SEED_HAD_V = 1005
+# Outlier-channel split: per role (keys, values), the channel list and the
+# rotations of the 32 outlier and the 96 regular channels.
+SEED_SPLIT_CH_K = 1006
+SEED_SPLIT_CH_V = 1007
+SEED_SPLIT_ROT_K = (1008, 1009)
+SEED_SPLIT_ROT_V = (1010, 1011)
+SPLIT_OUTLIER_SCALE = 4.0
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -114,6 +121,30 @@ def lognormal_kv(B: int, H: int, T: int, d: int, seed: int, sigma: float = 0.5,
     return round_bf16(x) if dtype == "bf16" else x
 
 
+def outlier_channels(d: int, seed: int, n: int = 32) -> np.ndarray:
+    """`n` distinct channels out of d, drawn without replacement, in draw order."""
+    return rng(seed).choice(d, size=n, replace=False).astype(np.int64)
+
+
+def split_constants(d: int = 128):
+    """Per role, the outlier-channel split's inputs: dict(ch_k, rk_o, rk_r,
+    ch_v, rv_o, rv_r) with ch_* 32 channel indices and r*_o (32x32), r*_r
+    (96x96) rotations drawn as the dense one is."""
+    n = 32
+    return dict(ch_k=outlier_channels(d, SEED_SPLIT_CH_K, n), rk_o=rotation(n, SEED_SPLIT_ROT_K[0]),
+                rk_r=rotation(d - n, SEED_SPLIT_ROT_K[1]), ch_v=outlier_channels(d, SEED_SPLIT_CH_V, n),
+                rv_o=rotation(n, SEED_SPLIT_ROT_V[0]), rv_r=rotation(d - n, SEED_SPLIT_ROT_V[1]))
+
+
+def split_kv(B: int, H: int, T: int, d: int, seed: int, channels, scale: float = SPLIT_OUTLIER_SCALE,
+             dtype: str = "bf16") -> np.ndarray:
+    """[B,H,T,d] N(0,1) cache whose listed channels (the same in every head)
+    are scaled by `scale`: the per-channel outlier pattern the split is for."""
+    x = rng(seed).standard_normal((B, H, T, d), dtype=np.float32)
+    x[..., np.asarray(channels)] *= np.float32(scale)
+    return round_bf16(x) if dtype == "bf16" else x
+
+
 @dataclasses.dataclass(frozen=True)
 class DecodeConfig:
     """One decode workload: the cache shape, the quantizers and the data recipe."""
@@ -126,9 +157,10 @@ class DecodeConfig:
     k_variant: str      # "mse" or "prod"
     k_bits: int         # total bits per coordinate for keys
     v_bits: int         # bits per coordinate for values (MSE)
-    recipe: str         # "gaussian", "outlier", "lognormal"
+    recipe: str         # "gaussian", "outlier", "lognormal", "split"
     dtype: str          # storage dtype of the raw K/V ("fp32" or "bf16")
     seed_base: int
+    split: bool = False  # outlier-channel split: k_bits / v_bits are the regular channels' bits
 
     @property
     def G(self) -> int:
@@ -142,6 +174,10 @@ CONFIGS = {
     3: DecodeConfig("llama8b_prod3_128k", 1, 8, 32, 131072, 128, "prod", 3, 3, "outlier", "bf16", 30),
     4: DecodeConfig("batch64_b2_16k", 64, 8, 32, 16384, 128, "mse", 2, 2, "lognormal", "bf16", 40),
     5: DecodeConfig("gqa8_prod4_128k_b4", 4, 8, 64, 131072, 128, "prod", 4, 4, "gaussian", "bf16", 50),
+    # outlier-channel split ("2.5-bit": 32 channels at 3 bits + 96 at 2;
+    # "3.5-bit": 4 + 3), mse keys and values, the benchmark's shape
+    6: DecodeConfig("gqa8_split25_128k_b4", 4, 8, 64, 131072, 128, "mse", 2, 2, "split", "bf16", 60, True),
+    7: DecodeConfig("gqa8_split35_128k_b4", 4, 8, 64, 131072, 128, "mse", 3, 3, "split", "bf16", 70, True),
 }
 
 
@@ -162,6 +198,10 @@ def make_kv(cfg: DecodeConfig, T: int | None = None, B: int | None = None):
     elif cfg.recipe == "lognormal":
         k = lognormal_kv(B, cfg.Hkv, T, cfg.d, sk, dtype=cfg.dtype)
         v = lognormal_kv(B, cfg.Hkv, T, cfg.d, sv, dtype=cfg.dtype)
+    elif cfg.recipe == "split":
+        c = split_constants(cfg.d)
+        k = split_kv(B, cfg.Hkv, T, cfg.d, sk, c["ch_k"], dtype=cfg.dtype)
+        v = split_kv(B, cfg.Hkv, T, cfg.d, sv, c["ch_v"], dtype=cfg.dtype)
     else:
         raise ValueError(cfg.recipe)
     return k, v
