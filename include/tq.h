@@ -55,6 +55,7 @@ enum tq_status {
 
 enum tq_variant { TQ_MSE = 0, TQ_PROD = 1 };
 enum tq_rotation { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 };
+enum tq_split { TQ_SPLIT_NONE = 0, TQ_SPLIT_OUTLIER32 = 1 };
 enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 };
 
 /* Head dimension supported by the GPU kernels. */
@@ -110,6 +111,26 @@ int tq_codebook(int d, int bits, double* centroids, double* boundaries, double* 
  *              entries enter the matrix cores (H·diag(s), exact in fp16) and
  *              1/√d is applied in fp32; rot itself must hold that matrix
  *              (the decode merge reads it as given).
+ *   split      TQ_SPLIT_NONE (0), or TQ_SPLIT_OUTLIER32 (1): the outlier-channel
+ *              split of [OM] section "Thực nghiệm: 3.5 bit…" — 32 outlier
+ *              channels at bits+1 bits and the other 96 at `bits` bits, as two
+ *              independent TurboQuant-mse instances (own norm, rotation and
+ *              codebook each). Requires variant TQ_MSE, bits 2 or 3 ("2.5-bit"
+ *              and "3.5-bit"), rotation TQ_ROT_DENSE. Then:
+ *                rot        the two rotations in one block-structured matrix:
+ *                           rot[P_o[k]][ch_o[j]] = Π_o[k][j] (32×32) and
+ *                           rot[P_r[k]][ch_r[j]] = Π_r[k][j] (96×96), zero
+ *                           elsewhere, where P_o = the positions p with
+ *                           p mod 8 < 2 (in increasing order), P_r = the other
+ *                           positions, ch_o = the caller's 32 outlier channels
+ *                           and ch_r = the other channels (both in the order
+ *                           Π_o's / Π_r's columns follow)
+ *                centroids  the regular group's codebook, tq_codebook(96, bits)
+ *                boundaries its midpoints
+ *                centroids_o, boundaries_o  the outlier group's codebook,
+ *                           tq_codebook(32, bits+1), float[2^(bits+1)] and
+ *                           float[2^(bits+1) - 1]
+ *              Unsplit quantizers leave centroids_o / boundaries_o NULL.
  */
 typedef struct tq_quantizer {
   int d;
@@ -121,6 +142,9 @@ typedef struct tq_quantizer {
   const float* boundaries;
   void* prep;
   int rotation;
+  int split;
+  const float* centroids_o;
+  const float* boundaries_o;
 } tq_quantizer;
 
 /*
@@ -135,6 +159,13 @@ typedef struct tq_quantizer {
  *           LSB-first order
  *   gammas  float[n] (PROD, else NULL): ‖r‖, the residual norm the QJL
  *           estimator scales by
+ * Split quantizers (TQ_SPLIT_OUTLIER32, b = bits):
+ *   codes   uint8[n][16·b + 4]: the 128 codes in position order, position p
+ *           with width b+1 when p mod 8 < 2 (outlier coordinate k sits at the
+ *           k-th such position) and b otherwise (regular coordinate k at the
+ *           k-th other position), one after another, each least significant
+ *           bit first; every 8 positions take 8b + 2 bits
+ *   norms   float[n][2]: ‖x_o‖ and ‖x_r‖ of the outlier and regular channels
  * Buffers must be 16-byte aligned.
  */
 typedef struct tq_packed {

@@ -23,6 +23,8 @@ TQ_F32 = 0
 TQ_BF16 = 1
 TQ_ROT_DENSE = 0
 TQ_ROT_HADAMARD = 1
+TQ_SPLIT_NONE = 0
+TQ_SPLIT_OUTLIER32 = 1
 TQ_HEAD_DIM = 128
 
 # Every function include/tq.h declares.
@@ -42,7 +44,8 @@ class tq_quantizer(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("bits", ctypes.c_int), ("variant", ctypes.c_int),
                 ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
                 ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p),
-                ("prep", ctypes.c_void_p), ("rotation", ctypes.c_int)]
+                ("prep", ctypes.c_void_p), ("rotation", ctypes.c_int), ("split", ctypes.c_int),
+                ("centroids_o", ctypes.c_void_p), ("boundaries_o", ctypes.c_void_p)]
 
 
 class tq_packed(ctypes.Structure):

@@ -1753,6 +1753,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   st = tq_check_quantizer(vq);
   if (st != TQ_OK) return st;
   if (vq->variant != TQ_MSE) return TQ_ERR_UNSUPPORTED;
+  if (kq->split != TQ_SPLIT_NONE || vq->split != TQ_SPLIT_NONE) return TQ_ERR_UNSUPPORTED;
   if (query == nullptr || out == nullptr || k_cache == nullptr || v_cache == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 1) return TQ_ERR_INVALID_ARG;
@@ -1899,6 +1900,7 @@ extern "C" int tq_search(const tq_quantizer* q, const float* query, int nq, cons
                          float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream) {
   const int st = tq_check_quantizer(q);
   if (st != TQ_OK) return st;
+  if (q->split != TQ_SPLIT_NONE) return TQ_ERR_UNSUPPORTED;
   if (query == nullptr || db == nullptr || scores == nullptr || index == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
   if (nq < 1 || n < 1 || k < 1 || k > n) return TQ_ERR_INVALID_ARG;

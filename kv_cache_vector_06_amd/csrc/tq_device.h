@@ -30,6 +30,8 @@ struct PrepHeader {
   float rot_scale;   // the rotation fragments hold rot_scale·Π: 16 (dense Π, fp16
                      // hi + lo), or √d for a randomized Hadamard Π = H·diag(s)/√d,
                      // whose fragments H·diag(s) are exact ±1 (lo parts zero)
+  uint32_t omask[4]; // outlier-channel split: bit c set when raw channel c is an
+                     // outlier channel (its column of Π lies in the outlier rows)
 };
 constexpr int kFragsPerSet = 2 * 8 * 4;               // (part, t, s)
 constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB

@@ -33,7 +33,8 @@ namespace tq {
 __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__ rot,
                                                        const float* __restrict__ proj,
                                                        const float* __restrict__ centroids, int bm,
-                                                       int hadamard, uint8_t* __restrict__ prep_base) {
+                                                       int hadamard, const float* __restrict__ centroids_o,
+                                                       uint8_t* __restrict__ prep_base) {
   __shared__ float red[1024];
   __shared__ int redi[1024];
   const int tid = threadIdx.x;
@@ -50,6 +51,13 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__
       for (int m = 0; m < half; ++m) {
         const float v = centroids[half + m] * kCentScale * sg;
         if (v > 0.f) err = fmaxf(err, fabsf(h2f(f2h_bits(v)) - v) / v);
+      }
+      if (centroids_o != nullptr) {   // split: the outlier codebook (bm + 1 bits) shares σ
+        const int ho = 1 << bm;
+        for (int m = 0; m < ho; ++m) {
+          const float v = centroids_o[ho + m] * kCentScale * sg;
+          if (v > 0.f) err = fmaxf(err, fabsf(h2f(f2h_bits(v)) - v) / v);
+        }
       }
       if (err < best) {
         best = err;
@@ -72,8 +80,24 @@ __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__
       h->sigma_err = red[0];
       h->sp_scale = 0.f;
       h->rot_scale = hadamard ? sqrtf(float(kD)) : kRotScale;
+      for (int w = 0; w < 4; ++w) h->omask[w] = 0u;
     }
     __syncthreads();
+  }
+  if (centroids_o != nullptr) {
+    // raw channel c is an outlier channel when its column of Π has its (unit)
+    // weight in the outlier rows p mod 8 < 2
+    __shared__ uint32_t om[4];
+    if (tid < 4) om[tid] = 0u;
+    __syncthreads();
+    if (tid < kD) {
+      float e = 0.f;
+      for (int p = 0; p < kD; ++p)
+        if ((p & 7) < 2) e = fmaf(rot[p * kD + tid], rot[p * kD + tid], e);
+      if (e > 0.5f) atomicOr(&om[tid >> 5], 1u << (tid & 31));
+    }
+    __syncthreads();
+    if (tid < 4) reinterpret_cast<PrepHeader*>(prep_base)->omask[tid] = om[tid];
   }
   uint16_t* prep = reinterpret_cast<uint16_t*>(prep_base + kPrepHeaderBytes);
   // Rotation fragments: A(t, s)[lane (i, g)][j] = rot_scale·Π[out_row(t,i)][32s + 8g + j]:
@@ -161,6 +185,8 @@ struct EncodeArgs {
   const float* centroids;
   const float* boundaries;
   const int64_t* slot;  // output slot of each row, or null for slot = row
+  const float* centroids_o;   // split: the outlier group's codebook
+  const float* boundaries_o;
 };
 
 constexpr int kEncWaves = 8;
@@ -172,6 +198,24 @@ struct Book {
   float t1, t2, t3, t4, t5, t6, t7;
   float c0, c1, c2, c3, c4, c5, c6, c7;
 };
+
+template <int BM>
+__device__ __forceinline__ Book load_book(const float* centroids, const float* boundaries) {
+  constexpr int K = 1 << BM;
+  Book bk{};
+  if constexpr (BM >= 1) {
+    const float* tb = boundaries + (K / 2 - 1);
+    const float* cb = centroids + K / 2;
+    bk.c0 = cb[0];
+    if constexpr (K / 2 > 1) { bk.t1 = tb[1]; bk.c1 = cb[1]; }
+    if constexpr (K / 2 > 2) { bk.t2 = tb[2]; bk.t3 = tb[3]; bk.c2 = cb[2]; bk.c3 = cb[3]; }
+    if constexpr (K / 2 > 4) {
+      bk.t4 = tb[4]; bk.t5 = tb[5]; bk.t6 = tb[6]; bk.t7 = tb[7];
+      bk.c4 = cb[4]; bk.c5 = cb[5]; bk.c6 = cb[6]; bk.c7 = cb[7];
+    }
+  }
+  return bk;
+}
 
 // Nearest-centroid code of y: idx = #{i : t_i < y}. With a = |y|:
 //   y > 0:  idx = K/2 + #{j >= 1 : tp[j] <  a}
@@ -535,6 +579,165 @@ __global__ __launch_bounds__(kRowWaves * 64) void row_encode_kernel(RowEncArgs a
   row_encode(a, blockIdx.x, X);
 }
 
+// Outlier-channel split encode ("TurboQuant của Google…" (omelet.tech),
+// section "Thực nghiệm: 3.5 bit…"): two TurboQuant-mse instances in one pass.
+// The block-structured Π puts the 32 outlier channels' rotation in the rows
+// p mod 8 < 2 and the 96 regular channels' in the others, so one product
+// rotates both groups; each group is then normalised by its own norm (from
+// the input channels that the prepared mask marks) and quantized with its own
+// codebook: BM + 1 bits on outlier rows, BM on the others. Lane (n, g) holds
+// rotated coordinates 32g + q, q = 4t + j; q is an outlier position when
+// t is even and j < 2. Its 32 codes form the bits [g·(32·BM + 8), (g+1)·(32·BM + 8))
+// of the vector's code string (byte aligned), written byte by byte.
+template <int BM, bool F32IN>
+__global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs a) {
+  constexpr int BO = BM + 1;
+  constexpr int SEG = 32 * BM + 8;           // bits of a lane's 32 codes
+  constexpr int NW = (SEG + 31) / 32;
+  constexpr int ROW = 16 * BM + 4;           // bytes of a vector's codes
+  __shared__ u32x4 lds_rot[kFragsPerSet * 64];
+  stage_frags(a.prep, lds_rot, nullptr, threadIdx.x);
+  const PrepHeader* hdr =
+      reinterpret_cast<const PrepHeader*>(reinterpret_cast<const uint8_t*>(a.prep) - kPrepHeaderBytes);
+  const float rot_scale = hdr->rot_scale;
+  const Book br = load_book<BM>(a.centroids, a.boundaries);
+  const Book bo = load_book<BO>(a.centroids_o, a.boundaries_o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  // bit 8s + j: the lane's input column 32s + 8g + j is an outlier channel
+  uint32_t omask = 0u;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) omask |= ((hdr->omask[s] >> (8 * g)) & 0xffu) << (8 * s);
+  __syncthreads();
+
+  const int64_t ntiles = (a.n + 15) / 16;
+  const int64_t tstride = int64_t(gridDim.x) * kEncWaves;
+  for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles; tile += tstride) {
+    const int64_t rowi = tile * 16 + n;
+    const bool valid = rowi < a.n;
+    const int64_t row = valid ? rowi : a.n - 1;
+    const int64_t vec = a.slot ? a.slot[row] : row;
+    int lofs = lane;
+    asm volatile("" : "+v"(lofs));
+    float xv[32];
+    if constexpr (!F32IN) {
+      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 r = *reinterpret_cast<const u32x4*>(xr + 32 * s);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          xv[8 * s + 2 * k] = bf16_to_f32(r[k] & 0xffffu);
+          xv[8 * s + 2 * k + 1] = bf16_to_f32(r[k] >> 16);
+        }
+      }
+    } else {
+      const float* xr = static_cast<const float*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(xr + 32 * s);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(xr + 32 * s + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          xv[8 * s + k] = w0[k];
+          xv[8 * s + 4 + k] = w1[k];
+        }
+      }
+    }
+    // scale by 2^-e (max|x| = m·2^e, m in [0.5, 1)) as in the unsplit encoder
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(xv[q]));
+    amax = max4g(amax);
+    int ex = 0;
+    if (amax > 0.f) frexpf(amax, &ex);
+    float sso = 0.f, ssr = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      xv[q] = ldexpf(xv[q], -ex);
+      const float v2 = xv[q] * xv[q];
+      if ((omask >> q) & 1u)
+        sso += v2;
+      else
+        ssr += v2;
+    }
+    sso = sum4g(sso);
+    ssr = sum4g(ssr);
+    const float rso = sqrtf(sso), rsr = sqrtf(ssr);
+    u32x4 bx[4], bxl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (!F32IN) {
+          bx[s][k] = pack_h2(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+        } else {
+          uint16_t h0, l0, h1, l1;
+          split_h(xv[8 * s + 2 * k], h0, l0);
+          split_h(xv[8 * s + 2 * k + 1], h1, l1);
+          bx[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
+          bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
+        }
+      }
+    f32x4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const u32x4 ah = lds_rot[frag_index(0, t, s) * 64 + lofs];
+        const u32x4 al = lds_rot[frag_index(1, t, s) * 64 + lofs];
+        acc[t] = mfma(ah, bx[s], acc[t]);
+        acc[t] = mfma(al, bx[s], acc[t]);
+        if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
+      }
+    }
+    // acc = rot_scale·Π·x·2^-e; a group's rotated unit vector is its rows
+    // over rot_scale·‖x_g‖·2^-e, so the thresholds scale by that
+    const float So = rso > 0.f ? rot_scale * rso : 1.0f;
+    const float Sr = rsr > 0.f ? rot_scale * rsr : 1.0f;
+    ScaledBook sbo, sbr;
+    {
+      const float to[8] = {0.f, bo.t1, bo.t2, bo.t3, bo.t4, bo.t5, bo.t6, bo.t7};
+      const float tr[8] = {0.f, br.t1, br.t2, br.t3, br.t4, br.t5, br.t6, br.t7};
+#pragma unroll
+      for (int j = 1; j < (1 << BO) / 2; ++j) sbo.t[j] = __builtin_bit_cast(uint32_t, to[j] * So);
+#pragma unroll
+      for (int j = 1; j < (1 << BM) / 2; ++j) sbr.t[j] = __builtin_bit_cast(uint32_t, tr[j] * Sr);
+    }
+    uint32_t w[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = 0u;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = 4 * t + j, c = q >> 3, r = q & 7;
+        const bool out = r < 2;
+        uint32_t m;
+        bool pos;
+        const uint32_t code = out ? quantize_scaled<BO>(acc[t][j], sbo, m, pos)
+                                  : quantize_scaled<BM>(acc[t][j], sbr, m, pos);
+        const int width = out ? BO : BM;
+        const int bit = c * (8 * BM + 2) + (out ? r * BO : 2 * BO + (r - 2) * BM);
+        const int wi = bit >> 5, off = bit & 31;
+        w[wi] |= code << off;
+        if (off + width > 32) w[wi + 1] |= code >> (32 - off);
+      }
+    }
+    if (valid) {
+      uint8_t* dst = a.codes + vec * ROW + g * (SEG / 8);
+#pragma unroll
+      for (int k = 0; k < SEG / 8; ++k) dst[k] = static_cast<uint8_t>(w[k >> 2] >> (8 * (k & 3)));
+      if (g == 0) {
+        a.norms[2 * vec] = ldexpf(rso, ex);
+        a.norms[2 * vec + 1] = ldexpf(rsr, ex);
+      }
+    }
+  }
+}
+
 template <int BM, bool PROD>
 hipError_t launch_encode_t(const EncodeArgs& a, bool f32in, int grid, hipStream_t st) {
   if (f32in)
@@ -562,6 +765,12 @@ int check_quantizer(const tq_quantizer* q) {
   if (q->variant == TQ_PROD && q->proj == nullptr) return TQ_ERR_INVALID_ARG;
   if (!aligned(q->prep, 256)) return TQ_ERR_WORKSPACE;
   if (q->rotation != TQ_ROT_DENSE && q->rotation != TQ_ROT_HADAMARD) return TQ_ERR_UNSUPPORTED;
+  if (q->split != TQ_SPLIT_NONE && q->split != TQ_SPLIT_OUTLIER32) return TQ_ERR_UNSUPPORTED;
+  if (q->split == TQ_SPLIT_OUTLIER32) {
+    if (q->variant != TQ_MSE || q->bits < 2 || q->bits > 3 || q->rotation != TQ_ROT_DENSE)
+      return TQ_ERR_UNSUPPORTED;
+    if (q->centroids_o == nullptr || q->boundaries_o == nullptr) return TQ_ERR_INVALID_ARG;
+  }
   return TQ_OK;
 }
 
@@ -582,7 +791,8 @@ extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
   const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
   hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), q->rot,
                      q->variant == TQ_PROD ? q->proj : nullptr, q->centroids, bm,
-                     q->rotation == TQ_ROT_HADAMARD ? 1 : 0, static_cast<uint8_t*>(q->prep));
+                     q->rotation == TQ_ROT_HADAMARD ? 1 : 0,
+                     q->split == TQ_SPLIT_OUTLIER32 ? q->centroids_o : nullptr, static_cast<uint8_t*>(q->prep));
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
@@ -619,8 +829,28 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
   a.centroids = q->centroids;
   a.boundaries = q->boundaries;
   a.slot = out_slot;
+  a.centroids_o = q->centroids_o;
+  a.boundaries_o = q->boundaries_o;
   const int64_t tiles = (n + 15) / 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q->split == TQ_SPLIT_OUTLIER32) {
+    const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
+    const int cap = device_cus() * 2;
+    const dim3 grid(static_cast<unsigned>(want < cap ? want : cap));
+    const bool f32 = x_dtype == TQ_F32;
+    if (q->bits == 2) {
+      if (f32)
+        hipLaunchKernelGGL((encode_split_kernel<2, true>), grid, dim3(kEncWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((encode_split_kernel<2, false>), grid, dim3(kEncWaves * 64), 0, s, a);
+    } else {
+      if (f32)
+        hipLaunchKernelGGL((encode_split_kernel<3, true>), grid, dim3(kEncWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((encode_split_kernel<3, false>), grid, dim3(kEncWaves * 64), 0, s, a);
+    }
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+  }
   if (tiles <= kRowTileMax) {
     RowEncArgs r{};
     r.x = x;

@@ -19,19 +19,44 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
 
 
+def split_rotation(rot_o: np.ndarray, rot_r: np.ndarray, channels) -> np.ndarray:
+    """The block-structured 128×128 rotation of an outlier-channel split
+    quantizer (tq_quantizer.split in include/tq.h): rows p mod 8 < 2 hold
+    rot_o over the outlier `channels` (in the order rot_o's columns follow),
+    the other rows hold rot_r over the remaining channels in increasing order."""
+    d = rot_o.shape[0] + rot_r.shape[0]
+    p = np.arange(d)
+    rows_o, rows_r = p[p % 8 < 2], p[p % 8 >= 2]
+    ch_o = np.asarray(channels, np.int64)
+    ch_r = np.setdiff1d(p, ch_o)
+    if rows_o.size != rot_o.shape[0] or ch_o.size != rot_o.shape[0] or np.unique(ch_o).size != ch_o.size:
+        raise ValueError("the split takes 32 distinct outlier channels and a 32×32 rotation for them")
+    out = np.zeros((d, d), np.float32)
+    out[np.ix_(rows_o, ch_o)] = rot_o
+    out[np.ix_(rows_r, ch_r)] = rot_r
+    return out
+
+
 class Quantizer:
     """One TurboQuant quantizer (rotation, optional QJL projection, codebook,
     prepared operands), all resident on `device`."""
 
-    def __init__(self, rot: np.ndarray, bits: int, variant: str = "mse",
-                 proj: np.ndarray | None = None, device: str = "cuda", rotation: str = "dense"):
+    def __init__(self, rot: np.ndarray | None, bits: int, variant: str = "mse",
+                 proj: np.ndarray | None = None, device: str = "cuda", rotation: str = "dense",
+                 split: tuple | None = None):
         """`rotation` is "dense" (any orthogonal rot) or "hadamard" (rot is the
-        randomized Walsh-Hadamard rotation H·diag(s)/√d)."""
+        randomized Walsh-Hadamard rotation H·diag(s)/√d). `split` =
+        (rot_o, rot_r, channels) makes an outlier-channel split quantizer: the
+        32 `channels` at bits + 1 bits with rotation rot_o (32×32), the other
+        96 at `bits` bits with rot_r (96×96); `rot` is then ignored."""
+        self.split = split is not None
+        if self.split:
+            rot = split_rotation(split[0], split[1], split[2])
         d = rot.shape[0]
         self.d, self.bits = d, bits
         self.variant = L.TQ_PROD if variant == "prod" else L.TQ_MSE
         self.bm = bits - 1 if self.variant == L.TQ_PROD else bits
-        c, t, self.mse_unit = L.tq_codebook(d, self.bm)
+        c, t, self.mse_unit = L.tq_codebook(d - 32 if self.split else d, self.bm)
         self.centroids64, self.boundaries64 = c, t
         dev = torch.device(device)
         self.rot = torch.as_tensor(np.ascontiguousarray(rot, np.float32)).to(dev)
@@ -44,13 +69,25 @@ class Quantizer:
         self.boundaries = torch.as_tensor(np.concatenate([t, [0.0]]).astype(np.float32)).to(dev)
         self.prep = torch.empty(L.tq_prep_bytes(), dtype=torch.uint8, device=dev)
         self.rotation = {"dense": L.TQ_ROT_DENSE, "hadamard": L.TQ_ROT_HADAMARD}[rotation]
+        self.centroids_o = self.boundaries_o = None
+        if self.split:
+            co, to, self.mse_unit_o = L.tq_codebook(32, bits + 1)
+            self.centroids64_o, self.boundaries64_o = co, to
+            self.centroids_o = torch.as_tensor(co.astype(np.float32)).to(dev)
+            self.boundaries_o = torch.as_tensor(np.concatenate([to, [0.0]]).astype(np.float32)).to(dev)
         self.c = L.tq_quantizer(d, bits, self.variant, _ptr(self.rot), _ptr(self.proj),
-                                _ptr(self.centroids), _ptr(self.boundaries), _ptr(self.prep), self.rotation)
+                                _ptr(self.centroids), _ptr(self.boundaries), _ptr(self.prep), self.rotation,
+                                L.TQ_SPLIT_OUTLIER32 if self.split else L.TQ_SPLIT_NONE,
+                                _ptr(self.centroids_o), _ptr(self.boundaries_o))
         L.tq_prepare(self.c, _stream())
 
     @property
     def code_bytes(self) -> int:
-        return self.d * self.bm // 8
+        return 16 * self.bits + 4 if self.split else self.d * self.bm // 8
+
+    @property
+    def norms_per_vector(self) -> int:
+        return 2 if self.split else 1
 
 
 class Packed:
@@ -60,7 +97,7 @@ class Packed:
         dev = torch.device(device)
         self.n = n
         self.codes = torch.zeros((n, q.code_bytes), dtype=torch.uint8, device=dev)
-        self.norms = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.norms = torch.zeros((n, 2) if q.split else n, dtype=torch.float32, device=dev)
         self.qjl = self.gammas = None
         if q.variant == L.TQ_PROD:
             self.qjl = torch.zeros((n, q.d // 8), dtype=torch.uint8, device=dev)

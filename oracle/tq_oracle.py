@@ -373,7 +373,8 @@ def encode_split(X, ch_o, rot_o, rot_r, c_o, c_r, bits: int):
     (32×32) and Lloyd-Max codebook c_o (d = 32, bits + 1 bits); the other 96
     channels, in increasing order, with rot_r (96×96) and c_r (d = 96, bits).
     Returns dict(codes=[N, (128·bits+32)/8] uint8, norms=[N, 2] (outlier,
-    regular), idx=[N,128] in position order, idx_o, idx_r)."""
+    regular), idx=[N,128] in position order, idx_o, idx_r, and each group's
+    rotated unit coordinates y_o, y_r)."""
     X = np.asarray(X, np.float64)
     d = X.shape[1]
     ch_r = _regular_channels(ch_o, d)
@@ -384,7 +385,7 @@ def encode_split(X, ch_o, rot_o, rot_r, c_o, c_r, bits: int):
     idx[:, P_o] = eo["idx"]
     idx[:, P_r] = er["idx"]
     return dict(codes=pack_split(idx, bits), norms=np.stack([eo["norms"], er["norms"]], axis=1), idx=idx,
-                idx_o=eo["idx"], idx_r=er["idx"])
+                idx_o=eo["idx"], idx_r=er["idx"], y_o=eo["y"], y_r=er["y"])
 
 
 def dequant_split(codes, norms, ch_o, rot_o, rot_r, c_o, c_r, bits: int, d: int = 128):

@@ -17,8 +17,9 @@ import torch
 import synth
 from kv_cache_vector_06_amd import _lib as L
 from kv_cache_vector_06_amd import torch_api as T
-from oracle import (decode_attention, dequant_mse, dequant_prod, encode_mse, encode_prod,
-                    lloyd_max, pack_codes, unpack_codes, unpack_signs)
+from oracle import (decode_attention, dequant_mse, dequant_prod, dequant_split, encode_mse, encode_prod,
+                    encode_split, lloyd_max, pack_codes, pack_split, split_positions, unpack_codes, unpack_signs,
+                    unpack_split)
 
 D = 128
 DEV = "cuda:0"
@@ -169,3 +170,61 @@ def encode_away_from_ties(X, rot, proj, bits, variant, seed, dtype):
         for k in enc:
             enc[k][rows] = sub[k]
     raise AssertionError("could not move rows away from ties")
+
+
+# ---------------------------------------------------------------------------
+# Outlier-channel split
+# ---------------------------------------------------------------------------
+_SPLIT_BOOKS = {}
+
+
+def split_books(bits):
+    """(outlier codebook: d = 32, bits + 1; regular: d = 96, bits) from the oracle."""
+    if bits not in _SPLIT_BOOKS:
+        _SPLIT_BOOKS[bits] = (lloyd_max(32, bits + 1), lloyd_max(96, bits))
+    return _SPLIT_BOOKS[bits]
+
+
+def split_quantizer(bits, role="k"):
+    c = synth.split_constants(D)
+    r = "k" if role == "k" else "v"
+    q = T.Quantizer(None, bits, "mse", None, DEV, split=(c[f"r{r}_o"], c[f"r{r}_r"], c[f"ch_{r}"]))
+    return q, (c[f"ch_{r}"], c[f"r{r}_o"], c[f"r{r}_r"])
+
+
+def oracle_encode_split(X, consts, bits, chunk=8192):
+    ch, ro, rr = consts
+    (co, _, _), (cr, _, _) = split_books(bits)
+    outs = [encode_split(X[i:i + chunk].astype(np.float64), ch, ro, rr, co, cr, bits)
+            for i in range(0, X.shape[0], chunk)]
+    return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
+
+
+def oracle_dequant_split(enc, consts, bits):
+    ch, ro, rr = consts
+    (co, _, _), (cr, _, _) = split_books(bits)
+    return dequant_split(enc["codes"], enc["norms"], ch, ro, rr, co, cr, bits)
+
+
+def check_encode_split(gpu: dict, ref: dict, bits: int):
+    """The encode parity rules for a split quantizer: both group norms within
+    1e-6 relative; the code string is the packing of its codes; a code may
+    differ only where its group's rotated value lies within 1e-6 of that
+    group's boundary, on at most 1e-5 of coordinates."""
+    gn, rn = gpu["norms"].astype(np.float64), ref["norms"]
+    nz = rn > 0
+    assert np.all(gn[~nz] == 0)
+    rel = np.abs(gn[nz] - rn[nz]) / rn[nz]
+    assert rel.max(initial=0) <= 1e-6, rel.max()
+    gidx = unpack_split(gpu["codes"], bits)
+    assert np.array_equal(pack_split(gidx, bits), gpu["codes"]), "code string is not the packing of its codes"
+    P_o, P_r = split_positions(D)
+    (_, to, _), (_, tr, _) = split_books(bits)
+    mism = 0
+    for P, key, t in ((P_o, "y_o", to), (P_r, "y_r", tr)):
+        bad = gidx[:, P] != ref["idx"][:, P]
+        dist = np.min(np.abs(ref[key][..., None] - t), axis=-1)
+        assert np.all(dist[bad] < 1e-6), "code mismatch away from a boundary"
+        mism += int(bad.sum())
+    assert mism <= 1e-5 * gidx.size, (mism, gidx.size)
+    return dict(norm_rel=float(rel.max(initial=0)), code_mismatch=mism)
