@@ -305,6 +305,8 @@ struct AttnArgs {
   const uint8_t* ws;
   float* part;
   int Hkv, G, ngroups, nsplit, split_len;
+  const float* kcent_o;   // outlier-channel split: the outlier groups' codebooks
+  const float* vcent_o;
 };
 
 // W bits at compile-time bit offset OFF of a little-endian word array,
@@ -1156,6 +1158,513 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// 2b. Decode attention over outlier-channel split caches
+// ---------------------------------------------------------------------------
+// Keys and values quantized with the outlier-channel split ("TurboQuant của
+// Google…" (omelet.tech), section "Thực nghiệm: 3.5 bit…"): code-string
+// position p holds an outlier coordinate (BK + 1 or BV + 1 bits) when
+// p mod 8 < 2 and a regular one (BK or BV bits) otherwise, and each vector
+// has a norm per group. The block-structured rotations keep the query prep and
+// the merge unchanged; here the positions line up with the matrix-core
+// operands:
+//   * a key tile's K-step S covers positions 32g + 8S + j of lane group g:
+//     elements j = 0, 1 (the first dword of the A operand) are outliers, so
+//     the scores take two products per K-step, one with only the outlier
+//     dword and one with the three regular dwords, weighted by the token's
+//     outlier and regular key norms;
+//   * the P·V product r covers positions 8n + r of column n: r = 0, 1 are
+//     outliers, so products 0 and 1 take the weights p·n_o and the others
+//     p·n_r, with no extra product.
+// The staged block is the 32 tokens' code strings as they lie in memory
+// (rows of 16·b + 4 bytes, copied as dwords), followed by the norm pairs.
+template <int BK, int BV>
+struct OStage {
+  static constexpr int KR = 16 * BK + 4, VR = 16 * BV + 4;   // code bytes per token
+  static constexpr int kc = 0;
+  static constexpr int vc = 32 * KR;
+  static constexpr int kn = vc + 32 * VR;                     // 32 × (n_o, n_r)
+  static constexpr int vn = kn + 256;
+  static constexpr int bytes = vn + 256;
+  static constexpr int kdw = 8 * KR, vdw = 8 * VR;            // dwords of the block's codes
+  static constexpr int kld = (kdw + 63) / 64, vld = (vdw + 63) / 64;
+  static constexpr int dma = kld + vld + 2;                   // load instructions per block
+  static_assert(kn % 16 == 0, "norm pairs are read as 16-byte vectors");
+};
+
+// Issue the block's direct-to-LDS dword loads. Without AL, dwords past the
+// last token's row (or norm pair) are clamped to the last one of it.
+template <int BK, int BV, bool AL>
+__device__ __forceinline__ void ostage_block(uint8_t* st, uint32_t t0, uint32_t last, int lane, const uint8_t* kc,
+                                             const uint8_t* vc, const float* kn, const float* vn) {
+  using L = OStage<BK, BV>;
+  const uint32_t ntok = last + 1 - t0;   // tokens of the block that exist (AL: at least 32)
+  const uint32_t* ks = reinterpret_cast<const uint32_t*>(kc + size_t(t0) * L::KR);
+  const uint32_t* vs = reinterpret_cast<const uint32_t*>(vc + size_t(t0) * L::VR);
+  const uint32_t klim = AL ? 0u : ntok * (L::KR / 4) - 1u, vlim = AL ? 0u : ntok * (L::VR / 4) - 1u;
+#pragma unroll
+  for (int j = 0; j < L::kld; ++j) {
+    const uint32_t i = 64u * j + lane;
+    if (j + 1 < L::kld || (L::kdw % 64) == 0 || i < uint32_t(L::kdw))
+      __builtin_amdgcn_global_load_lds(ks + (AL ? i : min(i, klim)), TQ_LDS(st + L::kc + 256 * j), 4, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < L::vld; ++j) {
+    const uint32_t i = 64u * j + lane;
+    if (j + 1 < L::vld || (L::vdw % 64) == 0 || i < uint32_t(L::vdw))
+      __builtin_amdgcn_global_load_lds(vs + (AL ? i : min(i, vlim)), TQ_LDS(st + L::vc + 256 * j), 4, 0, 0);
+  }
+  const uint32_t nl = AL ? uint32_t(lane) : min(uint32_t(lane), 2u * ntok - 1u);
+  __builtin_amdgcn_global_load_lds(kn + 2 * size_t(t0) + nl, TQ_LDS(st + L::kn), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(vn + 2 * size_t(t0) + nl, TQ_LDS(st + L::vn), 4, 0, 0);
+}
+
+// One lane's registers of a staged split block: its key words of both tiles
+// (lane group g's 32 positions, aligned to bit 0), the 8 slots' norm pairs and
+// value words (column n's 8 positions, aligned to bit 0).
+struct OBlock {
+  uint32_t kw[2][4];
+  float nko[8], nkr[8], nvo[8], nvr[8];
+  uint32_t vw[8];
+};
+
+struct OOffsets {
+  uint32_t k, n, v;          // byte offsets in the stage
+  uint32_t kshift, vshift;   // bit offsets of the lane's key / value bits in their first dword
+};
+
+template <int BK, int BV>
+__device__ __forceinline__ OOffsets ostage_offsets(int n, int g) {
+  using L = OStage<BK, BV>;
+  constexpr int KSB = 4 * BK + 1;          // bytes of a lane group's 32 key positions
+  constexpr int VCH = 8 * BV + 2;          // bits of a column's 8 value positions
+  OOffsets o;
+  o.k = L::kc + n * L::KR + 4 * ((g * KSB) >> 2);
+  o.kshift = 8 * ((g * KSB) & 3);
+  o.n = L::kn + 32 * g;
+  o.v = L::vc + 4 * g * L::VR + 4 * ((n * VCH) >> 5);
+  o.vshift = (n * VCH) & 31;
+  return o;
+}
+
+// Read a staged split block into registers: wait for its loads (all but the
+// newest PEND of this wavefront), every read of the stage, then the wait for
+// the reads, in one statement with early-clobber outputs.
+template <int BK, int BV, int PEND>
+__device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffsets& o) {
+  using L = OStage<BK, BV>;
+  constexpr int KT = 4 * L::KR;            // dwords between the two key tiles (16 rows)
+  constexpr int VT = L::VR / 4;            // dwords between consecutive tokens
+  static_assert(KT + 3 <= 255 && 19 * VT + 1 <= 255, "read2 offsets");
+  const uint32_t ak = sb + o.k, an = sb + o.n, av = sb + o.v;
+  u32x2 k0, k1, k2, k3;
+  f32x4 n0, n1, n2, n3, m0, m1, m2, m3;
+  u32x2 v0, v1, v2, v3, v4, v5, v6, v7;
+  // slot (τ, i) is token 16τ + 4g + i: dword offset (16τ + i)·VT
+  asm volatile(
+      "s_waitcnt vmcnt(%[pend])\n\t"
+      "ds_read2_b32 %[k0], %[ak] offset1:1\n\t"
+      "ds_read2_b32 %[k1], %[ak] offset0:2 offset1:3\n\t"
+      "ds_read2_b32 %[k2], %[ak] offset0:%[kt0] offset1:%[kt1]\n\t"
+      "ds_read2_b32 %[k3], %[ak] offset0:%[kt2] offset1:%[kt3]\n\t"
+      "ds_read_b128 %[n0], %[an]\n\t"
+      "ds_read_b128 %[n1], %[an] offset:16\n\t"
+      "ds_read_b128 %[n2], %[an] offset:128\n\t"
+      "ds_read_b128 %[n3], %[an] offset:144\n\t"
+      "ds_read_b128 %[m0], %[an] offset:256\n\t"
+      "ds_read_b128 %[m1], %[an] offset:272\n\t"
+      "ds_read_b128 %[m2], %[an] offset:384\n\t"
+      "ds_read_b128 %[m3], %[an] offset:400\n\t"
+      "ds_read2_b32 %[v0], %[av] offset0:%[s0] offset1:%[s0b]\n\t"
+      "ds_read2_b32 %[v1], %[av] offset0:%[s1] offset1:%[s1b]\n\t"
+      "ds_read2_b32 %[v2], %[av] offset0:%[s2] offset1:%[s2b]\n\t"
+      "ds_read2_b32 %[v3], %[av] offset0:%[s3] offset1:%[s3b]\n\t"
+      "ds_read2_b32 %[v4], %[av] offset0:%[s4] offset1:%[s4b]\n\t"
+      "ds_read2_b32 %[v5], %[av] offset0:%[s5] offset1:%[s5b]\n\t"
+      "ds_read2_b32 %[v6], %[av] offset0:%[s6] offset1:%[s6b]\n\t"
+      "ds_read2_b32 %[v7], %[av] offset0:%[s7] offset1:%[s7b]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2), [k3] "=&v"(k3), [n0] "=&v"(n0), [n1] "=&v"(n1),
+        [n2] "=&v"(n2), [n3] "=&v"(n3), [m0] "=&v"(m0), [m1] "=&v"(m1), [m2] "=&v"(m2), [m3] "=&v"(m3),
+        [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5),
+        [v6] "=&v"(v6), [v7] "=&v"(v7)
+      : [pend] "n"(PEND), [ak] "v"(ak), [an] "v"(an), [av] "v"(av), [kt0] "n"(KT), [kt1] "n"(KT + 1),
+        [kt2] "n"(KT + 2), [kt3] "n"(KT + 3), [s0] "n"(0), [s0b] "n"(1), [s1] "n"(VT), [s1b] "n"(VT + 1),
+        [s2] "n"(2 * VT), [s2b] "n"(2 * VT + 1), [s3] "n"(3 * VT), [s3b] "n"(3 * VT + 1), [s4] "n"(16 * VT),
+        [s4b] "n"(16 * VT + 1), [s5] "n"(17 * VT), [s5b] "n"(17 * VT + 1), [s6] "n"(18 * VT),
+        [s6b] "n"(18 * VT + 1), [s7] "n"(19 * VT), [s7b] "n"(19 * VT + 1)
+      : "memory");
+  const uint32_t ks = o.kshift, vs = o.vshift;
+  const u32x2 kk[2][2] = {{k0, k1}, {k2, k3}};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t d0 = kk[t][0][0], d1 = kk[t][0][1], d2 = kk[t][1][0], d3 = kk[t][1][1];
+    R.kw[t][0] = __builtin_amdgcn_alignbit(d1, d0, ks);
+    R.kw[t][1] = __builtin_amdgcn_alignbit(d2, d1, ks);
+    R.kw[t][2] = __builtin_amdgcn_alignbit(d3, d2, ks);
+    R.kw[t][3] = d3 >> ks;
+  }
+  const f32x4 nn[4] = {n0, n1, n2, n3}, mm[4] = {m0, m1, m2, m3};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    R.nko[j] = nn[j >> 1][2 * (j & 1)];
+    R.nkr[j] = nn[j >> 1][2 * (j & 1) + 1];
+    R.nvo[j] = mm[j >> 1][2 * (j & 1)];
+    R.nvr[j] = mm[j >> 1][2 * (j & 1) + 1];
+  }
+  const u32x2 vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) R.vw[j] = __builtin_amdgcn_alignbit(vv[j][1], vv[j][0], vs);
+}
+
+// Table rows of the split decode (the value pair tables fill the lower and the
+// upper half of rows 0..127; rows 128.. of the upper half hold key pairs):
+//   outlier value pairs  row e, byte 4c              (e = code0 | code1 << 4)
+//   regular value pairs  row e, byte 128 + 4c        (e <= 0x77)
+//   regular key pairs    row 128 + e, byte 128 + 4c  (e = 2·BK bits)
+//   3-bit outlier key pairs  row 192 + e, byte 128 + 4c
+// 4-bit outlier key pairs (hi and lo pairs, 8 bytes) have rows of their own
+// (128 bytes, 16 copies: row e, byte 8c').
+constexpr int kKeyRegRow = 128, kKeyOutRow = 192;
+
+template <int BK, int S>
+__device__ __forceinline__ void okey_operands(const uint32_t (&kw)[4], const uint8_t* tab, const uint8_t* tab2,
+                                              uint32_t lane_hi, uint32_t lane8, u32x4& ao, u32x4& aol, u32x4& ar) {
+  constexpr int BKO = BK + 1, CH = 8 * BK + 2, base = S * CH;
+  if constexpr (BKO == 4) {
+    const u32x2 e = *reinterpret_cast<const u32x2*>(tab2 + (field_shl<base, 8, 7>(kw) + lane8));
+    ao = u32x4{e[0], 0u, 0u, 0u};
+    aol = u32x4{e[1], 0u, 0u, 0u};
+  } else {
+    ao = u32x4{*reinterpret_cast<const uint32_t*>(tab + kKeyOutRow * 256 + (field_shl<base, 2 * BKO, 8>(kw) + lane_hi)),
+               0u, 0u, 0u};
+  }
+  const uint8_t* kb = tab + kKeyRegRow * 256;
+  ar[0] = 0u;
+  ar[1] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO, 2 * BK, 8>(kw) + lane_hi));
+  ar[2] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 2 * BK, 2 * BK, 8>(kw) + lane_hi));
+  ar[3] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 4 * BK, 2 * BK, 8>(kw) + lane_hi));
+}
+
+// Scores of a split block (the score is sc·iqs).
+template <int BK>
+__device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* tab, const uint8_t* tab2,
+                                              uint32_t lane_hi, uint32_t lane8, const u32x4 (&bq)[4],
+                                              float (&sc)[8]) {
+  u32x4 ao[2][4], aol[2][4], ar[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    okey_operands<BK, 0>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][0], aol[t][0], ar[t][0]);
+    okey_operands<BK, 1>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][1], aol[t][1], ar[t][1]);
+    okey_operands<BK, 2>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][2], aol[t][2], ar[t][2]);
+    okey_operands<BK, 3>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][3], aol[t][3], ar[t][3]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 dmo = f32x4{0.f, 0.f, 0.f, 0.f}, dmr = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int S = 0; S < 4; ++S) {
+      dmo = mfma(ao[t][S], bq[S], dmo);
+      if constexpr (BK + 1 == 4) dmo = mfma(aol[t][S], bq[S], dmo);
+      dmr = mfma(ar[t][S], bq[S], dmr);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * t + i;
+      sc[j] = add_ror8(fmaf(R.nko[j], dmo[i], R.nkr[j] * dmr[i]));
+    }
+  }
+}
+
+// Value positions 8n..8n+7 of a slot in nibble form (code of position 8n + r
+// in bits 4r..4r+3): the two outlier codes (BV + 1 bits) then six regular ones.
+template <int BV>
+__device__ __forceinline__ uint32_t onibbles(uint32_t w) {
+  constexpr int BVO = BV + 1;
+  const uint32_t o = bfe_u32<0, BVO>(w) | (bfe_u32<BVO, BVO>(w) << 4);
+  return o | (to_nibbles<BV>(w >> (2 * BVO)) << 8);
+}
+
+template <int BK, int BV>
+__device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint32_t t_end, int n, int g,
+                                              const uint8_t* tab, const uint8_t* tab2, uint32_t lane_lo,
+                                              uint32_t lane_hi, uint32_t lane8, const u32x4 (&bq)[4], float iqs,
+                                              uint32_t lomask, SoftmaxState& st, f32x4 (&acc)[8]) {
+  uint32_t X[4], Y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t a0 = onibbles<BV>(R.vw[2 * k]), a1 = onibbles<BV>(R.vw[2 * k + 1]);
+    X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
+    Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
+  }
+  float sc[8];
+  oblock_scores<BK>(R, tab, tab2, lane_hi, lane8, bq, sc);
+  Luts Tv;
+  Tv.v = tab;
+  Tv.vlane = lane_lo;
+  u32x4 bv[8];
+  bv[0] = pv_operand<0>(X, Y, Tv);
+  bv[1] = pv_operand<1>(X, Y, Tv);
+  Tv.vlane = lane_hi;
+  bv[2] = pv_operand<2>(X, Y, Tv);
+  bv[3] = pv_operand<3>(X, Y, Tv);
+  bv[4] = pv_operand<4>(X, Y, Tv);
+  bv[5] = pv_operand<5>(X, Y, Tv);
+  bv[6] = pv_operand<6>(X, Y, Tv);
+  bv[7] = pv_operand<7>(X, Y, Tv);
+  float nvo[8], nvr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    nvo[j] = R.nvo[j];
+    nvr[j] = R.nvr[j];
+  }
+  if (__builtin_expect(t0 + kBlockTok > t_end, 0)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = t0 + 16 * (j >> 2) + 4 * g + (j & 3) < t_end;
+      sc[j] = ok ? sc[j] : -INFINITY;
+      nvo[j] = ok ? nvo[j] : 0.f;
+      nvr[j] = ok ? nvr[j] : 0.f;
+    }
+  }
+  const float mloc = max8f(sc) * iqs;
+  const float nvl = fmaxf(max8f(nvo), max8f(nvr));
+  if (__builtin_expect(__any(mloc > st.m + kLazy || nvl > st.nvs), 0)) {
+    const float mg = max4g(mloc);
+    const float nvw = max4g(nvl);
+    const float m_new = mg > st.m + kLazy ? mg : st.m;
+    float nvs_new = st.nvs, knv_new = st.knv;
+    if (nvw > st.nvs) {
+      int e;
+      frexpf(nvw, &e);
+      nvs_new = ldexpf(1.0f, e + 1);
+      knv_new = static_cast<float>(e + 1);
+    }
+    const float mk_new = m_new + knv_new;
+    const float f = st.mk == -INFINITY ? 0.f : exp2f(st.mk - mk_new);
+    st.l *= f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float fi = __shfl(f, (4 * g + i) & 7, 64);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
+    }
+    st.m = m_new;
+    st.mk = mk_new;
+    st.nvs = nvs_new;
+    st.knv = knv_new;
+  }
+  // A operands of P·V: weights p·n_o for the outlier products (r = 0, 1),
+  // p·n_r for the others; rows n < 8 the fp16 hi part, rows n + 8 the lo part.
+  u32x4 pao, par;
+  const float nmk = -st.mk;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float xo[2], xr[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * k + e], iqs, nmk));
+      st.l += p;
+      const float wo = p * nvo[2 * k + e], wr = p * nvr[2 * k + e];
+      xo[e] = wo - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, wo) & lomask);
+      xr[e] = wr - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, wr) & lomask);
+    }
+    pao[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xo[0], xo[1]));
+    par[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xr[0], xr[1]));
+  }
+  acc[0] = mfma(pao, bv[0], acc[0]);
+  acc[1] = mfma(pao, bv[1], acc[1]);
+#pragma unroll
+  for (int r = 2; r < 8; ++r) acc[r] = mfma(par, bv[r], acc[r]);
+}
+
+// The workgroup's partials of a split (as in attn_split_kernel), with each
+// head's rows of hi and lo weights (lane groups g and g + 2) added before they
+// are staged, so a wavefront stages 8 rows of 128 floats (4 KiB).
+template <int RING>
+__device__ __forceinline__ void write_partials_o(const AttnArgs& a, const SoftmaxState& st, const f32x4 (&acc)[8],
+                                                 float (&wm)[kDecWaves][kMaxHeads], float (&wl)[kDecWaves][kMaxHeads],
+                                                 uint8_t (&stage)[kDecWaves][RING], int unit, int split, int gc,
+                                                 int n, int g, int wave, int tid) {
+  static_assert(RING >= kMaxHeads * kD * 4, "accumulator rows");
+  const float l_run = sum4g(st.l);
+  if (g == 0 && n < kMaxHeads) {
+    wm[wave][n] = st.mk;
+    wl[wave][n] = l_run;
+  }
+  float* wacc_own = reinterpret_cast<float*>(&stage[wave][0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float lo = __shfl_xor(acc[r][i], 32, 64);
+      if (g < 2) wacc_own[(4 * g + i) * kD + 8 * n + r] = acc[r][i] + lo;
+    }
+  }
+  __syncthreads();
+  constexpr int nthr = kDecWaves * 64;
+  float* part = a.part + ((size_t(unit) * a.nsplit + split) * kMaxHeads) * kPartStride;
+  for (int e = tid; e < gc * kD; e += nthr) {
+    const int head = e / kD, dim = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w][head]);
+    float Ls = 0.f, A = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float fw = exp2f(wm[w][head] - M);
+        Ls = fmaf(fw, wl[w][head], Ls);
+        A = fmaf(fw, reinterpret_cast<const float*>(&stage[w][0])[head * kD + dim], A);
+      }
+    }
+    float* o = part + head * kPartStride;
+    o[4 + dim] = A;
+    if (dim == 0) {
+      o[0] = M;
+      o[1] = Ls;
+    }
+  }
+}
+
+template <int BK, int BV, bool AL>
+__global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a) {
+  using SL = OStage<BK, BV>;
+  constexpr int BKO = BK + 1, BVO = BV + 1;
+  __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
+  __shared__ __attribute__((aligned(256))) uint8_t tab2[BKO == 4 ? 256 * 128 : 16];
+  __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
+  constexpr int kRing = kStages * SL::bytes > kMaxHeads * kD * 4 ? kStages * SL::bytes : kMaxHeads * kD * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][kRing];
+  // scaled centroids: outlier values 0..15, regular values 16..23, outlier
+  // keys 32..47, regular keys 48..55
+  __shared__ float cent[64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, unit = blockIdx.y;
+  const int grp = unit % a.ngroups;
+  const int kvh = (unit / a.ngroups) % a.Hkv;
+  const int b = unit / (a.ngroups * a.Hkv);
+  const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
+  constexpr int nthr = kDecWaves * 64;
+
+  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
+  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
+  u32x4 bq[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) bq[s] = fr[s * 64 + lane];
+  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
+  if (tid < 64) {
+    const int grp4 = tid >> 4, k = tid & 15;
+    float v = 0.f;
+    if (grp4 == 0 && k < (1 << BVO)) v = a.vcent_o[k] * (kCentScale * a.vh->sigma);
+    if (grp4 == 1 && k < (1 << BV)) v = a.vcent[k] * (kCentScale * a.vh->sigma);
+    if (grp4 == 2 && k < (1 << BKO)) v = a.kcent_o[k] * (kCentScale * a.kh->sigma);
+    if (grp4 == 3 && k < (1 << BK)) v = a.kcent[k] * (kCentScale * a.kh->sigma);
+    cent[tid] = v;
+  }
+
+  int64_t L = a.max_ctx;
+  if (a.ctx_lens) {
+    const int64_t l = a.ctx_lens[b];
+    L = l < 0 ? 0 : (l > a.max_ctx ? a.max_ctx : l);
+  }
+  const int64_t per_wave = a.split_len / kDecWaves;
+  const int64_t tb = int64_t(split) * a.split_len + wave * per_wave;
+  const int64_t te = min(tb + per_wave, L);
+  const uint32_t t_begin = static_cast<uint32_t>(tb);
+  const uint32_t t_end = te > tb ? static_cast<uint32_t>(te) : t_begin;
+  const uint32_t last = L > 0 ? static_cast<uint32_t>(L - 1) : 0u;
+  const int64_t base = (int64_t(b) * a.Hkv + kvh) * a.max_ctx;
+  const uint8_t* kc = a.kc + base * SL::KR;
+  const uint8_t* vc = a.vc + base * SL::VR;
+  const float* kn = a.kn + 2 * base;
+  const float* vn = a.vn + 2 * base;
+  __syncthreads();   // the centroids
+
+  // value pair tables first (their LDS writes then come before any direct
+  // load is in flight)
+  for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
+    const int e = idx / kCopies, c = idx % kCopies;
+    const int c0 = e & 15, c1 = e >> 4;
+    const uint32_t wo = (c0 < (1 << BVO) && c1 < (1 << BVO)) ? pack_h2(cent[c0], cent[c1]) : 0u;
+    *reinterpret_cast<uint32_t*>(tab + 256 * e + 4 * c) = wo;
+    if (e < kKeyRegRow) {
+      const uint32_t wr = (c0 < (1 << BV) && c1 < (1 << BV)) ? pack_h2(cent[16 + c0], cent[16 + c1]) : 0u;
+      *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) = wr;
+    }
+  }
+  uint8_t* ring = &stage[wave][0];
+  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const OOffsets so = ostage_offsets<BK, BV>(n, g);
+  const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
+  if (nblk > 0) ostage_block<BK, BV, AL>(ring, t_begin, last, lane, kc, vc, kn, vn);
+  if (nblk > 1) ostage_block<BK, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, vc, kn, vn);
+
+  // key pair tables: regular (2·BK-bit entries) and outlier
+  for (int idx = tid; idx < (1 << (2 * BK)) * kCopies; idx += nthr) {
+    const int e = idx / kCopies, c = idx % kCopies;
+    *reinterpret_cast<uint32_t*>(tab + 256 * (kKeyRegRow + e) + kTabK + 4 * c) =
+        pack_h2(cent[48 + (e & ((1 << BK) - 1))], cent[48 + (e >> BK)]);
+  }
+  if constexpr (BKO == 4) {
+    for (int idx = tid; idx < 256 * 16; idx += nthr) {
+      const int e = idx >> 4, c = idx & 15;
+      uint16_t h0, l0, h1, l1;
+      split_h(cent[32 + (e & 15)], h0, l0);
+      split_h(cent[32 + (e >> 4)], h1, l1);
+      *reinterpret_cast<u32x2*>(tab2 + 128 * e + 8 * c) =
+          u32x2{uint32_t(h0) | (uint32_t(h1) << 16), uint32_t(l0) | (uint32_t(l1) << 16)};
+    }
+  } else {
+    for (int idx = tid; idx < 64 * kCopies; idx += nthr) {
+      const int e = idx / kCopies, c = idx % kCopies;
+      *reinterpret_cast<uint32_t*>(tab + 256 * (kKeyOutRow + e) + kTabK + 4 * c) =
+          pack_h2(cent[32 + (e & 7)], cent[32 + (e >> 3)]);
+    }
+  }
+  const uint32_t cp = lane & 31;
+  const uint32_t lane_lo = 4u * cp, lane_hi = kTabK + 4u * cp, lane8 = 8u * (lane & 15);
+  const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
+  __syncthreads();
+
+  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
+  f32x4 acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int cur = 0;
+  for (uint32_t i = 0; i < nblk; ++i) {
+    const uint32_t t0 = t_begin + i * kBlockTok;
+    OBlock R;
+    const uint32_t sb = ring_addr + cur * SL::bytes;
+    if (i + 1 < nblk)
+      oread_block<BK, BV, SL::dma>(R, sb, so);
+    else
+      oread_block<BK, BV, 0>(R, sb, so);
+    if (i + 2 < nblk) {
+      const int nx = (cur + 2) % kStages;
+      ostage_block<BK, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, vc, kn, vn);
+    }
+    oattend_block<BK, BV>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bq, iqs, lomask, st, acc);
+    cur = cur + 1 == kStages ? 0 : cur + 1;
+  }
+  write_partials_o<kRing>(a, st, acc, wm, wl, stage, unit, split, gc, n, g, wave, tid);
+}
+
+template <int BK, int BV>
+hipError_t launch_outlier_t(const AttnArgs& a, bool al, dim3 grid, hipStream_t st) {
+  if (al)
+    hipLaunchKernelGGL((attn_outlier_kernel<BK, BV, true>), grid, dim3(kDecWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_outlier_kernel<BK, BV, false>), grid, dim3(kDecWaves * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // 3. Merge splits and rotate back
 // ---------------------------------------------------------------------------
 struct MergeArgs {
@@ -1753,7 +2262,10 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   st = tq_check_quantizer(vq);
   if (st != TQ_OK) return st;
   if (vq->variant != TQ_MSE) return TQ_ERR_UNSUPPORTED;
-  if (kq->split != TQ_SPLIT_NONE || vq->split != TQ_SPLIT_NONE) return TQ_ERR_UNSUPPORTED;
+  // Split caches: both quantizers split (the fused step's small encodes do
+  // not take them).
+  const bool osplit = kq->split != TQ_SPLIT_NONE;
+  if (osplit != (vq->split != TQ_SPLIT_NONE) || (osplit && step != nullptr)) return TQ_ERR_UNSUPPORTED;
   if (query == nullptr || out == nullptr || k_cache == nullptr || v_cache == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 1) return TQ_ERR_INVALID_ARG;
@@ -1820,11 +2332,18 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
     aa.ngroups = p.ngroups;
     aa.nsplit = p.nsplit;
     aa.split_len = p.split_len;
+    aa.kcent_o = kq->centroids_o;
+    aa.vcent_o = vq->centroids_o;
     const dim3 grid(p.nsplit, p.units);
     const int bv = vq->bits;
     const bool al = (max_ctx % kBlockTok) == 0;
     hipError_t e;
-    if (!prod) {
+    if (osplit) {
+      if (bk == 2)
+        e = bv == 2 ? launch_outlier_t<2, 2>(aa, al, grid, s) : launch_outlier_t<2, 3>(aa, al, grid, s);
+      else
+        e = bv == 2 ? launch_outlier_t<3, 2>(aa, al, grid, s) : launch_outlier_t<3, 3>(aa, al, grid, s);
+    } else if (!prod) {
       switch (bk) {
         case 1: e = launch_attn_bv<1, false>(aa, bv, al, grid, s); break;
         case 2: e = launch_attn_bv<2, false>(aa, bv, al, grid, s); break;

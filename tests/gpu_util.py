@@ -228,3 +228,36 @@ def check_encode_split(gpu: dict, ref: dict, bits: int):
         mism += int(bad.sum())
     assert mism <= 1e-5 * gidx.size, (mism, gidx.size)
     return dict(norm_rel=float(rel.max(initial=0)), code_mismatch=mism)
+
+
+def packed_from_oracle_split(enc: dict, q: T.Quantizer) -> T.Packed:
+    """Upload an oracle-produced split cache (norm pairs rounded to float32)."""
+    n = enc["norms"].shape[0]
+    p = T.Packed(q, n, DEV)
+    p.codes.copy_(torch.from_numpy(np.ascontiguousarray(enc["codes"])))
+    p.norms.copy_(torch.from_numpy(enc["norms"].astype(np.float32)))
+    return p
+
+
+def encode_split_away_from_ties(X, consts, bits, seed, dtype):
+    """Oracle split encode of X; rows with a group-rotated coordinate within
+    1e-6 of that group's boundary are redrawn (in place) until none is. Uses
+    the oracle only; the HIP path then encodes the same rows."""
+    (_, to, _), (_, tr, _) = split_books(bits)
+    enc = oracle_encode_split(X, consts, bits)
+    g = np.random.default_rng(seed)
+
+    def near(e):
+        return ((np.min(np.abs(e["y_o"][..., None] - to), axis=-1) < 1e-6).any(axis=1)
+                | (np.min(np.abs(e["y_r"][..., None] - tr), axis=-1) < 1e-6).any(axis=1))
+
+    for _ in range(20):
+        rows = np.nonzero(near(enc))[0]
+        if rows.size == 0:
+            return enc
+        new = X[rows] * (1 + 0.01 * g.standard_normal(X[rows].shape)).astype(np.float32)
+        X[rows] = synth.round_bf16(new) if dtype == "bf16" else new
+        sub = oracle_encode_split(X[rows], consts, bits)
+        for k in enc:
+            enc[k][rows] = sub[k]
+    raise AssertionError("could not move rows away from ties")

@@ -8,8 +8,10 @@ import torch
 
 import synth
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import (DEV, check_encode_split, gpu_packed_arrays, oracle_encode_split, say, split_quantizer,
-                      to_gpu_x)
+from gpu_util import (DEV, check_encode_split, encode_split_away_from_ties, gpu_packed_arrays,
+                      oracle_dequant_split, oracle_encode_split, packed_from_oracle_split, rel_l2_per_head, say,
+                      split_quantizer, to_gpu_x)
+from oracle import decode_attention
 
 pytestmark = pytest.mark.gpu
 D = 128
@@ -56,3 +58,90 @@ def test_split_encode_edge_cases(bits):
     for i, s in enumerate([7, 2, 40, 0]):
         np.testing.assert_array_equal(g["codes"][s], full["codes"][i])
         np.testing.assert_array_equal(g["norms"][s], full["norms"][i])
+
+
+def _split_case(bk, bv, B, Hkv, Hq, Tn, seed):
+    # rows near a tie are redrawn (oracle only), so that the GPU's encode of
+    # the same rows gives the same codes
+    kq, kcst = split_quantizer(bk, "k")
+    vq, vcst = split_quantizer(bv, "v")
+    K = synth.split_kv(B, Hkv, Tn, D, seed, kcst[0], dtype="bf16")
+    V = synth.split_kv(B, Hkv, Tn, D, seed + 1, vcst[0], dtype="bf16")
+    Kf, Vf = K.reshape(-1, D), V.reshape(-1, D)
+    ek = encode_split_away_from_ties(Kf, kcst, bk, seed + 3, "bf16")
+    ev = encode_split_away_from_ties(Vf, vcst, bv, seed + 4, "bf16")
+    Kt = oracle_dequant_split(ek, kcst, bk).reshape(B, Hkv, Tn, D)
+    Vt = oracle_dequant_split(ev, vcst, bv).reshape(B, Hkv, Tn, D)
+    q = synth.gaussian((B, Hq, D), seed + 2, "fp32")
+    return kq, vq, K, V, ek, ev, Kt, Vt, q
+
+
+@pytest.mark.parametrize("bk,bv", [(2, 2), (3, 3), (2, 3), (3, 2)])
+@pytest.mark.parametrize("Tn", [2048, 1000])
+def test_split_decode_parity(bk, bv, Tn):
+    # the oracle's own packed caches: 2 batches, 2 KV heads, 16 query heads
+    # (GQA 8), an aligned and a ragged context
+    B, Hkv, Hq = 2, 2, 16
+    kq, vq, K, V, ek, ev, Kt, Vt, q = _split_case(bk, bv, B, Hkv, Hq, Tn, 900 + 10 * bk + bv)
+    say("split decode", bk, bv, Tn)
+    scale = 1.0 / np.sqrt(D)
+    ref = decode_attention(q, Kt, Vt, scale)
+    kc = packed_from_oracle_split(ek, kq)
+    vc = packed_from_oracle_split(ev, vq)
+    dec = T.Decoder(B, Hq, Hkv, Tn, DEV)
+    out = dec(kq, vq, torch.from_numpy(q).to(DEV), kc, vc).cpu().numpy().astype(np.float64)
+    rel = rel_l2_per_head(out, ref)
+    say("max rel L2", rel.max())
+    assert rel.max() <= 1e-3, rel.max()
+    # ragged lengths per batch
+    lens = np.array([Tn - 7, 33], np.int32)
+    ref2 = decode_attention(q, Kt, Vt, scale, ctx_lens=lens)
+    out2 = dec(kq, vq, torch.from_numpy(q).to(DEV), kc, vc,
+               ctx_lens=torch.from_numpy(lens).to(DEV)).cpu().numpy().astype(np.float64)
+    rel2 = rel_l2_per_head(out2, ref2)
+    assert rel2.max() <= 1e-3, rel2.max()
+
+
+@pytest.mark.parametrize("bk,bv", [(2, 2), (3, 3)])
+def test_split_encode_then_decode(bk, bv):
+    # end to end: the GPU encodes the raw caches, then decodes them
+    B, Hkv, Hq, Tn = 1, 2, 16, 4096
+    kq, vq, K, V, ek, ev, Kt, Vt, q = _split_case(bk, bv, B, Hkv, Hq, Tn, 950 + bk)
+    kc = T.encode(kq, to_gpu_x(K.reshape(-1, D), "bf16"))
+    vc = T.encode(vq, to_gpu_x(V.reshape(-1, D), "bf16"))
+    check_encode_split(gpu_packed_arrays(kc, kq), ek, bk)
+    check_encode_split(gpu_packed_arrays(vc, vq), ev, bv)
+    dec = T.Decoder(B, Hq, Hkv, Tn, DEV)
+    out = dec(kq, vq, torch.from_numpy(q).to(DEV), kc, vc).cpu().numpy().astype(np.float64)
+    ref = decode_attention(q, Kt, Vt, 1.0 / np.sqrt(D))
+    rel = rel_l2_per_head(out, ref)
+    assert rel.max() <= 1e-3, rel.max()
+
+
+@pytest.mark.parametrize("cfg_id", [6, 7])
+def test_split_full_size_benchmark_shape_sampled(cfg_id):
+    # The split workloads' launch configuration: batch 4 x 8 KV heads x 131072
+    # tokens, 64 query heads, split keys and values; GPU encode + decode, the
+    # oracle evaluates two (batch, KV head) units.
+    cfg = synth.CONFIGS[cfg_id]
+    kq, kcst = split_quantizer(cfg.k_bits, "k")
+    vq, vcst = split_quantizer(cfg.v_bits, "v")
+    say("generating", cfg.name)
+    K, V = synth.make_kv(cfg)
+    q = synth.make_query(cfg)
+    units = ((0, 1), (3, 7))
+    encs = {u: (encode_split_away_from_ties(K[u], kcst, cfg.k_bits, 700 + 2 * u[1] + 17 * u[0], cfg.dtype),
+                encode_split_away_from_ties(V[u], vcst, cfg.v_bits, 701 + 2 * u[1] + 17 * u[0], cfg.dtype))
+            for u in units}
+    kp = T.encode(kq, to_gpu_x(K.reshape(-1, D), cfg.dtype))
+    vp = T.encode(vq, to_gpu_x(V.reshape(-1, D), cfg.dtype))
+    dec = T.Decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T, DEV)
+    out = dec(kq, vq, torch.from_numpy(q).to(DEV), kp, vp).cpu().numpy().astype(np.float64)
+    for (b, kvh) in units:
+        Kt = oracle_dequant_split(encs[(b, kvh)][0], kcst, cfg.k_bits)
+        Vt = oracle_dequant_split(encs[(b, kvh)][1], vcst, cfg.v_bits)
+        hs = list(range(kvh * cfg.G, (kvh + 1) * cfg.G))
+        ref = decode_attention(q[b:b + 1, hs], Kt[None, None], Vt[None, None], 1.0 / np.sqrt(D))
+        r = rel_l2_per_head(out[b, hs], ref[0])
+        say("  unit", b, kvh, "rel L2", r.max())
+        assert r.max() <= 1e-3, r.max()
