@@ -20,7 +20,9 @@ for the dominant kernel (the split-attention launch), timed with HIP events
 around that launch on its stream in a second run of the same steps.
 `hadamard_step_ms` / `hadamard_value` time the same step with randomized
 Walsh-Hadamard rotations for keys and values; the encode sweep adds mse-4 and
-prod-4 with that rotation.
+prod-4 with that rotation. `search` times inner-product top-10 of 64 queries
+over 2^20 prod-4 rows (with recall 1@10); `outlier_split` times encode and
+decode of the 2.5- and 3.5-bit outlier-channel split caches at the same shape.
 """
 from __future__ import annotations
 
@@ -128,6 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-encode-sweep", action="store_true")
+    ap.add_argument("--no-split", action="store_true", help="skip the outlier-channel split workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 512 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -326,8 +329,69 @@ def main():
               "db_gbs": round(db_bytes / (s_us * 1e-6) / 1e9, 1),
               "db_streamed_gbs": round((nq_s + 7) // 8 * db_bytes / (s_us * 1e-6) / 1e9, 1),
               "recall_1_at_10": round(recall, 4), "index_build_ms": round(build_ms, 4)}
-    del db, ws_s
+    del ws_s
     log(f"[bench] search: {search}")
+
+    # Outlier-channel split workloads ("2.5-bit": 32 channels at 3 bits + 96 at
+    # 2, and "3.5-bit": 4 + 3; mse keys and values, a norm per group) at the
+    # benchmark's shape: encode of the key cache, the decode call (query
+    # operands, split attention, merge) over three cache copies in turn, and
+    # the split-attention launch alone after a 1 GiB read.
+    split_res = {}
+    if not args.no_split:
+        del db
+        torch.cuda.empty_cache()
+        for cid in (6, 7):
+            c6 = synth.CONFIGS[cid]
+            sc = synth.split_constants(d)
+            kq6 = TA.Quantizer(None, c6.k_bits, "mse", None, dev, split=(sc["rk_o"], sc["rk_r"], sc["ch_k"]))
+            vq6 = TA.Quantizer(None, c6.v_bits, "mse", None, dev, split=(sc["rv_o"], sc["rv_r"], sc["ch_v"]))
+            K6, V6 = synth.make_kv(c6)
+            k6 = torch.from_numpy(K6.reshape(-1, d)).to(torch.bfloat16).to(dev)
+            v6 = torch.from_numpy(V6.reshape(-1, d)).to(torch.bfloat16).to(dev)
+            del K6, V6
+            n6 = c6.B * c6.Hkv * c6.T
+            kc6 = [TA.Packed(kq6, n6, dev) for _ in range(ncopy)]
+            vc6 = [TA.Packed(vq6, n6, dev) for _ in range(ncopy)]
+            for c in range(ncopy):
+                TA.encode(kq6, k6, kc6[c])
+                TA.encode(vq6, v6, vc6[c])
+            a_.record()
+            TA.encode(kq6, k6, kc6[0])
+            b_.record()
+            torch.cuda.synchronize()
+            enc6_ms = a_.elapsed_time(b_)
+            del k6, v6
+            dec6 = TA.Decoder(c6.B, c6.Hq, c6.Hkv, c6.T, dev)
+            for i in range(args.warmup):
+                dec6(kq6, vq6, q, kc6[i % ncopy], vc6[i % ncopy], out=out)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                dec6(kq6, vq6, q, kc6[i % ncopy], vc6[i % ncopy], out=out)
+            torch.cuda.synchronize()
+            ms6 = (time.perf_counter() - t0) / args.steps * 1e3
+            flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+            fl6 = []
+            for i in range(5):
+                dec6(kq6, vq6, q, kc6[0], vc6[0], out=out, phase=1)
+                flush.sum()
+                a_.record()
+                dec6(kq6, vq6, q, kc6[0], vc6[0], out=out, phase=2)
+                b_.record()
+                torch.cuda.synchronize()
+                fl6.append(a_.elapsed_time(b_))
+            del flush, kc6, vc6
+            torch.cuda.empty_cache()
+            us6 = sorted(fl6)[len(fl6) // 2] * 1e3
+            by6 = n6 * (kq6.code_bytes + 8 + vq6.code_bytes + 8)
+            split_res[c6.name] = {
+                "bytes_per_token_head": kq6.code_bytes + 8 + vq6.code_bytes + 8, "packed_cache_bytes": by6,
+                "decode_ms": round(ms6, 5), "decode_gbs": round(by6 / (ms6 * 1e-3) / 1e9, 1),
+                "split_after_flush_us": round(us6, 2), "split_gbs": round(by6 / us6 / 1e3, 1),
+                "frac": round(by6 / us6 / 1e3 / PEAK_HBM_GBS, 4),
+                "encode_mvec_s": round(n6 / (enc6_ms * 1e-3) / 1e6, 1)}
+            log(f"[bench] {c6.name}: {split_res[c6.name]}")
 
     enc = {}
     enc_roof = None
@@ -394,6 +458,7 @@ def main():
         "hadamard_step_ms": round(had_ms, 5),
         "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
         "search": search,
+        "outlier_split": split_res,
         "encode_mvec_s": enc,
         "encode_roofline": enc_roof,
         "cpu_baseline": cpu,
