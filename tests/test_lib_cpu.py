@@ -190,3 +190,49 @@ def test_search_argument_errors_are_synchronous():
     assert call(wsb=ws - 1) == L.TQ_ERR_WORKSPACE
     assert call(ws=(1 << 22) + 64) == L.TQ_ERR_WORKSPACE
     assert call(q=byref(_fake_quantizer(bits=3, variant=L.TQ_PROD))) == L.TQ_ERR_INVALID_ARG   # no sketch arrays
+
+
+def test_split_argument_errors_are_synchronous():
+    # The outlier-channel split takes mse quantizers at 2 or 3 bits with a
+    # dense (block-structured) rotation and the outlier codebook; decode
+    # needs both quantizers split; the fused step and search do not take them.
+    lib = L.load()
+    byref = ctypes.byref
+    p = 1 << 20
+    pk = L.tq_packed(p, p, None, None)
+
+    def split_q(bits=2, variant=L.TQ_MSE, **kw):
+        q = _fake_quantizer(bits=bits, variant=variant)
+        q.split, q.centroids_o, q.boundaries_o = L.TQ_SPLIT_OUTLIER32, p, p
+        for k, v in kw.items():
+            setattr(q, k, v)
+        return q
+
+    def enc(q):
+        return lib.tq_encode(byref(q), p, L.TQ_BF16, 10, 128, byref(pk), None, None)
+
+    assert lib.tq_encode(byref(split_q()), p, L.TQ_BF16, 0, 128, byref(pk), None, None) == L.TQ_OK   # no-op
+    assert lib.tq_encode(byref(split_q(bits=3)), p, L.TQ_BF16, 0, 128, byref(pk), None, None) == L.TQ_OK
+    assert enc(split_q(split=5)) == L.TQ_ERR_UNSUPPORTED
+    assert enc(split_q(bits=4)) == L.TQ_ERR_UNSUPPORTED
+    assert enc(split_q(bits=1)) == L.TQ_ERR_UNSUPPORTED
+    assert enc(split_q(bits=3, variant=L.TQ_PROD)) == L.TQ_ERR_UNSUPPORTED
+    assert enc(split_q(rotation=L.TQ_ROT_HADAMARD)) == L.TQ_ERR_UNSUPPORTED
+    assert enc(split_q(centroids_o=None)) == L.TQ_ERR_INVALID_ARG
+    assert enc(split_q(boundaries_o=None)) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_prepare(byref(split_q(bits=4)), None) == L.TQ_ERR_UNSUPPORTED
+    # decode: both quantizers split, or neither
+    sq, uq = split_q(), _fake_quantizer(bits=2)
+    ws = L.tq_attn_decode_workspace(1, 32, 8, 1000)
+
+    def dec(kq, vq):
+        return lib.tq_attn_decode(byref(kq), byref(vq), p, 1, 32, 8, None, 1000, byref(pk), byref(pk), 0.1, p, p, ws,
+                                  None)
+
+    assert dec(sq, uq) == L.TQ_ERR_UNSUPPORTED
+    assert dec(uq, sq) == L.TQ_ERR_UNSUPPORTED
+    # the fused step and search reject split quantizers
+    assert lib.tq_decode_step(byref(sq), byref(sq), p, 1 << 21, L.TQ_BF16, 128, p, 1, 32, 8, None, 1000, byref(pk),
+                              byref(pk), 0.1, p, p, ws, None) == L.TQ_ERR_UNSUPPORTED
+    sws = L.tq_search_workspace(10, 1000, 8)
+    assert lib.tq_search(byref(sq), p, 10, byref(pk), 1000, 8, p, 1 << 21, 1 << 22, sws, None) == L.TQ_ERR_UNSUPPORTED
