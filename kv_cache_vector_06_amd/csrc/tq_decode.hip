@@ -597,7 +597,9 @@ __device__ __forceinline__ StageOffsets stage_offsets(int n, int g) {
 // reads land asynchronously while later reads of the same statement still use
 // their address registers, so every output is early-clobber (never shares a
 // register with an input), and no statement has an output that goes unused.
-#define TQ_VMW "s_waitcnt vmcnt(%[pend])\n\t"
+// The statement also reads the LDS word at `ap` into `pw` (the partner
+// wavefront's progress; callers without one pass any LDS address).
+#define TQ_VMW "s_waitcnt vmcnt(%[pend])\n\tds_read_b32 %[pw], %[ap]\n\t"
 #define TQ_NORMS "ds_read_b128 %[n0], %[an]\n\tds_read_b128 %[n1], %[an] offset:64\n\t"
 #define TQ_VNORMS "ds_read_b128 %[n2], %[an] offset:128\n\tds_read_b128 %[n3], %[an] offset:192\n\t"
 #define TQ_GAMMA "ds_read_b128 %[n4], %[an] offset:256\n\tds_read_b128 %[n5], %[an] offset:320\n\t"
@@ -605,7 +607,8 @@ __device__ __forceinline__ StageOffsets stage_offsets(int n, int g) {
 #define TQ_LGK "s_waitcnt lgkmcnt(0)"
 
 template <int BK, bool PROD, int BV, int PEND>
-__device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, const StageOffsets& o) {
+__device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, const StageOffsets& o, uint32_t ap,
+                                           uint32_t& pw) {
   const uint32_t an = sb + o.n, ak = sb + o.k, aq = sb + o.q, av0 = sb + o.v0, av1 = sb + o.v1;
   f32x4 n0, n1, n2, n3, n4, n5;
   u32x2 q0, v0, v1, v2, v3, v4, v5, v6, v7;
@@ -633,7 +636,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 #define TQ_KO2 , [ka] "=&v"(ka)
 #define TQ_KO1 , [k0] "=&v"(k0)
 #define TQ_KO0
-#define TQ_OUT2 [n0] "=&v"(n0), [n1] "=&v"(n1)
+#define TQ_OUT2 [n0] "=&v"(n0), [n1] "=&v"(n1), [pw] "=&v"(pw)
 #define TQ_NO3 , [n2] "=&v"(n2), [n3] "=&v"(n3)
 #define TQ_NON TQ_NO3
 #define TQ_NO0
@@ -645,7 +648,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 #define TQ_VON , [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3)
 #define TQ_VO0
 #define TQ_OUTP , [n4] "=&v"(n4), [n5] "=&v"(n5), [q0] "=&v"(q0)
-#define TQ_IN [pend] "n"(PEND), [an] "v"(an), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1), [ak] "v"(ak)
+#define TQ_IN [pend] "n"(PEND), [ap] "v"(ap), [an] "v"(an), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1), [ak] "v"(ak)
 #define TQ_K(VP, VS, KB)                                                                           \
   if constexpr (BK == KB) {                                                                        \
     if constexpr (PROD)                                                                            \
@@ -938,6 +941,138 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
   for (int r = 0; r < 8; ++r) acc[r] = mfma(pa, bv[r], acc[r]);
 }
 
+// LDS stores for the table build, written as asm: the compiler would make a
+// plain LDS store wait for every direct-to-LDS load in flight (it cannot tell
+// the tables from the stage ring), and the first blocks' loads are issued
+// before the build. A build ends with lds_stores_done() before its barrier.
+__device__ __forceinline__ void lds_put4(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_put1(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_stores_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// A load through the scalar unit (uniform address, read-only data): its wait
+// does not include the vector memory loads in flight.
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Codebook of up to 16 entries into one VGPR: lane c (c = lane % 16 < K)
+// holds entry c.
+template <int K>
+__device__ __forceinline__ float codebook_lanes(const float* c, int n) {
+  float cv[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) cv[i] = scalar_load(c + i);
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < K; ++i) v = n == i ? cv[i] : v;
+  return v;
+}
+
+// a·b rounded to fp32: the opaque copy keeps the product out of a fused
+// multiply-add with what follows (the hi/lo split subtracts from it).
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+  float x = a * b;
+  asm("" : "+v"(x));
+  return x;
+}
+
+// v of lane `src` (a lane permute through the LDS crossbar, as asm for the
+// same reason as the stores; it waits for its own result).
+__device__ __forceinline__ float lane_val(float v, int src) {
+  float r;
+  asm volatile("ds_bpermute_b32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(src * 4), "v"(v));
+  return r;
+}
+
+// Fill the lookup tables of a split workgroup (layouts at KLut and kTabBytes)
+// from the codebooks scaled by 64σ; every store is 16 bytes (four private
+// copies of a 4-byte entry, or two of an 8-byte one). Lane c < 16 of each
+// wavefront holds value centroid c in `vcl` and key centroid c in `kcl`, and
+// vsig, ksig are the codebook scales σ (all loaded before the first blocks'
+// loads: a wait for a load issued after them would also wait for them).
+template <int BK, bool PROD, int BV>
+__device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, float ksig, uint8_t* tab,
+                                             uint8_t* lut_k, uint8_t* lut_q, int tid, int nthr) {
+  using KL = KLut<BK>;
+  constexpr int KV = 1 << BV, KK = BK > 0 ? (1 << BK) : 1;
+  const uint32_t tb = lds_addr(tab);
+  const float vs = kCentScale * vsig;
+  auto vcent = [&](int c) { return mul_rounded(lane_val(vcl, c), vs); };
+  // value pairs: entry (c0 | c1 << 4) holds the fp16 centroids of codes c0
+  // (low half) and c1, or 0 when a code is out of range
+  for (int q = tid; q < 256 * 8; q += nthr) {
+    const int e = q >> 3, c0 = e & 15, c1 = e >> 4;
+    const uint32_t w = (c0 < KV && c1 < KV) ? pack_h2(vcent(c0), vcent(c1)) : 0u;
+    lds_put4(tb + 256 * e + 16 * (q & 7), u32x4{w, w, w, w});
+  }
+  if constexpr (BK > 0) {
+    const float ks = kCentScale * ksig;
+    auto kcent = [&](int c) { return mul_rounded(lane_val(kcl, c), ks); };
+    if constexpr (KL::byte_indexed) {
+      // entry e: BK = 4: codes (e & 15, e >> 4), hi pair then lo pair;
+      // BK = 2: codes (e >> 2i) & 3, i < 4, as two pairs
+      for (int q = tid; q < 256 * 8; q += nthr) {
+        const int e = q >> 3;
+        uint32_t w0, w1;
+        if constexpr (BK == 4) {
+          uint16_t h0, l0, h1, l1;
+          split_h(kcent(e & 15), h0, l0);
+          split_h(kcent(e >> 4), h1, l1);
+          w0 = uint32_t(h0) | (uint32_t(h1) << 16);
+          w1 = uint32_t(l0) | (uint32_t(l1) << 16);
+        } else {
+          w0 = pack_h2(kcent(e & 3), kcent((e >> 2) & 3));
+          w1 = pack_h2(kcent((e >> 4) & 3), kcent(e >> 6));
+        }
+        lds_put4(tb + 256 * e + kTabK + 16 * (q & 7), u32x4{w0, w1, w0, w1});
+      }
+    } else if constexpr (KL::priv) {
+      for (int q = tid; q < KL::entries * 8; q += nthr) {
+        const int e = q >> 3;
+        const uint32_t w = pack_h2(kcent(e & (KK - 1)), kcent(e >> BK));
+        lds_put4(tb + 256 * e + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
+      }
+    } else {
+      // 1 bit: one shared table of octets, entry e = 8 codes (bit i of e)
+      const uint32_t w0 = pack_h2(kcent(0), kcent(0)), w1 = pack_h2(kcent(1), kcent(0)),
+                     w2 = pack_h2(kcent(0), kcent(1)), w3 = pack_h2(kcent(1), kcent(1));
+      for (int e = tid; e < KL::entries; e += nthr) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pr = (e >> (2 * i)) & 3;
+          v[i] = pr == 0 ? w0 : pr == 1 ? w1 : pr == 2 ? w2 : w3;
+        }
+        lds_put4(lds_addr(lut_k) + 16 * e, v);
+      }
+    }
+  }
+  if constexpr (PROD) {
+    // sketch nibbles: entry e (4 sign bits), dword w = signs of bits 2w and
+    // 2w + 1 as fp16 ±1 (bit set → +1); 8 bytes per copy
+    for (int q = tid; q < 16 * 16; q += nthr) {
+      const int e = q >> 4;
+      uint32_t d[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
+        const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
+        d[w] = s0 | (s1 << 16);
+      }
+      lds_put4(lds_addr(lut_q) + 256 * e + 16 * (q & 15), u32x4{d[0], d[1], d[0], d[1]});
+    }
+  }
+}
+
 template <int BK, bool PROD, int BV, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) {
   using SL = Stage<BK, PROD, BV>;
@@ -946,6 +1081,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
   __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
   __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
+  __shared__ uint32_t prog[kDecWaves];   // blocks started per wavefront (issue balance)
   // Per wavefront: the stage ring, large enough to hold the 16 x 128 fp32
   // accumulator rows in the epilogue.
   constexpr int kRing = kStages * SL::bytes > 2 * kMaxHeads * kD * 4 ? kStages * SL::bytes : 2 * kMaxHeads * kD * 4;
@@ -962,30 +1098,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
   constexpr int nthr = kDecWaves * 64;
 
-  // ---- query operands (loads issued first; used in the loop) ---------------
-  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
-  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bq[4], bs[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bq[s] = fr[s * 64 + lane];
-    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
-  }
-  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
-  // the scaled centroids for the table build: values in 0..15, keys in 16..31
-  __shared__ float cent[32];
-  if (tid < 32) {
-    constexpr int KK = BK > 0 ? (1 << BK) : 1, KV = 1 << BV;
-    float v = 0.f;
-    if (tid < 16) {
-      if (tid < KV) v = a.vcent[tid] * (kCentScale * a.vh->sigma);
-    } else if (BK > 0 && tid - 16 < KK) {
-      v = a.kcent[tid - 16] * (kCentScale * a.kh->sigma);
-    }
-    cent[tid] = v;
-  }
-
-  // ---- token range of this wavefront ---------------------------------------
+  // ---- token range of this wavefront; its first two blocks' loads go out
+  // before the table build, so their latency hides it ------------------------
   int64_t L = a.max_ctx;
   if (a.ctx_lens) {
     const int64_t l = a.ctx_lens[b];
@@ -1004,25 +1118,23 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const float* kg = PROD ? a.kg + base : a.kn;
   const uint8_t* vc = a.vc + base * (16 * BV);
   const float* vn = a.vn + base;
-
-  __syncthreads();   // the centroids
-
-  // ---- lookup tables (the value pair table first: the compiler orders its
-  // LDS writes after any pending direct-to-LDS loads) -------------------------
-  const float* vcs = cent;
-  const float* kcs = cent + 16;
-  {
-    // entry (c0 | c1 << 4): the fp16 centroids of value codes c0 (low half) and c1.
-    constexpr int KV = 1 << BV;
-    for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
-      const int e = idx / kCopies, c = idx % kCopies;
-      const int c0 = e & 15, c1 = e >> 4;
-      *reinterpret_cast<uint32_t*>(tab + 256 * e + 4 * c) = (c0 < KV && c1 < KV) ? pack_h2(vcs[c0], vcs[c1]) : 0u;
-    }
+  // the codebooks (lane c < 16 holds centroid c) and the query operands
+  constexpr int KV = 1 << BV, KK = BK > 0 ? (1 << BK) : 1;
+  const float vcl = codebook_lanes<KV>(a.vcent, n);
+  const float kcl = BK > 0 ? codebook_lanes<KK>(a.kcent, n) : 0.f;
+  const float vsig = scalar_load(&a.vh->sigma), ksig = BK > 0 ? scalar_load(&a.kh->sigma) : 0.f;
+  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
+  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
+  u32x4 bq[4], bs[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bq[s] = fr[s * 64 + lane];
+    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
   }
-  // The first two blocks' loads go out before the tables are built.
+  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
+  asm volatile("" ::: "memory");   // the loads above go out before the blocks' loads
   uint8_t* ring = &stage[wave][0];
-  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const uint32_t ring_addr = lds_addr(ring);
   const StageOffsets so = stage_offsets<BK, PROD, BV>(n, g);
   const DmaLane dl = dma_lane<BK, BV>(lane);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
@@ -1031,52 +1143,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   if (nblk > 1)
     stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, vc, kn, vn, kg);
 
-  if constexpr (BK > 0) {
-    constexpr int KK = 1 << BK;
-    if constexpr (KL::byte_indexed) {
-      // entry e: BK = 4: codes (e & 15, e >> 4), hi pair then lo pair;
-      // BK = 2: codes (e >> 2i) & 3, i < 4, as two pairs
-      for (int idx = tid; idx < 256 * 16; idx += nthr) {
-        const int e = idx >> 4, c = idx & 15;
-        uint32_t w0, w1;
-        if constexpr (BK == 4) {
-          uint16_t h0, l0, h1, l1;
-          split_h(kcs[e & 15], h0, l0);
-          split_h(kcs[e >> 4], h1, l1);
-          w0 = uint32_t(h0) | (uint32_t(h1) << 16);
-          w1 = uint32_t(l0) | (uint32_t(l1) << 16);
-        } else {
-          w0 = pack_h2(kcs[e & 3], kcs[(e >> 2) & 3]);
-          w1 = pack_h2(kcs[(e >> 4) & 3], kcs[e >> 6]);
-        }
-        *reinterpret_cast<u32x2*>(tab + 256 * e + kTabK + 8 * c) = u32x2{w0, w1};
-      }
-    } else if constexpr (KL::priv) {
-      for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
-        const int e = idx / kCopies, c = idx % kCopies;
-        *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) = pack_h2(kcs[e & (KK - 1)], kcs[e >> BK]);
-      }
-    } else {
-      uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
-      for (int e = tid; e < KL::entries; e += nthr) {
-        constexpr int per = KL::per;
-        uint16_t hi[8];
-#pragma unroll
-        for (int i = 0; i < per; ++i) hi[i] = f2h_bits(kcs[(e >> (BK * i)) & (KK - 1)]);
-#pragma unroll
-        for (int i = 0; i < per / 2; ++i) lk[e * KL::dwords + i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
-      }
-    }
-  }
-  if constexpr (PROD) {
-    // entry e (4 sign bits), dword w: signs of bits 2w and 2w + 1
-    for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
-      const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
-      const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
-      const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
-      *reinterpret_cast<uint32_t*>(lut_q + 256 * e + 8 * c + 4 * w) = s0 | (s1 << 16);
-    }
-  }
+  // ---- lookup tables ---------------------------------------------------------
+  build_tables<BK, PROD, BV>(vcl, kcl, vsig, ksig, tab, lut_k, lut_q, tid, nthr);
+  if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
+  lds_stores_done();
   Luts T;
   const uint32_t cp = lane & 31;            // private copy of this lane
   T.k = KL::priv ? tab : lut_k;
@@ -1095,15 +1165,27 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
 
   // Block i is read from stage i % kStages; the loads for block i + 2 go
   // into the stage just read.
+  // Issue balance: of the two wavefronts on a SIMD (w and w ^ 4), the older
+  // one wins issue ties and would finish its share long before the other,
+  // leaving its SIMD half idle while the workgroup waits. Each wavefront
+  // posts the number of its current block and, when it is ahead of its
+  // partner, lowers its priority until the partner catches up.
+  const uint32_t prog_own = lds_addr(&prog[wave]), prog_partner = lds_addr(&prog[wave ^ 4]);
   int cur = 0;
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint32_t t0 = t_begin + i * kBlockTok;
     Block<BK, PROD, BV> R;
     const uint32_t sb = ring_addr + cur * SL::bytes;
+    lds_put1(prog_own, i);
+    uint32_t pw;
     if (i + 1 < nblk)
-      read_block<BK, PROD, BV, SL::dma>(R, sb, so);
+      read_block<BK, PROD, BV, SL::dma>(R, sb, so, prog_partner, pw);
     else
-      read_block<BK, PROD, BV, 0>(R, sb, so);
+      read_block<BK, PROD, BV, 0>(R, sb, so, prog_partner, pw);
+    if (__builtin_amdgcn_readfirstlane(pw) < i)
+      __builtin_amdgcn_s_setprio(0);
+    else
+      __builtin_amdgcn_s_setprio(1);
     if (i + 2 < nblk) {
       // block i + 2 goes to stage (cur + 2) % kStages: with two stages, the one
       // just read (read_block waited for all of its reads)
@@ -1114,6 +1196,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     attend_block<BK, PROD, BV>(R, t0, t_end, n, g, T, bq, bs, iqs, lomask, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
   }
+  __builtin_amdgcn_s_setprio(0);
   const float l_run = sum4g(st.l);
 
   // ---- merge the workgroup's wavefronts ------------------------------------
@@ -2026,14 +2109,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
     const uint32_t sb = ring_addr + cur * SL::bytes;
     // the blocks after this one already issued: their loads may stay in flight
     const uint32_t ahead = min(nblk - 1 - i, uint32_t(NST - 1));
+    uint32_t pw;   // unused: the search has no issue balance
     if (ahead == uint32_t(NST - 1))
-      read_block<BK, PROD, 0, (NST - 1) * SL::dma>(R, sb, so);
+      read_block<BK, PROD, 0, (NST - 1) * SL::dma>(R, sb, so, sb, pw);
     else if (NST > 3 && ahead == 2)
-      read_block<BK, PROD, 0, (NST > 3 ? 2 : 0) * SL::dma>(R, sb, so);
+      read_block<BK, PROD, 0, (NST > 3 ? 2 : 0) * SL::dma>(R, sb, so, sb, pw);
     else if (NST > 2 && ahead == 1)
-      read_block<BK, PROD, 0, (NST > 2 ? 1 : 0) * SL::dma>(R, sb, so);
+      read_block<BK, PROD, 0, (NST > 2 ? 1 : 0) * SL::dma>(R, sb, so, sb, pw);
     else
-      read_block<BK, PROD, 0, 0>(R, sb, so);
+      read_block<BK, PROD, 0, 0>(R, sb, so, sb, pw);
     if (i + NST < nblk)
       stage_block<BK, PROD, 0, AL>(ring + cur * SL::bytes, t0 + NST * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
                                    a.kn, kg);
