@@ -504,6 +504,12 @@ __device__ __forceinline__ DmaLane dma_lane(int lane) {
   return d;
 }
 
+// Cache policy of the packed-cache loads: non-temporal. The cache is streamed
+// once per launch; kept out of the caches' normal replacement it leaves the
+// rotations, the query operands and the partials resident for the small
+// kernels around the scan.
+constexpr int kStream = 2;
+
 // Issue the direct-to-LDS loads of the block starting at token t0 into `st`
 // (a wave-uniform LDS address). Without AL, token indices past `last` are
 // clamped to it (those tokens are masked later); with AL every token of the
@@ -541,24 +547,24 @@ __device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t l
 #pragma unroll
   for (int j = 0; j < KD::full; ++j)
     __builtin_amdgcn_global_load_lds(src(kc, KR, d.ktok[j], d.kcol[j], d.koff[j]), TQ_LDS(st + L::kc + 1024 * j),
-                                     16, 0, 0);
+                                     16, 0, kStream);
 #pragma unroll
   for (int j = 0; j < VD::full; ++j)
     __builtin_amdgcn_global_load_lds(src(vc, VR, d.vtok[j], d.vcol[j], d.voff[j]), TQ_LDS(st + L::vc + 1024 * j),
-                                     16, 0, 0);
+                                     16, 0, kStream);
   if (lane < 32) {
     constexpr int kj = KD::full, vj = VD::full;
     if constexpr (KD::half)
       __builtin_amdgcn_global_load_lds(src(kc, KR, d.ktok[kj], d.kcol[kj], d.koff[kj]),
-                                       TQ_LDS(st + L::kc + 1024 * kj), 16, 0, 0);
+                                       TQ_LDS(st + L::kc + 1024 * kj), 16, 0, kStream);
     if constexpr (PROD)
-      __builtin_amdgcn_global_load_lds(src(kq, 16, d.ntok, 0, 16 * d.ntok), TQ_LDS(st + L::qj), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src(kq, 16, d.ntok, 0, 16 * d.ntok), TQ_LDS(st + L::qj), 16, 0, kStream);
     if constexpr (VD::half)
       __builtin_amdgcn_global_load_lds(src(vc, VR, d.vtok[vj], d.vcol[vj], d.voff[vj]),
-                                       TQ_LDS(st + L::vc + 1024 * vj), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(nsrc(kn), TQ_LDS(st + L::kn), 4, 0, 0);
-    if constexpr (BV > 0) __builtin_amdgcn_global_load_lds(nsrc(vn), TQ_LDS(st + L::vn), 4, 0, 0);
-    if constexpr (PROD) __builtin_amdgcn_global_load_lds(nsrc(kg), TQ_LDS(st + L::kg), 4, 0, 0);
+                                       TQ_LDS(st + L::vc + 1024 * vj), 16, 0, kStream);
+    __builtin_amdgcn_global_load_lds(nsrc(kn), TQ_LDS(st + L::kn), 4, 0, kStream);
+    if constexpr (BV > 0) __builtin_amdgcn_global_load_lds(nsrc(vn), TQ_LDS(st + L::vn), 4, 0, kStream);
+    if constexpr (PROD) __builtin_amdgcn_global_load_lds(nsrc(kg), TQ_LDS(st + L::kg), 4, 0, kStream);
   }
 }
 
@@ -953,6 +959,11 @@ __device__ __forceinline__ void lds_put1(uint32_t addr, uint32_t v) {
 }
 __device__ __forceinline__ void lds_stores_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// The workgroup barrier after a table build: the build's stores are done
+// (lds_stores_done), and no wait for the blocks' loads in flight (a
+// __syncthreads would wait for them: they write LDS).
+__device__ __forceinline__ void tables_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
@@ -985,8 +996,20 @@ __device__ __forceinline__ float mul_rounded(float a, float b) {
   return x;
 }
 
+// Codebook q of up to 16 entries into lanes 16q .. 16q + K - 1 of v.
+template <int K>
+__device__ __forceinline__ float codebook_group(const float* c, int q, int lane, float v) {
+  float cv[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) cv[i] = scalar_load(c + i);
+#pragma unroll
+  for (int i = 0; i < K; ++i) v = lane == 16 * q + i ? cv[i] : v;
+  return v;
+}
+
 // v of lane `src` (a lane permute through the LDS crossbar, as asm for the
-// same reason as the stores; it waits for its own result).
+// same reason as the stores; it waits for its own result). Called with every
+// lane active: a permute does not read the registers of inactive lanes.
 __device__ __forceinline__ float lane_val(float v, int src) {
   float r;
   asm volatile("ds_bpermute_b32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(src * 4), "v"(v));
@@ -1011,7 +1034,8 @@ __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, f
   // (low half) and c1, or 0 when a code is out of range
   for (int q = tid; q < 256 * 8; q += nthr) {
     const int e = q >> 3, c0 = e & 15, c1 = e >> 4;
-    const uint32_t w = (c0 < KV && c1 < KV) ? pack_h2(vcent(c0), vcent(c1)) : 0u;
+    const uint32_t p = pack_h2(vcent(c0 & (KV - 1)), vcent(c1 & (KV - 1)));
+    const uint32_t w = (c0 < KV && c1 < KV) ? p : 0u;
     lds_put4(tb + 256 * e + 16 * (q & 7), u32x4{w, w, w, w});
   }
   if constexpr (BK > 0) {
@@ -1156,7 +1180,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   T.qlane = 8u * cp;
   T.vlane = 4u * cp;
   const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
-  __syncthreads();
+  tables_barrier();
 
   SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
   f32x4 acc[8];
@@ -1288,17 +1312,17 @@ __device__ __forceinline__ void ostage_block(uint8_t* st, uint32_t t0, uint32_t 
   for (int j = 0; j < L::kld; ++j) {
     const uint32_t i = 64u * j + lane;
     if (j + 1 < L::kld || (L::kdw % 64) == 0 || i < uint32_t(L::kdw))
-      __builtin_amdgcn_global_load_lds(ks + (AL ? i : min(i, klim)), TQ_LDS(st + L::kc + 256 * j), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(ks + (AL ? i : min(i, klim)), TQ_LDS(st + L::kc + 256 * j), 4, 0, kStream);
   }
 #pragma unroll
   for (int j = 0; j < L::vld; ++j) {
     const uint32_t i = 64u * j + lane;
     if (j + 1 < L::vld || (L::vdw % 64) == 0 || i < uint32_t(L::vdw))
-      __builtin_amdgcn_global_load_lds(vs + (AL ? i : min(i, vlim)), TQ_LDS(st + L::vc + 256 * j), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs + (AL ? i : min(i, vlim)), TQ_LDS(st + L::vc + 256 * j), 4, 0, kStream);
   }
   const uint32_t nl = AL ? uint32_t(lane) : min(uint32_t(lane), 2u * ntok - 1u);
-  __builtin_amdgcn_global_load_lds(kn + 2 * size_t(t0) + nl, TQ_LDS(st + L::kn), 4, 0, 0);
-  __builtin_amdgcn_global_load_lds(vn + 2 * size_t(t0) + nl, TQ_LDS(st + L::vn), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(kn + 2 * size_t(t0) + nl, TQ_LDS(st + L::kn), 4, 0, kStream);
+  __builtin_amdgcn_global_load_lds(vn + 2 * size_t(t0) + nl, TQ_LDS(st + L::vn), 4, 0, kStream);
 }
 
 // One lane's registers of a staged split block: its key words of both tiles
@@ -1333,7 +1357,7 @@ __device__ __forceinline__ OOffsets ostage_offsets(int n, int g) {
 // newest PEND of this wavefront), every read of the stage, then the wait for
 // the reads, in one statement with early-clobber outputs.
 template <int BK, int BV, int PEND>
-__device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffsets& o) {
+__device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffsets& o, uint32_t ap, uint32_t& pw) {
   using L = OStage<BK, BV>;
   constexpr int KT = 4 * L::KR;            // dwords between the two key tiles (16 rows)
   constexpr int VT = L::VR / 4;            // dwords between consecutive tokens
@@ -1345,6 +1369,7 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
   // slot (τ, i) is token 16τ + 4g + i: dword offset (16τ + i)·VT
   asm volatile(
       "s_waitcnt vmcnt(%[pend])\n\t"
+      "ds_read_b32 %[pw], %[ap]\n\t"
       "ds_read2_b32 %[k0], %[ak] offset1:1\n\t"
       "ds_read2_b32 %[k1], %[ak] offset0:2 offset1:3\n\t"
       "ds_read2_b32 %[k2], %[ak] offset0:%[kt0] offset1:%[kt1]\n\t"
@@ -1369,8 +1394,8 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
       : [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2), [k3] "=&v"(k3), [n0] "=&v"(n0), [n1] "=&v"(n1),
         [n2] "=&v"(n2), [n3] "=&v"(n3), [m0] "=&v"(m0), [m1] "=&v"(m1), [m2] "=&v"(m2), [m3] "=&v"(m3),
         [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5),
-        [v6] "=&v"(v6), [v7] "=&v"(v7)
-      : [pend] "n"(PEND), [ak] "v"(ak), [an] "v"(an), [av] "v"(av), [kt0] "n"(KT), [kt1] "n"(KT + 1),
+        [v6] "=&v"(v6), [v7] "=&v"(v7), [pw] "=&v"(pw)
+      : [pend] "n"(PEND), [ap] "v"(ap), [ak] "v"(ak), [an] "v"(an), [av] "v"(av), [kt0] "n"(KT), [kt1] "n"(KT + 1),
         [kt2] "n"(KT + 2), [kt3] "n"(KT + 3), [s0] "n"(0), [s0b] "n"(1), [s1] "n"(VT), [s1b] "n"(VT + 1),
         [s2] "n"(2 * VT), [s2b] "n"(2 * VT + 1), [s3] "n"(3 * VT), [s3b] "n"(3 * VT + 1), [s4] "n"(16 * VT),
         [s4b] "n"(16 * VT + 1), [s5] "n"(17 * VT), [s5b] "n"(17 * VT + 1), [s6] "n"(18 * VT),
@@ -1611,6 +1636,56 @@ __device__ __forceinline__ void write_partials_o(const AttnArgs& a, const Softma
   }
 }
 
+// Lookup tables of the split kernel: value pairs (outlier codes in the lower
+// half of rows 0..255, regular codes in the upper half of rows below
+// kKeyRegRow), regular key pairs (rows kKeyRegRow + e, upper half) and
+// outlier key pairs (rows kKeyOutRow + e for 3 bits; for 4 bits `tab2`, hi
+// and lo pairs of copy c at 128e + 8c). Lane 16q + c of `cl` holds centroid c
+// of codebook q: 0 outlier values, 1 regular values, 2 outlier keys, 3 regular
+// keys. Stores and permutes as in build_tables.
+template <int BK, int BV>
+__device__ __forceinline__ void build_tables_o(float cl, float vsig, float ksig, uint8_t* tab, uint8_t* tab2,
+                                               int tid, int nthr) {
+  constexpr int BKO = BK + 1, BVO = BV + 1;
+  constexpr int KVO = 1 << BVO, KV = 1 << BV;
+  const uint32_t tb = lds_addr(tab);
+  const float vs = kCentScale * vsig, ks = kCentScale * ksig;
+  auto cent = [&](int q, int c, float sc) { return mul_rounded(lane_val(cl, 16 * q + c), sc); };
+  for (int q = tid; q < 256 * 8; q += nthr) {
+    const int e = q >> 3, c0 = e & 15, c1 = e >> 4;
+    const uint32_t po = pack_h2(cent(0, c0 & (KVO - 1), vs), cent(0, c1 & (KVO - 1), vs));
+    const uint32_t pr = pack_h2(cent(1, c0 & (KV - 1), vs), cent(1, c1 & (KV - 1), vs));
+    const uint32_t wo = (c0 < KVO && c1 < KVO) ? po : 0u;
+    lds_put4(tb + 256 * e + 16 * (q & 7), u32x4{wo, wo, wo, wo});
+    if (e < kKeyRegRow) {
+      const uint32_t wr = (c0 < KV && c1 < KV) ? pr : 0u;
+      lds_put4(tb + 256 * e + kTabK + 16 * (q & 7), u32x4{wr, wr, wr, wr});
+    }
+  }
+  constexpr int KR = 1 << (2 * BK);   // regular key pair entries
+  for (int q = tid; q < KR * 8; q += nthr) {
+    const int e = q >> 3;
+    const uint32_t w = pack_h2(cent(3, e & ((1 << BK) - 1), ks), cent(3, e >> BK, ks));
+    lds_put4(tb + 256 * (kKeyRegRow + e) + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
+  }
+  if constexpr (BKO == 4) {
+    for (int q = tid; q < 256 * 8; q += nthr) {
+      const int e = q >> 3;
+      uint16_t h0, l0, h1, l1;
+      split_h(cent(2, e & 15, ks), h0, l0);
+      split_h(cent(2, e >> 4, ks), h1, l1);
+      const uint32_t w0 = uint32_t(h0) | (uint32_t(h1) << 16), w1 = uint32_t(l0) | (uint32_t(l1) << 16);
+      lds_put4(lds_addr(tab2) + 128 * e + 16 * (q & 7), u32x4{w0, w1, w0, w1});
+    }
+  } else {
+    for (int q = tid; q < 64 * 8; q += nthr) {
+      const int e = q >> 3;
+      const uint32_t w = pack_h2(cent(2, e & 7, ks), cent(2, e >> 3, ks));
+      lds_put4(tb + 256 * (kKeyOutRow + e) + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
+    }
+  }
+}
+
 template <int BK, int BV, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a) {
   using SL = OStage<BK, BV>;
@@ -1618,11 +1693,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
   __shared__ __attribute__((aligned(256))) uint8_t tab2[BKO == 4 ? 256 * 128 : 16];
   __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
+  __shared__ uint32_t prog[kDecWaves];   // blocks started per wavefront (issue balance)
   constexpr int kRing = kStages * SL::bytes > kMaxHeads * kD * 4 ? kStages * SL::bytes : kMaxHeads * kD * 4;
   __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][kRing];
-  // scaled centroids: outlier values 0..15, regular values 16..23, outlier
-  // keys 32..47, regular keys 48..55
-  __shared__ float cent[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1634,22 +1707,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const int b = unit / (a.ngroups * a.Hkv);
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
   constexpr int nthr = kDecWaves * 64;
-
-  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
-  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bq[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) bq[s] = fr[s * 64 + lane];
-  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
-  if (tid < 64) {
-    const int grp4 = tid >> 4, k = tid & 15;
-    float v = 0.f;
-    if (grp4 == 0 && k < (1 << BVO)) v = a.vcent_o[k] * (kCentScale * a.vh->sigma);
-    if (grp4 == 1 && k < (1 << BV)) v = a.vcent[k] * (kCentScale * a.vh->sigma);
-    if (grp4 == 2 && k < (1 << BKO)) v = a.kcent_o[k] * (kCentScale * a.kh->sigma);
-    if (grp4 == 3 && k < (1 << BK)) v = a.kcent[k] * (kCentScale * a.kh->sigma);
-    cent[tid] = v;
-  }
 
   int64_t L = a.max_ctx;
   if (a.ctx_lens) {
@@ -1667,67 +1724,58 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const uint8_t* vc = a.vc + base * SL::VR;
   const float* kn = a.kn + 2 * base;
   const float* vn = a.vn + 2 * base;
-  __syncthreads();   // the centroids
 
-  // value pair tables first (their LDS writes then come before any direct
-  // load is in flight)
-  for (int idx = tid; idx < 256 * kCopies; idx += nthr) {
-    const int e = idx / kCopies, c = idx % kCopies;
-    const int c0 = e & 15, c1 = e >> 4;
-    const uint32_t wo = (c0 < (1 << BVO) && c1 < (1 << BVO)) ? pack_h2(cent[c0], cent[c1]) : 0u;
-    *reinterpret_cast<uint32_t*>(tab + 256 * e + 4 * c) = wo;
-    if (e < kKeyRegRow) {
-      const uint32_t wr = (c0 < (1 << BV) && c1 < (1 << BV)) ? pack_h2(cent[16 + c0], cent[16 + c1]) : 0u;
-      *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) = wr;
-    }
-  }
+  // the four codebooks, the scales σ and the query operands go out before
+  // the first blocks' loads (as in attn_split_kernel)
+  float cl = 0.f;
+  cl = codebook_group<1 << BVO>(a.vcent_o, 0, lane, cl);
+  cl = codebook_group<1 << BV>(a.vcent, 1, lane, cl);
+  cl = codebook_group<1 << BKO>(a.kcent_o, 2, lane, cl);
+  cl = codebook_group<1 << BK>(a.kcent, 3, lane, cl);
+  const float vsig = scalar_load(&a.vh->sigma), ksig = scalar_load(&a.kh->sigma);
+  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
+  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
+  u32x4 bq[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) bq[s] = fr[s * 64 + lane];
+  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
+  asm volatile("" ::: "memory");
   uint8_t* ring = &stage[wave][0];
-  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const uint32_t ring_addr = lds_addr(ring);
   const OOffsets so = ostage_offsets<BK, BV>(n, g);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
   if (nblk > 0) ostage_block<BK, BV, AL>(ring, t_begin, last, lane, kc, vc, kn, vn);
   if (nblk > 1) ostage_block<BK, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, vc, kn, vn);
 
-  // key pair tables: regular (2·BK-bit entries) and outlier
-  for (int idx = tid; idx < (1 << (2 * BK)) * kCopies; idx += nthr) {
-    const int e = idx / kCopies, c = idx % kCopies;
-    *reinterpret_cast<uint32_t*>(tab + 256 * (kKeyRegRow + e) + kTabK + 4 * c) =
-        pack_h2(cent[48 + (e & ((1 << BK) - 1))], cent[48 + (e >> BK)]);
-  }
-  if constexpr (BKO == 4) {
-    for (int idx = tid; idx < 256 * 16; idx += nthr) {
-      const int e = idx >> 4, c = idx & 15;
-      uint16_t h0, l0, h1, l1;
-      split_h(cent[32 + (e & 15)], h0, l0);
-      split_h(cent[32 + (e >> 4)], h1, l1);
-      *reinterpret_cast<u32x2*>(tab2 + 128 * e + 8 * c) =
-          u32x2{uint32_t(h0) | (uint32_t(h1) << 16), uint32_t(l0) | (uint32_t(l1) << 16)};
-    }
-  } else {
-    for (int idx = tid; idx < 64 * kCopies; idx += nthr) {
-      const int e = idx / kCopies, c = idx % kCopies;
-      *reinterpret_cast<uint32_t*>(tab + 256 * (kKeyOutRow + e) + kTabK + 4 * c) =
-          pack_h2(cent[32 + (e & 7)], cent[32 + (e >> 3)]);
-    }
-  }
+  build_tables_o<BK, BV>(cl, vsig, ksig, tab, tab2, tid, nthr);
+  if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
+  lds_stores_done();
   const uint32_t cp = lane & 31;
   const uint32_t lane_lo = 4u * cp, lane_hi = kTabK + 4u * cp, lane8 = 8u * (lane & 15);
   const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
-  __syncthreads();
+  tables_barrier();
 
   SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
   f32x4 acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // issue balance between the two wavefronts of a SIMD, as in attn_split_kernel
+  const uint32_t prog_own = lds_addr(&prog[wave]), prog_partner = lds_addr(&prog[wave ^ 4]);
   int cur = 0;
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint32_t t0 = t_begin + i * kBlockTok;
     OBlock R;
     const uint32_t sb = ring_addr + cur * SL::bytes;
+    lds_put1(prog_own, i);
+    uint32_t pw;
     if (i + 1 < nblk)
-      oread_block<BK, BV, SL::dma>(R, sb, so);
+      oread_block<BK, BV, SL::dma>(R, sb, so, prog_partner, pw);
     else
-      oread_block<BK, BV, 0>(R, sb, so);
+      oread_block<BK, BV, 0>(R, sb, so, prog_partner, pw);
+    if (__builtin_amdgcn_readfirstlane(pw) < i)
+      __builtin_amdgcn_s_setprio(0);
+    else
+      __builtin_amdgcn_s_setprio(1);
     if (i + 2 < nblk) {
       const int nx = (cur + 2) % kStages;
       ostage_block<BK, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, vc, kn, vn);
@@ -1735,6 +1783,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
     oattend_block<BK, BV>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bq, iqs, lomask, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
   }
+  __builtin_amdgcn_s_setprio(0);
   write_partials_o<kRing>(a, st, acc, wm, wl, stage, unit, split, gc, n, g, wave, tid);
 }
 
