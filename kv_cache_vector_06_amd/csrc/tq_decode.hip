@@ -1030,9 +1030,10 @@ __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, f
   const uint32_t tb = lds_addr(tab);
   const float vs = kCentScale * vsig;
   auto vcent = [&](int c) { return mul_rounded(lane_val(vcl, c), vs); };
-  // value pairs: entry (c0 | c1 << 4) holds the fp16 centroids of codes c0
-  // (low half) and c1, or 0 when a code is out of range
-  for (int q = tid; q < 256 * 8; q += nthr) {
+  // value pairs (none for BV = 0, keys only): entry (c0 | c1 << 4) holds the
+  // fp16 centroids of codes c0 (low half) and c1, or 0 when a code is out of
+  // range
+  for (int q = tid; BV > 0 && q < 256 * 8; q += nthr) {
     const int e = q >> 3, c0 = e & 15, c1 = e >> 4;
     const uint32_t p = pack_h2(vcent(c0 & (KV - 1)), vcent(c1 & (KV - 1)));
     const uint32_t w = (c0 < KV && c1 < KV) ? p : 0u;
@@ -2043,7 +2044,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][NST * SL::bytes];
   __shared__ SearchLds S;
-  __shared__ float cent[16];
+  __shared__ uint32_t prog[kDecWaves];   // blocks started per wavefront (issue balance)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -2053,18 +2054,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   const int gc = min(kMaxHeads, a.nq - unit * kMaxHeads);
   const int k = a.k;
   constexpr int nthr = kDecWaves * 64;
-
-  // ---- query operands and centroids ----
-  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
-  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bq[4], bs[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bq[s] = fr[s * 64 + lane];
-    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
-  }
-  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
-  if (tid < 16) cent[tid] = (BK > 0 && tid < (1 << BK)) ? a.kcent[tid] * (kCentScale * a.kh->sigma) : 0.f;
 
   // ---- token range of this wavefront ----
   const int64_t per_wave = a.split_len / kDecWaves;
@@ -2076,10 +2065,24 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   const uint8_t* kc = BK > 0 ? a.kc : reinterpret_cast<const uint8_t*>(a.kn);
   const uint8_t* kq = PROD ? a.kq : reinterpret_cast<const uint8_t*>(a.kn);
   const float* kg = PROD ? a.kg : a.kn;
-  __syncthreads();   // the centroids
 
+  // ---- codebook, scale and query operands, then the first blocks' loads
+  // (as in attn_split_kernel) ----
+  constexpr int KK = BK > 0 ? (1 << BK) : 1;
+  const float kcl = BK > 0 ? codebook_lanes<KK>(a.kcent, n) : 0.f;
+  const float ksig = BK > 0 ? scalar_load(&a.kh->sigma) : 0.f;
+  const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
+  const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
+  u32x4 bq[4], bs[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bq[s] = fr[s * 64 + lane];
+    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
+  }
+  const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
+  asm volatile("" ::: "memory");
   uint8_t* ring = &stage[wave][0];
-  const uint32_t ring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const uint32_t ring_addr = lds_addr(ring);
   const StageOffsets so = stage_offsets<BK, PROD, 0>(n, g);
   const DmaLane dl = dma_lane<BK, 0>(lane);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
@@ -2089,50 +2092,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
       stage_block<BK, PROD, 0, AL>(ring + b * SL::bytes, t_begin + b * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
                                    a.kn, kg);
 
-  // ---- key and sketch tables (as in the decode kernel) ----
-  if constexpr (BK > 0) {
-    constexpr int KK = 1 << BK;
-    if constexpr (KL::byte_indexed) {
-      for (int idx = tid; idx < 256 * 16; idx += nthr) {
-        const int e = idx >> 4, c = idx & 15;
-        uint32_t w0, w1;
-        if constexpr (BK == 4) {
-          uint16_t h0, l0, h1, l1;
-          split_h(cent[e & 15], h0, l0);
-          split_h(cent[e >> 4], h1, l1);
-          w0 = uint32_t(h0) | (uint32_t(h1) << 16);
-          w1 = uint32_t(l0) | (uint32_t(l1) << 16);
-        } else {
-          w0 = pack_h2(cent[e & 3], cent[(e >> 2) & 3]);
-          w1 = pack_h2(cent[(e >> 4) & 3], cent[e >> 6]);
-        }
-        *reinterpret_cast<u32x2*>(tab + 256 * e + kTabK + 8 * c) = u32x2{w0, w1};
-      }
-    } else if constexpr (KL::priv) {
-      for (int idx = tid; idx < KL::entries * kCopies; idx += nthr) {
-        const int e = idx / kCopies, c = idx % kCopies;
-        *reinterpret_cast<uint32_t*>(tab + 256 * e + kTabK + 4 * c) = pack_h2(cent[e & (KK - 1)], cent[e >> BK]);
-      }
-    } else {
-      uint32_t* lk = reinterpret_cast<uint32_t*>(lut_k);
-      for (int e = tid; e < KL::entries; e += nthr) {
-        constexpr int per = KL::per;
-        uint16_t hi[8];
-#pragma unroll
-        for (int i = 0; i < per; ++i) hi[i] = f2h_bits(cent[(e >> (BK * i)) & (KK - 1)]);
-#pragma unroll
-        for (int i = 0; i < per / 2; ++i) lk[e * KL::dwords + i] = uint32_t(hi[2 * i]) | (uint32_t(hi[2 * i + 1]) << 16);
-      }
-    }
-  }
-  if constexpr (PROD) {
-    for (int idx = tid; idx < 16 * kCopies * 2; idx += nthr) {
-      const int e = idx / (2 * kCopies), c = (idx >> 1) % kCopies, w = idx & 1;
-      const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
-      const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
-      *reinterpret_cast<uint32_t*>(lut_q + 256 * e + 8 * c + 4 * w) = s0 | (s1 << 16);
-    }
-  }
+  // ---- key and sketch tables (as in the decode kernel, no value table) ----
+  build_tables<BK, PROD, 0>(0.f, kcl, 0.f, ksig, tab, lut_k, lut_q, tid, nthr);
+  if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
+  lds_stores_done();
   Luts T;
   const uint32_t cp = lane & 31;
   T.k = KL::priv ? tab : lut_k;
@@ -2141,7 +2104,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   T.klane = KL::byte_indexed ? kTabK + 8u * (lane & 15) : KL::priv ? kTabK + 4u * cp : 0u;
   T.qlane = 8u * cp;
   T.vlane = 4u * cp;
-  __syncthreads();
+  tables_barrier();
 
   // ---- scan: scores of 32 vectors per block; candidates above the bar go to
   // the buffer of their query. Lanes n and n + 8 hold query n % 8 with equal
@@ -2152,21 +2115,28 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   float bar = -INFINITY;
   uint32_t cnt = 0;
   int cur = 0;
+  const uint32_t prog_own = lds_addr(&prog[wave]), prog_partner = lds_addr(&prog[wave ^ 4]);
   for (uint32_t i = 0; i < nblk; ++i) {
     const uint32_t t0 = t_begin + i * kBlockTok;
     Block<BK, PROD, 0> R;
     const uint32_t sb = ring_addr + cur * SL::bytes;
     // the blocks after this one already issued: their loads may stay in flight
     const uint32_t ahead = min(nblk - 1 - i, uint32_t(NST - 1));
-    uint32_t pw;   // unused: the search has no issue balance
+    // issue balance between the two wavefronts of a SIMD, as in attn_split_kernel
+    lds_put1(prog_own, i);
+    uint32_t pw;
     if (ahead == uint32_t(NST - 1))
-      read_block<BK, PROD, 0, (NST - 1) * SL::dma>(R, sb, so, sb, pw);
+      read_block<BK, PROD, 0, (NST - 1) * SL::dma>(R, sb, so, prog_partner, pw);
     else if (NST > 3 && ahead == 2)
-      read_block<BK, PROD, 0, (NST > 3 ? 2 : 0) * SL::dma>(R, sb, so, sb, pw);
+      read_block<BK, PROD, 0, (NST > 3 ? 2 : 0) * SL::dma>(R, sb, so, prog_partner, pw);
     else if (NST > 2 && ahead == 1)
-      read_block<BK, PROD, 0, (NST > 2 ? 1 : 0) * SL::dma>(R, sb, so, sb, pw);
+      read_block<BK, PROD, 0, (NST > 2 ? 1 : 0) * SL::dma>(R, sb, so, prog_partner, pw);
     else
-      read_block<BK, PROD, 0, 0>(R, sb, so, sb, pw);
+      read_block<BK, PROD, 0, 0>(R, sb, so, prog_partner, pw);
+    if (__builtin_amdgcn_readfirstlane(pw) < i)
+      __builtin_amdgcn_s_setprio(0);
+    else
+      __builtin_amdgcn_s_setprio(1);
     if (i + NST < nblk)
       stage_block<BK, PROD, 0, AL>(ring + cur * SL::bytes, t0 + NST * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
                                    a.kn, kg);
@@ -2219,6 +2189,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
     }
     cur = cur + 1 == NST ? 0 : cur + 1;
   }
+  __builtin_amdgcn_s_setprio(0);
   for (int q = 0; q < gc; ++q) {
     const uint32_t mq = __builtin_amdgcn_readlane(cnt, q);
     compact_cands(S, wave, q, k, lane, mq);
