@@ -1815,74 +1815,61 @@ struct MergeArgs {
 // (the Π_V column piece, then up to 16 splits' partials at a time).
 constexpr int kMergeChunk = 16;
 
-__global__ __launch_bounds__(512) void merge_kernel(MergeArgs a) {
-  __shared__ float acc[kMaxHeads][kD];
-  __shared__ float red[4][kMaxHeads][kD];
-  const int unit = blockIdx.x;
+__global__ __launch_bounds__(kD) void merge_kernel(MergeArgs a) {
+  // One workgroup per (unit, head); thread d owns output dim d. Every load
+  // (the column of Π_V, then the splits' partials) is issued before the
+  // first use, so the launch costs about one memory round trip.
+  __shared__ float accs[kD];
+  const int unit = blockIdx.x / kMaxHeads, head = blockIdx.x % kMaxHeads;
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
   const int b = unit / (a.ngroups * a.Hkv);
   const int gc = min(kMaxHeads, a.G - grp * kMaxHeads);
-  const int tid = threadIdx.x;
-  const int r = tid & (kD - 1), jq = tid >> 7;
-  float pv[kD / 4];
+  if (head >= gc) return;   // uniform over the workgroup
+  const int d = threadIdx.x;
+  float pv[kD];             // Π_V[k][d]: o_d = Σ_k Π_V[k][d]·acc_k
 #pragma unroll
-  for (int j = 0; j < kD / 4; ++j) pv[j] = a.rot_v[(jq * (kD / 4) + j) * kD + r];
-  const float* up = a.part + size_t(unit) * a.nsplit * kMaxHeads * kPartStride;
+  for (int k = 0; k < kD; ++k) pv[k] = a.rot_v[k * kD + d];
+  const float* ph = a.part + (size_t(unit) * a.nsplit * kMaxHeads + head) * kPartStride;
   const size_t sstride = size_t(kMaxHeads) * kPartStride;
   const float inv_cs = 1.0f / (kCentScale * a.vh->sigma);
-  for (int e = tid; e < kMaxHeads * kD; e += 512) {
-    const int head = e / kD, dim = e % kD;
-    float v = 0.f;
-    if (head < gc) {
-      const float* ph = up + head * kPartStride;
-      float M = -INFINITY, Ls = 0.f, A = 0.f;
-      for (int s0 = 0; s0 < a.nsplit; s0 += kMergeChunk) {
-        float ms[kMergeChunk], ls[kMergeChunk], as[kMergeChunk];
+  float M = -INFINITY, Ls = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += kMergeChunk) {
+    // unconditional loads (clamped to the last split), masked at use
+    float ms[kMergeChunk], ls[kMergeChunk], as[kMergeChunk];
 #pragma unroll
-        for (int i = 0; i < kMergeChunk; ++i) {
-          const bool ok = s0 + i < a.nsplit;
-          const float* q = ph + (ok ? s0 + i : 0) * sstride;
-          ms[i] = ok ? q[0] : -INFINITY;
-          ls[i] = ok ? q[1] : 0.f;
-          as[i] = ok ? q[4 + dim] : 0.f;
-        }
-        float mc = M;
-#pragma unroll
-        for (int i = 0; i < kMergeChunk; ++i) mc = fmaxf(mc, ms[i]);
-        if (mc > -INFINITY) {
-          const float fo = M > -INFINITY ? exp2f(M - mc) : 0.f;
-          Ls *= fo;
-          A *= fo;
-#pragma unroll
-          for (int i = 0; i < kMergeChunk; ++i) {
-            const float fw = exp2f(ms[i] - mc);
-            Ls = fmaf(fw, ls[i], Ls);
-            A = fmaf(fw, as[i], A);
-          }
-          M = mc;
-        }
-      }
-      v = Ls > 0.f ? A * inv_cs / Ls : 0.f;
+    for (int i = 0; i < kMergeChunk; ++i) {
+      const float* q = ph + size_t(min(s0 + i, a.nsplit - 1)) * sstride;
+      ms[i] = q[0];
+      ls[i] = q[1];
+      as[i] = q[4 + d];
     }
-    acc[head][dim] = v;
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+      if (s0 + i >= a.nsplit) ms[i] = -INFINITY;
+      mc = fmaxf(mc, ms[i]);
+    }
+    if (mc > -INFINITY) {
+      const float fo = M > -INFINITY ? exp2f(M - mc) : 0.f;
+      Ls *= fo;
+      A *= fo;
+#pragma unroll
+      for (int i = 0; i < kMergeChunk; ++i) {
+        const float fw = s0 + i < a.nsplit ? exp2f(ms[i] - mc) : 0.f;
+        Ls = fmaf(fw, ls[i], Ls);
+        A = fmaf(fw, as[i], A);
+      }
+      M = mc;
+    }
   }
+  accs[d] = Ls > 0.f ? A * inv_cs / Ls : 0.f;
   __syncthreads();
-  float o[kMaxHeads];
+  float o = 0.f;
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) o[h] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kD / 4; ++j)
-#pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h) o[h] = fmaf(pv[j], acc[h][jq * (kD / 4) + j], o[h]);
-#pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) red[jq][h][r] = o[h];
-  __syncthreads();
-  for (int e = tid; e < gc * kD; e += 512) {
-    const int head = e / kD, dim = e % kD;
-    const size_t hq = size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + head;
-    a.out[hq * kD + dim] = red[0][head][dim] + red[1][head][dim] + red[2][head][dim] + red[3][head][dim];
-  }
+  for (int k = 0; k < kD; ++k) o = fmaf(pv[k], accs[k], o);
+  const size_t hq = size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + head;
+  a.out[hq * kD + d] = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -2466,7 +2453,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   }
   if (phase == 0 || phase == 3) {
     MergeArgs ma{part, vq->rot, static_cast<const PrepHeader*>(vq->prep), out, Hq, Hkv, G, p.ngroups, p.nsplit};
-    hipLaunchKernelGGL(merge_kernel, dim3(p.units), dim3(512), 0, s, ma);
+    hipLaunchKernelGGL(merge_kernel, dim3(p.units * kMaxHeads), dim3(kD), 0, s, ma);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
   return TQ_OK;
