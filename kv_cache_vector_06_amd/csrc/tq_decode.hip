@@ -148,6 +148,9 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
   const bool live = c < gc;
   const bool prod = a.proj != nullptr;
   const u32x4* frag = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.kh) + kPrepHeaderBytes);
+  // the header's scales, read up front (not after the products)
+  const float rot_scale = scalar_load(&a.kh->rot_scale), sigma = scalar_load(&a.kh->sigma);
+  const float sp_scale = prod ? scalar_load(&a.kh->sp_scale) : 1.0f;
   u32x4 rh[4], rl[4], ph[4], pl[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -191,7 +194,7 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
   float qp[4], qs[4];                            // dims 32g + 4t + j
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    qp[j] = ldexpf(acc[j], ex) / a.kh->rot_scale;
+    qp[j] = ldexpf(acc[j], ex) / rot_scale;
     qs[j] = 0.f;
   }
   if (prod) {
@@ -227,12 +230,12 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
       z = mfma(pl[s], bh[s], z);
       z = mfma(ph[s], bl[s], z);
     }
-    const float inv = 1.0f / a.kh->sp_scale;
+    const float inv = 1.0f / sp_scale;
 #pragma unroll
     for (int j = 0; j < 4; ++j) qs[j] = ldexpf(z[j], e2) * inv;
   }
   // score = log2(e)·scale·n·(⟨Πq, c⟩ + √(π/2)/d·γ·⟨Sq, s⟩); centroids enter ×64σ.
-  const float fk = a.scale * kLog2e / (kCentScale * a.kh->sigma);
+  const float fk = a.scale * kLog2e / (kCentScale * sigma);
   const float fs = a.scale * kLog2e * 1.2533141373155003f / kD;       // √(π/2)/d
   float m = 0.f;
 #pragma unroll
@@ -966,13 +969,6 @@ __device__ __forceinline__ void tables_barrier() { asm volatile("s_barrier" ::: 
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// A load through the scalar unit (uniform address, read-only data): its wait
-// does not include the vector memory loads in flight.
-template <typename T>
-__device__ __forceinline__ T scalar_load(const T* p) {
-  return *(const __attribute__((address_space(4))) T*)p;
 }
 
 // Codebook of up to 16 entries into one VGPR: lane c (c = lane % 16 < K)

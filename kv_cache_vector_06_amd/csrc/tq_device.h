@@ -53,6 +53,13 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c) {
                                                 __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
+// A load through the scalar unit (uniform address, read-only data): its wait
+// does not include the vector memory loads in flight.
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ uint16_t f2h_bits(float x) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }

@@ -74,6 +74,18 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
     vec = row * a.max_ctx + (len - 1);
   }
 
+  // The header's rotation scale and the codebook, read up front through the
+  // scalar unit (uniform addresses), so that their latency overlaps the
+  // fragment loads instead of following the products.
+  const uint32_t K2 = a.bm > 0 ? (1u << a.bm) / 2 : 0u;
+  const float rot_scale =
+      scalar_load(&reinterpret_cast<const PrepHeader*>(reinterpret_cast<const uint8_t*>(a.frags) - kPrepHeaderBytes)->rot_scale);
+  float tb[8], cb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    tb[j] = (j >= 1 && uint32_t(j) < K2) ? scalar_load(a.boundaries + (K2 - 1 + j)) : 0.f;
+    cb[j] = uint32_t(j) < K2 ? scalar_load(a.centroids + (K2 + j)) : 0.f;
+  }
   // This wavefront's fragments: 16Π (hi, lo) and S' (hi, lo) of row tile t.
   u32x4 rh[4], rl[4], ph[4], pl[4];
 #pragma unroll
@@ -158,17 +170,14 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
 
   // Scaled codebook: T[j] = bits(S·t_j) for 1 <= j < K/2 (all ones above,
   // never below a magnitude), cs[m] = S·(centroid magnitude m).
-  const uint32_t K2 = a.bm > 0 ? (1u << a.bm) / 2 : 0u;
-  const float rot_scale =
-      reinterpret_cast<const PrepHeader*>(reinterpret_cast<const uint8_t*>(a.frags) - kPrepHeaderBytes)->rot_scale;
   const float S = (rs > 0.f) ? rot_scale * rs : 1.0f;
   const float up = 1.0f / S;
   uint32_t T[8];
   float cs[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    T[j] = (j >= 1 && uint32_t(j) < K2) ? __builtin_bit_cast(uint32_t, a.boundaries[K2 - 1 + j] * S) : 0xffffffffu;
-    cs[j] = uint32_t(j) < K2 ? a.centroids[K2 + j] * S : 0.f;
+    T[j] = (j >= 1 && uint32_t(j) < K2) ? __builtin_bit_cast(uint32_t, tb[j] * S) : 0xffffffffu;
+    cs[j] = uint32_t(j) < K2 ? cb[j] * S : 0.f;
   }
   // code = #{j >= 1 : T_j < |acc|} (|acc| + 1 ulp when acc <= 0: ties go to
   // the lower index), then m ^ K/2 or m ^ (K/2 - 1).
