@@ -94,4 +94,46 @@ __device__ __forceinline__ float max4g(float v) {
   return v;
 }
 
+// Scale of a row for its fp16 matrix-core operand. Each lane holds 32 of the
+// row's 128 values (xv; the row spans lane groups l, l^16, l^32, l^48) and ss
+// is the row's sum of squares. fp32 rows, and bf16 rows with ss outside
+// [1, 2^31), are scaled by 2^-ex with max|x| = m·2^ex, m in [0.5, 1): the
+// squares can then neither overflow nor vanish (xv and ss are replaced by the
+// scaled values). A bf16 row with ss in [1, 2^31) is used as it is (ex = 0):
+// every component is below 2^15.5, so its fp16 form is exact except where it
+// is an fp16 subnormal (below 2^-14), off by at most 2^-25, under 2^-25 of
+// the row's norm. Scaling by a power of two changes no code, norm or sketch
+// bit: the products, thresholds and residuals scale with it exactly.
+template <bool F32IN>
+__device__ __forceinline__ int row_exponent(float (&xv)[32], float& ss) {
+  int ex = 0;
+  if (F32IN || !(ss >= 1.0f && ss < 0x1p31f)) {
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(xv[q]));
+    amax = max4g(amax);
+    if (amax > 0.f) frexpf(amax, &ex);
+    ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      xv[q] = ldexpf(xv[q], -ex);    // a zero row stays ±0 (ex = 0)
+      ss = fmaf(xv[q], xv[q], ss);
+    }
+    ss = sum4g(ss);
+  }
+  return ex;
+}
+
+// Sum of squares of a bf16 row (0 for fp32 rows: row_exponent computes it).
+template <bool F32IN>
+__device__ __forceinline__ float row_ss(const float (&xv)[32]) {
+  float ss = 0.f;
+  if constexpr (!F32IN) {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) ss = fmaf(xv[q], xv[q], ss);
+    ss = sum4g(ss);
+  }
+  return ss;
+}
+
 }  // namespace tq

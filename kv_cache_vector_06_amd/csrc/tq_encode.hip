@@ -392,10 +392,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     int lofs = lane;
     asm volatile("" : "+v"(lofs));
 
-    // Columns held by this lane: slot 8s + j <-> column 32s + 8g + j.
-    // The vector is scaled by 2^-e with max|x| = m·2^e (m in [0.5, 1)): the
-    // squares can then neither overflow nor vanish, and every scaled component
-    // is below 1, so bf16 values convert to fp16 exactly.
+    // Columns held by this lane: slot 8s + j <-> column 32s + 8g + j. The
+    // row is used as it is or scaled by 2^-e (row_exponent).
     float xv[32];
     if constexpr (!F32IN) {
 #pragma unroll
@@ -418,19 +416,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
         }
       }
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(xv[q]));
-    amax = max4g(amax);
-    int ex = 0;
-    if (amax > 0.f) frexpf(amax, &ex);
-    float ss = 0.f;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      xv[q] = ldexpf(xv[q], -ex);    // a zero row stays ±0 (ex = 0)
-      ss = fmaf(xv[q], xv[q], ss);
-    }
-    ss = sum4g(ss);
+    float ss = row_ss<F32IN>(xv);
+    const int ex = row_exponent<F32IN>(xv, ss);
     const float rs = sqrtf(ss);                 // ‖x‖·2^-e
     const float nrm = ldexpf(rs, ex);
     u32x4 bx[4], bxl[4];
@@ -644,17 +631,12 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
         }
       }
     }
-    // scale by 2^-e (max|x| = m·2^e, m in [0.5, 1)) as in the unsplit encoder
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(xv[q]));
-    amax = max4g(amax);
-    int ex = 0;
-    if (amax > 0.f) frexpf(amax, &ex);
+    // the row as it is or scaled by 2^-e, as in the unsplit encoder
+    float ss = row_ss<F32IN>(xv);
+    const int ex = row_exponent<F32IN>(xv, ss);
     float sso = 0.f, ssr = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-      xv[q] = ldexpf(xv[q], -ex);
       const float v2 = xv[q] * xv[q];
       if ((omask >> q) & 1u)
         sso += v2;

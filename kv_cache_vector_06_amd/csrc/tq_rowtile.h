@@ -127,20 +127,16 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
       }
     }
   }
-  // Norm and the exact fp16 form of the row (scaled by 2^-e, max|x| = m·2^e).
-  float amax = 0.f;
-#pragma unroll
-  for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(xv[q]));
-  amax = max4g(amax);
-  int ex = 0;
-  if (amax > 0.f) frexpf(amax, &ex);
+  // Norm and the fp16 form of the row, as it is or scaled by 2^-e
+  // (row_exponent, the same choice as the full-size encoder's).
   float ss = 0.f;
-#pragma unroll
-  for (int q = 0; q < 32; ++q) {
-    xv[q] = ldexpf(xv[q], -ex);    // a zero row stays ±0 (ex = 0)
-    ss = fmaf(xv[q], xv[q], ss);
+  int ex = 0;
+  if (!a.f32in) {
+    ss = row_ss<false>(xv);
+    ex = row_exponent<false>(xv, ss);
+  } else {
+    ex = row_exponent<true>(xv, ss);
   }
-  ss = sum4g(ss);
   const float rs = sqrtf(ss);
   const float nrm = ldexpf(rs, ex);
   u32x4 bx[4], bxl[4];
