@@ -124,6 +124,13 @@ __device__ __forceinline__ int row_exponent(float (&xv)[32], float& ss) {
   return ex;
 }
 
+// fp16 pair of two values of a bf16 row (unscaled or scaled by a power of
+// two): the conversion is exact unless a value is an fp16 subnormal, so one
+// packed round-toward-zero conversion serves (the same in every encoder).
+__device__ __forceinline__ uint32_t bf16_row_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 // Sum of squares of a bf16 row (0 for fp32 rows: row_exponent computes it).
 template <bool F32IN>
 __device__ __forceinline__ float row_ss(const float (&xv)[32]) {

@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if constexpr (!F32IN) {
-          bx[s][k] = pack_h2(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+          bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
         } else {
           uint16_t h0, l0, h1, l1;
           split_h(xv[8 * s + 2 * k], h0, l0);
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if constexpr (!F32IN) {
-          bx[s][k] = pack_h2(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+          bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
         } else {
           uint16_t h0, l0, h1, l1;
           split_h(xv[8 * s + 2 * k], h0, l0);

@@ -145,7 +145,7 @@ __device__ __forceinline__ void row_encode(const RowEncArgs& a, int64_t tile, Ro
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (!a.f32in) {
-        bx[s][k] = pack_h2(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+        bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
         bxl[s][k] = 0u;
       } else {
         uint16_t h0, l0, h1, l1;

@@ -72,6 +72,13 @@ def test_decode_ragged_lengths(cfg_id):
     run_case(cfg, 2500, 4, lens=[2500, 1, 0, 777])
 
 
+def test_decode_many_splits():
+    # Batch 1, 40005 tokens: 8 units of 20 splits each, so the merge takes a
+    # full batch of 16 splits and a partial one, and the last block is ragged.
+    cfg = synth.CONFIGS[3]
+    run_case(cfg, 40005, 1, end_to_end=False)
+
+
 def test_decode_more_heads_than_a_group():
     # 16 query heads per KV head: two head groups share the KV head.
     base = synth.CONFIGS[5]
