@@ -1432,36 +1432,40 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
 constexpr int kKeyRegRow = 128, kKeyOutRow = 192;
 
 template <int BK, int S>
+// A operand of K-step S: the outlier pair (hi part) in dword 0 and the three
+// regular pairs in dwords 1..3; for 4-bit outlier codes `aol` holds the lo
+// part of the outlier pair in dword 0 (zeros elsewhere).
 __device__ __forceinline__ void okey_operands(const uint32_t (&kw)[4], const uint8_t* tab, const uint8_t* tab2,
-                                              uint32_t lane_hi, uint32_t lane8, u32x4& ao, u32x4& aol, u32x4& ar) {
+                                              uint32_t lane_hi, uint32_t lane8, u32x4& af, u32x4& aol) {
   constexpr int BKO = BK + 1, CH = 8 * BK + 2, base = S * CH;
   if constexpr (BKO == 4) {
     const u32x2 e = *reinterpret_cast<const u32x2*>(tab2 + (field_shl<base, 8, 7>(kw) + lane8));
-    ao = u32x4{e[0], 0u, 0u, 0u};
+    af[0] = e[0];
     aol = u32x4{e[1], 0u, 0u, 0u};
   } else {
-    ao = u32x4{*reinterpret_cast<const uint32_t*>(tab + kKeyOutRow * 256 + (field_shl<base, 2 * BKO, 8>(kw) + lane_hi)),
-               0u, 0u, 0u};
+    af[0] = *reinterpret_cast<const uint32_t*>(tab + kKeyOutRow * 256 + (field_shl<base, 2 * BKO, 8>(kw) + lane_hi));
   }
   const uint8_t* kb = tab + kKeyRegRow * 256;
-  ar[0] = 0u;
-  ar[1] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO, 2 * BK, 8>(kw) + lane_hi));
-  ar[2] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 2 * BK, 2 * BK, 8>(kw) + lane_hi));
-  ar[3] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 4 * BK, 2 * BK, 8>(kw) + lane_hi));
+  af[1] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO, 2 * BK, 8>(kw) + lane_hi));
+  af[2] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 2 * BK, 2 * BK, 8>(kw) + lane_hi));
+  af[3] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 4 * BK, 2 * BK, 8>(kw) + lane_hi));
 }
 
-// Scores of a split block (the score is sc·iqs).
+// Scores of a split block (the score is sc·iqs). The two products per K-step
+// take the whole A operand against the query split by position: `bqo` keeps
+// the outlier slots (dword 0 of each fragment) and `bqr` the regular ones,
+// so no A operand needs masking (zero slots contribute exact zeros).
 template <int BK>
 __device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* tab, const uint8_t* tab2,
-                                              uint32_t lane_hi, uint32_t lane8, const u32x4 (&bq)[4],
-                                              float (&sc)[8]) {
-  u32x4 ao[2][4], aol[2][4], ar[2][4];
+                                              uint32_t lane_hi, uint32_t lane8, const u32x4 (&bqo)[4],
+                                              const u32x4 (&bqr)[4], float (&sc)[8]) {
+  u32x4 af[2][4], aol[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    okey_operands<BK, 0>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][0], aol[t][0], ar[t][0]);
-    okey_operands<BK, 1>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][1], aol[t][1], ar[t][1]);
-    okey_operands<BK, 2>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][2], aol[t][2], ar[t][2]);
-    okey_operands<BK, 3>(R.kw[t], tab, tab2, lane_hi, lane8, ao[t][3], aol[t][3], ar[t][3]);
+    okey_operands<BK, 0>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][0], aol[t][0]);
+    okey_operands<BK, 1>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][1], aol[t][1]);
+    okey_operands<BK, 2>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][2], aol[t][2]);
+    okey_operands<BK, 3>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][3], aol[t][3]);
   }
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -1470,9 +1474,9 @@ __device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* ta
     f32x4 dmo = f32x4{0.f, 0.f, 0.f, 0.f}, dmr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int S = 0; S < 4; ++S) {
-      dmo = mfma(ao[t][S], bq[S], dmo);
-      if constexpr (BK + 1 == 4) dmo = mfma(aol[t][S], bq[S], dmo);
-      dmr = mfma(ar[t][S], bq[S], dmr);
+      dmo = mfma(af[t][S], bqo[S], dmo);
+      if constexpr (BK + 1 == 4) dmo = mfma(aol[t][S], bqo[S], dmo);
+      dmr = mfma(af[t][S], bqr[S], dmr);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1494,7 +1498,8 @@ __device__ __forceinline__ uint32_t onibbles(uint32_t w) {
 template <int BK, int BV>
 __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint32_t t_end, int n, int g,
                                               const uint8_t* tab, const uint8_t* tab2, uint32_t lane_lo,
-                                              uint32_t lane_hi, uint32_t lane8, const u32x4 (&bq)[4], float iqs,
+                                              uint32_t lane_hi, uint32_t lane8, const u32x4 (&bqo)[4],
+                                              const u32x4 (&bqr)[4], float iqs,
                                               uint32_t lomask, SoftmaxState& st, f32x4 (&acc)[8]) {
   uint32_t X[4], Y[4];
 #pragma unroll
@@ -1504,7 +1509,7 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
     Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
   }
   float sc[8];
-  oblock_scores<BK>(R, tab, tab2, lane_hi, lane8, bq, sc);
+  oblock_scores<BK>(R, tab, tab2, lane_hi, lane8, bqo, bqr, sc);
   Luts Tv;
   Tv.v = tab;
   Tv.vlane = lane_lo;
@@ -1732,9 +1737,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const float vsig = scalar_load(&a.vh->sigma), ksig = scalar_load(&a.kh->sigma);
   const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bq[4];
+  u32x4 bqo[4], bqr[4];   // the query fragments split by slot: outlier | regular
 #pragma unroll
-  for (int s = 0; s < 4; ++s) bq[s] = fr[s * 64 + lane];
+  for (int s = 0; s < 4; ++s) {
+    const u32x4 v = fr[s * 64 + lane];
+    bqo[s] = u32x4{v[0], 0u, 0u, 0u};
+    bqr[s] = u32x4{0u, v[1], v[2], v[3]};
+  }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   asm volatile("" ::: "memory");
   uint8_t* ring = &stage[wave][0];
@@ -1777,7 +1786,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
       const int nx = (cur + 2) % kStages;
       ostage_block<BK, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, vc, kn, vn);
     }
-    oattend_block<BK, BV>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bq, iqs, lomask, st, acc);
+    oattend_block<BK, BV>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bqo, bqr, iqs, lomask, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
   }
   __builtin_amdgcn_s_setprio(0);
