@@ -107,6 +107,11 @@ def cpu_baseline(cfg, units=6):
     }
 
 
+def _pct(sorted_vals, f: float) -> float:
+    """The f-quantile of an ascending list (nearest rank)."""
+    return sorted_vals[min(len(sorted_vals) - 1, max(0, round(f * (len(sorted_vals) - 1))))]
+
+
 def key_bytes(cfg) -> int:
     """Packed bytes of one key vector: codes + fp32 norm, plus the 16-byte
     sketch and fp32 γ for prod keys."""
@@ -222,6 +227,16 @@ def main():
     torch.cuda.synchronize()
     k_ms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(args.steps))
     k_avg = sum(k_ms) / len(k_ms)
+    # Spread of whole steps: one event after each step, in a third run (the
+    # events add their own small gaps, so the median sits a little above the
+    # event-free step time).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    step_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
     bpt = bytes_per_token(cfg)
     dec_bytes = n_vec * bpt
     value = dec_bytes / (ms_step * 1e-3) / 1e9
@@ -243,9 +258,38 @@ def main():
         b_.record()
         torch.cuda.synchronize()
         fl.append(a_.elapsed_time(b_))
-    del flush
     flushed_us = sorted(fl)[len(fl) // 2] * 1e3
     log(f"[bench] split-attention after a read-only cache flush: median {flushed_us:.1f} us")
+
+    # The part's practical read ceiling: one plain coalesced read
+    # (tq_read_probe, the decode stream's 16-byte non-temporal loads) of as
+    # many bytes as the packed cache, and of 4 GiB, back to back, each launch
+    # timed by events around it. A read carries a fixed cost of its own (the
+    # same-size read is the fair ceiling of one decode launch); the 4 GiB read
+    # gives the rate with that cost spread thin.
+    xo = torch.zeros(1, dtype=torch.int32, device=dev)
+    big = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+
+    def read_us(buf):
+        for _ in range(20):
+            TA.read_probe(buf, xo)
+        pr = []
+        for _ in range(30):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            TA.read_probe(buf, xo)
+            b_.record()
+            pr.append((a_, b_))
+        torch.cuda.synchronize()
+        return sorted(a_.elapsed_time(b_) for a_, b_ in pr)[len(pr) // 2] * 1e3
+
+    pr_us = read_us(flush.view(torch.uint8)[:dec_bytes])
+    read_peak = dec_bytes / (pr_us * 1e-6) / 1e9
+    pr4_us = read_us(big)
+    read_peak_4g = big.numel() * 4 / (pr4_us * 1e-6) / 1e9
+    del flush, xo, big
+    log(f"[bench] plain read of {dec_bytes} B: median {pr_us:.1f} us, {read_peak:.0f} GB/s; "
+        f"of 4 GiB: {pr4_us:.1f} us, {read_peak_4g:.0f} GB/s")
 
     # The same step with randomized Walsh-Hadamard rotations for keys and
     # values (the caches re-encoded with them).
@@ -451,7 +495,14 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": _traffic("attn_split_gqa8_prod4_128k.counters.json", "tq_decode.hip", dec_bytes),
                      "avg_launch_us": round(k_avg * 1e3, 2), "after_read_flush_us": round(flushed_us, 2),
+                     "launch_us_p10_p50_p90": [round(_pct(k_ms, f) * 1e3, 2) for f in (0.1, 0.5, 0.9)],
+                     "frac_of_measured_read": round(achieved / read_peak, 4),
                      "cache_copies": ncopy},
+        "step_us_p10_p50_p90": [round(_pct(step_us, f), 2) for f in (0.1, 0.5, 0.9)],
+        "measured_read_peak": {"gbs": round(read_peak, 1), "bytes": dec_bytes, "us": round(pr_us, 2),
+                               "gbs_4gib": round(read_peak_4g, 1),
+                               "kernel": "tq_read_probe: plain coalesced read, 16-byte non-temporal loads",
+                               "value_frac": round(value / read_peak, 4)},
         "cfg_llama8b_prod3_128k": {"workload": cfg3.name, "packed_cache_bytes": cfg3_bytes,
                                    "split_after_flush_us": round(cfg3_us, 2),
                                    "split_gbs": round(cfg3_bytes / cfg3_us / 1e3, 1),

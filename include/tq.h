@@ -333,6 +333,21 @@ size_t tq_search_workspace(int nq, int64_t n, int k);
 int tq_search(const tq_quantizer* q, const float* query, int nq, const tq_packed* db, int64_t n, int k,
               float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * tq_read_probe — a measurement aid, not a step of the codec: one plain
+ * coalesced read of `bytes` of device memory with the 16-byte non-temporal
+ * loads the decode kernels stream the packed cache with. Timed on a buffer
+ * far larger than the last-level cache, its rate is the part's practical
+ * read ceiling, beside which the decode rate is reported.
+ *   buf      device, 16-byte aligned, read only
+ *   bytes    > 0, a multiple of 16
+ *   xor_out  device uint32: the XOR of the buffer's little-endian 32-bit
+ *            words is XORed into it (set it to 0 first to read the XOR)
+ * One launch on `stream`. Errors: TQ_ERR_INVALID_ARG (null or misaligned
+ * pointers, bytes 0 or not a multiple of 16), TQ_ERR_HIP.
+ */
+int tq_read_probe(const void* buf, size_t bytes, uint32_t* xor_out, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* tq_status_string(int status);
 

@@ -31,7 +31,7 @@ TQ_HEAD_DIM = 128
 EXPORTED = ("tq_codebook", "tq_prep_bytes", "tq_prepare", "tq_encode",
             "tq_attn_decode_workspace", "tq_attn_decode", "tq_attn_decode_phase",
             "tq_decode_step", "tq_decode_step_phase", "tq_search_workspace", "tq_search",
-            "tq_status_string")
+            "tq_read_probe", "tq_status_string")
 
 
 class TQError(RuntimeError):
@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
     lib.tq_search_workspace.restype = SZ
     lib.tq_search.argtypes = [ctypes.POINTER(tq_quantizer), P, I, ctypes.POINTER(tq_packed), I64, I, P, P, P, SZ, P]
     lib.tq_search.restype = I
+    lib.tq_read_probe.argtypes = [P, SZ, P, P]
+    lib.tq_read_probe.restype = I
     lib.tq_status_string.argtypes = [I]
     lib.tq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -185,3 +187,7 @@ def tq_search(q: tq_quantizer, query: int, nq: int, db: tq_packed, n: int, k: in
               workspace: int, ws_bytes: int, stream: int | None) -> None:
     _check(load().tq_search(ctypes.byref(q), query, int(nq), ctypes.byref(db), int(n), int(k), scores, index,
                             workspace, int(ws_bytes), stream), "tq_search")
+
+
+def tq_read_probe(buf: int, nbytes: int, xor_out: int, stream: int | None) -> None:
+    _check(load().tq_read_probe(buf, int(nbytes), xor_out, stream), "tq_read_probe")

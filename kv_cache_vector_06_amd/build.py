@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip"]
+SOURCES = ["tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_probe.hip"]
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled on purpose for every device pass.
 # Matrix-core accumulators are kept in ordinary VGPRs (no AGPR copies around

@@ -200,3 +200,11 @@ def search(q: Quantizer, queries: torch.Tensor, db: Packed, k: int, n: int | Non
     L.tq_search(q.c, queries.data_ptr(), nq, db.c, n, k, scores.data_ptr(), index.data_ptr(),
                 workspace.data_ptr(), ws_bytes, _stream())
     return scores, index
+
+
+def read_probe(buf: torch.Tensor, xor_out: torch.Tensor) -> None:
+    """One plain read of the contiguous device tensor `buf` (tq_read_probe):
+    the XOR of its 32-bit words is XORed into the int32 tensor `xor_out`."""
+    if not buf.is_contiguous() or xor_out.dtype != torch.int32 or xor_out.numel() < 1:
+        raise ValueError("buf must be contiguous and xor_out an int32 tensor")
+    L.tq_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), xor_out.data_ptr(), _stream())

@@ -236,3 +236,14 @@ def test_split_argument_errors_are_synchronous():
                               byref(pk), 0.1, p, p, ws, None) == L.TQ_ERR_UNSUPPORTED
     sws = L.tq_search_workspace(10, 1000, 8)
     assert lib.tq_search(byref(sq), p, 10, byref(pk), 1000, 8, p, 1 << 21, 1 << 22, sws, None) == L.TQ_ERR_UNSUPPORTED
+
+
+def test_read_probe_argument_errors_are_synchronous():
+    lib = L.load()
+    p = 1 << 20
+    assert lib.tq_read_probe(None, 64, p, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_read_probe(p, 64, None, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_read_probe(p + 8, 64, p, None) == L.TQ_ERR_INVALID_ARG      # buffer must be 16-byte aligned
+    assert lib.tq_read_probe(p, 64, p + 2, None) == L.TQ_ERR_INVALID_ARG      # xor_out must be 4-byte aligned
+    assert lib.tq_read_probe(p, 0, p, None) == L.TQ_ERR_INVALID_ARG
+    assert lib.tq_read_probe(p, 72, p, None) == L.TQ_ERR_INVALID_ARG          # not a multiple of 16
