@@ -20,6 +20,8 @@
 // r̂ = y - c[idx] (S'·r̂ = S·r exactly), with three fp16-split passes.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tq.h"
 #include "tq_device.h"
 #include "tq_rowtile.h"
@@ -319,11 +321,65 @@ __device__ __forceinline__ float centroid_mag(const Book& bk, int m) {
   return c;
 }
 
+// Cell table of the nearest-centroid search (b_m >= 3). The code of y is
+// idx = #{i : t_i < y} over the K - 1 signed thresholds t (the magnitudes
+// tp[j] mirrored, t = 0 in the middle, as the search above reads them). On
+// the accumulator acc = S·y (S > 0) the search compares acc with fl(t_i·S),
+// exactly as the threshold search does. The cell of acc is the byte that
+// f = acc·(128/S) + 128 converts to with saturation: whether the conversion
+// floors or rounds, f lies in [k - 1/2, k + 1) for cell k, i.e. y in
+// [(k - 128.5)/128, (k - 127)/128] up to rounding; cell 0 reaches down and
+// cell 255 up without bound. Each cell is widened by 1/64 of its width on
+// both sides and stores below = #{t_i below it} and the one threshold inside
+// it (+inf if none), so idx = below + [acc > fl(t_inside·S)]. A codebook with
+// two thresholds in one widened cell (spacing under ≈1.52/128) cannot use the
+// table; the builder reports it and the encoder keeps the threshold search.
+// PROD entries add the signed centroids of codes below and below + 1.
+template <bool PROD>
+using CellEntry = std::conditional_t<PROD, u32x4, u32x2>;
+
+template <int BM, bool PROD>
+__device__ __forceinline__ int build_cell(const Book& bk, int k, CellEntry<PROD>* cells) {
+  constexpr int K = 1 << BM, H = K / 2;
+  const float tp[8] = {0.f, bk.t1, bk.t2, bk.t3, bk.t4, bk.t5, bk.t6, bk.t7};
+  const float cm[8] = {bk.c0, bk.c1, bk.c2, bk.c3, bk.c4, bk.c5, bk.c6, bk.c7};
+  const float lo = k == 0 ? -INFINITY : (float(k) - 128.5f - 1.0f / 64) * (1.0f / 128);
+  const float hi = k == 255 ? INFINITY : (float(k) - 127.0f + 1.0f / 64) * (1.0f / 128);
+  int below = 0, inside = 0;
+  float cand = INFINITY;
+#pragma unroll
+  for (int i = 0; i < K - 1; ++i) {
+    const float t = i < H - 1 ? -tp[H - 1 - i] : tp[i - (H - 1)];
+    if (t < lo) {
+      ++below;
+    } else if (t <= hi) {
+      if (inside == 0) cand = t;
+      ++inside;
+    }
+  }
+  if constexpr (!PROD) {
+    cells[k] = u32x2{uint32_t(below), __builtin_bit_cast(uint32_t, cand)};
+  } else {
+    float c0 = 0.f, c1 = 0.f;   // signed centroid of codes below and below + 1
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const float v = c >= H ? cm[c - H] : -cm[H - 1 - c];
+      c0 = c == below ? v : c0;
+      c1 = c == below + 1 ? v : c1;
+    }
+    cells[k] = u32x4{uint32_t(below), __builtin_bit_cast(uint32_t, cand), __builtin_bit_cast(uint32_t, c0),
+                     __builtin_bit_cast(uint32_t, c1)};
+  }
+  return inside > 1;
+}
+
 template <int BM, bool PROD, bool F32IN>
 __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   __shared__ u32x4 lds_rot[kFragsPerSet * 64];
   __shared__ u32x4 lds_proj[PROD ? kFragsPerSet * 64 : 1];
   constexpr int K = 1 << BM;
+  constexpr bool kCells = BM >= 3;
+  __shared__ CellEntry<PROD> lds_cells[kCells ? 256 : 1];
   const u32x4* frot = lds_rot;
   const u32x4* fproj = lds_proj;
 
@@ -344,7 +400,13 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       bk.c4 = cb[4]; bk.c5 = cb[5]; bk.c6 = cb[6]; bk.c7 = cb[7];
     }
   }
+  int bad_cell = 0;
+  if constexpr (kCells) {
+    if (threadIdx.x < 256) bad_cell = build_cell<BM, PROD>(bk, threadIdx.x, lds_cells);
+  }
+  // A full barrier (with its memory fence) publishes the table; then the vote.
   __syncthreads();
+  const bool use_cells = kCells && !__syncthreads_or(bad_cell);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -369,192 +431,222 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       }
     }
   };
-  // (bf16 input only; fp32 input, twice the registers, loads its tile in place.)
-  u32x4 raw_next[kRaw];
-  int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave;
-  if (!F32IN && tile < ntiles) load_raw(tile, raw_next);
-  for (; tile < ntiles; tile += tstride) {
-    u32x4 raw[kRaw];
-    if constexpr (F32IN) {
-      load_raw(tile, raw);
-    } else {
+  // The tile loop, with the cell table (USE) or the threshold search.
+  auto tiles = [&](auto use_tag) {
+    constexpr bool USE = decltype(use_tag)::value;
+    // (bf16 input only; fp32 input, twice the registers, loads its tile in place.)
+    u32x4 raw_next[kRaw];
+    int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave;
+    if (!F32IN && tile < ntiles) load_raw(tile, raw_next);
+    for (; tile < ntiles; tile += tstride) {
+      u32x4 raw[kRaw];
+      if constexpr (F32IN) {
+        load_raw(tile, raw);
+      } else {
 #pragma unroll
-      for (int k = 0; k < kRaw; ++k) raw[k] = raw_next[k];
-      if (tile + tstride < ntiles) load_raw(tile + tstride, raw_next);
-    }
-    const int64_t rowi = tile * 16 + n;
-    const bool valid = rowi < a.n;
-    const int64_t row = valid ? rowi : a.n - 1;
-    const int64_t vec = a.slot ? a.slot[row] : row;   // output slot
-    // The operand fragments in LDS are the same every tile; an opaque lane
-    // offset keeps the compiler from hoisting all 64 KiB of them into
-    // registers ahead of the loop.
-    int lofs = lane;
-    asm volatile("" : "+v"(lofs));
+        for (int k = 0; k < kRaw; ++k) raw[k] = raw_next[k];
+        if (tile + tstride < ntiles) load_raw(tile + tstride, raw_next);
+      }
+      const int64_t rowi = tile * 16 + n;
+      const bool valid = rowi < a.n;
+      const int64_t row = valid ? rowi : a.n - 1;
+      const int64_t vec = a.slot ? a.slot[row] : row;   // output slot
+      // The operand fragments in LDS are the same every tile; an opaque lane
+      // offset keeps the compiler from hoisting all 64 KiB of them into
+      // registers ahead of the loop.
+      int lofs = lane;
+      asm volatile("" : "+v"(lofs));
 
-    // Columns held by this lane: slot 8s + j <-> column 32s + 8g + j. The
-    // row is used as it is or scaled by 2^-e (row_exponent).
-    float xv[32];
-    if constexpr (!F32IN) {
+      // Columns held by this lane: slot 8s + j <-> column 32s + 8g + j. The
+      // row is used as it is or scaled by 2^-e (row_exponent).
+      float xv[32];
+      if constexpr (!F32IN) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          xv[8 * s + 2 * k] = bf16_to_f32(raw[s][k] & 0xffffu);
-          xv[8 * s + 2 * k + 1] = bf16_to_f32(raw[s][k] >> 16);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f32x4 w0 = __builtin_bit_cast(f32x4, raw[2 * s]);
-        const f32x4 w1 = __builtin_bit_cast(f32x4, raw[2 * s + 1]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          xv[8 * s + k] = w0[k];
-          xv[8 * s + 4 + k] = w1[k];
-        }
-      }
-    }
-    float ss = row_ss<F32IN>(xv);
-    const int ex = row_exponent<F32IN>(xv, ss);
-    const float rs = sqrtf(ss);                 // ‖x‖·2^-e
-    const float nrm = ldexpf(rs, ex);
-    u32x4 bx[4], bxl[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (!F32IN) {
-          bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
-        } else {
-          uint16_t h0, l0, h1, l1;
-          split_h(xv[8 * s + 2 * k], h0, l0);
-          split_h(xv[8 * s + 2 * k + 1], h1, l1);
-          bx[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
-          bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
-        }
-      }
-
-    f32x4 acc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const u32x4 ah = frot[frag_index(0, t, s) * 64 + lofs];
-        const u32x4 al = frot[frag_index(1, t, s) * 64 + lofs];
-        acc[t] = mfma(ah, bx[s], acc[t]);
-        acc[t] = mfma(al, bx[s], acc[t]);
-        if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
-      }
-    }
-
-    // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j, and
-    // acc = S·y with S = 16‖x‖·2^-e (any S > 0 for a zero vector, whose acc is 0).
-    const float S = (rs > 0.f) ? rot_scale * rs : 1.0f;
-    const float up = 1.0f / S;
-    ScaledBook sb;
-    {
-      const float tb[8] = {0.f, bk.t1, bk.t2, bk.t3, bk.t4, bk.t5, bk.t6, bk.t7};
-      const float cb[8] = {bk.c0, bk.c1, bk.c2, bk.c3, bk.c4, bk.c5, bk.c6, bk.c7};
-#pragma unroll
-      for (int j = 1; j < K / 2; ++j) sb.t[j] = __builtin_bit_cast(uint32_t, tb[j] * S);
-      if constexpr (PROD) {
-#pragma unroll
-        for (int j = 0; j < (K / 2 > 0 ? K / 2 : 1); ++j) sb.c[j] = cb[j] * S;
-      }
-    }
-    uint32_t w[BM > 0 ? BM : 1];
-#pragma unroll
-    for (int k = 0; k < (BM > 0 ? BM : 1); ++k) w[k] = 0u;
-    u32x4 brh[4], brl[4];
-    float r2 = 0.f;
-    const float rsc = up * kResScale;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float res[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t m;
-        bool pos;
-        const uint32_t code = quantize_scaled<BM>(acc[t][j], sb, m, pos);
-        if constexpr (BM > 0) {
-          const int q = 4 * t + j;
-          const int bit = q * BM, wi = bit >> 5, off = bit & 31;
-          w[wi] |= code << off;
-          if (off + BM > 32) w[wi + 1] |= code >> (32 - off);
-        }
-        if constexpr (PROD) {
-          float c = 0.f;
-          if constexpr (BM >= 1) {
-            c = scaled_mag<BM>(sb, m);
-            c = pos ? c : -c;
+          for (int k = 0; k < 4; ++k) {
+            xv[8 * s + 2 * k] = bf16_to_f32(raw[s][k] & 0xffffu);
+            xv[8 * s + 2 * k + 1] = bf16_to_f32(raw[s][k] >> 16);
           }
-          const float racc = acc[t][j] - c;      // S·(y - c)
-          r2 = fmaf(racc, racc, r2);
-          res[j] = racc * rsc;                   // 64·(y - c)
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 w0 = __builtin_bit_cast(f32x4, raw[2 * s]);
+          const f32x4 w1 = __builtin_bit_cast(f32x4, raw[2 * s + 1]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            xv[8 * s + k] = w0[k];
+            xv[8 * s + 4 + k] = w1[k];
+          }
         }
       }
-      if constexpr (PROD) {
-        // q = 4t + j  ->  K-step s = t/2, dword 2(t%2) + j/2, half j%2.
-        uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
-        split_h(res[0], h0, l0);
-        split_h(res[1], h1, l1);
-        split_h(res[2], h2, l2);
-        split_h(res[3], h3, l3);
-        const int s = t >> 1, k0 = 2 * (t & 1);
-        brh[s][k0] = uint32_t(h0) | (uint32_t(h1) << 16);
-        brh[s][k0 + 1] = uint32_t(h2) | (uint32_t(h3) << 16);
-        brl[s][k0] = uint32_t(l0) | (uint32_t(l1) << 16);
-        brl[s][k0 + 1] = uint32_t(l2) | (uint32_t(l3) << 16);
-      }
-    }
-
-    if constexpr (BM > 0) {
-      if (valid) {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + vec * (16 * BM) + 4 * BM * g);
-        if constexpr (BM == 4) {
-          *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-        } else if constexpr (BM == 2) {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-        } else {
+      float ss = row_ss<F32IN>(xv);
+      const int ex = row_exponent<F32IN>(xv, ss);
+      const float rs = sqrtf(ss);                 // ‖x‖·2^-e
+      const float nrm = ldexpf(rs, ex);
+      u32x4 bx[4], bxl[4];
 #pragma unroll
-          for (int k = 0; k < BM; ++k) dst[k] = w[k];
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (!F32IN) {
+            bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+          } else {
+            uint16_t h0, l0, h1, l1;
+            split_h(xv[8 * s + 2 * k], h0, l0);
+            split_h(xv[8 * s + 2 * k + 1], h1, l1);
+            bx[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
+            bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
+          }
         }
-      }
-    }
-    if (valid && g == 0) a.norms[vec] = nrm;
 
-    if constexpr (PROD) {
-      r2 = sum4g(r2);
-      f32x4 z[8];
+      f32x4 acc[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) z[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const u32x4 sh = fproj[frag_index(0, t, s) * 64 + lofs];
-          const u32x4 sl = fproj[frag_index(1, t, s) * 64 + lofs];
-          z[t] = mfma(sh, brh[s], z[t]);
-          z[t] = mfma(sl, brh[s], z[t]);
-          z[t] = mfma(sh, brl[s], z[t]);
+          const u32x4 ah = frot[frag_index(0, t, s) * 64 + lofs];
+          const u32x4 al = frot[frag_index(1, t, s) * 64 + lofs];
+          acc[t] = mfma(ah, bx[s], acc[t]);
+          acc[t] = mfma(al, bx[s], acc[t]);
+          if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
         }
       }
-      uint32_t bits = 0u;
+
+      // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j, and
+      // acc = S·y with S = 16‖x‖·2^-e (any S > 0 for a zero vector, whose acc is 0).
+      const float S = (rs > 0.f) ? rot_scale * rs : 1.0f;
+      const float up = 1.0f / S;
+      const float inv128 = 128.0f * up;
+      ScaledBook sb;
+      if constexpr (!USE) {
+        const float tb[8] = {0.f, bk.t1, bk.t2, bk.t3, bk.t4, bk.t5, bk.t6, bk.t7};
+        const float cb[8] = {bk.c0, bk.c1, bk.c2, bk.c3, bk.c4, bk.c5, bk.c6, bk.c7};
+#pragma unroll
+        for (int j = 1; j < K / 2; ++j) sb.t[j] = __builtin_bit_cast(uint32_t, tb[j] * S);
+        if constexpr (PROD) {
+#pragma unroll
+          for (int j = 0; j < (K / 2 > 0 ? K / 2 : 1); ++j) sb.c[j] = cb[j] * S;
+        }
+      }
+      uint32_t w[BM > 0 ? BM : 1];
+#pragma unroll
+      for (int k = 0; k < (BM > 0 ? BM : 1); ++k) w[k] = 0u;
+      u32x4 brh[4], brl[4];
+      float r2 = 0.f;
+      const float rsc = up * kResScale;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
+        float res[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bits |= uint32_t(z[t][j] >= 0.f) << (4 * t + j);
+        for (int j = 0; j < 4; ++j) {
+          uint32_t m = 0u, code;
+          bool pos = false;
+          float cell_c = 0.f;      // USE: the signed centroid of the code
+          if constexpr (USE) {
+            // (Entry words are read as floats through __uint_as_float:
+            // `__builtin_bit_cast` of a vector element in place compiled to a
+            // read of element 0.)
+            const float f = fmaf(acc[t][j], inv128, 128.0f);
+            const uint32_t k = __builtin_amdgcn_cvt_pk_u8_f32(f, 0, 0u);
+            if constexpr (PROD) {
+              const u32x4 e = lds_cells[k];
+              const bool up1 = acc[t][j] > __uint_as_float(e[1]) * S;
+              code = e[0] + (up1 ? 1u : 0u);
+              cell_c = __uint_as_float(up1 ? e[3] : e[2]);
+            } else {
+              const u32x2 e = lds_cells[k];
+              code = e[0] + (acc[t][j] > __uint_as_float(e[1]) * S ? 1u : 0u);
+            }
+          } else {
+            code = quantize_scaled<BM>(acc[t][j], sb, m, pos);
+          }
+          if constexpr (BM > 0) {
+            const int q = 4 * t + j;
+            const int bit = q * BM, wi = bit >> 5, off = bit & 31;
+            w[wi] |= code << off;
+            if (off + BM > 32) w[wi + 1] |= code >> (32 - off);
+          }
+          if constexpr (PROD) {
+            float c = 0.f;
+            if constexpr (USE) {
+              c = cell_c * S;                      // = ±fl(|c|·S), as below
+              asm volatile("" : "+v"(c));          // rounded product: no fused multiply-add
+            } else if constexpr (BM >= 1) {
+              c = scaled_mag<BM>(sb, m);
+              c = pos ? c : -c;
+            }
+            const float racc = acc[t][j] - c;      // S·(y - c)
+            r2 = fmaf(racc, racc, r2);
+            res[j] = racc * rsc;                   // 64·(y - c)
+          }
+        }
+        if constexpr (PROD) {
+          // q = 4t + j  ->  K-step s = t/2, dword 2(t%2) + j/2, half j%2.
+          uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
+          split_h(res[0], h0, l0);
+          split_h(res[1], h1, l1);
+          split_h(res[2], h2, l2);
+          split_h(res[3], h3, l3);
+          const int s = t >> 1, k0 = 2 * (t & 1);
+          brh[s][k0] = uint32_t(h0) | (uint32_t(h1) << 16);
+          brh[s][k0 + 1] = uint32_t(h2) | (uint32_t(h3) << 16);
+          brl[s][k0] = uint32_t(l0) | (uint32_t(l1) << 16);
+          brl[s][k0 + 1] = uint32_t(l2) | (uint32_t(l3) << 16);
+        }
       }
-      if (valid) {
-        *reinterpret_cast<uint32_t*>(a.qjl + vec * 16 + 4 * g) = bits;
-        if (g == 0) a.gammas[vec] = sqrtf(r2) * up;
+
+      if constexpr (BM > 0) {
+        if (valid) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + vec * (16 * BM) + 4 * BM * g);
+          if constexpr (BM == 4) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+          } else if constexpr (BM == 2) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+          } else {
+#pragma unroll
+            for (int k = 0; k < BM; ++k) dst[k] = w[k];
+          }
+        }
+      }
+      if (valid && g == 0) a.norms[vec] = nrm;
+
+      if constexpr (PROD) {
+        r2 = sum4g(r2);
+        f32x4 z[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) z[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const u32x4 sh = fproj[frag_index(0, t, s) * 64 + lofs];
+            const u32x4 sl = fproj[frag_index(1, t, s) * 64 + lofs];
+            z[t] = mfma(sh, brh[s], z[t]);
+            z[t] = mfma(sl, brh[s], z[t]);
+            z[t] = mfma(sh, brl[s], z[t]);
+          }
+        }
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bits |= uint32_t(z[t][j] >= 0.f) << (4 * t + j);
+        }
+        if (valid) {
+          *reinterpret_cast<uint32_t*>(a.qjl + vec * 16 + 4 * g) = bits;
+          if (g == 0) a.gammas[vec] = sqrtf(r2) * up;
+        }
       }
     }
-  }
+  };
+  if (use_cells)
+    tiles(std::integral_constant<bool, kCells>{});
+  else
+    tiles(std::integral_constant<bool, false>{});
 }
 
 // Encodes of at most this many 16-row tiles take the row-tile-parallel form:
@@ -595,129 +687,162 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
   uint32_t omask = 0u;
 #pragma unroll
   for (int s = 0; s < 4; ++s) omask |= ((hdr->omask[s] >> (8 * g)) & 0xffu) << (8 * s);
+  // Cell tables of both groups' searches (as in encode_kernel; the regular
+  // group's only at 3 bits): threads 0-255 build the outlier group's, 256-511
+  // the regular group's.
+  constexpr bool kCellsR = BM >= 3;
+  __shared__ u32x2 cells_o[256];
+  __shared__ u32x2 cells_r[kCellsR ? 256 : 1];
+  int bad_cell = 0;
+  if (threadIdx.x < 256)
+    bad_cell = build_cell<BO, false>(bo, threadIdx.x, cells_o);
+  else if (kCellsR)
+    bad_cell = build_cell<(kCellsR ? BM : 3), false>(br, threadIdx.x - 256, cells_r);
   __syncthreads();
+  const bool use_cells = !__syncthreads_or(bad_cell);
 
   const int64_t ntiles = (a.n + 15) / 16;
   const int64_t tstride = int64_t(gridDim.x) * kEncWaves;
-  for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles; tile += tstride) {
-    const int64_t rowi = tile * 16 + n;
-    const bool valid = rowi < a.n;
-    const int64_t row = valid ? rowi : a.n - 1;
-    const int64_t vec = a.slot ? a.slot[row] : row;
-    int lofs = lane;
-    asm volatile("" : "+v"(lofs));
-    float xv[32];
-    if constexpr (!F32IN) {
-      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.stride + 8 * g;
+  // The tile loop, with the cell tables (USE) or the threshold searches.
+  auto tiles = [&](auto use_tag) {
+    constexpr bool USE = decltype(use_tag)::value;
+    for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles; tile += tstride) {
+      const int64_t rowi = tile * 16 + n;
+      const bool valid = rowi < a.n;
+      const int64_t row = valid ? rowi : a.n - 1;
+      const int64_t vec = a.slot ? a.slot[row] : row;
+      int lofs = lane;
+      asm volatile("" : "+v"(lofs));
+      float xv[32];
+      if constexpr (!F32IN) {
+        const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.stride + 8 * g;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 r = *reinterpret_cast<const u32x4*>(xr + 32 * s);
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 r = *reinterpret_cast<const u32x4*>(xr + 32 * s);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            xv[8 * s + 2 * k] = bf16_to_f32(r[k] & 0xffffu);
+            xv[8 * s + 2 * k + 1] = bf16_to_f32(r[k] >> 16);
+          }
+        }
+      } else {
+        const float* xr = static_cast<const float*>(a.x) + row * a.stride + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(xr + 32 * s);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(xr + 32 * s + 4);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            xv[8 * s + k] = w0[k];
+            xv[8 * s + 4 + k] = w1[k];
+          }
+        }
+      }
+      // the row as it is or scaled by 2^-e, as in the unsplit encoder
+      float ss = row_ss<F32IN>(xv);
+      const int ex = row_exponent<F32IN>(xv, ss);
+      float sso = 0.f, ssr = 0.f;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const float v2 = xv[q] * xv[q];
+        if ((omask >> q) & 1u)
+          sso += v2;
+        else
+          ssr += v2;
+      }
+      sso = sum4g(sso);
+      ssr = sum4g(ssr);
+      const float rso = sqrtf(sso), rsr = sqrtf(ssr);
+      u32x4 bx[4], bxl[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          xv[8 * s + 2 * k] = bf16_to_f32(r[k] & 0xffffu);
-          xv[8 * s + 2 * k + 1] = bf16_to_f32(r[k] >> 16);
+          if constexpr (!F32IN) {
+            bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
+          } else {
+            uint16_t h0, l0, h1, l1;
+            split_h(xv[8 * s + 2 * k], h0, l0);
+            split_h(xv[8 * s + 2 * k + 1], h1, l1);
+            bx[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
+            bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
+          }
         }
-      }
-    } else {
-      const float* xr = static_cast<const float*>(a.x) + row * a.stride + 8 * g;
+      f32x4 acc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(xr + 32 * s);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(xr + 32 * s + 4);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          xv[8 * s + k] = w0[k];
-          xv[8 * s + 4 + k] = w1[k];
+        for (int t = 0; t < 8; ++t) {
+          const u32x4 ah = lds_rot[frag_index(0, t, s) * 64 + lofs];
+          const u32x4 al = lds_rot[frag_index(1, t, s) * 64 + lofs];
+          acc[t] = mfma(ah, bx[s], acc[t]);
+          acc[t] = mfma(al, bx[s], acc[t]);
+          if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
         }
       }
-    }
-    // the row as it is or scaled by 2^-e, as in the unsplit encoder
-    float ss = row_ss<F32IN>(xv);
-    const int ex = row_exponent<F32IN>(xv, ss);
-    float sso = 0.f, ssr = 0.f;
+      // acc = rot_scale·Π·x·2^-e; a group's rotated unit vector is its rows
+      // over rot_scale·‖x_g‖·2^-e, so the thresholds scale by that
+      const float So = rso > 0.f ? rot_scale * rso : 1.0f;
+      const float Sr = rsr > 0.f ? rot_scale * rsr : 1.0f;
+      ScaledBook sbo, sbr;
+      const float inv_o = 128.0f / So, inv_r = 128.0f / Sr;
+      // Scaled thresholds of the groups that search without a cell table.
+      if constexpr (!USE) {
+        const float to[8] = {0.f, bo.t1, bo.t2, bo.t3, bo.t4, bo.t5, bo.t6, bo.t7};
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const float v2 = xv[q] * xv[q];
-      if ((omask >> q) & 1u)
-        sso += v2;
-      else
-        ssr += v2;
-    }
-    sso = sum4g(sso);
-    ssr = sum4g(ssr);
-    const float rso = sqrtf(sso), rsr = sqrtf(ssr);
-    u32x4 bx[4], bxl[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (!F32IN) {
-          bx[s][k] = bf16_row_pair(xv[8 * s + 2 * k], xv[8 * s + 2 * k + 1]);
-        } else {
-          uint16_t h0, l0, h1, l1;
-          split_h(xv[8 * s + 2 * k], h0, l0);
-          split_h(xv[8 * s + 2 * k + 1], h1, l1);
-          bx[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
-          bxl[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
-        }
+        for (int j = 1; j < (1 << BO) / 2; ++j) sbo.t[j] = __builtin_bit_cast(uint32_t, to[j] * So);
       }
-    f32x4 acc[8];
+      if constexpr (!USE || !kCellsR) {
+        const float tr[8] = {0.f, br.t1, br.t2, br.t3, br.t4, br.t5, br.t6, br.t7};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 1; j < (1 << BM) / 2; ++j) sbr.t[j] = __builtin_bit_cast(uint32_t, tr[j] * Sr);
+      }
+      uint32_t w[NW];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int k = 0; k < NW; ++k) w[k] = 0u;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x4 ah = lds_rot[frag_index(0, t, s) * 64 + lofs];
-        const u32x4 al = lds_rot[frag_index(1, t, s) * 64 + lofs];
-        acc[t] = mfma(ah, bx[s], acc[t]);
-        acc[t] = mfma(al, bx[s], acc[t]);
-        if constexpr (F32IN) acc[t] = mfma(ah, bxl[s], acc[t]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = 4 * t + j, c = q >> 3, r = q & 7;
+          const bool out = r < 2;
+          uint32_t m;
+          bool pos;
+          uint32_t code;
+          if (USE && (out || kCellsR)) {
+            // cell of acc in the group's table: idx = below + [acc > fl(t·S)]
+            const float Sg = out ? So : Sr;
+            const float f = fmaf(acc[t][j], out ? inv_o : inv_r, 128.0f);
+            const uint32_t k = __builtin_amdgcn_cvt_pk_u8_f32(f, 0, 0u);
+            const u32x2 e = out ? cells_o[k] : cells_r[kCellsR ? k : 0];
+            code = e[0] + (acc[t][j] > __uint_as_float(e[1]) * Sg ? 1u : 0u);
+          } else {
+            code = out ? quantize_scaled<BO>(acc[t][j], sbo, m, pos) : quantize_scaled<BM>(acc[t][j], sbr, m, pos);
+          }
+          const int width = out ? BO : BM;
+          const int bit = c * (8 * BM + 2) + (out ? r * BO : 2 * BO + (r - 2) * BM);
+          const int wi = bit >> 5, off = bit & 31;
+          w[wi] |= code << off;
+          if (off + width > 32) w[wi + 1] |= code >> (32 - off);
+        }
+      }
+      if (valid) {
+        uint8_t* dst = a.codes + vec * ROW + g * (SEG / 8);
+#pragma unroll
+        for (int k = 0; k < SEG / 8; ++k) dst[k] = static_cast<uint8_t>(w[k >> 2] >> (8 * (k & 3)));
+        if (g == 0) {
+          a.norms[2 * vec] = ldexpf(rso, ex);
+          a.norms[2 * vec + 1] = ldexpf(rsr, ex);
+        }
       }
     }
-    // acc = rot_scale·Π·x·2^-e; a group's rotated unit vector is its rows
-    // over rot_scale·‖x_g‖·2^-e, so the thresholds scale by that
-    const float So = rso > 0.f ? rot_scale * rso : 1.0f;
-    const float Sr = rsr > 0.f ? rot_scale * rsr : 1.0f;
-    ScaledBook sbo, sbr;
-    {
-      const float to[8] = {0.f, bo.t1, bo.t2, bo.t3, bo.t4, bo.t5, bo.t6, bo.t7};
-      const float tr[8] = {0.f, br.t1, br.t2, br.t3, br.t4, br.t5, br.t6, br.t7};
-#pragma unroll
-      for (int j = 1; j < (1 << BO) / 2; ++j) sbo.t[j] = __builtin_bit_cast(uint32_t, to[j] * So);
-#pragma unroll
-      for (int j = 1; j < (1 << BM) / 2; ++j) sbr.t[j] = __builtin_bit_cast(uint32_t, tr[j] * Sr);
-    }
-    uint32_t w[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) w[k] = 0u;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = 4 * t + j, c = q >> 3, r = q & 7;
-        const bool out = r < 2;
-        uint32_t m;
-        bool pos;
-        const uint32_t code = out ? quantize_scaled<BO>(acc[t][j], sbo, m, pos)
-                                  : quantize_scaled<BM>(acc[t][j], sbr, m, pos);
-        const int width = out ? BO : BM;
-        const int bit = c * (8 * BM + 2) + (out ? r * BO : 2 * BO + (r - 2) * BM);
-        const int wi = bit >> 5, off = bit & 31;
-        w[wi] |= code << off;
-        if (off + width > 32) w[wi + 1] |= code >> (32 - off);
-      }
-    }
-    if (valid) {
-      uint8_t* dst = a.codes + vec * ROW + g * (SEG / 8);
-#pragma unroll
-      for (int k = 0; k < SEG / 8; ++k) dst[k] = static_cast<uint8_t>(w[k >> 2] >> (8 * (k & 3)));
-      if (g == 0) {
-        a.norms[2 * vec] = ldexpf(rso, ex);
-        a.norms[2 * vec + 1] = ldexpf(rsr, ex);
-      }
-    }
-  }
+  };
+  if (use_cells)
+    tiles(std::integral_constant<bool, true>{});
+  else
+    tiles(std::integral_constant<bool, false>{});
 }
 
 template <int BM, bool PROD>

@@ -4,8 +4,10 @@ import pytest
 import torch
 
 import synth
+from kv_cache_vector_06_amd import _lib as L
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import DEV, check_encode, gpu_packed_arrays, oracle_encode, say, to_gpu_x
+from gpu_util import DEV, book, check_encode, gpu_packed_arrays, oracle_encode, say, to_gpu_x
+from oracle import encode_mse, encode_prod, unpack_codes, unpack_signs
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +105,42 @@ def test_encode_full_size_sampled(consts):
         say("full encode", bits, variant)
         check_encode({k: v[rows] for k, v in g.items()}, oracle_encode(X[rows], Rk, S, bits, variant),
                      bits, variant)
+
+
+@pytest.mark.parametrize("variant", ["mse", "prod"])
+def test_encode_close_thresholds(consts, variant):
+    """A codebook with two thresholds closer together than the encoder's cell
+    table can separate (under 1.52/128 apart) makes the encoder keep its
+    threshold search; the codes still follow idx = #{t_i < y} for that
+    codebook, and the prod residual uses its centroids."""
+    Rk, _, S = consts
+    bits = 4
+    bm = bits - 1 if variant == "prod" else bits
+    c = book(bm)[0].astype(np.float32).astype(np.float64)
+    h = len(c) // 2
+    c[h + 1], c[h + 2] = c[h] + 0.002, c[h] + 0.004      # squeezed, still ascending
+    c[h - 2], c[h - 3] = -c[h + 1], -c[h + 2]            # and antisymmetric
+    t = (c[:-1] + c[1:]) / 2
+    assert np.min(np.diff(t)) < 1.52 / 128
+    q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV)
+    q.centroids.copy_(torch.from_numpy(c.astype(np.float32)))
+    q.boundaries[:len(t)].copy_(torch.from_numpy(t.astype(np.float32)))
+    L.tq_prepare(q.c, None)
+    n = 4096 + 37
+    X = synth.outlier_kv(1, 1, n, 128, seed=120 + bm, dtype="bf16")[0, 0]
+    say("encode close thresholds", variant, n)
+    g = gpu_packed_arrays(T.encode(q, to_gpu_x(X, "bf16")), q)
+    X64 = X.astype(np.float64)
+    ref = encode_prod(X64, Rk, S, c, bits) if variant == "prod" else encode_mse(X64, Rk, c, bits)
+    gidx = unpack_codes(g["codes"], 128, bm)
+    mism = gidx != ref["idx"]
+    dist = np.min(np.abs(ref["y"][..., None] - t), axis=-1)
+    assert np.all(dist[mism] < 1e-6), "code mismatch away from a boundary"
+    assert mism.sum() <= 1e-5 * mism.size
+    assert np.any(gidx == h + 1)                          # the squeezed cell is used
+    np.testing.assert_allclose(g["norms"], ref["norms"], rtol=1e-6)
+    if variant == "prod":
+        ok = ~mism.any(axis=1)
+        bad = (unpack_signs(g["qjl"], 128) != unpack_signs(ref["qjl"], 128)) & ok[:, None]
+        assert np.all(np.abs(ref["z"][bad]) < 1e-6), "sketch bit flipped away from zero"
+        np.testing.assert_allclose(g["gammas"][ok], ref["gammas"][ok], rtol=1e-5, atol=1e-6)
