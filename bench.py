@@ -337,11 +337,25 @@ def main():
         b_.record()
         torch.cuda.synchronize()
         fl3.append(a_.elapsed_time(b_))
-    del flush, kc3, vc3
     cfg3_us = sorted(fl3)[len(fl3) // 2] * 1e3
     cfg3_bytes = n3 * bytes_per_token(cfg3)
+    # Its ceiling: a plain read (tq_read_probe) of as many bytes, also after
+    # a 1 GiB read, so that none of them is in the last-level cache.
+    rb = torch.ones(cfg3_bytes // 4, dtype=torch.float32, device=dev)
+    xo3 = torch.zeros(1, dtype=torch.int32, device=dev)
+    rd3 = []
+    for i in range(7):
+        flush.sum()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        TA.read_probe(rb, xo3)
+        b_.record()
+        torch.cuda.synchronize()
+        rd3.append(a_.elapsed_time(b_))
+    del flush, kc3, vc3, rb, xo3
+    cfg3_read_us = sorted(rd3)[len(rd3) // 2] * 1e3
     log(f"[bench] {cfg3.name}: split attention after a cache flush {cfg3_us:.1f} us, "
-        f"{cfg3_bytes / cfg3_us / 1e3:.0f} GB/s")
+        f"{cfg3_bytes / cfg3_us / 1e3:.0f} GB/s; plain read of as many bytes {cfg3_read_us:.1f} us")
 
     # Inner-product search: the first 2^20 key rows as a prod-4 database
     # (index build = their encode), 64 N(0,1) queries, top 10 each; recall 1@10
@@ -506,7 +520,9 @@ def main():
         "cfg_llama8b_prod3_128k": {"workload": cfg3.name, "packed_cache_bytes": cfg3_bytes,
                                    "split_after_flush_us": round(cfg3_us, 2),
                                    "split_gbs": round(cfg3_bytes / cfg3_us / 1e3, 1),
-                                   "frac": round(cfg3_bytes / cfg3_us / 1e3 / PEAK_HBM_GBS, 4)},
+                                   "frac": round(cfg3_bytes / cfg3_us / 1e3 / PEAK_HBM_GBS, 4),
+                                   "same_size_read_us": round(cfg3_read_us, 2),
+                                   "frac_of_measured_read": round(cfg3_read_us / cfg3_us, 4)},
         "hadamard_step_ms": round(had_ms, 5),
         "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
         "search": search,
