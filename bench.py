@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0      # dense fp16 matrix cores
 WORKLOAD = 5
 
 
@@ -60,6 +61,22 @@ def _traffic(kernel_file: str, src: str, launches_bytes: float):
     if rec.get("source_sha") != _src_hash(src):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _mfma_busy(kernel_row: str):
+    """Matrix-core busy fraction of a kernel from the committed rocprofv3 SQ
+    counter summary, or None when absent or taken on another encoder source."""
+    path = os.path.join(ROOT, "profiles", "sq_counters_gqa8_prod4_128k.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        lines = f.read().splitlines()
+    if not any(l.startswith("# src sha256") and f"tq_encode.hip {_src_hash('tq_encode.hip')}" in l for l in lines):
+        return None
+    for l in lines:
+        if l.startswith(kernel_row):
+            return float(l[len(kernel_row):].split()[5])
+    return None
 
 
 def cpu_baseline(cfg, units=6):
@@ -454,6 +471,7 @@ def main():
 
     enc = {}
     enc_roof = None
+    enc_mfma = {}
     if not args.no_encode_sweep:
         n_sweep = (1 << 20) * 8
         xs = torch.cat([kg, vg])[:n_sweep]
@@ -479,6 +497,22 @@ def main():
                             "achieved": round(eb / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                             "traffic": _traffic("encode_mse4_sweep.counters.json", "tq_encode.hip", eb)}
+            if label in ("mse4", "prod4"):
+                # Matrix-core use: the algorithmic flops (2d² per vector for the
+                # rotation, 2d² more for the prod sketch) and the flops the
+                # fp16 matrix cores execute with the operands split into hi/lo
+                # parts (rotation 2 passes, sketch 3), against the dense fp16
+                # peak; plus the busy fraction the SQ counters measured.
+                alg = 2 * d * d * (2 if var == "prod" else 1)
+                exe = 2 * d * d * (5 if var == "prod" else 2)
+                rate = n_sweep / (ms * 1e-3)
+                enc_mfma[label] = {"flops_per_vec": alg, "executed_flops_per_vec": exe,
+                                   "tflops": round(rate * alg / 1e12, 1),
+                                   "executed_tflops": round(rate * exe / 1e12, 1), "peak_tflops": PEAK_F16_TFLOPS,
+                                   "frac": round(rate * alg / 1e12 / PEAK_F16_TFLOPS, 4),
+                                   "executed_frac": round(rate * exe / 1e12 / PEAK_F16_TFLOPS, 4),
+                                   "busy_counter": _mfma_busy(f"tq::encode_kernel<{bits - (var == 'prod')}, "
+                                                              f"{'true' if var == 'prod' else 'false'}, false>")}
             del pk, qq
             log(f"[bench] encode {label}: {enc[label]} Mvec/s")
 
@@ -529,6 +563,7 @@ def main():
         "outlier_split": split_res,
         "encode_mvec_s": enc,
         "encode_roofline": enc_roof,
+        "encode_mfma": enc_mfma or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
