@@ -205,6 +205,8 @@ int tq_prepare(const tq_quantizer* q, void* stream);
  *             `out` (NULL: at slot i). This appends new tokens into a cache
  *             laid out as in tq_attn_decode. Slots must be >= 0, inside the
  *             caller's buffers and distinct; they are not checked.
+ * Rows must hold finite values: the outputs of a row with a NaN or an
+ * infinity are unspecified (and may differ between calls of different n).
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP.
  */
 int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int64_t n,
@@ -277,7 +279,7 @@ int tq_attn_decode_phase(int phase, const tq_quantizer* kq, const tq_quantizer* 
  *                 [1, max_ctx] gets no write.
  *   other arguments as tq_attn_decode (same workspace size).
  * The result equals tq_encode of the new rows into those slots followed by
- * tq_attn_decode, bit for bit; the appends and the query operands share one
+ * tq_attn_decode, bit for bit, for rows of finite values; the appends and the query operands share one
  * launch, so the step takes three launches instead of five.
  * Errors: as tq_attn_decode and tq_encode (TQ_ERR_INVALID_ARG for null or
  * misaligned rows or a bad stride, TQ_ERR_UNSUPPORTED for another dtype).
