@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0      # dense fp16 matrix cores
-WORKLOAD = 5
+WORKLOAD = "gqa8_prod4_128k_b4"
 
 
 def _src_hash(name: str) -> str:
@@ -168,7 +168,7 @@ def main():
     from kv_cache_vector_06_amd import torch_api as TA
 
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
-    cfg = synth.CONFIGS[WORKLOAD]
+    cfg = synth.WORKLOADS[WORKLOAD]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     B, Hkv, Hq, T, d = cfg.B, cfg.Hkv, cfg.Hq, cfg.T, cfg.d
@@ -331,17 +331,17 @@ def main():
     # split launch is timed alone, after a 1 GiB read).
     del kcs, vcs
     torch.cuda.empty_cache()
-    cfg3 = synth.CONFIGS[3]
-    kq3 = TA.Quantizer(Rk, cfg3.k_bits, cfg3.k_variant, S, dev)
-    vq3 = TA.Quantizer(Rv, cfg3.v_bits, "mse", None, dev)
-    K3, V3 = synth.make_kv(cfg3)
-    n3 = cfg3.B * cfg3.Hkv * cfg3.T
+    cfg_b1 = synth.WORKLOADS["llama8b_prod3_128k"]
+    kq3 = TA.Quantizer(Rk, cfg_b1.k_bits, cfg_b1.k_variant, S, dev)
+    vq3 = TA.Quantizer(Rv, cfg_b1.v_bits, "mse", None, dev)
+    K3, V3 = synth.make_kv(cfg_b1)
+    n3 = cfg_b1.B * cfg_b1.Hkv * cfg_b1.T
     kc3, vc3 = TA.Packed(kq3, n3, dev), TA.Packed(vq3, n3, dev)
     TA.encode(kq3, torch.from_numpy(K3.reshape(-1, d)).to(torch.bfloat16).to(dev), kc3)
     TA.encode(vq3, torch.from_numpy(V3.reshape(-1, d)).to(torch.bfloat16).to(dev), vc3)
     del K3, V3
-    q3 = torch.from_numpy(synth.make_query(cfg3)).to(dev)
-    dec3 = TA.Decoder(cfg3.B, cfg3.Hq, cfg3.Hkv, cfg3.T, dev)
+    q3 = torch.from_numpy(synth.make_query(cfg_b1)).to(dev)
+    dec3 = TA.Decoder(cfg_b1.B, cfg_b1.Hq, cfg_b1.Hkv, cfg_b1.T, dev)
     out3 = torch.empty_like(q3)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     fl3 = []
@@ -354,11 +354,11 @@ def main():
         b_.record()
         torch.cuda.synchronize()
         fl3.append(a_.elapsed_time(b_))
-    cfg3_us = sorted(fl3)[len(fl3) // 2] * 1e3
-    cfg3_bytes = n3 * bytes_per_token(cfg3)
+    cfg_b1_us = sorted(fl3)[len(fl3) // 2] * 1e3
+    cfg_b1_bytes = n3 * bytes_per_token(cfg_b1)
     # Its ceiling: a plain read (tq_read_probe) of as many bytes, also after
     # a 1 GiB read, so that none of them is in the last-level cache.
-    rb = torch.ones(cfg3_bytes // 4, dtype=torch.float32, device=dev)
+    rb = torch.ones(cfg_b1_bytes // 4, dtype=torch.float32, device=dev)
     xo3 = torch.zeros(1, dtype=torch.int32, device=dev)
     rd3 = []
     for i in range(7):
@@ -370,9 +370,9 @@ def main():
         torch.cuda.synchronize()
         rd3.append(a_.elapsed_time(b_))
     del flush, kc3, vc3, rb, xo3
-    cfg3_read_us = sorted(rd3)[len(rd3) // 2] * 1e3
-    log(f"[bench] {cfg3.name}: split attention after a cache flush {cfg3_us:.1f} us, "
-        f"{cfg3_bytes / cfg3_us / 1e3:.0f} GB/s; plain read of as many bytes {cfg3_read_us:.1f} us")
+    cfg_b1_read_us = sorted(rd3)[len(rd3) // 2] * 1e3
+    log(f"[bench] {cfg_b1.name}: split attention after a cache flush {cfg_b1_us:.1f} us, "
+        f"{cfg_b1_bytes / cfg_b1_us / 1e3:.0f} GB/s; plain read of as many bytes {cfg_b1_read_us:.1f} us")
 
     # Inner-product search: the first 2^20 key rows as a prod-4 database
     # (index build = their encode), 64 N(0,1) queries, top 10 each; recall 1@10
@@ -417,16 +417,16 @@ def main():
     if not args.no_split:
         del db
         torch.cuda.empty_cache()
-        for cid in (6, 7):
-            c6 = synth.CONFIGS[cid]
+        for sname in ("gqa8_split25_128k_b4", "gqa8_split35_128k_b4"):
+            cs = synth.WORKLOADS[sname]
             sc = synth.split_constants(d)
-            kq6 = TA.Quantizer(None, c6.k_bits, "mse", None, dev, split=(sc["rk_o"], sc["rk_r"], sc["ch_k"]))
-            vq6 = TA.Quantizer(None, c6.v_bits, "mse", None, dev, split=(sc["rv_o"], sc["rv_r"], sc["ch_v"]))
-            K6, V6 = synth.make_kv(c6)
+            kq6 = TA.Quantizer(None, cs.k_bits, "mse", None, dev, split=(sc["rk_o"], sc["rk_r"], sc["ch_k"]))
+            vq6 = TA.Quantizer(None, cs.v_bits, "mse", None, dev, split=(sc["rv_o"], sc["rv_r"], sc["ch_v"]))
+            K6, V6 = synth.make_kv(cs)
             k6 = torch.from_numpy(K6.reshape(-1, d)).to(torch.bfloat16).to(dev)
             v6 = torch.from_numpy(V6.reshape(-1, d)).to(torch.bfloat16).to(dev)
             del K6, V6
-            n6 = c6.B * c6.Hkv * c6.T
+            n6 = cs.B * cs.Hkv * cs.T
             kc6 = [TA.Packed(kq6, n6, dev) for _ in range(ncopy)]
             vc6 = [TA.Packed(vq6, n6, dev) for _ in range(ncopy)]
             for c in range(ncopy):
@@ -438,7 +438,7 @@ def main():
             torch.cuda.synchronize()
             enc6_ms = a_.elapsed_time(b_)
             del k6, v6
-            dec6 = TA.Decoder(c6.B, c6.Hq, c6.Hkv, c6.T, dev)
+            dec6 = TA.Decoder(cs.B, cs.Hq, cs.Hkv, cs.T, dev)
             for i in range(args.warmup):
                 dec6(kq6, vq6, q, kc6[i % ncopy], vc6[i % ncopy], out=out)
             torch.cuda.synchronize()
@@ -461,13 +461,13 @@ def main():
             torch.cuda.empty_cache()
             us6 = sorted(fl6)[len(fl6) // 2] * 1e3
             by6 = n6 * (kq6.code_bytes + 8 + vq6.code_bytes + 8)
-            split_res[c6.name] = {
+            split_res[cs.name] = {
                 "bytes_per_token_head": kq6.code_bytes + 8 + vq6.code_bytes + 8, "packed_cache_bytes": by6,
                 "decode_ms": round(ms6, 5), "decode_gbs": round(by6 / (ms6 * 1e-3) / 1e9, 1),
                 "split_after_flush_us": round(us6, 2), "split_gbs": round(by6 / us6 / 1e3, 1),
                 "frac": round(by6 / us6 / 1e3 / PEAK_HBM_GBS, 4),
                 "encode_mvec_s": round(n6 / (enc6_ms * 1e-3) / 1e6, 1)}
-            log(f"[bench] {c6.name}: {split_res[c6.name]}")
+            log(f"[bench] {cs.name}: {split_res[cs.name]}")
 
     enc = {}
     enc_roof = None
@@ -551,12 +551,12 @@ def main():
                                "gbs_4gib": round(read_peak_4g, 1),
                                "kernel": "tq_read_probe: plain coalesced read, 16-byte non-temporal loads",
                                "value_frac": round(value / read_peak, 4)},
-        "cfg_llama8b_prod3_128k": {"workload": cfg3.name, "packed_cache_bytes": cfg3_bytes,
-                                   "split_after_flush_us": round(cfg3_us, 2),
-                                   "split_gbs": round(cfg3_bytes / cfg3_us / 1e3, 1),
-                                   "frac": round(cfg3_bytes / cfg3_us / 1e3 / PEAK_HBM_GBS, 4),
-                                   "same_size_read_us": round(cfg3_read_us, 2),
-                                   "frac_of_measured_read": round(cfg3_read_us / cfg3_us, 4)},
+        "cfg_llama8b_prod3_128k": {"workload": cfg_b1.name, "packed_cache_bytes": cfg_b1_bytes,
+                                   "split_after_flush_us": round(cfg_b1_us, 2),
+                                   "split_gbs": round(cfg_b1_bytes / cfg_b1_us / 1e3, 1),
+                                   "frac": round(cfg_b1_bytes / cfg_b1_us / 1e3 / PEAK_HBM_GBS, 4),
+                                   "same_size_read_us": round(cfg_b1_read_us, 2),
+                                   "frac_of_measured_read": round(cfg_b1_read_us / cfg_b1_us, 4)},
         "hadamard_step_ms": round(had_ms, 5),
         "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
         "search": search,

@@ -167,18 +167,21 @@ class DecodeConfig:
         return self.Hq // self.Hkv
 
 
-# The five workloads. "K" is 1024 tokens.
-CONFIGS = {
-    1: DecodeConfig("mse3_d128_4096_fp32", 1, 1, 1, 4096, 128, "mse", 3, 3, "gaussian", "fp32", 10),
-    2: DecodeConfig("llama8b_b4_32k", 1, 8, 32, 32768, 128, "mse", 4, 4, "outlier", "bf16", 20),
-    3: DecodeConfig("llama8b_prod3_128k", 1, 8, 32, 131072, 128, "prod", 3, 3, "outlier", "bf16", 30),
-    4: DecodeConfig("batch64_b2_16k", 64, 8, 32, 16384, 128, "mse", 2, 2, "lognormal", "bf16", 40),
-    5: DecodeConfig("gqa8_prod4_128k_b4", 4, 8, 64, 131072, 128, "prod", 4, 4, "gaussian", "bf16", 50),
+# The workloads, by name. "K" is 1024 tokens.
+_ALL = (
+    DecodeConfig("mse3_d128_4096_fp32", 1, 1, 1, 4096, 128, "mse", 3, 3, "gaussian", "fp32", 10),
+    DecodeConfig("llama8b_b4_32k", 1, 8, 32, 32768, 128, "mse", 4, 4, "outlier", "bf16", 20),
+    DecodeConfig("llama8b_prod3_128k", 1, 8, 32, 131072, 128, "prod", 3, 3, "outlier", "bf16", 30),
+    DecodeConfig("batch64_b2_16k", 64, 8, 32, 16384, 128, "mse", 2, 2, "lognormal", "bf16", 40),
+    DecodeConfig("gqa8_prod4_128k_b4", 4, 8, 64, 131072, 128, "prod", 4, 4, "gaussian", "bf16", 50),
     # outlier-channel split ("2.5-bit": 32 channels at 3 bits + 96 at 2;
     # "3.5-bit": 4 + 3), mse keys and values, the benchmark's shape
-    6: DecodeConfig("gqa8_split25_128k_b4", 4, 8, 64, 131072, 128, "mse", 2, 2, "split", "bf16", 60, True),
-    7: DecodeConfig("gqa8_split35_128k_b4", 4, 8, 64, 131072, 128, "mse", 3, 3, "split", "bf16", 70, True),
-}
+    DecodeConfig("gqa8_split25_128k_b4", 4, 8, 64, 131072, 128, "mse", 2, 2, "split", "bf16", 60, True),
+    DecodeConfig("gqa8_split35_128k_b4", 4, 8, 64, 131072, 128, "mse", 3, 3, "split", "bf16", 70, True),
+)
+WORKLOADS = {c.name: c for c in _ALL}
+# The five unsplit decode workloads, smallest first.
+DECODE_WORKLOADS = [c.name for c in _ALL if not c.split]
 
 
 def make_kv(cfg: DecodeConfig, T: int | None = None, B: int | None = None):

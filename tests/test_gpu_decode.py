@@ -59,29 +59,29 @@ def run_case(cfg, T_ctx, B, lens=None, end_to_end=True, rotation="dense"):
     return r.max()
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
-def test_decode_configs_small(cfg_id):
-    cfg = synth.CONFIGS[cfg_id]
+@pytest.mark.parametrize("name", synth.DECODE_WORKLOADS)
+def test_decode_configs_small(name):
+    cfg = synth.WORKLOADS[name]
     B = min(cfg.B, 2)
     run_case(cfg, 1000 + 7, B)                       # several 32-token blocks, ragged tail
 
 
-@pytest.mark.parametrize("cfg_id", [3, 5])
-def test_decode_ragged_lengths(cfg_id):
-    cfg = synth.CONFIGS[cfg_id]
+@pytest.mark.parametrize("name", ["llama8b_prod3_128k", "gqa8_prod4_128k_b4"])
+def test_decode_ragged_lengths(name):
+    cfg = synth.WORKLOADS[name]
     run_case(cfg, 2500, 4, lens=[2500, 1, 0, 777])
 
 
 def test_decode_many_splits():
     # Batch 1, 40005 tokens: 8 units of 20 splits each, so the merge takes a
     # full batch of 16 splits and a partial one, and the last block is ragged.
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS["llama8b_prod3_128k"]
     run_case(cfg, 40005, 1, end_to_end=False)
 
 
 def test_decode_more_heads_than_a_group():
     # 16 query heads per KV head: two head groups share the KV head.
-    base = synth.CONFIGS[5]
+    base = synth.WORKLOADS["gqa8_prod4_128k_b4"]
     cfg = synth.DecodeConfig("gqa16", 1, 2, 32, 600, 128, "prod", 3, 2, "gaussian", "bf16", 70)
     run_case(cfg, 600, 1)
 
@@ -93,18 +93,18 @@ def test_decode_odd_group_and_mse1():
     run_case(cfg, 300, 1)
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3, 5])
-def test_decode_hadamard_rotation(cfg_id):
+@pytest.mark.parametrize("name", ["llama8b_b4_32k", "llama8b_prod3_128k", "gqa8_prod4_128k_b4"])
+def test_decode_hadamard_rotation(name):
     # Randomized Walsh-Hadamard rotations for keys and values (exact ±1
     # matrix-core operands, 1/√d in fp32), same parity rules.
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = synth.WORKLOADS[name]
     run_case(cfg, 1000 + 7, min(cfg.B, 2), rotation="hadamard")
 
 
 def test_decode_full_size_sampled():
     # 128K context at the benchmark's shape (prod-3 keys, mse-3 values, GQA 4),
     # GPU encode + decode; the oracle evaluates two KV heads' query heads.
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS["llama8b_prod3_128k"]
     kq, vq, Rk, Rv, S = quantizers(cfg)
     say("generating", cfg.name)
     K, V = synth.make_kv(cfg)
@@ -176,10 +176,10 @@ def test_decode_step_full_size_benchmark_shape_sampled():
     # The benchmark's launch configuration: tq_decode_step at batch 4 x 8 KV
     # heads x 131072 tokens, 64 query heads (prod-4 keys, mse-4 values); the
     # oracle evaluates two (batch, KV head) units.
-    _full_size_units(synth.CONFIGS[5], [(0, 0), (3, 6)], 500, use_step=True)
+    _full_size_units(synth.WORKLOADS["gqa8_prod4_128k_b4"], [(0, 0), (3, 6)], 500, use_step=True)
 
 
 def test_decode_full_size_batched_sampled():
     # 64 sequences x 16384 tokens, 8 KV heads, 32 query heads, mse-2 keys and
     # values, log-normal per-token norms; two units sampled.
-    _full_size_units(synth.CONFIGS[4], [(0, 3), (63, 7)], 600, use_step=False)
+    _full_size_units(synth.WORKLOADS["batch64_b2_16k"], [(0, 3), (63, 7)], 600, use_step=False)

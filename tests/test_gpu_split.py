@@ -118,12 +118,12 @@ def test_split_encode_then_decode(bk, bv):
     assert rel.max() <= 1e-3, rel.max()
 
 
-@pytest.mark.parametrize("cfg_id", [6, 7])
-def test_split_full_size_benchmark_shape_sampled(cfg_id):
+@pytest.mark.parametrize("name", ["gqa8_split25_128k_b4", "gqa8_split35_128k_b4"])
+def test_split_full_size_benchmark_shape_sampled(name):
     # The split workloads' launch configuration: batch 4 x 8 KV heads x 131072
     # tokens, 64 query heads, split keys and values; GPU encode + decode, the
     # oracle evaluates two (batch, KV head) units.
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = synth.WORKLOADS[name]
     kq, kcst = split_quantizer(cfg.k_bits, "k")
     vq, vcst = split_quantizer(cfg.v_bits, "v")
     say("generating", cfg.name)

@@ -113,16 +113,16 @@ def _step_case(cfg, T_ctx, B, lens, dtype, seed):
     return out_b
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("name", synth.DECODE_WORKLOADS)
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_step_equals_append_then_decode(cfg_id, dtype):
-    cfg = synth.CONFIGS[cfg_id]
+def test_step_equals_append_then_decode(name, dtype):
+    cfg = synth.WORKLOADS[name]
     B = min(cfg.B, 3)
-    _step_case(cfg, 777, B, None, dtype, 40 + cfg_id)
+    _step_case(cfg, 777, B, None, dtype, 40 + cfg.seed_base // 10)
 
 
 def test_step_ragged_empty_and_out_of_range_lengths():
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS["gqa8_prod4_128k_b4"]
     out = _step_case(cfg, 600, 5, [600, 1, 0, 333, 601], "bf16", 60)
     assert torch.all(out[2] == 0)
     cfg = synth.DecodeConfig("prod1_g3", 3, 2, 6, 300, 128, "prod", 1, 2, "lognormal", "fp32", 61)
@@ -133,7 +133,7 @@ def test_step_ragged_empty_and_out_of_range_lengths():
 
 def test_step_full_size():
     # The benchmark shape: 4 x 8 KV heads x 131072 tokens, 64 query heads.
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS["gqa8_prod4_128k_b4"]
     kq, vq, Rk, Rv, S = quantizers(cfg)
     B, Tc = cfg.B, cfg.T
     say("full-size step: random packed caches")
@@ -176,7 +176,7 @@ def test_step_matches_oracle():
     # The oracle encodes every token (the last one of each row being the step's
     # new token) and evaluates attention; the GPU holds the oracle's cache for
     # the earlier tokens and appends the last one itself.
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS["llama8b_prod3_128k"]
     B, Tc = 2, 900
     lens = [Tc, 500]
     kq, vq, Rk, Rv, S = quantizers(cfg)
