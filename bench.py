@@ -1,28 +1,34 @@
 #!/usr/bin/env python3
 """TurboQuant hot-path benchmark on one MI355X.
 
-Workload: batch 4 x 8 KV heads x 131072 tokens, 64 query heads (GQA 8),
-d = 128; keys TurboQuant-prod at 4 bits (3-bit Lloyd-Max + 1-bit QJL sketch),
-values TurboQuant-mse at 4 bits; bf16 N(0,1) synthetic K/V (seeded). Plus the
-prefill-scale encode sweep over 2^20 tokens x 8 heads.
+Headline workload (gqa8_prod4_128k_b4): batch 4 x 8 KV heads x 131072
+tokens, 64 query heads (GQA 8), d = 128; keys TurboQuant-prod at 4 bits
+(3-bit Lloyd-Max + 1-bit QJL sketch), values TurboQuant-mse at 4 bits; bf16
+N(0,1) synthetic K/V (seeded).
 
 One step = one pass of the whole hot path on resident inputs: encode the new
 token's key and value of every (batch, KV head), append them to the packed
 cache, then decode attention of every query head over the 131072-token packed
 cache (tq_decode_step: the appends and the query operands in one launch, then
-the split attention and the merge). Steps rotate over three
-copies of the packed cache, so no step finds its cache in the 256 MB
-last-level cache.
+the split attention and the merge). Steps rotate over three copies of the
+packed cache, so no step finds its cache in the 256 MB last-level cache.
 
-Prints one JSON line. `value` is packed-cache bytes read by decode per step /
-step time (GB/s), timed without any event between the steps. `roofline` is
-for the dominant kernel (the split-attention launch), timed with HIP events
-around that launch on its stream in a second run of the same steps.
-`hadamard_step_ms` / `hadamard_value` time the same step with randomized
-Walsh-Hadamard rotations for keys and values; the encode sweep adds mse-4 and
-prod-4 with that rotation. `search` times inner-product top-10 of 64 queries
-over 2^20 prod-4 rows (with recall 1@10); `outlier_split` times encode and
-decode of the 2.5- and 3.5-bit outlier-channel split caches at the same shape.
+Prints one JSON line.
+  * `value`: packed-cache bytes read by decode per step / step time (GB/s),
+    over `--steps` steps after `--warmup` untimed ones. In every timed step
+    a pair of HIP events brackets the split-attention launch on its stream;
+    `roofline` is that kernel's average over the same steps (so it can never
+    exceed the step).
+  * `steady_state`: the same step after 300 warm-up steps (the chip's clocks
+    settle under sustained load over the first ~200 steps), 200 timed steps.
+  * `configs`: the other workloads, each as decode steps back to back over
+    rotating cache copies (enough to exceed the last-level cache where the
+    cache is small), its split launch alone after a 1 GiB read, and a plain
+    read (tq_read_probe) of as many bytes under the same conditions.
+  * `encode_mvec_s` (+ `encode_roofline`, `encode_mfma`): the 2^20 x 8-vector
+    bf16 encode sweep at mse-1..4 and prod-4 (dense and Hadamard rotations).
+  * `search`, `outlier_split`, `hadamard_*`: the other built rows.
+  * `cpu_baseline`: the float64 oracle on the host, one thread and all cores.
 """
 from __future__ import annotations
 
@@ -40,6 +46,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0      # dense fp16 matrix cores
 WORKLOAD = "gqa8_prod4_128k_b4"
+STEADY_WARMUP, STEADY_STEPS = 300, 200
 
 
 def _src_hash(name: str) -> str:
@@ -47,7 +54,7 @@ def _src_hash(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(kernel_file: str, src: str, launches_bytes: float):
+def _traffic(kernel_file: str, src: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None
     when absent or taken on another version of the kernel source."""
     path = os.path.join(ROOT, "profiles", kernel_file)
@@ -79,22 +86,25 @@ def _mfma_busy(kernel_row: str):
     return None
 
 
-def cpu_baseline(cfg, units=6):
-    """The oracle, as it stands, on a bounded sample of the same workload: the
-    first `units` (batch, KV head) pairs of batch row 0, each encoded (keys and
-    values over all 131072 tokens) and then decoded for its query heads."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_run(cfg, K, V, q, units):
+    """Oracle encode (keys prod, values mse, full length) and decode of the
+    first `units` (batch 0, KV head) pairs; returns (encode s, decode s)."""
     import numpy as np
     import synth
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     Rk, Rv, S = synth.constants(cfg.d)
     T = cfg.T
-    K, V = synth.make_kv(cfg, T=T, B=1)
-    q = synth.make_query(cfg, B=1)[0].astype(np.float64)
     ck = oracle.lloyd_max(cfg.d, cfg.k_bits - 1)[0]
     cv = oracle.lloyd_max(cfg.d, cfg.v_bits)[0]
     chunk = 8192
@@ -112,15 +122,43 @@ def cpu_baseline(cfg, units=6):
         for hq in range(h * cfg.G, (h + 1) * cfg.G):
             oracle.attention(q[hq], Kt, Vt, 1 / math.sqrt(cfg.d))
         t_dec += time.perf_counter() - t0
-    bytes_units = units * T * bytes_per_token(cfg)
+    return t_enc, t_dec
+
+
+def cpu_baseline(cfg):
+    """The oracle, as it stands, on a bounded sample of the headline workload:
+    whole (batch 0, KV head) units, each encoded (keys and values over all
+    131072 tokens) and then decoded for its 8 query heads, in float64 numpy.
+    Two modes: one thread (BLAS limited to 1) on 1 unit, and all host cores
+    (BLAS threads) on 4 units."""
+    import numpy as np
+    import synth
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    K, V = synth.make_kv(cfg, T=cfg.T, B=1)
+    K, V = K[:, :4], V[:, :4]
+    q = synth.make_query(cfg, B=1)[0].astype(np.float64)
+    bpt = bytes_per_token(cfg)
+    res = {}
+    for mode, units, limit in (("single_thread", 1, 1), ("all_cores", 4, None)):
+        if limit is None:
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            te, td = _oracle_run(cfg, K, V, q, units)
+        else:
+            with threadpool_limits(limits=limit):
+                threads = limit
+                te, td = _oracle_run(cfg, K, V, q, units)
+        res[mode] = {"threads": threads, "units": units, "decode_gbs": round(units * cfg.T * bpt / td / 1e9, 5),
+                     "decode_s": round(td, 3), "encode_mvec_s": round(2 * units * cfg.T / te / 1e6, 5),
+                     "encode_s": round(te, 3)}
+    allc = res["all_cores"]
     return {
-        "value": round(bytes_units / t_dec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": f"{units} of {cfg.B * cfg.Hkv} (batch, KV head) units, {T} tokens and {cfg.G} query heads "
-                  f"each; decode = dequantize + softmax attention in float64",
-        "decode_s": round(t_dec, 3),
-        "encode_mvec_s": round(2 * units * T / t_enc / 1e6, 5), "encode_s": round(t_enc, 3),
-        "encode_sample": f"{2 * units * T} vectors (keys prod-{cfg.k_bits}, values mse-{cfg.v_bits})",
-        "host_cpus": os.cpu_count(),
+        "value": allc["decode_gbs"], "unit": "GB/s", "cores": allc["threads"], "kind": "oracle",
+        "sample": f"(batch 0, KV head) units of {cfg.name}, {cfg.T} tokens and {cfg.G} query heads each: "
+                  f"encode = prod-{cfg.k_bits} keys + mse-{cfg.v_bits} values, decode = dequantize + softmax "
+                  f"attention, float64 numpy; 1 unit single-threaded, 4 units on all cores",
+        "single_thread": res["single_thread"], "all_cores": allc,
+        "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
     }
 
 
@@ -146,14 +184,12 @@ def bytes_per_token(cfg) -> int:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # Under sustained load the chip's clocks ramp up over the first ~200 steps
-    # (≈30 ms) and fall back after idling; the warm-up covers the ramp, so the
-    # timed steps measure the steady state.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-encode-sweep", action="store_true")
     ap.add_argument("--no-split", action="store_true", help="skip the outlier-channel split workloads")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other decode workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 512 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -175,6 +211,7 @@ def main():
     Rk, Rv, S = synth.constants(d)
     kq = TA.Quantizer(Rk, cfg.k_bits, cfg.k_variant, S, dev)
     vq = TA.Quantizer(Rv, cfg.v_bits, "mse", None, dev)
+    Event = lambda: torch.cuda.Event(enable_timing=True)
 
     log(f"[bench] generating {cfg.name}: B={B} Hkv={Hkv} T={T}")
     K, V = synth.make_kv(cfg)
@@ -182,20 +219,26 @@ def main():
     vg = torch.from_numpy(V.reshape(-1, d)).to(torch.bfloat16).to(dev)
     del K, V
     n_vec = B * Hkv * T
+
+    def packed_copies(kq_, vq_, kx, vx, n, ncopy):
+        """Encode kx/vx once, then copy the packed arrays into ncopy caches."""
+        kcs = [TA.Packed(kq_, n, dev) for _ in range(ncopy)]
+        vcs = [TA.Packed(vq_, n, dev) for _ in range(ncopy)]
+        TA.encode(kq_, kx, kcs[0])
+        TA.encode(vq_, vx, vcs[0])
+        for c in range(1, ncopy):
+            for src, dst in ((kcs[0], kcs[c]), (vcs[0], vcs[c])):
+                for name in ("codes", "norms", "qjl", "gammas"):
+                    if getattr(src, name) is not None:
+                        getattr(dst, name).copy_(getattr(src, name))
+        torch.cuda.synchronize()
+        return kcs, vcs
+
     # Three copies of the packed cache, used in turn: each step reads a cache
     # that two other steps' reads (1.2 GB) have since pushed out of the 256 MB
     # last-level cache, as when one layer's cache is read once per step.
     ncopy = 3
-    kcs = [TA.Packed(kq, n_vec, dev) for _ in range(ncopy)]
-    vcs = [TA.Packed(vq, n_vec, dev) for _ in range(ncopy)]
-    TA.encode(kq, kg, kcs[0])
-    TA.encode(vq, vg, vcs[0])
-    for c in range(1, ncopy):
-        for src, dst in ((kcs[0], kcs[c]), (vcs[0], vcs[c])):
-            for name in ("codes", "norms", "qjl", "gammas"):
-                if getattr(src, name) is not None:
-                    getattr(dst, name).copy_(getattr(src, name))
-    torch.cuda.synchronize()
+    kcs, vcs = packed_copies(kq, vq, kg, vg, n_vec, ncopy)
     log("[bench] packed cache ready")
 
     q = torch.from_numpy(synth.make_query(cfg)).to(dev)
@@ -204,21 +247,29 @@ def main():
     vnew = torch.from_numpy(synth.round_bf16(g.standard_normal((B * Hkv, d)).astype(np.float32))).to(torch.bfloat16).to(dev)
     dec = TA.Decoder(B, Hq, Hkv, T, dev)
     out = torch.empty_like(q)
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    def step(i, ev=None, qs=(kq, vq)):
-        # tq_decode_step: the new token of every (batch, KV head) goes to slot
-        # T - 1 (ctx_lens = NULL: every row is T long), then attention.
-        kc, vc = kcs[i % ncopy], vcs[i % ncopy]
-        if ev is None:
-            dec.step(*qs, knew, vnew, q, kc, vc, out=out)
-        else:
-            dec.step(*qs, knew, vnew, q, kc, vc, out=out, phase=1)
-            ev[0].record()
-            dec.step(*qs, knew, vnew, q, kc, vc, out=out, phase=2)
-            ev[1].record()
-            dec.step(*qs, knew, vnew, q, kc, vc, out=out, phase=3)
+    def timed_steps(dec_, qs, kcs_, vcs_, kn, vn, q_, out_, warmup, steps):
+        """`warmup` untimed fused decode steps, then `steps` timed ones over the
+        rotating cache copies, each with a pair of events around its split
+        launch (phase 2) on the current stream. Returns (ms per step by the
+        host clock between two synchronizations, split-launch µs list)."""
+        nc = len(kcs_)
+        for i in range(warmup):
+            dec_.step(*qs, kn, vn, q_, kcs_[i % nc], vcs_[i % nc], out=out_)
+        ea = [Event() for _ in range(steps)]
+        eb = [Event() for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            kc, vc = kcs_[i % nc], vcs_[i % nc]
+            dec_.step(*qs, kn, vn, q_, kc, vc, out=out_, phase=1)
+            ea[i].record()
+            dec_.step(*qs, kn, vn, q_, kc, vc, out=out_, phase=2)
+            eb[i].record()
+            dec_.step(*qs, kn, vn, q_, kc, vc, out=out_, phase=3)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        return ms, [a.elapsed_time(b) * 1e3 for a, b in zip(ea, eb)]
 
     if args.copy_calibration:
         src = torch.empty(1 << 27, dtype=torch.float32, device=dev).fill_(1.0)
@@ -227,159 +278,164 @@ def main():
         dst.copy_(src)                # reads 512 MiB, writes 512 MiB
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
-    # The dominant kernel: HIP events on its stream around its launch, in a
-    # second run of the same steps (the events' own gaps stay out of the step
-    # time above).
-    for i in range(args.steps):
-        step(i, (ev0[i], ev1[i]))
-    torch.cuda.synchronize()
-    k_ms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(args.steps))
-    k_avg = sum(k_ms) / len(k_ms)
-    # Spread of whole steps: one event after each step, in a third run (the
-    # events add their own small gaps, so the median sits a little above the
-    # event-free step time).
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    evs[0].record()
-    for i in range(args.steps):
-        step(i)
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    step_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
+
+    # ---- headline: the driver's warm-up and step counts ---------------------
+    ms_step, k_us = timed_steps(dec, (kq, vq), kcs, vcs, knew, vnew, q, out, args.warmup, args.steps)
+    k_avg = sum(k_us) / len(k_us)
+    k_sorted = sorted(k_us)
+    if k_avg > ms_step * 1e3:
+        log(f"[bench] WARNING: split-launch average {k_avg:.1f} us exceeds the step {ms_step * 1e3:.1f} us")
     bpt = bytes_per_token(cfg)
     dec_bytes = n_vec * bpt
     value = dec_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dec_bytes / (k_avg * 1e-3) / 1e9
-    log(f"[bench] step {ms_step:.4f} ms; split-attention kernel avg {k_avg * 1e3:.1f} us "
-        f"(min {k_ms[0] * 1e3:.1f}, max {k_ms[-1] * 1e3:.1f}); {achieved:.0f} GB/s")
+    achieved = dec_bytes / (k_avg * 1e-6) / 1e9
+    log(f"[bench] step {ms_step:.4f} ms; split-attention kernel avg {k_avg:.1f} us "
+        f"(min {k_sorted[0]:.1f}, max {k_sorted[-1]:.1f}); {achieved:.0f} GB/s")
 
-    # Same kernel on one copy, right after reading 1 GiB elsewhere (clean
-    # lines: nothing of the packed cache stays in the last-level cache and no
-    # write-back competes with the launch).
+    # ---- the same step in the steady state -----------------------------------
+    st_ms, st_k = timed_steps(dec, (kq, vq), kcs, vcs, knew, vnew, q, out, STEADY_WARMUP, STEADY_STEPS)
+    st_kavg = sum(st_k) / len(st_k)
+    steady = {"warmup": STEADY_WARMUP, "steps": STEADY_STEPS, "ms_per_step": round(st_ms, 5),
+              "value": round(dec_bytes / (st_ms * 1e-3) / 1e9, 1),
+              "frac": round(dec_bytes / (st_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+              "split_launch_us": round(st_kavg, 2),
+              "split_gbs": round(dec_bytes / (st_kavg * 1e-6) / 1e9, 1),
+              "split_frac": round(dec_bytes / (st_kavg * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+              "split_us_p10_p50_p90": [round(_pct(sorted(st_k), f), 2) for f in (0.1, 0.5, 0.9)]}
+    log(f"[bench] steady state: {steady}")
+
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    fl = []
-    for i in range(3):
-        dec(kq, vq, q, kcs[0], vcs[0], out=out, phase=1)
-        flush.sum()
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        dec(kq, vq, q, kcs[0], vcs[0], out=out, phase=2)
-        b_.record()
-        torch.cuda.synchronize()
-        fl.append(a_.elapsed_time(b_))
-    flushed_us = sorted(fl)[len(fl) // 2] * 1e3
+
+    def flushed_split_us(dec_, kq_, vq_, q_, kc, vc, out_, reps):
+        """Median µs of the split launch alone, each after a 1 GiB read (clean
+        lines: nothing of the packed cache stays in the last-level cache)."""
+        fl = []
+        for _ in range(reps):
+            dec_(kq_, vq_, q_, kc, vc, out=out_, phase=1)
+            flush.sum()
+            a_, b_ = Event(), Event()
+            a_.record()
+            dec_(kq_, vq_, q_, kc, vc, out=out_, phase=2)
+            b_.record()
+            torch.cuda.synchronize()
+            fl.append(a_.elapsed_time(b_) * 1e3)
+        return sorted(fl)[len(fl) // 2]
+
+    flushed_us = flushed_split_us(dec, kq, vq, q, kcs[0], vcs[0], out, 3)
     log(f"[bench] split-attention after a read-only cache flush: median {flushed_us:.1f} us")
 
-    # The part's practical read ceiling: one plain coalesced read
-    # (tq_read_probe, the decode stream's 16-byte non-temporal loads) of as
-    # many bytes as the packed cache, and of 4 GiB, back to back, each launch
-    # timed by events around it. A read carries a fixed cost of its own (the
-    # same-size read is the fair ceiling of one decode launch); the 4 GiB read
-    # gives the rate with that cost spread thin.
+    # ---- read ceilings --------------------------------------------------------
     xo = torch.zeros(1, dtype=torch.int32, device=dev)
-    big = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
 
-    def read_us(buf):
-        for _ in range(20):
-            TA.read_probe(buf, xo)
+    def read_back_to_back_us(bufs, reps=30, warm=20):
+        """Median µs of tq_read_probe over rotating buffers, back to back, each
+        launch between a pair of events."""
+        for i in range(warm):
+            TA.read_probe(bufs[i % len(bufs)], xo)
         pr = []
-        for _ in range(30):
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(reps):
+            a_, b_ = Event(), Event()
             a_.record()
-            TA.read_probe(buf, xo)
+            TA.read_probe(bufs[i % len(bufs)], xo)
             b_.record()
             pr.append((a_, b_))
         torch.cuda.synchronize()
         return sorted(a_.elapsed_time(b_) for a_, b_ in pr)[len(pr) // 2] * 1e3
 
-    pr_us = read_us(flush.view(torch.uint8)[:dec_bytes])
+    def read_after_flush_us(buf, reps=7):
+        rd = []
+        for _ in range(reps):
+            flush.sum()
+            a_, b_ = Event(), Event()
+            a_.record()
+            TA.read_probe(buf, xo)
+            b_.record()
+            torch.cuda.synchronize()
+            rd.append(a_.elapsed_time(b_) * 1e3)
+        return sorted(rd)[len(rd) // 2]
+
+    big = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+    pr_us = read_back_to_back_us([big.view(torch.uint8)[:dec_bytes]])
     read_peak = dec_bytes / (pr_us * 1e-6) / 1e9
-    pr4_us = read_us(big)
+    pr4_us = read_back_to_back_us([big])
     read_peak_4g = big.numel() * 4 / (pr4_us * 1e-6) / 1e9
-    del flush, xo, big
+    del big
     log(f"[bench] plain read of {dec_bytes} B: median {pr_us:.1f} us, {read_peak:.0f} GB/s; "
         f"of 4 GiB: {pr4_us:.1f} us, {read_peak_4g:.0f} GB/s")
 
-    # The same step with randomized Walsh-Hadamard rotations for keys and
-    # values (the caches re-encoded with them).
+    # ---- the same step with randomized Walsh-Hadamard rotations --------------
     Rkh, Rvh, _ = synth.hadamard_constants(d)
     kqh = TA.Quantizer(Rkh, cfg.k_bits, cfg.k_variant, S, dev, "hadamard")
     vqh = TA.Quantizer(Rvh, cfg.v_bits, "mse", None, dev, "hadamard")
     for c in range(ncopy):
         TA.encode(kqh, kg, kcs[c])
         TA.encode(vqh, vg, vcs[c])
-    for i in range(args.warmup):
-        step(i, qs=(kqh, vqh))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, qs=(kqh, vqh))
-    torch.cuda.synchronize()
-    had_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    had_ms, had_k = timed_steps(dec, (kqh, vqh), kcs, vcs, knew, vnew, q, out, args.warmup, args.steps)
     log(f"[bench] step with Hadamard rotations {had_ms:.4f} ms")
-
-    # The other 128K workload: batch 1, 8 KV heads, 32 query heads, prod-3 keys,
-    # mse-3 values (113 MB packed, which fits the 256 MB last-level cache: the
-    # split launch is timed alone, after a 1 GiB read).
     del kcs, vcs
     torch.cuda.empty_cache()
-    cfg_b1 = synth.WORKLOADS["llama8b_prod3_128k"]
-    kq3 = TA.Quantizer(Rk, cfg_b1.k_bits, cfg_b1.k_variant, S, dev)
-    vq3 = TA.Quantizer(Rv, cfg_b1.v_bits, "mse", None, dev)
-    K3, V3 = synth.make_kv(cfg_b1)
-    n3 = cfg_b1.B * cfg_b1.Hkv * cfg_b1.T
-    kc3, vc3 = TA.Packed(kq3, n3, dev), TA.Packed(vq3, n3, dev)
-    TA.encode(kq3, torch.from_numpy(K3.reshape(-1, d)).to(torch.bfloat16).to(dev), kc3)
-    TA.encode(vq3, torch.from_numpy(V3.reshape(-1, d)).to(torch.bfloat16).to(dev), vc3)
-    del K3, V3
-    q3 = torch.from_numpy(synth.make_query(cfg_b1)).to(dev)
-    dec3 = TA.Decoder(cfg_b1.B, cfg_b1.Hq, cfg_b1.Hkv, cfg_b1.T, dev)
-    out3 = torch.empty_like(q3)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    fl3 = []
-    for i in range(7):
-        dec3(kq3, vq3, q3, kc3, vc3, out=out3, phase=1)
-        flush.sum()
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        dec3(kq3, vq3, q3, kc3, vc3, out=out3, phase=2)
-        b_.record()
-        torch.cuda.synchronize()
-        fl3.append(a_.elapsed_time(b_))
-    cfg_b1_us = sorted(fl3)[len(fl3) // 2] * 1e3
-    cfg_b1_bytes = n3 * bytes_per_token(cfg_b1)
-    # Its ceiling: a plain read (tq_read_probe) of as many bytes, also after
-    # a 1 GiB read, so that none of them is in the last-level cache.
-    rb = torch.ones(cfg_b1_bytes // 4, dtype=torch.float32, device=dev)
-    xo3 = torch.zeros(1, dtype=torch.int32, device=dev)
-    rd3 = []
-    for i in range(7):
-        flush.sum()
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        TA.read_probe(rb, xo3)
-        b_.record()
-        torch.cuda.synchronize()
-        rd3.append(a_.elapsed_time(b_))
-    del flush, kc3, vc3, rb, xo3
-    cfg_b1_read_us = sorted(rd3)[len(rd3) // 2] * 1e3
-    log(f"[bench] {cfg_b1.name}: split attention after a cache flush {cfg_b1_us:.1f} us, "
-        f"{cfg_b1_bytes / cfg_b1_us / 1e3:.0f} GB/s; plain read of as many bytes {cfg_b1_read_us:.1f} us")
 
-    # Inner-product search: the first 2^20 key rows as a prod-4 database
-    # (index build = their encode), 64 N(0,1) queries, top 10 each; recall 1@10
-    # against the exact top-1 of the unquantized rows.
+    # ---- the other decode workloads -------------------------------------------
+    # Each: fused decode steps back to back over rotating cache copies (enough
+    # copies that the ones in rotation exceed the 256 MB last-level cache,
+    # except for the 0.4 MB single-head cache, which is latency-bound), its
+    # split launch alone after a 1 GiB read, and plain reads of as many bytes
+    # under both conditions.
+    configs = {}
+    if not args.no_configs:
+        for name, ncp, warm, steps in (("mse3_d128_4096_fp32", 1, 50, 200), ("llama8b_b4_32k", 12, 50, 200),
+                                       ("llama8b_prod3_128k", 4, 50, 200), ("batch64_b2_16k", 3, 20, 50)):
+            c = synth.WORKLOADS[name]
+            kqc = TA.Quantizer(Rk, c.k_bits, c.k_variant, S if c.k_variant == "prod" else None, dev)
+            vqc = TA.Quantizer(Rv, c.v_bits, "mse", None, dev)
+            n_c = c.B * c.Hkv * c.T
+            if n_c * c.d > (1 << 28):
+                kx, vx = synth.make_kv_device(c, dev)      # too large to draw on the host quickly
+            else:
+                K_, V_ = synth.make_kv(c)
+                tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+                kx = torch.from_numpy(K_.reshape(-1, d)).to(tdt).to(dev)
+                vx = torch.from_numpy(V_.reshape(-1, d)).to(tdt).to(dev)
+                del K_, V_
+            kcc, vcc = packed_copies(kqc, vqc, kx, vx, n_c, ncp)
+            qc = torch.from_numpy(synth.make_query(c)).to(dev)
+            oc = torch.empty_like(qc)
+            gn = np.random.default_rng(c.seed_base + 5)
+            rows = c.B * c.Hkv
+            tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+            kn_c = torch.from_numpy(synth.round_bf16(gn.standard_normal((rows, d)).astype(np.float32))).to(tdt).to(dev)
+            vn_c = torch.from_numpy(synth.round_bf16(gn.standard_normal((rows, d)).astype(np.float32))).to(tdt).to(dev)
+            dc = TA.Decoder(c.B, c.Hq, c.Hkv, c.T, dev)
+            ms_c, k_c = timed_steps(dc, (kqc, vqc), kcc, vcc, kn_c, vn_c, qc, oc, warm, steps)
+            kav = sum(k_c) / len(k_c)
+            fl_c = flushed_split_us(dc, kqc, vqc, qc, kcc[0], vcc[0], oc, 5)
+            by_c = n_c * bytes_per_token(c)
+            rbufs = [torch.ones(by_c // 4, dtype=torch.float32, device=dev) for _ in range(ncp)]
+            rd_b2b = read_back_to_back_us(rbufs, reps=30, warm=10)
+            rd_fl = read_after_flush_us(rbufs[0])
+            del rbufs, kcc, vcc, kx, vx
+            torch.cuda.empty_cache()
+            gbs = lambda us: round(by_c / (us * 1e-6) / 1e9, 1)
+            frac = lambda us: round(by_c / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            configs[name] = {
+                "shape": f"B={c.B} Hkv={c.Hkv} Hq={c.Hq} T={c.T}", "keys": f"{c.k_variant}-{c.k_bits}",
+                "values": f"mse-{c.v_bits}", "packed_cache_bytes": by_c, "cache_copies": ncp,
+                "warmup": warm, "steps": steps,
+                "step_us": round(ms_c * 1e3, 2), "step_gbs": gbs(ms_c * 1e3), "step_frac": frac(ms_c * 1e3),
+                "split_us": round(kav, 2), "split_gbs": gbs(kav), "split_frac": frac(kav),
+                "same_size_read_us": round(rd_b2b, 2), "split_over_read": round(rd_b2b / kav, 4),
+                "split_after_flush_us": round(fl_c, 2), "split_after_flush_frac": frac(fl_c),
+                "read_after_flush_us": round(rd_fl, 2),
+            }
+            log(f"[bench] {name}: {configs[name]}")
+
+    # ---- inner-product search -------------------------------------------------
+    # The first 2^20 key rows as a prod-4 database (index build = their
+    # encode), 64 N(0,1) queries, top 10 each; recall 1@10 against the exact
+    # top-1 of the unquantized rows.
     n_db, nq_s, k_s = 1 << 20, 64, 10
     db = TA.Packed(kq, n_db, dev)
-    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_, b_ = Event(), Event()
     TA.encode(kq, kg[:n_db], db)
     a_.record()
     TA.encode(kq, kg[:n_db], db)
@@ -405,18 +461,17 @@ def main():
               "db_gbs": round(db_bytes / (s_us * 1e-6) / 1e9, 1),
               "db_streamed_gbs": round((nq_s + 7) // 8 * db_bytes / (s_us * 1e-6) / 1e9, 1),
               "recall_1_at_10": round(recall, 4), "index_build_ms": round(build_ms, 4)}
-    del ws_s
+    del ws_s, db
+    torch.cuda.empty_cache()
     log(f"[bench] search: {search}")
 
-    # Outlier-channel split workloads ("2.5-bit": 32 channels at 3 bits + 96 at
-    # 2, and "3.5-bit": 4 + 3; mse keys and values, a norm per group) at the
-    # benchmark's shape: encode of the key cache, the decode call (query
+    # ---- outlier-channel split workloads ("2.5-bit": 32 channels at 3 bits + 96
+    # at 2, and "3.5-bit": 4 + 3; mse keys and values, a norm per group) at the
+    # headline's shape: encode of the key cache, the decode call (query
     # operands, split attention, merge) over three cache copies in turn, and
     # the split-attention launch alone after a 1 GiB read.
     split_res = {}
     if not args.no_split:
-        del db
-        torch.cuda.empty_cache()
         for sname in ("gqa8_split25_128k_b4", "gqa8_split35_128k_b4"):
             cs = synth.WORKLOADS[sname]
             sc = synth.split_constants(d)
@@ -427,11 +482,7 @@ def main():
             v6 = torch.from_numpy(V6.reshape(-1, d)).to(torch.bfloat16).to(dev)
             del K6, V6
             n6 = cs.B * cs.Hkv * cs.T
-            kc6 = [TA.Packed(kq6, n6, dev) for _ in range(ncopy)]
-            vc6 = [TA.Packed(vq6, n6, dev) for _ in range(ncopy)]
-            for c in range(ncopy):
-                TA.encode(kq6, k6, kc6[c])
-                TA.encode(vq6, v6, vc6[c])
+            kc6, vc6 = packed_copies(kq6, vq6, k6, v6, n6, ncopy)
             a_.record()
             TA.encode(kq6, k6, kc6[0])
             b_.record()
@@ -447,19 +498,9 @@ def main():
                 dec6(kq6, vq6, q, kc6[i % ncopy], vc6[i % ncopy], out=out)
             torch.cuda.synchronize()
             ms6 = (time.perf_counter() - t0) / args.steps * 1e3
-            flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-            fl6 = []
-            for i in range(5):
-                dec6(kq6, vq6, q, kc6[0], vc6[0], out=out, phase=1)
-                flush.sum()
-                a_.record()
-                dec6(kq6, vq6, q, kc6[0], vc6[0], out=out, phase=2)
-                b_.record()
-                torch.cuda.synchronize()
-                fl6.append(a_.elapsed_time(b_))
-            del flush, kc6, vc6
+            us6 = flushed_split_us(dec6, kq6, vq6, q, kc6[0], vc6[0], out, 5)
+            del kc6, vc6
             torch.cuda.empty_cache()
-            us6 = sorted(fl6)[len(fl6) // 2] * 1e3
             by6 = n6 * (kq6.code_bytes + 8 + vq6.code_bytes + 8)
             split_res[cs.name] = {
                 "bytes_per_token_head": kq6.code_bytes + 8 + vq6.code_bytes + 8, "packed_cache_bytes": by6,
@@ -468,9 +509,11 @@ def main():
                 "frac": round(by6 / us6 / 1e3 / PEAK_HBM_GBS, 4),
                 "encode_mvec_s": round(n6 / (enc6_ms * 1e-3) / 1e6, 1)}
             log(f"[bench] {cs.name}: {split_res[cs.name]}")
+    del flush
 
+    # ---- encode sweep ---------------------------------------------------------
     enc = {}
-    enc_roof = None
+    enc_roof = enc_roof_prod = None
     enc_mfma = {}
     if not args.no_encode_sweep:
         n_sweep = (1 << 20) * 8
@@ -482,7 +525,7 @@ def main():
             qq = TA.Quantizer(Rk if rot == "dense" else Rkh, bits, var, S if var == "prod" else None, dev, rot)
             pk = TA.Packed(qq, n_sweep, dev)
             TA.encode(qq, xs, pk)
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_, b_ = Event(), Event()
             reps = 3
             a_.record()
             for _ in range(reps):
@@ -491,13 +534,17 @@ def main():
             torch.cuda.synchronize()
             ms = a_.elapsed_time(b_) / reps
             enc[label] = round(n_sweep / (ms * 1e-3) / 1e6, 1)
-            if label == "mse4":
-                eb = n_sweep * (2 * d + d * 4 // 8 + 4)
-                enc_roof = {"kernel": "encode_kernel<4,mse,bf16>", "bound": "hbm",
-                            "achieved": round(eb / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                            "traffic": _traffic("encode_mse4_sweep.counters.json", "tq_encode.hip", eb)}
+            bm = bits - (var == "prod")
+            eb = n_sweep * (2 * d + d * bm // 8 + 4 + ((d // 8 + 4) if var == "prod" else 0))
             if label in ("mse4", "prod4"):
+                roof = {"kernel": f"encode_kernel<{bm},{var},bf16>", "bound": "hbm",
+                        "achieved": round(eb / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                if label == "mse4":
+                    roof["traffic"] = _traffic("encode_mse4_sweep.counters.json", "tq_encode.hip")
+                    enc_roof = roof
+                else:
+                    enc_roof_prod = roof
                 # Matrix-core use: the algorithmic flops (2d² per vector for the
                 # rotation, 2d² more for the prod sketch) and the flops the
                 # fp16 matrix cores execute with the operands split into hi/lo
@@ -511,10 +558,12 @@ def main():
                                    "executed_tflops": round(rate * exe / 1e12, 1), "peak_tflops": PEAK_F16_TFLOPS,
                                    "frac": round(rate * alg / 1e12 / PEAK_F16_TFLOPS, 4),
                                    "executed_frac": round(rate * exe / 1e12 / PEAK_F16_TFLOPS, 4),
-                                   "busy_counter": _mfma_busy(f"tq::encode_kernel<{bits - (var == 'prod')}, "
+                                   "busy_counter": _mfma_busy(f"tq::encode_kernel<{bm}, "
                                                               f"{'true' if var == 'prod' else 'false'}, false>")}
             del pk, qq
             log(f"[bench] encode {label}: {enc[label]} Mvec/s")
+        if enc_roof is not None and enc_roof_prod is not None:
+            enc_roof["prod4"] = enc_roof_prod
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -541,22 +590,19 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "roofline": {"kernel": "attn_split_kernel<3,prod,4>", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": _traffic("attn_split_gqa8_prod4_128k.counters.json", "tq_decode.hip", dec_bytes),
-                     "avg_launch_us": round(k_avg * 1e3, 2), "after_read_flush_us": round(flushed_us, 2),
-                     "launch_us_p10_p50_p90": [round(_pct(k_ms, f) * 1e3, 2) for f in (0.1, 0.5, 0.9)],
+                     "traffic": _traffic("attn_split_gqa8_prod4_128k.counters.json", "tq_decode.hip"),
+                     "bytes_per_launch": dec_bytes, "avg_launch_us": round(k_avg, 2),
+                     "launch_us_p10_p50_p90": [round(_pct(k_sorted, f), 2) for f in (0.1, 0.5, 0.9)],
+                     "timed_in": "the headline's timed steps (events around each split launch)",
+                     "after_read_flush_us": round(flushed_us, 2),
                      "frac_of_measured_read": round(achieved / read_peak, 4),
                      "cache_copies": ncopy},
-        "step_us_p10_p50_p90": [round(_pct(step_us, f), 2) for f in (0.1, 0.5, 0.9)],
+        "steady_state": steady,
         "measured_read_peak": {"gbs": round(read_peak, 1), "bytes": dec_bytes, "us": round(pr_us, 2),
                                "gbs_4gib": round(read_peak_4g, 1),
                                "kernel": "tq_read_probe: plain coalesced read, 16-byte non-temporal loads",
                                "value_frac": round(value / read_peak, 4)},
-        "cfg_llama8b_prod3_128k": {"workload": cfg_b1.name, "packed_cache_bytes": cfg_b1_bytes,
-                                   "split_after_flush_us": round(cfg_b1_us, 2),
-                                   "split_gbs": round(cfg_b1_bytes / cfg_b1_us / 1e3, 1),
-                                   "frac": round(cfg_b1_bytes / cfg_b1_us / 1e3 / PEAK_HBM_GBS, 4),
-                                   "same_size_read_us": round(cfg_b1_read_us, 2),
-                                   "frac_of_measured_read": round(cfg_b1_read_us / cfg_b1_us, 4)},
+        "configs": configs,
         "hadamard_step_ms": round(had_ms, 5),
         "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
         "search": search,

@@ -219,3 +219,33 @@ def make_query(cfg: DecodeConfig, B: int | None = None) -> np.ndarray:
 def constants(d: int = 128):
     """(rotation for keys, rotation for values, QJL projection), float32."""
     return rotation(d, SEED_ROT_K), rotation(d, SEED_ROT_V), projection(d, SEED_PROJ)
+
+
+def make_kv_device(cfg: DecodeConfig, device, T: int | None = None, B: int | None = None):
+    """Raw K and V caches [B*Hkv*T, d] drawn on the device by a seeded torch
+    generator with the same recipe as make_kv (N(0,1); the outlier recipe's
+    4 channels per head ×10; the log-normal recipe's per-token LogNormal(0,
+    0.5) scales), stored as cfg.dtype (bfloat16 by round-to-nearest-even, or
+    float32). The numbers differ from make_kv's (another generator); they
+    serve timing runs of caches too large to draw on the host quickly, never
+    a comparison with the oracle."""
+    import torch
+
+    T = cfg.T if T is None else T
+    B = cfg.B if B is None else B
+    out = []
+    for role in (0, 1):
+        g = torch.Generator(device=device).manual_seed(cfg.seed_base + role)
+        x = torch.randn((B, cfg.Hkv, T, cfg.d), generator=g, device=device, dtype=torch.float32)
+        if cfg.recipe == "outlier":
+            for h in range(cfg.Hkv):
+                ch = torch.randperm(cfg.d, generator=g, device=device)[:4]
+                x[:, h, :, ch] *= 10.0
+        elif cfg.recipe == "lognormal":
+            s = torch.randn((B, cfg.Hkv, T, 1), generator=g, device=device, dtype=torch.float32)
+            x *= torch.exp(0.5 * s)
+        elif cfg.recipe != "gaussian":
+            raise ValueError(cfg.recipe)
+        x = x.reshape(-1, cfg.d)
+        out.append(x.to(torch.bfloat16) if cfg.dtype == "bf16" else x)
+    return out[0], out[1]

@@ -113,9 +113,10 @@ def check_encode(gpu: dict, ref: dict, bits: int, variant: str, rows=None):
 
 
 def packed_from_oracle(enc: dict, q: T.Quantizer) -> T.Packed:
-    """Upload an oracle-produced packed cache (norms/γ rounded to float32)."""
+    """Upload an oracle-produced packed cache (norms/γ rounded to float32)
+    into guard-padded buffers."""
     n = enc["norms"].shape[0]
-    p = T.Packed(q, n, DEV)
+    p = guarded_packed(q, n)
     if q.code_bytes:
         p.codes.copy_(torch.from_numpy(np.ascontiguousarray(enc["codes"])))
     p.norms.copy_(torch.from_numpy(enc["norms"].astype(np.float32)))
@@ -231,9 +232,10 @@ def check_encode_split(gpu: dict, ref: dict, bits: int):
 
 
 def packed_from_oracle_split(enc: dict, q: T.Quantizer) -> T.Packed:
-    """Upload an oracle-produced split cache (norm pairs rounded to float32)."""
+    """Upload an oracle-produced split cache (norm pairs rounded to float32)
+    into guard-padded buffers."""
     n = enc["norms"].shape[0]
-    p = T.Packed(q, n, DEV)
+    p = guarded_packed(q, n)
     p.codes.copy_(torch.from_numpy(np.ascontiguousarray(enc["codes"])))
     p.norms.copy_(torch.from_numpy(enc["norms"].astype(np.float32)))
     return p
@@ -261,3 +263,69 @@ def encode_split_away_from_ties(X, consts, bits, seed, dtype):
         for k in enc:
             enc[k][rows] = sub[k]
     raise AssertionError("could not move rows away from ties")
+
+
+# ---------------------------------------------------------------------------
+# Guard-padded outputs: every output buffer of a parity call sits between two
+# canary-filled regions, which must be untouched afterwards (a write past
+# either end of an output is a failure even when the values inside are right).
+# ---------------------------------------------------------------------------
+GUARD = 4096           # bytes on each side; keeps the 256-byte alignment of the view
+CANARY = 0xA5
+
+
+class Guarded:
+    """A device byte buffer of `nbytes` between two canary-filled guards."""
+
+    def __init__(self, nbytes: int, fill: int = 0):
+        self.nbytes = nbytes
+        self.raw = torch.full((nbytes + 2 * GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+        self.view = self.raw[GUARD:GUARD + nbytes]
+        self.view.fill_(fill)
+
+    def intact(self) -> bool:
+        torch.cuda.synchronize()
+        return bool((self.raw[:GUARD] == CANARY).all()) and bool((self.raw[GUARD + self.nbytes:] == CANARY).all())
+
+
+def guarded_tensor(shape, dtype, fill: int = 0):
+    """(tensor, guard) with the tensor's bytes inside a Guarded buffer."""
+    n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    g = Guarded(n, fill)
+    return g.view.view(dtype).view(*shape), g
+
+
+def guarded_packed(q: T.Quantizer, n: int) -> T.Packed:
+    """A T.Packed of n slots whose arrays (codes, norms, sketch, γ) are
+    guard-padded; `p.guards` lists the guards."""
+    p = T.Packed(q, n, DEV)
+    p.guards = []
+    for name in ("codes", "norms", "qjl", "gammas"):
+        t = getattr(p, name)
+        if t is None:
+            continue
+        gt, g = guarded_tensor(tuple(t.shape), t.dtype)
+        setattr(p, name, gt)
+        p.guards.append(g)
+    p.c = L.tq_packed(p.codes.data_ptr() if q.code_bytes else None, p.norms.data_ptr(),
+                      None if p.qjl is None else p.qjl.data_ptr(),
+                      None if p.gammas is None else p.gammas.data_ptr())
+    return p
+
+
+def guarded_decoder(B, Hq, Hkv, max_ctx) -> T.Decoder:
+    """A T.Decoder whose workspace (query operands and split partials) is
+    guard-padded (`dec.guard`)."""
+    dec = T.Decoder(B, Hq, Hkv, max_ctx, DEV)
+    dec.guard = Guarded(dec.ws_bytes, CANARY)
+    dec.ws = dec.guard.view
+    return dec
+
+
+def assert_guards(*objs):
+    """Every guard of the given Guarded buffers, guarded Packed objects and
+    guarded decoders is intact."""
+    for o in objs:
+        gs = getattr(o, "guards", None) or ([o.guard] if hasattr(o, "guard") else [o])
+        for g in gs:
+            assert g.intact(), "a write landed outside an output buffer"

@@ -1,6 +1,19 @@
 """GPU parity of tq_attn_decode against the oracle (through the C ABI):
 (i) both sides decode the oracle-produced cache; (ii) GPU encode + GPU decode
-against oracle encode + oracle attention."""
+against oracle encode + oracle attention. Every output buffer (packed codes,
+norms, sketch, γ, the workspace with the split partials, and `out`) is
+guard-padded, and the guards must be intact after each call.
+
+The split-attention instantiations the five named workloads dispatch to are
+each compared with the oracle at the workload's own size:
+  mse3_d128_4096_fp32  attn_split_kernel<3, mse, 3, aligned>   test_decode_config1_full_size
+  llama8b_b4_32k       attn_split_kernel<4, mse, 4, aligned>   test_decode_config2_full_size_sampled
+  llama8b_prod3_128k   attn_split_kernel<2, prod, 3, aligned>  test_decode_full_size_sampled
+  batch64_b2_16k       attn_split_kernel<2, mse, 2, aligned>   test_decode_full_size_batched_sampled
+  gqa8_prod4_128k_b4   attn_split_kernel<3, prod, 4, aligned>  test_decode_step_full_size_benchmark_shape_sampled,
+                                                               test_decode_aligned_ragged_lengths_full_size
+("aligned": max_ctx is a multiple of the 32-token block, the variant without
+the ragged-tail clamps.)"""
 import math
 
 import numpy as np
@@ -9,8 +22,9 @@ import torch
 
 import synth
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import (DEV, check_encode, encode_away_from_ties, gpu_packed_arrays, oracle_dequant,
-                      packed_from_oracle, quantizers, rel_l2_per_head, say, to_gpu_x)
+from gpu_util import (DEV, assert_guards, check_encode, encode_away_from_ties, gpu_packed_arrays,
+                      guarded_decoder, guarded_packed, guarded_tensor, oracle_dequant, packed_from_oracle,
+                      quantizers, rel_l2_per_head, say, to_gpu_x)
 from oracle import decode_attention
 
 pytestmark = pytest.mark.gpu
@@ -34,25 +48,30 @@ def run_case(cfg, T_ctx, B, lens=None, end_to_end=True, rotation="dense"):
     Vt = oracle_dequant(ev, Rv, None, cfg.v_bits, "mse").reshape(shape)
     live = [(b, h) for b in range(B) for h in range(cfg.Hq) if lens is None or lens[b] > 0]
     ref = decode_attention(q, Kt, Vt, 1 / math.sqrt(128), ctx_lens=lens, heads=live)
-    dec = T.Decoder(B, cfg.Hq, cfg.Hkv, T_ctx, DEV)
+    dec = guarded_decoder(B, cfg.Hq, cfg.Hkv, T_ctx)
     qg = torch.from_numpy(q).to(DEV)
     lg = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    og, og_guard = guarded_tensor((B, cfg.Hq, 128), torch.float32)
     # (i) oracle cache
-    out = dec(kq, vq, qg, packed_from_oracle(ek, kq), packed_from_oracle(ev, vq), lg).cpu().numpy()
+    out = dec(kq, vq, qg, packed_from_oracle(ek, kq), packed_from_oracle(ev, vq), lg, out=og).cpu().numpy()
+    assert_guards(dec, og_guard)
     empty = np.zeros((B,), bool) if lens is None else (np.array(lens) == 0)
     assert np.all(out[empty] == 0)
     r = rel_l2_per_head(out[~empty], ref[~empty])
     say("  oracle-cache rel L2 max", r.max())
     assert r.max() <= TOL
     if end_to_end:
-        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
-        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
+        n = B * cfg.Hkv * T_ctx
+        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype), guarded_packed(kq, n))
+        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype), guarded_packed(vq, n))
+        assert_guards(kp, vp)
         # Away from ties the encodes agree exactly (codes, sketch bits).
         ks = check_encode(gpu_packed_arrays(kp, kq), ek, cfg.k_bits, cfg.k_variant)
         vs = check_encode(gpu_packed_arrays(vp, vq), ev, cfg.v_bits, "mse")
         assert ks.get("code_mismatch", 0) == 0 and ks.get("sketch_mismatch", 0) == 0
         assert vs.get("code_mismatch", 0) == 0
-        out2 = dec(kq, vq, qg, kp, vp, lg).cpu().numpy()
+        out2 = dec(kq, vq, qg, kp, vp, lg, out=og).cpu().numpy()
+        assert_guards(dec, og_guard, kp, vp)
         r2 = rel_l2_per_head(out2[~empty], ref[~empty])
         say("  end-to-end rel L2 max", r2.max())
         assert r2.max() <= TOL
@@ -102,73 +121,60 @@ def test_decode_hadamard_rotation(name):
 
 
 def test_decode_full_size_sampled():
-    # 128K context at the benchmark's shape (prod-3 keys, mse-3 values, GQA 4),
-    # GPU encode + decode; the oracle evaluates two KV heads' query heads.
-    cfg = synth.WORKLOADS["llama8b_prod3_128k"]
-    kq, vq, Rk, Rv, S = quantizers(cfg)
-    say("generating", cfg.name)
-    K, V = synth.make_kv(cfg)
-    q = synth.make_query(cfg)
-    encs = {}
-    for kvh in (0, 5):
-        encs[kvh] = (encode_away_from_ties(K[0, kvh], Rk, S, cfg.k_bits, cfg.k_variant, 300 + kvh, cfg.dtype),
-                     encode_away_from_ties(V[0, kvh], Rv, None, cfg.v_bits, "mse", 310 + kvh, cfg.dtype))
-    kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
-    vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
-    dec = T.Decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T, DEV)
-    out = dec(kq, vq, torch.from_numpy(q).to(DEV), kp, vp).cpu().numpy()
-    for kvh in (0, 5):
-        ek, ev = encs[kvh]
-        Kt = oracle_dequant(ek, Rk, S, cfg.k_bits, cfg.k_variant)[None, None]
-        Vt = oracle_dequant(ev, Rv, None, cfg.v_bits, "mse")[None, None]
-        hs = list(range(kvh * cfg.G, (kvh + 1) * cfg.G))
-        ref = decode_attention(q[:, hs], Kt, Vt, 1 / math.sqrt(128))
-        r = rel_l2_per_head(out[0, hs], ref[0])
-        say("  full-size kv head", kvh, "rel L2", r.max())
-        assert r.max() <= TOL
+    # 128K context at batch 1 (prod-3 keys, mse-3 values, GQA 4), GPU encode +
+    # decode; the oracle evaluates two KV heads' query heads.
+    _full_size_units(synth.WORKLOADS["llama8b_prod3_128k"], [(0, 0), (0, 5)], 300, use_step=False)
 
 
-def _full_size_units(cfg, units, seed, use_step):
+def _full_size_units(cfg, units, seed, use_step, lens=None):
     """Full-size decode of `cfg` on the GPU (encode + decode, or the fused
-    decode step whose new token is the last one), with the oracle evaluating
-    the query heads of the sampled (batch, KV head) units."""
+    decode step whose new token is each row's last one), with the oracle
+    evaluating the query heads of the sampled (batch, KV head) units over
+    their first lens[b] tokens (all T when lens is None)."""
     kq, vq, Rk, Rv, S = quantizers(cfg)
-    say("generating", cfg.name)
+    say("generating", cfg.name, "lens", lens)
     K, V = synth.make_kv(cfg)
     q = synth.make_query(cfg)
+    L = [cfg.T] * cfg.B if lens is None else lens
     encs = {}
     for (b, kvh) in units:
-        encs[(b, kvh)] = (encode_away_from_ties(K[b, kvh], Rk, S, cfg.k_bits, cfg.k_variant, seed + 2 * kvh + 17 * b,
-                                                cfg.dtype),
-                          encode_away_from_ties(V[b, kvh], Rv, None, cfg.v_bits, "mse", seed + 2 * kvh + 17 * b + 1,
-                                                cfg.dtype))
-    dec = T.Decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T, DEV)
+        n = L[b]
+        encs[(b, kvh)] = (encode_away_from_ties(K[b, kvh, :n], Rk, S, cfg.k_bits, cfg.k_variant,
+                                                seed + 2 * kvh + 17 * b, cfg.dtype),
+                          encode_away_from_ties(V[b, kvh, :n], Rv, None, cfg.v_bits, "mse",
+                                                seed + 2 * kvh + 17 * b + 1, cfg.dtype))
+    dec = guarded_decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T)
     qg = torch.from_numpy(q).to(DEV)
+    lg = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    og, og_guard = guarded_tensor((cfg.B, cfg.Hq, 128), torch.float32)
+    n_all = cfg.B * cfg.Hkv * cfg.T
+    kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype), guarded_packed(kq, n_all))
+    vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype), guarded_packed(vq, n_all))
     if use_step:
-        # the cache holds tokens 0..T-2; the step appends token T-1 of every row
-        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
-        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
-        last = torch.arange(cfg.B * cfg.Hkv, device=DEV) * cfg.T + cfg.T - 1
+        # the cache holds every row's tokens but its last one; the step appends it
+        rows = torch.arange(cfg.B * cfg.Hkv, device=DEV)
+        last = rows * cfg.T + torch.tensor(L, device=DEV).repeat_interleave(cfg.Hkv) - 1
         for p in (kp, vp):
             p.norms[last] = 0.0
             p.codes[last] = 0
             if p.qjl is not None:
                 p.qjl[last] = 0
                 p.gammas[last] = 0.0
-        kn = to_gpu_x(np.ascontiguousarray(K[:, :, -1].reshape(-1, 128)), cfg.dtype)
-        vn = to_gpu_x(np.ascontiguousarray(V[:, :, -1].reshape(-1, 128)), cfg.dtype)
-        out = dec.step(kq, vq, kn, vn, qg, kp, vp).cpu().numpy()
+        li = np.repeat(np.asarray(L) - 1, cfg.Hkv)
+        bi, hi = np.repeat(np.arange(cfg.B), cfg.Hkv), np.tile(np.arange(cfg.Hkv), cfg.B)
+        kn = to_gpu_x(np.ascontiguousarray(K[bi, hi, li]), cfg.dtype)
+        vn = to_gpu_x(np.ascontiguousarray(V[bi, hi, li]), cfg.dtype)
+        out = dec.step(kq, vq, kn, vn, qg, kp, vp, lg, out=og).cpu().numpy()
     else:
-        kp = T.encode(kq, to_gpu_x(_flat(K), cfg.dtype))
-        vp = T.encode(vq, to_gpu_x(_flat(V), cfg.dtype))
-        out = dec(kq, vq, qg, kp, vp).cpu().numpy()
+        out = dec(kq, vq, qg, kp, vp, lg, out=og).cpu().numpy()
+    assert_guards(dec, og_guard, kp, vp)
     for (b, kvh), (ek, ev) in encs.items():
         Kt = oracle_dequant(ek, Rk, S, cfg.k_bits, cfg.k_variant)[None, None]
         Vt = oracle_dequant(ev, Rv, None, cfg.v_bits, "mse")[None, None]
         hs = list(range(kvh * cfg.G, (kvh + 1) * cfg.G))
         ref = decode_attention(q[b:b + 1, hs], Kt, Vt, 1 / math.sqrt(128))
         r = rel_l2_per_head(out[b, hs], ref[0])
-        say("  full-size", cfg.name, "unit", (b, kvh), "rel L2", r.max())
+        say("  full-size", cfg.name, "unit", (b, kvh), "len", L[b], "rel L2", r.max())
         assert r.max() <= TOL
 
 
@@ -183,3 +189,32 @@ def test_decode_full_size_batched_sampled():
     # 64 sequences x 16384 tokens, 8 KV heads, 32 query heads, mse-2 keys and
     # values, log-normal per-token norms; two units sampled.
     _full_size_units(synth.WORKLOADS["batch64_b2_16k"], [(0, 3), (63, 7)], 600, use_step=False)
+
+
+def test_decode_config1_full_size():
+    # 4096 fp32 N(0,1) keys and values of one head, mse-3 both, one query:
+    # one unit of two 2048-token splits (aligned: 4096 is a multiple of 32),
+    # compared in full, on the oracle's cache and end to end.
+    cfg = synth.WORKLOADS["mse3_d128_4096_fp32"]
+    run_case(cfg, cfg.T, cfg.B)
+
+
+def test_decode_config2_full_size_sampled():
+    # Batch 1, 8 KV heads, 32 query heads, 32768 tokens, mse-4 keys and
+    # values (16 splits of 2048 tokens per unit, aligned); two units sampled.
+    _full_size_units(synth.WORKLOADS["llama8b_b4_32k"], [(0, 0), (0, 5)], 700, use_step=False)
+
+
+def test_decode_aligned_ragged_lengths_full_size():
+    # The benchmark's shape with max_ctx = 131072 (a multiple of 32: the
+    # aligned variant) and ragged lengths, one unit sampled per batch row;
+    # the row of length 1 reads a single token of its first split.
+    _full_size_units(synth.WORKLOADS["gqa8_prod4_128k_b4"], [(0, 0), (1, 3), (2, 7), (3, 2)], 800,
+                     use_step=False, lens=[131071, 12345, 65536, 1])
+
+
+def test_decode_step_aligned_ragged_lengths_full_size():
+    # The same through the fused decode step: each row's last token is
+    # appended by the step itself.
+    _full_size_units(synth.WORKLOADS["gqa8_prod4_128k_b4"], [(0, 5), (1, 0), (2, 4), (3, 7)], 900,
+                     use_step=True, lens=[131071, 12345, 65536, 1])

@@ -6,7 +6,8 @@ import torch
 import synth
 from kv_cache_vector_06_amd import _lib as L
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import DEV, book, check_encode, gpu_packed_arrays, oracle_encode, say, to_gpu_x
+from gpu_util import (DEV, assert_guards, book, check_encode, gpu_packed_arrays, guarded_packed, oracle_encode, say,
+                      to_gpu_x)
 from oracle import encode_mse, encode_prod, unpack_codes, unpack_signs
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +27,8 @@ def test_encode_parity(consts, bits, variant, dtype):
     X = synth.outlier_kv(1, 1, n, 128, seed=100 + bits, dtype=dtype)[0, 0]
     say("encode", bits, variant, dtype, n)
     q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV)
-    p = T.encode(q, to_gpu_x(X, dtype))
+    p = T.encode(q, to_gpu_x(X, dtype), guarded_packed(q, n))
+    assert_guards(p)
     st = check_encode(gpu_packed_arrays(p, q), oracle_encode(X, Rk, S, bits, variant), bits, variant)
     say(st)
 
@@ -47,11 +49,14 @@ def test_encode_parity_hadamard(bits, variant, dtype):
     say("encode hadamard", bits, variant, dtype, n)
     q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV, "hadamard")
     xg = to_gpu_x(X, dtype)
-    p = T.encode(q, xg)
+    p = T.encode(q, xg, guarded_packed(q, n))
+    assert_guards(p)
     g = gpu_packed_arrays(p, q)
     st = check_encode(g, oracle_encode(X, Rk, S, bits, variant), bits, variant)
     say(st)
-    small = gpu_packed_arrays(T.encode(q, xg[:37]), q)       # the row-tile encoder
+    ps = T.encode(q, xg[:37], guarded_packed(q, 37))          # the row-tile encoder
+    assert_guards(ps)
+    small = gpu_packed_arrays(ps, q)
     for k in g:
         np.testing.assert_array_equal(small[k], g[k][:37])
 

@@ -13,8 +13,9 @@ import torch
 
 import synth
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import (DEV, check_encode, encode_away_from_ties, gpu_packed_arrays, oracle_dequant,
-                      packed_from_oracle, quantizers, rel_l2_per_head, say, to_gpu_x)
+from gpu_util import (DEV, assert_guards, check_encode, encode_away_from_ties, gpu_packed_arrays,
+                      guarded_decoder, guarded_tensor, oracle_dequant, packed_from_oracle, quantizers,
+                      rel_l2_per_head, say, to_gpu_x)
 from oracle import decode_attention
 
 pytestmark = pytest.mark.gpu
@@ -200,9 +201,11 @@ def test_step_matches_oracle():
         if p.qjl is not None:
             p.qjl[sl] = 0
             p.gammas[sl] = 0
-    dec = T.Decoder(B, cfg.Hq, cfg.Hkv, Tc, DEV)
+    dec = guarded_decoder(B, cfg.Hq, cfg.Hkv, Tc)
+    og, og_guard = guarded_tensor((B, cfg.Hq, 128), torch.float32)
     out = dec.step(kq, vq, to_gpu_x(kn, cfg.dtype), to_gpu_x(vn, cfg.dtype), torch.from_numpy(q).to(DEV),
-                   kp, vp, torch.tensor(lens, dtype=torch.int32, device=DEV)).cpu().numpy()
+                   kp, vp, torch.tensor(lens, dtype=torch.int32, device=DEV), out=og).cpu().numpy()
+    assert_guards(dec, og_guard, kp, vp)
     gk, gv = gpu_packed_arrays(kp, kq), gpu_packed_arrays(vp, vq)
     sub = lambda e: {k: v[new_idx] for k, v in e.items()}
     ks = check_encode(sub(gk), sub(ek), cfg.k_bits, cfg.k_variant)
