@@ -27,8 +27,9 @@
  *   - Pointers named "device" must point to HIP device memory (or memory the
  *     GPU can address); "host" pointers to host memory. The caller owns every
  *     buffer; the library never allocates or frees memory and keeps no global
- *     mutable state, so calls on different streams may run concurrently as
- *     long as they do not write the same buffers.
+ *     mutable state (apart from the fixed scratch of tq_attn_decode_noalloc
+ *     and its per-device address), so calls on different streams may run
+ *     concurrently as long as they do not write the same buffers.
  *   - `stream` is a hipStream_t (NULL = the default stream). Launches are
  *     asynchronous on it; a launch failure returns TQ_ERR_HIP, and faults
  *     during execution surface at the caller's next synchronization.
@@ -302,6 +303,35 @@ int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_quantizer* 
                          const float* query, int B, int Hq, int Hkv, const int32_t* ctx_lens,
                          int64_t max_ctx, const tq_packed* k_cache, const tq_packed* v_cache,
                          float scale, float* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of the fixed device scratch tq_attn_decode_noalloc uses as its
+ * workspace (8 MiB: enough for tq_attn_decode_workspace() of batch 64 x 8 KV
+ * heads x 32 query heads at 16K tokens, or batch 4 x 8 x 64 at 128K). */
+#define TQ_STATIC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * tq_attn_decode_noalloc — tq_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same arguments without the workspace, the
+ * same kernels and the same result bit for bit. Its workspace is a fixed
+ * array of TQ_STATIC_SCRATCH_BYTES in the library's code object; each GPU
+ * the library runs on holds its own copy until the process ends (its device
+ * address is looked up on the first call on that GPU). The call allocates
+ * nothing and frees nothing. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * host threads onto streams that are not ordered) race and give undefined
+ * results; calls on one stream are ordered and safe. The array keeps the
+ * last call's contents; nothing in it needs to start at zero.
+ * Errors: as tq_attn_decode; TQ_ERR_WORKSPACE when the shape needs more
+ * than TQ_STATIC_SCRATCH_BYTES (tq_attn_decode_workspace(B, Hq, Hkv,
+ * max_ctx) > TQ_STATIC_SCRATCH_BYTES); TQ_ERR_HIP when no device is current
+ * or the array's address cannot be found; TQ_ERR_UNSUPPORTED on a device
+ * index of 64 or more.
+ */
+int tq_attn_decode_noalloc(const tq_quantizer* kq, const tq_quantizer* vq, const float* query,
+                           int B, int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx,
+                           const tq_packed* k_cache, const tq_packed* v_cache, float scale,
+                           float* out, void* stream);
 
 /*
  * tq_search_workspace — bytes of device workspace tq_search needs for these

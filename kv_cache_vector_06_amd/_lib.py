@@ -31,7 +31,8 @@ TQ_HEAD_DIM = 128
 EXPORTED = ("tq_codebook", "tq_prep_bytes", "tq_prepare", "tq_encode",
             "tq_attn_decode_workspace", "tq_attn_decode", "tq_attn_decode_phase",
             "tq_decode_step", "tq_decode_step_phase", "tq_search_workspace", "tq_search",
-            "tq_read_probe", "tq_status_string")
+            "tq_read_probe", "tq_status_string", "tq_attn_decode_noalloc")
+TQ_STATIC_SCRATCH_BYTES = 8 << 20
 
 
 class TQError(RuntimeError):
@@ -87,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.tq_decode_step.restype = I
     lib.tq_decode_step_phase.argtypes = [I] + lib.tq_decode_step.argtypes
     lib.tq_decode_step_phase.restype = I
+    lib.tq_attn_decode_noalloc.argtypes = lib.tq_attn_decode.argtypes[:12] + [P]
+    lib.tq_attn_decode_noalloc.restype = I
     lib.tq_search_workspace.argtypes = [I, I64, I]
     lib.tq_search_workspace.restype = SZ
     lib.tq_search.argtypes = [ctypes.POINTER(tq_quantizer), P, I, ctypes.POINTER(tq_packed), I64, I, P, P, P, SZ, P]
@@ -155,6 +158,14 @@ def tq_attn_decode_phase(phase: int, kq: tq_quantizer, vq: tq_quantizer, query: 
                                        int(Hq), int(Hkv), ctx_lens, int(max_ctx), ctypes.byref(k_cache),
                                        ctypes.byref(v_cache), float(scale), out, workspace,
                                        int(ws_bytes), stream), "tq_attn_decode_phase")
+
+
+def tq_attn_decode_noalloc(kq: tq_quantizer, vq: tq_quantizer, query: int, B: int, Hq: int, Hkv: int,
+                           ctx_lens: int | None, max_ctx: int, k_cache: tq_packed, v_cache: tq_packed,
+                           scale: float, out: int, stream: int | None) -> None:
+    _check(load().tq_attn_decode_noalloc(ctypes.byref(kq), ctypes.byref(vq), query, int(B), int(Hq), int(Hkv),
+                                         ctx_lens, int(max_ctx), ctypes.byref(k_cache), ctypes.byref(v_cache),
+                                         float(scale), out, stream), "tq_attn_decode_noalloc")
 
 
 def tq_decode_step(kq: tq_quantizer, vq: tq_quantizer, k_new: int, v_new: int, x_dtype: int,

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "tq.h"
 #include "tq_device.h"
 #include "tq_rowtile.h"
@@ -2351,7 +2353,7 @@ RowEncArgs append_args(const tq_quantizer* q, const StepRows& r, const void* x, 
 int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const float* query, int B,
                 int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx, const tq_packed* k_cache,
                 const tq_packed* v_cache, float scale, float* out, void* workspace, size_t ws_bytes,
-                void* stream, const StepRows* step = nullptr) {
+                void* stream, const StepRows* step = nullptr, bool checks_only = false) {
   if (phase < 0 || phase > 3) return TQ_ERR_INVALID_ARG;
   int st = tq_check_quantizer(kq);
   if (st != TQ_OK) return st;
@@ -2386,6 +2388,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   }
   const Plan p = make_plan(B, Hq, Hkv, max_ctx);
   if (ws_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TQ_ERR_WORKSPACE;
+  if (checks_only) return TQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int G = Hq / Hkv;
@@ -2503,6 +2506,56 @@ extern "C" int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_
   const StepRows r{k_new, v_new, x_dtype, x_row_stride};
   return decode_call(phase, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out,
                      workspace, ws_bytes, stream, &r);
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention with a library-owned workspace, for callers that cannot
+// allocate device memory. Its workspace is `scratch`, a fixed array in the
+// code object: every GPU the library runs on holds its own copy until the
+// process ends, and every call on that GPU shares it.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(TQ_STATIC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's `scratch` (in host code the
+// array's name is only a stand-in for it), looked up once per device.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return TQ_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" int tq_attn_decode_noalloc(const tq_quantizer* kq, const tq_quantizer* vq, const float* query,
+                                      int B, int Hq, int Hkv, const int32_t* ctx_lens, int64_t max_ctx,
+                                      const tq_packed* k_cache, const tq_packed* v_cache, float scale,
+                                      float* out, void* stream) {
+  // Every argument check first (a stand-in workspace address, never used),
+  // including the shape's workspace against the scratch's size.
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+  int st = decode_call(0, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out, stand_in,
+                       kStaticScratchBytes, stream, nullptr, true);
+  if (st != TQ_OK) return st;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != TQ_OK) return st;
+  return decode_call(0, kq, vq, query, B, Hq, Hkv, ctx_lens, max_ctx, k_cache, v_cache, scale, out, ws,
+                     kStaticScratchBytes, stream);
 }
 
 extern "C" size_t tq_search_workspace(int nq, int64_t n, int k) {
