@@ -15,7 +15,8 @@ packed cache, so no step finds its cache in the 256 MB last-level cache.
 
 Prints one JSON line.
   * `value`: packed-cache bytes read by decode per step / step time (GB/s),
-    over `--steps` steps after `--warmup` untimed ones. In every timed step
+    over `--steps` steps after `--warmup` untimed ones, right after the encode
+    sweep (prefill-scale encode, then decode steps). In every timed step
     a pair of HIP events brackets the split-attention launch on its stream;
     `roofline` is that kernel's average over the same steps (so it can never
     exceed the step).
@@ -279,6 +280,64 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---- encode sweep (prefill-scale encode), right before the headline decode:
+    # as in serving, where a prompt's keys and values are encoded and decode
+    # steps follow, the chip is already under load when the decode steps start.
+    Rkh, Rvh, _ = synth.hadamard_constants(d)
+    enc = {}
+    enc_roof = enc_roof_prod = None
+    enc_mfma = {}
+    if not args.no_encode_sweep:
+        n_sweep = (1 << 20) * 8
+        xs = torch.cat([kg, vg])[:n_sweep]
+        for label, bits, var, rot in (("mse1", 1, "mse", "dense"), ("mse2", 2, "mse", "dense"),
+                                      ("mse3", 3, "mse", "dense"), ("mse4", 4, "mse", "dense"),
+                                      ("prod4", 4, "prod", "dense"), ("mse4_hadamard", 4, "mse", "hadamard"),
+                                      ("prod4_hadamard", 4, "prod", "hadamard")):
+            qq = TA.Quantizer(Rk if rot == "dense" else Rkh, bits, var, S if var == "prod" else None, dev, rot)
+            pk = TA.Packed(qq, n_sweep, dev)
+            TA.encode(qq, xs, pk)
+            a_, b_ = Event(), Event()
+            reps = 3
+            a_.record()
+            for _ in range(reps):
+                TA.encode(qq, xs, pk)
+            b_.record()
+            torch.cuda.synchronize()
+            ms = a_.elapsed_time(b_) / reps
+            enc[label] = round(n_sweep / (ms * 1e-3) / 1e6, 1)
+            bm = bits - (var == "prod")
+            eb = n_sweep * (2 * d + d * bm // 8 + 4 + ((d // 8 + 4) if var == "prod" else 0))
+            if label in ("mse4", "prod4"):
+                roof = {"kernel": f"encode_kernel<{bm},{var},bf16>", "bound": "hbm",
+                        "achieved": round(eb / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                if label == "mse4":
+                    roof["traffic"] = _traffic("encode_mse4_sweep.counters.json", "tq_encode.hip")
+                    enc_roof = roof
+                else:
+                    enc_roof_prod = roof
+                # Matrix-core use: the algorithmic flops (2d² per vector for the
+                # rotation, 2d² more for the prod sketch) and the flops the
+                # fp16 matrix cores execute with the operands split into hi/lo
+                # parts (rotation 2 passes, sketch 3), against the dense fp16
+                # peak; plus the busy fraction the SQ counters measured.
+                alg = 2 * d * d * (2 if var == "prod" else 1)
+                exe = 2 * d * d * (5 if var == "prod" else 2)
+                rate = n_sweep / (ms * 1e-3)
+                enc_mfma[label] = {"flops_per_vec": alg, "executed_flops_per_vec": exe,
+                                   "tflops": round(rate * alg / 1e12, 1),
+                                   "executed_tflops": round(rate * exe / 1e12, 1), "peak_tflops": PEAK_F16_TFLOPS,
+                                   "frac": round(rate * alg / 1e12 / PEAK_F16_TFLOPS, 4),
+                                   "executed_frac": round(rate * exe / 1e12 / PEAK_F16_TFLOPS, 4),
+                                   "busy_counter": _mfma_busy(f"tq::encode_kernel<{bm}, "
+                                                              f"{'true' if var == 'prod' else 'false'}, false>")}
+            del pk, qq
+            log(f"[bench] encode {label}: {enc[label]} Mvec/s")
+        if enc_roof is not None and enc_roof_prod is not None:
+            enc_roof["prod4"] = enc_roof_prod
+
+
     # ---- headline: the driver's warm-up and step counts ---------------------
     ms_step, k_us = timed_steps(dec, (kq, vq), kcs, vcs, knew, vnew, q, out, args.warmup, args.steps)
     k_avg = sum(k_us) / len(k_us)
@@ -364,7 +423,6 @@ def main():
         f"of 4 GiB: {pr4_us:.1f} us, {read_peak_4g:.0f} GB/s")
 
     # ---- the same step with randomized Walsh-Hadamard rotations --------------
-    Rkh, Rvh, _ = synth.hadamard_constants(d)
     kqh = TA.Quantizer(Rkh, cfg.k_bits, cfg.k_variant, S, dev, "hadamard")
     vqh = TA.Quantizer(Rvh, cfg.v_bits, "mse", None, dev, "hadamard")
     for c in range(ncopy):
@@ -510,60 +568,6 @@ def main():
                 "encode_mvec_s": round(n6 / (enc6_ms * 1e-3) / 1e6, 1)}
             log(f"[bench] {cs.name}: {split_res[cs.name]}")
     del flush
-
-    # ---- encode sweep ---------------------------------------------------------
-    enc = {}
-    enc_roof = enc_roof_prod = None
-    enc_mfma = {}
-    if not args.no_encode_sweep:
-        n_sweep = (1 << 20) * 8
-        xs = torch.cat([kg, vg])[:n_sweep]
-        for label, bits, var, rot in (("mse1", 1, "mse", "dense"), ("mse2", 2, "mse", "dense"),
-                                      ("mse3", 3, "mse", "dense"), ("mse4", 4, "mse", "dense"),
-                                      ("prod4", 4, "prod", "dense"), ("mse4_hadamard", 4, "mse", "hadamard"),
-                                      ("prod4_hadamard", 4, "prod", "hadamard")):
-            qq = TA.Quantizer(Rk if rot == "dense" else Rkh, bits, var, S if var == "prod" else None, dev, rot)
-            pk = TA.Packed(qq, n_sweep, dev)
-            TA.encode(qq, xs, pk)
-            a_, b_ = Event(), Event()
-            reps = 3
-            a_.record()
-            for _ in range(reps):
-                TA.encode(qq, xs, pk)
-            b_.record()
-            torch.cuda.synchronize()
-            ms = a_.elapsed_time(b_) / reps
-            enc[label] = round(n_sweep / (ms * 1e-3) / 1e6, 1)
-            bm = bits - (var == "prod")
-            eb = n_sweep * (2 * d + d * bm // 8 + 4 + ((d // 8 + 4) if var == "prod" else 0))
-            if label in ("mse4", "prod4"):
-                roof = {"kernel": f"encode_kernel<{bm},{var},bf16>", "bound": "hbm",
-                        "achieved": round(eb / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-                if label == "mse4":
-                    roof["traffic"] = _traffic("encode_mse4_sweep.counters.json", "tq_encode.hip")
-                    enc_roof = roof
-                else:
-                    enc_roof_prod = roof
-                # Matrix-core use: the algorithmic flops (2d² per vector for the
-                # rotation, 2d² more for the prod sketch) and the flops the
-                # fp16 matrix cores execute with the operands split into hi/lo
-                # parts (rotation 2 passes, sketch 3), against the dense fp16
-                # peak; plus the busy fraction the SQ counters measured.
-                alg = 2 * d * d * (2 if var == "prod" else 1)
-                exe = 2 * d * d * (5 if var == "prod" else 2)
-                rate = n_sweep / (ms * 1e-3)
-                enc_mfma[label] = {"flops_per_vec": alg, "executed_flops_per_vec": exe,
-                                   "tflops": round(rate * alg / 1e12, 1),
-                                   "executed_tflops": round(rate * exe / 1e12, 1), "peak_tflops": PEAK_F16_TFLOPS,
-                                   "frac": round(rate * alg / 1e12 / PEAK_F16_TFLOPS, 4),
-                                   "executed_frac": round(rate * exe / 1e12 / PEAK_F16_TFLOPS, 4),
-                                   "busy_counter": _mfma_busy(f"tq::encode_kernel<{bm}, "
-                                                              f"{'true' if var == 'prod' else 'false'}, false>")}
-            del pk, qq
-            log(f"[bench] encode {label}: {enc[label]} Mvec/s")
-        if enc_roof is not None and enc_roof_prod is not None:
-            enc_roof["prod4"] = enc_roof_prod
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -305,9 +305,9 @@ int tq_decode_step_phase(int phase, const tq_quantizer* kq, const tq_quantizer* 
                          float scale, float* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Bytes of the fixed device scratch tq_attn_decode_noalloc uses as its
- * workspace (8 MiB: enough for tq_attn_decode_workspace() of batch 64 x 8 KV
+ * workspace (16 MiB: enough for tq_attn_decode_workspace() of batch 64 x 8 KV
  * heads x 32 query heads at 16K tokens, or batch 4 x 8 x 64 at 128K). */
-#define TQ_STATIC_SCRATCH_BYTES (8u << 20)
+#define TQ_STATIC_SCRATCH_BYTES (16u << 20)
 
 /*
  * tq_attn_decode_noalloc — tq_attn_decode for callers that cannot allocate

@@ -32,7 +32,7 @@ EXPORTED = ("tq_codebook", "tq_prep_bytes", "tq_prepare", "tq_encode",
             "tq_attn_decode_workspace", "tq_attn_decode", "tq_attn_decode_phase",
             "tq_decode_step", "tq_decode_step_phase", "tq_search_workspace", "tq_search",
             "tq_read_probe", "tq_status_string", "tq_attn_decode_noalloc")
-TQ_STATIC_SCRATCH_BYTES = 8 << 20
+TQ_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class TQError(RuntimeError):

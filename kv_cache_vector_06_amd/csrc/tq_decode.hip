@@ -52,7 +52,12 @@ constexpr int kBlockTok = 32;            // tokens per wavefront step
 constexpr int kMaxHeads = 8;             // query heads per unit
 constexpr int kPartStride = 132;         // floats per (unit, split, head) partial: M, L, pad, pad, acc[128]
 constexpr int kQFrags = 8;              // q' (hi | lo columns), q_S (hi | lo) × 4 K-steps
-constexpr size_t kUnitBytes = kQFrags * 1024 + 256;  // operand fragments + scales
+// Per unit: the fp16 fragments, the per-head score scales, then the sketch
+// operand of the split kernel's scaled fp4 × fp8 matrix-core products (two
+// products: 64 lanes × 32 fp8 bytes each) and their per-lane E8M0 scales.
+constexpr size_t kSkOff = kQFrags * 1024 + 256;
+constexpr size_t kSkScaleOff = kSkOff + 2 * 64 * 32;
+constexpr size_t kUnitBytes = kSkScaleOff + 2 * 64 * 4;
 constexpr int kTargetGroups = 256;       // split workgroups per launch: one per compute unit
 constexpr int64_t kMaxSplitsPlan = 4096;        // splits per unit (merge keeps one weight each)
 constexpr int64_t kMaxCtx = int64_t(1) << 26;   // tokens per (batch, KV head): 32-bit offsets
@@ -118,6 +123,29 @@ __device__ __forceinline__ void split_pairs(const float (&v)[32], u32x4 (&hi)[4]
       hi[s][k] = uint32_t(h0) | (uint32_t(h1) << 16);
       lo[s][k] = uint32_t(l0) | (uint32_t(l1) << 16);
     }
+}
+
+// OCP fp8 E4M3 (bias 7) of a finite y with |y| < 448, rounded to nearest
+// even, and the value of a code. Prep-time only.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t sgn = y < 0.f ? 0x80u : 0u;
+  const float a = fabsf(y);
+  if (a < 0x1p-6f) return sgn | static_cast<uint32_t>(rintf(a * 512.0f));   // subnormals: units of 2^-9
+  int e;
+  const float m = frexpf(a, &e);                                             // a = 2m·2^(e-1), 2m in [1, 2)
+  uint32_t q = static_cast<uint32_t>(rintf((2.0f * m - 1.0f) * 8.0f));
+  int ex = e - 1;
+  if (q == 8u) {
+    q = 0u;
+    ++ex;
+  }
+  return sgn | (static_cast<uint32_t>(ex + 7) << 3) | q;
+}
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t ef = (c >> 3) & 15u, mf = c & 7u;
+  const float mag = ef ? ldexpf(1.0f + 0.125f * static_cast<float>(mf), static_cast<int>(ef) - 7)
+                       : 0x1p-9f * static_cast<float>(mf);
+  return (c & 0x80u) ? -mag : mag;
 }
 
 // Four values of one column into the two dwords of fp16 pairs (v0, v1),
@@ -264,6 +292,55 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
   reinterpret_cast<u32x2*>(fr + (t >> 1) * 64 + lane)[t & 1] = hilo_pairs(qp, scl, n < 8);
   reinterpret_cast<u32x2*>(fr + (4 + (t >> 1)) * 64 + lane)[t & 1] = hilo_pairs(qs, scl, n < 8);
   if (t == 0 && g == 0 && n < kMaxHeads) reinterpret_cast<float*>(blk + kQFrags * 1024)[n] = live ? 1.0f / scl : 0.f;
+  if (prod) {
+    // The split kernel's sketch product runs on the scaled fp4 × fp8 matrix
+    // cores: its A operand holds -s (fp4 ±1 straight from the sketch bits),
+    // so the B operand holds v = -q_S·scl, split into four fp8 parts of four
+    // significant bits; part p of (head, 32-coordinate block) is scaled by
+    // 2^(S1 - 4p), S1 putting the block's max|v| in [2^7, 2^8). Product 0
+    // takes parts 0 (columns 0..7) and 1 (8..15), product 1 parts 2 and 3,
+    // so the two products accumulate into columns h and h + 8 like the fp16
+    // hi/lo operands. Operand layout (gfx950, 16x16x128): K index k of
+    // column c sits in lane c + 16·((k mod 64) / 16), byte (k mod 16) +
+    // 16·(k / 64); the E8M0 scale of (column c, block b = k / 32) in lane
+    // c + 16b. Coordinate 32g + 4n + m of the sign operand is K index
+    // 32g + 8m + n, so this wavefront's coordinate 32g + 4t + j is 32g + 8j + t.
+    float v[4], vm = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = -qs[j] * scl;
+      vm = fmaxf(vm, fabsf(v[j]));
+    }
+    X.bmax[t][lane] = vm;
+    __syncthreads();
+    float M = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) M = fmaxf(M, X.bmax[tt][lane]);
+    int e = 0;
+    if (M > 0.f) frexpf(M, &e);
+    const int S1 = M > 0.f ? max(e - 8, -100) : 0;
+    uint8_t* sk = blk + kSkOff;
+    const int odd = n >= 8 ? 1 : 0;      // this lane's column takes the odd parts
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int S = S1 - 4 * p;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t code = e4m3_rne(ldexpf(v[j], -S));
+        v[j] -= ldexpf(e4m3_value(code), S);
+        if ((p & 1) == odd) {
+          const int k = 32 * g + 8 * j + t;
+          const int lb = n + 16 * ((k & 63) >> 4);
+          sk[(p >> 1) * 2048 + lb * 32 + (k & 15) + 16 * (k >> 6)] = static_cast<uint8_t>(code);
+        }
+      }
+    }
+    if (t == 0) {
+      uint32_t* sc = reinterpret_cast<uint32_t*>(blk + kSkScaleOff);
+      sc[lane] = static_cast<uint32_t>(127 + S1 - 4 * odd);            // product 0: part odd
+      sc[64 + lane] = static_cast<uint32_t>(127 + S1 - 4 * (2 + odd));  // product 1: part 2 + odd
+    }
+  }
 }
 
 __global__ __launch_bounds__(kRowWaves * 64) void query_prep_kernel(PrepArgs a) {
@@ -316,14 +393,11 @@ struct AttnArgs {
 
 // W bits at compile-time bit offset OFF of a little-endian word array,
 // returned shifted left by SH. The extract is one v_bfe_u32 (an alignbit
-// first when the field straddles two words), written as asm so that it is not
-// split into a shift and a mask; the shift then folds into the address add
-// (v_lshl_add_u32): two operations per table address.
+// first when the field straddles two words); the shift then folds into the
+// address add (v_lshl_add_u32): two operations per table address.
 template <int OFF, int W>
 __device__ __forceinline__ uint32_t bfe_u32(uint32_t x) {
-  uint32_t r;
-  asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "n"(OFF), "n"(W));
-  return r;
+  return __builtin_amdgcn_ubfe(x, OFF, W);
 }
 
 template <int OFF, int W, int SH, int N>
@@ -849,109 +923,6 @@ __device__ __forceinline__ void block_scores(const Block<BK, PROD, BV>& R, const
   }
 }
 
-template <int BK, bool PROD, int BV>
-__device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint32_t t0, uint32_t t_end,
-                                             int n, int g, const Luts& T, const u32x4 (&bq)[4],
-                                             const u32x4 (&bs)[4], float iqs, uint32_t lomask,
-                                             SoftmaxState& st, f32x4 (&acc)[8]) {
-  // Value codes regrouped for the pair-table addresses.
-  uint32_t X[4], Y[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t a0, a1;
-    if constexpr (BV == 3) {
-      const int off = (24 * n) & 31;
-      a0 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k], R.vw[2 * k], off));
-      a1 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k + 1], R.vw[2 * k + 1], off));
-    } else if constexpr (BV == 2) {
-      a0 = to_nibbles<2>(R.vw[2 * k] >> (16 * (n & 1)));
-      a1 = to_nibbles<2>(R.vw[2 * k + 1] >> (16 * (n & 1)));
-    } else if constexpr (BV == 1) {
-      a0 = to_nibbles<1>(R.vw[2 * k] >> (8 * (n & 3)));
-      a1 = to_nibbles<1>(R.vw[2 * k + 1] >> (8 * (n & 3)));
-    } else {
-      a0 = R.vw[2 * k];
-      a1 = R.vw[2 * k + 1];
-    }
-    // byte q of X: (slot 2k, slot 2k+1) codes of dim 8n + 2q; of Y: dim 8n + 2q + 1
-    X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
-    Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
-  }
-  float sc[8];
-  block_scores<BK, PROD, BV>(R, T, bq, bs, sc);
-  // ---- P·V operands: column n = dim 8n + r, rows = token slots ----
-  u32x4 bv[8];
-  bv[0] = pv_operand<0>(X, Y, T);
-  bv[1] = pv_operand<1>(X, Y, T);
-  bv[2] = pv_operand<2>(X, Y, T);
-  bv[3] = pv_operand<3>(X, Y, T);
-  bv[4] = pv_operand<4>(X, Y, T);
-  bv[5] = pv_operand<5>(X, Y, T);
-  bv[6] = pv_operand<6>(X, Y, T);
-  bv[7] = pv_operand<7>(X, Y, T);
-  float nv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) nv[j] = R.nv[j];
-  if (__builtin_expect(t0 + kBlockTok > t_end, 0)) {   // last block of the range: mask
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = t0 + 16 * (j >> 2) + 4 * g + (j & 3) < t_end;
-      sc[j] = ok ? sc[j] : -INFINITY;
-      nv[j] = ok ? nv[j] : 0.f;
-    }
-  }
-
-  // ---- online softmax (log2 domain), lazily rescaled ----------------------
-  const float mloc = max8f(sc) * iqs;
-  const float nvl = max8f(nv);
-  if (__builtin_expect(__any(mloc > st.m + kLazy || nvl > st.nvs), 0)) {
-    const float mg = max4g(mloc);           // this block's max for the head
-    const float nvw = max4g(nvl);           // this block's max value norm (every lane)
-    const float m_new = mg > st.m + kLazy ? mg : st.m;
-    float nvs_new = st.nvs, knv_new = st.knv;
-    if (nvw > st.nvs) {
-      int e;
-      frexpf(nvw, &e);                      // nvw < 2^e
-      nvs_new = ldexpf(1.0f, e + 1);
-      knv_new = static_cast<float>(e + 1);
-    }
-    const float mk_new = m_new + knv_new;
-    const float f = st.mk == -INFINITY ? 0.f : exp2f(st.mk - mk_new);
-    st.l *= f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float fi = __shfl(f, (4 * g + i) & 7, 64);   // row 4g+i holds head (4g+i)%8
-#pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
-    }
-    st.m = m_new;
-    st.mk = mk_new;
-    st.nvs = nvs_new;
-    st.knv = knv_new;
-  }
-  // A operand of P·V: row n < 8 carries the fp16 hi part of head n's weights,
-  // row n + 8 the lo part (the weight minus its value truncated to fp16
-  // precision); rows h and h + 8 of the result are summed at the end.
-  u32x4 pa;
-  const float nmk = -st.mk;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float x[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * k + e], iqs, nmk));
-      st.l += p;
-      const float w = p * nv[2 * k + e];
-      x[e] = w - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, w) & lomask);
-    }
-    pa[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[0], x[1]));
-  }
-
-  // ---- P·V -------------------------------------------------------------------
-#pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = mfma(pa, bv[r], acc[r]);
-}
-
 // LDS stores for the table build, written as asm: the compiler would make a
 // plain LDS store wait for every direct-to-LDS load in flight (it cannot tell
 // the tables from the stage ring), and the first blocks' loads are issued
@@ -1096,13 +1067,333 @@ __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, f
   }
 }
 
+// read_block for the split-attention kernel: the key and value norms of the
+// lane's own tile only (own_off = 0 for tile 0, 64 bytes for tile 1), γ of
+// both tiles, and everything else as read_block.
+#define TQ_VMW "s_waitcnt vmcnt(%[pend])\n\tds_read_b32 %[pw], %[ap]\n\t"
+#define TQ_NORMS "ds_read_b128 %[n0], %[ao]\n\t"
+#define TQ_VNORMS "ds_read_b128 %[n2], %[ao] offset:128\n\t"
+#define TQ_GAMMA "ds_read_b128 %[n4], %[an] offset:256\n\tds_read_b128 %[n5], %[an] offset:320\n\t"
+#define TQ_QJ "ds_read2_b32 %[q0], %[aq] offset1:64\n\t"
+#define TQ_LGK "s_waitcnt lgkmcnt(0)"
+
+template <int BK, bool PROD, int BV, int PEND>
+__device__ __forceinline__ void read_block_own(Block<BK, PROD, BV>& R, uint32_t sb, const StageOffsets& o, uint32_t own_off,
+                                               uint32_t ap, uint32_t& pw) {
+  const uint32_t an = sb + o.n, ao = an + own_off, ak = sb + o.k, aq = sb + o.q, av0 = sb + o.v0, av1 = sb + o.v1;
+  f32x4 n0, n2, n4, n5;
+  u32x2 q0, v0, v1, v2, v3, v4, v5, v6, v7;
+  u32x4 ka, kb;         // key words: BK = 4 (two tiles), BK = 2 (both tiles)
+  u32x2 k0, k1, k2;     // key words: BK = 3 (word pairs), BK = 1
+  // One asm statement per layout: the wait for the block's loads, every read
+  // of the stage (norms, γ, sketch, value and key codes), then the wait for
+  // the reads, so no output is used early.
+#define TQ_VPAIRS(A, B, C)                                                                          \
+  "ds_read2_b32 %[v0], %[av0] offset1:" #A "\n\tds_read2_b32 %[v1], %[av0] offset0:" #B " offset1:" #C "\n\t" \
+  "ds_read2_b32 %[v2], %[av1] offset1:" #A "\n\tds_read2_b32 %[v3], %[av1] offset0:" #B " offset1:" #C "\n\t"
+#define TQ_VPAIRS3                                                                                   \
+  "ds_read2_b32 %[v0], %[av0] offset1:1\n\tds_read2_b32 %[v1], %[av0] offset0:48 offset1:49\n\t"     \
+  "ds_read2_b32 %[v2], %[av0] offset0:96 offset1:97\n\tds_read2_b32 %[v3], %[av0] offset0:144 offset1:145\n\t" \
+  "ds_read2_b32 %[v4], %[av1] offset1:1\n\tds_read2_b32 %[v5], %[av1] offset0:48 offset1:49\n\t"     \
+  "ds_read2_b32 %[v6], %[av1] offset0:96 offset1:97\n\tds_read2_b32 %[v7], %[av1] offset0:144 offset1:145\n\t"
+#define TQ_KR4 "ds_read_b128 %[ka], %[ak]\n\tds_read_b128 %[kb], %[ak] offset:1024\n\t"
+#define TQ_KR3 "ds_read2_b32 %[k0], %[ak] offset1:192\n\tds_read2_b32 %[k1], %[ak] offset0:1 offset1:193\n\t" \
+               "ds_read2_b32 %[k2], %[ak] offset0:2 offset1:194\n\t"
+#define TQ_KR2 "ds_read2_b64 %[ka], %[ak] offset1:64\n\t"
+#define TQ_KR1 "ds_read2_b32 %[k0], %[ak] offset1:64\n\t"
+#define TQ_KR0 ""
+#define TQ_KO4 , [ka] "=&v"(ka), [kb] "=&v"(kb)
+#define TQ_KO3 , [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2)
+#define TQ_KO2 , [ka] "=&v"(ka)
+#define TQ_KO1 , [k0] "=&v"(k0)
+#define TQ_KO0
+#define TQ_OUT2 [n0] "=&v"(n0), [pw] "=&v"(pw)
+#define TQ_NO3 , [n2] "=&v"(n2)
+#define TQ_NON TQ_NO3
+#define TQ_NO0
+#define TQ_NR3 TQ_VNORMS
+#define TQ_NRN TQ_VNORMS
+#define TQ_NR0 ""
+#define TQ_VO3 , [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3), \
+               [v4] "=&v"(v4), [v5] "=&v"(v5), [v6] "=&v"(v6), [v7] "=&v"(v7)
+#define TQ_VON , [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3)
+#define TQ_VO0
+#define TQ_OUTP , [n4] "=&v"(n4), [n5] "=&v"(n5), [q0] "=&v"(q0)
+#define TQ_IN [pend] "n"(PEND), [ap] "v"(ap), [an] "v"(an), [ao] "v"(ao), [aq] "v"(aq), [av0] "v"(av0), [av1] "v"(av1), [ak] "v"(ak)
+#define TQ_K(VP, VS, KB)                                                                           \
+  if constexpr (BK == KB) {                                                                        \
+    if constexpr (PROD)                                                                            \
+      asm volatile(TQ_VMW TQ_NORMS TQ_NR##VS TQ_GAMMA TQ_QJ VP TQ_KR##KB TQ_LGK                    \
+                   : TQ_OUT2 TQ_NO##VS TQ_VO##VS TQ_OUTP TQ_KO##KB : TQ_IN : "memory");            \
+    else                                                                                           \
+      asm volatile(TQ_VMW TQ_NORMS TQ_NR##VS VP TQ_KR##KB TQ_LGK                                   \
+                   : TQ_OUT2 TQ_NO##VS TQ_VO##VS TQ_KO##KB : TQ_IN : "memory");                    \
+  }
+#define TQ_V(VP, VS) TQ_K(VP, VS, 0) TQ_K(VP, VS, 1) TQ_K(VP, VS, 2) TQ_K(VP, VS, 3) TQ_K(VP, VS, 4)
+  // slot i is 4 rows (16·BV dwords) after slot i-1; pairs (0, 1) and (2, 3) of each tile
+  if constexpr (BV == 3) { TQ_V(TQ_VPAIRS3, 3) }
+  if constexpr (BV == 4) { TQ_V(TQ_VPAIRS(64, 128, 192), N) }
+  if constexpr (BV == 2) { TQ_V(TQ_VPAIRS(32, 64, 96), N) }
+  if constexpr (BV == 1) { TQ_V(TQ_VPAIRS(16, 32, 48), N) }
+  if constexpr (BV == 0) { TQ_V("", 0) }
+#undef TQ_V
+#undef TQ_K
+#undef TQ_VPAIRS
+#undef TQ_VPAIRS3
+#undef TQ_KR4
+#undef TQ_KR3
+#undef TQ_KR2
+#undef TQ_KR1
+#undef TQ_KR0
+#undef TQ_KO4
+#undef TQ_KO3
+#undef TQ_KO2
+#undef TQ_KO1
+#undef TQ_KO0
+#undef TQ_OUT2
+#undef TQ_NO3
+#undef TQ_NON
+#undef TQ_NO0
+#undef TQ_NR3
+#undef TQ_NRN
+#undef TQ_NR0
+#undef TQ_VO3
+#undef TQ_VON
+#undef TQ_VO0
+#undef TQ_OUTP
+#undef TQ_IN
+  if constexpr (BK == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { R.kw[0][k] = ka[k]; R.kw[1][k] = kb[k]; }
+  } else if constexpr (BK == 3) {
+    R.kw[0][0] = k0[0]; R.kw[1][0] = k0[1];
+    R.kw[0][1] = k1[0]; R.kw[1][1] = k1[1];
+    R.kw[0][2] = k2[0]; R.kw[1][2] = k2[1];
+  } else if constexpr (BK == 2) {
+    R.kw[0][0] = ka[0]; R.kw[0][1] = ka[1]; R.kw[1][0] = ka[2]; R.kw[1][1] = ka[3];
+  } else if constexpr (BK == 1) {
+    R.kw[0][0] = k0[0]; R.kw[1][0] = k0[1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    R.nk[i] = n0[i];
+    if constexpr (BV > 0) R.nv[i] = n2[i];
+    if constexpr (PROD) { R.gk[i] = n4[i]; R.gk[4 + i] = n5[i]; }
+  }
+  if constexpr (PROD) { R.qw[0] = q0[0]; R.qw[1] = q0[1]; }
+  if constexpr (BV == 3) {
+    const u32x2 vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { R.vw[j] = vv[j][0]; R.vw2[j] = vv[j][1]; }
+  } else if constexpr (BV > 0) {
+    const u32x2 vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { R.vw[2 * k] = vv[k][0]; R.vw[2 * k + 1] = vv[k][1]; }
+  }
+}
+#undef TQ_VMW
+#undef TQ_NORMS
+#undef TQ_VNORMS
+#undef TQ_GAMMA
+#undef TQ_QJ
+#undef TQ_LGK
+
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Sign operand of a sketch word for the scaled fp4 products: nibble m·8 + c
+// (dword m, nibble c) holds coordinate 4c + m of the word as fp4 0x2 | bit<<3:
+// -1 for a set bit, +1 otherwise, i.e. -s (the query operand holds -q_S).
+__device__ __forceinline__ i32x8 sign_operand4(uint32_t w) {
+  // ((w << k) | 0x2...2) & 0xA...A: one shift-or and one and per dword
+  constexpr uint32_t kOne = 0x22222222u, kKeep = 0xAAAAAAAAu;
+  i32x8 v;
+  v[0] = static_cast<int32_t>(((w << 3) | kOne) & kKeep);
+  v[1] = static_cast<int32_t>(((w << 2) | kOne) & kKeep);
+  v[2] = static_cast<int32_t>(((w << 1) | kOne) & kKeep);
+  v[3] = static_cast<int32_t>((w | kOne) & kKeep);
+  v[4] = v[5] = v[6] = v[7] = 0;
+  return v;
+}
+
+// The value of lane n ^ 8 (row rotation by 8 within each 16-lane row).
+__device__ __forceinline__ float ror8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float max4f(float a, float b, float c, float d) { return fmaxf(fmaxf(a, b), fmaxf(c, d)); }
+
+// Weights are formed as 2^(s - mk)·n_v·(1 + 2^-11) and converted to fp16 by
+// one round-toward-zero packed conversion: the factor makes the conversion
+// round to the nearer of the two neighbours (ties up) instead of toward zero.
+constexpr float kRoundUp = 1.0f + 0x1p-11f;
+
+template <int BK, bool PROD, int BV>
+__device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint32_t t0, uint32_t t_end, int n, int g,
+                                             bool own1, const Luts& T, const u32x4 (&bq)[4], const i32x8 (&bs)[2],
+                                             int ssc0, int ssc1, float iqs, SoftmaxState& st, f32x4 (&acc)[8]) {
+  // Value codes regrouped for the pair-table addresses: byte q of X holds
+  // the codes of slots (2k, 2k+1) for dim 8n + 2q, of Y for dim 8n + 2q + 1.
+  uint32_t X[4], Y[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t a0, a1;
+    if constexpr (BV == 3) {
+      const int off = (24 * n) & 31;
+      a0 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k], R.vw[2 * k], off));
+      a1 = to_nibbles<3>(__builtin_amdgcn_alignbit(R.vw2[2 * k + 1], R.vw[2 * k + 1], off));
+    } else if constexpr (BV == 2) {
+      a0 = to_nibbles<2>(R.vw[2 * k] >> (16 * (n & 1)));
+      a1 = to_nibbles<2>(R.vw[2 * k + 1] >> (16 * (n & 1)));
+    } else if constexpr (BV == 1) {
+      a0 = to_nibbles<1>(R.vw[2 * k] >> (8 * (n & 3)));
+      a1 = to_nibbles<1>(R.vw[2 * k + 1] >> (8 * (n & 3)));
+    } else {
+      a0 = R.vw[2 * k];
+      a1 = R.vw[2 * k + 1];
+    }
+    X[k] = ((a1 << 4) & 0xf0f0f0f0u) | (a0 & 0x0f0f0f0fu);
+    Y[k] = (a1 & 0xf0f0f0f0u) | ((a0 >> 4) & 0x0f0f0f0fu);
+  }
+  // ---- scores: every key-table read of both tiles goes out before the
+  // first product, every product before the first use of a result
+  u32x4 kh[2][4], kl[2][4];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    if constexpr (BK > 0) {
+      key_operands<BK, 0>(R.kw[tau], T.k, T.klane, kh[tau][0], kl[tau][0]);
+      key_operands<BK, 1>(R.kw[tau], T.k, T.klane, kh[tau][1], kl[tau][1]);
+      key_operands<BK, 2>(R.kw[tau], T.k, T.klane, kh[tau][2], kl[tau][2]);
+      key_operands<BK, 3>(R.kw[tau], T.k, T.klane, kh[tau][3], kl[tau][3]);
+    }
+  }
+  i32x8 sa[2];
+  if constexpr (PROD) {
+    sa[0] = sign_operand4(R.qw[0]);
+    sa[1] = sign_operand4(R.qw[1]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 dm[2], dq[2];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    dm[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BK > 0) {
+#pragma unroll
+      for (int S = 0; S < 4; ++S) {
+        dm[tau] = mfma(kh[tau][S], bq[S], dm[tau]);
+        if constexpr (BK == 4) dm[tau] = mfma(kl[tau][S], bq[S], dm[tau]);
+      }
+    }
+  }
+  if constexpr (PROD) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      dq[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dq[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[tau], bs[0], dq[tau], 4, 0, 0, 127, 0, ssc0);
+      dq[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[tau], bs[1], dq[tau], 4, 0, 0, 127, 0, ssc1);
+    }
+  }
+  // ---- P·V operands (column n = dim 8n + r, rows = token slots): their
+  // table reads run while the products finish
+  u32x4 bv[8];
+  bv[0] = pv_operand<0>(X, Y, T);
+  bv[1] = pv_operand<1>(X, Y, T);
+  bv[2] = pv_operand<2>(X, Y, T);
+  bv[3] = pv_operand<3>(X, Y, T);
+  bv[4] = pv_operand<4>(X, Y, T);
+  bv[5] = pv_operand<5>(X, Y, T);
+  bv[6] = pv_operand<6>(X, Y, T);
+  bv[7] = pv_operand<7>(X, Y, T);
+  float br[2][4];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (PROD)
+        br[tau][i] = fmaf(R.gk[4 * tau + i], dq[tau][i], dm[tau][i]);
+      else
+        br[tau][i] = dm[tau][i];
+    }
+  // Columns h and h + 8 hold the two halves of head h's score (the query's
+  // hi and lo parts); lane n takes the full scores of its own tile (tile 0
+  // for n < 8, tile 1 for n >= 8) and hands the other tile's half over.
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float own = own1 ? br[1][i] : br[0][i];
+    const float oth = own1 ? br[0][i] : br[1][i];
+    sc[i] = (own + ror8(oth)) * R.nk[i];     // the score is sc·iqs
+  }
+  float nv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nv[i] = R.nv[i];
+  if (__builtin_expect(t0 + kBlockTok > t_end, 0)) {   // last block of the range: mask
+    const uint32_t tb = t0 + (own1 ? 16u : 0u) + 4u * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = tb + i < t_end;
+      sc[i] = ok ? sc[i] : -INFINITY;
+      nv[i] = ok ? nv[i] : 0.f;
+    }
+  }
+
+  // ---- online softmax (log2 domain), lazily rescaled; lanes n and n ^ 8
+  // (the two tiles of head n % 8) share one state ------------------------------
+  const float mloc = max4f(sc[0], sc[1], sc[2], sc[3]) * iqs;
+  const float nvl = max4f(nv[0], nv[1], nv[2], nv[3]);
+  if (__builtin_expect(__any(mloc > st.m + kLazy || nvl > st.nvs), 0)) {
+    float mg = max4g(mloc);
+    mg = fmaxf(mg, ror8(mg));               // this block's max for the head
+    float nvw = max4g(nvl);
+    nvw = fmaxf(nvw, ror8(nvw));            // and of the value norms (every lane)
+    const float m_new = mg > st.m + kLazy ? mg : st.m;
+    float nvs_new = st.nvs, knv_new = st.knv;
+    if (nvw > st.nvs) {
+      int e;
+      frexpf(nvw, &e);                      // nvw < 2^e
+      nvs_new = ldexpf(1.0f, e + 1);
+      knv_new = static_cast<float>(e + 1);
+    }
+    const float mk_new = m_new + knv_new;
+    const float f = st.mk == -INFINITY ? 0.f : exp2f(st.mk - mk_new);
+    st.l *= f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float fi = __shfl(f, (4 * g + i) & 7, 64);   // row 4g+i holds head (4g+i)%8
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
+    }
+    st.m = m_new;
+    st.mk = mk_new;
+    st.nvs = nvs_new;
+    st.knv = knv_new;
+  }
+  // A operand of P·V: row n < 8 carries head n's weights of tile 0 (slots
+  // 0..3 of each lane group), row n + 8 those of tile 1 (slots 4..7); rows h
+  // and h + 8 of the result are summed at the end.
+  const float nmk = -st.mk;
+  float w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], iqs, nmk));
+    st.l += p;
+    w[i] = p * (nv[i] * kRoundUp);
+  }
+  const uint32_t x0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
+  const uint32_t x1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[2], w[3]));
+  const u32x4 pa = own1 ? u32x4{0u, 0u, x0, x1} : u32x4{x0, x1, 0u, 0u};
+
+  // ---- P·V -------------------------------------------------------------------
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = mfma(pa, bv[r], acc[r]);
+}
+
 template <int BK, bool PROD, int BV, bool AL>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) {
   using SL = Stage<BK, PROD, BV>;
   using KL = KLut<BK>;
   __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
-  __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
   __shared__ float wm[kDecWaves][kMaxHeads], wl[kDecWaves][kMaxHeads];
   __shared__ uint32_t prog[kDecWaves];   // blocks started per wavefront (issue balance)
   // Per wavefront: the stage ring, large enough to hold the 16 x 128 fp32
@@ -1114,6 +1405,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar token ranges
   const int n = lane & 15, g = lane >> 4;
+  const bool own1 = n >= 8;                 // the lane's own tile: tokens 16..31 of each block
   const int split = blockIdx.x, unit = blockIdx.y;
   const int grp = unit % a.ngroups;
   const int kvh = (unit / a.ngroups) % a.Hkv;
@@ -1148,17 +1440,25 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const float vsig = scalar_load(&a.vh->sigma), ksig = BK > 0 ? scalar_load(&a.kh->sigma) : 0.f;
   const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bq[4], bs[4];
+  u32x4 bq[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bq[s] = fr[s * 64 + lane];
-    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
+  for (int s = 0; s < 4; ++s) bq[s] = fr[s * 64 + lane];
+  i32x8 bs[2];
+  int ssc0 = 127, ssc1 = 127;
+  if constexpr (PROD) {
+    const i32x8* sk = reinterpret_cast<const i32x8*>(blk + kSkOff);
+    bs[0] = sk[lane];
+    bs[1] = sk[64 + lane];
+    const int32_t* ss = reinterpret_cast<const int32_t*>(blk + kSkScaleOff);
+    ssc0 = ss[lane];
+    ssc1 = ss[64 + lane];
   }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   asm volatile("" ::: "memory");   // the loads above go out before the blocks' loads
   uint8_t* ring = &stage[wave][0];
   const uint32_t ring_addr = lds_addr(ring);
   const StageOffsets so = stage_offsets<BK, PROD, BV>(n, g);
+  const uint32_t own_off = own1 ? 64u : 0u;
   const DmaLane dl = dma_lane<BK, BV>(lane);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
   if (nblk > 0)
@@ -1167,18 +1467,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, vc, kn, vn, kg);
 
   // ---- lookup tables ---------------------------------------------------------
-  build_tables<BK, PROD, BV>(vcl, kcl, vsig, ksig, tab, lut_k, lut_q, tid, nthr);
+  build_tables<BK, false, BV>(vcl, kcl, vsig, ksig, tab, lut_k, nullptr, tid, nthr);
   if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
   lds_stores_done();
   Luts T;
   const uint32_t cp = lane & 31;            // private copy of this lane
   T.k = KL::priv ? tab : lut_k;
-  T.q = lut_q;
+  T.q = nullptr;
   T.v = tab;
   T.klane = KL::byte_indexed ? kTabK + 8u * (lane & 15) : KL::priv ? kTabK + 4u * cp : 0u;
-  T.qlane = 8u * cp;
+  T.qlane = 0u;
   T.vlane = 4u * cp;
-  const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
   tables_barrier();
 
   SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
@@ -1202,9 +1501,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     lds_put1(prog_own, i);
     uint32_t pw;
     if (i + 1 < nblk)
-      read_block<BK, PROD, BV, SL::dma>(R, sb, so, prog_partner, pw);
+      read_block_own<BK, PROD, BV, SL::dma>(R, sb, so, own_off, prog_partner, pw);
     else
-      read_block<BK, PROD, BV, 0>(R, sb, so, prog_partner, pw);
+      read_block_own<BK, PROD, BV, 0>(R, sb, so, own_off, prog_partner, pw);
     if (__builtin_amdgcn_readfirstlane(pw) < i)
       __builtin_amdgcn_s_setprio(0);
     else
@@ -1216,11 +1515,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
       stage_block<BK, PROD, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, dl, kc, kq, vc, kn,
                                     vn, kg);
     }
-    attend_block<BK, PROD, BV>(R, t0, t_end, n, g, T, bq, bs, iqs, lomask, st, acc);
+    attend_block<BK, PROD, BV>(R, t0, t_end, n, g, own1, T, bq, bs, ssc0, ssc1, iqs, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
   }
   __builtin_amdgcn_s_setprio(0);
-  const float l_run = sum4g(st.l);
+  float l_run = sum4g(st.l);
+  l_run += ror8(l_run);                     // both tiles of the head
 
   // ---- merge the workgroup's wavefronts ------------------------------------
   if (g == 0 && n < kMaxHeads) {
@@ -1228,8 +1528,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     wl[wave][n] = l_run;
   }
   // The wavefront's stage ring is free now (its last read waited for every
-  // load): reuse it for its accumulator (rows 0..7: hi-weight parts of heads
-  // 0..7, rows 8..15: lo-weight parts).
+  // load): reuse it for its accumulator (rows 0..7: heads 0..7 over the
+  // blocks' tokens 0..15, rows 8..15: over tokens 16..31).
   float* wacc_own = reinterpret_cast<float*>(&stage[wave][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -2303,6 +2603,7 @@ hipError_t launch_attn_bv(const AttnArgs& a, int bv, bool al, dim3 grid, hipStre
     default: return launch_attn_t<BK, PROD, 4>(a, al, grid, st);
   }
 }
+
 
 }  // namespace tq
 

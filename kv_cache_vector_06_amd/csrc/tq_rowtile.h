@@ -24,13 +24,14 @@ namespace tq {
 
 constexpr int kRowWaves = 8;   // one wavefront per output row tile
 
-// LDS exchange area of a row-tile workgroup (21.5 KiB).
+// LDS exchange area of a row-tile workgroup (23.5 KiB).
 struct RowXchg {
   u32x2 b[2][8][64];      // fp16 hi (0) / lo (1) B-operand dwords from row tile t
   float racc[8][4][64];   // S·(y - c) of row tile t, element j
   uint32_t piece[8][64];  // code bits of row tile t
   uint32_t sbits[8][64];  // sketch bits of row tile t
   float red[2][8][16];    // per-(row tile, column) maxima, two rounds
+  float bmax[8][64];      // per-(row tile, lane) maxima (query prep: sketch operand blocks)
 };
 
 struct RowEncArgs {
