@@ -191,9 +191,13 @@ def main():
     ap.add_argument("--no-encode-sweep", action="store_true")
     ap.add_argument("--no-split", action="store_true", help="skip the outlier-channel split workloads")
     ap.add_argument("--no-configs", action="store_true", help="skip the other decode workloads")
+    ap.add_argument("--quick", action="store_true",
+                    help="the encode sweep and the headline steps only (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 512 MiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
+    if args.quick:
+        args.no_cpu_baseline = args.no_split = args.no_configs = True
     if args.gpus != 1:
         print("bench.py: this hot path runs on one GPU only (no multi-GPU path is built); "
               "use --gpus 1", file=sys.stderr)
@@ -283,6 +287,9 @@ def main():
     # ---- encode sweep (prefill-scale encode), right before the headline decode:
     # as in serving, where a prompt's keys and values are encoded and decode
     # steps follow, the chip is already under load when the decode steps start.
+    # The quantizers and outputs are made first; then every configuration's
+    # encodes run back to back (one untimed, then three between a pair of
+    # events), with a single synchronization at the end.
     Rkh, Rvh, _ = synth.hadamard_constants(d)
     enc = {}
     enc_roof = enc_roof_prod = None
@@ -290,20 +297,23 @@ def main():
     if not args.no_encode_sweep:
         n_sweep = (1 << 20) * 8
         xs = torch.cat([kg, vg])[:n_sweep]
+        sweep = []
         for label, bits, var, rot in (("mse1", 1, "mse", "dense"), ("mse2", 2, "mse", "dense"),
                                       ("mse3", 3, "mse", "dense"), ("mse4", 4, "mse", "dense"),
                                       ("prod4", 4, "prod", "dense"), ("mse4_hadamard", 4, "mse", "hadamard"),
                                       ("prod4_hadamard", 4, "prod", "hadamard")):
             qq = TA.Quantizer(Rk if rot == "dense" else Rkh, bits, var, S if var == "prod" else None, dev, rot)
-            pk = TA.Packed(qq, n_sweep, dev)
+            sweep.append((label, bits, var, qq, TA.Packed(qq, n_sweep, dev), Event(), Event()))
+        torch.cuda.synchronize()
+        reps = 3
+        for label, bits, var, qq, pk, a_, b_ in sweep:
             TA.encode(qq, xs, pk)
-            a_, b_ = Event(), Event()
-            reps = 3
             a_.record()
             for _ in range(reps):
                 TA.encode(qq, xs, pk)
             b_.record()
-            torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        for label, bits, var, qq, pk, a_, b_ in sweep:
             ms = a_.elapsed_time(b_) / reps
             enc[label] = round(n_sweep / (ms * 1e-3) / 1e6, 1)
             bm = bits - (var == "prod")
@@ -332,11 +342,9 @@ def main():
                                    "executed_frac": round(rate * exe / 1e12 / PEAK_F16_TFLOPS, 4),
                                    "busy_counter": _mfma_busy(f"tq::encode_kernel<{bm}, "
                                                               f"{'true' if var == 'prod' else 'false'}, false>")}
-            del pk, qq
             log(f"[bench] encode {label}: {enc[label]} Mvec/s")
         if enc_roof is not None and enc_roof_prod is not None:
             enc_roof["prod4"] = enc_roof_prod
-
 
     # ---- headline: the driver's warm-up and step counts ---------------------
     ms_step, k_us = timed_steps(dec, (kq, vq), kcs, vcs, knew, vnew, q, out, args.warmup, args.steps)
@@ -350,6 +358,10 @@ def main():
     achieved = dec_bytes / (k_avg * 1e-6) / 1e9
     log(f"[bench] step {ms_step:.4f} ms; split-attention kernel avg {k_avg:.1f} us "
         f"(min {k_sorted[0]:.1f}, max {k_sorted[-1]:.1f}); {achieved:.0f} GB/s")
+
+    if not args.no_encode_sweep:
+        del sweep, xs
+        torch.cuda.empty_cache()
 
     # ---- the same step in the steady state -----------------------------------
     st_ms, st_k = timed_steps(dec, (kq, vq), kcs, vcs, knew, vnew, q, out, STEADY_WARMUP, STEADY_STEPS)
