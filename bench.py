@@ -535,6 +535,51 @@ def main():
     torch.cuda.empty_cache()
     log(f"[bench] search: {search}")
 
+    # ---- vectors longer than 128 coordinates: zero-padded chunks of 128 -------
+    # d = 200 search (the pages' GloVe dimension; seeded N(0,1) vectors stand
+    # in for the data set): 2^20 vectors, 64 queries, top 10, prod-4, recall
+    # 1@10 against the exact top-1 of the unquantized vectors. d = 1536 index
+    # build: 2^17 bf16 vectors encoded as 12 chunks each.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed_base + 11)
+    chunked = {}
+    for dim, n_c, nq_c in ((200, 1 << 20, 64), (1536, 1 << 17, 64)):
+        C = -(-dim // d)
+        xr = torch.randn((n_c, dim), generator=gen, device=dev).to(torch.bfloat16)
+        xp = torch.zeros((n_c, C * d), dtype=torch.bfloat16, device=dev)
+        xp[:, :dim] = xr
+        dbc = TA.Packed(kq, C * n_c, dev)
+        TA.encode_chunked(kq, xp, C, dbc)
+        a_.record()
+        TA.encode_chunked(kq, xp, C, dbc)
+        b_.record()
+        torch.cuda.synchronize()
+        bms = a_.elapsed_time(b_)
+        qr = torch.randn((nq_c, dim), generator=gen, device=dev)
+        qp = torch.zeros((nq_c, C * d), dtype=torch.float32, device=dev)
+        qp[:, :dim] = qr
+        ws_c = torch.empty(TA.L.tq_search_chunked_workspace(nq_c, n_c, k_s, C), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            TA.search_chunked(kq, qp, dbc, C, k_s, workspace=ws_c)
+        reps = 10
+        a_.record()
+        for _ in range(reps):
+            _, c_idx = TA.search_chunked(kq, qp, dbc, C, k_s, workspace=ws_c)
+        b_.record()
+        torch.cuda.synchronize()
+        c_us = a_.elapsed_time(b_) / reps * 1e3
+        top1 = (qr @ xr.float().T).argmax(dim=1)
+        rec = float((c_idx == top1[:, None]).any(dim=1).float().mean())
+        chunked[f"d{dim}"] = {
+            "workload": f"{n_c} x d{dim} (bf16 N(0,1)) as {C} chunks of {d}, prod-{cfg.k_bits}; "
+                        f"{nq_c} queries, top {k_s}",
+            "index_build_ms": round(bms, 4), "build_mvec_s": round(n_c / (bms * 1e-3) / 1e6, 1),
+            "search_us": round(c_us, 1), "gpairs_s": round(nq_c * n_c / (c_us * 1e-6) / 1e9, 1),
+            "recall_1_at_10": round(rec, 4)}
+        log(f"[bench] chunked d{dim}: {chunked[f'd{dim}']}")
+        del xr, xp, dbc, ws_c
+        torch.cuda.empty_cache()
+
     # ---- outlier-channel split workloads ("2.5-bit": 32 channels at 3 bits + 96
     # at 2, and "3.5-bit": 4 + 3; mse keys and values, a norm per group) at the
     # headline's shape: encode of the key cache, the decode call (query
@@ -622,6 +667,7 @@ def main():
         "hadamard_step_ms": round(had_ms, 5),
         "hadamard_value": round(dec_bytes / (had_ms * 1e-3) / 1e9, 1),
         "search": search,
+        "search_chunked": chunked,
         "outlier_split": split_res,
         "encode_mvec_s": enc,
         "encode_roofline": enc_roof,

@@ -366,6 +366,56 @@ int tq_search(const tq_quantizer* q, const float* query, int nq, const tq_packed
               float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Vectors longer than d = 128 (chunked search)
+ * [WY] section 6.4 searches vectors of 200 (GloVe) and 1536 coordinates. A
+ * vector of D coordinates is read here as C = ceil(D/128) chunks of 128
+ * (coordinates D..128C-1 are zero), each chunk quantized on its own by the
+ * same 128-coordinate quantizer (its own norm, and for PROD its own sketch and
+ * γ). The estimated inner product of a query with a vector is the sum of the
+ * chunks' estimates, Σ_c ⟨q_c, x̃_c⟩; zero padding leaves every exact inner
+ * product unchanged. Packed chunked vectors are chunk-major: chunk c of
+ * vector v is in slot c·n + v of the tq_packed buffers (n vectors), so that
+ * every chunk's vectors form one ordinary packed database.
+ */
+
+/*
+ * tq_encode_chunked — encode n vectors of `chunks` chunks each.
+ *   x         device, row i (vector i) at x + i*x_row_stride elements, holding
+ *             chunks·128 values (zero beyond the vector's own length); rows
+ *             16-byte aligned; dtype TQ_F32 or TQ_BF16
+ *   chunks    1 <= chunks <= 64
+ *   x_row_stride  >= chunks·128, multiple of 8
+ *   out       chunk-major packed output with room for chunks·n slots
+ * One encoder launch per chunk on `stream`; same per-row definition and
+ * errors as tq_encode.
+ */
+int tq_encode_chunked(const tq_quantizer* q, const void* x, int x_dtype, int64_t n, int chunks,
+                      int64_t x_row_stride, const tq_packed* out, void* stream);
+
+/*
+ * tq_search_chunked_workspace — bytes of device workspace tq_search_chunked
+ * needs (a pure function of its arguments); 0 for invalid sizes. For
+ * chunks > 1 it includes a float buffer of 8·ceil(nq/8)·n running scores.
+ */
+size_t tq_search_chunked_workspace(int nq, int64_t n, int k, int chunks);
+
+/*
+ * tq_search_chunked — tq_search over chunked vectors: for each query q_i
+ * (device float[nq][chunks·128], zero beyond the vectors' length, 16-byte
+ * aligned), the k vectors with the largest Σ_c ⟨q_{i,c}, x̃_{j,c}⟩, best first,
+ * equal scores ordered by the lower index. db is chunk-major (see above);
+ * 1 <= chunks <= 64; the other arguments as in tq_search. Launches on
+ * `stream`: per chunk, the query operands and a scan (chunks before the last
+ * store running scores in the workspace, the last adds them and keeps
+ * candidates), then the merge. chunks = 1 is tq_search.
+ * Errors: as tq_search; chunks < 1 is TQ_ERR_INVALID_ARG, chunks > 64
+ * TQ_ERR_UNSUPPORTED.
+ */
+int tq_search_chunked(const tq_quantizer* q, const float* query, int nq, int chunks, const tq_packed* db,
+                      int64_t n, int k, float* scores, int64_t* index, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/*
  * tq_read_probe — a measurement aid, not a step of the codec: one plain
  * coalesced read of `bytes` of device memory with the 16-byte non-temporal
  * loads the decode kernels stream the packed cache with. Timed on a buffer

@@ -31,6 +31,7 @@ TQ_HEAD_DIM = 128
 EXPORTED = ("tq_codebook", "tq_prep_bytes", "tq_prepare", "tq_encode",
             "tq_attn_decode_workspace", "tq_attn_decode", "tq_attn_decode_phase",
             "tq_decode_step", "tq_decode_step_phase", "tq_search_workspace", "tq_search",
+            "tq_encode_chunked", "tq_search_chunked_workspace", "tq_search_chunked",
             "tq_read_probe", "tq_status_string", "tq_attn_decode_noalloc")
 TQ_STATIC_SCRATCH_BYTES = 16 << 20
 
@@ -94,6 +95,13 @@ def load() -> ctypes.CDLL:
     lib.tq_search_workspace.restype = SZ
     lib.tq_search.argtypes = [ctypes.POINTER(tq_quantizer), P, I, ctypes.POINTER(tq_packed), I64, I, P, P, P, SZ, P]
     lib.tq_search.restype = I
+    lib.tq_encode_chunked.argtypes = [ctypes.POINTER(tq_quantizer), P, I, I64, I, I64, ctypes.POINTER(tq_packed), P]
+    lib.tq_encode_chunked.restype = I
+    lib.tq_search_chunked_workspace.argtypes = [I, I64, I, I]
+    lib.tq_search_chunked_workspace.restype = SZ
+    lib.tq_search_chunked.argtypes = [ctypes.POINTER(tq_quantizer), P, I, I, ctypes.POINTER(tq_packed), I64, I, P, P,
+                                      P, SZ, P]
+    lib.tq_search_chunked.restype = I
     lib.tq_read_probe.argtypes = [P, SZ, P, P]
     lib.tq_read_probe.restype = I
     lib.tq_status_string.argtypes = [I]
@@ -188,6 +196,22 @@ def tq_decode_step_phase(phase: int, kq: tq_quantizer, vq: tq_quantizer, k_new: 
                                        ctx_lens, int(max_ctx), ctypes.byref(k_cache), ctypes.byref(v_cache),
                                        float(scale), out, workspace, int(ws_bytes), stream),
            "tq_decode_step_phase")
+
+
+def tq_encode_chunked(q: tq_quantizer, x: int, x_dtype: int, n: int, chunks: int, x_row_stride: int,
+                      out: tq_packed, stream: int | None) -> None:
+    _check(load().tq_encode_chunked(ctypes.byref(q), x, int(x_dtype), int(n), int(chunks), int(x_row_stride),
+                                    ctypes.byref(out), stream), "tq_encode_chunked")
+
+
+def tq_search_chunked_workspace(nq: int, n: int, k: int, chunks: int) -> int:
+    return int(load().tq_search_chunked_workspace(int(nq), int(n), int(k), int(chunks)))
+
+
+def tq_search_chunked(q: tq_quantizer, query: int, nq: int, chunks: int, db: tq_packed, n: int, k: int,
+                      scores: int, index: int, workspace: int, ws_bytes: int, stream: int | None) -> None:
+    _check(load().tq_search_chunked(ctypes.byref(q), query, int(nq), int(chunks), ctypes.byref(db), int(n), int(k),
+                                    scores, index, workspace, int(ws_bytes), stream), "tq_search_chunked")
 
 
 def tq_search_workspace(nq: int, n: int, k: int) -> int:

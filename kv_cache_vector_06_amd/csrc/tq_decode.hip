@@ -99,6 +99,7 @@ struct PrepArgs {
   float scale;
   int Hq, Hkv, G, ngroups, units;
   uint8_t* ws;
+  int64_t qstride = kD;   // floats between query rows (row b·Hq + head)
 };
 
 __device__ __forceinline__ int max_exponent(float (&v)[32]) {
@@ -197,7 +198,8 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
   // B operand of the rotation: slot 8s + j of this lane is dim 32s + 8g + j.
   float xv[32];
   {
-    const float* qr = a.query + (size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + (live ? c : 0)) * kD + 8 * g;
+    const float* qr =
+        a.query + (size_t(b) * a.Hq + kvh * a.G + grp * kMaxHeads + (live ? c : 0)) * size_t(a.qstride) + 8 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const f32x4 w0 = *reinterpret_cast<const f32x4*>(qr + 32 * s);
@@ -2312,6 +2314,11 @@ struct SearchArgs {
   const uint8_t* ws;
   uint64_t* part;     // [units][nsplit][8][k] best-first keys of each split
   int ngroups, nq, nsplit, split_len, k;
+  // Chunked vectors (one pass per 128-coordinate chunk): partial[q·n + v] holds
+  // query q's summed score of vector v over the chunks before this pass.
+  float* partial;
+  int pin;            // add partial to this pass's scores
+  int pout;           // store the sums to partial and keep no candidates
 };
 
 // LDS of the search scan: the key table holds only the rows its entries use
@@ -2436,10 +2443,33 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
                                    a.kn, kg);
     float sc[8];
     block_scores<BK, PROD, 0>(R, T, bq, bs, sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[j] *= iqs;
+    if (a.pin | a.pout) {
+      // chunked vectors: the sum over this and the earlier chunks' passes
+      // (lanes n and n + 8 hold the same scores; lanes n < 8 load and store)
+      float* pq = a.partial + size_t(unit * kMaxHeads + c) * size_t(a.n);
+      const bool io = live && n < 8;
+      if (a.pin) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+          sc[j] += (io && t < t_end) ? pq[t] : 0.f;
+        }
+      }
+      if (a.pout) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+          if (io && t < t_end) pq[t] = sc[j];
+        }
+        cur = cur + 1 == NST ? 0 : cur + 1;
+        continue;
+      }
+    }
     uint32_t msk = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      sc[j] *= iqs;
       const uint32_t t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
       if (t < t_end && sc[j] > bar) msk |= 1u << j;
     }
@@ -2859,21 +2889,38 @@ extern "C" int tq_attn_decode_noalloc(const tq_quantizer* kq, const tq_quantizer
                      kStaticScratchBytes, stream);
 }
 
-extern "C" size_t tq_search_workspace(int nq, int64_t n, int k) {
-  if (nq < 1 || n < 1 || n > kMaxCtx || k < 1 || k > kSearchMaxK || k > n) return 0;
+namespace {
+
+constexpr int kMaxChunks = 64;   // vectors of up to 8192 coordinates
+
+// Workspace of a search: the query operands and per-split lists, then (for
+// vectors of more than one chunk) the running partial scores, float[units·8][n].
+size_t search_ws_bytes(int nq, int64_t n, int k, int chunks, size_t* partial_off) {
   const Plan p = make_plan(1, nq, 1, n);
-  return p.part_off + size_t(p.units) * p.nsplit * kMaxHeads * k * sizeof(uint64_t);
+  const size_t lists = p.part_off + size_t(p.units) * p.nsplit * kMaxHeads * k * sizeof(uint64_t);
+  const size_t poff = (lists + 255) / 256 * 256;
+  if (partial_off != nullptr) *partial_off = poff;
+  return chunks > 1 ? poff + size_t(p.units) * kMaxHeads * size_t(n) * sizeof(float) : lists;
 }
 
-extern "C" int tq_search(const tq_quantizer* q, const float* query, int nq, const tq_packed* db, int64_t n, int k,
-                         float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream) {
+bool search_sizes_ok(int nq, int64_t n, int k, int chunks) {
+  return nq >= 1 && n >= 1 && n <= kMaxCtx && k >= 1 && k <= kSearchMaxK && k <= n && chunks >= 1 &&
+         chunks <= kMaxChunks;
+}
+
+// One search over vectors of `chunks` 128-coordinate chunks, chunk c of vector
+// v in slot c·n + v of db. Pass c takes the query operands of the queries'
+// chunk c and scans chunk c's vectors; the scores of passes 0..chunks-2 go to
+// the partial buffer, and the last pass adds them and keeps the candidates.
+int search_call(const tq_quantizer* q, const float* query, int nq, int chunks, const tq_packed* db, int64_t n,
+                int k, float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream) {
   const int st = tq_check_quantizer(q);
   if (st != TQ_OK) return st;
   if (q->split != TQ_SPLIT_NONE) return TQ_ERR_UNSUPPORTED;
   if (query == nullptr || db == nullptr || scores == nullptr || index == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
-  if (nq < 1 || n < 1 || k < 1 || k > n) return TQ_ERR_INVALID_ARG;
-  if (k > kSearchMaxK || n > kMaxCtx) return TQ_ERR_UNSUPPORTED;
+  if (nq < 1 || n < 1 || k < 1 || k > n || chunks < 1) return TQ_ERR_INVALID_ARG;
+  if (k > kSearchMaxK || n > kMaxCtx || chunks > kMaxChunks) return TQ_ERR_UNSUPPORTED;
   const bool prod = q->variant == TQ_PROD;
   const int bk = prod ? q->bits - 1 : q->bits;
   if (db->norms == nullptr || (bk > 0 && db->codes == nullptr)) return TQ_ERR_INVALID_ARG;
@@ -2882,49 +2929,81 @@ extern "C" int tq_search(const tq_quantizer* q, const float* query, int nq, cons
       (prod && (!aligned(db->qjl, 16) || !aligned(db->gammas, 4))))
     return TQ_ERR_INVALID_ARG;
   const Plan p = make_plan(1, nq, 1, n);
-  const size_t need = p.part_off + size_t(p.units) * p.nsplit * kMaxHeads * k * sizeof(uint64_t);
+  size_t poff = 0;
+  const size_t need = search_ws_bytes(nq, n, k, chunks, &poff);
   if (ws_bytes < need || !aligned(workspace, 256)) return TQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const PrepHeader* kh = static_cast<const PrepHeader*>(q->prep);
-  // query operands with log2(e)·scale = 1: the scores are plain inner products
-  PrepArgs pa{query, q->rot, prod ? q->proj : nullptr, kh, 0.69314718055994531f, nq, 1, nq, p.ngroups, p.units, ws};
-  hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
-  if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
-  SearchArgs sa;
-  sa.kc = db->codes;
-  sa.kn = db->norms;
-  sa.kq = db->qjl;
-  sa.kg = db->gammas;
-  sa.n = n;
-  sa.kcent = q->centroids;
-  sa.kh = kh;
-  sa.ws = ws;
-  sa.part = reinterpret_cast<uint64_t*>(ws + p.part_off);
-  sa.ngroups = p.ngroups;
-  sa.nq = nq;
-  sa.nsplit = p.nsplit;
-  sa.split_len = p.split_len;
-  sa.k = k;
-  const dim3 grid(p.nsplit, p.units);
   const bool al = (n % kBlockTok) == 0;
-  hipError_t e;
-  if (!prod) {
-    switch (bk) {
-      case 1: e = launch_search_t<1, false>(sa, al, grid, s); break;
-      case 2: e = launch_search_t<2, false>(sa, al, grid, s); break;
-      case 3: e = launch_search_t<3, false>(sa, al, grid, s); break;
-      default: e = launch_search_t<4, false>(sa, al, grid, s); break;
+  const dim3 grid(p.nsplit, p.units);
+  const size_t code_row = size_t(kD) * bk / 8;
+  for (int c = 0; c < chunks; ++c) {
+    // query operands of chunk c with log2(e)·scale = 1: the scores are plain
+    // inner products
+    PrepArgs pa{query + size_t(c) * kD, q->rot, prod ? q->proj : nullptr, kh, 0.69314718055994531f, nq, 1, nq,
+                p.ngroups, p.units, ws, int64_t(chunks) * kD};
+    hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
+    if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+    const size_t row0 = size_t(c) * size_t(n);
+    SearchArgs sa;
+    sa.kc = bk > 0 ? db->codes + row0 * code_row : nullptr;
+    sa.kn = db->norms + row0;
+    sa.kq = prod ? db->qjl + row0 * (kD / 8) : nullptr;
+    sa.kg = prod ? db->gammas + row0 : nullptr;
+    sa.n = n;
+    sa.kcent = q->centroids;
+    sa.kh = kh;
+    sa.ws = ws;
+    sa.part = reinterpret_cast<uint64_t*>(ws + p.part_off);
+    sa.ngroups = p.ngroups;
+    sa.nq = nq;
+    sa.nsplit = p.nsplit;
+    sa.split_len = p.split_len;
+    sa.k = k;
+    sa.partial = chunks > 1 ? reinterpret_cast<float*>(ws + poff) : nullptr;
+    sa.pin = c > 0;
+    sa.pout = c + 1 < chunks;
+    hipError_t e;
+    if (!prod) {
+      switch (bk) {
+        case 1: e = launch_search_t<1, false>(sa, al, grid, s); break;
+        case 2: e = launch_search_t<2, false>(sa, al, grid, s); break;
+        case 3: e = launch_search_t<3, false>(sa, al, grid, s); break;
+        default: e = launch_search_t<4, false>(sa, al, grid, s); break;
+      }
+    } else {
+      switch (bk) {
+        case 0: e = launch_search_t<0, true>(sa, al, grid, s); break;
+        case 1: e = launch_search_t<1, true>(sa, al, grid, s); break;
+        case 2: e = launch_search_t<2, true>(sa, al, grid, s); break;
+        default: e = launch_search_t<3, true>(sa, al, grid, s); break;
+      }
     }
-  } else {
-    switch (bk) {
-      case 0: e = launch_search_t<0, true>(sa, al, grid, s); break;
-      case 1: e = launch_search_t<1, true>(sa, al, grid, s); break;
-      case 2: e = launch_search_t<2, true>(sa, al, grid, s); break;
-      default: e = launch_search_t<3, true>(sa, al, grid, s); break;
-    }
+    if (e != hipSuccess) return TQ_ERR_HIP;
   }
-  if (e != hipSuccess) return TQ_ERR_HIP;
-  hipLaunchKernelGGL(search_merge_kernel, dim3(nq), dim3(kDecWaves * 64), 0, s, sa.part, p.nsplit, k, scores, index);
+  hipLaunchKernelGGL(search_merge_kernel, dim3(nq), dim3(kDecWaves * 64), 0, s,
+                     reinterpret_cast<uint64_t*>(ws + p.part_off), p.nsplit, k, scores, index);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" size_t tq_search_workspace(int nq, int64_t n, int k) {
+  return search_sizes_ok(nq, n, k, 1) ? search_ws_bytes(nq, n, k, 1, nullptr) : 0;
+}
+
+extern "C" int tq_search(const tq_quantizer* q, const float* query, int nq, const tq_packed* db, int64_t n, int k,
+                         float* scores, int64_t* index, void* workspace, size_t ws_bytes, void* stream) {
+  return search_call(q, query, nq, 1, db, n, k, scores, index, workspace, ws_bytes, stream);
+}
+
+extern "C" size_t tq_search_chunked_workspace(int nq, int64_t n, int k, int chunks) {
+  return search_sizes_ok(nq, n, k, chunks) ? search_ws_bytes(nq, n, k, chunks, nullptr) : 0;
+}
+
+extern "C" int tq_search_chunked(const tq_quantizer* q, const float* query, int nq, int chunks, const tq_packed* db,
+                                 int64_t n, int k, float* scores, int64_t* index, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return search_call(q, query, nq, chunks, db, n, k, scores, index, workspace, ws_bytes, stream);
 }

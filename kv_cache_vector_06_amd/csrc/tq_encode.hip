@@ -903,6 +903,34 @@ extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+extern "C" int tq_encode_chunked(const tq_quantizer* q, const void* x, int x_dtype, int64_t n, int chunks,
+                                 int64_t x_row_stride, const tq_packed* out, void* stream) {
+  int st = check_quantizer(q);
+  if (st != TQ_OK) return st;
+  if (chunks < 1 || n < 0 || out == nullptr) return TQ_ERR_INVALID_ARG;
+  if (chunks > 64) return TQ_ERR_UNSUPPORTED;
+  if (q->split != TQ_SPLIT_NONE) return TQ_ERR_UNSUPPORTED;
+  if (x_row_stride < int64_t(chunks) * TQ_HEAD_DIM) return TQ_ERR_INVALID_ARG;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_UNSUPPORTED;
+  const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  const bool prod = q->variant == TQ_PROD;
+  const int bm = prod ? q->bits - 1 : q->bits;
+  const size_t code_row = size_t(TQ_HEAD_DIM) * bm / 8;
+  // chunk c: the rows' coordinates 128c..128c+127, stored in slots c·n + i
+  for (int c = 0; c < chunks; ++c) {
+    const size_t row0 = size_t(c) * size_t(n);
+    tq_packed o;
+    o.codes = bm > 0 && out->codes != nullptr ? out->codes + row0 * code_row : nullptr;
+    o.norms = out->norms != nullptr ? out->norms + row0 : nullptr;
+    o.qjl = prod && out->qjl != nullptr ? out->qjl + row0 * (TQ_HEAD_DIM / 8) : nullptr;
+    o.gammas = prod && out->gammas != nullptr ? out->gammas + row0 : nullptr;
+    const void* xc = x != nullptr ? static_cast<const uint8_t*>(x) + size_t(c) * TQ_HEAD_DIM * esz : nullptr;
+    st = tq_encode(q, xc, x_dtype, n, x_row_stride, &o, nullptr, stream);
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
+
 // Exported for the decoder, which checks quantizers the same way.
 int tq_check_quantizer(const tq_quantizer* q) { return check_quantizer(q); }
 int tq_device_cus() { return device_cus(); }

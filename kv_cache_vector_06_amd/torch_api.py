@@ -202,6 +202,43 @@ def search(q: Quantizer, queries: torch.Tensor, db: Packed, k: int, n: int | Non
     return scores, index
 
 
+def encode_chunked(q: Quantizer, x: torch.Tensor, chunks: int, out: Packed | None = None) -> Packed:
+    """Encode rows of x ([n, >= chunks·128], zero beyond each vector's length)
+    as chunks of 128 coordinates (tq_encode_chunked): chunk c of row i goes to
+    slot c·n + i of `out` (a Packed of chunks·n slots)."""
+    if x.dim() != 2 or x.shape[1] < chunks * q.d or x.stride(1) != 1:
+        raise ValueError("x must be [n, >= chunks*d] with unit column stride")
+    dt = {torch.float32: L.TQ_F32, torch.bfloat16: L.TQ_BF16}[x.dtype]
+    n = x.shape[0]
+    out = out if out is not None else Packed(q, chunks * n, x.device)
+    if out.n < chunks * n:
+        raise ValueError("out holds fewer than chunks*n slots")
+    L.tq_encode_chunked(q.c, x.data_ptr(), dt, n, chunks, x.stride(0), out.c, _stream())
+    return out
+
+
+def search_chunked(q: Quantizer, queries: torch.Tensor, db: Packed, chunks: int, k: int, n: int | None = None,
+                   workspace: torch.Tensor | None = None):
+    """Inner-product top-k over n chunked vectors (tq_search_chunked): queries
+    are contiguous float32 [nq, chunks·128], db chunk-major. Returns
+    (scores [nq, k] float32, index [nq, k] int64), best first."""
+    if (queries.dim() != 2 or queries.dtype != torch.float32 or not queries.is_contiguous()
+            or queries.shape[1] != chunks * q.d):
+        raise ValueError("queries must be contiguous float32 [nq, chunks*d]")
+    nq = queries.shape[0]
+    n = db.n // chunks if n is None else n
+    ws_bytes = L.tq_search_chunked_workspace(nq, n, k, chunks)
+    if ws_bytes == 0:
+        raise ValueError("invalid search sizes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=queries.device)
+    scores = torch.empty((nq, k), dtype=torch.float32, device=queries.device)
+    index = torch.empty((nq, k), dtype=torch.int64, device=queries.device)
+    L.tq_search_chunked(q.c, queries.data_ptr(), nq, chunks, db.c, n, k, scores.data_ptr(), index.data_ptr(),
+                        workspace.data_ptr(), ws_bytes, _stream())
+    return scores, index
+
+
 def read_probe(buf: torch.Tensor, xor_out: torch.Tensor) -> None:
     """One plain read of the contiguous device tensor `buf` (tq_read_probe):
     the XOR of its 32-bit words is XORed into the int32 tensor `xor_out`."""

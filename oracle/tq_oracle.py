@@ -42,6 +42,12 @@ Readings of points the pages leave open (each is listed in the design doc too):
     average, (32·3 + 96·2)/128 = 2.5, is 2.25 bits of codes; the other 0.25
     bit per channel matches two 16-bit group norms. The counts and widths
     are kept as printed.
+  * vectors longer than 128 coordinates ([WY] section 6.4 searches d = 200
+    and d = 1536): zero-padded to C = ceil(d/128)·128 coordinates and cut into
+    C chunks of 128, each quantized on its own by the same 128-coordinate
+    quantizer (own norm; own sketch and γ for prod). The estimate of ⟨q, x⟩ is
+    Σ_c ⟨q_c, x̃_c⟩, i.e. the inner product with the chunks' dequantized
+    vectors laid side by side.
 """
 from __future__ import annotations
 
@@ -55,7 +61,7 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_signs", "unpack_signs",
     "encode_mse", "encode_prod", "dequant_mse", "dequant_prod",
     "attention", "decode_attention", "fwht", "hadamard_rotate",
-    "search_topk", "recall_1_at_k",
+    "search_topk", "recall_1_at_k", "chunk_vectors", "unchunk_vectors",
     "SPLIT_OUTLIERS", "split_positions", "split_widths", "pack_split", "unpack_split",
     "encode_split", "dequant_split",
 ]
@@ -459,3 +465,28 @@ def recall_1_at_k(true_top1, found):
     true_top1 = np.asarray(true_top1).reshape(-1)
     found = np.asarray(found)
     return float(np.mean([true_top1[i] in found[i] for i in range(found.shape[0])]))
+
+
+# ---------------------------------------------------------------------------
+# Vectors longer than one 128-coordinate block  ([WY] section 6.4: search over
+# 200-dimensional GloVe vectors and index build for 1536-dimensional ones)
+# ---------------------------------------------------------------------------
+
+def chunk_vectors(X, width: int = 128):
+    """Rows of X ([n, D]) zero-padded to C·width coordinates, C = ceil(D/width),
+    and cut into chunks: returns [C, n, width] with out[c, i] = coordinates
+    c·width .. c·width+width-1 of row i."""
+    X = np.asarray(X, np.float64)
+    n, D = X.shape
+    C = max(1, -(-D // width))
+    P = np.zeros((n, C * width))
+    P[:, :D] = X
+    return np.ascontiguousarray(P.reshape(n, C, width).transpose(1, 0, 2))
+
+
+def unchunk_vectors(Xc):
+    """[C, n, width] → [n, C·width]: chunk c of row i back at coordinates
+    c·width ..; the inverse of chunk_vectors on the padded length."""
+    Xc = np.asarray(Xc, np.float64)
+    C, n, w = Xc.shape
+    return np.ascontiguousarray(Xc.transpose(1, 0, 2).reshape(n, C * w))

@@ -134,6 +134,21 @@ static void argument_checks() {
   EXPECT(tq_search(&q, qv, 4, &pk, 5, 10, sc, ix, fake(), sws, nullptr) == TQ_ERR_INVALID_ARG, "search k > n");
   EXPECT(tq_search(&q, qv, 4, &pk, 1000, 10, sc, ix, fake(), sws - 8, nullptr) == TQ_ERR_WORKSPACE,
          "search workspace size");
+  // chunked encode and search
+  EXPECT(tq_encode_chunked(&q, x, TQ_BF16, 8, 0, 256, &pk, nullptr) == TQ_ERR_INVALID_ARG, "chunked encode chunks");
+  EXPECT(tq_encode_chunked(&q, x, TQ_BF16, 8, 65, 65 * 128, &pk, nullptr) == TQ_ERR_UNSUPPORTED,
+         "chunked encode chunks > 64");
+  EXPECT(tq_encode_chunked(&q, x, TQ_BF16, 8, 2, 128, &pk, nullptr) == TQ_ERR_INVALID_ARG, "chunked encode stride");
+  const size_t cws = tq_search_chunked_workspace(4, 1000, 10, 12);
+  EXPECT(cws > sws && tq_search_chunked_workspace(4, 1000, 10, 1) == sws &&
+             tq_search_chunked_workspace(4, 1000, 10, 0) == 0 && tq_search_chunked_workspace(4, 1000, 10, 65) == 0,
+         "chunked search workspace");
+  EXPECT(tq_search_chunked(&q, qv, 4, 0, &pk, 1000, 10, sc, ix, fake(), cws, nullptr) == TQ_ERR_INVALID_ARG,
+         "chunked search chunks");
+  EXPECT(tq_search_chunked(&q, qv, 4, 65, &pk, 1000, 10, sc, ix, fake(), cws, nullptr) == TQ_ERR_UNSUPPORTED,
+         "chunked search chunks > 64");
+  EXPECT(tq_search_chunked(&q, qv, 4, 12, &pk, 1000, 10, sc, ix, fake(), cws - 8, nullptr) == TQ_ERR_WORKSPACE,
+         "chunked search workspace size");
   // read probe
   uint32_t* xo = static_cast<uint32_t*>(fake());
   EXPECT(tq_read_probe(nullptr, 16, xo, nullptr) == TQ_ERR_INVALID_ARG, "probe null");

@@ -15,8 +15,10 @@ import torch
 
 import synth
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import DEV, oracle_dequant, oracle_encode, packed_from_oracle, say
-from oracle import recall_1_at_k, search_topk
+from kv_cache_vector_06_amd import _lib as L
+from gpu_util import (DEV, assert_guards, check_encode, gpu_packed_arrays, guarded_packed, oracle_dequant,
+                      oracle_encode, packed_from_oracle, say, to_gpu_x)
+from oracle import chunk_vectors, recall_1_at_k, search_topk, unchunk_vectors
 
 pytestmark = pytest.mark.gpu
 D = 128
@@ -119,3 +121,127 @@ def test_search_full_size_sampled():
     sc, ix = sc.cpu().numpy().astype(np.float64), ix.cpu().numpy()
     rows = [0, 17, 40, 63]
     check_search(Q[rows], Xt, sc[rows], ix[rows], k)
+
+
+# ---------------------------------------------------------------------------
+# Vectors of more than 128 coordinates ("内存厂商的噩梦来了…" section 6.4:
+# d = 200 search, d = 1536 index build), read as zero-padded chunks of 128
+# quantized on their own; the estimate is summed over chunks.
+# ---------------------------------------------------------------------------
+
+def _chunked_db(n, dim, seed, variant, bits):
+    """Oracle encode of n Gaussian vectors of `dim` coordinates as chunks;
+    the packed database is chunk-major (chunk c of vector v in slot c·n + v)."""
+    Rk, _, S = synth.constants(D)
+    X = synth.gaussian((n, dim), seed, "bf16")
+    Xc = chunk_vectors(X, D)
+    encs = [oracle_encode(ch, Rk, S, bits, variant) for ch in Xc]
+    Xt = unchunk_vectors(np.stack([oracle_dequant(e, Rk, S, bits, variant) for e in encs]))
+    enc = {key: np.concatenate([e[key] for e in encs]) for key in encs[0]}
+    q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV)
+    return X, Xt, enc, q, packed_from_oracle(enc, q), Xc.shape[0]
+
+
+def _padded(A, chunks):
+    return np.ascontiguousarray(unchunk_vectors(chunk_vectors(A, D)), np.float32)
+
+
+@pytest.mark.parametrize("dim,variant,bits", [(200, "prod", 4), (200, "mse", 2), (200, "prod", 1),
+                                              (1536, "prod", 3), (129, "mse", 4)])
+def test_search_chunked_parity(dim, variant, bits):
+    n = 3000 + 17 if dim < 1536 else 700 + 5
+    X, Xt, enc, q, db, C = _chunked_db(n, dim, 760 + dim + bits, variant, bits)
+    Q = _padded(synth.gaussian((11, dim), 770 + dim, "fp32"), C)
+    for k in (1, 10, 32):
+        say("search_chunked", dim, variant, bits, "chunks", C, "k", k)
+        sc, ix = T.search_chunked(q, torch.from_numpy(Q).to(DEV), db, C, k)
+        check_search(Q, Xt, sc.cpu().numpy().astype(np.float64), ix.cpu().numpy(), k)
+    assert_guards(db)
+
+
+def test_search_chunked_one_chunk_is_search():
+    # chunks = 1 is tq_search itself: identical results
+    X, enc, Xt, q, db = _db(2500, 780, "prod", 4)
+    Q = torch.from_numpy(synth.gaussian((13, D), 781, "fp32")).to(DEV)
+    a = T.search(q, Q, db, 10)
+    b = T.search_chunked(q, Q, db, 1, 10)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_search_chunked_recall_at_d200():
+    # recall 1@10 against the unquantized top-1 on Gaussian d = 200 data is
+    # the oracle's own (up to near-tie flips)
+    n, nq, k, dim = 20000, 64, 10, 200
+    X, Xt, enc, q, db, C = _chunked_db(n, dim, 790, "prod", 4)
+    Q = synth.gaussian((nq, dim), 791, "fp32")
+    true1 = np.argmax(Q.astype(np.float64) @ X.astype(np.float64).T, axis=1)
+    Qp = _padded(Q, C)
+    sc, ix = T.search_chunked(q, torch.from_numpy(Qp).to(DEV), db, C, k)
+    got = recall_1_at_k(true1, ix.cpu().numpy())
+    want = recall_1_at_k(true1, search_topk(Qp, Xt, k)[1])
+    say("d=200 recall 1@10: gpu", got, "oracle", want)
+    assert abs(got - want) <= 2 / nq
+    assert want > 0.8
+
+
+def test_search_chunked_sampled_at_scale():
+    # 2^18 vectors at d = 200 (two chunks, 2^19 packed rows), 64 queries;
+    # the oracle checks four sampled queries
+    n, nq, k, dim = 1 << 18, 64, 10, 200
+    X, Xt, enc, q, db, C = _chunked_db(n, dim, 800, "prod", 4)
+    Q = _padded(synth.gaussian((nq, dim), 801, "fp32"), C)
+    sc, ix = T.search_chunked(q, torch.from_numpy(Q).to(DEV), db, C, k)
+    sc, ix = sc.cpu().numpy().astype(np.float64), ix.cpu().numpy()
+    rows = [0, 21, 42, 63]
+    check_search(Q[rows], Xt, sc[rows], ix[rows], k)
+
+
+@pytest.mark.parametrize("dim,variant,bits,dtype", [(200, "prod", 4, "bf16"), (1536, "mse", 3, "fp32"),
+                                                    (1536, "prod", 2, "bf16")])
+def test_encode_chunked_matches_oracle(dim, variant, bits, dtype):
+    # the index build: every chunk of every vector encoded as the oracle
+    # encodes it, chunk-major, within the encode parity rules
+    n = 4000 + 3
+    Rk, _, S = synth.constants(D)
+    X = synth.gaussian((n, dim), 810 + dim + bits, dtype)
+    Xc = chunk_vectors(X, D)
+    C = Xc.shape[0]
+    encs = [oracle_encode(ch, Rk, S, bits, variant) for ch in Xc]
+    ref = {key: np.concatenate([e[key] for e in encs]) for key in encs[0]}
+    q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV)
+    xg = to_gpu_x(unchunk_vectors(Xc), dtype)
+    out = guarded_packed(q, C * n)
+    say("encode_chunked", dim, variant, bits, dtype, "chunks", C)
+    T.encode_chunked(q, xg, C, out)
+    stats = check_encode(gpu_packed_arrays(out, q), ref, bits, variant)
+    say("  ", stats)
+    assert_guards(out)
+
+
+def test_chunked_argument_errors():
+    q = T.Quantizer(synth.constants(D)[0], 4, "mse", None, DEV)
+    db = T.Packed(q, 64, DEV)
+    Q = torch.zeros((2, 2 * D), dtype=torch.float32, device=DEV)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    assert L.tq_search_chunked_workspace(2, 32, 4, 0) == 0
+    assert L.tq_search_chunked_workspace(2, 32, 4, 65) == 0
+    assert L.tq_search_chunked_workspace(2, 32, 4, 2) > L.tq_search_chunked_workspace(2, 32, 4, 1)
+    sc = torch.empty((2, 4), dtype=torch.float32, device=DEV)
+    ix = torch.empty((2, 4), dtype=torch.int64, device=DEV)
+    with pytest.raises(L.TQError) as e:
+        L.tq_search_chunked(q.c, Q.data_ptr(), 2, 0, db.c, 32, 4, sc.data_ptr(), ix.data_ptr(), ws.data_ptr(),
+                            ws.numel(), T._stream())
+    assert e.value.status == L.TQ_ERR_INVALID_ARG
+    with pytest.raises(L.TQError) as e:
+        L.tq_search_chunked(q.c, Q.data_ptr(), 2, 65, db.c, 32, 4, sc.data_ptr(), ix.data_ptr(), ws.data_ptr(),
+                            ws.numel(), T._stream())
+    assert e.value.status == L.TQ_ERR_UNSUPPORTED
+    with pytest.raises(L.TQError) as e:
+        L.tq_search_chunked(q.c, Q.data_ptr(), 2, 2, db.c, 32, 4, sc.data_ptr(), ix.data_ptr(), ws.data_ptr(),
+                            256, T._stream())
+    assert e.value.status == L.TQ_ERR_WORKSPACE
+    x = torch.zeros((8, 2 * D), dtype=torch.float32, device=DEV)
+    with pytest.raises(L.TQError) as e:
+        L.tq_encode_chunked(q.c, x.data_ptr(), L.TQ_F32, 8, 2, D, db.c, T._stream())   # stride < chunks·128
+    assert e.value.status == L.TQ_ERR_INVALID_ARG
+    torch.cuda.synchronize()
