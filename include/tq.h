@@ -118,20 +118,26 @@ int tq_codebook(int d, int bits, double* centroids, double* boundaries, double* 
  *              independent TurboQuant-mse instances (own norm, rotation and
  *              codebook each). Requires variant TQ_MSE, bits 2 or 3 ("2.5-bit"
  *              and "3.5-bit"), rotation TQ_ROT_DENSE. Then:
- *                rot        the two rotations in one block-structured matrix:
- *                           rot[P_o[k]][ch_o[j]] = Π_o[k][j] (32×32) and
- *                           rot[P_r[k]][ch_r[j]] = Π_r[k][j] (96×96), zero
- *                           elsewhere, where P_o = the positions p with
- *                           p mod 8 < 2 (in increasing order), P_r = the other
- *                           positions, ch_o = the caller's 32 outlier channels
- *                           and ch_r = the other channels (both in the order
- *                           Π_o's / Π_r's columns follow)
+ *                rot        unused (NULL allowed)
+ *                rot_o      device float[32][32] row-major, the outlier
+ *                           group's orthogonal Π_o
+ *                rot_r      device float[96][96] row-major, the regular
+ *                           group's orthogonal Π_r
+ *                channels_o host int32[32]: the outlier channels, distinct,
+ *                           in [0, 128), in the order of Π_o's columns; the
+ *                           regular channels are the other 96 in increasing
+ *                           order, the order of Π_r's columns. Read (and
+ *                           checked) by tq_prepare only.
  *                centroids  the regular group's codebook, tq_codebook(96, bits)
  *                boundaries its midpoints
  *                centroids_o, boundaries_o  the outlier group's codebook,
  *                           tq_codebook(32, bits+1), float[2^(bits+1)] and
  *                           float[2^(bits+1) - 1]
- *              Unsplit quantizers leave centroids_o / boundaries_o NULL.
+ *              tq_prepare combines Π_o, Π_r and the channel list into the
+ *              library's own operands in `prep`; afterwards only `prep` and
+ *              the codebooks are read.
+ *              Unsplit quantizers leave centroids_o, boundaries_o, rot_o,
+ *              rot_r and channels_o NULL.
  */
 typedef struct tq_quantizer {
   int d;
@@ -146,6 +152,9 @@ typedef struct tq_quantizer {
   int split;
   const float* centroids_o;
   const float* boundaries_o;
+  const float* rot_o;
+  const float* rot_r;
+  const int32_t* channels_o;
 } tq_quantizer;
 
 /*
@@ -182,10 +191,12 @@ size_t tq_prep_bytes(void);
 /*
  * tq_prepare — derive the GPU operands of a quantizer into q->prep.
  * Splits Π (and S·Πᵀ for PROD) into the matrix-core operand layout the
- * encoder uses. Run once per quantizer (after its rot/proj/centroids are
- * written), on `stream`; later calls on the same stream see the result.
- * Errors: TQ_ERR_INVALID_ARG (null q/fields, prep misaligned),
- * TQ_ERR_UNSUPPORTED (d, bits, variant, rotation), TQ_ERR_HIP.
+ * encoder uses; for a split quantizer it first assembles Π from Π_o, Π_r and
+ * the outlier channels. Run once per quantizer (after its rot/proj/centroids
+ * are written), on `stream`; later calls on the same stream see the result.
+ * Errors: TQ_ERR_INVALID_ARG (null q/fields, prep misaligned, outlier
+ * channels not 32 distinct values in [0, 128)), TQ_ERR_UNSUPPORTED (d, bits,
+ * variant, rotation), TQ_ERR_HIP.
  */
 int tq_prepare(const tq_quantizer* q, void* stream);
 
@@ -281,7 +292,9 @@ int tq_attn_decode_phase(int phase, const tq_quantizer* kq, const tq_quantizer* 
  *   other arguments as tq_attn_decode (same workspace size).
  * The result equals tq_encode of the new rows into those slots followed by
  * tq_attn_decode, bit for bit, for rows of finite values; the appends and the query operands share one
- * launch, so the step takes three launches instead of five.
+ * launch, so the step takes three launches instead of five. With split
+ * quantizers (TQ_SPLIT_OUTLIER32, both) the appends run the split encoder,
+ * and the query operands and the two appends are three launches of phase 1.
  * Errors: as tq_attn_decode and tq_encode (TQ_ERR_INVALID_ARG for null or
  * misaligned rows or a bad stride, TQ_ERR_UNSUPPORTED for another dtype).
  */

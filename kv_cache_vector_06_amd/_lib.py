@@ -47,7 +47,8 @@ class tq_quantizer(ctypes.Structure):
                 ("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p),
                 ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p),
                 ("prep", ctypes.c_void_p), ("rotation", ctypes.c_int), ("split", ctypes.c_int),
-                ("centroids_o", ctypes.c_void_p), ("boundaries_o", ctypes.c_void_p)]
+                ("centroids_o", ctypes.c_void_p), ("boundaries_o", ctypes.c_void_p),
+                ("rot_o", ctypes.c_void_p), ("rot_r", ctypes.c_void_p), ("channels_o", ctypes.c_void_p)]
 
 
 class tq_packed(ctypes.Structure):

@@ -41,6 +41,9 @@
 #include "tq_rowtile.h"
 
 int tq_check_quantizer(const tq_quantizer* q);
+const float* tq_rotation_matrix(const tq_quantizer* q);
+int tq_split_append(const tq_quantizer* q, const void* x, int x_dtype, int64_t rows, int64_t x_row_stride,
+                    const tq_packed* cache, const int32_t* lens, int64_t max_ctx, int hkv, void* stream);
 
 #define TQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -2691,10 +2694,9 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   st = tq_check_quantizer(vq);
   if (st != TQ_OK) return st;
   if (vq->variant != TQ_MSE) return TQ_ERR_UNSUPPORTED;
-  // Split caches: both quantizers split (the fused step's small encodes do
-  // not take them).
+  // Split caches: both quantizers split.
   const bool osplit = kq->split != TQ_SPLIT_NONE;
-  if (osplit != (vq->split != TQ_SPLIT_NONE) || (osplit && step != nullptr)) return TQ_ERR_UNSUPPORTED;
+  if (osplit != (vq->split != TQ_SPLIT_NONE)) return TQ_ERR_UNSUPPORTED;
   if (query == nullptr || out == nullptr || k_cache == nullptr || v_cache == nullptr || workspace == nullptr)
     return TQ_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_ctx < 1) return TQ_ERR_INVALID_ARG;
@@ -2726,10 +2728,22 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   float* part = reinterpret_cast<float*>(ws + p.part_off);
 
   if (phase == 0 || phase == 1) {
-    PrepArgs pa{query, kq->rot, prod ? kq->proj : nullptr, static_cast<const PrepHeader*>(kq->prep), scale,
+    PrepArgs pa{query, tq_rotation_matrix(kq), prod ? kq->proj : nullptr, static_cast<const PrepHeader*>(kq->prep), scale,
                 Hq, Hkv, G, p.ngroups, p.units, ws};
     if (step == nullptr) {
       hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
+    } else if (osplit) {
+      // split caches: the query operands, then the split encoder's appends
+      // of the keys and the values (three launches)
+      hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
+      if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+      const int rows = B * Hkv;
+      st = tq_split_append(kq, step->k_new, step->x_dtype, rows, step->x_row_stride, k_cache, ctx_lens, max_ctx,
+                           Hkv, stream);
+      if (st != TQ_OK) return st;
+      st = tq_split_append(vq, step->v_new, step->x_dtype, rows, step->x_row_stride, v_cache, ctx_lens, max_ctx,
+                           Hkv, stream);
+      if (st != TQ_OK) return st;
     } else {
       StepArgs sa;
       sa.prep = pa;
@@ -2791,7 +2805,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
     if (e != hipSuccess) return TQ_ERR_HIP;
   }
   if (phase == 0 || phase == 3) {
-    MergeArgs ma{part, vq->rot, static_cast<const PrepHeader*>(vq->prep), out, Hq, Hkv, G, p.ngroups, p.nsplit};
+    MergeArgs ma{part, tq_rotation_matrix(vq), static_cast<const PrepHeader*>(vq->prep), out, Hq, Hkv, G, p.ngroups, p.nsplit};
     hipLaunchKernelGGL(merge_kernel, dim3(p.units * kMaxHeads), dim3(kD), 0, s, ma);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
   }
@@ -2941,7 +2955,7 @@ int search_call(const tq_quantizer* q, const float* query, int nq, int chunks, c
   for (int c = 0; c < chunks; ++c) {
     // query operands of chunk c with log2(e)·scale = 1: the scores are plain
     // inner products
-    PrepArgs pa{query + size_t(c) * kD, q->rot, prod ? q->proj : nullptr, kh, 0.69314718055994531f, nq, 1, nq,
+    PrepArgs pa{query + size_t(c) * kD, tq_rotation_matrix(q), prod ? q->proj : nullptr, kh, 0.69314718055994531f, nq, 1, nq,
                 p.ngroups, p.units, ws, int64_t(chunks) * kD};
     hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;

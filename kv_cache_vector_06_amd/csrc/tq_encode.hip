@@ -30,6 +30,34 @@ namespace tq {
 
 
 // ---------------------------------------------------------------------------
+// Outlier-channel split ("TurboQuant của Google…" (omelet.tech), section
+// "Thực nghiệm: 3.5 bit…"): the two groups' rotations as one d×d matrix.
+// Position p with p mod 8 < 2 is outlier row k = 2(p/8) + p mod 8 and holds
+// Π_o[k][j] at the j-th outlier channel; another position p is regular row
+// k = 6(p/8) + p mod 8 - 2 and holds Π_r[k][j] at the j-th regular channel
+// (increasing order). Every other entry is zero. One workgroup per row.
+// ---------------------------------------------------------------------------
+struct SplitChannels {
+  // column c of the block matrix: j < 32 when c is the j-th outlier channel
+  // (Π_o's column j), 32 + j when c is the j-th regular channel (Π_r's column j)
+  int32_t slot[128];
+};
+
+__global__ __launch_bounds__(128) void split_rotation_kernel(const float* __restrict__ rot_o,
+                                                             const float* __restrict__ rot_r, SplitChannels ch,
+                                                             float* __restrict__ out) {
+  const int p = blockIdx.x, col = threadIdx.x;
+  const int j = ch.slot[col];
+  float v = 0.f;
+  if ((p & 7) < 2) {
+    if (j < 32) v = rot_o[(2 * (p >> 3) + (p & 7)) * 32 + j];
+  } else {
+    if (j >= 32) v = rot_r[(6 * (p >> 3) + (p & 7) - 2) * 96 + (j - 32)];
+  }
+  out[p * kD + col] = v;
+}
+
+// ---------------------------------------------------------------------------
 // tq_prepare: fragment the rotation (and S' = S·Πᵀ) into matrix-core A operands
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void prepare_kernel(const float* __restrict__ rot,
@@ -189,6 +217,13 @@ struct EncodeArgs {
   const int64_t* slot;  // output slot of each row, or null for slot = row
   const float* centroids_o;   // split: the outlier group's codebook
   const float* boundaries_o;
+  // Append mode of the split encoder (slot == null, append != 0): row
+  // r = b·hkv + h goes to slot r·max_ctx + lens[b] - 1 (max_ctx when lens is
+  // null) and is not written unless 1 <= lens[b] <= max_ctx.
+  const int32_t* lens;
+  int64_t max_ctx;
+  int hkv;
+  int append;
 };
 
 constexpr int kEncWaves = 8;
@@ -708,9 +743,16 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
     constexpr bool USE = decltype(use_tag)::value;
     for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles; tile += tstride) {
       const int64_t rowi = tile * 16 + n;
-      const bool valid = rowi < a.n;
+      bool valid = rowi < a.n;
       const int64_t row = valid ? rowi : a.n - 1;
-      const int64_t vec = a.slot ? a.slot[row] : row;
+      int64_t vec = row;
+      if (a.slot != nullptr) {
+        vec = a.slot[row];
+      } else if (a.append) {
+        const int64_t len = a.lens != nullptr ? int64_t(a.lens[row / a.hkv]) : a.max_ctx;
+        valid = valid && len >= 1 && len <= a.max_ctx;
+        vec = row * a.max_ctx + (len - 1);
+      }
       int lofs = lane;
       asm volatile("" : "+v"(lofs));
       float xv[32];
@@ -867,7 +909,8 @@ int check_quantizer(const tq_quantizer* q) {
   if (q->variant != TQ_MSE && q->variant != TQ_PROD) return TQ_ERR_UNSUPPORTED;
   if (q->bits < 1 || q->bits > 4) return TQ_ERR_UNSUPPORTED;
   const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
-  if (q->rot == nullptr || q->centroids == nullptr || q->prep == nullptr) return TQ_ERR_INVALID_ARG;
+  if (q->centroids == nullptr || q->prep == nullptr) return TQ_ERR_INVALID_ARG;
+  if (q->split == TQ_SPLIT_NONE && q->rot == nullptr) return TQ_ERR_INVALID_ARG;
   if (bm > 0 && q->boundaries == nullptr) return TQ_ERR_INVALID_ARG;
   if (q->variant == TQ_PROD && q->proj == nullptr) return TQ_ERR_INVALID_ARG;
   if (!aligned(q->prep, 256)) return TQ_ERR_WORKSPACE;
@@ -877,8 +920,20 @@ int check_quantizer(const tq_quantizer* q) {
     if (q->variant != TQ_MSE || q->bits < 2 || q->bits > 3 || q->rotation != TQ_ROT_DENSE)
       return TQ_ERR_UNSUPPORTED;
     if (q->centroids_o == nullptr || q->boundaries_o == nullptr) return TQ_ERR_INVALID_ARG;
+    if (q->rot_o == nullptr || q->rot_r == nullptr || q->channels_o == nullptr) return TQ_ERR_INVALID_ARG;
   }
   return TQ_OK;
+}
+
+// The caller's outlier channels: 32 distinct values in [0, d).
+bool channels_valid(const int32_t* ch) {
+  uint32_t seen[4] = {0u, 0u, 0u, 0u};
+  for (int j = 0; j < 32; ++j) {
+    const int32_t c = ch[j];
+    if (c < 0 || c >= TQ_HEAD_DIM || ((seen[c >> 5] >> (c & 31)) & 1u)) return false;
+    seen[c >> 5] |= 1u << (c & 31);
+  }
+  return true;
 }
 
 int device_cus() {
@@ -892,11 +947,49 @@ int device_cus() {
 
 extern "C" size_t tq_prep_bytes(void) { return kPrepBytes; }
 
+namespace {
+int launch_split(const tq_quantizer* q, const EncodeArgs& a, bool f32, hipStream_t s) {
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
+  const int cap = device_cus() * 2;
+  const dim3 grid(static_cast<unsigned>(want < cap ? want : cap));
+  if (q->bits == 2) {
+    if (f32)
+      hipLaunchKernelGGL((encode_split_kernel<2, true>), grid, dim3(kEncWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((encode_split_kernel<2, false>), grid, dim3(kEncWaves * 64), 0, s, a);
+  } else {
+    if (f32)
+      hipLaunchKernelGGL((encode_split_kernel<3, true>), grid, dim3(kEncWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((encode_split_kernel<3, false>), grid, dim3(kEncWaves * 64), 0, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+}  // namespace
+
 extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
   const int st = check_quantizer(q);
   if (st != TQ_OK) return st;
   const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
-  hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), q->rot,
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* rot = q->rot;
+  if (q->split == TQ_SPLIT_OUTLIER32) {
+    // the whole rotation as one block-structured matrix, built in the
+    // prepared buffer from the caller's Π_o, Π_r and outlier channels
+    if (!channels_valid(q->channels_o)) return TQ_ERR_INVALID_ARG;
+    SplitChannels ch;
+    for (int c = 0; c < TQ_HEAD_DIM; ++c) ch.slot[c] = -1;
+    for (int j = 0; j < 32; ++j) ch.slot[q->channels_o[j]] = j;
+    int r = 32;
+    for (int c = 0; c < TQ_HEAD_DIM; ++c)
+      if (ch.slot[c] < 0) ch.slot[c] = r++;
+    float* block = reinterpret_cast<float*>(static_cast<uint8_t*>(q->prep) + kPrepRotOff);
+    hipLaunchKernelGGL(split_rotation_kernel, dim3(kD), dim3(kD), 0, s, q->rot_o, q->rot_r, ch, block);
+    if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+    rot = block;
+  }
+  hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, s, rot,
                      q->variant == TQ_PROD ? q->proj : nullptr, q->centroids, bm,
                      q->rotation == TQ_ROT_HADAMARD ? 1 : 0,
                      q->split == TQ_SPLIT_OUTLIER32 ? q->centroids_o : nullptr, static_cast<uint8_t*>(q->prep));
@@ -931,8 +1024,37 @@ extern "C" int tq_encode_chunked(const tq_quantizer* q, const void* x, int x_dty
   return TQ_OK;
 }
 
+// The decode step's append for split quantizers: rows r = b·hkv + h of x
+// (already checked by the caller) into slot r·max_ctx + lens[b] - 1 of cache.
+int tq_split_append(const tq_quantizer* q, const void* x, int x_dtype, int64_t rows, int64_t x_row_stride,
+                    const tq_packed* cache, const int32_t* lens, int64_t max_ctx, int hkv, void* stream) {
+  EncodeArgs a{};
+  a.x = x;
+  a.n = rows;
+  a.stride = x_row_stride;
+  a.codes = cache->codes;
+  a.norms = cache->norms;
+  a.prep = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(q->prep) + kPrepHeaderBytes);
+  a.centroids = q->centroids;
+  a.boundaries = q->boundaries;
+  a.centroids_o = q->centroids_o;
+  a.boundaries_o = q->boundaries_o;
+  a.lens = lens;
+  a.max_ctx = max_ctx;
+  a.hkv = hkv;
+  a.append = 1;
+  return launch_split(q, a, x_dtype == TQ_F32, static_cast<hipStream_t>(stream));
+}
+
 // Exported for the decoder, which checks quantizers the same way.
 int tq_check_quantizer(const tq_quantizer* q) { return check_quantizer(q); }
+// The quantizer's whole d×d rotation as the decoder reads it (a split
+// quantizer's is the block matrix in its prepared buffer).
+const float* tq_rotation_matrix(const tq_quantizer* q) {
+  return q->split == TQ_SPLIT_OUTLIER32
+             ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(q->prep) + kPrepRotOff)
+             : q->rot;
+}
 int tq_device_cus() { return device_cus(); }
 
 extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int64_t n,
@@ -952,7 +1074,7 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
       (prod && (!aligned(out->qjl, 16) || !aligned(out->gammas, 4))))
     return TQ_ERR_INVALID_ARG;
 
-  EncodeArgs a;
+  EncodeArgs a{};
   a.x = x;
   a.n = n;
   a.stride = x_row_stride;
@@ -968,24 +1090,7 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
   a.boundaries_o = q->boundaries_o;
   const int64_t tiles = (n + 15) / 16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q->split == TQ_SPLIT_OUTLIER32) {
-    const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
-    const int cap = device_cus() * 2;
-    const dim3 grid(static_cast<unsigned>(want < cap ? want : cap));
-    const bool f32 = x_dtype == TQ_F32;
-    if (q->bits == 2) {
-      if (f32)
-        hipLaunchKernelGGL((encode_split_kernel<2, true>), grid, dim3(kEncWaves * 64), 0, s, a);
-      else
-        hipLaunchKernelGGL((encode_split_kernel<2, false>), grid, dim3(kEncWaves * 64), 0, s, a);
-    } else {
-      if (f32)
-        hipLaunchKernelGGL((encode_split_kernel<3, true>), grid, dim3(kEncWaves * 64), 0, s, a);
-      else
-        hipLaunchKernelGGL((encode_split_kernel<3, false>), grid, dim3(kEncWaves * 64), 0, s, a);
-    }
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-  }
+  if (q->split == TQ_SPLIT_OUTLIER32) return launch_split(q, a, x_dtype == TQ_F32, s);
   if (tiles <= kRowTileMax) {
     RowEncArgs r{};
     r.x = x;

@@ -134,6 +134,32 @@ static void argument_checks() {
   EXPECT(tq_search(&q, qv, 4, &pk, 5, 10, sc, ix, fake(), sws, nullptr) == TQ_ERR_INVALID_ARG, "search k > n");
   EXPECT(tq_search(&q, qv, 4, &pk, 1000, 10, sc, ix, fake(), sws - 8, nullptr) == TQ_ERR_WORKSPACE,
          "search workspace size");
+  // outlier-channel split: Π_o, Π_r and a host channel list; tq_prepare
+  // checks the list (32 distinct channels in [0, 128)) before device work
+  {
+    tq_quantizer sq = quant(128, 2, TQ_MSE);
+    sq.rot = nullptr;
+    sq.split = TQ_SPLIT_OUTLIER32;
+    sq.centroids_o = static_cast<const float*>(fake());
+    sq.boundaries_o = static_cast<const float*>(fake());
+    sq.rot_o = static_cast<const float*>(fake());
+    sq.rot_r = static_cast<const float*>(fake());
+    int32_t* ch = new int32_t[32];   // exactly 32 entries: a read past them is an ASan error
+    for (int j = 0; j < 32; ++j) ch[j] = 4 * j;
+    ch[31] = 0;
+    sq.channels_o = ch;
+    EXPECT(tq_prepare(&sq, nullptr) == TQ_ERR_INVALID_ARG, "split duplicate channel");
+    ch[31] = 128;
+    EXPECT(tq_prepare(&sq, nullptr) == TQ_ERR_INVALID_ARG, "split channel out of range");
+    ch[31] = 124;
+    sq.rot_o = nullptr;
+    EXPECT(tq_prepare(&sq, nullptr) == TQ_ERR_INVALID_ARG, "split without rot_o");
+    sq.rot_o = static_cast<const float*>(fake());
+    sq.channels_o = nullptr;
+    EXPECT(tq_prepare(&sq, nullptr) == TQ_ERR_INVALID_ARG, "split without channels");
+    EXPECT(tq_encode(&sq, x, TQ_BF16, 0, 128, &pk, nullptr, nullptr) == TQ_ERR_INVALID_ARG, "split encode channels");
+    delete[] ch;
+  }
   // chunked encode and search
   EXPECT(tq_encode_chunked(&q, x, TQ_BF16, 8, 0, 256, &pk, nullptr) == TQ_ERR_INVALID_ARG, "chunked encode chunks");
   EXPECT(tq_encode_chunked(&q, x, TQ_BF16, 8, 65, 65 * 128, &pk, nullptr) == TQ_ERR_UNSUPPORTED,

@@ -145,3 +145,76 @@ def test_split_full_size_benchmark_shape_sampled(name):
         r = rel_l2_per_head(out[b, hs], ref[0])
         say("  unit", b, kvh, "rel L2", r.max())
         assert r.max() <= 1e-3, r.max()
+
+
+def _same(a, b):
+    torch.cuda.synchronize()
+    for name in ("codes", "norms"):
+        x, y = getattr(a, name).cpu(), getattr(b, name).cpu()
+        if x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        assert torch.equal(x, y), name
+
+
+@pytest.mark.parametrize("bk,bv,lens", [(2, 2, None), (3, 3, [600, 1, 0, 333, 601]), (2, 3, [64, 599, 600])])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_split_step_equals_append_then_decode(bk, bv, lens, dtype):
+    # tq_decode_step over split caches: the split encoder's appends into
+    # slot row·T + len - 1 (none outside [1, T]) followed by the decode, bit
+    # for bit against tq_encode into those slots followed by tq_attn_decode
+    B = 3 if lens is None else len(lens)
+    Hkv, Hq, Tn = 2, 16, 600
+    kq, kcst = split_quantizer(bk, "k")
+    vq, vcst = split_quantizer(bv, "v")
+    K = synth.split_kv(B, Hkv, Tn, D, 1000 + bk, kcst[0], dtype="bf16").reshape(-1, D)
+    V = synth.split_kv(B, Hkv, Tn, D, 1001 + bv, vcst[0], dtype="bf16").reshape(-1, D)
+    rows = B * Hkv
+    kn = synth.split_kv(1, 1, rows, D, 1002, kcst[0], dtype=dtype)[0, 0]
+    vn = synth.split_kv(1, 1, rows, D, 1003, vcst[0], dtype=dtype)[0, 0]
+    kng, vng = to_gpu_x(kn, dtype), to_gpu_x(vn, dtype)
+    q = torch.from_numpy(synth.gaussian((B, Hq, D), 1004, "fp32")).to(DEV)
+    lg = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    say("split step", bk, bv, lens, dtype)
+    ka, va = T.encode(kq, to_gpu_x(K, "bf16")), T.encode(vq, to_gpu_x(V, "bf16"))
+    kb, vb = T.encode(kq, to_gpu_x(K, "bf16")), T.encode(vq, to_gpu_x(V, "bf16"))
+    Ls = [Tn] * B if lens is None else lens
+    sel = [r for r in range(rows) if 1 <= Ls[r // Hkv] <= Tn]
+    slots = torch.tensor([r * Tn + Ls[r // Hkv] - 1 for r in sel], dtype=torch.int64, device=DEV)
+    idx = torch.tensor(sel, dtype=torch.int64, device=DEV)
+    T.encode(kq, kng[idx].contiguous(), ka, slots)
+    T.encode(vq, vng[idx].contiguous(), va, slots)
+    dec = T.Decoder(B, Hq, Hkv, Tn, DEV)
+    out_a = dec(kq, vq, q, ka, va, lg)
+    out_b = dec.step(kq, vq, kng, vng, q, kb, vb, lg)
+    _same(ka, kb)
+    _same(va, vb)
+    assert torch.equal(out_a.view(torch.int32), out_b.view(torch.int32))
+    if lens is not None and 0 in lens:
+        assert torch.all(out_b[lens.index(0)] == 0)
+
+
+def test_split_step_matches_oracle():
+    # the oracle encodes every token (the last of each row being the step's
+    # new one) and evaluates attention; the GPU holds the oracle's cache for
+    # the earlier tokens and appends the last one itself
+    bk, bv, B, Hkv, Hq, Tn = 2, 3, 2, 2, 16, 900
+    lens = [Tn, 500]
+    kq, vq, K, V, ek, ev, Kt, Vt, q = _split_case(bk, bv, B, Hkv, Hq, Tn, 1010)
+    ref = decode_attention(q, Kt, Vt, 1.0 / np.sqrt(D), ctx_lens=lens)
+    new_idx = np.array([(b * Hkv + h) * Tn + lens[b] - 1 for b in range(B) for h in range(Hkv)])
+    kn, vn = K.reshape(-1, D)[new_idx], V.reshape(-1, D)[new_idx]
+    kc, vc = packed_from_oracle_split(ek, kq), packed_from_oracle_split(ev, vq)
+    sl = torch.from_numpy(new_idx).to(DEV)
+    for p in (kc, vc):                                   # the step must write these slots
+        p.codes[sl] = 0
+        p.norms[sl] = 0
+    dec = T.Decoder(B, Hq, Hkv, Tn, DEV)
+    out = dec.step(kq, vq, to_gpu_x(kn, "bf16"), to_gpu_x(vn, "bf16"), torch.from_numpy(q).to(DEV), kc, vc,
+                   torch.tensor(lens, dtype=torch.int32, device=DEV)).cpu().numpy().astype(np.float64)
+    gk, gv = gpu_packed_arrays(kc, kq), gpu_packed_arrays(vc, vq)
+    sub = lambda e: {k: v[new_idx] for k, v in e.items()}
+    check_encode_split(sub(gk), sub(ek), bk)
+    check_encode_split(sub(gv), sub(ev), bv)
+    rel = rel_l2_per_head(out, ref)
+    say("split step vs oracle rel L2 max", rel.max())
+    assert rel.max() <= 1e-3, rel.max()

@@ -201,9 +201,12 @@ def test_split_argument_errors_are_synchronous():
     p = 1 << 20
     pk = L.tq_packed(p, p, None, None)
 
+    channels = np.arange(0, 128, 4, dtype=np.int32)     # host memory, as tq_prepare reads it
+
     def split_q(bits=2, variant=L.TQ_MSE, **kw):
         q = _fake_quantizer(bits=bits, variant=variant)
         q.split, q.centroids_o, q.boundaries_o = L.TQ_SPLIT_OUTLIER32, p, p
+        q.rot, q.rot_o, q.rot_r, q.channels_o = None, p, p, channels.ctypes.data
         for k, v in kw.items():
             setattr(q, k, v)
         return q
@@ -231,9 +234,15 @@ def test_split_argument_errors_are_synchronous():
 
     assert dec(sq, uq) == L.TQ_ERR_UNSUPPORTED
     assert dec(uq, sq) == L.TQ_ERR_UNSUPPORTED
-    # the fused step and search reject split quantizers
-    assert lib.tq_decode_step(byref(sq), byref(sq), p, 1 << 21, L.TQ_BF16, 128, p, 1, 32, 8, None, 1000, byref(pk),
-                              byref(pk), 0.1, p, p, ws, None) == L.TQ_ERR_UNSUPPORTED
+    # the fused step takes split quantizers (both or neither) with the same
+    # row checks; search rejects them
+    def step(kq, vq, stride=128):
+        return lib.tq_decode_step(byref(kq), byref(vq), p, 1 << 21, L.TQ_BF16, stride, p, 1, 32, 8, None, 1000,
+                                  byref(pk), byref(pk), 0.1, p, p, ws, None)
+
+    assert step(sq, uq) == L.TQ_ERR_UNSUPPORTED
+    assert step(uq, sq) == L.TQ_ERR_UNSUPPORTED
+    assert step(sq, sq, stride=100) == L.TQ_ERR_INVALID_ARG
     sws = L.tq_search_workspace(10, 1000, 8)
     assert lib.tq_search(byref(sq), p, 10, byref(pk), 1000, 8, p, 1 << 21, 1 << 22, sws, None) == L.TQ_ERR_UNSUPPORTED
 
@@ -247,3 +256,32 @@ def test_read_probe_argument_errors_are_synchronous():
     assert lib.tq_read_probe(p, 64, p + 2, None) == L.TQ_ERR_INVALID_ARG      # xor_out must be 4-byte aligned
     assert lib.tq_read_probe(p, 0, p, None) == L.TQ_ERR_INVALID_ARG
     assert lib.tq_read_probe(p, 72, p, None) == L.TQ_ERR_INVALID_ARG          # not a multiple of 16
+
+
+def test_split_quantizer_takes_the_pages_objects():
+    # An outlier-channel split quantizer crosses the ABI as Π_o (32×32),
+    # Π_r (96×96) and the 32 outlier channels (host int32); `rot` may be NULL.
+    # tq_prepare rejects a channel list that is not 32 distinct values in
+    # [0, 128) before any device work, and a split quantizer missing Π_o, Π_r
+    # or the list.
+    lib = L.load()
+    p = 1 << 20
+
+    def split_q(channels, rot_o=p, rot_r=p):
+        ch = np.ascontiguousarray(channels, np.int32)
+        q = L.tq_quantizer(128, 2, L.TQ_MSE, None, None, p, p, p, L.TQ_ROT_DENSE, L.TQ_SPLIT_OUTLIER32, p, p,
+                           rot_o, rot_r, ch.ctypes.data if ch.size else None)
+        return q, ch
+
+    for bad in (list(range(31)) + [0], list(range(31)) + [128], list(range(31)) + [-1]):
+        q, keep = split_q(bad)
+        assert lib.tq_prepare(ctypes.byref(q), None) == L.TQ_ERR_INVALID_ARG, bad
+    q, keep = split_q(np.arange(32), rot_o=None)
+    assert lib.tq_prepare(ctypes.byref(q), None) == L.TQ_ERR_INVALID_ARG
+    q, keep = split_q(np.arange(32), rot_r=None)
+    assert lib.tq_prepare(ctypes.byref(q), None) == L.TQ_ERR_INVALID_ARG
+    q, keep = split_q(np.zeros(0))
+    assert lib.tq_prepare(ctypes.byref(q), None) == L.TQ_ERR_INVALID_ARG
+    # an unsplit quantizer still needs `rot`
+    q = L.tq_quantizer(128, 2, L.TQ_MSE, None, None, p, p, p)
+    assert lib.tq_prepare(ctypes.byref(q), None) == L.TQ_ERR_INVALID_ARG
