@@ -42,6 +42,13 @@ Readings of points the pages leave open (each is listed in the design doc too):
     average, (32·3 + 96·2)/128 = 2.5, is 2.25 bits of codes; the other 0.25
     bit per channel matches two 16-bit group norms. The counts and widths
     are kept as printed.
+  * outlier-channel split with prod keys: the same two groups, each a
+    TurboQuant-prod instance at its group's width — the outlier group at
+    bits+1 (bits of Lloyd-Max, d = 32 codebook, plus a 1-bit sketch with its
+    own 32×32 Gaussian S_o) and the regular group at bits (bits-1 of
+    Lloyd-Max, d = 96, plus a 1-bit sketch with a 96×96 S_r); each group keeps
+    its own norm and γ. The sketch bits sit at the groups' positions of the
+    split layout, and the correction scale √(π/2)/d_g uses the group's d_g.
   * vectors longer than 128 coordinates ([WY] section 6.4 searches d = 200
     and d = 1536): zero-padded to C = ceil(d/128)·128 coordinates and cut into
     C chunks of 128, each quantized on its own by the same 128-coordinate
@@ -63,7 +70,7 @@ __all__ = [
     "attention", "decode_attention", "fwht", "hadamard_rotate",
     "search_topk", "recall_1_at_k", "chunk_vectors", "unchunk_vectors",
     "SPLIT_OUTLIERS", "split_positions", "split_widths", "pack_split", "unpack_split",
-    "encode_split", "dequant_split",
+    "encode_split", "dequant_split", "encode_split_prod", "dequant_split_prod", "pack_positions",
 ]
 
 
@@ -403,6 +410,62 @@ def dequant_split(codes, norms, ch_o, rot_o, rot_r, c_o, c_r, bits: int, d: int 
     out = np.zeros((idx.shape[0], d))
     out[:, np.asarray(ch_o)] = norms[:, :1] * (np.asarray(c_o, np.float64)[idx[:, P_o]] @ np.asarray(rot_o, np.float64))
     out[:, ch_r] = norms[:, 1:] * (np.asarray(c_r, np.float64)[idx[:, P_r]] @ np.asarray(rot_r, np.float64))
+    return out
+
+
+def pack_positions(z_o, z_r, d: int = 128) -> np.ndarray:
+    """The two groups' sketch values laid out by position (outlier coordinate
+    k at P_o[k], regular k at P_r[k]) and packed as sign bits, bit p = 1 iff
+    the value at position p is >= 0."""
+    P_o, P_r = split_positions(d)
+    z = np.zeros((np.asarray(z_o).shape[0], d))
+    z[:, P_o] = z_o
+    z[:, P_r] = z_r
+    return pack_signs(z)
+
+
+def encode_split_prod(X, ch_o, rot_o, rot_r, proj_o, proj_r, c_o, c_r, bits: int):
+    """Outlier-channel split with prod keys: two independent TurboQuant-prod
+    instances. The outlier channels ch_o (in the order of rot_o's columns) at
+    bits + 1 (Lloyd-Max codebook c_o for d = 32 at `bits` bits, sketch S_o =
+    proj_o, 32×32), the other 96 channels in increasing order at `bits`
+    (c_r for d = 96 at bits - 1 bits, S_r = proj_r, 96×96). The Lloyd-Max
+    codes form the split code string of width bits - 1 (outlier positions
+    `bits` wide); the sketch bits sit at the same positions.
+    Returns dict(codes, norms=[N,2], qjl=[N,16], gammas=[N,2] (outlier,
+    regular), idx (position order), y_o, y_r, z_o, z_r)."""
+    X = np.asarray(X, np.float64)
+    d = X.shape[1]
+    ch_r = _regular_channels(ch_o, d)
+    eo = encode_prod(X[:, np.asarray(ch_o)], rot_o, proj_o, c_o, bits + 1)
+    er = encode_prod(X[:, ch_r], rot_r, proj_r, c_r, bits)
+    P_o, P_r = split_positions(d)
+    idx = np.zeros((X.shape[0], d), np.int64)
+    idx[:, P_o] = eo["idx"]
+    idx[:, P_r] = er["idx"]
+    return dict(codes=pack_split(idx, bits - 1), norms=np.stack([eo["norms"], er["norms"]], axis=1),
+                qjl=pack_positions(eo["z"], er["z"], d), gammas=np.stack([eo["gammas"], er["gammas"]], axis=1),
+                idx=idx, y_o=eo["y"], y_r=er["y"], z_o=eo["z"], z_r=er["z"])
+
+
+def dequant_split_prod(codes, norms, qjl, gammas, ch_o, rot_o, rot_r, proj_o, proj_r, c_o, c_r, bits: int,
+                       d: int = 128):
+    """x̃[ch_o] = n_o (Π_oᵀ c_o[idx_o] + √(π/2)/32 · γ_o S_oᵀ s_o) and
+    x̃[ch_r] = n_r (Π_rᵀ c_r[idx_r] + √(π/2)/96 · γ_r S_rᵀ s_r), s_g the
+    group's sketch signs read at its positions."""
+    idx = unpack_split(codes, bits - 1, d)
+    P_o, P_r = split_positions(d)
+    s = unpack_signs(qjl, d)
+    norms = np.asarray(norms, np.float64)
+    gammas = np.asarray(gammas, np.float64)
+    ch_r = _regular_channels(ch_o, d)
+    out = np.zeros((idx.shape[0], d))
+    for ch, P, R, S, c, col in ((np.asarray(ch_o), P_o, rot_o, proj_o, c_o, 0), (ch_r, P_r, rot_r, proj_r, c_r, 1)):
+        R = np.asarray(R, np.float64)
+        S = np.asarray(S, np.float64)
+        base = np.asarray(c, np.float64)[idx[:, P]] @ R
+        corr = (math.sqrt(math.pi / 2) / S.shape[0]) * gammas[:, col:col + 1] * (s[:, P] @ S)
+        out[:, ch] = norms[:, col:col + 1] * (base + corr)
     return out
 
 

@@ -36,6 +36,7 @@ SEED_SPLIT_CH_K = 1006
 SEED_SPLIT_CH_V = 1007
 SEED_SPLIT_ROT_K = (1008, 1009)
 SEED_SPLIT_ROT_V = (1010, 1011)
+SEED_SPLIT_PROJ_K = (1012, 1013)
 SPLIT_OUTLIER_SCALE = 4.0
 
 
@@ -128,12 +129,14 @@ def outlier_channels(d: int, seed: int, n: int = 32) -> np.ndarray:
 
 def split_constants(d: int = 128):
     """Per role, the outlier-channel split's inputs: dict(ch_k, rk_o, rk_r,
-    ch_v, rv_o, rv_r) with ch_* 32 channel indices and r*_o (32x32), r*_r
-    (96x96) rotations drawn as the dense one is."""
+    ch_v, rv_o, rv_r, sk_o, sk_r) with ch_* 32 channel indices, r*_o (32x32)
+    and r*_r (96x96) rotations drawn as the dense one is, and the keys' QJL
+    projections sk_o (32x32) and sk_r (96x96) for prod keys."""
     n = 32
     return dict(ch_k=outlier_channels(d, SEED_SPLIT_CH_K, n), rk_o=rotation(n, SEED_SPLIT_ROT_K[0]),
                 rk_r=rotation(d - n, SEED_SPLIT_ROT_K[1]), ch_v=outlier_channels(d, SEED_SPLIT_CH_V, n),
-                rv_o=rotation(n, SEED_SPLIT_ROT_V[0]), rv_r=rotation(d - n, SEED_SPLIT_ROT_V[1]))
+                rv_o=rotation(n, SEED_SPLIT_ROT_V[0]), rv_r=rotation(d - n, SEED_SPLIT_ROT_V[1]),
+                sk_o=projection(n, SEED_SPLIT_PROJ_K[0]), sk_r=projection(d - n, SEED_SPLIT_PROJ_K[1]))
 
 
 def split_kv(B: int, H: int, T: int, d: int, seed: int, channels, scale: float = SPLIT_OUTLIER_SCALE,
