@@ -115,9 +115,14 @@ int tq_codebook(int d, int bits, double* centroids, double* boundaries, double* 
  *   split      TQ_SPLIT_NONE (0), or TQ_SPLIT_OUTLIER32 (1): the outlier-channel
  *              split of [OM] section "Thực nghiệm: 3.5 bit…" — 32 outlier
  *              channels at bits+1 bits and the other 96 at `bits` bits, as two
- *              independent TurboQuant-mse instances (own norm, rotation and
- *              codebook each). Requires variant TQ_MSE, bits 2 or 3 ("2.5-bit"
- *              and "3.5-bit"), rotation TQ_ROT_DENSE. Then:
+ *              independent TurboQuant instances (own norm, rotation and
+ *              codebook each). Requires bits 2 or 3 ("2.5-bit" and
+ *              "3.5-bit") and rotation TQ_ROT_DENSE. With TQ_MSE both groups
+ *              are mse instances (Lloyd-Max widths bm + 1 and bm, bm = bits);
+ *              with TQ_PROD both are prod instances (the outlier group at
+ *              bits+1: `bits` of Lloyd-Max plus a 1-bit sketch with its own
+ *              32×32 S_o; the regular group at bits: bits-1 of Lloyd-Max plus
+ *              a sketch with a 96×96 S_r; own γ each), bm = bits - 1. Then:
  *                rot        unused (NULL allowed)
  *                rot_o      device float[32][32] row-major, the outlier
  *                           group's orthogonal Π_o
@@ -128,16 +133,20 @@ int tq_codebook(int d, int bits, double* centroids, double* boundaries, double* 
  *                           regular channels are the other 96 in increasing
  *                           order, the order of Π_r's columns. Read (and
  *                           checked) by tq_prepare only.
- *                centroids  the regular group's codebook, tq_codebook(96, bits)
+ *                proj       unused (NULL allowed)
+ *                proj_o, proj_r  TQ_PROD: device float[32][32] and
+ *                           float[96][96] row-major, the groups' Gaussian
+ *                           sketch matrices S_o and S_r (NULL for TQ_MSE)
+ *                centroids  the regular group's codebook, tq_codebook(96, bm)
  *                boundaries its midpoints
  *                centroids_o, boundaries_o  the outlier group's codebook,
- *                           tq_codebook(32, bits+1), float[2^(bits+1)] and
- *                           float[2^(bits+1) - 1]
- *              tq_prepare combines Π_o, Π_r and the channel list into the
- *              library's own operands in `prep`; afterwards only `prep` and
- *              the codebooks are read.
+ *                           tq_codebook(32, bm+1), float[2^(bm+1)] and
+ *                           float[2^(bm+1) - 1]
+ *              tq_prepare combines Π_o, Π_r, S_o, S_r and the channel list
+ *              into the library's own operands in `prep`; afterwards only
+ *              `prep` and the codebooks are read.
  *              Unsplit quantizers leave centroids_o, boundaries_o, rot_o,
- *              rot_r and channels_o NULL.
+ *              rot_r, channels_o, proj_o and proj_r NULL.
  */
 typedef struct tq_quantizer {
   int d;
@@ -155,6 +164,8 @@ typedef struct tq_quantizer {
   const float* rot_o;
   const float* rot_r;
   const int32_t* channels_o;
+  const float* proj_o;
+  const float* proj_r;
 } tq_quantizer;
 
 /*
@@ -169,13 +180,18 @@ typedef struct tq_quantizer {
  *           LSB-first order
  *   gammas  float[n] (PROD, else NULL): ‖r‖, the residual norm the QJL
  *           estimator scales by
- * Split quantizers (TQ_SPLIT_OUTLIER32, b = bits):
+ * Split quantizers (TQ_SPLIT_OUTLIER32, b = bm: bits for TQ_MSE, bits-1 for
+ * TQ_PROD):
  *   codes   uint8[n][16·b + 4]: the 128 codes in position order, position p
  *           with width b+1 when p mod 8 < 2 (outlier coordinate k sits at the
  *           k-th such position) and b otherwise (regular coordinate k at the
  *           k-th other position), one after another, each least significant
  *           bit first; every 8 positions take 8b + 2 bits
  *   norms   float[n][2]: ‖x_o‖ and ‖x_r‖ of the outlier and regular channels
+ *   qjl     TQ_PROD: uint8[n][16], bit p the sign bit of the sketch value at
+ *           position p (outlier sketch coordinate k at the k-th position with
+ *           p mod 8 < 2, regular k at the k-th other one)
+ *   gammas  TQ_PROD: float[n][2], γ_o and γ_r
  * Buffers must be 16-byte aligned.
  */
 typedef struct tq_packed {

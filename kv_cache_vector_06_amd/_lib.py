@@ -48,7 +48,8 @@ class tq_quantizer(ctypes.Structure):
                 ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p),
                 ("prep", ctypes.c_void_p), ("rotation", ctypes.c_int), ("split", ctypes.c_int),
                 ("centroids_o", ctypes.c_void_p), ("boundaries_o", ctypes.c_void_p),
-                ("rot_o", ctypes.c_void_p), ("rot_r", ctypes.c_void_p), ("channels_o", ctypes.c_void_p)]
+                ("rot_o", ctypes.c_void_p), ("rot_r", ctypes.c_void_p), ("channels_o", ctypes.c_void_p),
+                ("proj_o", ctypes.c_void_p), ("proj_r", ctypes.c_void_p)]
 
 
 class tq_packed(ctypes.Structure):

@@ -42,6 +42,7 @@
 
 int tq_check_quantizer(const tq_quantizer* q);
 const float* tq_rotation_matrix(const tq_quantizer* q);
+const float* tq_projection_matrix(const tq_quantizer* q);
 int tq_split_append(const tq_quantizer* q, const void* x, int x_dtype, int64_t rows, int64_t x_row_stride,
                     const tq_packed* cache, const int32_t* lens, int64_t max_ctx, int hkv, void* stream);
 
@@ -2719,6 +2720,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
       return TQ_ERR_INVALID_ARG;
     if (int64_t(B) * Hkv > (int64_t(1) << 30)) return TQ_ERR_UNSUPPORTED;
   }
+  if (osplit && prod) return TQ_ERR_UNSUPPORTED;
   const Plan p = make_plan(B, Hq, Hkv, max_ctx);
   if (ws_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TQ_ERR_WORKSPACE;
   if (checks_only) return TQ_OK;
@@ -2728,7 +2730,7 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
   float* part = reinterpret_cast<float*>(ws + p.part_off);
 
   if (phase == 0 || phase == 1) {
-    PrepArgs pa{query, tq_rotation_matrix(kq), prod ? kq->proj : nullptr, static_cast<const PrepHeader*>(kq->prep), scale,
+    PrepArgs pa{query, tq_rotation_matrix(kq), tq_projection_matrix(kq), static_cast<const PrepHeader*>(kq->prep), scale,
                 Hq, Hkv, G, p.ngroups, p.units, ws};
     if (step == nullptr) {
       hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
@@ -2955,7 +2957,7 @@ int search_call(const tq_quantizer* q, const float* query, int nq, int chunks, c
   for (int c = 0; c < chunks; ++c) {
     // query operands of chunk c with log2(e)·scale = 1: the scores are plain
     // inner products
-    PrepArgs pa{query + size_t(c) * kD, tq_rotation_matrix(q), prod ? q->proj : nullptr, kh, 0.69314718055994531f, nq, 1, nq,
+    PrepArgs pa{query + size_t(c) * kD, tq_rotation_matrix(q), tq_projection_matrix(q), kh, 0.69314718055994531f, nq, 1, nq,
                 p.ngroups, p.units, ws, int64_t(chunks) * kD};
     hipLaunchKernelGGL(query_prep_kernel, dim3(p.units), dim3(kRowWaves * 64), 0, s, pa);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;

@@ -39,8 +39,11 @@ constexpr size_t kSetBytes = size_t(kFragsPerSet) * 64 * 16;  // 64 KiB
 // block-structured matrix tq_prepare builds from Π_o, Π_r and the channel list
 // (rows p mod 8 < 2 hold Π_o over the outlier channels, the other rows Π_r
 // over the regular channels); unused otherwise.
+// A split prod quantizer's sketch matrix follows in the same structure
+// (rows: sketch positions, columns: channels).
 constexpr size_t kPrepRotOff = kPrepHeaderBytes + 2 * kSetBytes;
-constexpr size_t kPrepBytes = kPrepRotOff + size_t(kD) * kD * sizeof(float);
+constexpr size_t kPrepProjOff = kPrepRotOff + size_t(kD) * kD * sizeof(float);
+constexpr size_t kPrepBytes = kPrepProjOff + size_t(kD) * kD * sizeof(float);
 constexpr float kRotScale = 16.0f;                    // dense Π: |Π| <= 1 → |16Π| <= 16
 constexpr float kResScale = 64.0f;                    // residual scale of the sketch operand
 

@@ -703,14 +703,21 @@ __global__ __launch_bounds__(kRowWaves * 64) void row_encode_kernel(RowEncArgs a
 // rotated coordinates 32g + q, q = 4t + j; q is an outlier position when
 // t is even and j < 2. Its 32 codes form the bits [g·(32·BM + 8), (g+1)·(32·BM + 8))
 // of the vector's code string (byte aligned), written byte by byte.
-template <int BM, bool F32IN>
+//
+// PROD (prod keys): each group is a TurboQuant-prod instance. The residual of
+// a coordinate is taken in its group's scale, S_g·(y - c), as in the unsplit
+// encoder; the sketch runs on the block-structured S' = S·Πᵀ of the prepared
+// buffer (zero across the groups), so one product gives both groups' sketch
+// values at their positions; γ_o and γ_r are the groups' residual norms.
+template <int BM, bool F32IN, bool PROD>
 __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs a) {
   constexpr int BO = BM + 1;
   constexpr int SEG = 32 * BM + 8;           // bits of a lane's 32 codes
   constexpr int NW = (SEG + 31) / 32;
   constexpr int ROW = 16 * BM + 4;           // bytes of a vector's codes
   __shared__ u32x4 lds_rot[kFragsPerSet * 64];
-  stage_frags(a.prep, lds_rot, nullptr, threadIdx.x);
+  __shared__ u32x4 lds_proj[PROD ? kFragsPerSet * 64 : 1];
+  stage_frags(a.prep, lds_rot, PROD ? lds_proj : nullptr, threadIdx.x);
   const PrepHeader* hdr =
       reinterpret_cast<const PrepHeader*>(reinterpret_cast<const uint8_t*>(a.prep) - kPrepHeaderBytes);
   const float rot_scale = hdr->rot_scale;
@@ -841,17 +848,30 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
 #pragma unroll
         for (int j = 1; j < (1 << BM) / 2; ++j) sbr.t[j] = __builtin_bit_cast(uint32_t, tr[j] * Sr);
       }
+      if constexpr (PROD) {
+        // the groups' centroid magnitudes in their scales, fl(|c|·S_g)
+        const float co[8] = {bo.c0, bo.c1, bo.c2, bo.c3, bo.c4, bo.c5, bo.c6, bo.c7};
+        const float cr[8] = {br.c0, br.c1, br.c2, br.c3, br.c4, br.c5, br.c6, br.c7};
+#pragma unroll
+        for (int j = 0; j < (1 << BO) / 2; ++j) sbo.c[j] = co[j] * So;
+#pragma unroll
+        for (int j = 0; j < ((1 << BM) / 2 > 0 ? (1 << BM) / 2 : 1); ++j) sbr.c[j] = cr[j] * Sr;
+      }
       uint32_t w[NW];
 #pragma unroll
       for (int k = 0; k < NW; ++k) w[k] = 0u;
+      u32x4 brh[4], brl[4];
+      float r2o = 0.f, r2r = 0.f;
+      const float rsco = kResScale / So, rscr = kResScale / Sr;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
+        float res[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int q = 4 * t + j, c = q >> 3, r = q & 7;
           const bool out = r < 2;
-          uint32_t m;
-          bool pos;
+          uint32_t m = 0u;
+          bool pos = false;
           uint32_t code;
           if (USE && (out || kCellsR)) {
             // cell of acc in the group's table: idx = below + [acc > fl(t·S)]
@@ -860,6 +880,12 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
             const uint32_t k = __builtin_amdgcn_cvt_pk_u8_f32(f, 0, 0u);
             const u32x2 e = out ? cells_o[k] : cells_r[kCellsR ? k : 0];
             code = e[0] + (acc[t][j] > __uint_as_float(e[1]) * Sg ? 1u : 0u);
+            if constexpr (PROD) {
+              // the code's magnitude index and sign
+              const uint32_t h = out ? (1u << BO) / 2 : (1u << BM) / 2;
+              pos = code >= h;
+              m = pos ? code - h : h - 1u - code;
+            }
           } else {
             code = out ? quantize_scaled<BO>(acc[t][j], sbo, m, pos) : quantize_scaled<BM>(acc[t][j], sbr, m, pos);
           }
@@ -868,6 +894,29 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
           const int wi = bit >> 5, off = bit & 31;
           w[wi] |= code << off;
           if (off + width > 32) w[wi + 1] |= code >> (32 - off);
+          if constexpr (PROD) {
+            float cv = out ? scaled_mag<BO>(sbo, m) : scaled_mag<BM>(sbr, m);
+            cv = pos ? cv : -cv;
+            const float racc = acc[t][j] - cv;                 // S_g·(y - c)
+            if (out)
+              r2o = fmaf(racc, racc, r2o);
+            else
+              r2r = fmaf(racc, racc, r2r);
+            res[j] = racc * (out ? rsco : rscr);               // 64·(y - c)
+          }
+        }
+        if constexpr (PROD) {
+          // q = 4t + j  ->  K-step s = t/2, dword 2(t%2) + j/2, half j%2.
+          uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
+          split_h(res[0], h0, l0);
+          split_h(res[1], h1, l1);
+          split_h(res[2], h2, l2);
+          split_h(res[3], h3, l3);
+          const int s = t >> 1, k0 = 2 * (t & 1);
+          brh[s][k0] = uint32_t(h0) | (uint32_t(h1) << 16);
+          brh[s][k0 + 1] = uint32_t(h2) | (uint32_t(h3) << 16);
+          brl[s][k0] = uint32_t(l0) | (uint32_t(l1) << 16);
+          brl[s][k0 + 1] = uint32_t(l2) | (uint32_t(l3) << 16);
         }
       }
       if (valid) {
@@ -877,6 +926,37 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
         if (g == 0) {
           a.norms[2 * vec] = ldexpf(rso, ex);
           a.norms[2 * vec + 1] = ldexpf(rsr, ex);
+        }
+      }
+      if constexpr (PROD) {
+        r2o = sum4g(r2o);
+        r2r = sum4g(r2r);
+        f32x4 z[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) z[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const u32x4 sh = lds_proj[frag_index(0, t, s) * 64 + lofs];
+            const u32x4 sl = lds_proj[frag_index(1, t, s) * 64 + lofs];
+            z[t] = mfma(sh, brh[s], z[t]);
+            z[t] = mfma(sl, brh[s], z[t]);
+            z[t] = mfma(sh, brl[s], z[t]);
+          }
+        }
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bits |= uint32_t(z[t][j] >= 0.f) << (4 * t + j);
+        }
+        if (valid) {
+          *reinterpret_cast<uint32_t*>(a.qjl + vec * 16 + 4 * g) = bits;
+          if (g == 0) {
+            a.gammas[2 * vec] = sqrtf(r2o) / So;
+            a.gammas[2 * vec + 1] = sqrtf(r2r) / Sr;
+          }
         }
       }
     }
@@ -912,15 +992,15 @@ int check_quantizer(const tq_quantizer* q) {
   if (q->centroids == nullptr || q->prep == nullptr) return TQ_ERR_INVALID_ARG;
   if (q->split == TQ_SPLIT_NONE && q->rot == nullptr) return TQ_ERR_INVALID_ARG;
   if (bm > 0 && q->boundaries == nullptr) return TQ_ERR_INVALID_ARG;
-  if (q->variant == TQ_PROD && q->proj == nullptr) return TQ_ERR_INVALID_ARG;
+  if (q->variant == TQ_PROD && q->split == TQ_SPLIT_NONE && q->proj == nullptr) return TQ_ERR_INVALID_ARG;
   if (!aligned(q->prep, 256)) return TQ_ERR_WORKSPACE;
   if (q->rotation != TQ_ROT_DENSE && q->rotation != TQ_ROT_HADAMARD) return TQ_ERR_UNSUPPORTED;
   if (q->split != TQ_SPLIT_NONE && q->split != TQ_SPLIT_OUTLIER32) return TQ_ERR_UNSUPPORTED;
   if (q->split == TQ_SPLIT_OUTLIER32) {
-    if (q->variant != TQ_MSE || q->bits < 2 || q->bits > 3 || q->rotation != TQ_ROT_DENSE)
-      return TQ_ERR_UNSUPPORTED;
+    if (q->bits < 2 || q->bits > 3 || q->rotation != TQ_ROT_DENSE) return TQ_ERR_UNSUPPORTED;
     if (q->centroids_o == nullptr || q->boundaries_o == nullptr) return TQ_ERR_INVALID_ARG;
     if (q->rot_o == nullptr || q->rot_r == nullptr || q->channels_o == nullptr) return TQ_ERR_INVALID_ARG;
+    if (q->variant == TQ_PROD && (q->proj_o == nullptr || q->proj_r == nullptr)) return TQ_ERR_INVALID_ARG;
   }
   return TQ_OK;
 }
@@ -948,21 +1028,30 @@ int device_cus() {
 extern "C" size_t tq_prep_bytes(void) { return kPrepBytes; }
 
 namespace {
+template <int BM, bool PROD>
+void launch_split_t(const EncodeArgs& a, bool f32, dim3 grid, hipStream_t s) {
+  if (f32)
+    hipLaunchKernelGGL((encode_split_kernel<BM, true, PROD>), grid, dim3(kEncWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((encode_split_kernel<BM, false, PROD>), grid, dim3(kEncWaves * 64), 0, s, a);
+}
+
 int launch_split(const tq_quantizer* q, const EncodeArgs& a, bool f32, hipStream_t s) {
+  const bool prod = q->variant == TQ_PROD;
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
-  const int cap = device_cus() * 2;
+  const int cap = device_cus() * (prod ? 1 : 2);
   const dim3 grid(static_cast<unsigned>(want < cap ? want : cap));
-  if (q->bits == 2) {
-    if (f32)
-      hipLaunchKernelGGL((encode_split_kernel<2, true>), grid, dim3(kEncWaves * 64), 0, s, a);
+  if (!prod) {
+    if (q->bits == 2)
+      launch_split_t<2, false>(a, f32, grid, s);
     else
-      hipLaunchKernelGGL((encode_split_kernel<2, false>), grid, dim3(kEncWaves * 64), 0, s, a);
+      launch_split_t<3, false>(a, f32, grid, s);
   } else {
-    if (f32)
-      hipLaunchKernelGGL((encode_split_kernel<3, true>), grid, dim3(kEncWaves * 64), 0, s, a);
+    if (q->bits == 2)
+      launch_split_t<1, true>(a, f32, grid, s);
     else
-      hipLaunchKernelGGL((encode_split_kernel<3, false>), grid, dim3(kEncWaves * 64), 0, s, a);
+      launch_split_t<2, true>(a, f32, grid, s);
   }
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -974,6 +1063,7 @@ extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
   const int bm = q->variant == TQ_PROD ? q->bits - 1 : q->bits;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* rot = q->rot;
+  const float* proj = q->proj;
   if (q->split == TQ_SPLIT_OUTLIER32) {
     // the whole rotation as one block-structured matrix, built in the
     // prepared buffer from the caller's Π_o, Π_r and outlier channels
@@ -988,9 +1078,17 @@ extern "C" int tq_prepare(const tq_quantizer* q, void* stream) {
     hipLaunchKernelGGL(split_rotation_kernel, dim3(kD), dim3(kD), 0, s, q->rot_o, q->rot_r, ch, block);
     if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
     rot = block;
+    if (q->variant == TQ_PROD) {
+      // the sketch matrices in the same block structure (rows: sketch
+      // positions; columns: channels)
+      float* sblock = reinterpret_cast<float*>(static_cast<uint8_t*>(q->prep) + kPrepProjOff);
+      hipLaunchKernelGGL(split_rotation_kernel, dim3(kD), dim3(kD), 0, s, q->proj_o, q->proj_r, ch, sblock);
+      if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+      proj = sblock;
+    }
   }
-  hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, s, rot,
-                     q->variant == TQ_PROD ? q->proj : nullptr, q->centroids, bm,
+  hipLaunchKernelGGL(prepare_kernel, dim3(1), dim3(1024), 0, s, rot, q->variant == TQ_PROD ? proj : nullptr,
+                     q->centroids, bm,
                      q->rotation == TQ_ROT_HADAMARD ? 1 : 0,
                      q->split == TQ_SPLIT_OUTLIER32 ? q->centroids_o : nullptr, static_cast<uint8_t*>(q->prep));
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
@@ -1034,6 +1132,8 @@ int tq_split_append(const tq_quantizer* q, const void* x, int x_dtype, int64_t r
   a.stride = x_row_stride;
   a.codes = cache->codes;
   a.norms = cache->norms;
+  a.qjl = cache->qjl;
+  a.gammas = cache->gammas;
   a.prep = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(q->prep) + kPrepHeaderBytes);
   a.centroids = q->centroids;
   a.boundaries = q->boundaries;
@@ -1054,6 +1154,13 @@ const float* tq_rotation_matrix(const tq_quantizer* q) {
   return q->split == TQ_SPLIT_OUTLIER32
              ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(q->prep) + kPrepRotOff)
              : q->rot;
+}
+// The same for the sketch matrix S of a prod quantizer (null for mse).
+const float* tq_projection_matrix(const tq_quantizer* q) {
+  if (q->variant != TQ_PROD) return nullptr;
+  return q->split == TQ_SPLIT_OUTLIER32
+             ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(q->prep) + kPrepProjOff)
+             : q->proj;
 }
 int tq_device_cus() { return device_cus(); }
 

@@ -30,7 +30,9 @@ class Quantizer:
         randomized Walsh-Hadamard rotation H·diag(s)/√d). `split` =
         (rot_o, rot_r, channels) makes an outlier-channel split quantizer: the
         32 `channels` at bits + 1 bits with rotation rot_o (32×32), the other
-        96 at `bits` bits with rot_r (96×96); `rot` is then ignored."""
+        96 at `bits` bits with rot_r (96×96); `rot` is then ignored. A prod
+        split adds the groups' sketch matrices: (rot_o, rot_r, channels,
+        proj_o (32×32), proj_r (96×96)); `proj` is then ignored."""
         self.split = split is not None
         d = 128 if self.split else rot.shape[0]
         self.d, self.bits = d, bits
@@ -40,8 +42,8 @@ class Quantizer:
         self.centroids64, self.boundaries64 = c, t
         dev = torch.device(device)
         self.rot = None if self.split else torch.as_tensor(np.ascontiguousarray(rot, np.float32)).to(dev)
-        self.proj = None
-        if self.variant == L.TQ_PROD:
+        self.proj = self.proj_o = self.proj_r = None
+        if self.variant == L.TQ_PROD and not self.split:
             if proj is None:
                 raise ValueError("prod quantizer needs a projection")
             self.proj = torch.as_tensor(np.ascontiguousarray(proj, np.float32)).to(dev)
@@ -52,14 +54,19 @@ class Quantizer:
         self.centroids_o = self.boundaries_o = self.rot_o = self.rot_r = None
         self.channels_o = None
         if self.split:
-            rot_o, rot_r, channels = split
+            rot_o, rot_r, channels = split[:3]
             if np.shape(rot_o) != (32, 32) or np.shape(rot_r) != (96, 96) or np.size(channels) != 32:
                 raise ValueError("the split takes a 32x32 and a 96x96 rotation and 32 outlier channels")
+            if self.variant == L.TQ_PROD:
+                if len(split) != 5 or np.shape(split[3]) != (32, 32) or np.shape(split[4]) != (96, 96):
+                    raise ValueError("a prod split also takes the groups' 32x32 and 96x96 sketch matrices")
+                self.proj_o = torch.as_tensor(np.ascontiguousarray(split[3], np.float32)).to(dev)
+                self.proj_r = torch.as_tensor(np.ascontiguousarray(split[4], np.float32)).to(dev)
             self.rot_o = torch.as_tensor(np.ascontiguousarray(rot_o, np.float32)).to(dev)
             self.rot_r = torch.as_tensor(np.ascontiguousarray(rot_r, np.float32)).to(dev)
             # host memory: read by tq_prepare only
             self.channels_o = np.ascontiguousarray(np.asarray(channels).reshape(32), np.int32)
-            co, to, self.mse_unit_o = L.tq_codebook(32, bits + 1)
+            co, to, self.mse_unit_o = L.tq_codebook(32, self.bm + 1)
             self.centroids64_o, self.boundaries64_o = co, to
             self.centroids_o = torch.as_tensor(co.astype(np.float32)).to(dev)
             self.boundaries_o = torch.as_tensor(np.concatenate([to, [0.0]]).astype(np.float32)).to(dev)
@@ -68,12 +75,13 @@ class Quantizer:
                                 L.TQ_SPLIT_OUTLIER32 if self.split else L.TQ_SPLIT_NONE,
                                 _ptr(self.centroids_o), _ptr(self.boundaries_o), _ptr(self.rot_o),
                                 _ptr(self.rot_r),
-                                None if self.channels_o is None else self.channels_o.ctypes.data)
+                                None if self.channels_o is None else self.channels_o.ctypes.data,
+                                _ptr(self.proj_o), _ptr(self.proj_r))
         L.tq_prepare(self.c, _stream())
 
     @property
     def code_bytes(self) -> int:
-        return 16 * self.bits + 4 if self.split else self.d * self.bm // 8
+        return 16 * self.bm + 4 if self.split else self.d * self.bm // 8
 
     @property
     def norms_per_vector(self) -> int:
@@ -91,7 +99,7 @@ class Packed:
         self.qjl = self.gammas = None
         if q.variant == L.TQ_PROD:
             self.qjl = torch.zeros((n, q.d // 8), dtype=torch.uint8, device=dev)
-            self.gammas = torch.zeros(n, dtype=torch.float32, device=dev)
+            self.gammas = torch.zeros((n, 2) if q.split else n, dtype=torch.float32, device=dev)
         self.c = L.tq_packed(_ptr(self.codes) if q.code_bytes else None, _ptr(self.norms),
                              _ptr(self.qjl), _ptr(self.gammas))
 

@@ -17,9 +17,9 @@ import torch
 import synth
 from kv_cache_vector_06_amd import _lib as L
 from kv_cache_vector_06_amd import torch_api as T
-from oracle import (decode_attention, dequant_mse, dequant_prod, dequant_split, encode_mse, encode_prod,
-                    encode_split, lloyd_max, pack_codes, pack_split, split_positions, unpack_codes, unpack_signs,
-                    unpack_split)
+from oracle import (decode_attention, dequant_mse, dequant_prod, dequant_split, dequant_split_prod, encode_mse,
+                    encode_prod, encode_split, encode_split_prod, lloyd_max, pack_codes, pack_split,
+                    split_positions, unpack_codes, unpack_signs, unpack_split)
 
 D = 128
 DEV = "cuda:0"
@@ -232,13 +232,126 @@ def check_encode_split(gpu: dict, ref: dict, bits: int):
 
 
 def packed_from_oracle_split(enc: dict, q: T.Quantizer) -> T.Packed:
-    """Upload an oracle-produced split cache (norm pairs rounded to float32)
-    into guard-padded buffers."""
+    """Upload an oracle-produced split cache (norm and γ pairs rounded to
+    float32) into guard-padded buffers."""
     n = enc["norms"].shape[0]
     p = guarded_packed(q, n)
     p.codes.copy_(torch.from_numpy(np.ascontiguousarray(enc["codes"])))
     p.norms.copy_(torch.from_numpy(enc["norms"].astype(np.float32)))
+    if "qjl" in enc:
+        p.qjl.copy_(torch.from_numpy(np.ascontiguousarray(enc["qjl"])))
+        p.gammas.copy_(torch.from_numpy(enc["gammas"].astype(np.float32)))
     return p
+
+
+# ---------------------------------------------------------------------------
+# Outlier-channel split with prod keys: each group a TurboQuant-prod instance
+# (outlier: `bits` of Lloyd-Max for d = 32 plus a sketch; regular: bits - 1
+# for d = 96 plus a sketch)
+# ---------------------------------------------------------------------------
+
+def split_prod_books(bits):
+    """(outlier codebook: d = 32, bits; regular: d = 96, bits - 1) from the oracle."""
+    key = ("prod", bits)
+    if key not in _SPLIT_BOOKS:
+        _SPLIT_BOOKS[key] = (lloyd_max(32, bits), lloyd_max(96, bits - 1))
+    return _SPLIT_BOOKS[key]
+
+
+def split_prod_quantizer(bits):
+    c = synth.split_constants(D)
+    q = T.Quantizer(None, bits, "prod", None, DEV, split=(c["rk_o"], c["rk_r"], c["ch_k"], c["sk_o"], c["sk_r"]))
+    return q, (c["ch_k"], c["rk_o"], c["rk_r"], c["sk_o"], c["sk_r"])
+
+
+def oracle_encode_split_prod(X, consts, bits, chunk=8192):
+    ch, ro, rr, so, sr = consts
+    (co, _, _), (cr, _, _) = split_prod_books(bits)
+    outs = [encode_split_prod(X[i:i + chunk].astype(np.float64), ch, ro, rr, so, sr, co, cr, bits)
+            for i in range(0, X.shape[0], chunk)]
+    return {k: np.concatenate([o[k] for o in outs]) for k in outs[0]}
+
+
+def oracle_dequant_split_prod(enc, consts, bits):
+    ch, ro, rr, so, sr = consts
+    (co, _, _), (cr, _, _) = split_prod_books(bits)
+    return dequant_split_prod(enc["codes"], enc["norms"], enc["qjl"], enc["gammas"], ch, ro, rr, so, sr, co, cr,
+                              bits)
+
+
+def check_encode_split_prod(gpu: dict, ref: dict, bits: int):
+    """The encode parity rules for a split prod quantizer: both group norms
+    within 1e-6 relative; the code string is the packing of its codes (width
+    bits - 1, outlier positions one wider); a code may differ only where its
+    group's rotated value lies within 1e-6 of that group's boundary, on at
+    most 1e-5 of coordinates; on vectors whose codes all match, sketch bits
+    may differ only where the group's sketch value is below 1e-6 in
+    magnitude (at most 1e-5 of bits) and both γ lie within 1e-5 relative
+    (1e-6 absolute below 1e-6)."""
+    bm = bits - 1
+    gn, rn = gpu["norms"].astype(np.float64), ref["norms"]
+    nz = rn > 0
+    assert np.all(gn[~nz] == 0)
+    rel = np.abs(gn[nz] - rn[nz]) / rn[nz]
+    assert rel.max(initial=0) <= 1e-6, rel.max()
+    gidx = unpack_split(gpu["codes"], bm)
+    assert np.array_equal(pack_split(gidx, bm), gpu["codes"]), "code string is not the packing of its codes"
+    P_o, P_r = split_positions(D)
+    (_, to, _), (_, tr, _) = split_prod_books(bits)
+    mism = 0
+    vec_ok = np.ones(gidx.shape[0], bool)
+    for P, key, t in ((P_o, "y_o", to), (P_r, "y_r", tr)):
+        bad = gidx[:, P] != ref["idx"][:, P]
+        if t.size:
+            dist = np.min(np.abs(ref[key][..., None] - t), axis=-1)
+            assert np.all(dist[bad] < 1e-6), "code mismatch away from a boundary"
+        else:
+            assert not bad.any()
+        mism += int(bad.sum())
+        vec_ok &= ~bad.any(axis=1)
+    assert mism <= 1e-5 * gidx.size, (mism, gidx.size)
+    gs = unpack_signs(gpu["qjl"], D)
+    rs = unpack_signs(ref["qjl"], D)
+    z = np.zeros_like(gs, dtype=np.float64)
+    z[:, P_o] = ref["z_o"]
+    z[:, P_r] = ref["z_r"]
+    flips = (gs != rs) & vec_ok[:, None]
+    assert np.all(np.abs(z[flips]) < 1e-6), "sketch bit flipped away from zero"
+    assert flips.sum() <= 1e-5 * flips.size, (flips.sum(), flips.size)
+    gg = gpu["gammas"].astype(np.float64)[vec_ok]
+    rg = ref["gammas"][vec_ok]
+    big = rg > 1e-6
+    grel = np.abs(gg[big] - rg[big]) / rg[big]
+    assert grel.max(initial=0) <= 1e-5, grel.max()
+    assert np.all(np.abs(gg[~big] - rg[~big]) <= 1e-6)
+    return dict(norm_rel=float(rel.max(initial=0)), code_mismatch=mism, sketch_flips=int(flips.sum()),
+                gamma_rel=float(grel.max(initial=0)))
+
+
+def encode_split_prod_away_from_ties(X, consts, bits, seed, dtype):
+    """Oracle split prod encode of X; rows with a group-rotated coordinate
+    within 1e-6 of a boundary or a sketch value within 1e-6 of zero are
+    redrawn (in place) until none is. Uses the oracle only."""
+    (_, to, _), (_, tr, _) = split_prod_books(bits)
+    enc = oracle_encode_split_prod(X, consts, bits)
+    g = np.random.default_rng(seed)
+
+    def near(e):
+        out = (np.min(np.abs(e["y_o"][..., None] - to), axis=-1) < 1e-6).any(axis=1)
+        if tr.size:
+            out |= (np.min(np.abs(e["y_r"][..., None] - tr), axis=-1) < 1e-6).any(axis=1)
+        return out | (np.abs(e["z_o"]) < 1e-6).any(axis=1) | (np.abs(e["z_r"]) < 1e-6).any(axis=1)
+
+    for _ in range(20):
+        rows = np.nonzero(near(enc))[0]
+        if rows.size == 0:
+            return enc
+        new = X[rows] * (1 + 0.01 * g.standard_normal(X[rows].shape)).astype(np.float32)
+        X[rows] = synth.round_bf16(new) if dtype == "bf16" else new
+        sub = oracle_encode_split_prod(X[rows], consts, bits)
+        for k in enc:
+            enc[k][rows] = sub[k]
+    raise AssertionError("could not move rows away from ties")
 
 
 def encode_split_away_from_ties(X, consts, bits, seed, dtype):

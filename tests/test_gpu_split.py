@@ -8,9 +8,11 @@ import torch
 
 import synth
 from kv_cache_vector_06_amd import torch_api as T
-from gpu_util import (DEV, check_encode_split, encode_split_away_from_ties, gpu_packed_arrays,
-                      oracle_dequant_split, oracle_encode_split, packed_from_oracle_split, rel_l2_per_head, say,
-                      split_quantizer, to_gpu_x)
+from gpu_util import (DEV, assert_guards, check_encode_split, check_encode_split_prod, encode_split_away_from_ties,
+                      encode_split_prod_away_from_ties, gpu_packed_arrays, guarded_packed, oracle_dequant_split,
+                      oracle_dequant_split_prod, oracle_encode_split, oracle_encode_split_prod,
+                      packed_from_oracle_split, rel_l2_per_head, say, split_prod_quantizer, split_quantizer,
+                      to_gpu_x)
 from oracle import decode_attention
 
 pytestmark = pytest.mark.gpu
@@ -218,3 +220,33 @@ def test_split_step_matches_oracle():
     rel = rel_l2_per_head(out, ref)
     say("split step vs oracle rel L2 max", rel.max())
     assert rel.max() <= 1e-3, rel.max()
+
+
+# ---------------------------------------------------------------------------
+# Prod keys: each group a TurboQuant-prod instance with its own sketch and γ
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_split_prod_encode_parity(bits, dtype):
+    q, consts = split_prod_quantizer(bits)
+    n = 4096 + 37
+    X = synth.split_kv(1, 1, n, D, 1100 + bits, consts[0], dtype=dtype)[0, 0].copy()
+    X[5] = 0.0                                          # a zero vector
+    X[6, np.setdiff1d(np.arange(D), consts[0])] = 0.0   # an empty regular group
+    say("split prod encode", bits, dtype, n)
+    out = guarded_packed(q, n)
+    T.encode(q, to_gpu_x(X, dtype), out)
+    st = check_encode_split_prod(gpu_packed_arrays(out, q), oracle_encode_split_prod(X, consts, bits), bits)
+    say(st)
+    assert_guards(out)
+    # small encodes and a scatter into slots give the same rows
+    xg = to_gpu_x(X, dtype)
+    full = gpu_packed_arrays(out, q)
+    slots = torch.tensor([7, 2, 40, 0], dtype=torch.int64, device=DEV)
+    sc = T.Packed(q, 41, DEV)
+    T.encode(q, xg[:4], sc, slots)
+    g = gpu_packed_arrays(sc, q)
+    for i, s_ in enumerate([7, 2, 40, 0]):
+        for k in ("codes", "norms", "qjl", "gammas"):
+            np.testing.assert_array_equal(g[k][s_], full[k][i])

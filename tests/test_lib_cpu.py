@@ -219,7 +219,11 @@ def test_split_argument_errors_are_synchronous():
     assert enc(split_q(split=5)) == L.TQ_ERR_UNSUPPORTED
     assert enc(split_q(bits=4)) == L.TQ_ERR_UNSUPPORTED
     assert enc(split_q(bits=1)) == L.TQ_ERR_UNSUPPORTED
-    assert enc(split_q(bits=3, variant=L.TQ_PROD)) == L.TQ_ERR_UNSUPPORTED
+    # prod keys: the groups' sketch matrices are required
+    assert enc(split_q(bits=3, variant=L.TQ_PROD)) == L.TQ_ERR_INVALID_ARG
+    sp = split_q(bits=3, variant=L.TQ_PROD, proj_o=p, proj_r=p)
+    assert lib.tq_encode(byref(sp), p, L.TQ_BF16, 0, 128, byref(pk), None, None) == L.TQ_OK
+    assert enc(split_q(bits=3, variant=L.TQ_PROD, proj_o=p)) == L.TQ_ERR_INVALID_ARG
     assert enc(split_q(rotation=L.TQ_ROT_HADAMARD)) == L.TQ_ERR_UNSUPPORTED
     assert enc(split_q(centroids_o=None)) == L.TQ_ERR_INVALID_ARG
     assert enc(split_q(boundaries_o=None)) == L.TQ_ERR_INVALID_ARG
