@@ -581,16 +581,22 @@ def main():
         torch.cuda.empty_cache()
 
     # ---- outlier-channel split workloads ("2.5-bit": 32 channels at 3 bits + 96
-    # at 2, and "3.5-bit": 4 + 3; mse keys and values, a norm per group) at the
-    # headline's shape: encode of the key cache, the decode call (query
-    # operands, split attention, merge) over three cache copies in turn, and
-    # the split-attention launch alone after a 1 GiB read.
+    # at 2, and "3.5-bit": 4 + 3; mse or prod keys, mse values, a norm (and
+    # for prod a γ) per group) at the headline's shape: encode of the key
+    # cache, the decode call (query operands, split attention, merge) over
+    # three cache copies in turn, and the split-attention launch alone after
+    # a 1 GiB read.
     split_res = {}
     if not args.no_split:
-        for sname in ("gqa8_split25_128k_b4", "gqa8_split35_128k_b4"):
+        for sname in ("gqa8_split25_128k_b4", "gqa8_split35_128k_b4", "gqa8_splitprod25_128k_b4",
+                      "gqa8_splitprod35_128k_b4"):
             cs = synth.WORKLOADS[sname]
             sc = synth.split_constants(d)
-            kq6 = TA.Quantizer(None, cs.k_bits, "mse", None, dev, split=(sc["rk_o"], sc["rk_r"], sc["ch_k"]))
+            if cs.k_variant == "prod":
+                kq6 = TA.Quantizer(None, cs.k_bits, "prod", None, dev,
+                                   split=(sc["rk_o"], sc["rk_r"], sc["ch_k"], sc["sk_o"], sc["sk_r"]))
+            else:
+                kq6 = TA.Quantizer(None, cs.k_bits, "mse", None, dev, split=(sc["rk_o"], sc["rk_r"], sc["ch_k"]))
             vq6 = TA.Quantizer(None, cs.v_bits, "mse", None, dev, split=(sc["rv_o"], sc["rv_r"], sc["ch_v"]))
             K6, V6 = synth.make_kv(cs)
             k6 = torch.from_numpy(K6.reshape(-1, d)).to(torch.bfloat16).to(dev)
@@ -616,9 +622,10 @@ def main():
             us6 = flushed_split_us(dec6, kq6, vq6, q, kc6[0], vc6[0], out, 5)
             del kc6, vc6
             torch.cuda.empty_cache()
-            by6 = n6 * (kq6.code_bytes + 8 + vq6.code_bytes + 8)
+            tok6 = kq6.code_bytes + 8 + (16 + 8 if cs.k_variant == "prod" else 0) + vq6.code_bytes + 8
+            by6 = n6 * tok6
             split_res[cs.name] = {
-                "bytes_per_token_head": kq6.code_bytes + 8 + vq6.code_bytes + 8, "packed_cache_bytes": by6,
+                "bytes_per_token_head": tok6, "packed_cache_bytes": by6,
                 "decode_ms": round(ms6, 5), "decode_gbs": round(by6 / (ms6 * 1e-3) / 1e9, 1),
                 "split_after_flush_us": round(us6, 2), "split_gbs": round(by6 / us6 / 1e3, 1),
                 "frac": round(by6 / us6 / 1e3 / PEAK_HBM_GBS, 4),

@@ -1589,26 +1589,31 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
 //     p·n_r, with no extra product.
 // The staged block is the 32 tokens' code strings as they lie in memory
 // (rows of 16·b + 4 bytes, copied as dwords), followed by the norm pairs.
-template <int BK, int BV>
+// Prod keys (PROD) add the 32 tokens' sketch words (16 bytes each) and their
+// (γ_o, γ_r) pairs.
+template <int BK, int BV, bool PROD = false>
 struct OStage {
   static constexpr int KR = 16 * BK + 4, VR = 16 * BV + 4;   // code bytes per token
   static constexpr int kc = 0;
   static constexpr int vc = 32 * KR;
   static constexpr int kn = vc + 32 * VR;                     // 32 × (n_o, n_r)
   static constexpr int vn = kn + 256;
-  static constexpr int bytes = vn + 256;
+  static constexpr int qs = vn + 256;                         // PROD: 32 × 16 sketch bytes
+  static constexpr int kg = qs + 512;                         // PROD: 32 × (γ_o, γ_r)
+  static constexpr int bytes = PROD ? kg + 256 : vn + 256;
   static constexpr int kdw = 8 * KR, vdw = 8 * VR;            // dwords of the block's codes
   static constexpr int kld = (kdw + 63) / 64, vld = (vdw + 63) / 64;
-  static constexpr int dma = kld + vld + 2;                   // load instructions per block
+  static constexpr int dma = kld + vld + 2 + (PROD ? 3 : 0);  // load instructions per block
   static_assert(kn % 16 == 0, "norm pairs are read as 16-byte vectors");
 };
 
 // Issue the block's direct-to-LDS dword loads. Without AL, dwords past the
 // last token's row (or norm pair) are clamped to the last one of it.
-template <int BK, int BV, bool AL>
+template <int BK, int BV, bool AL, bool PROD = false>
 __device__ __forceinline__ void ostage_block(uint8_t* st, uint32_t t0, uint32_t last, int lane, const uint8_t* kc,
-                                             const uint8_t* vc, const float* kn, const float* vn) {
-  using L = OStage<BK, BV>;
+                                             const uint8_t* vc, const float* kn, const float* vn,
+                                             const uint8_t* kq = nullptr, const float* kg = nullptr) {
+  using L = OStage<BK, BV, PROD>;
   const uint32_t ntok = last + 1 - t0;   // tokens of the block that exist (AL: at least 32)
   const uint32_t* ks = reinterpret_cast<const uint32_t*>(kc + size_t(t0) * L::KR);
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(vc + size_t(t0) * L::VR);
@@ -1628,6 +1633,17 @@ __device__ __forceinline__ void ostage_block(uint8_t* st, uint32_t t0, uint32_t 
   const uint32_t nl = AL ? uint32_t(lane) : min(uint32_t(lane), 2u * ntok - 1u);
   __builtin_amdgcn_global_load_lds(kn + 2 * size_t(t0) + nl, TQ_LDS(st + L::kn), 4, 0, kStream);
   __builtin_amdgcn_global_load_lds(vn + 2 * size_t(t0) + nl, TQ_LDS(st + L::vn), 4, 0, kStream);
+  if constexpr (PROD) {
+    // sketch words (4 per token) and γ pairs, clamped like the rest
+    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(kq + size_t(t0) * 16);
+    const uint32_t qlim = AL ? 0u : ntok * 4u - 1u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t i = 64u * j + lane;
+      __builtin_amdgcn_global_load_lds(qsrc + (AL ? i : min(i, qlim)), TQ_LDS(st + L::qs + 256 * j), 4, 0, kStream);
+    }
+    __builtin_amdgcn_global_load_lds(kg + 2 * size_t(t0) + nl, TQ_LDS(st + L::kg), 4, 0, kStream);
+  }
 }
 
 // One lane's registers of a staged split block: its key words of both tiles
@@ -1637,6 +1653,8 @@ struct OBlock {
   uint32_t kw[2][4];
   float nko[8], nkr[8], nvo[8], nvr[8];
   uint32_t vw[8];
+  uint32_t qw[2];          // prod keys: sketch word g of tokens n and 16 + n
+  float gko[8], gkr[8];    // prod keys: the slots' scaled γ_o and γ_r, see oread_prod
 };
 
 struct OOffsets {
@@ -1729,6 +1747,37 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
   for (int j = 0; j < 8; ++j) R.vw[j] = __builtin_amdgcn_alignbit(vv[j][1], vv[j][0], vs);
 }
 
+// Prod keys: the lane's sketch words of both tiles (word g of tokens n and
+// 16 + n) and the 8 slots' γ pairs. The query's sketch operand carries the
+// correction scale √(π/2)/128 of a whole vector; a group's estimate takes
+// √(π/2)/d_g, so γ_o is scaled by 128/32 and γ_r by 128/96 here.
+template <int BK, int BV>
+__device__ __forceinline__ void oread_prod(OBlock& R, uint32_t sb, int n, int g) {
+  using L = OStage<BK, BV, true>;
+  const uint32_t aq = sb + L::qs + 16 * n + 4 * g, ag = sb + L::kg + 32 * g;
+  uint32_t q0, q1;
+  f32x4 g0, g1, g2, g3;
+  asm volatile(
+      "ds_read_b32 %[q0], %[aq]\n\t"
+      "ds_read_b32 %[q1], %[aq] offset:256\n\t"
+      "ds_read_b128 %[g0], %[ag]\n\t"
+      "ds_read_b128 %[g1], %[ag] offset:16\n\t"
+      "ds_read_b128 %[g2], %[ag] offset:128\n\t"
+      "ds_read_b128 %[g3], %[ag] offset:144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [q0] "=&v"(q0), [q1] "=&v"(q1), [g0] "=&v"(g0), [g1] "=&v"(g1), [g2] "=&v"(g2), [g3] "=&v"(g3)
+      : [aq] "v"(aq), [ag] "v"(ag)
+      : "memory");
+  R.qw[0] = q0;
+  R.qw[1] = q1;
+  const f32x4 gg[4] = {g0, g1, g2, g3};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    R.gko[j] = gg[j >> 1][2 * (j & 1)] * 4.0f;
+    R.gkr[j] = gg[j >> 1][2 * (j & 1) + 1] * (4.0f / 3.0f);
+  }
+}
+
 // Table rows of the split decode (the value pair tables fill the lower and the
 // upper half of rows 0..127; rows 128.. of the upper half hold key pairs):
 //   outlier value pairs  row e, byte 4c              (e = code0 | code1 << 4)
@@ -1763,10 +1812,15 @@ __device__ __forceinline__ void okey_operands(const uint32_t (&kw)[4], const uin
 // take the whole A operand against the query split by position: `bqo` keeps
 // the outlier slots (dword 0 of each fragment) and `bqr` the regular ones,
 // so no A operand needs masking (zero slots contribute exact zeros).
-template <int BK>
+//
+// Prod keys add each group's sketch product on the scaled fp4 × fp8 matrix
+// cores (as attn_split_kernel's): `bso` holds the query's sketch operand with
+// only the outlier positions kept, `bsr` with only the regular ones.
+template <int BK, bool PROD>
 __device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* tab, const uint8_t* tab2,
                                               uint32_t lane_hi, uint32_t lane8, const u32x4 (&bqo)[4],
-                                              const u32x4 (&bqr)[4], float (&sc)[8]) {
+                                              const u32x4 (&bqr)[4], const i32x8 (&bso)[2], const i32x8 (&bsr)[2],
+                                              int ssc0, int ssc1, float (&sc)[8]) {
   u32x4 af[2][4], aol[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -1774,6 +1828,11 @@ __device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* ta
     okey_operands<BK, 1>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][1], aol[t][1]);
     okey_operands<BK, 2>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][2], aol[t][2]);
     okey_operands<BK, 3>(R.kw[t], tab, tab2, lane_hi, lane8, af[t][3], aol[t][3]);
+  }
+  i32x8 sa[2];
+  if constexpr (PROD) {
+    sa[0] = sign_operand4(R.qw[0]);
+    sa[1] = sign_operand4(R.qw[1]);
   }
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -1785,6 +1844,18 @@ __device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* ta
       dmo = mfma(af[t][S], bqo[S], dmo);
       if constexpr (BK + 1 == 4) dmo = mfma(aol[t][S], bqo[S], dmo);
       dmr = mfma(af[t][S], bqr[S], dmr);
+    }
+    if constexpr (PROD) {
+      f32x4 dqo = f32x4{0.f, 0.f, 0.f, 0.f}, dqr = f32x4{0.f, 0.f, 0.f, 0.f};
+      dqo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[t], bso[0], dqo, 4, 0, 0, 127, 0, ssc0);
+      dqo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[t], bso[1], dqo, 4, 0, 0, 127, 0, ssc1);
+      dqr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[t], bsr[0], dqr, 4, 0, 0, 127, 0, ssc0);
+      dqr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[t], bsr[1], dqr, 4, 0, 0, 127, 0, ssc1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dmo[i] = fmaf(R.gko[4 * t + i], dqo[i], dmo[i]);
+        dmr[i] = fmaf(R.gkr[4 * t + i], dqr[i], dmr[i]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1803,11 +1874,12 @@ __device__ __forceinline__ uint32_t onibbles(uint32_t w) {
   return o | (to_nibbles<BV>(w >> (2 * BVO)) << 8);
 }
 
-template <int BK, int BV>
+template <int BK, int BV, bool PROD>
 __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint32_t t_end, int n, int g,
                                               const uint8_t* tab, const uint8_t* tab2, uint32_t lane_lo,
                                               uint32_t lane_hi, uint32_t lane8, const u32x4 (&bqo)[4],
-                                              const u32x4 (&bqr)[4], float iqs,
+                                              const u32x4 (&bqr)[4], const i32x8 (&bso)[2],
+                                              const i32x8 (&bsr)[2], int ssc0, int ssc1, float iqs,
                                               uint32_t lomask, SoftmaxState& st, f32x4 (&acc)[8]) {
   uint32_t X[4], Y[4];
 #pragma unroll
@@ -1817,7 +1889,7 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
     Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
   }
   float sc[8];
-  oblock_scores<BK>(R, tab, tab2, lane_hi, lane8, bqo, bqr, sc);
+  oblock_scores<BK, PROD>(R, tab, tab2, lane_hi, lane8, bqo, bqr, bso, bsr, ssc0, ssc1, sc);
   Luts Tv;
   Tv.v = tab;
   Tv.vlane = lane_lo;
@@ -1973,10 +2045,12 @@ __device__ __forceinline__ void build_tables_o(float cl, float vsig, float ksig,
     }
   }
   constexpr int KR = 1 << (2 * BK);   // regular key pair entries
-  for (int q = tid; q < KR * 8; q += nthr) {
+  // (whole wavefronts run the loop: the permutes in `cent` read every lane)
+  constexpr int NQR = (KR * 8 + 63) / 64 * 64;
+  for (int q = tid; q < NQR; q += nthr) {
     const int e = q >> 3;
-    const uint32_t w = pack_h2(cent(3, e & ((1 << BK) - 1), ks), cent(3, e >> BK, ks));
-    lds_put4(tb + 256 * (kKeyRegRow + e) + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
+    const uint32_t w = pack_h2(cent(3, e & ((1 << BK) - 1), ks), cent(3, (e >> BK) & ((1 << BK) - 1), ks));
+    if (e < KR) lds_put4(tb + 256 * (kKeyRegRow + e) + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
   }
   if constexpr (BKO == 4) {
     for (int q = tid; q < 256 * 8; q += nthr) {
@@ -1988,17 +2062,18 @@ __device__ __forceinline__ void build_tables_o(float cl, float vsig, float ksig,
       lds_put4(lds_addr(tab2) + 128 * e + 16 * (q & 7), u32x4{w0, w1, w0, w1});
     }
   } else {
-    for (int q = tid; q < 64 * 8; q += nthr) {
+    constexpr int KO = 1 << BKO;   // outlier key pair entries: e = code0 | code1 << BKO
+    for (int q = tid; q < KO * KO * 8; q += nthr) {
       const int e = q >> 3;
-      const uint32_t w = pack_h2(cent(2, e & 7, ks), cent(2, e >> 3, ks));
+      const uint32_t w = pack_h2(cent(2, e & (KO - 1), ks), cent(2, e >> BKO, ks));
       lds_put4(tb + 256 * (kKeyOutRow + e) + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
     }
   }
 }
 
-template <int BK, int BV, bool AL>
+template <int BK, int BV, bool AL, bool PROD>
 __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a) {
-  using SL = OStage<BK, BV>;
+  using SL = OStage<BK, BV, PROD>;
   constexpr int BKO = BK + 1, BVO = BV + 1;
   __shared__ __attribute__((aligned(256))) uint8_t tab[kTabBytes];
   __shared__ __attribute__((aligned(256))) uint8_t tab2[BKO == 4 ? 256 * 128 : 16];
@@ -2034,6 +2109,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const uint8_t* vc = a.vc + base * SL::VR;
   const float* kn = a.kn + 2 * base;
   const float* vn = a.vn + 2 * base;
+  const uint8_t* kqs = PROD ? a.kq + base * 16 : nullptr;
+  const float* kgs = PROD ? a.kg + 2 * base : nullptr;
 
   // the four codebooks, the scales σ and the query operands go out before
   // the first blocks' loads (as in attn_split_kernel)
@@ -2052,14 +2129,37 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
     bqo[s] = u32x4{v[0], 0u, 0u, 0u};
     bqr[s] = u32x4{0u, v[1], v[2], v[3]};
   }
+  // Prod keys: the query's sketch operand split by position. K index k of the
+  // operand is sketch coordinate 32(k/32) + 4c + m with k mod 32 = 8m + c; an
+  // outlier coordinate (mod 8 < 2) has c even and m < 2, i.e. k mod 32 even
+  // and below 16: the even bytes of lane groups 0 and 2.
+  i32x8 bso[2], bsr[2];
+  int ssc0 = 127, ssc1 = 127;
+  if constexpr (PROD) {
+    const i32x8* sk = reinterpret_cast<const i32x8*>(blk + kSkOff);
+    const int32_t mo = ((lane >> 4) & 1) ? 0 : 0x00FF00FF;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const i32x8 v = sk[h * 64 + lane];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        bso[h][d] = v[d] & mo;
+        bsr[h][d] = v[d] & ~mo;
+      }
+    }
+    const int32_t* ss = reinterpret_cast<const int32_t*>(blk + kSkScaleOff);
+    ssc0 = ss[lane];
+    ssc1 = ss[64 + lane];
+  }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   asm volatile("" ::: "memory");
   uint8_t* ring = &stage[wave][0];
   const uint32_t ring_addr = lds_addr(ring);
   const OOffsets so = ostage_offsets<BK, BV>(n, g);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
-  if (nblk > 0) ostage_block<BK, BV, AL>(ring, t_begin, last, lane, kc, vc, kn, vn);
-  if (nblk > 1) ostage_block<BK, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, vc, kn, vn);
+  if (nblk > 0) ostage_block<BK, BV, AL, PROD>(ring, t_begin, last, lane, kc, vc, kn, vn, kqs, kgs);
+  if (nblk > 1)
+    ostage_block<BK, BV, AL, PROD>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, vc, kn, vn, kqs, kgs);
 
   build_tables_o<BK, BV>(cl, vsig, ksig, tab, tab2, tid, nthr);
   if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
@@ -2086,27 +2186,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
       oread_block<BK, BV, SL::dma>(R, sb, so, prog_partner, pw);
     else
       oread_block<BK, BV, 0>(R, sb, so, prog_partner, pw);
+    if constexpr (PROD) oread_prod<BK, BV>(R, sb, n, g);
     if (__builtin_amdgcn_readfirstlane(pw) < i)
       __builtin_amdgcn_s_setprio(0);
     else
       __builtin_amdgcn_s_setprio(1);
     if (i + 2 < nblk) {
       const int nx = (cur + 2) % kStages;
-      ostage_block<BK, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, vc, kn, vn);
+      ostage_block<BK, BV, AL, PROD>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, vc, kn, vn, kqs,
+                                     kgs);
     }
-    oattend_block<BK, BV>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bqo, bqr, iqs, lomask, st, acc);
+    oattend_block<BK, BV, PROD>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bqo, bqr, bso, bsr, ssc0,
+                                ssc1, iqs, lomask, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
   }
   __builtin_amdgcn_s_setprio(0);
   write_partials_o<kRing>(a, st, acc, wm, wl, stage, unit, split, gc, n, g, wave, tid);
 }
 
-template <int BK, int BV>
+template <int BK, int BV, bool PROD = false>
 hipError_t launch_outlier_t(const AttnArgs& a, bool al, dim3 grid, hipStream_t st) {
   if (al)
-    hipLaunchKernelGGL((attn_outlier_kernel<BK, BV, true>), grid, dim3(kDecWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_outlier_kernel<BK, BV, true, PROD>), grid, dim3(kDecWaves * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_outlier_kernel<BK, BV, false>), grid, dim3(kDecWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_outlier_kernel<BK, BV, false, PROD>), grid, dim3(kDecWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -2720,7 +2823,6 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
       return TQ_ERR_INVALID_ARG;
     if (int64_t(B) * Hkv > (int64_t(1) << 30)) return TQ_ERR_UNSUPPORTED;
   }
-  if (osplit && prod) return TQ_ERR_UNSUPPORTED;
   const Plan p = make_plan(B, Hq, Hkv, max_ctx);
   if (ws_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TQ_ERR_WORKSPACE;
   if (checks_only) return TQ_OK;
@@ -2784,7 +2886,13 @@ int decode_call(int phase, const tq_quantizer* kq, const tq_quantizer* vq, const
     const int bv = vq->bits;
     const bool al = (max_ctx % kBlockTok) == 0;
     hipError_t e;
-    if (osplit) {
+    if (osplit && prod) {
+      // prod keys: regular Lloyd-Max width bits - 1 (1 or 2)
+      if (bk == 1)
+        e = bv == 2 ? launch_outlier_t<1, 2, true>(aa, al, grid, s) : launch_outlier_t<1, 3, true>(aa, al, grid, s);
+      else
+        e = bv == 2 ? launch_outlier_t<2, 2, true>(aa, al, grid, s) : launch_outlier_t<2, 3, true>(aa, al, grid, s);
+    } else if (osplit) {
       if (bk == 2)
         e = bv == 2 ? launch_outlier_t<2, 2>(aa, al, grid, s) : launch_outlier_t<2, 3>(aa, al, grid, s);
       else

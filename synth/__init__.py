@@ -181,6 +181,10 @@ _ALL = (
     # "3.5-bit": 4 + 3), mse keys and values, the benchmark's shape
     DecodeConfig("gqa8_split25_128k_b4", 4, 8, 64, 131072, 128, "mse", 2, 2, "split", "bf16", 60, True),
     DecodeConfig("gqa8_split35_128k_b4", 4, 8, 64, 131072, 128, "mse", 3, 3, "split", "bf16", 70, True),
+    # the same split with prod keys (each group a prod instance: 32 channels
+    # at 3 bits + 96 at 2, or 4 + 3, counting the sketch bit), mse values
+    DecodeConfig("gqa8_splitprod25_128k_b4", 4, 8, 64, 131072, 128, "prod", 2, 2, "split", "bf16", 80, True),
+    DecodeConfig("gqa8_splitprod35_128k_b4", 4, 8, 64, 131072, 128, "prod", 3, 3, "split", "bf16", 90, True),
 )
 WORKLOADS = {c.name: c for c in _ALL}
 # The five unsplit decode workloads, smallest first.

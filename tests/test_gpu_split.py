@@ -120,19 +120,22 @@ def test_split_encode_then_decode(bk, bv):
     assert rel.max() <= 1e-3, rel.max()
 
 
-@pytest.mark.parametrize("name", ["gqa8_split25_128k_b4", "gqa8_split35_128k_b4"])
+@pytest.mark.parametrize("name", ["gqa8_split25_128k_b4", "gqa8_split35_128k_b4", "gqa8_splitprod25_128k_b4",
+                                  "gqa8_splitprod35_128k_b4"])
 def test_split_full_size_benchmark_shape_sampled(name):
     # The split workloads' launch configuration: batch 4 x 8 KV heads x 131072
-    # tokens, 64 query heads, split keys and values; GPU encode + decode, the
-    # oracle evaluates two (batch, KV head) units.
+    # tokens, 64 query heads, split keys (mse or prod) and values; GPU encode
+    # + decode, the oracle evaluates two (batch, KV head) units.
     cfg = synth.WORKLOADS[name]
-    kq, kcst = split_quantizer(cfg.k_bits, "k")
+    prod = cfg.k_variant == "prod"
+    kq, kcst = split_prod_quantizer(cfg.k_bits) if prod else split_quantizer(cfg.k_bits, "k")
     vq, vcst = split_quantizer(cfg.v_bits, "v")
     say("generating", cfg.name)
     K, V = synth.make_kv(cfg)
     q = synth.make_query(cfg)
     units = ((0, 1), (3, 7))
-    encs = {u: (encode_split_away_from_ties(K[u], kcst, cfg.k_bits, 700 + 2 * u[1] + 17 * u[0], cfg.dtype),
+    kenc = encode_split_prod_away_from_ties if prod else encode_split_away_from_ties
+    encs = {u: (kenc(K[u], kcst, cfg.k_bits, 700 + 2 * u[1] + 17 * u[0], cfg.dtype),
                 encode_split_away_from_ties(V[u], vcst, cfg.v_bits, 701 + 2 * u[1] + 17 * u[0], cfg.dtype))
             for u in units}
     kp = T.encode(kq, to_gpu_x(K.reshape(-1, D), cfg.dtype))
@@ -140,7 +143,7 @@ def test_split_full_size_benchmark_shape_sampled(name):
     dec = T.Decoder(cfg.B, cfg.Hq, cfg.Hkv, cfg.T, DEV)
     out = dec(kq, vq, torch.from_numpy(q).to(DEV), kp, vp).cpu().numpy().astype(np.float64)
     for (b, kvh) in units:
-        Kt = oracle_dequant_split(encs[(b, kvh)][0], kcst, cfg.k_bits)
+        Kt = (oracle_dequant_split_prod if prod else oracle_dequant_split)(encs[(b, kvh)][0], kcst, cfg.k_bits)
         Vt = oracle_dequant_split(encs[(b, kvh)][1], vcst, cfg.v_bits)
         hs = list(range(kvh * cfg.G, (kvh + 1) * cfg.G))
         ref = decode_attention(q[b:b + 1, hs], Kt[None, None], Vt[None, None], 1.0 / np.sqrt(D))
@@ -250,3 +253,80 @@ def test_split_prod_encode_parity(bits, dtype):
     for i, s_ in enumerate([7, 2, 40, 0]):
         for k in ("codes", "norms", "qjl", "gammas"):
             np.testing.assert_array_equal(g[k][s_], full[k][i])
+
+
+def _split_prod_case(bits, bv, B, Hkv, Hq, Tn, seed):
+    # prod keys, mse values; rows near a tie are redrawn (oracle only)
+    kq, kcst = split_prod_quantizer(bits)
+    vq, vcst = split_quantizer(bv, "v")
+    K = synth.split_kv(B, Hkv, Tn, D, seed, kcst[0], dtype="bf16")
+    V = synth.split_kv(B, Hkv, Tn, D, seed + 1, vcst[0], dtype="bf16")
+    ek = encode_split_prod_away_from_ties(K.reshape(-1, D), kcst, bits, seed + 3, "bf16")
+    ev = encode_split_away_from_ties(V.reshape(-1, D), vcst, bv, seed + 4, "bf16")
+    Kt = oracle_dequant_split_prod(ek, kcst, bits).reshape(B, Hkv, Tn, D)
+    Vt = oracle_dequant_split(ev, vcst, bv).reshape(B, Hkv, Tn, D)
+    q = synth.gaussian((B, Hq, D), seed + 2, "fp32")
+    return kq, vq, K, V, ek, ev, Kt, Vt, q
+
+
+@pytest.mark.parametrize("bits,bv", [(3, 3), (2, 2), (3, 2), (2, 3)])
+@pytest.mark.parametrize("Tn", [2048, 1000])
+def test_split_prod_decode_parity(bits, bv, Tn):
+    # the oracle's own packed caches (prod keys at 2.5 or 3.5 bits, mse
+    # values): 2 batches, 2 KV heads, 16 query heads, an aligned and a
+    # ragged context, then ragged lengths per batch
+    B, Hkv, Hq = 2, 2, 16
+    kq, vq, K, V, ek, ev, Kt, Vt, q = _split_prod_case(bits, bv, B, Hkv, Hq, Tn, 1200 + 10 * bits + bv)
+    say("split prod decode", bits, bv, Tn)
+    scale = 1.0 / np.sqrt(D)
+    kc = packed_from_oracle_split(ek, kq)
+    vc = packed_from_oracle_split(ev, vq)
+    dec = T.Decoder(B, Hq, Hkv, Tn, DEV)
+    for lens in (None, np.array([Tn - 7, 33], np.int32)):
+        ref = decode_attention(q, Kt, Vt, scale, ctx_lens=lens)
+        lg = None if lens is None else torch.from_numpy(lens).to(DEV)
+        out = dec(kq, vq, torch.from_numpy(q).to(DEV), kc, vc, ctx_lens=lg).cpu().numpy().astype(np.float64)
+        rel = rel_l2_per_head(out, ref)
+        say("  lens", lens, "max rel L2", rel.max())
+        assert rel.max() <= 1e-3, rel.max()
+    assert_guards(kc, vc)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_split_prod_step_matches_oracle_and_unfused(bits):
+    # the step appends the last token of each (batch, KV head) through the
+    # split prod encoder; the output matches the oracle, and equals the
+    # unfused encode into the slots followed by the decode, bit for bit
+    B, Hkv, Hq, Tn, bv = 2, 2, 16, 900, 3
+    lens = [Tn, 500]
+    kq, vq, K, V, ek, ev, Kt, Vt, q = _split_prod_case(bits, bv, B, Hkv, Hq, Tn, 1300 + bits)
+    ref = decode_attention(q, Kt, Vt, 1.0 / np.sqrt(D), ctx_lens=lens)
+    new_idx = np.array([(b * Hkv + h) * Tn + lens[b] - 1 for b in range(B) for h in range(Hkv)])
+    kn, vn = K.reshape(-1, D)[new_idx], V.reshape(-1, D)[new_idx]
+    sl = torch.from_numpy(new_idx).to(DEV)
+    kc, vc = packed_from_oracle_split(ek, kq), packed_from_oracle_split(ev, vq)
+    ka, va = packed_from_oracle_split(ek, kq), packed_from_oracle_split(ev, vq)
+    for p in (kc, vc, ka, va):                           # the appends must write these slots
+        p.codes[sl] = 0
+        p.norms[sl] = 0
+        if p.qjl is not None:
+            p.qjl[sl] = 0
+            p.gammas[sl] = 0
+    dec = T.Decoder(B, Hq, Hkv, Tn, DEV)
+    qg = torch.from_numpy(q).to(DEV)
+    lg = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kng, vng = to_gpu_x(kn, "bf16"), to_gpu_x(vn, "bf16")
+    out = dec.step(kq, vq, kng, vng, qg, kc, vc, lg)
+    T.encode(kq, kng, ka, sl)
+    T.encode(vq, vng, va, sl)
+    out_u = dec(kq, vq, qg, ka, va, lg)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out_u.view(torch.int32))
+    gk, gv = gpu_packed_arrays(kc, kq), gpu_packed_arrays(vc, vq)
+    sub = lambda e: {k: v[new_idx] for k, v in e.items()}
+    check_encode_split_prod(sub(gk), sub(ek), bits)
+    check_encode_split(sub(gv), sub(ev), bv)
+    rel = rel_l2_per_head(out.cpu().numpy().astype(np.float64), ref)
+    say("split prod step vs oracle rel L2 max", rel.max())
+    assert rel.max() <= 1e-3, rel.max()
+    assert_guards(kc, vc)
