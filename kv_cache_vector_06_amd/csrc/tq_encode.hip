@@ -408,13 +408,27 @@ __device__ __forceinline__ int build_cell(const Book& bk, int k, CellEntry<PROD>
   return inside > 1;
 }
 
+// Wavefronts per workgroup of the full-size encoder. mse encodes with a cell
+// table (b_m >= 3) run one workgroup of 16 wavefronts per compute unit
+// sharing one staged copy of the fragments and a conflict-free table (below);
+// the others two workgroups of 8.
+template <int BM, bool PROD>
+constexpr int enc_waves() { return (BM >= 3 && !PROD) ? 16 : kEncWaves; }
+
 template <int BM, bool PROD, bool F32IN>
-__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
-  __shared__ u32x4 lds_rot[kFragsPerSet * 64];
-  __shared__ u32x4 lds_proj[PROD ? kFragsPerSet * 64 : 1];
+__global__ __launch_bounds__((enc_waves<BM, PROD>() * 64)) void encode_kernel(EncodeArgs a) {
   constexpr int K = 1 << BM;
   constexpr bool kCells = BM >= 3;
-  __shared__ CellEntry<PROD> lds_cells[kCells ? 256 : 1];
+  constexpr int kW = enc_waves<BM, PROD>();
+  // mse: 32 interleaved copies of the cell table (entry k of copy c at
+  // 256k + 8c bytes, c = lane % 32), so the 32 lanes of a half-wavefront read
+  // 32 different bank pairs whatever their cells; prod (16-byte entries,
+  // with S' staged too) keeps one copy. (Declared first: at LDS offset 0 the
+  // lookups need no base address.)
+  constexpr int kCellCopies = (kCells && !PROD) ? 32 : 1;
+  __shared__ __attribute__((aligned(256))) CellEntry<PROD> lds_cells[kCells ? 256 * kCellCopies : 1];
+  __shared__ u32x4 lds_rot[kFragsPerSet * 64];
+  __shared__ u32x4 lds_proj[PROD ? kFragsPerSet * 64 : 1];
   const u32x4* frot = lds_rot;
   const u32x4* fproj = lds_proj;
 
@@ -438,6 +452,18 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   int bad_cell = 0;
   if constexpr (kCells) {
     if (threadIdx.x < 256) bad_cell = build_cell<BM, PROD>(bk, threadIdx.x, lds_cells);
+    if constexpr (kCellCopies > 1) {
+      // entry k was built at index k; spread it to its copies at 32k + c
+      // (every (k, c) read before any is written)
+      constexpr int kPer = 256 * kCellCopies / (kW * 64);
+      __syncthreads();
+      CellEntry<PROD> e[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) e[r] = lds_cells[(threadIdx.x + kW * 64 * r) >> 5];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) lds_cells[threadIdx.x + kW * 64 * r] = e[r];
+    }
   }
   // A full barrier (with its memory fence) publishes the table; then the vote.
   __syncthreads();
@@ -445,8 +471,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
+  const uint32_t cell_lane = 8u * uint32_t(lane & 31);   // the lane's table copy
   const int64_t ntiles = (a.n + 15) / 16;
-  const int64_t tstride = int64_t(gridDim.x) * kEncWaves;
+  const int64_t tstride = int64_t(gridDim.x) * kW;
   // Raw input words of this lane's row for one tile: columns 32s + 8g + j.
   // The next tile's words are loaded while the current one is computed.
   constexpr int kRaw = F32IN ? 8 : 4;
@@ -471,7 +498,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     constexpr bool USE = decltype(use_tag)::value;
     // (bf16 input only; fp32 input, twice the registers, loads its tile in place.)
     u32x4 raw_next[kRaw];
-    int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave;
+    int64_t tile = int64_t(blockIdx.x) * kW + wave;
     if (!F32IN && tile < ntiles) load_raw(tile, raw_next);
     for (; tile < ntiles; tile += tstride) {
       u32x4 raw[kRaw];
@@ -593,7 +620,10 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
               code = e[0] + (up1 ? 1u : 0u);
               cell_c = __uint_as_float(up1 ? e[3] : e[2]);
             } else {
-              const u32x2 e = lds_cells[k];
+              // byte offset 256·cell + 8·(lane % 32): the conversion writes the
+              // cell into byte 1 of the lane's copy offset
+              const uint32_t off = __builtin_amdgcn_cvt_pk_u8_f32(f, 1, cell_lane);
+              const u32x2 e = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(lds_cells) + off);
               code = e[0] + (acc[t][j] > __uint_as_float(e[1]) * S ? 1u : 0u);
             }
           } else {
@@ -970,9 +1000,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_split_kernel(EncodeArgs
 template <int BM, bool PROD>
 hipError_t launch_encode_t(const EncodeArgs& a, bool f32in, int grid, hipStream_t st) {
   if (f32in)
-    hipLaunchKernelGGL((encode_kernel<BM, PROD, true>), dim3(grid), dim3(kEncWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((encode_kernel<BM, PROD, true>), dim3(grid), dim3(enc_waves<BM, PROD>() * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((encode_kernel<BM, PROD, false>), dim3(grid), dim3(kEncWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((encode_kernel<BM, PROD, false>), dim3(grid), dim3(enc_waves<BM, PROD>() * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1217,8 +1247,11 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
     hipLaunchKernelGGL(row_encode_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kRowWaves * 64), 0, s, r);
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
   }
-  const int64_t want = (tiles + kEncWaves - 1) / kEncWaves;
-  const int cap = device_cus() * (prod ? 1 : 2);
+  // one workgroup of 16 wavefronts per compute unit for mse with a cell
+  // table, two of 8 for the other mse encodes, one of 8 for prod
+  const int waves = (!prod && bm >= 3) ? 16 : kEncWaves;
+  const int64_t want = (tiles + waves - 1) / waves;
+  const int cap = device_cus() * ((prod || bm >= 3) ? 1 : 2);
   const int grid = static_cast<int>(want < cap ? want : cap);
   const bool f32 = x_dtype == TQ_F32;
   hipError_t e;
