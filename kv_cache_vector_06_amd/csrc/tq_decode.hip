@@ -1808,7 +1808,9 @@ __device__ __forceinline__ void okey_operands(const uint32_t (&kw)[4], const uin
   af[3] = *reinterpret_cast<const uint32_t*>(kb + (field_shl<base + 2 * BKO + 4 * BK, 2 * BK, 8>(kw) + lane_hi));
 }
 
-// Scores of a split block (the score is sc·iqs). The two products per K-step
+// Column n's parts of a split block's scores (head n % 8; columns h and
+// h + 8 hold the query's hi and lo parts, and their sum times iqs is the
+// score). The two products per K-step
 // take the whole A operand against the query split by position: `bqo` keeps
 // the outlier slots (dword 0 of each fragment) and `bqr` the regular ones,
 // so no A operand needs masking (zero slots contribute exact zeros).
@@ -1860,7 +1862,7 @@ __device__ __forceinline__ void oblock_scores(const OBlock& R, const uint8_t* ta
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * t + i;
-      sc[j] = add_ror8(fmaf(R.nko[j], dmo[i], R.nkr[j] * dmr[i]));
+      sc[j] = fmaf(R.nko[j], dmo[i], R.nkr[j] * dmr[i]);   // column n's part of slot j's score
     }
   }
 }
@@ -1880,7 +1882,7 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
                                               uint32_t lane_hi, uint32_t lane8, const u32x4 (&bqo)[4],
                                               const u32x4 (&bqr)[4], const i32x8 (&bso)[2],
                                               const i32x8 (&bsr)[2], int ssc0, int ssc1, float iqs,
-                                              uint32_t lomask, SoftmaxState& st, f32x4 (&acc)[8]) {
+                                              bool own1, SoftmaxState& st, f32x4 (&acc)[8]) {
   uint32_t X[4], Y[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -1888,8 +1890,8 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
     X[k] = (a0 & 0x0f0f0f0fu) | ((a1 << 4) & 0xf0f0f0f0u);
     Y[k] = ((a0 >> 4) & 0x0f0f0f0fu) | (a1 & 0xf0f0f0f0u);
   }
-  float sc[8];
-  oblock_scores<BK, PROD>(R, tab, tab2, lane_hi, lane8, bqo, bqr, bso, bsr, ssc0, ssc1, sc);
+  float part[8];
+  oblock_scores<BK, PROD>(R, tab, tab2, lane_hi, lane8, bqo, bqr, bso, bsr, ssc0, ssc1, part);
   Luts Tv;
   Tv.v = tab;
   Tv.vlane = lane_lo;
@@ -1903,26 +1905,35 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
   bv[5] = pv_operand<5>(X, Y, Tv);
   bv[6] = pv_operand<6>(X, Y, Tv);
   bv[7] = pv_operand<7>(X, Y, Tv);
-  float nvo[8], nvr[8];
+  // Each lane finishes the scores of its own 16-token tile (tile 0 for
+  // n < 8, tile 1 for n >= 8), taking the other column half of them from
+  // lane n ^ 8, as in attn_split_kernel.
+  float sc[4], nvo[4], nvr[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    nvo[j] = R.nvo[j];
-    nvr[j] = R.nvr[j];
+  for (int i = 0; i < 4; ++i) {
+    const float own = own1 ? part[4 + i] : part[i];
+    const float oth = own1 ? part[i] : part[4 + i];
+    sc[i] = own + ror8(oth);
+    nvo[i] = own1 ? R.nvo[4 + i] : R.nvo[i];
+    nvr[i] = own1 ? R.nvr[4 + i] : R.nvr[i];
   }
   if (__builtin_expect(t0 + kBlockTok > t_end, 0)) {
+    const uint32_t tb = t0 + (own1 ? 16u : 0u) + 4u * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = t0 + 16 * (j >> 2) + 4 * g + (j & 3) < t_end;
-      sc[j] = ok ? sc[j] : -INFINITY;
-      nvo[j] = ok ? nvo[j] : 0.f;
-      nvr[j] = ok ? nvr[j] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = tb + i < t_end;
+      sc[i] = ok ? sc[i] : -INFINITY;
+      nvo[i] = ok ? nvo[i] : 0.f;
+      nvr[i] = ok ? nvr[i] : 0.f;
     }
   }
-  const float mloc = max8f(sc) * iqs;
-  const float nvl = fmaxf(max8f(nvo), max8f(nvr));
+  const float mloc = max4f(sc[0], sc[1], sc[2], sc[3]) * iqs;
+  const float nvl = fmaxf(max4f(nvo[0], nvo[1], nvo[2], nvo[3]), max4f(nvr[0], nvr[1], nvr[2], nvr[3]));
   if (__builtin_expect(__any(mloc > st.m + kLazy || nvl > st.nvs), 0)) {
-    const float mg = max4g(mloc);
-    const float nvw = max4g(nvl);
+    float mg = max4g(mloc);
+    mg = fmaxf(mg, ror8(mg));               // this block's max for the head
+    float nvw = max4g(nvl);
+    nvw = fmaxf(nvw, ror8(nvw));            // and of the value norms (every lane)
     const float m_new = mg > st.m + kLazy ? mg : st.m;
     float nvs_new = st.nvs, knv_new = st.knv;
     if (nvw > st.nvs) {
@@ -1936,7 +1947,7 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
     st.l *= f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float fi = __shfl(f, (4 * g + i) & 7, 64);
+      const float fi = __shfl(f, (4 * g + i) & 7, 64);   // row 4g+i holds head (4g+i)%8
 #pragma unroll
       for (int r = 0; r < 8; ++r) acc[r][i] *= fi;
     }
@@ -1946,23 +1957,24 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
     st.knv = knv_new;
   }
   // A operands of P·V: weights p·n_o for the outlier products (r = 0, 1),
-  // p·n_r for the others; rows n < 8 the fp16 hi part, rows n + 8 the lo part.
-  u32x4 pao, par;
+  // p·n_r for the others, as fp16 rounded to nearest (kRoundUp); row n < 8
+  // carries head n's weights of tile 0, row n + 8 those of tile 1, and rows h
+  // and h + 8 of the result are summed at the end.
   const float nmk = -st.mk;
+  float wo[4], wr[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float xo[2], xr[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sc[2 * k + e], iqs, nmk));
-      st.l += p;
-      const float wo = p * nvo[2 * k + e], wr = p * nvr[2 * k + e];
-      xo[e] = wo - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, wo) & lomask);
-      xr[e] = wr - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, wr) & lomask);
-    }
-    pao[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xo[0], xo[1]));
-    par[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xr[0], xr[1]));
+  for (int i = 0; i < 4; ++i) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], iqs, nmk));
+    st.l += p;
+    wo[i] = p * (nvo[i] * kRoundUp);
+    wr[i] = p * (nvr[i] * kRoundUp);
   }
+  const uint32_t xo0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(wo[0], wo[1]));
+  const uint32_t xo1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(wo[2], wo[3]));
+  const uint32_t xr0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(wr[0], wr[1]));
+  const uint32_t xr1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(wr[2], wr[3]));
+  const u32x4 pao = own1 ? u32x4{0u, 0u, xo0, xo1} : u32x4{xo0, xo1, 0u, 0u};
+  const u32x4 par = own1 ? u32x4{0u, 0u, xr0, xr1} : u32x4{xr0, xr1, 0u, 0u};
   acc[0] = mfma(pao, bv[0], acc[0]);
   acc[1] = mfma(pao, bv[1], acc[1]);
 #pragma unroll
@@ -1970,15 +1982,17 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
 }
 
 // The workgroup's partials of a split (as in attn_split_kernel), with each
-// head's rows of hi and lo weights (lane groups g and g + 2) added before they
-// are staged, so a wavefront stages 8 rows of 128 floats (4 KiB).
+// head's rows of tile-0 and tile-1 weights (lane groups g and g + 2) added
+// before they are staged, so a wavefront stages 8 rows of 128 floats (4 KiB).
+// Lanes n and n ^ 8 hold the running sums of the two tiles of head n % 8.
 template <int RING>
 __device__ __forceinline__ void write_partials_o(const AttnArgs& a, const SoftmaxState& st, const f32x4 (&acc)[8],
                                                  float (&wm)[kDecWaves][kMaxHeads], float (&wl)[kDecWaves][kMaxHeads],
                                                  uint8_t (&stage)[kDecWaves][RING], int unit, int split, int gc,
                                                  int n, int g, int wave, int tid) {
   static_assert(RING >= kMaxHeads * kD * 4, "accumulator rows");
-  const float l_run = sum4g(st.l);
+  float l_run = sum4g(st.l);
+  l_run += ror8(l_run);
   if (g == 0 && n < kMaxHeads) {
     wm[wave][n] = st.mk;
     wl[wave][n] = l_run;
@@ -2166,7 +2180,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   lds_stores_done();
   const uint32_t cp = lane & 31;
   const uint32_t lane_lo = 4u * cp, lane_hi = kTabK + 4u * cp, lane8 = 8u * (lane & 15);
-  const uint32_t lomask = n >= 8 ? 0xFFFFE000u : 0u;
+  const bool own1 = n >= 8;                 // the lane's own tile: tokens 16..31 of each block
   tables_barrier();
 
   SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
@@ -2197,7 +2211,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
                                      kgs);
     }
     oattend_block<BK, BV, PROD>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bqo, bqr, bso, bsr, ssc0,
-                                ssc1, iqs, lomask, st, acc);
+                                ssc1, iqs, own1, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
   }
   __builtin_amdgcn_s_setprio(0);
