@@ -457,6 +457,50 @@ __device__ __forceinline__ uint32_t row_addr(uint32_t w, uint32_t lane_off) {
   return __builtin_amdgcn_perm(w, lane_off, 0x03020000u | ((4u + B) << 8));
 }
 
+// The same for byte B (0..11) of a 96-bit string held in three words.
+template <int B>
+__device__ __forceinline__ uint32_t byte_addr(const uint32_t (&w)[3], uint32_t lane_off) {
+  return row_addr<B & 3>(w[B >> 2], lane_off);
+}
+
+// 3-bit keys with the replicated pair table (row r holds pair r & 63, so
+// the two bits above a 6-bit field do not matter): pair field f of the lane's
+// 96-bit code string starts at bit 6f, i.e. at bit 0, 6, 4 or 2 of a byte for
+// f mod 4 = 0, 1, 2, 3. The string shifted right by 6, 4 and 2 bits puts
+// every field at the bottom of a byte, and one byte permute per field then
+// forms its table address (nine funnel shifts per tile instead of one shift
+// per field).
+struct KeyShifts {
+  uint32_t s6[3], s4[3], s2[3];
+};
+__device__ __forceinline__ KeyShifts key_shifts(const uint32_t (&w)[3]) {
+  KeyShifts k;
+  k.s6[0] = __builtin_amdgcn_alignbit(w[1], w[0], 6);
+  k.s6[1] = __builtin_amdgcn_alignbit(w[2], w[1], 6);
+  k.s6[2] = w[2] >> 6;
+  k.s4[0] = __builtin_amdgcn_alignbit(w[1], w[0], 4);
+  k.s4[1] = __builtin_amdgcn_alignbit(w[2], w[1], 4);
+  k.s4[2] = w[2] >> 4;
+  k.s2[0] = __builtin_amdgcn_alignbit(w[1], w[0], 2);
+  k.s2[1] = __builtin_amdgcn_alignbit(w[2], w[1], 2);
+  k.s2[2] = w[2] >> 2;
+  return k;
+}
+
+// A operand of K-step S (fields 4S .. 4S + 3, in bytes 3S of the unshifted
+// and the 6-shifted string, 3S + 1 of the 4-shifted, 3S + 2 of the
+// 2-shifted one) from the replicated 3-bit pair table.
+template <int S>
+__device__ __forceinline__ u32x4 key_operand3r(const uint32_t (&kw)[3], const KeyShifts& ks, const uint8_t* lut,
+                                               uint32_t lane4) {
+  u32x4 hi;
+  hi[0] = *reinterpret_cast<const uint32_t*>(lut + byte_addr<3 * S>(kw, lane4));
+  hi[1] = *reinterpret_cast<const uint32_t*>(lut + byte_addr<3 * S>(ks.s6, lane4));
+  hi[2] = *reinterpret_cast<const uint32_t*>(lut + byte_addr<3 * S + 1>(ks.s4, lane4));
+  hi[3] = *reinterpret_cast<const uint32_t*>(lut + byte_addr<3 * S + 2>(ks.s2, lane4));
+  return hi;
+}
+
 // A operands of K-step S from the lane's 32 key codes (hi; lo for 4 bits).
 // `lut` is the table; `lane4` the byte offset of the lane's private copy.
 template <int BK, int S>
@@ -829,6 +873,7 @@ struct SoftmaxState {
   float l;        // Σ 2^(s - mk) over this lane's tokens
   float nvs;      // value-norm scale 2^knv (wave-uniform); 0 until a nonzero norm is seen
   float knv;
+  float nmr;      // log2(kRoundUp) - mk: exponent offset of the rounded weights
 };
 
 constexpr float kLazy = 8.0f;   // rescale only when a score exceeds m by more than 2^8
@@ -997,7 +1042,9 @@ __device__ __forceinline__ float lane_val(float v, int src) {
 // wavefront holds value centroid c in `vcl` and key centroid c in `kcl`, and
 // vsig, ksig are the codebook scales σ (all loaded before the first blocks'
 // loads: a wait for a load issued after them would also wait for them).
-template <int BK, bool PROD, int BV>
+// REP: 3-bit key pairs replicated over all 256 rows (row r holds pair r & 63)
+// for the byte-permute addresses of key_operand3r; otherwise rows 0..63.
+template <int BK, bool PROD, int BV, bool REP = false>
 __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, float ksig, uint8_t* tab,
                                              uint8_t* lut_k, uint8_t* lut_q, int tid, int nthr) {
   using KL = KLut<BK>;
@@ -1036,10 +1083,11 @@ __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, f
         lds_put4(tb + 256 * e + kTabK + 16 * (q & 7), u32x4{w0, w1, w0, w1});
       }
     } else if constexpr (KL::priv) {
-      for (int q = tid; q < KL::entries * 8; q += nthr) {
-        const int e = q >> 3;
+      constexpr int rows = (REP && BK == 3) ? 256 : KL::entries;
+      for (int q = tid; q < rows * 8; q += nthr) {
+        const int r = q >> 3, e = r & (KL::entries - 1);
         const uint32_t w = pack_h2(kcent(e & (KK - 1)), kcent(e >> BK));
-        lds_put4(tb + 256 * e + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
+        lds_put4(tb + 256 * r + kTabK + 16 * (q & 7), u32x4{w, w, w, w});
       }
     } else {
       // 1 bit: one shared table of octets, entry e = 8 codes (bit i of e)
@@ -1210,14 +1258,23 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 // Sign operand of a sketch word for the scaled fp4 products: nibble m·8 + c
 // (dword m, nibble c) holds coordinate 4c + m of the word as fp4 0x2 | bit<<3:
 // -1 for a set bit, +1 otherwise, i.e. -s (the query operand holds -q_S).
+// (x & m) | o in one v_and_or_b32 (the mask from a scalar register, the
+// other constant from a vector register: one scalar operand per instruction).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+  return r;
+}
+
 __device__ __forceinline__ i32x8 sign_operand4(uint32_t w) {
-  // ((w << k) | 0x2...2) & 0xA...A: one shift-or and one and per dword
-  constexpr uint32_t kOne = 0x22222222u, kKeep = 0xAAAAAAAAu;
+  // ((w << k) & 0x8...8) | 0x2...2: the sign bit moved to bit 3 of each
+  // nibble, exponent bits 01 (magnitude 1)
+  constexpr uint32_t kSign = 0x88888888u, kOne = 0x22222222u;
   i32x8 v;
-  v[0] = static_cast<int32_t>(((w << 3) | kOne) & kKeep);
-  v[1] = static_cast<int32_t>(((w << 2) | kOne) & kKeep);
-  v[2] = static_cast<int32_t>(((w << 1) | kOne) & kKeep);
-  v[3] = static_cast<int32_t>((w | kOne) & kKeep);
+  v[0] = static_cast<int32_t>(and_or(w << 3, kSign, kOne));
+  v[1] = static_cast<int32_t>(and_or(w << 2, kSign, kOne));
+  v[2] = static_cast<int32_t>(and_or(w << 1, kSign, kOne));
+  v[3] = static_cast<int32_t>(and_or(w, kSign, kOne));
   v[4] = v[5] = v[6] = v[7] = 0;
   return v;
 }
@@ -1227,12 +1284,39 @@ __device__ __forceinline__ float ror8(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float max4f(float a, float b, float c, float d) { return fmaxf(fmaxf(a, b), fmaxf(c, d)); }
+// max of 4 values in two instructions (no NaN canonicalisation, as max8f).
+__device__ __forceinline__ float max4f(float a, float b, float c, float d) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(max3f(a, b, c)), "v"(d));
+  return r;
+}
+
+// Full scores of the lane's own tile: lanes n < 8 of each 16-lane row add
+// their tile-0 column to that of lane n + 8, lanes n >= 8 their tile-1 column
+// to that of lane n - 8 (row rotation by 8; each add writes one half of every
+// row through its bank mask). The leading wait covers the DPP read of
+// registers just written by vector instructions.
+__device__ __forceinline__ void own_tile_sums(const float (&b0)[4], const float (&b1)[4], float (&s)[4]) {
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(s[0]), "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3])
+      : "v"(b0[0]), "v"(b0[1]), "v"(b0[2]), "v"(b0[3]), "v"(b1[0]), "v"(b1[1]), "v"(b1[2]), "v"(b1[3]));
+}
 
 // Weights are formed as 2^(s - mk)·n_v·(1 + 2^-11) and converted to fp16 by
 // one round-toward-zero packed conversion: the factor makes the conversion
 // round to the nearer of the two neighbours (ties up) instead of toward zero.
 constexpr float kRoundUp = 1.0f + 0x1p-11f;
+// log2(kRoundUp): the factor is applied as an offset of the exponent, so the
+// running sums l carry it too and are divided by kRoundUp at the end.
+constexpr float kLog2RoundUp = 7.04269011e-4f;
 
 template <int BK, bool PROD, int BV>
 __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint32_t t0, uint32_t t_end, int n, int g,
@@ -1266,7 +1350,13 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
   u32x4 kh[2][4], kl[2][4];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    if constexpr (BK > 0) {
+    if constexpr (BK == 3) {
+      const KeyShifts ks = key_shifts(R.kw[tau]);
+      kh[tau][0] = key_operand3r<0>(R.kw[tau], ks, T.k, T.klane);
+      kh[tau][1] = key_operand3r<1>(R.kw[tau], ks, T.k, T.klane);
+      kh[tau][2] = key_operand3r<2>(R.kw[tau], ks, T.k, T.klane);
+      kh[tau][3] = key_operand3r<3>(R.kw[tau], ks, T.k, T.klane);
+    } else if constexpr (BK > 0) {
       key_operands<BK, 0>(R.kw[tau], T.k, T.klane, kh[tau][0], kl[tau][0]);
       key_operands<BK, 1>(R.kw[tau], T.k, T.klane, kh[tau][1], kl[tau][1]);
       key_operands<BK, 2>(R.kw[tau], T.k, T.klane, kh[tau][2], kl[tau][2]);
@@ -1324,12 +1414,9 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
   // hi and lo parts); lane n takes the full scores of its own tile (tile 0
   // for n < 8, tile 1 for n >= 8) and hands the other tile's half over.
   float sc[4];
+  own_tile_sums(br[0], br[1], sc);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float own = own1 ? br[1][i] : br[0][i];
-    const float oth = own1 ? br[0][i] : br[1][i];
-    sc[i] = (own + ror8(oth)) * R.nk[i];     // the score is sc·iqs
-  }
+  for (int i = 0; i < 4; ++i) sc[i] *= R.nk[i];     // the score is sc·iqs
   float nv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) nv[i] = R.nv[i];
@@ -1371,19 +1458,19 @@ __device__ __forceinline__ void attend_block(const Block<BK, PROD, BV>& R, uint3
     }
     st.m = m_new;
     st.mk = mk_new;
+    st.nmr = kLog2RoundUp - mk_new;
     st.nvs = nvs_new;
     st.knv = knv_new;
   }
   // A operand of P·V: row n < 8 carries head n's weights of tile 0 (slots
   // 0..3 of each lane group), row n + 8 those of tile 1 (slots 4..7); rows h
   // and h + 8 of the result are summed at the end.
-  const float nmk = -st.mk;
   float w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], iqs, nmk));
+    const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], iqs, st.nmr));   // 2^(s - mk)·kRoundUp
     st.l += p;
-    w[i] = p * (nv[i] * kRoundUp);
+    w[i] = p * nv[i];
   }
   const uint32_t x0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
   const uint32_t x1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[2], w[3]));
@@ -1473,7 +1560,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
     stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, vc, kn, vn, kg);
 
   // ---- lookup tables ---------------------------------------------------------
-  build_tables<BK, false, BV>(vcl, kcl, vsig, ksig, tab, lut_k, nullptr, tid, nthr);
+  build_tables<BK, false, BV, true>(vcl, kcl, vsig, ksig, tab, lut_k, nullptr, tid, nthr);
   if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
   lds_stores_done();
   Luts T;
@@ -1486,7 +1573,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   T.vlane = 4u * cp;
   tables_barrier();
 
-  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
+  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, INFINITY};
   f32x4 acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1527,6 +1614,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   __builtin_amdgcn_s_setprio(0);
   float l_run = sum4g(st.l);
   l_run += ror8(l_run);                     // both tiles of the head
+  l_run *= 1.0f / kRoundUp;
 
   // ---- merge the workgroup's wavefronts ------------------------------------
   if (g == 0 && n < kMaxHeads) {
@@ -1909,11 +1997,10 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
   // n < 8, tile 1 for n >= 8), taking the other column half of them from
   // lane n ^ 8, as in attn_split_kernel.
   float sc[4], nvo[4], nvr[4];
+  const float pt0[4] = {part[0], part[1], part[2], part[3]}, pt1[4] = {part[4], part[5], part[6], part[7]};
+  own_tile_sums(pt0, pt1, sc);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float own = own1 ? part[4 + i] : part[i];
-    const float oth = own1 ? part[i] : part[4 + i];
-    sc[i] = own + ror8(oth);
     nvo[i] = own1 ? R.nvo[4 + i] : R.nvo[i];
     nvr[i] = own1 ? R.nvr[4 + i] : R.nvr[i];
   }
@@ -1953,6 +2040,7 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
     }
     st.m = m_new;
     st.mk = mk_new;
+    st.nmr = kLog2RoundUp - mk_new;
     st.nvs = nvs_new;
     st.knv = knv_new;
   }
@@ -1960,14 +2048,13 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
   // p·n_r for the others, as fp16 rounded to nearest (kRoundUp); row n < 8
   // carries head n's weights of tile 0, row n + 8 those of tile 1, and rows h
   // and h + 8 of the result are summed at the end.
-  const float nmk = -st.mk;
   float wo[4], wr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], iqs, nmk));
+    const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], iqs, st.nmr));   // 2^(s - mk)·kRoundUp
     st.l += p;
-    wo[i] = p * (nvo[i] * kRoundUp);
-    wr[i] = p * (nvr[i] * kRoundUp);
+    wo[i] = p * nvo[i];
+    wr[i] = p * nvr[i];
   }
   const uint32_t xo0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(wo[0], wo[1]));
   const uint32_t xo1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(wo[2], wo[3]));
@@ -1993,6 +2080,7 @@ __device__ __forceinline__ void write_partials_o(const AttnArgs& a, const Softma
   static_assert(RING >= kMaxHeads * kD * 4, "accumulator rows");
   float l_run = sum4g(st.l);
   l_run += ror8(l_run);
+  l_run *= 1.0f / kRoundUp;
   if (g == 0 && n < kMaxHeads) {
     wm[wave][n] = st.mk;
     wl[wave][n] = l_run;
@@ -2183,7 +2271,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const bool own1 = n >= 8;                 // the lane's own tile: tokens 16..31 of each block
   tables_barrier();
 
-  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f};
+  SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, INFINITY};
   f32x4 acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
