@@ -610,6 +610,7 @@ struct DmaLane {
   uint32_t ktok[2], kcol[2], koff[2];   // key codes: token, byte in row, byte offset from the block
   uint32_t vtok[2], vcol[2], voff[2];   // value codes (rows transposed within tiles)
   uint32_t ntok;                        // sketch rows, norms and γ: lane % 32
+  uint32_t noff, qoff;                  // 4·ntok, 16·ntok
 };
 
 template <int BK, int BV>
@@ -630,6 +631,8 @@ __device__ __forceinline__ DmaLane dma_lane(int lane) {
     }
   }
   d.ntok = lane & 31;
+  d.noff = 4 * d.ntok;
+  d.qoff = 16 * d.ntok;
   return d;
 }
 
@@ -694,6 +697,54 @@ __device__ __forceinline__ void stage_block(uint8_t* st, uint32_t t0, uint32_t l
     __builtin_amdgcn_global_load_lds(nsrc(kn), TQ_LDS(st + L::kn), 4, 0, kStream);
     if constexpr (BV > 0) __builtin_amdgcn_global_load_lds(nsrc(vn), TQ_LDS(st + L::vn), 4, 0, kStream);
     if constexpr (PROD) __builtin_amdgcn_global_load_lds(nsrc(kg), TQ_LDS(st + L::kg), 4, 0, kStream);
+  }
+}
+
+// Buffer resources over one wavefront's token range of each packed array,
+// for launches in which every block of the range exists (AL): a block's loads
+// then take the lane's 32-bit offset and a scalar offset, with no address
+// arithmetic in vector registers. The range is checked by the hardware (an
+// access past it would read zeros).
+struct StreamRsrc {
+  __amdgpu_buffer_rsrc_t kc, kq, vc, kn, vn, kg;
+};
+constexpr int kRawBufferFlags = 0x00020000;   // 32-bit data format, no swizzle
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kRawBufferFlags);
+}
+
+// stage_block for the AL launches through the buffer resources: `trel` is
+// the block's first token relative to the start of the wavefront's range.
+template <int BK, bool PROD, int BV>
+__device__ __forceinline__ void stage_block_rs(uint8_t* st, uint32_t trel, int lane, const DmaLane& d,
+                                               const StreamRsrc& rs) {
+  using L = Stage<BK, PROD, BV>;
+  using KD = RowLoads<BK>;
+  using VD = RowLoads<BV>;
+  constexpr uint32_t KR = 16 * BK, VR = 16 * BV;
+#pragma unroll
+  for (int j = 0; j < KD::full; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kc, TQ_LDS(st + L::kc + 1024 * j), 16, d.koff[j], trel * KR, 0,
+                                             kStream);
+#pragma unroll
+  for (int j = 0; j < VD::full; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.vc, TQ_LDS(st + L::vc + 1024 * j), 16, d.voff[j], trel * VR, 0,
+                                             kStream);
+  if (lane < 32) {
+    constexpr int kj = KD::full, vj = VD::full;
+    if constexpr (KD::half)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kc, TQ_LDS(st + L::kc + 1024 * kj), 16, d.koff[kj], trel * KR, 0,
+                                               kStream);
+    if constexpr (PROD)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kq, TQ_LDS(st + L::qj), 16, d.qoff, trel * 16, 0, kStream);
+    if constexpr (VD::half)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.vc, TQ_LDS(st + L::vc + 1024 * vj), 16, d.voff[vj], trel * VR, 0,
+                                               kStream);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kn, TQ_LDS(st + L::kn), 4, d.noff, trel * 4, 0, kStream);
+    if constexpr (BV > 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.vn, TQ_LDS(st + L::vn), 4, d.noff, trel * 4, 0, kStream);
+    if constexpr (PROD)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kg, TQ_LDS(st + L::kg), 4, d.noff, trel * 4, 0, kStream);
   }
 }
 
@@ -1554,10 +1605,24 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   const uint32_t own_off = own1 ? 64u : 0u;
   const DmaLane dl = dma_lane<BK, BV>(lane);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
-  if (nblk > 0)
-    stage_block<BK, PROD, BV, AL>(ring, t_begin, last, lane, dl, kc, kq, vc, kn, vn, kg);
-  if (nblk > 1)
-    stage_block<BK, PROD, BV, AL>(ring + SL::bytes, t_begin + kBlockTok, last, lane, dl, kc, kq, vc, kn, vn, kg);
+  StreamRsrc rs;
+  if constexpr (AL) {
+    const uint32_t ntok = nblk * kBlockTok;   // every block of the range exists
+    rs.kc = raw_rsrc(kc + size_t(t_begin) * (16 * BK), ntok * (16 * BK));
+    rs.kq = raw_rsrc(kq + size_t(t_begin) * 16, PROD ? ntok * 16 : 0u);
+    rs.vc = raw_rsrc(vc + size_t(t_begin) * (16 * BV), ntok * (16 * BV));
+    rs.kn = raw_rsrc(kn + t_begin, ntok * 4);
+    rs.vn = raw_rsrc(vn + t_begin, BV > 0 ? ntok * 4 : 0u);
+    rs.kg = raw_rsrc(kg + t_begin, PROD ? ntok * 4 : 0u);
+  }
+  auto stage_at = [&](uint8_t* st, uint32_t t0) {
+    if constexpr (AL)
+      stage_block_rs<BK, PROD, BV>(st, t0 - t_begin, lane, dl, rs);
+    else
+      stage_block<BK, PROD, BV, AL>(st, t0, last, lane, dl, kc, kq, vc, kn, vn, kg);
+  };
+  if (nblk > 0) stage_at(ring, t_begin);
+  if (nblk > 1) stage_at(ring + SL::bytes, t_begin + kBlockTok);
 
   // ---- lookup tables ---------------------------------------------------------
   build_tables<BK, false, BV, true>(vcl, kcl, vsig, ksig, tab, lut_k, nullptr, tid, nthr);
@@ -1605,8 +1670,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
       // block i + 2 goes to stage (cur + 2) % kStages: with two stages, the one
       // just read (read_block waited for all of its reads)
       const int nx = (cur + 2) % kStages;
-      stage_block<BK, PROD, BV, AL>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, dl, kc, kq, vc, kn,
-                                    vn, kg);
+      stage_at(ring + nx * SL::bytes, t0 + 2 * kBlockTok);
     }
     attend_block<BK, PROD, BV>(R, t0, t_end, n, g, own1, T, bq, bs, ssc0, ssc1, iqs, st, acc);
     cur = cur + 1 == kStages ? 0 : cur + 1;
