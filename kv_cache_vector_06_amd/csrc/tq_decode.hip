@@ -1902,7 +1902,8 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
 // Prod keys: the lane's sketch words of both tiles (word g of tokens n and
 // 16 + n) and the 8 slots' γ pairs. The query's sketch operand carries the
 // correction scale √(π/2)/128 of a whole vector; a group's estimate takes
-// √(π/2)/d_g, so γ_o is scaled by 128/32 and γ_r by 128/96 here.
+// √(π/2)/d_g, i.e. γ_o·128/32 and γ_r·128/96: the factor 4 is applied as
+// +2 in the sketch products' E8M0 scales, the remaining 1/3 here.
 template <int BK, int BV>
 __device__ __forceinline__ void oread_prod(OBlock& R, uint32_t sb, int n, int g) {
   using L = OStage<BK, BV, true>;
@@ -1925,8 +1926,8 @@ __device__ __forceinline__ void oread_prod(OBlock& R, uint32_t sb, int n, int g)
   const f32x4 gg[4] = {g0, g1, g2, g3};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    R.gko[j] = gg[j >> 1][2 * (j & 1)] * 4.0f;
-    R.gkr[j] = gg[j >> 1][2 * (j & 1) + 1] * (4.0f / 3.0f);
+    R.gko[j] = gg[j >> 1][2 * (j & 1)];
+    R.gkr[j] = gg[j >> 1][2 * (j & 1) + 1] * (1.0f / 3.0f);
   }
 }
 
@@ -2314,8 +2315,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
       }
     }
     const int32_t* ss = reinterpret_cast<const int32_t*>(blk + kSkScaleOff);
-    ssc0 = ss[lane];
-    ssc1 = ss[64 + lane];
+    ssc0 = ss[lane] + 2;       // ×4: both groups' √(π/2)/d_g share the factor 128/32
+    ssc1 = ss[64 + lane] + 2;
   }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   asm volatile("" ::: "memory");
@@ -2323,9 +2324,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const uint32_t ring_addr = lds_addr(ring);
   const OOffsets so = ostage_offsets<BK, BV>(n, g);
   const uint32_t nblk = (t_end - t_begin + kBlockTok - 1) / kBlockTok;
-  if (nblk > 0) ostage_block<BK, BV, AL, PROD>(ring, t_begin, last, lane, kc, vc, kn, vn, kqs, kgs);
-  if (nblk > 1)
-    ostage_block<BK, BV, AL, PROD>(ring + SL::bytes, t_begin + kBlockTok, last, lane, kc, vc, kn, vn, kqs, kgs);
+  auto stage_at = [&](uint8_t* st, uint32_t t0) {
+    ostage_block<BK, BV, AL, PROD>(st, t0, last, lane, kc, vc, kn, vn, kqs, kgs);
+  };
+  if (nblk > 0) stage_at(ring, t_begin);
+  if (nblk > 1) stage_at(ring + SL::bytes, t_begin + kBlockTok);
 
   build_tables_o<BK, BV>(cl, vsig, ksig, tab, tab2, tid, nthr);
   if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
@@ -2359,8 +2362,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
       __builtin_amdgcn_s_setprio(1);
     if (i + 2 < nblk) {
       const int nx = (cur + 2) % kStages;
-      ostage_block<BK, BV, AL, PROD>(ring + nx * SL::bytes, t0 + 2 * kBlockTok, last, lane, kc, vc, kn, vn, kqs,
-                                     kgs);
+      stage_at(ring + nx * SL::bytes, t0 + 2 * kBlockTok);
     }
     oattend_block<BK, BV, PROD>(R, t0, t_end, n, g, tab, tab2, lane_lo, lane_hi, lane8, bqo, bqr, bso, bsr, ssc0,
                                 ssc1, iqs, own1, st, acc);
