@@ -1803,7 +1803,8 @@ __device__ __forceinline__ void ostage_block(uint8_t* st, uint32_t t0, uint32_t 
 // value words (column n's 8 positions, aligned to bit 0).
 struct OBlock {
   uint32_t kw[2][4];
-  float nko[8], nkr[8], nvo[8], nvr[8];
+  float nko[8], nkr[8];    // key norm pairs of the 8 slots (both tiles)
+  float nvo[4], nvr[4];    // value norm pairs of the lane's own tile's 4 slots
   uint32_t vw[8];
   uint32_t qw[2];          // prod keys: sketch word g of tokens n and 16 + n
   float gko[8], gkr[8];    // prod keys: the slots' scaled γ_o and γ_r, see oread_prod
@@ -1830,16 +1831,20 @@ __device__ __forceinline__ OOffsets ostage_offsets(int n, int g) {
 
 // Read a staged split block into registers: wait for its loads (all but the
 // newest PEND of this wavefront), every read of the stage, then the wait for
-// the reads, in one statement with early-clobber outputs.
+// the reads, in one statement with early-clobber outputs. The value norms
+// are read for the lane's own tile only (own_off: 0 for tile 0, 128 bytes
+// for tile 1); the key norms for both, since each lane forms column parts of
+// both tiles' scores.
 template <int BK, int BV, int PEND>
-__device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffsets& o, uint32_t ap, uint32_t& pw) {
+__device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffsets& o, uint32_t own_off, uint32_t ap,
+                                            uint32_t& pw) {
   using L = OStage<BK, BV>;
   constexpr int KT = 4 * L::KR;            // dwords between the two key tiles (16 rows)
   constexpr int VT = L::VR / 4;            // dwords between consecutive tokens
   static_assert(KT + 3 <= 255 && 19 * VT + 1 <= 255, "read2 offsets");
-  const uint32_t ak = sb + o.k, an = sb + o.n, av = sb + o.v;
+  const uint32_t ak = sb + o.k, an = sb + o.n, av = sb + o.v, ao = an + own_off;
   u32x2 k0, k1, k2, k3;
-  f32x4 n0, n1, n2, n3, m0, m1, m2, m3;
+  f32x4 n0, n1, n2, n3, m0, m1;
   u32x2 v0, v1, v2, v3, v4, v5, v6, v7;
   // slot (τ, i) is token 16τ + 4g + i: dword offset (16τ + i)·VT
   asm volatile(
@@ -1853,10 +1858,8 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
       "ds_read_b128 %[n1], %[an] offset:16\n\t"
       "ds_read_b128 %[n2], %[an] offset:128\n\t"
       "ds_read_b128 %[n3], %[an] offset:144\n\t"
-      "ds_read_b128 %[m0], %[an] offset:256\n\t"
-      "ds_read_b128 %[m1], %[an] offset:272\n\t"
-      "ds_read_b128 %[m2], %[an] offset:384\n\t"
-      "ds_read_b128 %[m3], %[an] offset:400\n\t"
+      "ds_read_b128 %[m0], %[ao] offset:256\n\t"
+      "ds_read_b128 %[m1], %[ao] offset:272\n\t"
       "ds_read2_b32 %[v0], %[av] offset0:%[s0] offset1:%[s0b]\n\t"
       "ds_read2_b32 %[v1], %[av] offset0:%[s1] offset1:%[s1b]\n\t"
       "ds_read2_b32 %[v2], %[av] offset0:%[s2] offset1:%[s2b]\n\t"
@@ -1867,10 +1870,11 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
       "ds_read2_b32 %[v7], %[av] offset0:%[s7] offset1:%[s7b]\n\t"
       "s_waitcnt lgkmcnt(0)"
       : [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2), [k3] "=&v"(k3), [n0] "=&v"(n0), [n1] "=&v"(n1),
-        [n2] "=&v"(n2), [n3] "=&v"(n3), [m0] "=&v"(m0), [m1] "=&v"(m1), [m2] "=&v"(m2), [m3] "=&v"(m3),
+        [n2] "=&v"(n2), [n3] "=&v"(n3), [m0] "=&v"(m0), [m1] "=&v"(m1),
         [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2), [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5),
         [v6] "=&v"(v6), [v7] "=&v"(v7), [pw] "=&v"(pw)
-      : [pend] "n"(PEND), [ap] "v"(ap), [ak] "v"(ak), [an] "v"(an), [av] "v"(av), [kt0] "n"(KT), [kt1] "n"(KT + 1),
+      : [pend] "n"(PEND), [ap] "v"(ap), [ak] "v"(ak), [an] "v"(an), [ao] "v"(ao), [av] "v"(av), [kt0] "n"(KT),
+        [kt1] "n"(KT + 1),
         [kt2] "n"(KT + 2), [kt3] "n"(KT + 3), [s0] "n"(0), [s0b] "n"(1), [s1] "n"(VT), [s1b] "n"(VT + 1),
         [s2] "n"(2 * VT), [s2b] "n"(2 * VT + 1), [s3] "n"(3 * VT), [s3b] "n"(3 * VT + 1), [s4] "n"(16 * VT),
         [s4b] "n"(16 * VT + 1), [s5] "n"(17 * VT), [s5b] "n"(17 * VT + 1), [s6] "n"(18 * VT),
@@ -1886,13 +1890,16 @@ __device__ __forceinline__ void oread_block(OBlock& R, uint32_t sb, const OOffse
     R.kw[t][2] = __builtin_amdgcn_alignbit(d3, d2, ks);
     R.kw[t][3] = d3 >> ks;
   }
-  const f32x4 nn[4] = {n0, n1, n2, n3}, mm[4] = {m0, m1, m2, m3};
+  const f32x4 nn[4] = {n0, n1, n2, n3}, mm[2] = {m0, m1};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     R.nko[j] = nn[j >> 1][2 * (j & 1)];
     R.nkr[j] = nn[j >> 1][2 * (j & 1) + 1];
-    R.nvo[j] = mm[j >> 1][2 * (j & 1)];
-    R.nvr[j] = mm[j >> 1][2 * (j & 1) + 1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    R.nvo[i] = mm[i >> 1][2 * (i & 1)];
+    R.nvr[i] = mm[i >> 1][2 * (i & 1) + 1];
   }
   const u32x2 vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
 #pragma unroll
@@ -2066,8 +2073,8 @@ __device__ __forceinline__ void oattend_block(const OBlock& R, uint32_t t0, uint
   own_tile_sums(pt0, pt1, sc);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    nvo[i] = own1 ? R.nvo[4 + i] : R.nvo[i];
-    nvr[i] = own1 ? R.nvr[4 + i] : R.nvr[i];
+    nvo[i] = R.nvo[i];
+    nvr[i] = R.nvr[i];
   }
   if (__builtin_expect(t0 + kBlockTok > t_end, 0)) {
     const uint32_t tb = t0 + (own1 ? 16u : 0u) + 4u * g;
@@ -2336,6 +2343,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
   const uint32_t cp = lane & 31;
   const uint32_t lane_lo = 4u * cp, lane_hi = kTabK + 4u * cp, lane8 = 8u * (lane & 15);
   const bool own1 = n >= 8;                 // the lane's own tile: tokens 16..31 of each block
+  const uint32_t own_off = own1 ? 128u : 0u;
   tables_barrier();
 
   SoftmaxState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, INFINITY};
@@ -2352,9 +2360,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_outlier_kernel(AttnArgs a
     lds_put1(prog_own, i);
     uint32_t pw;
     if (i + 1 < nblk)
-      oread_block<BK, BV, SL::dma>(R, sb, so, prog_partner, pw);
+      oread_block<BK, BV, SL::dma>(R, sb, so, own_off, prog_partner, pw);
     else
-      oread_block<BK, BV, 0>(R, sb, so, prog_partner, pw);
+      oread_block<BK, BV, 0>(R, sb, so, own_off, prog_partner, pw);
     if constexpr (PROD) oread_prod<BK, BV>(R, sb, n, g);
     if (__builtin_amdgcn_readfirstlane(pw) < i)
       __builtin_amdgcn_s_setprio(0);
