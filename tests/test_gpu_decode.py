@@ -218,3 +218,13 @@ def test_decode_step_aligned_ragged_lengths_full_size():
     # appended by the step itself.
     _full_size_units(synth.WORKLOADS["gqa8_prod4_128k_b4"], [(0, 5), (1, 0), (2, 4), (3, 7)], 900,
                      use_step=True, lens=[131071, 12345, 65536, 1])
+
+
+@pytest.mark.parametrize("T_ctx,lens", [(32, [32, 1, 0, 17]), (96, [96, 33, 64, 5]), (288, [288, 257, 31, 0])])
+def test_decode_aligned_short_contexts(T_ctx, lens):
+    # max_ctx a multiple of the 32-token block (the variant that streams
+    # through per-wavefront buffer resources) but so short that most
+    # wavefronts get no block and the others one to a few, with ragged
+    # lengths: 0, 1, a partial last block, a full one.
+    cfg = synth.WORKLOADS["gqa8_prod4_128k_b4"]
+    run_case(cfg, T_ctx, 4, lens=lens)
