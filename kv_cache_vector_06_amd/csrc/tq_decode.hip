@@ -426,7 +426,9 @@ constexpr int kCopies = 32;
 //   value pairs: entry e in row e at byte 4c, c = lane % 32 (the lower half
 //     of the row), so that one byte permute forms the address (entry in bits
 //     8..15, 4c in bits 0..7);
-//   3-bit key pairs: entry e in row e at byte 128 + 4c, c = lane % 32;
+//   3-bit key pairs: entry e in row e at byte 128 + 4c, c = lane % 32 (the
+//     decode kernel replicates them over all 256 rows, row r holding pair
+//     r & 63, for byte-permute addresses; the search table has rows 0..63);
 //   4-bit key pairs and 2-bit key quads (8-byte entries, indexed by a whole
 //     code byte): entry e in row e at byte 128 + 8c', c' = lane % 16 (two
 //     lanes of a half-wavefront share a copy), addressed by one byte permute.
@@ -564,10 +566,11 @@ __device__ __forceinline__ uint32_t to_nibbles(uint32_t w) {
 
 // ---- LDS staging of 32-token blocks ----------------------------------------
 // Each wavefront owns a ring of kStages stage buffers. A block's packed data
-// is copied HBM → LDS by the direct-to-LDS loads (global_load_lds: each lane
-// names a global address and the wavefront fills consecutive LDS, 16 bytes per
-// lane), so the loads for blocks i+1 and i+2 are in flight while block i is
-// computed, without holding registers. Each load instruction reads one array:
+// is copied HBM → LDS by direct-to-LDS loads (global_load_lds, or the buffer
+// form in stage_block_rs: each lane names a source and the wavefront fills
+// consecutive LDS, 16 bytes per lane), so the loads for blocks i+1 and i+2
+// are in flight while block i is computed, without holding registers. Each
+// load instruction reads one array:
 // a block's 32 rows of 16·bits bytes take bits/2 wavefront loads plus a
 // half-wavefront (32-lane) one when bits is odd. Stage layout (bytes): key
 // codes [32][16·BK] | sketch [32][16] | value codes [32][16·BV] (rows
@@ -921,7 +924,7 @@ __device__ __forceinline__ void read_block(Block<BK, PROD, BV>& R, uint32_t sb, 
 struct SoftmaxState {
   float m;        // reference max of the scores (log2 domain)
   float mk;       // m + knv
-  float l;        // Σ 2^(s - mk) over this lane's tokens
+  float l;        // Σ 2^(s - mk)·kRoundUp over this lane's tokens (the factor is divided out at the end)
   float nvs;      // value-norm scale 2^knv (wave-uniform); 0 until a nonzero norm is seen
   float knv;
   float nmr;      // log2(kRoundUp) - mk: exponent offset of the rounded weights
