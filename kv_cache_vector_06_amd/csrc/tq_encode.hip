@@ -408,12 +408,13 @@ __device__ __forceinline__ int build_cell(const Book& bk, int k, CellEntry<PROD>
   return inside > 1;
 }
 
-// Wavefronts per workgroup of the full-size encoder. mse encodes with a cell
-// table (b_m >= 3) run one workgroup of 16 wavefronts per compute unit
-// sharing one staged copy of the fragments and a conflict-free table (below);
-// the others two workgroups of 8.
+// Wavefronts per workgroup of the full-size encoder. Encodes with a cell
+// table (b_m >= 3) run one workgroup per compute unit that shares one staged
+// copy of the fragments: 16 wavefronts for mse (with a conflict-free table,
+// below), 12 for prod (three per SIMD, as many as its registers allow). The
+// other mse encodes run two workgroups of 8, the other prod encodes one.
 template <int BM, bool PROD>
-constexpr int enc_waves() { return (BM >= 3 && !PROD) ? 16 : kEncWaves; }
+constexpr int enc_waves() { return BM >= 3 ? (PROD ? 12 : 16) : kEncWaves; }
 
 template <int BM, bool PROD, bool F32IN>
 __global__ __launch_bounds__((enc_waves<BM, PROD>() * 64)) void encode_kernel(EncodeArgs a) {
@@ -1247,9 +1248,10 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
     hipLaunchKernelGGL(row_encode_kernel, dim3(static_cast<unsigned>(tiles)), dim3(kRowWaves * 64), 0, s, r);
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
   }
-  // one workgroup of 16 wavefronts per compute unit for mse with a cell
-  // table, two of 8 for the other mse encodes, one of 8 for prod
-  const int waves = (!prod && bm >= 3) ? 16 : kEncWaves;
+  // one workgroup per compute unit of 16 wavefronts for mse with a cell
+  // table and of 12 for prod with one, two of 8 for the other mse encodes,
+  // one of 8 for the other prod encodes
+  const int waves = bm >= 3 ? (prod ? 12 : 16) : kEncWaves;
   const int64_t want = (tiles + waves - 1) / waves;
   const int cap = device_cus() * ((prod || bm >= 3) ? 1 : 2);
   const int grid = static_cast<int>(want < cap ? want : cap);
