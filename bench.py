@@ -430,6 +430,16 @@ def main():
     read_peak = dec_bytes / (pr_us * 1e-6) / 1e9
     pr4_us = read_back_to_back_us([big])
     read_peak_4g = big.numel() * 4 / (pr4_us * 1e-6) / 1e9
+    # Read time against size (every size above the 256 MB last-level cache, so
+    # back-to-back reads of one buffer come from HBM): the least-squares line
+    # t = t0 + bytes / bw splits a launch into a fixed part and a streaming part.
+    sweep_mib = (512, 768, 1024, 1536, 2048, 3072, 4096)
+    sweep_us = [read_back_to_back_us([big.view(torch.uint8)[:m << 20]], reps=20, warm=5) for m in sweep_mib]
+    xs_b = [float(m << 20) for m in sweep_mib]
+    mx, my = sum(xs_b) / len(xs_b), sum(sweep_us) / len(sweep_us)
+    slope = sum((x - mx) * (y - my) for x, y in zip(xs_b, sweep_us)) / sum((x - mx) ** 2 for x in xs_b)
+    read_sweep = {"mib": list(sweep_mib), "us": [round(u, 2) for u in sweep_us],
+                  "fixed_us": round(my - slope * mx, 2), "streaming_gbs": round(1e-3 / slope, 1)}
     del big
     log(f"[bench] plain read of {dec_bytes} B: median {pr_us:.1f} us, {read_peak:.0f} GB/s; "
         f"of 4 GiB: {pr4_us:.1f} us, {read_peak_4g:.0f} GB/s")
@@ -668,6 +678,7 @@ def main():
         "steady_state": steady,
         "measured_read_peak": {"gbs": round(read_peak, 1), "bytes": dec_bytes, "us": round(pr_us, 2),
                                "gbs_4gib": round(read_peak_4g, 1),
+                               "size_sweep": read_sweep,
                                "kernel": "tq_read_probe: plain coalesced read, 16-byte non-temporal loads",
                                "value_frac": round(value / read_peak, 4)},
         "configs": configs,

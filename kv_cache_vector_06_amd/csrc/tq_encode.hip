@@ -582,7 +582,10 @@ __global__ __launch_bounds__((enc_waves<BM, PROD>() * 64)) void encode_kernel(En
       // Row tile t, element j is rotated coordinate 32g + q, q = 4t + j, and
       // acc = S·y with S = 16‖x‖·2^-e (any S > 0 for a zero vector, whose acc is 0).
       const float S = (rs > 0.f) ? rot_scale * rs : 1.0f;
-      const float up = 1.0f / S;
+      // mse uses 1/S only for the cell lookup, whose cells are widened by far
+      // more than the hardware reciprocal's error: one instruction instead of a
+      // division. prod scales residuals and γ by it: the rounded quotient.
+      const float up = PROD ? 1.0f / S : __builtin_amdgcn_rcpf(S);
       const float inv128 = 128.0f * up;
       ScaledBook sb;
       if constexpr (!USE) {
