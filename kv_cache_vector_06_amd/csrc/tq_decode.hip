@@ -55,9 +55,9 @@ constexpr int kDecWaves = 8;             // wavefronts per split workgroup (2 pe
 constexpr int kBlockTok = 32;            // tokens per wavefront step
 constexpr int kMaxHeads = 8;             // query heads per unit
 constexpr int kPartStride = 132;         // floats per (unit, split, head) partial: M, L, pad, pad, acc[128]
-constexpr int kQFrags = 8;              // q' (hi | lo columns), q_S (hi | lo) × 4 K-steps
+constexpr int kQFrags = 4;              // q' (hi | lo columns) × 4 K-steps
 // Per unit: the fp16 fragments, the per-head score scales, then the sketch
-// operand of the split kernel's scaled fp4 × fp8 matrix-core products (two
+// operand of the scaled fp4 × fp8 sketch products (split and search kernels; two
 // products: 64 lanes × 32 fp8 bytes each) and their per-lane E8M0 scales.
 constexpr size_t kSkOff = kQFrags * 1024 + 256;
 constexpr size_t kSkScaleOff = kSkOff + 2 * 64 * 32;
@@ -290,13 +290,11 @@ __device__ __forceinline__ void row_prep(const PrepArgs& a, int unit, RowXchg& X
   int e3 = 0;
   if (m > 0.f) frexpf(m, &e3);
   const float scl = m > 0.f ? ldexpf(1.0f, 10 - e3) : 1.0f;
-  // Fragment f (f < 4: q', K-step f; f >= 4: q_S, K-step f - 4), lane (n, g),
-  // slot j holds dim 32g + 8(f%4) + j: this wavefront's dims are dwords
-  // 2(t%2), 2(t%2) + 1 of fragments t/2 and 4 + t/2.
+  // Fragment f (q', K-step f), lane (n, g), slot j holds dim 32g + 8f + j:
+  // this wavefront's dims are dwords 2(t%2), 2(t%2) + 1 of fragment t/2.
   uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   u32x4* fr = reinterpret_cast<u32x4*>(blk);
   reinterpret_cast<u32x2*>(fr + (t >> 1) * 64 + lane)[t & 1] = hilo_pairs(qp, scl, n < 8);
-  reinterpret_cast<u32x2*>(fr + (4 + (t >> 1)) * 64 + lane)[t & 1] = hilo_pairs(qs, scl, n < 8);
   if (t == 0 && g == 0 && n < kMaxHeads) reinterpret_cast<float*>(blk + kQFrags * 1024)[n] = live ? 1.0f / scl : 0.f;
   if (prod) {
     // The split kernel's sketch product runs on the scaled fp4 × fp8 matrix
@@ -532,15 +530,30 @@ __device__ __forceinline__ void key_operands(const uint32_t (&kw)[BK > 0 ? BK : 
   }
 }
 
-// Sketch operand of K-step S: the 8 sign bits of the step, as fp16 ±1 (bit
-// set → +1), from a private table of the 16 nibbles (2 dwords per entry;
-// entry e of copy c at byte 256e + 8c).
-template <int S>
-__device__ __forceinline__ u32x4 sign_operand(uint32_t qw, const uint8_t* lut, uint32_t lane8) {
-  const uint32_t w[1] = {qw};
-  const u32x2 a = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S, 4, 8>(w) + lane8));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(lut + (field_shl<8 * S + 4, 4, 8>(w) + lane8));
-  return u32x4{a[0], a[1], b[0], b[1]};
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// (x & m) | o in one v_and_or_b32 (the mask from a scalar register, the
+// other constant from a vector register: one scalar operand per instruction).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+  return r;
+}
+
+// Sign operand of a sketch word for the scaled fp4 products: nibble m·8 + c
+// (dword m, nibble c) holds coordinate 4c + m of the word as fp4 0x2 | bit<<3:
+// -1 for a set bit, +1 otherwise, i.e. -s (the query operand holds -q_S).
+__device__ __forceinline__ i32x8 sign_operand4(uint32_t w) {
+  // ((w << k) & 0x8...8) | 0x2...2: the sign bit moved to bit 3 of each
+  // nibble, exponent bits 01 (magnitude 1)
+  constexpr uint32_t kSign = 0x88888888u, kOne = 0x22222222u;
+  i32x8 v;
+  v[0] = static_cast<int32_t>(and_or(w << 3, kSign, kOne));
+  v[1] = static_cast<int32_t>(and_or(w << 2, kSign, kOne));
+  v[2] = static_cast<int32_t>(and_or(w << 1, kSign, kOne));
+  v[3] = static_cast<int32_t>(and_or(w, kSign, kOne));
+  v[4] = v[5] = v[6] = v[7] = 0;
+  return v;
 }
 
 // Value codes of dims 8n..8n+7 → "nibble form": code of dim 8n+r in bits
@@ -953,9 +966,8 @@ __device__ __forceinline__ float max8f(const float (&v)[8]) {
 
 struct Luts {
   const uint8_t* k;
-  const uint8_t* q;
   const uint8_t* v;
-  uint32_t klane, qlane, vlane;   // byte offsets of the lane's private copies
+  uint32_t klane, vlane;   // byte offsets of the lane's private copies
 };
 
 // B operand of P·V for dims 8n + r: four dwords, the fp16 pairs of the value
@@ -979,13 +991,15 @@ __device__ __forceinline__ u32x4 pv_operand(const uint32_t (&X)[4], const uint32
 // above); slot j = 4τ + i is token 16τ + 4g + i. The score is sc·iqs.
 template <int BK, bool PROD, int BV>
 __device__ __forceinline__ void block_scores(const Block<BK, PROD, BV>& R, const Luts& T, const u32x4 (&bq)[4],
-                                             const u32x4 (&bs)[4], float (&sc)[8]) {
-  // Every table read of both tiles' score operands is issued before the
-  // first product, so the block waits for one LDS round trip instead of one
-  // per product (the scheduler would otherwise put each read just before its
-  // product); the value-table reads follow the products and complete while
-  // the softmax runs.
-  u32x4 kh[2][4], kl[2][4], sg[2][4];
+                                             const i32x8 (&bs)[2], int ssc0, int ssc1, float (&sc)[8]) {
+  // Every table read of both tiles' key operands is issued before the first
+  // product, so the block waits for one LDS round trip instead of one per
+  // product (the scheduler would otherwise put each read just before its
+  // product). The sketch product runs on the scaled fp4 × fp8 matrix cores as
+  // in attend_block: A = -s from the sketch word, B = the query's -q_S in
+  // four fp8 parts (parts 0/1 into columns 0-15 with scale ssc0, parts 2/3
+  // with ssc1), so dq has the hi/lo column halves of the fp16 key product.
+  u32x4 kh[2][4], kl[2][4];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
     if constexpr (BK > 0) {
@@ -994,12 +1008,11 @@ __device__ __forceinline__ void block_scores(const Block<BK, PROD, BV>& R, const
       key_operands<BK, 2>(R.kw[tau], T.k, T.klane, kh[tau][2], kl[tau][2]);
       key_operands<BK, 3>(R.kw[tau], T.k, T.klane, kh[tau][3], kl[tau][3]);
     }
-    if constexpr (PROD) {
-      sg[tau][0] = sign_operand<0>(R.qw[tau], T.q, T.qlane);
-      sg[tau][1] = sign_operand<1>(R.qw[tau], T.q, T.qlane);
-      sg[tau][2] = sign_operand<2>(R.qw[tau], T.q, T.qlane);
-      sg[tau][3] = sign_operand<3>(R.qw[tau], T.q, T.qlane);
-    }
+  }
+  i32x8 sa[2];
+  if constexpr (PROD) {
+    sa[0] = sign_operand4(R.qw[0]);
+    sa[1] = sign_operand4(R.qw[1]);
   }
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
@@ -1016,8 +1029,8 @@ __device__ __forceinline__ void block_scores(const Block<BK, PROD, BV>& R, const
       }
     }
     if constexpr (PROD) {
-#pragma unroll
-      for (int S = 0; S < 4; ++S) dq = mfma(sg[tau][S], bs[S], dq);
+      dq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[tau], bs[0], dq, 4, 0, 0, 127, 0, ssc0);
+      dq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sa[tau], bs[1], dq, 4, 0, 0, 127, 0, ssc1);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1098,9 +1111,9 @@ __device__ __forceinline__ float lane_val(float v, int src) {
 // loads: a wait for a load issued after them would also wait for them).
 // REP: 3-bit key pairs replicated over all 256 rows (row r holds pair r & 63)
 // for the byte-permute addresses of key_operand3r; otherwise rows 0..63.
-template <int BK, bool PROD, int BV, bool REP = false>
+template <int BK, int BV, bool REP = false>
 __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, float ksig, uint8_t* tab,
-                                             uint8_t* lut_k, uint8_t* lut_q, int tid, int nthr) {
+                                             uint8_t* lut_k, int tid, int nthr) {
   using KL = KLut<BK>;
   constexpr int KV = 1 << BV, KK = BK > 0 ? (1 << BK) : 1;
   const uint32_t tb = lds_addr(tab);
@@ -1156,21 +1169,6 @@ __device__ __forceinline__ void build_tables(float vcl, float kcl, float vsig, f
         }
         lds_put4(lds_addr(lut_k) + 16 * e, v);
       }
-    }
-  }
-  if constexpr (PROD) {
-    // sketch nibbles: entry e (4 sign bits), dword w = signs of bits 2w and
-    // 2w + 1 as fp16 ±1 (bit set → +1); 8 bytes per copy
-    for (int q = tid; q < 16 * 16; q += nthr) {
-      const int e = q >> 4;
-      uint32_t d[2];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t s0 = ((e >> (2 * w)) & 1) ? 0x3C00u : 0xBC00u;
-        const uint32_t s1 = ((e >> (2 * w + 1)) & 1) ? 0x3C00u : 0xBC00u;
-        d[w] = s0 | (s1 << 16);
-      }
-      lds_put4(lds_addr(lut_q) + 256 * e + 16 * (q & 15), u32x4{d[0], d[1], d[0], d[1]});
     }
   }
 }
@@ -1305,33 +1303,6 @@ __device__ __forceinline__ void read_block_own(Block<BK, PROD, BV>& R, uint32_t 
 #undef TQ_GAMMA
 #undef TQ_QJ
 #undef TQ_LGK
-
-
-typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-
-// Sign operand of a sketch word for the scaled fp4 products: nibble m·8 + c
-// (dword m, nibble c) holds coordinate 4c + m of the word as fp4 0x2 | bit<<3:
-// -1 for a set bit, +1 otherwise, i.e. -s (the query operand holds -q_S).
-// (x & m) | o in one v_and_or_b32 (the mask from a scalar register, the
-// other constant from a vector register: one scalar operand per instruction).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
-  return r;
-}
-
-__device__ __forceinline__ i32x8 sign_operand4(uint32_t w) {
-  // ((w << k) & 0x8...8) | 0x2...2: the sign bit moved to bit 3 of each
-  // nibble, exponent bits 01 (magnitude 1)
-  constexpr uint32_t kSign = 0x88888888u, kOne = 0x22222222u;
-  i32x8 v;
-  v[0] = static_cast<int32_t>(and_or(w << 3, kSign, kOne));
-  v[1] = static_cast<int32_t>(and_or(w << 2, kSign, kOne));
-  v[2] = static_cast<int32_t>(and_or(w << 1, kSign, kOne));
-  v[3] = static_cast<int32_t>(and_or(w, kSign, kOne));
-  v[4] = v[5] = v[6] = v[7] = 0;
-  return v;
-}
 
 // The value of lane n ^ 8 (row rotation by 8 within each 16-lane row).
 __device__ __forceinline__ float ror8(float v) {
@@ -1628,16 +1599,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void attn_split_kernel(AttnArgs a) 
   if (nblk > 1) stage_at(ring + SL::bytes, t_begin + kBlockTok);
 
   // ---- lookup tables ---------------------------------------------------------
-  build_tables<BK, false, BV, true>(vcl, kcl, vsig, ksig, tab, lut_k, nullptr, tid, nthr);
+  build_tables<BK, BV, true>(vcl, kcl, vsig, ksig, tab, lut_k, tid, nthr);
   if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
   lds_stores_done();
   Luts T;
   const uint32_t cp = lane & 31;            // private copy of this lane
   T.k = KL::priv ? tab : lut_k;
-  T.q = nullptr;
   T.v = tab;
   T.klane = KL::byte_indexed ? kTabK + 8u * (lane & 15) : KL::priv ? kTabK + 4u * cp : 0u;
-  T.qlane = 0u;
   T.vlane = 4u * cp;
   tables_barrier();
 
@@ -2614,8 +2583,7 @@ template <int BK, bool PROD>
 struct SearchPlan {
   using KL = KLut<BK>;
   static constexpr int tab_bytes = KL::priv ? KL::entries * 256 : 256;
-  static constexpr int fixed = tab_bytes + KL::bytes + (PROD ? 16 * kCopies * 8 : 16) +
-                               int(sizeof(SearchLds)) + 64 + 1024;
+  static constexpr int fixed = tab_bytes + KL::bytes + int(sizeof(SearchLds)) + 64 + 1024;
   static constexpr int ring = (160 * 1024 - fixed) / (kDecWaves * Stage<BK, PROD, 0>::bytes);
   static constexpr int stages = ring > 4 ? 4 : ring;
   static_assert(stages >= 2, "search staging ring");
@@ -2628,7 +2596,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   constexpr int NST = SearchPlan<BK, PROD>::stages;
   __shared__ __attribute__((aligned(256))) uint8_t tab[SearchPlan<BK, PROD>::tab_bytes];
   __shared__ __attribute__((aligned(16))) uint8_t lut_k[KL::bytes];
-  __shared__ __attribute__((aligned(256))) uint8_t lut_q[PROD ? 16 * kCopies * 8 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kDecWaves][NST * SL::bytes];
   __shared__ SearchLds S;
   __shared__ uint32_t prog[kDecWaves];   // blocks started per wavefront (issue balance)
@@ -2660,11 +2627,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
   const float ksig = BK > 0 ? scalar_load(&a.kh->sigma) : 0.f;
   const uint8_t* blk = a.ws + size_t(unit) * kUnitBytes;
   const u32x4* fr = reinterpret_cast<const u32x4*>(blk);
-  u32x4 bq[4], bs[4];
+  u32x4 bq[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bq[s] = fr[s * 64 + lane];
-    if constexpr (PROD) bs[s] = fr[(4 + s) * 64 + lane];
+  for (int s = 0; s < 4; ++s) bq[s] = fr[s * 64 + lane];
+  i32x8 bs[2];
+  int ssc0 = 127, ssc1 = 127;
+  if constexpr (PROD) {
+    const i32x8* sk = reinterpret_cast<const i32x8*>(blk + kSkOff);
+    bs[0] = sk[lane];
+    bs[1] = sk[64 + lane];
+    const int32_t* ss = reinterpret_cast<const int32_t*>(blk + kSkScaleOff);
+    ssc0 = ss[lane];
+    ssc1 = ss[64 + lane];
   }
   const float iqs = reinterpret_cast<const float*>(blk + kQFrags * 1024)[n & 7];
   asm volatile("" ::: "memory");
@@ -2679,17 +2653,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
       stage_block<BK, PROD, 0, AL>(ring + b * SL::bytes, t_begin + b * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
                                    a.kn, kg);
 
-  // ---- key and sketch tables (as in the decode kernel, no value table) ----
-  build_tables<BK, PROD, 0>(0.f, kcl, 0.f, ksig, tab, lut_k, lut_q, tid, nthr);
+  // ---- key tables (as in the decode kernel, no value table) ----
+  build_tables<BK, 0>(0.f, kcl, 0.f, ksig, tab, lut_k, tid, nthr);
   if (tid < kDecWaves) lds_put1(lds_addr(&prog[tid]), 0u);
   lds_stores_done();
   Luts T;
   const uint32_t cp = lane & 31;
   T.k = KL::priv ? tab : lut_k;
-  T.q = lut_q;
   T.v = tab;
   T.klane = KL::byte_indexed ? kTabK + 8u * (lane & 15) : KL::priv ? kTabK + 4u * cp : 0u;
-  T.qlane = 8u * cp;
   T.vlane = 4u * cp;
   tables_barrier();
 
@@ -2728,7 +2700,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void search_scan_kernel(SearchArgs 
       stage_block<BK, PROD, 0, AL>(ring + cur * SL::bytes, t0 + NST * kBlockTok, last, lane, dl, kc, kq, kc, a.kn,
                                    a.kn, kg);
     float sc[8];
-    block_scores<BK, PROD, 0>(R, T, bq, bs, sc);
+    block_scores<BK, PROD, 0>(R, T, bq, bs, ssc0, ssc1, sc);
 #pragma unroll
     for (int j = 0; j < 8; ++j) sc[j] *= iqs;
     if (a.pin | a.pout) {

@@ -113,7 +113,7 @@ static void argument_checks() {
                                 nullptr) == TQ_ERR_INVALID_ARG, "decode phase");
   EXPECT(tq_attn_decode_noalloc(&q, &q, qv, 1, 30, 8, nullptr, 1000, &pk, &pk, 0.1f, out, nullptr) ==
              TQ_ERR_INVALID_ARG, "noalloc Hq % Hkv");
-  EXPECT(tq_attn_decode_noalloc(&q, &q, qv, 64, 128, 8, nullptr, 1024, &pk, &pk, 0.1f, out, nullptr) ==
+  EXPECT(tq_attn_decode_noalloc(&q, &q, qv, 128, 128, 8, nullptr, 1024, &pk, &pk, 0.1f, out, nullptr) ==
              TQ_ERR_WORKSPACE, "noalloc beyond the scratch");
   // decode step
   EXPECT(tq_decode_step(&q, &q, x, x, 9, 128, qv, 1, 32, 8, nullptr, 1000, &pk, &pk, 0.1f, out, fake(), ws,

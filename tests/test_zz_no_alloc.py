@@ -59,11 +59,11 @@ def test_noalloc_equals_workspace_call_twice():
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
-    # 1024 units need more workspace than the fixed scratch holds: rejected
+    # 2048 units need more workspace than the fixed scratch holds: rejected
     # before anything is launched, with no output written.
     cfg = synth.WORKLOADS["gqa8_prod4_128k_b4"]
     kq, vq, _, _, _ = quantizers(cfg)
-    B, Hq, Hkv, T_ctx = 64, 128, 8, 1024
+    B, Hq, Hkv, T_ctx = 128, 128, 8, 1024
     assert L.tq_attn_decode_workspace(B, Hq, Hkv, T_ctx) > L.TQ_STATIC_SCRATCH_BYTES
     kp, vp = T.Packed(kq, B * Hkv * T_ctx, DEV), T.Packed(vq, B * Hkv * T_ctx, DEV)
     qg = torch.zeros((B, Hq, 128), dtype=torch.float32, device=DEV)
