@@ -356,7 +356,7 @@ __device__ __forceinline__ float centroid_mag(const Book& bk, int m) {
   return c;
 }
 
-// Cell table of the nearest-centroid search (b_m >= 3). The code of y is
+// Cell table of the nearest-centroid search (b_m >= 2). The code of y is
 // idx = #{i : t_i < y} over the K - 1 signed thresholds t (the magnitudes
 // tp[j] mirrored, t = 0 in the middle, as the search above reads them). On
 // the accumulator acc = S·y (S > 0) the search compares acc with fl(t_i·S),
@@ -409,17 +409,17 @@ __device__ __forceinline__ int build_cell(const Book& bk, int k, CellEntry<PROD>
 }
 
 // Wavefronts per workgroup of the full-size encoder. Encodes with a cell
-// table (b_m >= 3) run one workgroup per compute unit that shares one staged
+// table (b_m >= 2) run one workgroup per compute unit that shares one staged
 // copy of the fragments: 16 wavefronts for mse (with a conflict-free table,
 // below), 12 for prod (three per SIMD, as many as its registers allow). The
 // other mse encodes run two workgroups of 8, the other prod encodes one.
 template <int BM, bool PROD>
-constexpr int enc_waves() { return BM >= 3 ? (PROD ? 12 : 16) : kEncWaves; }
+constexpr int enc_waves() { return BM >= 2 ? (PROD ? 12 : 16) : kEncWaves; }
 
 template <int BM, bool PROD, bool F32IN>
 __global__ __launch_bounds__((enc_waves<BM, PROD>() * 64)) void encode_kernel(EncodeArgs a) {
   constexpr int K = 1 << BM;
-  constexpr bool kCells = BM >= 3;
+  constexpr bool kCells = BM >= 2;
   constexpr int kW = enc_waves<BM, PROD>();
   // mse: 32 interleaved copies of the cell table (entry k of copy c at
   // 256k + 8c bytes, c = lane % 32), so the 32 lanes of a half-wavefront read
@@ -1254,9 +1254,9 @@ extern "C" int tq_encode(const tq_quantizer* q, const void* x, int x_dtype, int6
   // one workgroup per compute unit of 16 wavefronts for mse with a cell
   // table and of 12 for prod with one, two of 8 for the other mse encodes,
   // one of 8 for the other prod encodes
-  const int waves = bm >= 3 ? (prod ? 12 : 16) : kEncWaves;
+  const int waves = bm >= 2 ? (prod ? 12 : 16) : kEncWaves;
   const int64_t want = (tiles + waves - 1) / waves;
-  const int cap = device_cus() * ((prod || bm >= 3) ? 1 : 2);
+  const int cap = device_cus() * ((prod || bm >= 2) ? 1 : 2);
   const int grid = static_cast<int>(want < cap ? want : cap);
   const bool f32 = x_dtype == TQ_F32;
   hipError_t e;
