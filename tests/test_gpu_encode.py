@@ -112,19 +112,23 @@ def test_encode_full_size_sampled(consts):
                      bits, variant)
 
 
-@pytest.mark.parametrize("variant", ["mse", "prod"])
-def test_encode_close_thresholds(consts, variant):
+@pytest.mark.parametrize("variant,bits", [("mse", 4), ("prod", 4), ("mse", 2), ("prod", 3)])
+def test_encode_close_thresholds(consts, variant, bits):
     """A codebook with two thresholds closer together than the encoder's cell
     table can separate (under 1.52/128 apart) makes the encoder keep its
     threshold search; the codes still follow idx = #{t_i < y} for that
-    codebook, and the prod residual uses its centroids."""
+    codebook, and the prod residual uses its centroids. Both table widths:
+    3/4-bit and 2-bit searches."""
     Rk, _, S = consts
-    bits = 4
     bm = bits - 1 if variant == "prod" else bits
     c = book(bm)[0].astype(np.float32).astype(np.float64)
     h = len(c) // 2
-    c[h + 1], c[h + 2] = c[h] + 0.002, c[h] + 0.004      # squeezed, still ascending
-    c[h - 2], c[h - 3] = -c[h + 1], -c[h + 2]            # and antisymmetric
+    if bm >= 3:
+        c[h + 1], c[h + 2] = c[h] + 0.002, c[h] + 0.004      # squeezed, still ascending
+        c[h - 2], c[h - 3] = -c[h + 1], -c[h + 2]            # and antisymmetric
+    else:
+        c[h], c[h + 1] = 0.002, 0.004                        # thresholds -0.003, 0, 0.003
+        c[h - 1], c[h - 2] = -c[h], -c[h + 1]
     t = (c[:-1] + c[1:]) / 2
     assert np.min(np.diff(t)) < 1.52 / 128
     q = T.Quantizer(Rk, bits, variant, S if variant == "prod" else None, DEV)
